@@ -1,0 +1,9 @@
+"""Hierarchical Sparse Attention (HSA) for AMD Instinct MI355X (gfx950).
+
+The operator lives in libhsa.so (hand-written HIP kernels behind the C ABI of
+include/hsa.h); this package is its thin Python binding.  Importing the package does not
+load the library; the first call does, and fails loudly if it has not been built.
+"""
+from .ops import bwd, decode, fwd, pool, problem, select, workspace, workspace_size  # noqa: F401
+
+__all__ = ["select", "pool", "fwd", "bwd", "decode", "problem", "workspace", "workspace_size"]

@@ -1,0 +1,542 @@
+// bwd_generic.hip -- chunk->token inverse index and the plain vector-ALU backward.
+//
+// The backward runs in two phases ("Hardware-aligned Hierarchical Sparse Attention ...",
+// papernotes.org note, 方法详解 › 硬件对齐 Kernel): per token the gradients of the queries and
+// of the chunk weights; then per chunk, over every token that selected it, the gradients of
+// the keys and values.  The weight gradient flows on into the selection scores and from
+// there into the selection query and the pooled chunk key (same note, 层次化稀疏注意力（HSA）
+// 端到端学习).  Phase 2 reads a chunk -> (token, slot) index built without atomics contention:
+// per-tile histograms, an exclusive scan, and a stable scatter in (token, slot) order.
+#include "hsa_common.h"
+#include "hsa_launch.h"
+
+namespace hsa {
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdLayout bwd_layout(const Dims& d) {
+  BwdLayout l{};
+  int tt = 256;
+  while ((d.L + tt - 1) / tt > 256) tt *= 2;
+  l.tile_tokens = tt;
+  l.n_tiles = (d.L + tt - 1) / tt;
+  l.seg = 128;
+  const int64_t bg = (int64_t)d.B * d.Hkv;
+  const int64_t E = (int64_t)d.L * d.K;  // entry capacity per (b, g)
+  l.max_seg = (E + l.seg - 1) / l.seg + d.nC;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  l.ds = take(sizeof(float) * bg * E);
+  l.dw = take(sizeof(float) * bg * E);
+  l.tile_counts = take(sizeof(int32_t) * bg * l.n_tiles * d.nC);
+  l.tile_base = take(sizeof(int32_t) * bg * l.n_tiles * d.nC);
+  l.offsets = take(sizeof(int32_t) * bg * (d.nC + 1));
+  l.entries = take(sizeof(int32_t) * bg * E);
+  l.seg_start = take(sizeof(int32_t) * bg * (d.nC + 1));
+  l.seg_chunk = take(sizeof(int32_t) * bg * l.max_seg);
+  l.n_seg = take(sizeof(int32_t) * bg);
+  l.part_dk = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
+  l.part_dv = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
+  l.part_dks = take(sizeof(float) * bg * l.max_seg * d.D);
+  l.total = o;
+  return l;
+}
+
+// ---- inverse index ---------------------------------------------------------------------
+
+// Per (b, g, tile): how many of the tile's (token, slot) entries chose each chunk.
+__global__ void __launch_bounds__(256) k_inv_count(const int32_t* __restrict__ idx,
+                                                   int32_t* __restrict__ tile_counts, int L,
+                                                   int Hkv, int K, int nC, int tile_tokens,
+                                                   int n_tiles) {
+  extern __shared__ int32_t cnt[];
+  const int tile = blockIdx.x % n_tiles;
+  const int bg = blockIdx.x / n_tiles;
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  for (int c = threadIdx.x; c < nC; c += blockDim.x) cnt[c] = 0;
+  __syncthreads();
+  const int t0 = tile * tile_tokens;
+  const int t1 = min(L, t0 + tile_tokens);
+  for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
+    const int32_t* ir = idx + ((b * L + t) * Hkv + g) * K;
+    for (int k = 0; k < K; ++k) {
+      int c = ir[k];
+      if (c >= 0 && c < nC) atomicAdd(&cnt[c], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* out = tile_counts + ((size_t)bg * n_tiles + tile) * nC;
+  for (int c = threadIdx.x; c < nC; c += blockDim.x) out[c] = cnt[c];
+}
+
+// Exclusive scan of n ints in place (one block of 1024 threads; thread-contiguous runs).
+__device__ void block_exclusive_scan(int32_t* a, int n, int32_t* total_out) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int lo = min(n, tid * per);
+  const int hi = min(n, lo + per);
+  int32_t s = 0;
+  for (int i = lo; i < hi; ++i) s += a[i];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      int32_t v = part[i];
+      part[i] = run;
+      run += v;
+    }
+    *total_out = run;
+  }
+  __syncthreads();
+  int32_t run = part[tid];
+  for (int i = lo; i < hi; ++i) {
+    int32_t v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  __syncthreads();
+}
+
+// Per (b, g): chunk offsets, each tile's base position per chunk, and the phase-2 segments
+// (ceil(n_c / seg) per chunk) with their chunk ids.
+__global__ void __launch_bounds__(1024) k_inv_scan(const int32_t* __restrict__ tile_counts,
+                                                   int32_t* __restrict__ tile_base,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ seg_start,
+                                                   int32_t* __restrict__ seg_chunk,
+                                                   int32_t* __restrict__ n_seg, int nC,
+                                                   int n_tiles, int seg, int64_t max_seg) {
+  __shared__ int32_t total_e, total_s;
+  const int bg = blockIdx.x;
+  const int32_t* tc = tile_counts + (size_t)bg * n_tiles * nC;
+  int32_t* tb = tile_base + (size_t)bg * n_tiles * nC;
+  int32_t* off = offsets + (size_t)bg * (nC + 1);
+  int32_t* ss = seg_start + (size_t)bg * (nC + 1);
+  for (int c = threadIdx.x; c < nC; c += blockDim.x) {
+    int32_t col = 0;
+    for (int tile = 0; tile < n_tiles; ++tile) col += tc[(size_t)tile * nC + c];
+    off[c] = col;
+    ss[c] = (col + seg - 1) / seg;
+  }
+  __syncthreads();
+  block_exclusive_scan(off, nC, &total_e);
+  block_exclusive_scan(ss, nC, &total_s);
+  if (threadIdx.x == 0) {
+    off[nC] = total_e;
+    ss[nC] = total_s;
+    n_seg[bg] = total_s;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < nC; c += blockDim.x) {
+    int32_t run = off[c];
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      tb[(size_t)tile * nC + c] = run;
+      run += tc[(size_t)tile * nC + c];
+    }
+    int32_t* sc = seg_chunk + (size_t)bg * max_seg;
+    for (int s = ss[c]; s < ss[c + 1]; ++s) sc[s] = c;
+  }
+}
+
+// Per (b, g, tile), one wave: walk the tile's tokens in order; lane k places slot k.  A token's
+// chunks are distinct, so the lanes of one step never share a counter.
+__global__ void __launch_bounds__(64) k_inv_scatter(const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ tile_base,
+                                                    int32_t* __restrict__ entries, int L,
+                                                    int Hkv, int K, int nC, int tile_tokens,
+                                                    int n_tiles) {
+  extern __shared__ int32_t cnt[];
+  const int tile = blockIdx.x % n_tiles;
+  const int bg = blockIdx.x / n_tiles;
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const int lane = threadIdx.x;
+  for (int c = lane; c < nC; c += kWave) cnt[c] = 0;
+  __syncthreads();
+  const int32_t* tb = tile_base + ((size_t)bg * n_tiles + tile) * nC;
+  int32_t* ent = entries + (size_t)bg * L * K;
+  const int t0 = tile * tile_tokens;
+  const int t1 = min(L, t0 + tile_tokens);
+  for (int t = t0; t < t1; ++t) {
+    if (lane < K) {
+      int c = idx[((b * L + t) * Hkv + g) * K + lane];
+      if (c >= 0 && c < nC) {
+        int pos = tb[c] + cnt[c];
+        cnt[c] += 1;
+        ent[pos] = t * K + lane;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_invidx(const Dims& d, const BwdLayout& lay, const int32_t* idx, char* ws,
+                         hipStream_t s) {
+  const int bg = d.B * d.Hkv;
+  if (bg == 0 || d.nC == 0) return hipSuccess;
+  int32_t* tc = (int32_t*)(ws + lay.tile_counts);
+  int32_t* tb = (int32_t*)(ws + lay.tile_base);
+  size_t lds = sizeof(int32_t) * d.nC;
+  k_inv_count<<<dim3(bg * lay.n_tiles), 256, lds, s>>>(idx, tc, d.L, d.Hkv, d.K, d.nC,
+                                                        lay.tile_tokens, lay.n_tiles);
+  k_inv_scan<<<dim3(bg), 1024, 0, s>>>(tc, tb, (int32_t*)(ws + lay.offsets),
+                                       (int32_t*)(ws + lay.seg_start),
+                                       (int32_t*)(ws + lay.seg_chunk),
+                                       (int32_t*)(ws + lay.n_seg), d.nC, lay.n_tiles, lay.seg,
+                                       lay.max_seg);
+  k_inv_scatter<<<dim3(bg * lay.n_tiles), 64, lds, s>>>(idx, tb, (int32_t*)(ws + lay.entries),
+                                                         d.L, d.Hkv, d.K, d.nC, lay.tile_tokens,
+                                                         lay.n_tiles);
+  return hipGetLastError();
+}
+
+// ---- phase 1: per token ----------------------------------------------------------------
+
+// One wave per (b, t, g) row: recompute each selected chunk's probabilities, accumulate
+// dQ, the weight gradients dw_k = sum_h <dO_h, O_{t,h,k}>, the score gradients ds through
+// the stick-breaking chain, and dQs.
+template <typename T>
+__global__ void __launch_bounds__(64) k_bwd_p1_generic(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ Kslc, const int32_t* __restrict__ idx,
+    const float* __restrict__ score, const float* __restrict__ w, const T* __restrict__ dO,
+    T* __restrict__ dQ, T* __restrict__ dQs, float* __restrict__ ds_out,
+    float* __restrict__ dw_out, int L, int Hq, int Hkv, int D, int S, int Kt, int G, int nC,
+    float sm_scale, float sel_scale) {
+  __shared__ float qsh[kMaxG][128];
+  __shared__ float dosh[kMaxG][128];
+  __shared__ float dzsh[kMaxG][kChunk];
+  __shared__ float dwsh[kMaxK];
+  __shared__ float dssh[kMaxK];
+  const int lane = threadIdx.x;
+  const size_t row = blockIdx.x;
+  const int g = (int)(row % Hkv);
+  const size_t bt = row / Hkv;
+  const size_t b = bt / L;
+  const size_t qbase = (bt * Hq + (size_t)g * G) * D;
+  for (int i = lane; i < G * D; i += kWave) {
+    qsh[i / D][i % D] = to_f32(Q[qbase + i]);
+    dosh[i / D][i % D] = to_f32(dO[qbase + i]);
+  }
+  float dq[kMaxG][2];
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) dq[h][0] = dq[h][1] = 0.0f;
+  __syncthreads();
+
+  const size_t kvstride = (size_t)Hkv * D;
+  for (int k = 0; k < Kt; ++k) {
+    const int c = idx[row * Kt + k];
+    if (c < 0 || c >= nC) {
+      if (lane == 0) dwsh[k] = 0.0f;
+      continue;
+    }
+    const float wk = w[row * Kt + k];
+    const size_t cbase = ((b * L + (size_t)c * S) * Hkv + g) * D;
+    float z[kMaxG], da[kMaxG];
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) z[h] = da[h] = 0.0f;
+    const T* kr = K + cbase + (size_t)lane * kvstride;
+    const T* vr = V + cbase + (size_t)lane * kvstride;
+    for (int e = 0; e < D; e += 8) {
+      float kv[8], vv[8];
+      load8(kr + e, kv);
+      load8(vr + e, vv);
+#pragma unroll
+      for (int h = 0; h < kMaxG; ++h) {
+        if (h < G) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            z[h] += qsh[h][e + i] * kv[i];
+            da[h] += dosh[h][e + i] * vv[i];
+          }
+        }
+      }
+    }
+    float dwk = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+      if (h < G) {
+        float zz = z[h] * sm_scale;
+        float m = fmaxf(0.0f, wave_max(zz));
+        float ex = __expf(zz - m);
+        float a = ex / (__expf(-m) + wave_sum(ex));
+        float Dh = wave_sum(a * da[h]);
+        dzsh[h][lane] = wk * a * (da[h] - Dh);
+        dwk += Dh;
+      }
+    }
+    if (lane == 0) dwsh[k] = dwk;
+    __syncthreads();
+    const T* kc = K + cbase;
+    for (int j = 0; j < kChunk; ++j) {
+      float k0 = to_f32(kc[(size_t)j * kvstride + lane]);
+      float k1 = (D > 64) ? to_f32(kc[(size_t)j * kvstride + 64 + lane]) : 0.0f;
+#pragma unroll
+      for (int h = 0; h < kMaxG; ++h) {
+        if (h < G) {
+          float dz = dzsh[h][j];
+          dq[h][0] += dz * k0;
+          dq[h][1] += dz * k1;
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < kMaxG; ++h) {
+    if (h < G) {
+      dQ[qbase + (size_t)h * D + lane] = from_f32<T>(dq[h][0] * sm_scale);
+      if (D > 64) dQ[qbase + (size_t)h * D + 64 + lane] = from_f32<T>(dq[h][1] * sm_scale);
+    }
+  }
+  // stick-breaking chain rule over the valid prefix, newest slot first:
+  // ds_k = dw_k w_k (1 - p_k) - p_k * sum_{k' > k} dw_k' w_k'
+  if (lane == 0) {
+    double suffix = 0.0;
+    for (int k = Kt - 1; k >= 0; --k) {
+      int c = idx[row * Kt + k];
+      double dsk = 0.0;
+      if (c >= 0 && c < nC) {
+        double p = sigmoid_d((double)score[row * Kt + k]);
+        double dwk = (double)dwsh[k], wk = (double)w[row * Kt + k];
+        dsk = dwk * wk * (1.0 - p) - p * suffix;
+        suffix += dwk * wk;
+      }
+      dssh[k] = (float)dsk;
+      ds_out[row * Kt + k] = (float)dsk;
+      dw_out[row * Kt + k] = (c >= 0 && c < nC) ? dwsh[k] : 0.0f;
+    }
+  }
+  __syncthreads();
+  const size_t qsrow = row * D;
+  for (int e = lane; e < D; e += kWave) {
+    float acc = 0.0f;
+    for (int k = 0; k < Kt; ++k) {
+      int c = idx[row * Kt + k];
+      if (c < 0 || c >= nC) continue;
+      acc += dssh[k] * to_f32(Kslc[((b * nC + c) * Hkv + g) * D + e]);
+    }
+    dQs[qsrow + e] = from_f32<T>(acc * sel_scale);
+  }
+}
+
+// ---- phase 2: per chunk segment ----------------------------------------------------------
+
+// One block of two waves per segment of a chunk's selector list.  Lane j of wave 0 keeps
+// row j of the segment's partial dK in registers, lane j of wave 1 row j of dV; wave 1
+// also sums the segment's partial dKslc.  Partials are reduced in segment order later.
+template <typename T, int D>
+__global__ void __launch_bounds__(128) k_bwd_p2_seg(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ Qs, const float* __restrict__ w, const T* __restrict__ dO,
+    const float* __restrict__ ds_in, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ entries, const int32_t* __restrict__ seg_start,
+    const int32_t* __restrict__ seg_chunk, const int32_t* __restrict__ n_seg,
+    float* __restrict__ part_dk, float* __restrict__ part_dv, float* __restrict__ part_dks,
+    int L, int Hq, int Hkv, int S, int Kt, int G, int nC, int seg, int64_t max_seg,
+    float sm_scale, float sel_scale) {
+  __shared__ float qsh[kMaxG][D];
+  __shared__ float dosh[kMaxG][D];
+  __shared__ float qssh[D];
+  const int64_t sidx = blockIdx.x % max_seg;
+  const int bg = (int)(blockIdx.x / max_seg);
+  if (sidx >= n_seg[bg]) return;  // uniform for the whole block
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const int c = seg_chunk[(size_t)bg * max_seg + sidx];
+  const int32_t* off = offsets + (size_t)bg * (nC + 1);
+  const int32_t* ss = seg_start + (size_t)bg * (nC + 1);
+  const int e0 = off[c] + (int)(sidx - ss[c]) * seg;
+  const int e1 = min(off[c + 1], e0 + seg);
+  const int32_t* ent = entries + (size_t)bg * L * Kt;
+
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const size_t kvstride = (size_t)Hkv * D;
+  const size_t cbase = ((b * L + (size_t)c * S) * Hkv + g) * D;
+  const T* krow = K + cbase + (size_t)lane * kvstride;  // this lane's key row
+  const T* vrow = V + cbase + (size_t)lane * kvstride;  // and value row
+  float acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) acc[e] = 0.0f;
+  float dks0 = 0.0f, dks1 = 0.0f;
+
+  for (int ei = e0; ei < e1; ++ei) {
+    const int val = ent[ei];
+    if (val < 0 || val >= L * Kt) continue;  // only an invalid selection leaves a hole here
+    const int t = val / Kt;
+    const int k = val % Kt;
+    const size_t srow = ((b * L + t) * Hkv + g);
+    const float wk = w[srow * Kt + k];
+    const float dsk = ds_in[srow * Kt + k];
+    const size_t qbase = ((b * L + t) * Hq + (size_t)g * G) * D;
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * D; i += 2 * kWave) {
+      qsh[i / D][i % D] = to_f32(Q[qbase + i]);
+      dosh[i / D][i % D] = to_f32(dO[qbase + i]);
+    }
+    for (int i = threadIdx.x; i < D; i += 2 * kWave) qssh[i] = to_f32(Qs[srow * D + i]);
+    __syncthreads();
+    float z[kMaxG], da[kMaxG];
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) z[h] = da[h] = 0.0f;
+    for (int e = 0; e < D; e += 8) {
+      float kv[8], vv[8];
+      load8(krow + e, kv);
+      load8(vrow + e, vv);
+#pragma unroll
+      for (int h = 0; h < kMaxG; ++h) {
+        if (h < G) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            z[h] += qsh[h][e + i] * kv[i];
+            da[h] += dosh[h][e + i] * vv[i];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+      if (h < G) {
+        float zz = z[h] * sm_scale;
+        float m = fmaxf(0.0f, wave_max(zz));
+        float ex = __expf(zz - m);
+        float a = ex / (__expf(-m) + wave_sum(ex));
+        if (wave == 0) {
+          float Dh = wave_sum(a * da[h]);
+          float dz = wk * a * (da[h] - Dh) * sm_scale;
+#pragma unroll
+          for (int e = 0; e < D; ++e) acc[e] += dz * qsh[h][e];
+        } else {
+          float wa = wk * a;
+#pragma unroll
+          for (int e = 0; e < D; ++e) acc[e] += wa * dosh[h][e];
+        }
+      }
+    }
+    if (wave == 1) {
+      dks0 += dsk * qssh[lane];
+      if (D > 64) dks1 += dsk * qssh[(lane + 64) % D];
+    }
+  }
+  const size_t pbase = ((size_t)bg * max_seg + sidx);
+  float* dst = (wave == 0 ? part_dk : part_dv) + (pbase * kChunk + lane) * D;
+  for (int e = 0; e < D; e += 4) {
+    *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  }
+  if (wave == 1) {
+    part_dks[pbase * D + lane] = dks0 * sel_scale;
+    if (D > 64) part_dks[pbase * D + 64 + lane] = dks1 * sel_scale;
+  }
+}
+
+// One block per chunk (including the incomplete tail chunk, whose rows get zero): sum the
+// chunk's segment partials in segment order, fold dKslc/S into dK if asked, store.
+template <typename T>
+__global__ void __launch_bounds__(256) k_bwd_p2_reduce(
+    const float* __restrict__ part_dk, const float* __restrict__ part_dv,
+    const float* __restrict__ part_dks, const int32_t* __restrict__ seg_start, T* __restrict__ dK,
+    T* __restrict__ dV, float* __restrict__ dKslc, int L, int Hkv, int D, int S, int nC,
+    int n_chunks_all, int64_t max_seg, int fold) {
+  __shared__ float dks[128];
+  const int c = blockIdx.x % n_chunks_all;
+  const int bg = blockIdx.x / n_chunks_all;
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const size_t kvstride = (size_t)Hkv * D;
+  const size_t cbase = ((b * L + (size_t)c * S) * Hkv + g) * D;
+  if (c >= nC) {  // incomplete tail chunk: never selectable
+    for (int i = threadIdx.x; i < kChunk * D; i += blockDim.x) {
+      int j = i / D, e = i % D;
+      if ((size_t)c * S + j < (size_t)L) {
+        dK[cbase + j * kvstride + e] = from_f32<T>(0.0f);
+        dV[cbase + j * kvstride + e] = from_f32<T>(0.0f);
+      }
+    }
+    return;
+  }
+  const int32_t* ss = seg_start + (size_t)bg * (nC + 1);
+  const int s0 = ss[c], s1 = ss[c + 1];
+  const size_t pb = (size_t)bg * max_seg;
+  for (int e = threadIdx.x; e < D; e += blockDim.x) {
+    float a = 0.0f;
+    for (int s = s0; s < s1; ++s) a += part_dks[(pb + s) * D + e];
+    dks[e] = a;
+    if (dKslc) dKslc[((b * nC + c) * Hkv + g) * D + e] = a;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kChunk * D; i += blockDim.x) {
+    int j = i / D, e = i % D;
+    float ak = 0.0f, av = 0.0f;
+    for (int s = s0; s < s1; ++s) {
+      ak += part_dk[((pb + s) * kChunk + j) * D + e];
+      av += part_dv[((pb + s) * kChunk + j) * D + e];
+    }
+    if (fold) ak += dks[e] / (float)S;
+    dK[cbase + j * kvstride + e] = from_f32<T>(ak);
+    dV[cbase + j * kvstride + e] = from_f32<T>(av);
+  }
+}
+
+template <typename T>
+static void launch_bwd_typed(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
+                             const void* V, const void* Qs, const void* Kslc,
+                             const int32_t* idx, const float* score, const float* w,
+                             const void* dO, void* dQ, void* dK, void* dV, void* dQs,
+                             float* dKslc, bool fold, char* ws, hipStream_t s) {
+  const size_t rows = (size_t)d.B * d.L * d.Hkv;
+  const float sm = (float)d.sm_scale, sel = (float)d.sel_scale;
+  float* ds = (float*)(ws + lay.ds);
+  float* dw = (float*)(ws + lay.dw);
+  k_bwd_p1_generic<T><<<dim3((unsigned)rows), 64, 0, s>>>(
+      (const T*)Q, (const T*)K, (const T*)V, (const T*)Kslc, idx, score, w, (const T*)dO,
+      (T*)dQ, (T*)dQs, ds, dw, d.L, d.Hq, d.Hkv, d.D, d.S, d.K, d.G, d.nC, sm, sel);
+  const int bg = d.B * d.Hkv;
+  if (d.nC > 0) {
+    dim3 grid((unsigned)(bg * lay.max_seg));
+    auto args = [&](auto kern) {
+      kern<<<grid, 128, 0, s>>>((const T*)Q, (const T*)K, (const T*)V, (const T*)Qs, w,
+                                (const T*)dO, ds, (const int32_t*)(ws + lay.offsets),
+                                (const int32_t*)(ws + lay.entries),
+                                (const int32_t*)(ws + lay.seg_start),
+                                (const int32_t*)(ws + lay.seg_chunk),
+                                (const int32_t*)(ws + lay.n_seg), (float*)(ws + lay.part_dk),
+                                (float*)(ws + lay.part_dv), (float*)(ws + lay.part_dks), d.L, d.Hq,
+                                d.Hkv, d.S, d.K, d.G, d.nC, lay.seg, lay.max_seg, sm, sel);
+    };
+    if (d.D == 64)
+      args(k_bwd_p2_seg<T, 64>);
+    else
+      args(k_bwd_p2_seg<T, 128>);
+  }
+  const int n_all = (d.L + d.S - 1) / d.S;
+  k_bwd_p2_reduce<T><<<dim3((unsigned)(bg * n_all)), 256, 0, s>>>(
+      (const float*)(ws + lay.part_dk), (const float*)(ws + lay.part_dv),
+      (const float*)(ws + lay.part_dks), (const int32_t*)(ws + lay.seg_start), (T*)dK, (T*)dV,
+      dKslc, d.L, d.Hkv, d.D, d.S, d.nC, n_all, lay.max_seg, fold ? 1 : 0);
+}
+
+hipError_t launch_bwd_generic(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
+                              const void* V, const void* Qs, const void* Kslc,
+                              const int32_t* idx, const float* score, const float* w,
+                              const void* dO, void* dQ, void* dK, void* dV, void* dQs,
+                              float* dKslc, bool fold, char* ws, hipStream_t s) {
+  hipError_t e = launch_invidx(d, lay, idx, ws, s);
+  if (e != hipSuccess) return e;
+  if (d.dtype == 1)
+    launch_bwd_typed<bf16>(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK, dV, dQs, dKslc,
+                           fold, ws, s);
+  else
+    launch_bwd_typed<float>(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK, dV, dQs, dKslc,
+                            fold, ws, s);
+  return hipGetLastError();
+}
+
+}  // namespace hsa

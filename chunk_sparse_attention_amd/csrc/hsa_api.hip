@@ -1,0 +1,260 @@
+// hsa_api.hip -- the C ABI of libhsa.so: validation, workspace sizing and dispatch.
+//
+// Every entry point validates its arguments before enqueuing anything; on failure it
+// returns a status, records a message for hsa_last_error(), launches nothing and writes
+// nothing.  The library never allocates, frees or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "hsa.h"
+#include "hsa_common.h"
+#include "hsa_launch.h"
+
+#define HSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hsa_status_t fail(hsa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hsa_status_t ok() {
+  g_last_error.clear();
+  return HSA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Common shape checks.  `op` decides which limits apply.
+hsa_status_t check_problem(int op, const hsa_problem_t* p, hsa::Dims* d) {
+  if (!p) return fail(HSA_ERR_INVALID_ARG, "problem pointer is NULL");
+  if (op < HSA_OP_SELECT || op > HSA_OP_DECODE)
+    return fail(HSA_ERR_INVALID_ARG, "unknown op %d", op);
+  if (p->B < 1 || p->L < 1 || p->Hq < 1 || p->Hkv < 1 || p->D < 1 || p->S < 1 || p->K < 1)
+    return fail(HSA_ERR_INVALID_ARG, "sizes must be positive (B=%d L=%d Hq=%d Hkv=%d D=%d S=%d K=%d)",
+                p->B, p->L, p->Hq, p->Hkv, p->D, p->S, p->K);
+  if (p->dtype != HSA_F32 && p->dtype != HSA_BF16)
+    return fail(HSA_ERR_UNSUPPORTED, "dtype %d is not fp32 (0) or bf16 (1)", p->dtype);
+  if (p->Hq % p->Hkv != 0)
+    return fail(HSA_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
+  if (p->Hq / p->Hkv > hsa::kMaxG)
+    return fail(HSA_ERR_UNSUPPORTED, "Hq/Hkv=%d exceeds %d", p->Hq / p->Hkv, hsa::kMaxG);
+  if (p->S != hsa::kChunk) return fail(HSA_ERR_UNSUPPORTED, "chunk size S=%d (only 64)", p->S);
+  if (p->D != 64 && p->D != 128)
+    return fail(HSA_ERR_UNSUPPORTED, "head dim D=%d (only 64 or 128)", p->D);
+  if (p->K > hsa::kMaxK) return fail(HSA_ERR_UNSUPPORTED, "K=%d exceeds %d", p->K, hsa::kMaxK);
+  if ((int64_t)p->L * p->K >= ((int64_t)1 << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "L*K=%lld does not fit int32", (long long)p->L * p->K);
+  if ((int64_t)p->B * p->L * p->Hkv >= ((int64_t)1 << 31))
+    return fail(HSA_ERR_UNSUPPORTED, "B*L*Hkv rows exceed the grid limit");
+  if (!isfinite(p->sm_scale) || !isfinite(p->sel_scale))
+    return fail(HSA_ERR_INVALID_ARG, "scales must be finite");
+  const int nC = p->L / p->S;
+  if (op == HSA_OP_BWD && nC > 16384)
+    return fail(HSA_ERR_UNSUPPORTED, "backward supports at most 16384 chunks (nC=%d)", nC);
+  d->B = p->B;
+  d->L = p->L;
+  d->Hq = p->Hq;
+  d->Hkv = p->Hkv;
+  d->D = p->D;
+  d->S = p->S;
+  d->K = p->K;
+  d->nC = nC;
+  d->G = p->Hq / p->Hkv;
+  d->sm_scale = p->sm_scale != 0.0f ? (double)p->sm_scale : 1.0 / sqrt((double)p->D);
+  d->sel_scale = p->sel_scale != 0.0f ? (double)p->sel_scale : 1.0 / sqrt((double)p->D);
+  d->dtype = p->dtype;
+  d->flags = p->flags;
+  return HSA_OK;
+}
+
+hsa_status_t need_tensor(const void* ptr, const char* name) {
+  if (!ptr) return fail(HSA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(ptr, 16)) return fail(HSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return HSA_OK;
+}
+
+hsa_status_t need_small(const void* ptr, const char* name) {
+  if (!ptr) return fail(HSA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(ptr, 4)) return fail(HSA_ERR_INVALID_ARG, "%s is not 4-byte aligned", name);
+  return HSA_OK;
+}
+
+size_t ws_bytes_for(int op, const hsa::Dims& d) {
+  switch (op) {
+    case HSA_OP_BWD:
+      return hsa::bwd_layout(d).total;
+    case HSA_OP_DECODE:
+      return hsa::dec_layout(d).total;
+    default:
+      return 0;
+  }
+}
+
+hsa_status_t check_ws(int op, const hsa::Dims& d, const void* ws, size_t ws_bytes) {
+  size_t need = ws_bytes_for(op, d);
+  if (need == 0) return HSA_OK;
+  if (!ws || ws_bytes < need)
+    return fail(HSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, ws_bytes,
+                ws ? "" : " (NULL)");
+  if (!aligned(ws, 256)) return fail(HSA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  return HSA_OK;
+}
+
+// Refuse to enqueue behind an unreported failure of earlier work.
+hsa_status_t check_pending() {
+  hipError_t e = hipPeekAtLastError();
+  if (e != hipSuccess)
+    return fail(HSA_ERR_HIP, "a HIP error is pending from earlier work: %s", hipGetErrorString(e));
+  return HSA_OK;
+}
+
+hsa_status_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(HSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define TRY(x)                          \
+  do {                                  \
+    hsa_status_t st_ = (x);             \
+    if (st_ != HSA_OK) return st_;      \
+  } while (0)
+
+}  // namespace
+
+HSA_EXPORT const char* hsa_status_string(hsa_status_t s) {
+  switch (s) {
+    case HSA_OK:
+      return "HSA_OK";
+    case HSA_ERR_INVALID_ARG:
+      return "HSA_ERR_INVALID_ARG";
+    case HSA_ERR_UNSUPPORTED:
+      return "HSA_ERR_UNSUPPORTED";
+    case HSA_ERR_WORKSPACE:
+      return "HSA_ERR_WORKSPACE";
+    case HSA_ERR_HIP:
+      return "HSA_ERR_HIP";
+  }
+  return "HSA_ERR_UNKNOWN";
+}
+
+HSA_EXPORT const char* hsa_last_error(void) { return g_last_error.c_str(); }
+
+HSA_EXPORT const char* hsa_version(void) { return "0.1.0"; }
+
+HSA_EXPORT hsa_status_t hsa_workspace_size(int op, const hsa_problem_t* p, size_t* bytes) {
+  hsa::Dims d;
+  if (!bytes) return fail(HSA_ERR_INVALID_ARG, "bytes pointer is NULL");
+  TRY(check_problem(op, p, &d));
+  *bytes = ws_bytes_for(op, d);
+  return ok();
+}
+
+HSA_EXPORT hsa_status_t hsa_select(const hsa_problem_t* p, const void* Qs, const void* K,
+                                   void* Kslc, int32_t* idx, float* score, float* w, void* ws,
+                                   size_t ws_bytes, hsa_stream_t stream) {
+  hsa::Dims d;
+  TRY(check_problem(HSA_OP_SELECT, p, &d));
+  TRY(need_tensor(K, "K"));
+  if (d.nC > 0) TRY(need_tensor(Kslc, "Kslc"));
+  if (Qs) {
+    TRY(need_tensor(Qs, "Qs"));
+    TRY(need_small(idx, "idx"));
+    TRY(need_small(score, "score"));
+    TRY(need_small(w, "w"));
+  }
+  TRY(check_ws(HSA_OP_SELECT, d, ws, ws_bytes));
+  TRY(check_pending());
+  hipStream_t s = (hipStream_t)stream;
+  if (d.nC > 0) {
+    hipError_t e = hsa::launch_pool(d, K, Kslc, s);
+    if (e != hipSuccess) return launched(e, "pool");
+  }
+  if (!Qs) return ok();
+  return launched(hsa::launch_select_generic(d, Qs, Kslc, idx, score, w, s), "select");
+}
+
+HSA_EXPORT hsa_status_t hsa_fwd(const hsa_problem_t* p, const void* Q, const void* K,
+                                const void* V, const int32_t* idx, const float* w, void* O,
+                                void* ws, size_t ws_bytes, hsa_stream_t stream) {
+  hsa::Dims d;
+  TRY(check_problem(HSA_OP_FWD, p, &d));
+  TRY(need_tensor(Q, "Q"));
+  TRY(need_tensor(K, "K"));
+  TRY(need_tensor(V, "V"));
+  TRY(need_small(idx, "idx"));
+  TRY(need_small(w, "w"));
+  TRY(need_tensor(O, "O"));
+  TRY(check_ws(HSA_OP_FWD, d, ws, ws_bytes));
+  TRY(check_pending());
+  hipStream_t s = (hipStream_t)stream;
+  return launched(hsa::launch_fwd_generic(d, Q, K, V, idx, w, O, s), "fwd");
+}
+
+HSA_EXPORT hsa_status_t hsa_bwd(const hsa_problem_t* p, const void* Q, const void* K,
+                                const void* V, const void* Qs, const void* Kslc,
+                                const int32_t* idx, const float* score, const float* w,
+                                const void* dO, void* dQ, void* dK, void* dV, void* dQs,
+                                float* dKslc, uint32_t flags, void* ws, size_t ws_bytes,
+                                hsa_stream_t stream) {
+  hsa::Dims d;
+  TRY(check_problem(HSA_OP_BWD, p, &d));
+  TRY(need_tensor(Q, "Q"));
+  TRY(need_tensor(K, "K"));
+  TRY(need_tensor(V, "V"));
+  TRY(need_tensor(Qs, "Qs"));
+  if (d.nC > 0) TRY(need_tensor(Kslc, "Kslc"));
+  TRY(need_small(idx, "idx"));
+  TRY(need_small(score, "score"));
+  TRY(need_small(w, "w"));
+  TRY(need_tensor(dO, "dO"));
+  TRY(need_tensor(dQ, "dQ"));
+  TRY(need_tensor(dK, "dK"));
+  TRY(need_tensor(dV, "dV"));
+  TRY(need_tensor(dQs, "dQs"));
+  if (dKslc && !aligned(dKslc, 16)) return fail(HSA_ERR_INVALID_ARG, "dKslc is not 16-byte aligned");
+  if (flags & ~(uint32_t)HSA_BWD_FOLD_KSLC) return fail(HSA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  TRY(check_ws(HSA_OP_BWD, d, ws, ws_bytes));
+  TRY(check_pending());
+  hipStream_t s = (hipStream_t)stream;
+  hsa::BwdLayout lay = hsa::bwd_layout(d);
+  return launched(hsa::launch_bwd_generic(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK,
+                                          dV, dQs, dKslc, (flags & HSA_BWD_FOLD_KSLC) != 0,
+                                          (char*)ws, s),
+                  "bwd");
+}
+
+HSA_EXPORT hsa_status_t hsa_decode(const hsa_problem_t* p, const void* q, const void* qs,
+                                   const void* Kcache, const void* Vcache, const void* Kslc,
+                                   void* O, int32_t* idx, float* score, float* w, void* ws,
+                                   size_t ws_bytes, hsa_stream_t stream) {
+  hsa::Dims d;
+  TRY(check_problem(HSA_OP_DECODE, p, &d));
+  TRY(need_tensor(q, "q"));
+  TRY(need_tensor(qs, "qs"));
+  TRY(need_tensor(Kcache, "Kcache"));
+  TRY(need_tensor(Vcache, "Vcache"));
+  if (d.nC > 0) TRY(need_tensor(Kslc, "Kslc"));
+  TRY(need_tensor(O, "O"));
+  TRY(need_small(idx, "idx"));
+  TRY(need_small(w, "w"));
+  if (score && !aligned(score, 4)) return fail(HSA_ERR_INVALID_ARG, "score is not 4-byte aligned");
+  TRY(check_ws(HSA_OP_DECODE, d, ws, ws_bytes));
+  TRY(check_pending());
+  hipStream_t s = (hipStream_t)stream;
+  hsa::DecLayout lay = hsa::dec_layout(d);
+  return launched(hsa::launch_decode_generic(d, lay, q, qs, Kcache, Vcache, Kslc, O, idx, score,
+                                             w, (char*)ws, s),
+                  "decode");
+}

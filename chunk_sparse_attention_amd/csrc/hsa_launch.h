@@ -1,0 +1,59 @@
+// hsa_launch.h -- host-side launchers behind the C ABI (internal to libhsa.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hsa {
+
+// Validated problem, with derived sizes and the scales resolved in double.
+struct Dims {
+  int B, L, Hq, Hkv, D, S, K;
+  int nC;  // complete chunks floor(L/S)
+  int G;   // query heads per group
+  double sm_scale, sel_scale;
+  int dtype;  // 0 fp32, 1 bf16
+  unsigned flags;
+};
+
+// Backward workspace carve-up (byte offsets into the caller's workspace).
+struct BwdLayout {
+  int tile_tokens;  // tokens per tile of the inverse-index build
+  int n_tiles;      // tiles per (b, g)
+  int seg;          // entries per backward-phase-2 segment
+  int64_t max_seg;  // segment capacity per (b, g)
+  size_t ds, dw, tile_counts, tile_base, offsets, entries, seg_start, seg_chunk, n_seg,
+      part_dk, part_dv, part_dks, total;
+};
+BwdLayout bwd_layout(const Dims& d);
+
+// Decode workspace: per (b, g) the candidate keys of every scan block.
+struct DecLayout {
+  int chunks_per_block;
+  int n_blocks;  // scan blocks per (b, g)
+  size_t cand, total;
+};
+DecLayout dec_layout(const Dims& d);
+
+// F1 pooling (both dtypes).
+hipError_t launch_pool(const Dims& d, const void* K, void* Kslc, hipStream_t s);
+
+// Generic vector-ALU kernels (fp32 and bf16).
+hipError_t launch_select_generic(const Dims& d, const void* Qs, const void* Kslc, int32_t* idx,
+                                 float* score, float* w, hipStream_t s);
+hipError_t launch_fwd_generic(const Dims& d, const void* Q, const void* K, const void* V,
+                              const int32_t* idx, const float* w, void* O, hipStream_t s);
+hipError_t launch_invidx(const Dims& d, const BwdLayout& lay, const int32_t* idx, char* ws,
+                         hipStream_t s);
+hipError_t launch_bwd_generic(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
+                              const void* V, const void* Qs, const void* Kslc,
+                              const int32_t* idx, const float* score, const float* w,
+                              const void* dO, void* dQ, void* dK, void* dV, void* dQs,
+                              float* dKslc, bool fold, char* ws, hipStream_t s);
+hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void* q,
+                                 const void* qs, const void* Kc, const void* Vc,
+                                 const void* Kslc, void* O, int32_t* idx, float* score,
+                                 float* w, char* ws, hipStream_t s);
+
+}  // namespace hsa

@@ -1,0 +1,131 @@
+// select_generic.hip -- chunk-key pooling and the plain vector-ALU selection kernel.
+//
+// Chunk selection ("Hardware-aligned Hierarchical Sparse Attention ...", papernotes.org note,
+// 方法详解 › 层次化稀疏注意力（HSA）, Chunk Selection): each chunk is keyed by the mean of its
+// keys; each token scores the earlier chunks with its selection query and keeps the top-K,
+// per query group.  The chunk weights are stick-breaking over the sigmoid of the ranked
+// scores (same section, 第二阶段).
+#include "hsa_common.h"
+#include "hsa_launch.h"
+
+namespace hsa {
+
+// Kslc[b,c,g,e] = mean_j K[b, c*S+j, g, e]: one thread per output element; the sum runs in
+// fp64 in row order so the result is the exact mean for any bf16/fp32 chunk in practice,
+// rounded once to the storage type.  Consecutive threads read consecutive e (coalesced).
+template <typename T>
+__global__ void __launch_bounds__(256) k_pool(const T* __restrict__ K, T* __restrict__ Kslc,
+                                              int L, int Hkv, int D, int S, int nC,
+                                              size_t total) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  int e = (int)(i % D);
+  size_t r = i / D;
+  int g = (int)(r % Hkv);
+  r /= Hkv;
+  int c = (int)(r % nC);
+  size_t b = r / nC;
+  const T* src = K + ((b * L + (size_t)c * S) * Hkv + g) * D + e;
+  size_t stride = (size_t)Hkv * D;
+  double sum = 0.0;
+  for (int j = 0; j < S; ++j) sum += (double)to_f32(src[j * stride]);
+  Kslc[i] = from_f64<T>(sum / S);
+}
+
+hipError_t launch_pool(const Dims& d, const void* K, void* Kslc, hipStream_t s) {
+  size_t total = (size_t)d.B * d.nC * d.Hkv * d.D;
+  if (total == 0) return hipSuccess;
+  dim3 grid((unsigned)((total + 255) / 256));
+  if (d.dtype == 1)
+    k_pool<bf16><<<grid, 256, 0, s>>>((const bf16*)K, (bf16*)Kslc, d.L, d.Hkv, d.D, d.S, d.nC,
+                                      total);
+  else
+    k_pool<float><<<grid, 256, 0, s>>>((const float*)K, (float*)Kslc, d.L, d.Hkv, d.D, d.S,
+                                       d.nC, total);
+  return hipGetLastError();
+}
+
+// Selection, one wave per (b, t, g) row.  Lane l scores chunks l, l+64, ... with an fp64
+// dot product of the stored values (exact products, sequential sum), keeps a private
+// ranked list, and the wave merges the lists K times by a 64-bit max.  Lane 0 then forms
+// the stick-breaking weights in fp64 and writes the K slots.
+template <typename T>
+__global__ void __launch_bounds__(64) k_select_generic(const T* __restrict__ Qs,
+                                                       const T* __restrict__ Kslc,
+                                                       int32_t* __restrict__ idx,
+                                                       float* __restrict__ score,
+                                                       float* __restrict__ w, int L, int Hkv,
+                                                       int D, int S, int K, int nC,
+                                                       double sel_scale) {
+  __shared__ double qsh[128];
+  __shared__ uint64_t chosen[kMaxK];
+  const int lane = threadIdx.x;
+  const size_t row = blockIdx.x;  // (b*L + t)*Hkv + g
+  const int g = (int)(row % Hkv);
+  const size_t bt = row / Hkv;
+  const int t = (int)(bt % L);
+  const size_t b = bt / L;
+  int n_avail = t / S;
+  if (n_avail > nC) n_avail = nC;
+
+  for (int e = lane; e < D; e += kWave) qsh[e] = (double)to_f32(Qs[row * D + e]);
+  __syncthreads();
+
+  uint64_t top[kMaxK];
+#pragma unroll
+  for (int i = 0; i < kMaxK; ++i) top[i] = 0;
+  for (int c = lane; c < n_avail; c += kWave) {
+    const T* kr = Kslc + ((b * nC + c) * Hkv + g) * D;
+    double dot = 0.0;
+    for (int e = 0; e < D; e += 8) {
+      float kv[8];
+      load8(kr + e, kv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot += qsh[e + i] * (double)kv[i];
+    }
+    float s = (float)(sel_scale * dot);
+    topk_insert(top, rank_key(s, c), K);
+  }
+  for (int k = 0; k < K; ++k) {
+    uint64_t best = wave_max_u64(top[0]);
+    if (best != 0 && top[0] == best) topk_pop(top);
+    if (lane == 0) chosen[k] = best;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    double remaining = 1.0;
+    size_t o = row * K;
+    for (int k = 0; k < K; ++k) {
+      uint64_t key = chosen[k];
+      if (key == 0) {
+        idx[o + k] = -1;
+        score[o + k] = -__builtin_inff();
+        w[o + k] = 0.0f;
+      } else {
+        float s = key_score(key);
+        double p = sigmoid_d((double)s);
+        idx[o + k] = key_chunk(key);
+        score[o + k] = s;
+        w[o + k] = (float)(p * remaining);
+        remaining *= 1.0 - p;
+      }
+    }
+  }
+}
+
+hipError_t launch_select_generic(const Dims& d, const void* Qs, const void* Kslc, int32_t* idx,
+                                 float* score, float* w, hipStream_t s) {
+  size_t rows = (size_t)d.B * d.L * d.Hkv;
+  if (rows == 0) return hipSuccess;
+  if (d.dtype == 1)
+    k_select_generic<bf16><<<dim3((unsigned)rows), 64, 0, s>>>(
+        (const bf16*)Qs, (const bf16*)Kslc, idx, score, w, d.L, d.Hkv, d.D, d.S, d.K, d.nC,
+        d.sel_scale);
+  else
+    k_select_generic<float><<<dim3((unsigned)rows), 64, 0, s>>>(
+        (const float*)Qs, (const float*)Kslc, idx, score, w, d.L, d.Hkv, d.D, d.S, d.K, d.nC,
+        d.sel_scale);
+  return hipGetLastError();
+}
+
+}  // namespace hsa

@@ -1,0 +1,186 @@
+"""Tensor-level Python binding of libhsa.so: argument marshalling only.
+
+Each function checks that its tensors are contiguous device tensors of the expected dtype,
+allocates the outputs (and the workspace, unless one is passed), and calls the C entry
+point of the same name on torch's current stream.  Every step of the computation runs in
+the library's HIP kernels.
+
+Shapes (BSHD, see include/hsa.h):
+    Q, dO, O  [B, L, Hq, D]       K, V, Qs  [B, L, Hkv, D]      Kslc [B, L//64, Hkv, D]
+    idx [B, L, Hkv, K] int32      score, w  [B, L, Hkv, K] fp32
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import Problem, check
+
+S_CHUNK = 64
+_DT = {torch.float32: _lib.HSA_F32, torch.bfloat16: _lib.HSA_BF16}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the operator has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def problem(B, L, Hq, Hkv, D, K, dtype, sm_scale=None, sel_scale=None, generic=False,
+            S=S_CHUNK) -> Problem:
+    if dtype not in _DT:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return Problem(int(B), int(L), int(Hq), int(Hkv), int(D), int(S), int(K),
+                   0.0 if sm_scale is None else float(sm_scale),
+                   0.0 if sel_scale is None else float(sel_scale), _DT[dtype],
+                   _lib.HSA_FLAG_GENERIC if generic else 0)
+
+
+def workspace_size(op: int, prob: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    check(_lib.lib().hsa_workspace_size(int(op), ctypes.byref(prob), ctypes.byref(n)),
+          "hsa_workspace_size")
+    return int(n.value)
+
+
+def workspace(op: int, prob: Problem, device) -> torch.Tensor | None:
+    n = workspace_size(op, prob)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _ws_args(ws):
+    if ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def pool(K: torch.Tensor, K_top: int = 1, generic=False) -> torch.Tensor:
+    """Chunk keys Kslc = mean of each chunk's key rows (hsa_select with Qs = NULL)."""
+    _need(K, "K")
+    B, L, Hkv, D = K.shape
+    prob = problem(B, L, Hkv, Hkv, D, K_top, K.dtype, generic=generic)
+    Kslc = torch.empty((B, L // S_CHUNK, Hkv, D), dtype=K.dtype, device=K.device)
+    ws = workspace(_lib.HSA_OP_SELECT, prob, K.device)
+    wp, wn = _ws_args(ws)
+    check(_lib.lib().hsa_select(ctypes.byref(prob), None, _ptr(K), _ptr(Kslc), None, None, None,
+                                wp, wn, _stream()), "hsa_select")
+    return Kslc
+
+
+def select(Qs: torch.Tensor, K: torch.Tensor, K_top: int, sel_scale=None, generic=False,
+           ws=None):
+    """Pool + top-K selection + stick-breaking weights.  Returns (Kslc, idx, score, w)."""
+    _need(K, "K")
+    B, L, Hkv, D = K.shape
+    _need(Qs, "Qs", K.dtype, (B, L, Hkv, D), K.device)
+    prob = problem(B, L, Hkv, Hkv, D, K_top, K.dtype, sel_scale=sel_scale, generic=generic)
+    dev = K.device
+    Kslc = torch.empty((B, L // S_CHUNK, Hkv, D), dtype=K.dtype, device=dev)
+    idx = torch.empty((B, L, Hkv, K_top), dtype=torch.int32, device=dev)
+    score = torch.empty((B, L, Hkv, K_top), dtype=torch.float32, device=dev)
+    w = torch.empty((B, L, Hkv, K_top), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(_lib.HSA_OP_SELECT, prob, dev)
+    wp, wn = _ws_args(ws)
+    check(_lib.lib().hsa_select(ctypes.byref(prob), _ptr(Qs), _ptr(K), _ptr(Kslc), _ptr(idx),
+                                _ptr(score), _ptr(w), wp, wn, _stream()), "hsa_select")
+    return Kslc, idx, score, w
+
+
+def fwd(Q, K, V, idx, w, sm_scale=None, generic=False, ws=None, out=None):
+    """O = sum_k w_k softmax1-attention of Q over the selected chunks of K/V."""
+    _need(Q, "Q")
+    B, L, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    Kt = idx.shape[-1]
+    _need(K, "K", Q.dtype, (B, L, Hkv, D), Q.device)
+    _need(V, "V", Q.dtype, (B, L, Hkv, D), Q.device)
+    _need(idx, "idx", torch.int32, (B, L, Hkv, Kt), Q.device)
+    _need(w, "w", torch.float32, (B, L, Hkv, Kt), Q.device)
+    prob = problem(B, L, Hq, Hkv, D, Kt, Q.dtype, sm_scale=sm_scale, generic=generic)
+    O = torch.empty_like(Q) if out is None else _need(out, "out", Q.dtype, Q.shape, Q.device)
+    if ws is None:
+        ws = workspace(_lib.HSA_OP_FWD, prob, Q.device)
+    wp, wn = _ws_args(ws)
+    check(_lib.lib().hsa_fwd(ctypes.byref(prob), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(w),
+                             _ptr(O), wp, wn, _stream()), "hsa_fwd")
+    return O
+
+
+def bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, fold=True, want_dkslc=True, sm_scale=None,
+        sel_scale=None, generic=False, ws=None):
+    """Gradients with the selection fixed.  Returns dict(dQ, dK, dV, dQs, dKslc)."""
+    _need(Q, "Q")
+    B, L, Hq, D = Q.shape
+    Hkv = K.shape[2]
+    Kt = idx.shape[-1]
+    dev = Q.device
+    for name, t, h in (("K", K, Hkv), ("V", V, Hkv), ("Qs", Qs, Hkv), ("dO", dO, Hq)):
+        _need(t, name, Q.dtype, (B, L, h, D), dev)
+    _need(Kslc, "Kslc", Q.dtype, (B, L // S_CHUNK, Hkv, D), dev)
+    _need(idx, "idx", torch.int32, (B, L, Hkv, Kt), dev)
+    _need(score, "score", torch.float32, (B, L, Hkv, Kt), dev)
+    _need(w, "w", torch.float32, (B, L, Hkv, Kt), dev)
+    prob = problem(B, L, Hq, Hkv, D, Kt, Q.dtype, sm_scale=sm_scale, sel_scale=sel_scale,
+                   generic=generic)
+    dQ = torch.empty_like(Q)
+    dK = torch.empty_like(K)
+    dV = torch.empty_like(V)
+    dQs = torch.empty_like(Qs)
+    dKslc = (torch.empty((B, L // S_CHUNK, Hkv, D), dtype=torch.float32, device=dev)
+             if want_dkslc else None)
+    if ws is None:
+        ws = workspace(_lib.HSA_OP_BWD, prob, dev)
+    wp, wn = _ws_args(ws)
+    flags = _lib.HSA_BWD_FOLD_KSLC if fold else 0
+    check(_lib.lib().hsa_bwd(ctypes.byref(prob), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qs), _ptr(Kslc),
+                             _ptr(idx), _ptr(score), _ptr(w), _ptr(dO), _ptr(dQ), _ptr(dK),
+                             _ptr(dV), _ptr(dQs), _ptr(dKslc), flags, wp, wn, _stream()),
+          "hsa_bwd")
+    return dict(dQ=dQ, dK=dK, dV=dV, dQs=dQs, dKslc=dKslc)
+
+
+def decode(q, qs, Kc, Vc, Kslc, K_top, sm_scale=None, sel_scale=None, generic=False, ws=None):
+    """One decode step: q [B,Hq,D], qs [B,Hkv,D], caches [B,ctx,Hkv,D], Kslc [B,ctx//64,Hkv,D].
+    Returns (O [B,Hq,D], idx, score, w [B,Hkv,K])."""
+    _need(Kc, "Kcache")
+    B, ctx, Hkv, D = Kc.shape
+    dev = Kc.device
+    Hq = q.shape[1]
+    _need(q, "q", Kc.dtype, (B, Hq, D), dev)
+    _need(qs, "qs", Kc.dtype, (B, Hkv, D), dev)
+    _need(Vc, "Vcache", Kc.dtype, (B, ctx, Hkv, D), dev)
+    _need(Kslc, "Kslc", Kc.dtype, (B, ctx // S_CHUNK, Hkv, D), dev)
+    prob = problem(B, ctx, Hq, Hkv, D, K_top, Kc.dtype, sm_scale=sm_scale, sel_scale=sel_scale,
+                   generic=generic)
+    O = torch.empty((B, Hq, D), dtype=Kc.dtype, device=dev)
+    idx = torch.empty((B, Hkv, K_top), dtype=torch.int32, device=dev)
+    score = torch.empty((B, Hkv, K_top), dtype=torch.float32, device=dev)
+    w = torch.empty((B, Hkv, K_top), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(_lib.HSA_OP_DECODE, prob, dev)
+    wp, wn = _ws_args(ws)
+    check(_lib.lib().hsa_decode(ctypes.byref(prob), _ptr(q), _ptr(qs), _ptr(Kc), _ptr(Vc),
+                                _ptr(Kslc), _ptr(O), _ptr(idx), _ptr(score), _ptr(w), wp, wn,
+                                _stream()), "hsa_decode")
+    return O, idx, score, w

@@ -1,0 +1,165 @@
+/*
+ * hsa.h -- C ABI of libhsa.so, Hierarchical Sparse Attention (HSA) on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (from "Hardware-aligned Hierarchical Sparse Attention for Efficient
+ * Long-term Memory Access", papernotes.org note, section 方法详解 › 层次化稀疏注意力（HSA）,
+ * and the atlas.scime.ai summary of the same paper, section "Approach"):
+ *   1. Chunk selection: the sequence is cut into chunks of S tokens; every chunk is keyed by
+ *      the mean of its key rows; every token scores each earlier chunk with its own selection
+ *      query and keeps the top-K chunks, separately for each query group (KV head).
+ *   2. Token level: inside each selected chunk, ordinary attention of the token's query over
+ *      the chunk's S keys, normalised with softmax-off-by-one (note section 硬件对齐 Kernel).
+ *   3. Chunk level: the K per-chunk outputs are fused with stick-breaking weights computed
+ *      from the sigmoid of the selection scores, with no positional term.
+ *   The backward runs in two phases (note section 硬件对齐 Kernel): per token the query and
+ *   chunk-weight gradients, then per chunk the key and value gradients over every token that
+ *   selected it.  The gradient also flows through the weights into the selection scores.
+ *   Decode (note section 训练与推理优化, KV Cache Offloading): one new token per sequence is
+ *   scored against the resident chunk-key table and reads only the selected chunks' K/V.
+ *
+ * Definitions used where the pages are silent (the numbers refer to no page):
+ *   nC        = floor(L / S) complete chunks; a trailing partial chunk is never selectable.
+ *   Kslc      [b,c,g,:] = mean_{j<S} K[b, c*S+j, g, :], summed in fp64 in row order and
+ *             rounded once (nearest, ties to even) to the storage dtype.
+ *   score     s = sel_scale * <Qs[b,t,g,:], Kslc[b,c,g,:]>, for c < min(floor(t/S), nC),
+ *             taken in fp32; NaN counts as -inf.
+ *   ranking   score descending, ties to the lower chunk index; slots past the number of
+ *             candidates are masked: idx -1, score -inf, w 0.
+ *   weights   w_k = sigmoid(s_k) * prod_{j<k} (1 - sigmoid(s_j)) over the valid slots.
+ *   attention z_j = sm_scale * <Q[b,t,h,:], K[b,c*S+j,g,:]>,
+ *             a_j = exp(z_j) / (1 + sum_i exp(z_i)), O_{t,h,k} = sum_j a_j V[b,c*S+j,g,:],
+ *             O[b,t,h,:] = sum_k w_k O_{t,h,k} (0 when no slot is valid).
+ *   groups    query head h belongs to KV group g = floor(h / (Hq/Hkv)).
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers to dense row-major arrays in the layouts given
+ *     below ("BSHD": [batch, token, head, dim]), 16-byte aligned.  Inputs are read only.
+ *   - The caller owns all memory.  The library never allocates, frees or synchronises;
+ *     scratch memory comes from the caller's workspace `ws` of at least
+ *     hsa_workspace_size() bytes (256-byte aligned; may be NULL when that size is 0).
+ *   - Outputs are fully overwritten, never accumulated.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns without waiting.  Asynchronous faults surface at the caller's next sync.
+ *   - Arguments are validated before anything is enqueued; on a nonzero status nothing was
+ *     launched and nothing was written.  hsa_last_error() then describes the problem.
+ *   - Calls are reentrant; concurrent calls must use distinct workspaces.
+ *
+ * Supported envelope: S = 64; D in {64, 128}; 1 <= K <= 16; Hq % Hkv == 0 with
+ * 1 <= Hq/Hkv <= 16; dtype fp32 or bf16; L*K < 2^31.  Anything else returns
+ * HSA_ERR_UNSUPPORTED.
+ */
+#ifndef HSA_H_
+#define HSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSA_OK = 0,
+  HSA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, non-positive size, bad scale */
+  HSA_ERR_UNSUPPORTED = 2, /* outside the supported envelope above */
+  HSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than hsa_workspace_size() */
+  HSA_ERR_HIP = 4          /* a HIP launch failed; see hsa_last_error() */
+} hsa_status_t;
+
+typedef enum { HSA_F32 = 0, HSA_BF16 = 1 } hsa_dtype_t;
+
+typedef enum { HSA_OP_SELECT = 0, HSA_OP_FWD = 1, HSA_OP_BWD = 2, HSA_OP_DECODE = 3 } hsa_op_t;
+
+/* hsa_problem_t.flags */
+#define HSA_FLAG_GENERIC 0x1u /* use the plain vector-ALU kernels even where MFMA kernels exist */
+
+/* hsa_bwd flags */
+#define HSA_BWD_FOLD_KSLC 0x1u /* add dKslc/S into every key row of the chunk (Kslc = mean K) */
+
+typedef struct hsa_problem {
+  int32_t B;        /* batch (decode: number of sequences) */
+  int32_t L;        /* tokens per sequence (decode: context length already cached) */
+  int32_t Hq;       /* query heads */
+  int32_t Hkv;      /* KV heads = query groups */
+  int32_t D;        /* head dimension */
+  int32_t S;        /* chunk size */
+  int32_t K;        /* chunks kept per (token, group) */
+  float sm_scale;   /* token-level logit scale; 0 => 1/sqrt(D) (taken in double) */
+  float sel_scale;  /* selection score scale; 0 => 1/sqrt(D) (taken in double) */
+  int32_t dtype;    /* hsa_dtype_t of Q, K, V, Qs, Kslc, dO and of O and the gradients */
+  uint32_t flags;   /* HSA_FLAG_* */
+} hsa_problem_t;
+
+typedef void* hsa_stream_t; /* hipStream_t */
+
+/* Human-readable name of a status code (static string). */
+const char* hsa_status_string(hsa_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* hsa_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* hsa_version(void);
+
+/* Workspace bytes the entry point `op` (hsa_op_t) needs for problem *p.  Writes *bytes;
+ * returns the same validation status the entry point itself would. */
+hsa_status_t hsa_workspace_size(int op, const hsa_problem_t* p, size_t* bytes);
+
+/* Chunk-key pooling and top-K selection with stick-breaking weights
+ * (note section 层次化稀疏注意力（HSA）: Chunk Selection and 第二阶段).
+ *   Qs    [B, L, Hkv, D] dtype  selection queries; NULL => pool only
+ *   K     [B, L, Hkv, D] dtype  keys
+ *   Kslc  [B, nC, Hkv, D] dtype out: chunk keys (mean of each chunk's key rows)
+ *   idx   [B, L, Hkv, K] int32 out: selected chunks in rank order, -1 = masked
+ *   score [B, L, Hkv, K] fp32  out: their scores, -inf = masked
+ *   w     [B, L, Hkv, K] fp32  out: stick-breaking weights, 0 = masked
+ * With Qs == NULL only Kslc is written and idx/score/w may be NULL (used to build the
+ * resident chunk table for decode); otherwise all must be non-NULL. */
+hsa_status_t hsa_select(const hsa_problem_t* p, const void* Qs, const void* K, void* Kslc,
+                        int32_t* idx, float* score, float* w, void* ws, size_t ws_bytes,
+                        hsa_stream_t stream);
+
+/* Token-level softmax-off-by-one attention inside the selected chunks, fused with the
+ * chunk weights (note sections 层次化稀疏注意力（HSA） 第一阶段/第二阶段 and 硬件对齐 Kernel).
+ *   Q   [B, L, Hq, D] dtype;  K, V [B, L, Hkv, D] dtype
+ *   idx [B, L, Hkv, K] int32 and w [B, L, Hkv, K] fp32 as written by hsa_select (any valid
+ *       selection works: valid slots first, each chunk < min(floor(t/S), nC), -1 after)
+ *   O   [B, L, Hq, D] dtype out */
+hsa_status_t hsa_fwd(const hsa_problem_t* p, const void* Q, const void* K, const void* V,
+                     const int32_t* idx, const float* w, void* O, void* ws, size_t ws_bytes,
+                     hsa_stream_t stream);
+
+/* Backward of hsa_select's scores/weights and hsa_fwd with the selection held fixed
+ * (note section 硬件对齐 Kernel: two phases; section 层次化稀疏注意力（HSA）: end-to-end
+ * gradients through the chunk weights).  Inputs as in hsa_select / hsa_fwd plus
+ *   Kslc [B, nC, Hkv, D] dtype (the chunk keys the scores were computed from)
+ *   dO   [B, L, Hq, D] dtype  upstream gradient of O
+ * Outputs (all fully written):
+ *   dQ [B, L, Hq, D], dK, dV, dQs [B, L, Hkv, D] dtype
+ *   dKslc [B, nC, Hkv, D] fp32, gradient with respect to Kslc (may be NULL)
+ * flags: HSA_BWD_FOLD_KSLC adds dKslc[c]/S to dK of every row of chunk c, which is the
+ * complete key gradient when Kslc was pooled from K. */
+hsa_status_t hsa_bwd(const hsa_problem_t* p, const void* Q, const void* K, const void* V,
+                     const void* Qs, const void* Kslc, const int32_t* idx, const float* score,
+                     const float* w, const void* dO, void* dQ, void* dK, void* dV, void* dQs,
+                     float* dKslc, uint32_t flags, void* ws, size_t ws_bytes,
+                     hsa_stream_t stream);
+
+/* One decode step for B sequences with L = ctx tokens already cached (note section
+ * 训练与推理优化: only the chunk-key table is scanned; only the selected chunks' K/V are read).
+ * The new token sits at position ctx and may select chunks c < floor(ctx/S).
+ *   q  [B, Hq, D] dtype;  qs [B, Hkv, D] dtype
+ *   Kcache, Vcache [B, ctx, Hkv, D] dtype;  Kslc [B, floor(ctx/S), Hkv, D] dtype
+ *   O  [B, Hq, D] dtype out;  idx [B, Hkv, K] int32 out;  w [B, Hkv, K] fp32 out;
+ *   score [B, Hkv, K] fp32 out (may be NULL) */
+hsa_status_t hsa_decode(const hsa_problem_t* p, const void* q, const void* qs,
+                        const void* Kcache, const void* Vcache, const void* Kslc, void* O,
+                        int32_t* idx, float* score, float* w, void* ws, size_t ws_bytes,
+                        hsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSA_H_ */

@@ -1,0 +1,268 @@
+"""GPU parity: libhsa.so (through its C ABI) against the CPU oracle on seeded inputs.
+
+Small cases compare every output element; the full-size workloads compare sampled rows and
+chunks the oracle computes one by one.  Tolerances: selection indices bit-exact outside
+near-tie rows (see hsa_compare), scores and weights 1e-5, outputs and gradients max-abs 2e-2
+for bf16 and 1e-4 for fp32.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from hsa_compare import check_selection, max_abs, near_tie_rows, tol_for
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.Workload
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def hsa():
+    import chunk_sparse_attention_amd as m
+    return m
+
+
+def npy(t):
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy().astype(np.float64) if t.is_floating_point() else t.cpu().numpy()
+
+
+def head_mask(row_mask_bLg, G):
+    """[B, L, Hkv] -> [B, L, Hkv*G] (query head h belongs to group h // G)."""
+    return np.repeat(row_mask_bLg, G, axis=2)
+
+
+def gpu_forward(hsa, x, wl, dev, generic=False):
+    Q, K, V, Qs = (x[k].to(dev) for k in ("Q", "K", "V", "Qs"))
+    Kslc, idx, score, w = hsa.select(Qs, K, wl.K, generic=generic)
+    O = hsa.fwd(Q, K, V, idx, w, generic=generic)
+    return dict(Q=Q, K=K, V=V, Qs=Qs, Kslc=Kslc, idx=idx, score=score, w=w, O=O)
+
+
+def compare_forward(orc, x, wl, g, row_mask=None):
+    f = orc.forward(x["Q"], x["K"], x["V"], x["Qs"], wl.S, wl.K, row_mask=row_mask)
+    near = near_tie_rows(orc, x["Qs"], f["Kslc"], wl.S, wl.K, row_mask=row_mask)
+    assert np.array_equal(npy(g["Kslc"]), f["Kslc"]), "pooled chunk keys differ"
+    gpu = dict(idx=npy(g["idx"]), score=npy(g["score"]), w=npy(g["w"]))
+    diff, rep = check_selection(gpu, f, near, x["Qs"], f["Kslc"], wl.S, 1.0 / np.sqrt(wl.D),
+                                row_mask)
+    rows = np.ones(diff.shape, bool) if row_mask is None else np.broadcast_to(
+        np.asarray(row_mask, bool).reshape(wl.B, wl.L, 1), diff.shape)
+    keep = head_mask(rows & ~diff, wl.G)
+    err = max_abs(npy(g["O"]), f["O"], keep)
+    rep["O_max_abs"] = err
+    say("forward", wl.name, rep)
+    assert err <= tol_for(wl.dtype), err
+    return f, diff, rep
+
+
+def compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=None, chunk_mask=None):
+    o = orc.backward(x["Q"], x["K"], x["V"], x["Qs"], f["Kslc"], f["idx"], f["score"], f["w"],
+                     x["dO"], wl.S, tok_mask=tok_mask, chunk_mask=chunk_mask)
+    tol = tol_for(wl.dtype)
+    B, L, nC = wl.B, wl.L, wl.nC
+    tm = np.ones((B, L), bool) if tok_mask is None else np.asarray(tok_mask, bool).reshape(B, L)
+    cm = np.ones((B, nC), bool) if chunk_mask is None else np.asarray(chunk_mask, bool).reshape(B, nC)
+    # chunks whose selector sets differ between the two sides are not comparable
+    touched = np.zeros((B, nC), bool)
+    for (b, t, gg) in np.argwhere(diff):
+        for arr in (npy(g["idx"])[b, t, gg], f["idx"][b, t, gg]):
+            for c in arr:
+                if c >= 0:
+                    touched[b, c] = True
+    trow = tm[:, :, None] & ~diff  # [B, L, Hkv]
+    rep = {}
+    rep["dQ"] = max_abs(npy(grads["dQ"]), o["dQ"], head_mask(trow, wl.G))
+    rep["dQs"] = max_abs(npy(grads["dQs"]), o["dQs"], trow)
+    crow = np.repeat(cm & ~touched, wl.S, axis=1)  # [B, nC*S]
+    crow = np.concatenate([crow, np.zeros((B, L - nC * wl.S), bool)], axis=1)[:, :, None]
+    crow = np.broadcast_to(crow, (B, L, wl.Hkv))
+    rep["dK"] = max_abs(npy(grads["dK"]), o["dK"], crow)
+    rep["dV"] = max_abs(npy(grads["dV"]), o["dV"], crow)
+    ck = np.broadcast_to((cm & ~touched)[:, :, None], (B, nC, wl.Hkv))
+    rep["dKslc"] = max_abs(npy(grads["dKslc"]), o["dKslc"], ck)
+    if chunk_mask is None:  # the incomplete tail chunk's rows must be exactly zero
+        assert np.all(npy(grads["dK"])[:, nC * wl.S:] == 0)
+        assert np.all(npy(grads["dV"])[:, nC * wl.S:] == 0)
+    rep["touched_chunks"] = int(touched.sum())
+    say("backward", wl.name, rep)
+    for k in ("dQ", "dQs", "dK", "dV", "dKslc"):
+        assert rep[k] <= tol, (k, rep[k])
+    return rep
+
+
+SMALL = [
+    W("tiny_fp32", 1, 1024, 4, 1, 64, 64, 4, torch.float32, 1.0, 1.0),
+    W("bf16_d64_ragged", 2, 64 * 24 + 37, 16, 2, 64, 64, 8, torch.bfloat16),
+    W("bf16_d128_ragged", 1, 64 * 20 + 5, 16, 2, 128, 64, 8, torch.bfloat16),
+    W("bf16_g1_k3", 1, 64 * 10, 8, 8, 64, 64, 3, torch.bfloat16),
+    W("bf16_g16_k16", 1, 64 * 21, 16, 1, 128, 64, 16, torch.bfloat16),
+    W("fp32_k1", 2, 64 * 9 + 1, 4, 2, 64, 64, 1, torch.float32, 1.0, 1.0),
+    W("bf16_no_chunk", 1, 50, 8, 2, 64, 64, 4, torch.bfloat16),
+    W("planted_d128", 1, 64 * 100, 16, 2, 128, 64, 8, torch.bfloat16, planted=True),
+]
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_small_end_to_end(hsa, dev, wl, generic):
+    say("case", wl, "generic" if generic else "default")
+    orc = oracle.get()
+    x = workloads.make_inputs(wl, seed=0)
+    g = gpu_forward(hsa, x, wl, dev, generic)
+    grads = hsa.bwd(g["Q"], g["K"], g["V"], g["Qs"], g["Kslc"], g["idx"], g["score"], g["w"],
+                    x["dO"].to(dev), generic=generic)
+    torch.cuda.synchronize()
+    f, diff, _ = compare_forward(orc, x, wl, g)
+    compare_backward(orc, x, wl, g, f, diff, grads)
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
+@pytest.mark.parametrize("wl", SMALL[1:4], ids=lambda w: w.name)
+def test_given_selection(hsa, dev, wl, generic):
+    """Attention and backward with one random valid selection given to both sides."""
+    say("case", wl, "given selection", generic)
+    orc = oracle.get()
+    x = workloads.make_inputs(wl, seed=3)
+    sel = workloads.make_selection(wl.B, wl.L, wl.Hkv, wl.S, wl.K, seed=4)
+    Q, K, V, Qs, dO = (x[k].to(dev) for k in ("Q", "K", "V", "Qs", "dO"))
+    idx, score, w = (sel[k].to(dev) for k in ("idx", "score", "w"))
+    Kslc = hsa.pool(K)
+    O = hsa.fwd(Q, K, V, idx, w, generic=generic)
+    grads = hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, generic=generic)
+    torch.cuda.synchronize()
+    ks = orc.pool(x["K"], wl.S)
+    Oo = orc.attend(x["Q"], x["K"], x["V"], sel["idx"], sel["w"], wl.S)
+    tol = tol_for(wl.dtype)
+    assert max_abs(npy(O), Oo) <= tol
+    o = orc.backward(x["Q"], x["K"], x["V"], x["Qs"], ks, sel["idx"], sel["score"], sel["w"],
+                     x["dO"], wl.S)
+    rep = {k: max_abs(npy(grads[k]), o[k]) for k in ("dQ", "dK", "dV", "dQs", "dKslc")}
+    say("given-selection", wl.name, rep)
+    for k, v in rep.items():
+        assert v <= tol, (k, v)
+
+
+def test_backward_bitwise_reproducible(hsa, dev):
+    wl = SMALL[1]
+    x = workloads.make_inputs(wl, seed=5)
+    g = gpu_forward(hsa, x, wl, dev)
+    dO = x["dO"].to(dev)
+    a = hsa.bwd(g["Q"], g["K"], g["V"], g["Qs"], g["Kslc"], g["idx"], g["score"], g["w"], dO)
+    b = hsa.bwd(g["Q"], g["K"], g["V"], g["Qs"], g["Kslc"], g["idx"], g["score"], g["w"], dO)
+    torch.cuda.synchronize()
+    for k in ("dQ", "dK", "dV", "dQs", "dKslc"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_fold_flag(hsa, dev):
+    """Without HSA_BWD_FOLD_KSLC, dK lacks exactly dKslc/S on every row of each chunk."""
+    wl = SMALL[5]
+    x = workloads.make_inputs(wl, seed=6)
+    g = gpu_forward(hsa, x, wl, dev)
+    dO = x["dO"].to(dev)
+    a = hsa.bwd(g["Q"], g["K"], g["V"], g["Qs"], g["Kslc"], g["idx"], g["score"], g["w"], dO)
+    b = hsa.bwd(g["Q"], g["K"], g["V"], g["Qs"], g["Kslc"], g["idx"], g["score"], g["w"], dO,
+                fold=False)
+    torch.cuda.synchronize()
+    nC = wl.nC
+    fold = a["dKslc"].repeat_interleave(64, dim=1) / 64
+    d = (a["dK"][:, :nC * 64] - b["dK"][:, :nC * 64]).double()
+    assert (d - fold.double()).abs().max().item() <= 1e-5
+    assert torch.equal(a["dV"], b["dV"]) and torch.equal(a["dQ"], b["dQ"])
+
+
+@pytest.mark.parametrize("ctx", [40, 64, 64 * 7 + 13, 64 * 33])
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
+def test_decode_small(hsa, dev, ctx, generic):
+    wl = W("decode_small", 3, ctx, 16, 2, 64, 64, 8, torch.bfloat16)
+    say("case decode", ctx, generic)
+    x = workloads.make_decode_inputs(wl, seed=7, ctx=ctx)
+    q, qs, Kc, Vc = (x[k].to(dev) for k in ("q", "qs", "Kc", "Vc"))
+    Kslc = hsa.pool(Kc)
+    O, idx, score, w = hsa.decode(q, qs, Kc, Vc, Kslc, wl.K, generic=generic)
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    ks = orc.pool(x["Kc"], 64)
+    assert np.array_equal(npy(Kslc), ks)
+    d = orc.decode(x["q"], x["qs"], x["Kc"], x["Vc"], ks, 64, wl.K)
+    assert np.array_equal(npy(idx), d["idx"])
+    assert max_abs(npy(w), d["w"]) <= 1e-5
+    assert max_abs(npy(O), d["O"]) <= 2e-2
+
+
+# ---- full-size workloads, sampled --------------------------------------------------------
+
+def _sample_rows(wl, n, seed):
+    rng = np.random.default_rng(seed)
+    m = np.zeros((wl.B, wl.L), np.uint8)
+    for b in range(wl.B):
+        ts = rng.choice(wl.L, size=min(n, wl.L), replace=False)
+        m[b, ts] = 1
+        m[b, [0, wl.S - 1, wl.S, 2 * wl.S - 1, wl.L - 1]] = 1  # boundaries
+    return m
+
+
+@pytest.mark.parametrize("name", ["fwd_16k", "fwd_64k"])
+def test_full_forward_sampled(hsa, dev, name):
+    wl = workloads.WORKLOADS[name]
+    say("case full forward", name)
+    x = workloads.make_inputs(wl, seed=0, with_grad=False)
+    g = gpu_forward(hsa, x, wl, dev)
+    torch.cuda.synchronize()
+    mask = _sample_rows(wl, 384, seed=1)
+    compare_forward(oracle.get(), x, wl, g, row_mask=mask)
+
+
+def test_full_backward_sampled(hsa, dev):
+    wl = workloads.WORKLOADS["bwd_16k"]
+    say("case full backward bwd_16k")
+    x = workloads.make_inputs(wl, seed=0)
+    g = gpu_forward(hsa, x, wl, dev)
+    grads = hsa.bwd(g["Q"], g["K"], g["V"], g["Qs"], g["Kslc"], g["idx"], g["score"], g["w"],
+                    x["dO"].to(dev))
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    f, diff, _ = compare_forward(orc, x, wl, g)  # full oracle selection (needed for phase 2)
+    tm = _sample_rows(wl, 48, seed=2)
+    rng = np.random.default_rng(3)
+    cm = np.zeros((wl.B, wl.nC), np.uint8)
+    for b in range(wl.B):
+        cm[b, rng.choice(wl.nC, size=6, replace=False)] = 1
+        cm[b, [0, 1, wl.nC - 2, wl.nC - 1]] = 1
+    compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=tm, chunk_mask=cm)
+
+
+def test_full_decode(hsa, dev):
+    wl = workloads.WORKLOADS["decode_1m"]
+    say("case full decode decode_1m")
+    x = workloads.make_decode_inputs(wl, seed=0, slab=1)
+    q, qs = x["q"].to(dev), x["qs"].to(dev)
+    Kc, Vc = x["Kc"].to(dev), x["Vc"].to(dev)
+    Kslc = hsa.pool(Kc)
+    O, idx, score, w = hsa.decode(q, qs, Kc, Vc, Kslc, wl.K)
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    ks = orc.pool(x["Kc"], 64)
+    assert np.array_equal(npy(Kslc), ks)
+    d = orc.decode(x["q"], x["qs"], x["Kc"], x["Vc"], ks, 64, wl.K)
+    say("decode idx equal:", bool(np.array_equal(npy(idx), d["idx"])))
+    assert np.array_equal(npy(idx), d["idx"])
+    assert max_abs(npy(w), d["w"]) <= 1e-5
+    assert max_abs(npy(O), d["O"]) <= 2e-2
