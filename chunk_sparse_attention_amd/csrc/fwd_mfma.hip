@@ -1,0 +1,236 @@
+// fwd_mfma.hip -- bf16 forward on the matrix cores (gfx950).
+//
+// Token-level softmax-off-by-one attention inside each selected chunk fused with the
+// stick-breaking chunk weights ("Hardware-aligned Hierarchical Sparse Attention ...",
+// papernotes.org note, 方法详解 › 层次化稀疏注意力（HSA） 第一阶段/第二阶段, 硬件对齐 Kernel).
+//
+// One workgroup owns a tile of TT consecutive tokens of one (batch, group) and keeps their
+// fp32 outputs in LDS.  The tile's (token, slot) edges are sorted by chunk; each wave takes a
+// contiguous range of 16-column jobs (16/G tokens of one chunk, G heads each), holds that
+// chunk's key and transposed value operands in registers while its jobs share the chunk, and
+// per job computes
+//   S^T = K_c Q^T            (keys x columns, MFMA)
+//   P   = w * softmax1(S)    (per column, fp32, exp2 with the logit scale folded in)
+//   O^T += V_c^T P^T         (MFMA), added into the tile's LDS accumulators.
+// The LDS additions are atomic; their order between waves is not fixed, so O can differ
+// from run to run in the last fp32 bits before the bf16 rounding.
+#include "hsa_common.h"
+#include "hsa_launch.h"
+#include "mfma_common.h"
+#include "tile_common.h"
+
+namespace hsa {
+
+// Vt[((b*Hkv+g)*nC + c)*D*64 + d*64 + p] = V[b, 64c + perm_key(p), g, d]: each chunk's values
+// transposed, keys in the order the P.V contraction consumes them.
+__global__ void __launch_bounds__(256) k_prep_vt(const bf16* __restrict__ V, bf16* __restrict__ Vt,
+                                                 int L, int Hkv, int D, int nC) {
+  __shared__ uint16_t tile[64][129];
+  const int c = blockIdx.x % nC;
+  const int bg = blockIdx.x / nC;
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const bf16* src = V + ((b * L + (size_t)c * 64) * Hkv + g) * D;
+  for (int i = threadIdx.x; i < 64 * D; i += 256) {
+    int key = i / D, d = i % D;
+    tile[key][d] = src[(size_t)key * Hkv * D + d].bits;
+  }
+  __syncthreads();
+  bf16* dst = Vt + ((size_t)bg * nC + c) * D * 64;
+  for (int i = threadIdx.x; i < 64 * D; i += 256) {
+    int d = i / 64, p = i % 64;
+    dst[i].bits = tile[perm_key(p / 32, (p / 8) % 4, p % 8)][d];
+  }
+}
+
+template <int D, int TT, int G>
+__global__ void __launch_bounds__(512) k_fwd_tile(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
+    const int32_t* __restrict__ idx, const float* __restrict__ w, bf16* __restrict__ O, int L,
+    int Hq, int Hkv, int Kt, int nC, int BG, float c2) {
+  constexpr int NT = 512, NW = NT / 64;
+  constexpr int TPJ = 16 / G;  // tokens per 16-column job
+  constexpr int DP = D + 1;    // padded accumulator row
+  constexpr int KS = D / 32;   // k-steps of S^T
+  constexpr int DT = D / 16;   // d-tiles of O^T
+  constexpr int NMAX = TT * 16;
+  __shared__ float acc[TT * G * DP];
+  __shared__ uint32_t keys[NMAX];
+  __shared__ uint32_t jobs[NMAX];
+  __shared__ int scratch[3 * NMAX];
+  __shared__ float wsh[TT * 16];
+  __shared__ int n_valid_sh, n_jobs_sh;
+
+  const int bg = blockIdx.x % BG;  // consecutive blocks: different (b, g), XCD-interleaved
+  const int tile = blockIdx.x / BG;
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const int t0 = tile * TT;
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+
+  // 1. edges of the tile, weights, zeroed accumulators
+  int N = 1;
+  while (N < TT * Kt) N <<= 1;
+  for (int i = tid; i < N; i += NT) {
+    uint32_t key = kNoEdge;
+    if (i < TT * Kt) {
+      const int tl = i / Kt, k = i % Kt, t = t0 + tl;
+      if (t < L) {
+        const size_t o = ((b * L + t) * Hkv + g) * Kt + k;
+        const int c = idx[o];
+        if (c >= 0 && c < nC) {
+          key = edge_key(c, tl, k);
+          wsh[tl * 16 + k] = w[o];
+        }
+      }
+    }
+    keys[i] = key;
+  }
+  for (int i = tid; i < TT * G * DP; i += NT) acc[i] = 0.0f;
+  __syncthreads();
+
+  // 2. group by chunk, 3. jobs
+  block_bitonic_sort<NT>(keys, N);
+  build_jobs<NT>(keys, N, TPJ, scratch, scratch + NMAX, jobs, &n_valid_sh, &n_jobs_sh);
+  const int n_jobs = n_jobs_sh;
+
+  // 4. jobs, a contiguous range per wave
+  const int j0 = (int)((long)n_jobs * wave / NW);
+  const int j1 = (int)((long)n_jobs * (wave + 1) / NW);
+  const int col = lane % 16, blk = lane / 16;
+  const int slot = col / G, head = col % G;
+  bf16x8 ka[4][KS];   // K_c rows (A operand of S^T)
+  bf16x8 va[DT][2];   // V_c^T rows (A operand of O^T)
+  int cur = -1;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t job = jobs[j];
+    const int e0 = (int)(job & 0xffff), cnt = (int)(job >> 16);
+    const int c = edge_chunk(keys[e0]);
+    if (c != cur) {
+      cur = c;
+      const bf16* kc = K + ((b * L + (size_t)c * 64) * Hkv + g) * D;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          ka[kt][ks] = ld_bf16x8(kc + (size_t)(16 * kt + col) * Hkv * D + 32 * ks + 8 * blk);
+      const bf16* vt = Vt + ((size_t)bg * nC + c) * D * 64;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          va[dt][s] = ld_bf16x8(vt + (size_t)(16 * dt + col) * 64 + 32 * s + 8 * blk);
+    }
+    const bool valid = slot < cnt;
+    const uint32_t ek = valid ? keys[e0 + slot] : 0u;
+    const int tl = edge_token(ek), k = edge_slot(ek);
+    const bf16* qrow = Q + ((b * L + t0 + tl) * Hq + (size_t)g * G + head) * D;
+    bf16x8 qb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = valid ? ld_bf16x8(qrow + 32 * ks + 8 * blk) : zero_bf16x8();
+    f32x4 s_acc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s_acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s_acc[kt] = mfma_16x16x32(ka[kt][ks], qb[ks], s_acc[kt]);
+    }
+    // softmax-off-by-one over the 64 keys of this column (4 lanes x 16 values)
+    float m = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s_acc[kt][i] *= c2;
+        m = fmaxf(m, s_acc[kt][i]);
+      }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    float sum = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s_acc[kt][i] = exp2_fast(s_acc[kt][i] - m);
+        sum += s_acc[kt][i];
+      }
+    sum += __shfl_xor(sum, 16, 64);
+    sum += __shfl_xor(sum, 32, 64);
+    const float f = valid ? wsh[tl * 16 + k] / (exp2_fast(-m) + sum) : 0.0f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) pb[s] = pack_bf16x8(s_acc[2 * s] * f, s_acc[2 * s + 1] * f);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      o = mfma_16x16x32(va[dt][0], pb[0], o);
+      o = mfma_16x16x32(va[dt][1], pb[1], o);
+      if (valid) {
+        float* dst = acc + (tl * G + head) * DP + 16 * dt + 4 * blk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) atomicAdd(dst + i, o[i]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 5. outputs (rows past L skipped; tokens with no chunk stay 0)
+  for (int i = tid; i < TT * G * D / 8; i += NT) {
+    const int e = i * 8;
+    const int tl = e / (G * D), h = (e / D) % G, d = e % D;
+    const int t = t0 + tl;
+    if (t >= L) continue;
+    const float* src = acc + (tl * G + h) * DP + d;
+    f32x4 lo = {src[0], src[1], src[2], src[3]};
+    f32x4 hi = {src[4], src[5], src[6], src[7]};
+    *reinterpret_cast<bf16x8*>(O + ((b * L + t) * Hq + (size_t)g * G + h) * D + d) = pack_bf16x8(lo, hi);
+  }
+}
+
+template <int D, int TT, int G>
+static void launch_fwd_tile(const Dims& d, const void* Q, const void* K, const void* Vt,
+                            const int32_t* idx, const float* w, void* O, hipStream_t s) {
+  const int BG = d.B * d.Hkv;
+  const int n_tiles = (d.L + TT - 1) / TT;
+  const float c2 = (float)(d.sm_scale * 1.4426950408889634);  // logit scale * log2(e)
+  k_fwd_tile<D, TT, G><<<dim3(BG * n_tiles), 512, 0, s>>>(
+      (const bf16*)Q, (const bf16*)K, (const bf16*)Vt, idx, w, (bf16*)O, d.L, d.Hq, d.Hkv, d.K,
+      d.nC, BG, c2);
+}
+
+template <int D, int TT>
+static bool launch_fwd_tile_g(const Dims& d, const void* Q, const void* K, const void* Vt,
+                              const int32_t* idx, const float* w, void* O, hipStream_t s) {
+  switch (d.G) {
+    case 1: launch_fwd_tile<D, TT, 1>(d, Q, K, Vt, idx, w, O, s); return true;
+    case 2: launch_fwd_tile<D, TT, 2>(d, Q, K, Vt, idx, w, O, s); return true;
+    case 4: launch_fwd_tile<D, TT, 4>(d, Q, K, Vt, idx, w, O, s); return true;
+    case 8: launch_fwd_tile<D, TT, 8>(d, Q, K, Vt, idx, w, O, s); return true;
+    case 16: launch_fwd_tile<D, TT / 2, 16>(d, Q, K, Vt, idx, w, O, s); return true;
+  }
+  return false;
+}
+
+bool fwd_mfma_supported(const Dims& d) {
+  return d.dtype == 1 && (d.D == 64 || d.D == 128) &&
+         (d.G == 1 || d.G == 2 || d.G == 4 || d.G == 8 || d.G == 16) && d.nC < 32768 &&
+         !(d.flags & 1u);
+}
+
+size_t fwd_mfma_ws(const Dims& d) {
+  return ((size_t)d.B * d.Hkv * d.nC * 64 * d.D * sizeof(uint16_t) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,
+                           const int32_t* idx, const float* w, void* O, char* ws, hipStream_t s) {
+  const int BG = d.B * d.Hkv;
+  if (d.nC > 0)
+    k_prep_vt<<<dim3(BG * d.nC), 256, 0, s>>>((const bf16*)V, (bf16*)ws, d.L, d.Hkv, d.D, d.nC);
+  if (d.D == 64)
+    launch_fwd_tile_g<64, 64>(d, Q, K, ws, idx, w, O, s);
+  else
+    launch_fwd_tile_g<128, 32>(d, Q, K, ws, idx, w, O, s);
+  return hipGetLastError();
+}
+
+}  // namespace hsa

@@ -97,6 +97,8 @@ size_t ws_bytes_for(int op, const hsa::Dims& d) {
       return hsa::bwd_layout(d).total;
     case HSA_OP_DECODE:
       return hsa::dec_layout(d).total;
+    case HSA_OP_FWD:
+      return hsa::fwd_mfma_supported(d) ? hsa::fwd_mfma_ws(d) : 0;
     default:
       return 0;
   }
@@ -199,6 +201,8 @@ HSA_EXPORT hsa_status_t hsa_fwd(const hsa_problem_t* p, const void* Q, const voi
   TRY(check_ws(HSA_OP_FWD, d, ws, ws_bytes));
   TRY(check_pending());
   hipStream_t s = (hipStream_t)stream;
+  if (hsa::fwd_mfma_supported(d))
+    return launched(hsa::launch_fwd_mfma(d, Q, K, V, idx, w, O, (char*)ws, s), "fwd");
   return launched(hsa::launch_fwd_generic(d, Q, K, V, idx, w, O, s), "fwd");
 }
 

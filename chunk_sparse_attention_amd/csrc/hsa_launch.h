@@ -51,6 +51,12 @@ hipError_t launch_bwd_generic(const Dims& d, const BwdLayout& lay, const void* Q
                               const int32_t* idx, const float* score, const float* w,
                               const void* dO, void* dQ, void* dK, void* dV, void* dQs,
                               float* dKslc, bool fold, char* ws, hipStream_t s);
+// Matrix-core (MFMA) kernels for bf16.
+bool fwd_mfma_supported(const Dims& d);
+size_t fwd_mfma_ws(const Dims& d);
+hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,
+                           const int32_t* idx, const float* w, void* O, char* ws, hipStream_t s);
+
 hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void* q,
                                  const void* qs, const void* Kc, const void* Vc,
                                  const void* Kslc, void* O, int32_t* idx, float* score,
