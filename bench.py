@@ -129,6 +129,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--decode", action="store_true", help="also time the 1M-context decode step")
+    ap.add_argument("--only", choices=["select", "fwd", "bwd"], default=None,
+                    help="profiling aid: after one full step, run only this entry point "
+                         "--steps times and print its mean time (no JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build of the HSA operator has no multi-GPU "
@@ -168,6 +171,25 @@ def main() -> int:
         idx, _, _ = step()
     torch.cuda.synchronize()
     n_slots = int((idx >= 0).sum().item())
+
+    if args.only:
+        Kslc, idx, score, w = hsa.select(Qs, K, wl.K, generic=gen)
+        prob_fwd = hsa.problem(wl.B, wl.L, wl.Hq, wl.Hkv, wl.D, wl.K, wl.dtype, generic=gen)
+        ws_fwd = hsa.workspace(_lib.HSA_OP_FWD, prob_fwd, dev)
+        O = torch.empty_like(Q)
+        run = {"select": lambda: hsa.select(Qs, K, wl.K, generic=gen),
+               "fwd": lambda: hsa.fwd(Q, K, V, idx, w, generic=gen, ws=ws_fwd, out=O),
+               "bwd": lambda: hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, generic=gen,
+                                      ws=ws_bwd)}[args.only]
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        log(f"bench: only {args.only}: {e0.elapsed_time(e1) / args.steps:.4f} ms per call")
+        return 0
 
     log(f"bench: timing {args.steps} steps")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]

@@ -42,6 +42,7 @@ BwdLayout bwd_layout(const Dims& d) {
   l.part_dk = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
   l.part_dv = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
   l.part_dks = take(sizeof(float) * bg * l.max_seg * d.D);
+  l.kt = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
   l.total = o;
   return l;
 }
@@ -486,41 +487,67 @@ __global__ void __launch_bounds__(256) k_bwd_p2_reduce(
 }
 
 template <typename T>
-static void launch_bwd_typed(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
-                             const void* V, const void* Qs, const void* Kslc,
-                             const int32_t* idx, const float* score, const float* w,
-                             const void* dO, void* dQ, void* dK, void* dV, void* dQs,
-                             float* dKslc, bool fold, char* ws, hipStream_t s) {
+static void launch_p1_generic(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
+                              const void* V, const void* Kslc, const int32_t* idx,
+                              const float* score, const float* w, const void* dO, void* dQ,
+                              void* dQs, char* ws, hipStream_t s) {
   const size_t rows = (size_t)d.B * d.L * d.Hkv;
-  const float sm = (float)d.sm_scale, sel = (float)d.sel_scale;
-  float* ds = (float*)(ws + lay.ds);
-  float* dw = (float*)(ws + lay.dw);
   k_bwd_p1_generic<T><<<dim3((unsigned)rows), 64, 0, s>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)Kslc, idx, score, w, (const T*)dO,
-      (T*)dQ, (T*)dQs, ds, dw, d.L, d.Hq, d.Hkv, d.D, d.S, d.K, d.G, d.nC, sm, sel);
+      (T*)dQ, (T*)dQs, (float*)(ws + lay.ds), (float*)(ws + lay.dw), d.L, d.Hq, d.Hkv, d.D, d.S,
+      d.K, d.G, d.nC, (float)d.sm_scale, (float)d.sel_scale);
+}
+
+template <typename T>
+static void launch_p2_generic(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
+                              const void* V, const void* Qs, const float* w, const void* dO,
+                              char* ws, hipStream_t s) {
   const int bg = d.B * d.Hkv;
-  if (d.nC > 0) {
-    dim3 grid((unsigned)(bg * lay.max_seg));
-    auto args = [&](auto kern) {
-      kern<<<grid, 128, 0, s>>>((const T*)Q, (const T*)K, (const T*)V, (const T*)Qs, w,
-                                (const T*)dO, ds, (const int32_t*)(ws + lay.offsets),
-                                (const int32_t*)(ws + lay.entries),
-                                (const int32_t*)(ws + lay.seg_start),
-                                (const int32_t*)(ws + lay.seg_chunk),
-                                (const int32_t*)(ws + lay.n_seg), (float*)(ws + lay.part_dk),
-                                (float*)(ws + lay.part_dv), (float*)(ws + lay.part_dks), d.L, d.Hq,
-                                d.Hkv, d.S, d.K, d.G, d.nC, lay.seg, lay.max_seg, sm, sel);
-    };
-    if (d.D == 64)
-      args(k_bwd_p2_seg<T, 64>);
-    else
-      args(k_bwd_p2_seg<T, 128>);
-  }
+  const float sm = (float)d.sm_scale, sel = (float)d.sel_scale;
+  dim3 grid((unsigned)(bg * lay.max_seg));
+  auto args = [&](auto kern) {
+    kern<<<grid, 128, 0, s>>>((const T*)Q, (const T*)K, (const T*)V, (const T*)Qs, w,
+                              (const T*)dO, (const float*)(ws + lay.ds),
+                              (const int32_t*)(ws + lay.offsets),
+                              (const int32_t*)(ws + lay.entries),
+                              (const int32_t*)(ws + lay.seg_start),
+                              (const int32_t*)(ws + lay.seg_chunk),
+                              (const int32_t*)(ws + lay.n_seg), (float*)(ws + lay.part_dk),
+                              (float*)(ws + lay.part_dv), (float*)(ws + lay.part_dks), d.L, d.Hq,
+                              d.Hkv, d.S, d.K, d.G, d.nC, lay.seg, lay.max_seg, sm, sel);
+  };
+  if (d.D == 64)
+    args(k_bwd_p2_seg<T, 64>);
+  else
+    args(k_bwd_p2_seg<T, 128>);
+}
+
+hipError_t launch_bwd_generic_p2(const Dims& d, const BwdLayout& lay, const void* Q,
+                                 const void* K, const void* V, const void* Qs, const float* w,
+                                 const void* dO, char* ws, hipStream_t s) {
+  if (d.nC == 0) return hipSuccess;
+  if (d.dtype == 1)
+    launch_p2_generic<bf16>(d, lay, Q, K, V, Qs, w, dO, ws, s);
+  else
+    launch_p2_generic<float>(d, lay, Q, K, V, Qs, w, dO, ws, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const Dims& d, const BwdLayout& lay, void* dK, void* dV,
+                             float* dKslc, bool fold, char* ws, hipStream_t s) {
+  const int bg = d.B * d.Hkv;
   const int n_all = (d.L + d.S - 1) / d.S;
-  k_bwd_p2_reduce<T><<<dim3((unsigned)(bg * n_all)), 256, 0, s>>>(
-      (const float*)(ws + lay.part_dk), (const float*)(ws + lay.part_dv),
-      (const float*)(ws + lay.part_dks), (const int32_t*)(ws + lay.seg_start), (T*)dK, (T*)dV,
-      dKslc, d.L, d.Hkv, d.D, d.S, d.nC, n_all, lay.max_seg, fold ? 1 : 0);
+  auto go = [&](auto kern, auto* dk, auto* dv) {
+    kern<<<dim3((unsigned)(bg * n_all)), 256, 0, s>>>(
+        (const float*)(ws + lay.part_dk), (const float*)(ws + lay.part_dv),
+        (const float*)(ws + lay.part_dks), (const int32_t*)(ws + lay.seg_start), dk, dv, dKslc,
+        d.L, d.Hkv, d.D, d.S, d.nC, n_all, lay.max_seg, fold ? 1 : 0);
+  };
+  if (d.dtype == 1)
+    go(k_bwd_p2_reduce<bf16>, (bf16*)dK, (bf16*)dV);
+  else
+    go(k_bwd_p2_reduce<float>, (float*)dK, (float*)dV);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_generic(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
@@ -531,12 +558,12 @@ hipError_t launch_bwd_generic(const Dims& d, const BwdLayout& lay, const void* Q
   hipError_t e = launch_invidx(d, lay, idx, ws, s);
   if (e != hipSuccess) return e;
   if (d.dtype == 1)
-    launch_bwd_typed<bf16>(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK, dV, dQs, dKslc,
-                           fold, ws, s);
+    launch_p1_generic<bf16>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
   else
-    launch_bwd_typed<float>(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK, dV, dQs, dKslc,
-                            fold, ws, s);
-  return hipGetLastError();
+    launch_p1_generic<float>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
+  e = launch_bwd_generic_p2(d, lay, Q, K, V, Qs, w, dO, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_bwd_reduce(d, lay, dK, dV, dKslc, fold, ws, s);
 }
 
 }  // namespace hsa

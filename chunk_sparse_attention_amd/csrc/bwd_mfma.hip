@@ -1,0 +1,490 @@
+// bwd_mfma.hip -- bf16 backward on the matrix cores (gfx950), in two phases.
+//
+// "Hardware-aligned Hierarchical Sparse Attention ...", papernotes.org note, 方法详解 ›
+// 硬件对齐 Kernel: the backward first accumulates the gradients of the queries and of the chunk
+// weights per token, then the gradients of keys and values per chunk over every token that
+// selected it; the chunk weights pass gradient on into the selection scores (same note,
+// 层次化稀疏注意力（HSA）, 端到端学习).
+//
+// Phase 1 (token tiles, like the forward): per 16-column job of one chunk
+//   S^T = K_c Q^T, dP^T = V_c dO^T                     (MFMA)
+//   P = softmax1(S), D = sum_keys P.dP, dS = w P (dP - D)   (per column, fp32)
+//   dQ^T += K_c^T dS^T                                  (MFMA, into LDS by rounds)
+//   dw_edge = sum over the token's heads of D
+// then per token the stick-breaking chain rule gives ds and dQs.
+// Phase 2 (chunk segments over the chunk -> (token, slot) index): per job of 16 query rows
+//   S = Q K_c^T, dP = dO V_c^T, P, D, dS as above (rows = queries, columns = keys)
+//   dV^T += dO^T (w P),  dK^T += Q^T dS                  (MFMA 16x16x16, registers)
+//   dKslc += ds * Qs
+// and every segment writes fp32 partials that a fixed-order reduction sums per chunk.
+#include "hsa_common.h"
+#include "hsa_launch.h"
+#include "mfma_common.h"
+#include "tile_common.h"
+
+namespace hsa {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ s16x4 pack_bf16x4(f32x4 v) {
+  return __builtin_bit_cast(s16x4, __builtin_convertvector(v, bf16x4));
+}
+
+
+// ---- phase 1 -------------------------------------------------------------------------------
+
+template <int D, int TT, int G>
+__global__ void __launch_bounds__(512) k_bwd_p1_tile(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ Kt, const bf16* __restrict__ Kslc, const int32_t* __restrict__ idx,
+    const float* __restrict__ score, const float* __restrict__ w, const bf16* __restrict__ dO,
+    bf16* __restrict__ dQ, bf16* __restrict__ dQs, float* __restrict__ ds_out,
+    float* __restrict__ dw_out, int L, int Hq, int Hkv, int Kn, int nC, int BG, float c2,
+    float sm_scale, float sel_scale) {
+  constexpr int NT = 512, NW = NT / 64;
+  constexpr int TPJ = 16 / G;
+  constexpr int DP = D + 1;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int NMAX = TT * 16;
+  __shared__ float acc[TT * G * DP];  // dQ (without the logit scale)
+  __shared__ uint32_t keys[NMAX];
+  __shared__ uint32_t jobs[NMAX];     // later: ds per (token, slot)
+  __shared__ int scratch[3 * NMAX];
+  __shared__ float wsh[TT * 16];
+  __shared__ float dwsh[TT * 16];
+  __shared__ int n_valid_sh, n_jobs_sh, n_rounds_sh;
+
+  const int bg = blockIdx.x % BG;
+  const int tile = blockIdx.x / BG;
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const int t0 = tile * TT;
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+
+  int N = 1;
+  while (N < TT * Kn) N <<= 1;
+  for (int i = tid; i < N; i += NT) {
+    uint32_t key = kNoEdge;
+    if (i < TT * Kn) {
+      const int tl = i / Kn, k = i % Kn, t = t0 + tl;
+      if (t < L) {
+        const size_t o = ((b * L + t) * Hkv + g) * Kn + k;
+        const int c = idx[o];
+        if (c >= 0 && c < nC) {
+          key = edge_key(c, tl, k);
+          wsh[tl * 16 + k] = w[o];
+        }
+      }
+    }
+    keys[i] = key;
+  }
+  for (int i = tid; i < TT * 16; i += NT) dwsh[i] = 0.0f;
+  for (int i = tid; i < TT * G * DP; i += NT) acc[i] = 0.0f;
+  __syncthreads();
+  block_bitonic_sort<NT>(keys, N);
+  build_jobs<NT>(keys, N, TPJ, scratch, scratch + NMAX, jobs, &n_valid_sh, &n_jobs_sh);
+  const int n_jobs = n_jobs_sh;
+  uint32_t* order = reinterpret_cast<uint32_t*>(scratch + NMAX);
+  uint64_t* tmask = reinterpret_cast<uint64_t*>(scratch + 2 * NMAX);
+  int* roff = scratch + 2 * NMAX + 2 * TT;
+  build_rounds<NT, TT>(keys, jobs, n_jobs, tmask, scratch, roff, order, &n_rounds_sh);
+  const int n_rounds = n_rounds_sh;
+
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int col = lane % 16, blk = lane / 16;
+  const int slot = col / G, head = col % G;
+  const size_t kvrow = (size_t)Hkv * D;
+  bf16x8 ka[4][KS], vr[4][KS], kt[DT][2];
+  int cur = -1;
+  for (int r = 0; r < n_rounds; ++r) {
+    const int a = roff[r], n = roff[r + 1] - a;
+    const int jb = a + (int)((long)n * wv / NW), je = a + (int)((long)n * (wv + 1) / NW);
+    for (int j = jb; j < je; ++j) {
+      const uint32_t job = __builtin_amdgcn_readfirstlane(order[j]);
+      const int e0 = (int)(job & 0xffff), cnt = (int)(job >> 16);
+      const int c = __builtin_amdgcn_readfirstlane(edge_chunk(keys[e0]));
+      const bool valid = slot < cnt;
+      const uint32_t ek = keys[e0 + (valid ? slot : 0)];
+      const int tl = edge_token(ek), k = edge_slot(ek);
+      const size_t qoff = ((b * L + t0 + tl) * Hq + (size_t)g * G + head) * D;
+      bf16x8 qb[KS], db[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qb[ks] = ld_bf16x8(Q + qoff + 32 * ks + 8 * blk);
+        db[ks] = ld_bf16x8(dO + qoff + 32 * ks + 8 * blk);
+      }
+      if (c != cur) {
+        cur = c;
+        const size_t cb = ((b * L + (size_t)c * 64) * Hkv + g) * D;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            ka[t4][ks] = ld_bf16x8(K + cb + (size_t)(16 * t4 + col) * kvrow + 32 * ks + 8 * blk);
+            vr[t4][ks] = ld_bf16x8(V + cb + (size_t)(16 * t4 + col) * kvrow + 32 * ks + 8 * blk);
+          }
+        const bf16* kc = Kt + ((size_t)bg * nC + c) * D * 64;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            kt[dt][s] = ld_bf16x8(kc + (size_t)(16 * dt + col) * 64 + 32 * s + 8 * blk);
+      }
+      f32x4 sa[4], pa[4];
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        sa[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pa[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          sa[t4] = mfma_16x16x32(ka[t4][ks], qb[ks], sa[t4]);
+          pa[t4] = mfma_16x16x32(vr[t4][ks], db[ks], pa[t4]);
+        }
+      }
+      float m = 0.0f;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, sa[t4][i] * c2);
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      float sum = 0.0f;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sa[t4][i] = exp2_fast(sa[t4][i] * c2 - m);
+          sum += sa[t4][i];
+        }
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      const float inv = 1.0f / (exp2_fast(-m) + sum);
+      float dsum = 0.0f;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sa[t4][i] *= inv;  // P
+          dsum += sa[t4][i] * pa[t4][i];
+        }
+      dsum += __shfl_xor(dsum, 16, 64);
+      dsum += __shfl_xor(dsum, 32, 64);  // D of this column
+      const float wk = valid ? wsh[tl * 16 + k] : 0.0f;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[t4][i] = wk * sa[t4][i] * (pa[t4][i] - dsum);  // dS
+      bf16x8 sb[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) sb[s] = pack_bf16x8(sa[2 * s], sa[2 * s + 1]);
+      // dw of this edge: sum of D over the token's G head columns (lanes of one slot)
+      float dw = dsum;
+#pragma unroll
+      for (int o = 1; o < G; o <<= 1) dw += __shfl_xor(dw, o, 64);
+      if (valid && head == 0 && blk == 0) dwsh[tl * 16 + k] = dw;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        o = mfma_16x16x32(kt[dt][0], sb[0], o);
+        o = mfma_16x16x32(kt[dt][1], sb[1], o);
+        if (valid) {
+          float* dst = acc + (tl * G + head) * DP + 16 * dt + 4 * blk;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i] += o[i];
+        }
+      }
+    }
+    __syncthreads();  // end of round r
+  }
+
+  // per token: ds by the stick-breaking chain rule (newest slot first)
+  float* dssh = reinterpret_cast<float*>(jobs);
+  if (tid < TT) {
+    const int tl = tid, t = t0 + tl;
+    if (t < L) {
+      const size_t o = ((b * L + t) * Hkv + g) * Kn;
+      double suffix = 0.0;
+      for (int k = Kn - 1; k >= 0; --k) {
+        const int c = idx[o + k];
+        double dsk = 0.0, dwk = 0.0;
+        if (c >= 0 && c < nC) {
+          const double p = sigmoid_d((double)score[o + k]);
+          const double wk = (double)wsh[tl * 16 + k];
+          dwk = (double)dwsh[tl * 16 + k];
+          dsk = dwk * wk * (1.0 - p) - p * suffix;
+          suffix += dwk * wk;
+        }
+        dssh[tl * 16 + k] = (float)dsk;
+        ds_out[o + k] = (float)dsk;
+        dw_out[o + k] = (float)dwk;
+      }
+    }
+  }
+  __syncthreads();
+  // dQs = sel_scale * sum_k ds_k Kslc[c_k]
+  for (int i = tid; i < TT * D; i += NT) {
+    const int tl = i / D, e = i % D, t = t0 + tl;
+    if (t >= L) continue;
+    const size_t o = ((b * L + t) * Hkv + g) * Kn;
+    float a = 0.0f;
+    for (int k = 0; k < Kn; ++k) {
+      const int c = idx[o + k];
+      if (c >= 0 && c < nC) a += dssh[tl * 16 + k] * to_f32(Kslc[((b * nC + c) * Hkv + g) * D + e]);
+    }
+    dQs[((b * L + t) * Hkv + g) * D + e] = from_f32<bf16>(a * sel_scale);
+  }
+  // dQ
+  for (int i = tid; i < TT * G * D / 8; i += NT) {
+    const int e = i * 8;
+    const int tl = e / (G * D), h = (e / D) % G, d = e % D;
+    const int t = t0 + tl;
+    if (t >= L) continue;
+    const float* src = acc + (tl * G + h) * DP + d;
+    f32x4 lo = {src[0], src[1], src[2], src[3]};
+    f32x4 hi = {src[4], src[5], src[6], src[7]};
+    *reinterpret_cast<bf16x8*>(dQ + ((b * L + t) * Hq + (size_t)g * G + h) * D + d) =
+        pack_bf16x8(lo * sm_scale, hi * sm_scale);
+  }
+}
+
+// ---- phase 2 -------------------------------------------------------------------------------
+
+// One wave per segment of a chunk's selector list (D = 64).  The chunk's keys and values sit
+// in LDS; a job takes 16/G selectors (16 query rows).  dK^T and dV^T accumulate in registers
+// (MFMA accumulators) for the whole segment.
+template <int G>
+__global__ void __launch_bounds__(64) k_bwd_p2_mfma(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ Qs, const float* __restrict__ w, const bf16* __restrict__ dO,
+    const float* __restrict__ ds_in, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ entries, const int32_t* __restrict__ seg_start,
+    const int32_t* __restrict__ seg_chunk, const int32_t* __restrict__ n_seg,
+    float* __restrict__ part_dk, float* __restrict__ part_dv, float* __restrict__ part_dks,
+    int L, int Hq, int Hkv, int Kn, int nC, int seg, int64_t max_seg, float c2, float sm_scale,
+    float sel_scale) {
+  constexpr int D = 64, TPJ = 16 / G, KS = D / 32, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t kl[64][D + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vl[64][D + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t ql[16][D + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t dl[16][D + 8];
+  const int64_t sidx = blockIdx.x % max_seg;
+  const int bg = (int)(blockIdx.x / max_seg);
+  if (sidx >= n_seg[bg]) return;  // whole wave
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const int c = seg_chunk[(size_t)bg * max_seg + sidx];
+  const int32_t* off = offsets + (size_t)bg * (nC + 1);
+  const int32_t* ss = seg_start + (size_t)bg * (nC + 1);
+  const int e0 = off[c] + (int)(sidx - ss[c]) * seg;
+  const int e1 = min(off[c + 1], e0 + seg);
+  const int32_t* ent = entries + (size_t)bg * L * Kn;
+  const int lane = threadIdx.x, col = lane % 16, blk = lane / 16;
+  const size_t kvrow = (size_t)Hkv * D;
+  const size_t cb = ((b * L + (size_t)c * 64) * Hkv + g) * D;
+  for (int i = lane; i < 64 * (D / 8); i += 64) {
+    const int key = i / (D / 8), d = (i % (D / 8)) * 8;
+    *reinterpret_cast<uint4*>(&kl[key][d]) = *reinterpret_cast<const uint4*>(K + cb + key * kvrow + d);
+    *reinterpret_cast<uint4*>(&vl[key][d]) = *reinterpret_cast<const uint4*>(V + cb + key * kvrow + d);
+  }
+  f32x4 dk[DT][4], dv[DT][4];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      dk[dt][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[dt][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  float dks = 0.0f;
+  const int qs_sel = col / G, qs_head = col % G;  // this lane's A-operand row -> selector, head
+  __syncthreads();
+
+  for (int ej = e0; ej < e1; ej += TPJ) {
+    const int n_here = min(TPJ, e1 - ej);
+    // this lane's query row (A operand): selector qs_sel of the job
+    const int my_sel = qs_sel < n_here ? qs_sel : 0;
+    const int val = ent[ej + my_sel];
+    const int t = val / Kn;
+    const size_t qoff = ((b * L + t) * Hq + (size_t)g * G + qs_head) * D;
+    bf16x8 qa[KS], da[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qa[ks] = ld_bf16x8(Q + qoff + 32 * ks + 8 * blk);
+      da[ks] = ld_bf16x8(dO + qoff + 32 * ks + 8 * blk);
+      *reinterpret_cast<bf16x8*>(&ql[col][32 * ks + 8 * blk]) = qa[ks];
+      *reinterpret_cast<bf16x8*>(&dl[col][32 * ks + 8 * blk]) = da[ks];
+    }
+    __syncthreads();  // ql/dl are read transposed below
+    // S = Q K_c^T, dP = dO V_c^T (rows: the 16 query rows; columns: keys 16*t4 + col)
+    f32x4 sa[4], pa[4];
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      sa[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pa[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(&kl[16 * t4 + col][32 * ks + 8 * blk]);
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&vl[16 * t4 + col][32 * ks + 8 * blk]);
+        sa[t4] = mfma_16x16x32(qa[ks], kb, sa[t4]);
+        pa[t4] = mfma_16x16x32(da[ks], vb, pa[t4]);
+      }
+    }
+    // per query row r = 4*blk + i: softmax1 over the 64 keys (4 tiles x 16 lanes)
+    float wr[4], dr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * blk + i, s = r / G;
+      float m = 0.0f;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) m = fmaxf(m, sa[t4][i] * c2);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      float sum = 0.0f;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        sa[t4][i] = exp2_fast(sa[t4][i] * c2 - m);
+        sum += sa[t4][i];
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+      const float inv = 1.0f / (exp2_fast(-m) + sum);
+      float dsum = 0.0f;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        sa[t4][i] *= inv;
+        dsum += sa[t4][i] * pa[t4][i];
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) dsum += __shfl_xor(dsum, o, 64);
+      float wv = 0.0f;
+      if (s < n_here) {
+        const int v2 = ent[ej + s];
+        wv = w[((b * L + v2 / Kn) * Hkv + g) * Kn + v2 % Kn];
+      }
+      wr[i] = wv;
+      dr[i] = dsum;
+    }
+    // dV^T += dO^T (w P), dK^T += Q^T dS  (k = the 16 query rows, 4 per lane block)
+    s16x4 doT[DT], qT[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      s16x4 a, q;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = (short)dl[4 * blk + e][16 * dt + col];
+        q[e] = (short)ql[4 * blk + e][16 * dt + col];
+      }
+      doT[dt] = a;
+      qT[dt] = q;
+    }
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      f32x4 wp, dsv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wp[i] = wr[i] * sa[t4][i];
+        dsv[i] = wr[i] * sa[t4][i] * (pa[t4][i] - dr[i]);
+      }
+      const s16x4 wpb = pack_bf16x4(wp), dsb = pack_bf16x4(dsv);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dv[dt][t4] = mfma_16x16x16(doT[dt], wpb, dv[dt][t4]);
+        dk[dt][t4] = mfma_16x16x16(qT[dt], dsb, dk[dt][t4]);
+      }
+    }
+    // dKslc += ds * Qs for each selector of the job (lane = dimension)
+    for (int s = 0; s < n_here; ++s) {
+      const int v2 = ent[ej + s];
+      const size_t srow = (b * L + v2 / Kn) * Hkv + g;
+      dks += ds_in[srow * Kn + v2 % Kn] * to_f32(Qs[srow * D + lane]);
+    }
+    __syncthreads();  // ql/dl reuse by the next job
+  }
+  const size_t pb = (size_t)bg * max_seg + sidx;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const int key = 16 * t4 + col, d = 16 * dt + 4 * blk;
+      *reinterpret_cast<f32x4*>(part_dk + (pb * 64 + key) * D + d) = dk[dt][t4] * sm_scale;
+      *reinterpret_cast<f32x4*>(part_dv + (pb * 64 + key) * D + d) = dv[dt][t4];
+    }
+  part_dks[pb * D + lane] = dks * sel_scale;
+}
+
+bool bwd_mfma_supported(const Dims& d) {
+  return d.dtype == 1 && (d.D == 64 || d.D == 128) && (d.G == 4 || d.G == 8 || d.G == 16) &&
+         d.nC < 32768 && !(d.flags & 1u);
+}
+
+template <int D, int TT, int G>
+static void launch_p1(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
+                      const void* V, const void* Kslc, const int32_t* idx, const float* score,
+                      const float* w, const void* dO, void* dQ, void* dQs, char* ws,
+                      hipStream_t s) {
+  const int BG = d.B * d.Hkv;
+  const int n_tiles = (d.L + TT - 1) / TT;
+  const float c2 = (float)(d.sm_scale * 1.4426950408889634);
+  k_bwd_p1_tile<D, TT, G><<<dim3(BG * n_tiles), 512, 0, s>>>(
+      (const bf16*)Q, (const bf16*)K, (const bf16*)V, (const bf16*)(ws + lay.kt),
+      (const bf16*)Kslc, idx, score, w, (const bf16*)dO, (bf16*)dQ, (bf16*)dQs,
+      (float*)(ws + lay.ds), (float*)(ws + lay.dw), d.L, d.Hq, d.Hkv, d.K, d.nC, BG, c2,
+      (float)d.sm_scale, (float)d.sel_scale);
+}
+
+template <int D, int TT>
+static void launch_p1_g(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
+                        const void* V, const void* Kslc, const int32_t* idx, const float* score,
+                        const float* w, const void* dO, void* dQ, void* dQs, char* ws,
+                        hipStream_t s) {
+  if (d.G == 4) launch_p1<D, TT, 4>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
+  else if (d.G == 8) launch_p1<D, TT, 8>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
+  else launch_p1<D, TT / 2, 16>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
+}
+
+
+hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
+                           const void* V, const void* Qs, const void* Kslc, const int32_t* idx,
+                           const float* score, const float* w, const void* dO, void* dQ,
+                           void* dK, void* dV, void* dQs, float* dKslc, bool fold, char* ws,
+                           hipStream_t s) {
+  hipError_t e = launch_invidx(d, lay, idx, ws, s);
+  if (e != hipSuccess) return e;
+  const int BG = d.B * d.Hkv;
+  launch_prep_transpose(d, K, ws + lay.kt, s);
+  if (d.D == 64)
+    launch_p1_g<64, 64>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
+  else
+    launch_p1_g<128, 32>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
+  if (d.nC > 0) {
+    if (d.D == 64) {
+      const float c2 = (float)(d.sm_scale * 1.4426950408889634);
+      dim3 grid((unsigned)(BG * lay.max_seg));
+      auto go = [&](auto kern) {
+        kern<<<grid, 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)V,
+                                 (const bf16*)Qs, w, (const bf16*)dO,
+                                 (const float*)(ws + lay.ds), (const int32_t*)(ws + lay.offsets),
+                                 (const int32_t*)(ws + lay.entries),
+                                 (const int32_t*)(ws + lay.seg_start),
+                                 (const int32_t*)(ws + lay.seg_chunk),
+                                 (const int32_t*)(ws + lay.n_seg), (float*)(ws + lay.part_dk),
+                                 (float*)(ws + lay.part_dv), (float*)(ws + lay.part_dks), d.L,
+                                 d.Hq, d.Hkv, d.K, d.nC, lay.seg, lay.max_seg, c2,
+                                 (float)d.sm_scale, (float)d.sel_scale);
+      };
+      if (d.G == 4) go(k_bwd_p2_mfma<4>);
+      else if (d.G == 8) go(k_bwd_p2_mfma<8>);
+      else go(k_bwd_p2_mfma<16>);
+    } else {
+      e = launch_bwd_generic_p2(d, lay, Q, K, V, Qs, w, dO, ws, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return launch_bwd_reduce(d, lay, dK, dV, dKslc, fold, ws, s);
+}
+
+}  // namespace hsa

@@ -12,8 +12,9 @@
 //   S^T = K_c Q^T            (keys x columns, MFMA)
 //   P   = w * softmax1(S)    (per column, fp32, exp2 with the logit scale folded in)
 //   O^T += V_c^T P^T         (MFMA), added into the tile's LDS accumulators.
-// The LDS additions are atomic; their order between waves is not fixed, so O can differ
-// from run to run in the last fp32 bits before the bf16 rounding.
+// Jobs are coloured into rounds in which no token appears twice; the waves of a round add
+// into LDS with plain read-add-write and a barrier separates rounds, so the result does not
+// depend on wave timing.
 #include "hsa_common.h"
 #include "hsa_launch.h"
 #include "mfma_common.h"
@@ -59,7 +60,7 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
   __shared__ uint32_t jobs[NMAX];
   __shared__ int scratch[3 * NMAX];
   __shared__ float wsh[TT * 16];
-  __shared__ int n_valid_sh, n_jobs_sh;
+  __shared__ int n_valid_sh, n_jobs_sh, n_rounds_sh;
 
   const int bg = blockIdx.x % BG;  // consecutive blocks: different (b, g), XCD-interleaved
   const int tile = blockIdx.x / BG;
@@ -93,41 +94,128 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
   block_bitonic_sort<NT>(keys, N);
   build_jobs<NT>(keys, N, TPJ, scratch, scratch + NMAX, jobs, &n_valid_sh, &n_jobs_sh);
   const int n_jobs = n_jobs_sh;
+  // 3b. rounds: scratch now holds [jround: NMAX][order: NMAX][tmask: 2*TT][roff: 65]
+  uint32_t* order = reinterpret_cast<uint32_t*>(scratch + NMAX);
+  uint64_t* tmask = reinterpret_cast<uint64_t*>(scratch + 2 * NMAX);
+  int* roff = scratch + 2 * NMAX + 2 * TT;
+  build_rounds<NT, TT>(keys, jobs, n_jobs, tmask, scratch, roff, order, &n_rounds_sh);
+  const int n_rounds = n_rounds_sh;
 
-  // 4. jobs, a contiguous range per wave
-  const int j0 = (int)((long)n_jobs * wave / NW);
-  const int j1 = (int)((long)n_jobs * (wave + 1) / NW);
+  // 4. jobs, a contiguous range per wave.  The loads for job j+1 (its queries and, when its
+  //    chunk differs, the chunk's keys -- and values for D=64, where registers allow) are
+  //    issued before job j is computed, so their latency overlaps job j's matrix work.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // this wave's share of round r: [rb(r), re(r))
+  auto rb = [&](int r) {
+    const int a = roff[r], n = roff[r + 1] - a;
+    return a + (int)((long)n * wv / NW);
+  };
+  auto re = [&](int r) {
+    const int a = roff[r], n = roff[r + 1] - a;
+    return a + (int)((long)n * (wv + 1) / NW);
+  };
+  // next job of this wave after job j of round r (or -1): uniform scalar work
+  auto next_job = [&](int r, int j) {
+    if (j + 1 < re(r)) return j + 1;
+    for (int r2 = r + 1; r2 < n_rounds; ++r2)
+      if (rb(r2) < re(r2)) return rb(r2);
+    return -1;
+  };
   const int col = lane % 16, blk = lane / 16;
   const int slot = col / G, head = col % G;
-  bf16x8 ka[4][KS];   // K_c rows (A operand of S^T)
-  bf16x8 va[DT][2];   // V_c^T rows (A operand of O^T)
-  int cur = -1;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t job = jobs[j];
+  // D=64: the next chunk's keys and values are prefetched into a second register set.
+  // D=128 has no registers to spare for that; its chunk operands load when the chunk changes.
+  constexpr bool kPrefetchKV = (D == 64);
+  bf16x8 ka[4][KS], kn[4][KS];           // K_c rows (A operand of S^T): current, next
+  bf16x8 va[DT][2], vn[DT][2];           // V_c^T rows (A operand of O^T): current, next
+  bf16x8 qb[KS], qn[KS];                 // Q^T columns (B operand of S^T): current, next
+  int tl_c = 0, k_c = 0, tl_n = 0, k_n = 0;
+  bool valid_c = false, valid_n = false;
+  const size_t kvrow = (size_t)Hkv * D;
+
+  auto chunk_of = [&](int j) {
+    return __builtin_amdgcn_readfirstlane(edge_chunk(keys[order[j] & 0xffff]));
+  };
+  auto load_k = [&](bf16x8 (&dst)[4][KS], int c) {
+    const bf16* kc = K + ((b * L + (size_t)c * 64) * Hkv + g) * D;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        dst[kt][ks] = ld_bf16x8(kc + (size_t)(16 * kt + col) * kvrow + 32 * ks + 8 * blk);
+  };
+  auto load_v = [&](bf16x8 (&dst)[DT][2], int c) {
+    const bf16* vt = Vt + ((size_t)bg * nC + c) * D * 64;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        dst[dt][s] = ld_bf16x8(vt + (size_t)(16 * dt + col) * 64 + 32 * s + 8 * blk);
+  };
+  auto load_q = [&](bf16x8 (&dst)[KS], int j, int& tl, int& k, bool& valid) {
+    const uint32_t job = __builtin_amdgcn_readfirstlane(order[j]);
     const int e0 = (int)(job & 0xffff), cnt = (int)(job >> 16);
-    const int c = edge_chunk(keys[e0]);
-    if (c != cur) {
-      cur = c;
-      const bf16* kc = K + ((b * L + (size_t)c * 64) * Hkv + g) * D;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ka[kt][ks] = ld_bf16x8(kc + (size_t)(16 * kt + col) * Hkv * D + 32 * ks + 8 * blk);
-      const bf16* vt = Vt + ((size_t)bg * nC + c) * D * 64;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          va[dt][s] = ld_bf16x8(vt + (size_t)(16 * dt + col) * 64 + 32 * s + 8 * blk);
-    }
-    const bool valid = slot < cnt;
-    const uint32_t ek = valid ? keys[e0 + slot] : 0u;
-    const int tl = edge_token(ek), k = edge_slot(ek);
+    valid = slot < cnt;
+    // a padding column reads the job's first token: its weight factor is 0 and nothing of it
+    // is stored, and an unconditional load keeps the prefetch free of branches and waits
+    const uint32_t ek = keys[e0 + (valid ? slot : 0)];
+    tl = edge_token(ek);
+    k = edge_slot(ek);
     const bf16* qrow = Q + ((b * L + t0 + tl) * Hq + (size_t)g * G + head) * D;
-    bf16x8 qb[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = valid ? ld_bf16x8(qrow + 32 * ks + 8 * blk) : zero_bf16x8();
+    for (int ks = 0; ks < KS; ++ks) dst[ks] = ld_bf16x8(qrow + 32 * ks + 8 * blk);
+  };
+
+  // The loads for a wave's next job are issued before its current job is computed; at the
+  // top of each job the prefetched registers move into the working set, so the matrix work
+  // only waits for loads issued a whole job earlier.  Loads may cross a round barrier: only
+  // the LDS accumulation is ordered by rounds.
+  int cur = -1, nxt = -1;
+  int jn = -1;
+  for (int r = 0; r < n_rounds && jn < 0; ++r)
+    if (rb(r) < re(r)) jn = rb(r);
+  if (jn >= 0) {
+    nxt = chunk_of(jn);
+    if (kPrefetchKV) {
+      load_k(kn, nxt);
+      load_v(vn, nxt);
+    }
+    load_q(qn, jn, tl_n, k_n, valid_n);
+  }
+  for (int r = 0; r < n_rounds; ++r) {
+  const int jr1 = re(r);
+  for (int j = rb(r); j < jr1; ++j) {
+    if (nxt != cur) {
+      if (kPrefetchKV) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) ka[kt][ks] = kn[kt][ks];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) va[dt][s] = vn[dt][s];
+      } else {
+        load_k(ka, nxt);
+        load_v(va, nxt);
+      }
+      cur = nxt;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = qn[ks];
+    tl_c = tl_n;
+    k_c = k_n;
+    valid_c = valid_n;
+    jn = next_job(r, j);
+    if (jn >= 0) {
+      nxt = chunk_of(jn);
+      if (kPrefetchKV && nxt != cur) {
+        load_k(kn, nxt);
+        load_v(vn, nxt);
+      }
+      load_q(qn, jn, tl_n, k_n, valid_n);
+    }
+    // S^T = K_c Q^T
     f32x4 s_acc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -156,7 +244,7 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
       }
     sum += __shfl_xor(sum, 16, 64);
     sum += __shfl_xor(sum, 32, 64);
-    const float f = valid ? wsh[tl * 16 + k] / (exp2_fast(-m) + sum) : 0.0f;
+    const float f = valid_c ? wsh[tl_c * 16 + k_c] / (exp2_fast(-m) + sum) : 0.0f;
     bf16x8 pb[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) pb[s] = pack_bf16x8(s_acc[2 * s] * f, s_acc[2 * s + 1] * f);
@@ -165,14 +253,15 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
       o = mfma_16x16x32(va[dt][0], pb[0], o);
       o = mfma_16x16x32(va[dt][1], pb[1], o);
-      if (valid) {
-        float* dst = acc + (tl * G + head) * DP + 16 * dt + 4 * blk;
+      if (valid_c) {
+        float* dst = acc + (tl_c * G + head) * DP + 16 * dt + 4 * blk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(dst + i, o[i]);
+        for (int i = 0; i < 4; ++i) dst[i] += o[i];
       }
     }
   }
-  __syncthreads();
+  __syncthreads();  // end of round r
+  }
 
   // 5. outputs (rows past L skipped; tokens with no chunk stay 0)
   for (int i = tid; i < TT * G * D / 8; i += NT) {
@@ -202,8 +291,6 @@ template <int D, int TT>
 static bool launch_fwd_tile_g(const Dims& d, const void* Q, const void* K, const void* Vt,
                               const int32_t* idx, const float* w, void* O, hipStream_t s) {
   switch (d.G) {
-    case 1: launch_fwd_tile<D, TT, 1>(d, Q, K, Vt, idx, w, O, s); return true;
-    case 2: launch_fwd_tile<D, TT, 2>(d, Q, K, Vt, idx, w, O, s); return true;
     case 4: launch_fwd_tile<D, TT, 4>(d, Q, K, Vt, idx, w, O, s); return true;
     case 8: launch_fwd_tile<D, TT, 8>(d, Q, K, Vt, idx, w, O, s); return true;
     case 16: launch_fwd_tile<D, TT / 2, 16>(d, Q, K, Vt, idx, w, O, s); return true;
@@ -213,12 +300,18 @@ static bool launch_fwd_tile_g(const Dims& d, const void* Q, const void* K, const
 
 bool fwd_mfma_supported(const Dims& d) {
   return d.dtype == 1 && (d.D == 64 || d.D == 128) &&
-         (d.G == 1 || d.G == 2 || d.G == 4 || d.G == 8 || d.G == 16) && d.nC < 32768 &&
+         (d.G == 4 || d.G == 8 || d.G == 16) && d.nC < 32768 &&
          !(d.flags & 1u);
 }
 
 size_t fwd_mfma_ws(const Dims& d) {
   return ((size_t)d.B * d.Hkv * d.nC * 64 * d.D * sizeof(uint16_t) + 255) & ~(size_t)255;
+}
+
+void launch_prep_transpose(const Dims& d, const void* src, void* dst, hipStream_t s) {
+  if (d.nC > 0)
+    k_prep_vt<<<dim3(d.B * d.Hkv * d.nC), 256, 0, s>>>((const bf16*)src, (bf16*)dst, d.L, d.Hkv,
+                                                       d.D, d.nC);
 }
 
 hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,

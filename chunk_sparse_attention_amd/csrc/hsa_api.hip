@@ -233,6 +233,11 @@ HSA_EXPORT hsa_status_t hsa_bwd(const hsa_problem_t* p, const void* Q, const voi
   TRY(check_pending());
   hipStream_t s = (hipStream_t)stream;
   hsa::BwdLayout lay = hsa::bwd_layout(d);
+  if (hsa::bwd_mfma_supported(d))
+    return launched(hsa::launch_bwd_mfma(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK,
+                                         dV, dQs, dKslc, (flags & HSA_BWD_FOLD_KSLC) != 0,
+                                         (char*)ws, s),
+                    "bwd");
   return launched(hsa::launch_bwd_generic(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK,
                                           dV, dQs, dKslc, (flags & HSA_BWD_FOLD_KSLC) != 0,
                                           (char*)ws, s),

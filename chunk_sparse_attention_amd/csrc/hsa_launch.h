@@ -24,7 +24,7 @@ struct BwdLayout {
   int seg;          // entries per backward-phase-2 segment
   int64_t max_seg;  // segment capacity per (b, g)
   size_t ds, dw, tile_counts, tile_base, offsets, entries, seg_start, seg_chunk, n_seg,
-      part_dk, part_dv, part_dks, total;
+      part_dk, part_dv, part_dks, kt, total;
 };
 BwdLayout bwd_layout(const Dims& d);
 
@@ -51,7 +51,22 @@ hipError_t launch_bwd_generic(const Dims& d, const BwdLayout& lay, const void* Q
                               const int32_t* idx, const float* score, const float* w,
                               const void* dO, void* dQ, void* dK, void* dV, void* dQs,
                               float* dKslc, bool fold, char* ws, hipStream_t s);
+hipError_t launch_bwd_generic_p2(const Dims& d, const BwdLayout& lay, const void* Q,
+                                 const void* K, const void* V, const void* Qs, const float* w,
+                                 const void* dO, char* ws, hipStream_t s);
+hipError_t launch_bwd_reduce(const Dims& d, const BwdLayout& lay, void* dK, void* dV,
+                             float* dKslc, bool fold, char* ws, hipStream_t s);
+
 // Matrix-core (MFMA) kernels for bf16.
+// Per-chunk transpose used by the matrix-core kernels:
+// dst[((b*Hkv+g)*nC + c)*D*64 + d*64 + p] = src[b, 64c + perm_key(p), g, d].
+void launch_prep_transpose(const Dims& d, const void* src, void* dst, hipStream_t s);
+bool bwd_mfma_supported(const Dims& d);
+hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
+                           const void* V, const void* Qs, const void* Kslc, const int32_t* idx,
+                           const float* score, const float* w, const void* dO, void* dQ,
+                           void* dK, void* dV, void* dQs, float* dKslc, bool fold, char* ws,
+                           hipStream_t s);
 bool fwd_mfma_supported(const Dims& d);
 size_t fwd_mfma_ws(const Dims& d);
 hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,

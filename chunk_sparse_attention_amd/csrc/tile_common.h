@@ -93,4 +93,46 @@ __device__ void build_jobs(const uint32_t* keys, int N, int tpj, int* rs, int* t
   __syncthreads();
 }
 
+// Conflict-free rounds.  Jobs of one round touch disjoint tokens, so the waves of a round
+// can update the tile's LDS accumulators with plain read-add-write (LDS float atomics are
+// slow on this part).  Greedy colouring in job order by one thread: a job takes the lowest
+// round none of its tokens is in yet.  A token has at most 16 edges, so with at most 4
+// tokens per job no job needs a round above 4*15 = 60.
+// In: jobs[0..n_jobs), keys.  Out: order[] = jobs grouped by round (job order kept inside
+// a round), roff[0..n_rounds] = round offsets, *n_rounds.  Scratch: tmask[TT] (uint64),
+// jround[n_jobs] (int).
+template <int NT, int TT>
+__device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, int n_jobs,
+                             uint64_t* tmask, int* jround, int* roff, uint32_t* order,
+                             int* n_rounds) {
+  for (int i = threadIdx.x; i < TT; i += NT) tmask[i] = 0;
+  for (int i = threadIdx.x; i <= 64; i += NT) roff[i] = 0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int rmax = -1;
+    for (int j = 0; j < n_jobs; ++j) {
+      const uint32_t job = jobs[j];
+      const int e0 = (int)(job & 0xffff), cnt = (int)(job >> 16);
+      uint64_t used = 0;
+      for (int i = 0; i < cnt; ++i) used |= tmask[edge_token(keys[e0 + i])];
+      const int r = __builtin_ctzll(~used);
+      for (int i = 0; i < cnt; ++i) tmask[edge_token(keys[e0 + i])] |= 1ull << r;
+      jround[j] = r;
+      roff[r + 1] += 1;
+      rmax = max(rmax, r);
+    }
+    int run = 0;
+    for (int r = 0; r <= rmax; ++r) {
+      run += roff[r + 1];
+      roff[r + 1] = run;
+    }
+    *n_rounds = rmax + 1;
+    // stable placement: position = round offset + number of earlier jobs of that round
+    for (int j = 0; j < n_jobs; ++j) order[roff[jround[j]]++] = jobs[j];
+    for (int r = rmax; r >= 1; --r) roff[r] = roff[r - 1];
+    roff[0] = 0;
+  }
+  __syncthreads();
+}
+
 }  // namespace hsa
