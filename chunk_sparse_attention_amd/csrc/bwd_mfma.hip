@@ -90,9 +90,8 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
   build_jobs<NT>(keys, N, TPJ, scratch, scratch + NMAX, jobs, &n_valid_sh, &n_jobs_sh);
   const int n_jobs = n_jobs_sh;
   uint32_t* order = reinterpret_cast<uint32_t*>(scratch + NMAX);
-  uint64_t* tmask = reinterpret_cast<uint64_t*>(scratch + 2 * NMAX);
-  int* roff = scratch + 2 * NMAX + 2 * TT;
-  build_rounds<NT, TT>(keys, jobs, n_jobs, tmask, scratch, roff, order, &n_rounds_sh);
+  int* roff = scratch + 2 * NMAX;
+  build_rounds<NT>(keys, jobs, n_jobs, scratch, roff, order, &n_rounds_sh);
   const int n_rounds = n_rounds_sh;
 
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -151,8 +150,7 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
       for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = fmaxf(m, sa[t4][i] * c2);
-      m = fmaxf(m, __shfl_xor(m, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      m = rows4_max(m);
       float sum = 0.0f;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
@@ -161,8 +159,7 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
           sa[t4][i] = exp2_fast(sa[t4][i] * c2 - m);
           sum += sa[t4][i];
         }
-      sum += __shfl_xor(sum, 16, 64);
-      sum += __shfl_xor(sum, 32, 64);
+      sum = rows4_sum(sum);
       const float inv = 1.0f / (exp2_fast(-m) + sum);
       float dsum = 0.0f;
 #pragma unroll
@@ -172,8 +169,7 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
           sa[t4][i] *= inv;  // P
           dsum += sa[t4][i] * pa[t4][i];
         }
-      dsum += __shfl_xor(dsum, 16, 64);
-      dsum += __shfl_xor(dsum, 32, 64);  // D of this column
+      dsum = rows4_sum(dsum);  // D of this column
       const float wk = valid ? wsh[tl * 16 + k] : 0.0f;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
@@ -183,9 +179,7 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
 #pragma unroll
       for (int s = 0; s < 2; ++s) sb[s] = pack_bf16x8(sa[2 * s], sa[2 * s + 1]);
       // dw of this edge: sum of D over the token's G head columns (lanes of one slot)
-      float dw = dsum;
-#pragma unroll
-      for (int o = 1; o < G; o <<= 1) dw += __shfl_xor(dw, o, 64);
+      const float dw = group_sum<G>(dsum);
       if (valid && head == 0 && blk == 0) dwsh[tl * 16 + k] = dw;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -341,16 +335,14 @@ __global__ void __launch_bounds__(64) k_bwd_p2_mfma(
       float m = 0.0f;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) m = fmaxf(m, sa[t4][i] * c2);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      m = row16_max(m);
       float sum = 0.0f;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
         sa[t4][i] = exp2_fast(sa[t4][i] * c2 - m);
         sum += sa[t4][i];
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+      sum = row16_sum(sum);
       const float inv = 1.0f / (exp2_fast(-m) + sum);
       float dsum = 0.0f;
 #pragma unroll
@@ -358,8 +350,7 @@ __global__ void __launch_bounds__(64) k_bwd_p2_mfma(
         sa[t4][i] *= inv;
         dsum += sa[t4][i] * pa[t4][i];
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) dsum += __shfl_xor(dsum, o, 64);
+      dsum = row16_sum(dsum);
       float wv = 0.0f;
       if (s < n_here) {
         const int v2 = ent[ej + s];

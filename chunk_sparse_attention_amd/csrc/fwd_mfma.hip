@@ -94,11 +94,10 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
   block_bitonic_sort<NT>(keys, N);
   build_jobs<NT>(keys, N, TPJ, scratch, scratch + NMAX, jobs, &n_valid_sh, &n_jobs_sh);
   const int n_jobs = n_jobs_sh;
-  // 3b. rounds: scratch now holds [jround: NMAX][order: NMAX][tmask: 2*TT][roff: 65]
+  // 3b. rounds: scratch now holds [jround: NMAX][order: NMAX][roff: 65]
   uint32_t* order = reinterpret_cast<uint32_t*>(scratch + NMAX);
-  uint64_t* tmask = reinterpret_cast<uint64_t*>(scratch + 2 * NMAX);
-  int* roff = scratch + 2 * NMAX + 2 * TT;
-  build_rounds<NT, TT>(keys, jobs, n_jobs, tmask, scratch, roff, order, &n_rounds_sh);
+  int* roff = scratch + 2 * NMAX;
+  build_rounds<NT>(keys, jobs, n_jobs, scratch, roff, order, &n_rounds_sh);
   const int n_rounds = n_rounds_sh;
 
   // 4. jobs, a contiguous range per wave.  The loads for job j+1 (its queries and, when its
@@ -232,8 +231,7 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
         s_acc[kt][i] *= c2;
         m = fmaxf(m, s_acc[kt][i]);
       }
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    m = rows4_max(m);
     float sum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -242,8 +240,7 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
         s_acc[kt][i] = exp2_fast(s_acc[kt][i] - m);
         sum += s_acc[kt][i];
       }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
+    sum = rows4_sum(sum);
     const float f = valid_c ? wsh[tl_c * 16 + k_c] / (exp2_fast(-m) + sum) : 0.0f;
     bf16x8 pb[2];
 #pragma unroll

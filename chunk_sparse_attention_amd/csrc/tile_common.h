@@ -95,44 +95,137 @@ __device__ void build_jobs(const uint32_t* keys, int N, int tpj, int* rs, int* t
 
 // Conflict-free rounds.  Jobs of one round touch disjoint tokens, so the waves of a round
 // can update the tile's LDS accumulators with plain read-add-write (LDS float atomics are
-// slow on this part).  Greedy colouring in job order by one thread: a job takes the lowest
-// round none of its tokens is in yet.  A token has at most 16 edges, so with at most 4
-// tokens per job no job needs a round above 4*15 = 60.
-// In: jobs[0..n_jobs), keys.  Out: order[] = jobs grouped by round (job order kept inside
-// a round), roff[0..n_rounds] = round offsets, *n_rounds.  Scratch: tmask[TT] (uint64),
-// jround[n_jobs] (int).
-template <int NT, int TT>
+// slow on this part).  Greedy colouring in job order: a job takes the lowest round none of
+// its tokens is in yet.  A token has at most 16 edges and a job at most 4 tokens, so no job
+// needs a round above 4*15 = 60.  Wave 0 does the colouring with the per-token round masks
+// in registers (lane tl holds token tl's mask) so the sequential loop has no memory latency.
+// In: jobs[0..n_jobs), keys.  Out: order[] = jobs grouped by round (job order kept inside a
+// round), roff[0..n_rounds] = round offsets, *n_rounds.  Scratch: jround[n_jobs] (int).
+template <int NT>
 __device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, int n_jobs,
-                             uint64_t* tmask, int* jround, int* roff, uint32_t* order,
-                             int* n_rounds) {
-  for (int i = threadIdx.x; i < TT; i += NT) tmask[i] = 0;
-  for (int i = threadIdx.x; i <= 64; i += NT) roff[i] = 0;
-  __syncthreads();
-  if (threadIdx.x == 0) {
+                             int* jround, int* roff, uint32_t* order, int* n_rounds) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    uint64_t tmask = 0;   // rounds used by token `lane`
+    uint32_t count = 0;   // jobs in round `lane`
     int rmax = -1;
-    for (int j = 0; j < n_jobs; ++j) {
-      const uint32_t job = jobs[j];
-      const int e0 = (int)(job & 0xffff), cnt = (int)(job >> 16);
-      uint64_t used = 0;
-      for (int i = 0; i < cnt; ++i) used |= tmask[edge_token(keys[e0 + i])];
-      const int r = __builtin_ctzll(~used);
-      for (int i = 0; i < cnt; ++i) tmask[edge_token(keys[e0 + i])] |= 1ull << r;
-      jround[j] = r;
-      roff[r + 1] += 1;
-      rmax = max(rmax, r);
+    for (int jb = 0; jb < n_jobs; jb += 64) {
+      // lane i fetches job jb+i: its tokens packed 6 bits each, count in the top bits
+      uint32_t packed = 0;
+      if (jb + lane < n_jobs) {
+        const uint32_t job = jobs[jb + lane];
+        const int e0 = (int)(job & 0xffff), cnt = (int)(job >> 16);
+        packed = (uint32_t)cnt << 24;
+        for (int i = 0; i < cnt; ++i) packed |= (uint32_t)edge_token(keys[e0 + i]) << (6 * i);
+      }
+      int myr = 0;
+      const int nb = min(64, n_jobs - jb);
+      for (int i = 0; i < nb; ++i) {
+        const uint32_t pk = __builtin_amdgcn_readlane(packed, i);
+        const int cnt = (int)(pk >> 24);
+        uint64_t used = 0;
+        bool mine = false;
+        for (int q = 0; q < cnt; ++q) {
+          const int tl = (int)((pk >> (6 * q)) & 63);
+          used |= ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(tmask >> 32), tl) << 32) |
+                  (uint64_t)__builtin_amdgcn_readlane((uint32_t)tmask, tl);
+          mine |= lane == tl;
+        }
+        const int r = __builtin_ctzll(~used);
+        if (mine) tmask |= 1ull << r;
+        if (lane == r) ++count;
+        if (lane == i) myr = r;
+        rmax = max(rmax, r);
+      }
+      if (jb + lane < n_jobs) jround[jb + lane] = myr;
     }
-    int run = 0;
-    for (int r = 0; r <= rmax; ++r) {
-      run += roff[r + 1];
-      roff[r + 1] = run;
+    // exclusive scan of the round sizes (lane r holds round r's size)
+    uint32_t incl = count;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
     }
-    *n_rounds = rmax + 1;
-    // stable placement: position = round offset + number of earlier jobs of that round
-    for (int j = 0; j < n_jobs; ++j) order[roff[jround[j]]++] = jobs[j];
-    for (int r = rmax; r >= 1; --r) roff[r] = roff[r - 1];
-    roff[0] = 0;
+    uint32_t next = incl - count;  // start of round `lane`, advanced as jobs are placed
+    if (lane <= rmax) roff[lane] = (int)next;
+    if (lane == 0) {
+      roff[rmax + 1] = n_jobs;
+      *n_rounds = rmax + 1;
+    }
+    // stable placement in job order
+    for (int jb = 0; jb < n_jobs; jb += 64) {
+      const int myr = jb + lane < n_jobs ? jround[jb + lane] : 0;
+      const uint32_t myjob = jb + lane < n_jobs ? jobs[jb + lane] : 0u;
+      const int nb = min(64, n_jobs - jb);
+      for (int i = 0; i < nb; ++i) {
+        const int r = __builtin_amdgcn_readlane(myr, i);
+        const uint32_t pos = __builtin_amdgcn_readlane(next, r);
+        if (lane == r) ++next;
+        if (lane == i) order[pos] = myjob;
+      }
+    }
   }
   __syncthreads();
+}
+
+// ---- cross-lane reductions without LDS ----------------------------------------------------
+// Over the 16 lanes of a row (DPP butterfly: xor 1, xor 2, half-row mirror, row mirror).
+template <int CTRL>
+__device__ __forceinline__ float dppc(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dppc<0xB1>(v);
+  v += dppc<0x4E>(v);
+  v += dppc<0x141>(v);
+  v += dppc<0x140>(v);
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dppc<0xB1>(v));
+  v = fmaxf(v, dppc<0x4E>(v));
+  v = fmaxf(v, dppc<0x141>(v));
+  v = fmaxf(v, dppc<0x140>(v));
+  return v;
+}
+// Sum over aligned groups of N lanes inside a row (N = 2, 4, 8 or 16).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if (N >= 2) v += dppc<0xB1>(v);
+  if (N >= 4) v += dppc<0x4E>(v);
+  if (N >= 8) v += dppc<0x141>(v);
+  if (N >= 16) v += dppc<0x140>(v);
+  return v;
+}
+// Across the four 16-lane rows at the same position (lanes l, l^16, l^32, l^48), with the
+// gfx950 row-swap instructions.  Both inputs of a swap are the same value; the empty asm
+// keeps the compiler from treating the two swapped results as one (it folds them otherwise).
+__device__ __forceinline__ void swap16(float v, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  unsigned p0 = p[0], p1 = p[1];
+  asm volatile("" : "+v"(p0), "+v"(p1));
+  a = __builtin_bit_cast(float, p0);
+  b = __builtin_bit_cast(float, p1);
+}
+__device__ __forceinline__ void swap32(float v, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  unsigned p0 = p[0], p1 = p[1];
+  asm volatile("" : "+v"(p0), "+v"(p1));
+  a = __builtin_bit_cast(float, p0);
+  b = __builtin_bit_cast(float, p1);
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  float a, b;
+  swap16(v, a, b);
+  swap32(a + b, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float rows4_max(float v) {
+  float a, b;
+  swap16(v, a, b);
+  swap32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 
 }  // namespace hsa
