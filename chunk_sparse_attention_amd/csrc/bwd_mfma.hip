@@ -42,22 +42,21 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ Kt, const bf16* __restrict__ Kslc, const int32_t* __restrict__ idx,
     const float* __restrict__ score, const float* __restrict__ w, const bf16* __restrict__ dO,
-    bf16* __restrict__ dQ, bf16* __restrict__ dQs, float* __restrict__ ds_out,
-    float* __restrict__ dw_out, int L, int Hq, int Hkv, int Kn, int nC, int BG, float c2,
-    float sm_scale, float sel_scale) {
+    const uint32_t* __restrict__ prep, bf16* __restrict__ dQ, bf16* __restrict__ dQs,
+    float* __restrict__ ds_out, float* __restrict__ dw_out, int L, int Hq, int Hkv, int Kn,
+    int nC, int BG, float c2, float sm_scale, float sel_scale) {
   constexpr int NT = 512, NW = NT / 64;
-  constexpr int TPJ = 16 / G;
   constexpr int DP = D + 1;
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int NMAX = TT * 16;
   __shared__ float acc[TT * G * DP];  // dQ (without the logit scale)
   __shared__ uint32_t keys[NMAX];
-  __shared__ uint32_t jobs[NMAX];     // later: ds per (token, slot)
-  __shared__ int scratch[3 * NMAX];
+  __shared__ uint32_t order[NMAX];    // later: ds per (token, slot)
+  __shared__ int roff[65];
   __shared__ float wsh[TT * 16];
   __shared__ float dwsh[TT * 16];
-  __shared__ int n_valid_sh, n_jobs_sh, n_rounds_sh;
+  __shared__ int hdr[3];
 
   const int bg = blockIdx.x % BG;
   const int tile = blockIdx.x / BG;
@@ -66,33 +65,15 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
   const int t0 = tile * TT;
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
 
-  int N = 1;
-  while (N < TT * Kn) N <<= 1;
-  for (int i = tid; i < N; i += NT) {
-    uint32_t key = kNoEdge;
-    if (i < TT * Kn) {
-      const int tl = i / Kn, k = i % Kn, t = t0 + tl;
-      if (t < L) {
-        const size_t o = ((b * L + t) * Hkv + g) * Kn + k;
-        const int c = idx[o];
-        if (c >= 0 && c < nC) {
-          key = edge_key(c, tl, k);
-          wsh[tl * 16 + k] = w[o];
-        }
-      }
-    }
-    keys[i] = key;
+  load_prep<NT, TT>(prep + (size_t)blockIdx.x * prep_words(TT), keys, order, roff, hdr);
+  for (int i = tid; i < TT * Kn; i += NT) {
+    const int tl = i / Kn, k = i % Kn, t = t0 + tl;
+    if (t < L) wsh[tl * 16 + k] = w[((b * L + t) * Hkv + g) * Kn + k];
   }
   for (int i = tid; i < TT * 16; i += NT) dwsh[i] = 0.0f;
   for (int i = tid; i < TT * G * DP; i += NT) acc[i] = 0.0f;
   __syncthreads();
-  block_bitonic_sort<NT>(keys, N);
-  build_jobs<NT>(keys, N, TPJ, scratch, scratch + NMAX, jobs, &n_valid_sh, &n_jobs_sh);
-  const int n_jobs = n_jobs_sh;
-  uint32_t* order = reinterpret_cast<uint32_t*>(scratch + NMAX);
-  int* roff = scratch + 2 * NMAX;
-  build_rounds<NT>(keys, jobs, n_jobs, scratch, roff, order, &n_rounds_sh);
-  const int n_rounds = n_rounds_sh;
+  const int n_rounds = hdr[2];
 
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int col = lane % 16, blk = lane / 16;
@@ -197,7 +178,7 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
   }
 
   // per token: ds by the stick-breaking chain rule (newest slot first)
-  float* dssh = reinterpret_cast<float*>(jobs);
+  float* dssh = reinterpret_cast<float*>(order);
   if (tid < TT) {
     const int tl = tid, t = t0 + tl;
     if (t < L) {
@@ -422,7 +403,8 @@ static void launch_p1(const Dims& d, const BwdLayout& lay, const void* Q, const 
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);
   k_bwd_p1_tile<D, TT, G><<<dim3(BG * n_tiles), 512, 0, s>>>(
       (const bf16*)Q, (const bf16*)K, (const bf16*)V, (const bf16*)(ws + lay.kt),
-      (const bf16*)Kslc, idx, score, w, (const bf16*)dO, (bf16*)dQ, (bf16*)dQs,
+      (const bf16*)Kslc, idx, score, w, (const bf16*)dO, (const uint32_t*)(ws + lay.prep),
+      (bf16*)dQ, (bf16*)dQs,
       (float*)(ws + lay.ds), (float*)(ws + lay.dw), d.L, d.Hq, d.Hkv, d.K, d.nC, BG, c2,
       (float)d.sm_scale, (float)d.sel_scale);
 }
@@ -447,6 +429,7 @@ hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, c
   if (e != hipSuccess) return e;
   const int BG = d.B * d.Hkv;
   launch_prep_transpose(d, K, ws + lay.kt, s);
+  launch_tile_prep(d, idx, ws + lay.prep, s);
   if (d.D == 64)
     launch_p1_g<64, 64>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
   else

@@ -47,20 +47,20 @@ __global__ void __launch_bounds__(256) k_prep_vt(const bf16* __restrict__ V, bf1
 template <int D, int TT, int G>
 __global__ void __launch_bounds__(512) k_fwd_tile(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
-    const int32_t* __restrict__ idx, const float* __restrict__ w, bf16* __restrict__ O, int L,
-    int Hq, int Hkv, int Kt, int nC, int BG, float c2) {
+    const int32_t* __restrict__ idx, const float* __restrict__ w,
+    const uint32_t* __restrict__ prep, bf16* __restrict__ O, int L, int Hq, int Hkv, int Kt,
+    int nC, int BG, float c2) {
   constexpr int NT = 512, NW = NT / 64;
-  constexpr int TPJ = 16 / G;  // tokens per 16-column job
   constexpr int DP = D + 1;    // padded accumulator row
   constexpr int KS = D / 32;   // k-steps of S^T
   constexpr int DT = D / 16;   // d-tiles of O^T
   constexpr int NMAX = TT * 16;
   __shared__ float acc[TT * G * DP];
   __shared__ uint32_t keys[NMAX];
-  __shared__ uint32_t jobs[NMAX];
-  __shared__ int scratch[3 * NMAX];
+  __shared__ uint32_t order[NMAX];
+  __shared__ int roff[65];
   __shared__ float wsh[TT * 16];
-  __shared__ int n_valid_sh, n_jobs_sh, n_rounds_sh;
+  __shared__ int hdr[3];
 
   const int bg = blockIdx.x % BG;  // consecutive blocks: different (b, g), XCD-interleaved
   const int tile = blockIdx.x / BG;
@@ -69,40 +69,16 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
   const int t0 = tile * TT;
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
 
-  // 1. edges of the tile, weights, zeroed accumulators
-  int N = 1;
-  while (N < TT * Kt) N <<= 1;
-  for (int i = tid; i < N; i += NT) {
-    uint32_t key = kNoEdge;
-    if (i < TT * Kt) {
-      const int tl = i / Kt, k = i % Kt, t = t0 + tl;
-      if (t < L) {
-        const size_t o = ((b * L + t) * Hkv + g) * Kt + k;
-        const int c = idx[o];
-        if (c >= 0 && c < nC) {
-          key = edge_key(c, tl, k);
-          wsh[tl * 16 + k] = w[o];
-        }
-      }
-    }
-    keys[i] = key;
+  // 1. the tile's prepared edges, jobs and rounds; weights; zeroed accumulators
+  load_prep<NT, TT>(prep + (size_t)blockIdx.x * prep_words(TT), keys, order, roff, hdr);
+  for (int i = tid; i < TT * Kt; i += NT) {
+    const int tl = i / Kt, k = i % Kt, t = t0 + tl;
+    if (t < L) wsh[tl * 16 + k] = w[((b * L + t) * Hkv + g) * Kt + k];
   }
   for (int i = tid; i < TT * G * DP; i += NT) acc[i] = 0.0f;
   __syncthreads();
+  const int n_rounds = hdr[2];
 
-  // 2. group by chunk, 3. jobs
-  block_bitonic_sort<NT>(keys, N);
-  build_jobs<NT>(keys, N, TPJ, scratch, scratch + NMAX, jobs, &n_valid_sh, &n_jobs_sh);
-  const int n_jobs = n_jobs_sh;
-  // 3b. rounds: scratch now holds [jround: NMAX][order: NMAX][roff: 65]
-  uint32_t* order = reinterpret_cast<uint32_t*>(scratch + NMAX);
-  int* roff = scratch + 2 * NMAX;
-  build_rounds<NT>(keys, jobs, n_jobs, scratch, roff, order, &n_rounds_sh);
-  const int n_rounds = n_rounds_sh;
-
-  // 4. jobs, a contiguous range per wave.  The loads for job j+1 (its queries and, when its
-  //    chunk differs, the chunk's keys -- and values for D=64, where registers allow) are
-  //    issued before job j is computed, so their latency overlaps job j's matrix work.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   // this wave's share of round r: [rb(r), re(r))
   auto rb = [&](int r) {
@@ -273,24 +249,50 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
   }
 }
 
+int tile_tokens(const Dims& d) { return (d.D == 64 ? 64 : 32) / (d.G == 16 ? 2 : 1); }
+
+size_t tile_prep_bytes(const Dims& d) {
+  const int tt = tile_tokens(d);
+  const size_t tiles = (size_t)d.B * d.Hkv * ((d.L + tt - 1) / tt);
+  return (tiles * prep_words(tt) * sizeof(uint32_t) + 255) & ~(size_t)255;
+}
+
+template <int TT>
+static void launch_prep_tt(const Dims& d, const int32_t* idx, uint32_t* prep, hipStream_t s) {
+  const int BG = d.B * d.Hkv;
+  const int n_tiles = (d.L + TT - 1) / TT;
+  k_tile_prep<256, TT><<<dim3(BG * n_tiles), 256, 0, s>>>(idx, prep, d.L, d.Hkv, d.K, d.nC, BG,
+                                                          16 / d.G);
+}
+
+void launch_tile_prep(const Dims& d, const int32_t* idx, void* prep, hipStream_t s) {
+  switch (tile_tokens(d)) {
+    case 64: launch_prep_tt<64>(d, idx, (uint32_t*)prep, s); break;
+    case 32: launch_prep_tt<32>(d, idx, (uint32_t*)prep, s); break;
+    default: launch_prep_tt<16>(d, idx, (uint32_t*)prep, s); break;
+  }
+}
+
 template <int D, int TT, int G>
 static void launch_fwd_tile(const Dims& d, const void* Q, const void* K, const void* Vt,
-                            const int32_t* idx, const float* w, void* O, hipStream_t s) {
+                            const int32_t* idx, const float* w, const void* prep, void* O,
+                            hipStream_t s) {
   const int BG = d.B * d.Hkv;
   const int n_tiles = (d.L + TT - 1) / TT;
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);  // logit scale * log2(e)
   k_fwd_tile<D, TT, G><<<dim3(BG * n_tiles), 512, 0, s>>>(
-      (const bf16*)Q, (const bf16*)K, (const bf16*)Vt, idx, w, (bf16*)O, d.L, d.Hq, d.Hkv, d.K,
-      d.nC, BG, c2);
+      (const bf16*)Q, (const bf16*)K, (const bf16*)Vt, idx, w, (const uint32_t*)prep, (bf16*)O,
+      d.L, d.Hq, d.Hkv, d.K, d.nC, BG, c2);
 }
 
 template <int D, int TT>
 static bool launch_fwd_tile_g(const Dims& d, const void* Q, const void* K, const void* Vt,
-                              const int32_t* idx, const float* w, void* O, hipStream_t s) {
+                              const int32_t* idx, const float* w, const void* prep, void* O,
+                              hipStream_t s) {
   switch (d.G) {
-    case 4: launch_fwd_tile<D, TT, 4>(d, Q, K, Vt, idx, w, O, s); return true;
-    case 8: launch_fwd_tile<D, TT, 8>(d, Q, K, Vt, idx, w, O, s); return true;
-    case 16: launch_fwd_tile<D, TT / 2, 16>(d, Q, K, Vt, idx, w, O, s); return true;
+    case 4: launch_fwd_tile<D, TT, 4>(d, Q, K, Vt, idx, w, prep, O, s); return true;
+    case 8: launch_fwd_tile<D, TT, 8>(d, Q, K, Vt, idx, w, prep, O, s); return true;
+    case 16: launch_fwd_tile<D, TT / 2, 16>(d, Q, K, Vt, idx, w, prep, O, s); return true;
   }
   return false;
 }
@@ -301,9 +303,11 @@ bool fwd_mfma_supported(const Dims& d) {
          !(d.flags & 1u);
 }
 
-size_t fwd_mfma_ws(const Dims& d) {
+static size_t vt_bytes(const Dims& d) {
   return ((size_t)d.B * d.Hkv * d.nC * 64 * d.D * sizeof(uint16_t) + 255) & ~(size_t)255;
 }
+
+size_t fwd_mfma_ws(const Dims& d) { return vt_bytes(d) + tile_prep_bytes(d); }
 
 void launch_prep_transpose(const Dims& d, const void* src, void* dst, hipStream_t s) {
   if (d.nC > 0)
@@ -316,10 +320,12 @@ hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const vo
   const int BG = d.B * d.Hkv;
   if (d.nC > 0)
     k_prep_vt<<<dim3(BG * d.nC), 256, 0, s>>>((const bf16*)V, (bf16*)ws, d.L, d.Hkv, d.D, d.nC);
+  char* prep = ws + vt_bytes(d);
+  launch_tile_prep(d, idx, prep, s);
   if (d.D == 64)
-    launch_fwd_tile_g<64, 64>(d, Q, K, ws, idx, w, O, s);
+    launch_fwd_tile_g<64, 64>(d, Q, K, ws, idx, w, prep, O, s);
   else
-    launch_fwd_tile_g<128, 32>(d, Q, K, ws, idx, w, O, s);
+    launch_fwd_tile_g<128, 32>(d, Q, K, ws, idx, w, prep, O, s);
   return hipGetLastError();
 }
 

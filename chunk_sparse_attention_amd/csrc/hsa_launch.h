@@ -24,7 +24,7 @@ struct BwdLayout {
   int seg;          // entries per backward-phase-2 segment
   int64_t max_seg;  // segment capacity per (b, g)
   size_t ds, dw, tile_counts, tile_base, offsets, entries, seg_start, seg_chunk, n_seg,
-      part_dk, part_dv, part_dks, kt, total;
+      part_dk, part_dv, part_dks, kt, prep, total;
 };
 BwdLayout bwd_layout(const Dims& d);
 
@@ -61,6 +61,10 @@ hipError_t launch_bwd_reduce(const Dims& d, const BwdLayout& lay, void* dK, void
 // Per-chunk transpose used by the matrix-core kernels:
 // dst[((b*Hkv+g)*nC + c)*D*64 + d*64 + p] = src[b, 64c + perm_key(p), g, d].
 void launch_prep_transpose(const Dims& d, const void* src, void* dst, hipStream_t s);
+// Token tiles of the matrix-core kernels: tokens per tile, and the prepared job lists.
+int tile_tokens(const Dims& d);
+size_t tile_prep_bytes(const Dims& d);
+void launch_tile_prep(const Dims& d, const int32_t* idx, void* prep, hipStream_t s);
 bool bwd_mfma_supported(const Dims& d);
 hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
                            const void* V, const void* Qs, const void* Kslc, const int32_t* idx,

@@ -167,6 +167,72 @@ __device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, int n_j
   __syncthreads();
 }
 
+// ---- prepared tiles ------------------------------------------------------------------------
+// A tile-prep kernel sorts each tile's edges, builds its jobs and colours them into rounds,
+// and stores the result; the attention kernels then only copy it into LDS.  Per tile:
+//   [0] n_valid, [1] n_jobs, [2] n_rounds, [3..3+65) round offsets,
+//   [68 .. 68+TT*16) sorted edge keys, [68+TT*16 .. 68+2*TT*16) jobs grouped by round.
+__host__ __device__ constexpr int prep_words(int tt) { return 68 + 2 * tt * 16; }
+
+template <int NT, int TT>
+__global__ void __launch_bounds__(NT) k_tile_prep(const int32_t* __restrict__ idx,
+                                                  uint32_t* __restrict__ prep, int L, int Hkv,
+                                                  int Kt, int nC, int BG, int tpj) {
+  constexpr int NMAX = TT * 16;
+  __shared__ uint32_t keys[NMAX];
+  __shared__ uint32_t jobs[NMAX];
+  __shared__ int scratch[3 * NMAX];
+  __shared__ int n_valid_sh, n_jobs_sh, n_rounds_sh;
+  const int bg = blockIdx.x % BG;
+  const int tile = blockIdx.x / BG;
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const int t0 = tile * TT;
+  int N = 1;
+  while (N < TT * Kt) N <<= 1;
+  for (int i = threadIdx.x; i < N; i += NT) {
+    uint32_t key = kNoEdge;
+    if (i < TT * Kt) {
+      const int tl = i / Kt, k = i % Kt, t = t0 + tl;
+      if (t < L) {
+        const int c = idx[((b * L + t) * Hkv + g) * Kt + k];
+        if (c >= 0 && c < nC) key = edge_key(c, tl, k);
+      }
+    }
+    keys[i] = key;
+  }
+  __syncthreads();
+  block_bitonic_sort<NT>(keys, N);
+  build_jobs<NT>(keys, N, tpj, scratch, scratch + NMAX, jobs, &n_valid_sh, &n_jobs_sh);
+  const int n_jobs = n_jobs_sh;
+  uint32_t* order = reinterpret_cast<uint32_t*>(scratch + NMAX);
+  int* roff = scratch + 2 * NMAX;
+  build_rounds<NT>(keys, jobs, n_jobs, scratch, roff, order, &n_rounds_sh);
+  uint32_t* out = prep + (size_t)blockIdx.x * prep_words(TT);
+  const int nv = n_valid_sh, nr = n_rounds_sh;
+  if (threadIdx.x == 0) {
+    out[0] = (uint32_t)nv;
+    out[1] = (uint32_t)n_jobs;
+    out[2] = (uint32_t)nr;
+  }
+  for (int i = threadIdx.x; i <= nr; i += NT) out[3 + i] = (uint32_t)roff[i];
+  for (int i = threadIdx.x; i < nv; i += NT) out[68 + i] = keys[i];
+  for (int i = threadIdx.x; i < n_jobs; i += NT) out[68 + NMAX + i] = order[i];
+}
+
+// Copy a prepared tile into LDS; returns n_jobs and n_rounds through the pointers (uniform).
+template <int NT, int TT>
+__device__ void load_prep(const uint32_t* __restrict__ src, uint32_t* keys, uint32_t* order,
+                          int* roff, int* hdr) {
+  constexpr int NMAX = TT * 16;
+  if (threadIdx.x < 3) hdr[threadIdx.x] = (int)src[threadIdx.x];
+  __syncthreads();
+  const int nv = hdr[0], nj = hdr[1], nr = hdr[2];
+  for (int i = threadIdx.x; i <= nr; i += NT) roff[i] = (int)src[3 + i];
+  for (int i = threadIdx.x; i < nv; i += NT) keys[i] = src[68 + i];
+  for (int i = threadIdx.x; i < nj; i += NT) order[i] = src[68 + NMAX + i];
+}
+
 // ---- cross-lane reductions without LDS ----------------------------------------------------
 // Over the 16 lanes of a row (DPP butterfly: xor 1, xor 2, half-row mirror, row mirror).
 template <int CTRL>
