@@ -233,7 +233,8 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
 // in LDS; a job takes 16/G selectors (16 query rows).  dK^T and dV^T accumulate in registers
 // (MFMA accumulators) for the whole segment.
 template <int G>
-__global__ void __launch_bounds__(64) k_bwd_p2_mfma(
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+k_bwd_p2_mfma(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ Qs, const float* __restrict__ w, const bf16* __restrict__ dO,
     const float* __restrict__ ds_in, const int32_t* __restrict__ offsets,
@@ -243,10 +244,13 @@ __global__ void __launch_bounds__(64) k_bwd_p2_mfma(
     int L, int Hq, int Hkv, int Kn, int nC, int seg, int64_t max_seg, float c2, float sm_scale,
     float sel_scale) {
   constexpr int D = 64, TPJ = 16 / G, KS = D / 32, DT = D / 16;
+  constexpr int SEGMAX = 128;
   __shared__ __attribute__((aligned(16))) uint16_t kl[64][D + 8];
   __shared__ __attribute__((aligned(16))) uint16_t vl[64][D + 8];
   __shared__ __attribute__((aligned(16))) uint16_t ql[16][D + 8];
   __shared__ __attribute__((aligned(16))) uint16_t dl[16][D + 8];
+  __shared__ int tok_l[SEGMAX];
+  __shared__ float w_l[SEGMAX], ds_l[SEGMAX];
   const int64_t sidx = blockIdx.x % max_seg;
   const int bg = (int)(blockIdx.x / max_seg);
   if (sidx >= n_seg[bg]) return;  // whole wave
@@ -256,11 +260,20 @@ __global__ void __launch_bounds__(64) k_bwd_p2_mfma(
   const int32_t* off = offsets + (size_t)bg * (nC + 1);
   const int32_t* ss = seg_start + (size_t)bg * (nC + 1);
   const int e0 = off[c] + (int)(sidx - ss[c]) * seg;
-  const int e1 = min(off[c + 1], e0 + seg);
-  const int32_t* ent = entries + (size_t)bg * L * Kn;
+  const int ne = min(off[c + 1], e0 + seg) - e0;  // <= seg <= SEGMAX
+  const int32_t* ent = entries + (size_t)bg * L * Kn + e0;
   const int lane = threadIdx.x, col = lane % 16, blk = lane / 16;
   const size_t kvrow = (size_t)Hkv * D;
   const size_t cb = ((b * L + (size_t)c * 64) * Hkv + g) * D;
+  // the segment's selectors: token, weight, score gradient (one gather per entry)
+  for (int i = lane; i < ne; i += 64) {
+    const int val = ent[i];
+    const int t = val / Kn, k = val % Kn;
+    const size_t o = ((b * L + t) * Hkv + g) * Kn + k;
+    tok_l[i] = t;
+    w_l[i] = w[o];
+    ds_l[i] = ds_in[o];
+  }
   for (int i = lane; i < 64 * (D / 8); i += 64) {
     const int key = i / (D / 8), d = (i % (D / 8)) * 8;
     *reinterpret_cast<uint4*>(&kl[key][d]) = *reinterpret_cast<const uint4*>(K + cb + key * kvrow + d);
@@ -278,18 +291,45 @@ __global__ void __launch_bounds__(64) k_bwd_p2_mfma(
   const int qs_sel = col / G, qs_head = col % G;  // this lane's A-operand row -> selector, head
   __syncthreads();
 
-  for (int ej = e0; ej < e1; ej += TPJ) {
-    const int n_here = min(TPJ, e1 - ej);
-    // this lane's query row (A operand): selector qs_sel of the job
-    const int my_sel = qs_sel < n_here ? qs_sel : 0;
-    const int val = ent[ej + my_sel];
-    const int t = val / Kn;
+  // this lane's query row of job j (a padding row repeats the job's first selector)
+  auto load_rows = [&](int ej, bf16x8 (&qa)[KS], bf16x8 (&da)[KS]) {
+    const int n_here = min(TPJ, ne - ej);
+    const int t = tok_l[ej + (qs_sel < n_here ? qs_sel : 0)];
     const size_t qoff = ((b * L + t) * Hq + (size_t)g * G + qs_head) * D;
-    bf16x8 qa[KS], da[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qa[ks] = ld_bf16x8(Q + qoff + 32 * ks + 8 * blk);
       da[ks] = ld_bf16x8(dO + qoff + 32 * ks + 8 * blk);
+    }
+  };
+  bf16x8 qn[KS], dn[KS];
+  float qsn = 0.0f;  // Qs of the next job's selectors, summed with their ds
+  auto load_qs = [&](int ej) {
+    float a = 0.0f;
+    const int n_here = min(TPJ, ne - ej);
+    for (int s2 = 0; s2 < n_here; ++s2)
+      a += ds_l[ej + s2] * to_f32(Qs[((b * L + tok_l[ej + s2]) * Hkv + g) * D + lane]);
+    return a;
+  };
+  if (ne > 0) {
+    load_rows(0, qn, dn);
+    qsn = load_qs(0);
+  }
+  for (int ej = 0; ej < ne; ej += TPJ) {
+    const int n_here = min(TPJ, ne - ej);
+    bf16x8 qa[KS], da[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qa[ks] = qn[ks];
+      da[ks] = dn[ks];
+    }
+    dks += qsn;
+    if (ej + TPJ < ne) {
+      load_rows(ej + TPJ, qn, dn);
+      qsn = load_qs(ej + TPJ);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
       *reinterpret_cast<bf16x8*>(&ql[col][32 * ks + 8 * blk]) = qa[ks];
       *reinterpret_cast<bf16x8*>(&dl[col][32 * ks + 8 * blk]) = da[ks];
     }
@@ -332,12 +372,7 @@ __global__ void __launch_bounds__(64) k_bwd_p2_mfma(
         dsum += sa[t4][i] * pa[t4][i];
       }
       dsum = row16_sum(dsum);
-      float wv = 0.0f;
-      if (s < n_here) {
-        const int v2 = ent[ej + s];
-        wv = w[((b * L + v2 / Kn) * Hkv + g) * Kn + v2 % Kn];
-      }
-      wr[i] = wv;
+      wr[i] = s < n_here ? w_l[ej + s] : 0.0f;
       dr[i] = dsum;
     }
     // dV^T += dO^T (w P), dK^T += Q^T dS  (k = the 16 query rows, 4 per lane block)
@@ -367,12 +402,6 @@ __global__ void __launch_bounds__(64) k_bwd_p2_mfma(
         dv[dt][t4] = mfma_16x16x16(doT[dt], wpb, dv[dt][t4]);
         dk[dt][t4] = mfma_16x16x16(qT[dt], dsb, dk[dt][t4]);
       }
-    }
-    // dKslc += ds * Qs for each selector of the job (lane = dimension)
-    for (int s = 0; s < n_here; ++s) {
-      const int v2 = ent[ej + s];
-      const size_t srow = (b * L + v2 / Kn) * Hkv + g;
-      dks += ds_in[srow * Kn + v2 % Kn] * to_f32(Qs[srow * D + lane]);
     }
     __syncthreads();  // ql/dl reuse by the next job
   }
