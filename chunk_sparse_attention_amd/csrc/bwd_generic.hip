@@ -43,6 +43,8 @@ BwdLayout bwd_layout(const Dims& d) {
   l.part_dv = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
   l.part_dks = take(sizeof(float) * bg * l.max_seg * d.D);
   l.kt = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
+  l.kop = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
+  l.vop = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
   l.prep = take(tile_prep_bytes(d));
   l.total = o;
   return l;

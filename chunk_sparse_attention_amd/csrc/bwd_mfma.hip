@@ -39,7 +39,7 @@ __device__ __forceinline__ s16x4 pack_bf16x4(f32x4 v) {
 
 template <int D, int TT, int G>
 __global__ void __launch_bounds__(512) k_bwd_p1_tile(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ Q, const bf16* __restrict__ Kop, const bf16* __restrict__ Vop,
     const bf16* __restrict__ Kt, const bf16* __restrict__ Kslc, const int32_t* __restrict__ idx,
     const float* __restrict__ score, const float* __restrict__ w, const bf16* __restrict__ dO,
     const uint32_t* __restrict__ prep, bf16* __restrict__ dQ, bf16* __restrict__ dQs,
@@ -78,7 +78,6 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int col = lane % 16, blk = lane / 16;
   const int slot = col / G, head = col % G;
-  const size_t kvrow = (size_t)Hkv * D;
   bf16x8 ka[4][KS], vr[4][KS], kt[DT][2];
   int cur = -1;
   for (int r = 0; r < n_rounds; ++r) {
@@ -100,20 +99,18 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
       }
       if (c != cur) {
         cur = c;
-        const size_t cb = ((b * L + (size_t)c * 64) * Hkv + g) * D;
+        const size_t co = ((size_t)bg * nC + c) * D * 64 + lane * 8;
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            ka[t4][ks] = ld_bf16x8(K + cb + (size_t)(16 * t4 + col) * kvrow + 32 * ks + 8 * blk);
-            vr[t4][ks] = ld_bf16x8(V + cb + (size_t)(16 * t4 + col) * kvrow + 32 * ks + 8 * blk);
+            ka[t4][ks] = ld_bf16x8(Kop + co + (t4 * KS + ks) * 512);
+            vr[t4][ks] = ld_bf16x8(Vop + co + (t4 * KS + ks) * 512);
           }
-        const bf16* kc = Kt + ((size_t)bg * nC + c) * D * 64;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int s = 0; s < 2; ++s)
-            kt[dt][s] = ld_bf16x8(kc + (size_t)(16 * dt + col) * 64 + 32 * s + 8 * blk);
+          for (int s = 0; s < 2; ++s) kt[dt][s] = ld_bf16x8(Kt + co + (dt * 2 + s) * 512);
       }
       f32x4 sa[4], pa[4];
 #pragma unroll
@@ -431,7 +428,8 @@ static void launch_p1(const Dims& d, const BwdLayout& lay, const void* Q, const 
   const int n_tiles = (d.L + TT - 1) / TT;
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);
   k_bwd_p1_tile<D, TT, G><<<dim3(BG * n_tiles), 512, 0, s>>>(
-      (const bf16*)Q, (const bf16*)K, (const bf16*)V, (const bf16*)(ws + lay.kt),
+      (const bf16*)Q, (const bf16*)(ws + lay.kop), (const bf16*)(ws + lay.vop),
+      (const bf16*)(ws + lay.kt),
       (const bf16*)Kslc, idx, score, w, (const bf16*)dO, (const uint32_t*)(ws + lay.prep),
       (bf16*)dQ, (bf16*)dQs,
       (float*)(ws + lay.ds), (float*)(ws + lay.dw), d.L, d.Hq, d.Hkv, d.K, d.nC, BG, c2,
@@ -457,7 +455,9 @@ hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, c
   hipError_t e = launch_invidx(d, lay, idx, ws, s);
   if (e != hipSuccess) return e;
   const int BG = d.B * d.Hkv;
-  launch_prep_transpose(d, K, ws + lay.kt, s);
+  launch_prep_ops(d, K, ws + lay.kt, true, s);
+  launch_prep_ops(d, K, ws + lay.kop, false, s);
+  launch_prep_ops(d, V, ws + lay.vop, false, s);
   launch_tile_prep(d, idx, ws + lay.prep, s);
   if (d.D == 64)
     launch_p1_g<64, 64>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);

@@ -22,31 +22,47 @@
 
 namespace hsa {
 
-// Vt[((b*Hkv+g)*nC + c)*D*64 + d*64 + p] = V[b, 64c + perm_key(p), g, d]: each chunk's values
-// transposed, keys in the order the P.V contraction consumes them.
-__global__ void __launch_bounds__(256) k_prep_vt(const bf16* __restrict__ V, bf16* __restrict__ Vt,
-                                                 int L, int Hkv, int D, int nC) {
-  __shared__ uint16_t tile[64][129];
+// Chunk operands in the order one wave's MFMA operand loads consume them, so every load is
+// one contiguous 1 KB block (64 lanes x 16 bytes) per chunk, tile and step.
+//   ROWS (A operand [key x d], for S^T = K Q^T or dP^T = V dO^T), per chunk:
+//     out[((t4 * (D/32) + ks) * 64 + lane) * 8 + e] = src[16*t4 + lane%16][32*ks + 8*(lane/16) + e]
+//   TRANS (A operand [d x key], for O^T = V^T P^T or dQ^T = K^T dS^T), per chunk:
+//     out[((dt * 2 + s) * 64 + lane) * 8 + e] = src[perm_key(s, lane/16, e)][16*dt + lane%16]
+// src is one KV group of a [B, L, Hkv, D] tensor; out is [B*Hkv][nC][64*D].
+template <bool TRANS>
+__global__ void __launch_bounds__(256) k_prep_ops(const bf16* __restrict__ src, bf16* __restrict__ out,
+                                                  int L, int Hkv, int D, int nC) {
+  __shared__ uint16_t tile[64][136];
   const int c = blockIdx.x % nC;
   const int bg = blockIdx.x / nC;
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
-  const bf16* src = V + ((b * L + (size_t)c * 64) * Hkv + g) * D;
-  for (int i = threadIdx.x; i < 64 * D; i += 256) {
-    int key = i / D, d = i % D;
-    tile[key][d] = src[(size_t)key * Hkv * D + d].bits;
+  const bf16* s0 = src + ((b * L + (size_t)c * 64) * Hkv + g) * D;
+  for (int i = threadIdx.x; i < 64 * D / 8; i += 256) {
+    const int key = i / (D / 8), d = (i % (D / 8)) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(s0 + (size_t)key * Hkv * D + d);
+    *reinterpret_cast<uint4*>(&tile[key][d]) = v;
   }
   __syncthreads();
-  bf16* dst = Vt + ((size_t)bg * nC + c) * D * 64;
+  bf16* dst = out + ((size_t)bg * nC + c) * 64 * D;
   for (int i = threadIdx.x; i < 64 * D; i += 256) {
-    int d = i / 64, p = i % 64;
-    dst[i].bits = tile[perm_key(p / 32, (p / 8) % 4, p % 8)][d];
+    const int e = i % 8, lane = (i / 8) % 64, step = i / 512;  // step = t4*KS+ks or dt*2+s
+    const int col = lane % 16, blk = lane / 16;
+    uint16_t v;
+    if (!TRANS) {
+      const int ks_n = D / 32, t4 = step / ks_n, ks = step % ks_n;
+      v = tile[16 * t4 + col][32 * ks + 8 * blk + e];
+    } else {
+      const int dt = step / 2, s = step % 2;
+      v = tile[perm_key(s, blk, e)][16 * dt + col];
+    }
+    dst[i].bits = v;
   }
 }
 
 template <int D, int TT, int G>
 __global__ void __launch_bounds__(512) k_fwd_tile(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
+    const bf16* __restrict__ Q, const bf16* __restrict__ Kop, const bf16* __restrict__ Vt,
     const int32_t* __restrict__ idx, const float* __restrict__ w,
     const uint32_t* __restrict__ prep, bf16* __restrict__ O, int L, int Hq, int Hkv, int Kt,
     int nC, int BG, float c2) {
@@ -106,26 +122,23 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
   bf16x8 qb[KS], qn[KS];                 // Q^T columns (B operand of S^T): current, next
   int tl_c = 0, k_c = 0, tl_n = 0, k_n = 0;
   bool valid_c = false, valid_n = false;
-  const size_t kvrow = (size_t)Hkv * D;
 
   auto chunk_of = [&](int j) {
     return __builtin_amdgcn_readfirstlane(edge_chunk(keys[order[j] & 0xffff]));
   };
   auto load_k = [&](bf16x8 (&dst)[4][KS], int c) {
-    const bf16* kc = K + ((b * L + (size_t)c * 64) * Hkv + g) * D;
+    const bf16* kc = Kop + ((size_t)bg * nC + c) * D * 64 + lane * 8;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        dst[kt][ks] = ld_bf16x8(kc + (size_t)(16 * kt + col) * kvrow + 32 * ks + 8 * blk);
+      for (int ks = 0; ks < KS; ++ks) dst[kt][ks] = ld_bf16x8(kc + (kt * KS + ks) * 512);
   };
   auto load_v = [&](bf16x8 (&dst)[DT][2], int c) {
-    const bf16* vt = Vt + ((size_t)bg * nC + c) * D * 64;
+    const bf16* vt = Vt + ((size_t)bg * nC + c) * D * 64 + lane * 8;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-        dst[dt][s] = ld_bf16x8(vt + (size_t)(16 * dt + col) * 64 + 32 * s + 8 * blk);
+      for (int s = 0; s < 2; ++s) dst[dt][s] = ld_bf16x8(vt + (dt * 2 + s) * 512);
   };
   auto load_q = [&](bf16x8 (&dst)[KS], int j, int& tl, int& k, bool& valid) {
     const uint32_t job = __builtin_amdgcn_readfirstlane(order[j]);
@@ -303,29 +316,33 @@ bool fwd_mfma_supported(const Dims& d) {
          !(d.flags & 1u);
 }
 
-static size_t vt_bytes(const Dims& d) {
-  return ((size_t)d.B * d.Hkv * d.nC * 64 * d.D * sizeof(uint16_t) + 255) & ~(size_t)255;
+size_t fwd_mfma_ws(const Dims& d) { return 2 * chunk_ops_bytes(d) + tile_prep_bytes(d); }
+
+void launch_prep_ops(const Dims& d, const void* src, void* dst, bool trans, hipStream_t s) {
+  if (d.nC == 0) return;
+  dim3 grid(d.B * d.Hkv * d.nC);
+  if (trans)
+    k_prep_ops<true><<<grid, 256, 0, s>>>((const bf16*)src, (bf16*)dst, d.L, d.Hkv, d.D, d.nC);
+  else
+    k_prep_ops<false><<<grid, 256, 0, s>>>((const bf16*)src, (bf16*)dst, d.L, d.Hkv, d.D, d.nC);
 }
 
-size_t fwd_mfma_ws(const Dims& d) { return vt_bytes(d) + tile_prep_bytes(d); }
-
-void launch_prep_transpose(const Dims& d, const void* src, void* dst, hipStream_t s) {
-  if (d.nC > 0)
-    k_prep_vt<<<dim3(d.B * d.Hkv * d.nC), 256, 0, s>>>((const bf16*)src, (bf16*)dst, d.L, d.Hkv,
-                                                       d.D, d.nC);
+size_t chunk_ops_bytes(const Dims& d) {
+  return ((size_t)d.B * d.Hkv * d.nC * 64 * d.D * sizeof(uint16_t) + 255) & ~(size_t)255;
 }
 
 hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,
                            const int32_t* idx, const float* w, void* O, char* ws, hipStream_t s) {
-  const int BG = d.B * d.Hkv;
-  if (d.nC > 0)
-    k_prep_vt<<<dim3(BG * d.nC), 256, 0, s>>>((const bf16*)V, (bf16*)ws, d.L, d.Hkv, d.D, d.nC);
-  char* prep = ws + vt_bytes(d);
+  char* kop = ws;
+  char* vt = ws + chunk_ops_bytes(d);
+  char* prep = ws + 2 * chunk_ops_bytes(d);
+  launch_prep_ops(d, K, kop, false, s);
+  launch_prep_ops(d, V, vt, true, s);
   launch_tile_prep(d, idx, prep, s);
   if (d.D == 64)
-    launch_fwd_tile_g<64, 64>(d, Q, K, ws, idx, w, prep, O, s);
+    launch_fwd_tile_g<64, 64>(d, Q, kop, vt, idx, w, prep, O, s);
   else
-    launch_fwd_tile_g<128, 32>(d, Q, K, ws, idx, w, prep, O, s);
+    launch_fwd_tile_g<128, 32>(d, Q, kop, vt, idx, w, prep, O, s);
   return hipGetLastError();
 }
 

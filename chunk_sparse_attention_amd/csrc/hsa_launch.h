@@ -24,7 +24,7 @@ struct BwdLayout {
   int seg;          // entries per backward-phase-2 segment
   int64_t max_seg;  // segment capacity per (b, g)
   size_t ds, dw, tile_counts, tile_base, offsets, entries, seg_start, seg_chunk, n_seg,
-      part_dk, part_dv, part_dks, kt, prep, total;
+      part_dk, part_dv, part_dks, kt, kop, vop, prep, total;
 };
 BwdLayout bwd_layout(const Dims& d);
 
@@ -58,9 +58,10 @@ hipError_t launch_bwd_reduce(const Dims& d, const BwdLayout& lay, void* dK, void
                              float* dKslc, bool fold, char* ws, hipStream_t s);
 
 // Matrix-core (MFMA) kernels for bf16.
-// Per-chunk transpose used by the matrix-core kernels:
-// dst[((b*Hkv+g)*nC + c)*D*64 + d*64 + p] = src[b, 64c + perm_key(p), g, d].
-void launch_prep_transpose(const Dims& d, const void* src, void* dst, hipStream_t s);
+// Per-chunk operand copies for the matrix-core kernels (layouts in fwd_mfma.hip):
+// trans = false: key rows in A-operand order; trans = true: transposed, P.V key order.
+void launch_prep_ops(const Dims& d, const void* src, void* dst, bool trans, hipStream_t s);
+size_t chunk_ops_bytes(const Dims& d);
 // Token tiles of the matrix-core kernels: tokens per tile, and the prepared job lists.
 int tile_tokens(const Dims& d);
 size_t tile_prep_bytes(const Dims& d);
