@@ -57,6 +57,11 @@ hipError_t launch_bwd_generic_p2(const Dims& d, const BwdLayout& lay, const void
 hipError_t launch_bwd_reduce(const Dims& d, const BwdLayout& lay, void* dK, void* dV,
                              float* dKslc, bool fold, char* ws, hipStream_t s);
 
+// Tiled selection (exact fp64 scores, any dtype).
+bool select_tile_supported(const Dims& d);
+hipError_t launch_select_tile(const Dims& d, const void* Qs, const void* Kslc, int32_t* idx,
+                              float* score, float* w, hipStream_t s);
+
 // Matrix-core (MFMA) kernels for bf16.
 // Per-chunk operand copies for the matrix-core kernels (layouts in fwd_mfma.hip):
 // trans = false: key rows in A-operand order; trans = true: transposed, P.V key order.
