@@ -8,12 +8,16 @@ through attention, weights and selection scores), on the fwd_16k workload
 (B=4, L=16384, Hq=16, Hkv=2, d=64, S=64, K=8, bf16).  Inputs are resident in HBM before the
 timed region starts.  value = B*L tokens per step / seconds per step.
 
-    python bench.py [--steps 20] [--warmup 3] [--no-cpu-baseline] [--decode]
+    python bench.py [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-secondary]
+                    [--no-decode]
 
-The roofline object describes the entry point that takes the most time; its duration is the
-average over the timed steps measured with HIP events on the stream the kernels run on.
-cpu_baseline times the CPU oracle (test infrastructure) on a bounded sample of the same
-workload; it is a reported baseline, not the target.
+The roofline object describes the kernel that takes the most time per step.  Its duration is
+the average launch time over the timed steps, from the HIP events libhsa.so records around
+each of its launches on the launch's own stream (hsa_timer_enable / hsa_timer_read); its
+algorithmic bytes and flops per launch are the workload's, from kernel_counts().  "kernels"
+holds the same for every kernel class, "secondary" the select+fwd pass of the L=65536, d=128
+workload, "decode" the 1M-context decode step.  cpu_baseline times the CPU oracle (test
+infrastructure) on the same workload; it is a reported baseline, not the target.
 """
 from __future__ import annotations
 
@@ -31,7 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "HSA fwd+bwd tokens/sec at L=16K/64K bf16; % HBM roofline / MFMA util"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-FP32_PEAK_TFLOPS = 157.3
+FP64_VALU_PEAK_TFLOPS = 78.6   # 256 CUs x 4 SIMD x 16 lanes x 2 (FMA) x 2.4 GHz
 
 
 def log(*a):
@@ -52,32 +56,44 @@ def causal_candidates(wl) -> int:
     return wl.B * wl.Hkv * per_seq
 
 
-def alg_counts(wl, n_slots: int) -> dict:
-    """Algorithmic bytes (every input read once, every output written once) and flops per
-    launch of each entry point.  n_slots = valid (b, t, g, k) selections."""
+def kernel_counts(wl, n_slots: int) -> dict:
+    """Algorithmic bytes (each input the kernel needs read once, each output it produces
+    written once; workspace copies of the design are not counted) and flops per launch of
+    each kernel class.  n_slots = valid (b, t, g, k) selections; every slot is attended by
+    G query heads over S keys."""
     el = 2 if str(wl.dtype).endswith("bfloat16") else 4
     B, L, Hq, Hkv, D, K, S = wl.B, wl.L, wl.Hq, wl.Hkv, wl.D, wl.K, wl.S
-    q = B * L * Hq * D * el
-    kv = B * L * Hkv * D * el
-    kslc = B * wl.nC * Hkv * D * el
-    slot = B * L * Hkv * K * 4
-    edges_heads = n_slots * wl.G
+    q = B * L * Hq * D * el                 # Q, dO, O or dQ
+    kv = B * L * Hkv * D * el               # K, V, Qs, dQs, dK or dV
+    kslc = B * wl.nC * Hkv * D * el         # Kslc
+    slot = B * L * Hkv * K * 4              # idx, score, w or ds
+    eg = n_slots * wl.G
     return {
-        "hsa_select": dict(bytes=2 * kv + kslc + 3 * slot, flops=2 * D * causal_candidates(wl)),
-        "hsa_fwd": dict(bytes=q + 2 * kv + 2 * slot + q, flops=4 * S * D * edges_heads),
-        "hsa_bwd": dict(bytes=(2 * q + 3 * kv + kslc + 3 * slot) + (q + 3 * kv)
-                        + B * wl.nC * Hkv * D * 4,
-                        flops=10 * S * D * edges_heads),
+        "pool": dict(bytes=kv + kslc, flops=B * wl.nC * Hkv * D * S),
+        "select": dict(bytes=kv + kslc + 3 * slot, flops=2 * D * causal_candidates(wl),
+                       alu=True),
+        "tile_prep": dict(bytes=slot, flops=0),
+        "prep_ops": dict(bytes=2 * kv, flops=0),
+        "fwd": dict(bytes=2 * q + 2 * kv + 2 * slot, flops=4 * S * D * eg),
+        "invidx": dict(bytes=slot + 4 * n_slots, flops=0),
+        "bwd_p1": dict(bytes=3 * q + 4 * kv + kslc + 4 * slot, flops=6 * S * D * eg),
+        "bwd_p2": dict(bytes=2 * q + 5 * kv + 2 * slot + 4 * n_slots + 2 * kslc, flops=8 * S * D * eg),
+        "bwd_reduce": dict(bytes=2 * kv + 2 * kslc, flops=0),
     }
 
 
 def roofline(name: str, counts: dict, avg_ms: float, traffic) -> dict:
+    """Price one kernel's average launch against MI355X's peaks: HBM bandwidth, dense bf16
+    MFMA or, for the fp64 vector-ALU scoring, the fp64 vector rate."""
     t_hbm = counts["bytes"] / (HBM_PEAK_GBS * 1e9)
-    t_mfma = counts["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    alu = counts.get("alu", False)
+    peak_f = FP64_VALU_PEAK_TFLOPS if alu else BF16_PEAK_TFLOPS
+    t_f = counts["flops"] / (peak_f * 1e12)
     s = avg_ms / 1e3
-    if t_mfma >= t_hbm:
+    if t_f >= t_hbm:
         ach = counts["flops"] / s / 1e12
-        r = dict(bound="mfma", achieved=round(ach, 3), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s")
+        r = dict(bound="alu" if alu else "mfma", achieved=round(ach, 3), peak=peak_f,
+                 unit="TFLOP/s")
     else:
         ach = counts["bytes"] / s / 1e9
         r = dict(bound="hbm", achieved=round(ach, 2), peak=HBM_PEAK_GBS, unit="GB/s")
@@ -103,20 +119,28 @@ def measured_traffic(entry: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, x) -> dict:
-    """The oracle (pool, select, attend, backward) on sequence 0 of the workload."""
+def cpu_baseline(wl, x, budget_s: float = 20.0) -> dict:
+    """The oracle (pool, select, attend, backward) over the workload's sequences, one at a
+    time, until all are done or budget_s has passed."""
     import oracle
     orc = oracle.get()
-    sl = {k: x[k][:1] for k in ("Q", "K", "V", "Qs", "dO")}
     t0 = time.perf_counter()
-    f = orc.forward(sl["Q"], sl["K"], sl["V"], sl["Qs"], wl.S, wl.K)
-    orc.backward(sl["Q"], sl["K"], sl["V"], sl["Qs"], f["Kslc"], f["idx"], f["score"], f["w"],
-                 sl["dO"], wl.S)
+    done = 0
+    for b in range(wl.B):
+        sl = {k: x[k][b:b + 1] for k in ("Q", "K", "V", "Qs", "dO")}
+        f = orc.forward(sl["Q"], sl["K"], sl["V"], sl["Qs"], wl.S, wl.K)
+        orc.backward(sl["Q"], sl["K"], sl["V"], sl["Qs"], f["Kslc"], f["idx"], f["score"],
+                     f["w"], sl["dO"], wl.S)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
     el = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=round(wl.L / el, 2), unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"sequence 0 of {wl.B} ({wl.L} tokens): pool+select+attend+backward, "
-                       f"{el:.1f} s")
+    # OpenMP uses OMP_NUM_THREADS threads when it is set, else one per CPU of the affinity mask
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    cores = int(env) if env.isdigit() else len(os.sched_getaffinity(0))
+    return dict(value=round(done * wl.L / el, 2), unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{done} of {wl.B} sequences x {wl.L} tokens: pool+select+attend+"
+                       f"backward in {el:.1f} s")
 
 
 def main() -> int:
@@ -128,7 +152,10 @@ def main() -> int:
     ap.add_argument("--generic", action="store_true", help="force the vector-ALU kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--decode", action="store_true", help="also time the 1M-context decode step")
+    ap.add_argument("--no-decode", action="store_true", help="skip the 1M-context decode step")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="profiling aid: with --only, first copy this many MiB once with a plain "
+                         "device copy (the scale reference for HBM byte counters)")
     ap.add_argument("--only", choices=["select", "fwd", "bwd"], default=None,
                     help="profiling aid: after one full step, run only this entry point "
                          "--steps times and print its mean time (no JSON line)")
@@ -182,6 +209,13 @@ def main() -> int:
                "bwd": lambda: hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, generic=gen,
                                       ws=ws_bwd)}[args.only]
         torch.cuda.synchronize()
+        if args.copy_mib:
+            src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"bench: copied {args.copy_mib} MiB")
+            del src, dst
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
@@ -194,20 +228,31 @@ def main() -> int:
     log(f"bench: timing {args.steps} steps")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    hsa.timer_enable(True)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    hsa.timer_enable(False)
+    ktimes = hsa.timer_read()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     names = ["hsa_select", "hsa_fwd", "hsa_bwd"]
-    avg = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
-           for j, n in enumerate(names)}
-    log("bench: per-entry ms", {k: round(v, 4) for k, v in avg.items()})
-    counts = alg_counts(wl, n_slots)
-    dominant = max(avg, key=avg.get)
-    roof = roofline(dominant, counts[dominant], avg[dominant], measured_traffic(dominant))
-    others = {n: roofline(n, counts[n], avg[n], measured_traffic(n)) for n in names}
+    entry_ms = {n: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps, 4)
+                for j, n in enumerate(names)}
+    log("bench: per-entry ms", entry_ms)
+    counts = kernel_counts(wl, n_slots)
+    kern = {}
+    for name, (n, total) in ktimes.items():
+        if n == 0:
+            continue
+        r = roofline(name, counts[name], total / n, measured_traffic(name))
+        r["launches_per_step"] = round(n / args.steps, 3)
+        r["ms_per_step"] = round(total / args.steps, 4)
+        kern[name] = r
+    log("bench: per-kernel ms/step", {k: v["ms_per_step"] for k, v in kern.items()})
+    dominant = max(kern, key=lambda k: kern[k]["ms_per_step"])
+    roof = {k: v for k, v in kern[dominant].items() if k not in ("launches_per_step",)}
 
     tokens = wl.B * wl.L
     out = {
@@ -228,7 +273,8 @@ def main() -> int:
                    "global_batch": wl.B, "seq_len": wl.L, "parallelism": "single GPU",
                    "kernels": "generic" if gen else "default"},
         "roofline": roof,
-        "entry_points": others,
+        "entry_ms": entry_ms,
+        "kernels": kern,
     }
 
     if not args.no_secondary:
@@ -236,61 +282,79 @@ def main() -> int:
         log(f"bench: secondary {wl2.name} select+fwd")
         x2 = workloads.make_inputs(wl2, seed=0, with_grad=False)
         Q2, K2, V2, Qs2 = (x2[k].to(dev) for k in ("Q", "K", "V", "Qs"))
+        prob2 = hsa.problem(wl2.B, wl2.L, wl2.Hq, wl2.Hkv, wl2.D, wl2.K, wl2.dtype, generic=gen)
+        ws2 = hsa.workspace(_lib.HSA_OP_FWD, prob2, dev)
+        O2 = torch.empty_like(Q2)
         for _ in range(2):
             _, i2, _, w2 = hsa.select(Qs2, K2, wl2.K, generic=gen)
-            hsa.fwd(Q2, K2, V2, i2, w2, generic=gen)
+            hsa.fwd(Q2, K2, V2, i2, w2, generic=gen, ws=ws2, out=O2)
         torch.cuda.synchronize()
         n2 = int((i2 >= 0).sum().item())
         reps = max(3, args.steps // 4)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         ts, tf = 0.0, 0.0
+        hsa.timer_enable(True)
         for _ in range(reps):
             e[0].record()
             _, i2, _, w2 = hsa.select(Qs2, K2, wl2.K, generic=gen)
             e[1].record()
-            hsa.fwd(Q2, K2, V2, i2, w2, generic=gen)
+            hsa.fwd(Q2, K2, V2, i2, w2, generic=gen, ws=ws2, out=O2)
             e[2].record()
             torch.cuda.synchronize()
             ts += e[0].elapsed_time(e[1])
             tf += e[1].elapsed_time(e[2])
+        hsa.timer_enable(False)
+        kt2 = hsa.timer_read()
         ts /= reps
         tf /= reps
-        c2 = alg_counts(wl2, n2)
+        c2 = kernel_counts(wl2, n2)
+        k2 = {name: roofline(name, c2[name], total / n, None)
+              for name, (n, total) in kt2.items() if n}
         out["secondary"] = {
-            "workload": f"{wl2.name}: select+fwd B={wl2.B} L={wl2.L} d={wl2.D} K={wl2.K}",
+            "workload": f"{wl2.name}: select+fwd B={wl2.B} L={wl2.L} Hq={wl2.Hq} "
+                        f"Hkv={wl2.Hkv} d={wl2.D} K={wl2.K}",
             "select_ms": round(ts, 4), "fwd_ms": round(tf, 4),
             "tokens_per_s": round(wl2.B * wl2.L / ((ts + tf) / 1e3), 1),
-            "fwd_roofline": roofline("hsa_fwd", c2["hsa_fwd"], tf, None),
+            "kernels": k2,
         }
-        del Q2, K2, V2, Qs2, x2
+        del Q2, K2, V2, Qs2, x2, O2, ws2
 
-    if args.decode:
+    if not args.no_decode:
         wl3 = workloads.WORKLOADS["decode_1m"]
         log(f"bench: decode {wl3.name} (generating caches)")
-        x3 = workloads.make_decode_inputs(wl3, seed=0)
+        x3 = workloads.make_decode_inputs(wl3, seed=0, slab=4)
         q, qs = x3["q"].to(dev), x3["qs"].to(dev)
         Kc, Vc = x3["Kc"].to(dev), x3["Vc"].to(dev)
+        del x3
         Kslc3 = hsa.pool(Kc)
-        prob3 = hsa.problem(wl3.B, wl3.L, wl3.Hq, wl3.Hkv, wl3.D, wl3.K, wl3.dtype)
+        prob3 = hsa.problem(wl3.B, wl3.L, wl3.Hq, wl3.Hkv, wl3.D, wl3.K, wl3.dtype, generic=gen)
         ws3 = hsa.workspace(_lib.HSA_OP_DECODE, prob3, dev)
         for _ in range(3):
             hsa.decode(q, qs, Kc, Vc, Kslc3, wl3.K, generic=gen, ws=ws3)
         torch.cuda.synchronize()
+        log("bench: decode timing")
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 50
+        hsa.timer_enable(True)
         e0.record()
         for _ in range(reps):
             hsa.decode(q, qs, Kc, Vc, Kslc3, wl3.K, generic=gen, ws=ws3)
         e1.record()
         torch.cuda.synchronize()
+        hsa.timer_enable(False)
+        n3, tot3 = hsa.timer_read()["decode"]
         dms = e0.elapsed_time(e1) / reps
         el = 2
+        # the chunk-key table, the selected chunks' K and V, q, qs and O
         dbytes = (wl3.B * wl3.nC * wl3.Hkv * wl3.D * el
                   + 2 * wl3.B * wl3.Hkv * wl3.K * wl3.S * wl3.D * el
                   + 2 * wl3.B * wl3.Hq * wl3.D * el + wl3.B * wl3.Hkv * wl3.D * el)
-        out["decode"] = {"workload": f"{wl3.name}: B={wl3.B} ctx={wl3.L} K={wl3.K} (warm)",
+        out["decode"] = {"workload": f"{wl3.name}: B={wl3.B} ctx={wl3.L} Hq={wl3.Hq} "
+                                     f"Hkv={wl3.Hkv} d={wl3.D} K={wl3.K}",
                          "ms": round(dms, 4), "new_tokens_per_s": round(wl3.B / (dms / 1e3), 1),
-                         "hbm_frac": round(dbytes / (dms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+                         "roofline": roofline("decode", dict(bytes=dbytes, flops=0),
+                                              tot3 / max(n3, 1), None)}
+        del q, qs, Kc, Vc, Kslc3
 
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")

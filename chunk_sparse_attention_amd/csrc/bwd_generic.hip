@@ -188,6 +188,7 @@ hipError_t launch_invidx(const Dims& d, const BwdLayout& lay, const int32_t* idx
   int32_t* tc = (int32_t*)(ws + lay.tile_counts);
   int32_t* tb = (int32_t*)(ws + lay.tile_base);
   size_t lds = sizeof(int32_t) * d.nC;
+  Timed tm(HSA_KERNEL_INVIDX, s);
   k_inv_count<<<dim3(bg * lay.n_tiles), 256, lds, s>>>(idx, tc, d.L, d.Hkv, d.K, d.nC,
                                                         lay.tile_tokens, lay.n_tiles);
   k_inv_scan<<<dim3(bg), 1024, 0, s>>>(tc, tb, (int32_t*)(ws + lay.offsets),
@@ -495,6 +496,7 @@ static void launch_p1_generic(const Dims& d, const BwdLayout& lay, const void* Q
                               const float* score, const float* w, const void* dO, void* dQ,
                               void* dQs, char* ws, hipStream_t s) {
   const size_t rows = (size_t)d.B * d.L * d.Hkv;
+  Timed tm(HSA_KERNEL_BWD_P1, s);
   k_bwd_p1_generic<T><<<dim3((unsigned)rows), 64, 0, s>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)Kslc, idx, score, w, (const T*)dO,
       (T*)dQ, (T*)dQs, (float*)(ws + lay.ds), (float*)(ws + lay.dw), d.L, d.Hq, d.Hkv, d.D, d.S,
@@ -509,6 +511,7 @@ static void launch_p2_generic(const Dims& d, const BwdLayout& lay, const void* Q
   const float sm = (float)d.sm_scale, sel = (float)d.sel_scale;
   dim3 grid((unsigned)(bg * lay.max_seg));
   auto args = [&](auto kern) {
+    Timed tm(HSA_KERNEL_BWD_P2, s);
     kern<<<grid, 128, 0, s>>>((const T*)Q, (const T*)K, (const T*)V, (const T*)Qs, w,
                               (const T*)dO, (const float*)(ws + lay.ds),
                               (const int32_t*)(ws + lay.offsets),
@@ -541,6 +544,7 @@ hipError_t launch_bwd_reduce(const Dims& d, const BwdLayout& lay, void* dK, void
   const int bg = d.B * d.Hkv;
   const int n_all = (d.L + d.S - 1) / d.S;
   auto go = [&](auto kern, auto* dk, auto* dv) {
+    Timed tm(HSA_KERNEL_BWD_REDUCE, s);
     kern<<<dim3((unsigned)(bg * n_all)), 256, 0, s>>>(
         (const float*)(ws + lay.part_dk), (const float*)(ws + lay.part_dv),
         (const float*)(ws + lay.part_dks), (const int32_t*)(ws + lay.seg_start), dk, dv, dKslc,

@@ -427,6 +427,7 @@ static void launch_p1(const Dims& d, const BwdLayout& lay, const void* Q, const 
   const int BG = d.B * d.Hkv;
   const int n_tiles = (d.L + TT - 1) / TT;
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);
+  Timed tm(HSA_KERNEL_BWD_P1, s);
   k_bwd_p1_tile<D, TT, G><<<dim3(BG * n_tiles), 512, 0, s>>>(
       (const bf16*)Q, (const bf16*)(ws + lay.kop), (const bf16*)(ws + lay.vop),
       (const bf16*)(ws + lay.kt),
@@ -468,6 +469,7 @@ hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, c
       const float c2 = (float)(d.sm_scale * 1.4426950408889634);
       dim3 grid((unsigned)(BG * lay.max_seg));
       auto go = [&](auto kern) {
+        Timed tm(HSA_KERNEL_BWD_P2, s);
         kern<<<grid, 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)V,
                                  (const bf16*)Qs, w, (const bf16*)dO,
                                  (const float*)(ws + lay.ds), (const int32_t*)(ws + lay.offsets),

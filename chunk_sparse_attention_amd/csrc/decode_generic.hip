@@ -187,6 +187,7 @@ hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void
   uint64_t* cand = (uint64_t*)(ws + lay.cand);
   float sm = (float)d.sm_scale;
   // d.L is the context length; the new token may select every complete chunk.
+  Timed tm(HSA_KERNEL_DECODE, s);
   if (d.dtype == 1) {
     k_dec_scan<bf16><<<dim3(bg * lay.n_blocks), 256, 0, s>>>(
         (const bf16*)qs, (const bf16*)Kslc, cand, d.Hkv, d.D, d.K, d.nC, lay.n_blocks,

@@ -93,6 +93,7 @@ hipError_t launch_fwd_generic(const Dims& d, const void* Q, const void* K, const
   size_t rows = (size_t)d.B * d.L * d.Hkv;
   if (rows == 0) return hipSuccess;
   float sm = (float)d.sm_scale;
+  Timed tm(HSA_KERNEL_FWD, s);
   if (d.dtype == 1)
     k_fwd_generic<bf16><<<dim3((unsigned)rows), 64, 0, s>>>(
         (const bf16*)Q, (const bf16*)K, (const bf16*)V, idx, w, (bf16*)O, d.L, d.Hq, d.Hkv, d.D,

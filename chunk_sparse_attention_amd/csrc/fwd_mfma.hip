@@ -274,6 +274,7 @@ template <int TT>
 static void launch_prep_tt(const Dims& d, const int32_t* idx, uint32_t* prep, hipStream_t s) {
   const int BG = d.B * d.Hkv;
   const int n_tiles = (d.L + TT - 1) / TT;
+  Timed tm(HSA_KERNEL_TILE_PREP, s);
   k_tile_prep<256, TT><<<dim3(BG * n_tiles), 256, 0, s>>>(idx, prep, d.L, d.Hkv, d.K, d.nC, BG,
                                                           16 / d.G);
 }
@@ -293,6 +294,7 @@ static void launch_fwd_tile(const Dims& d, const void* Q, const void* K, const v
   const int BG = d.B * d.Hkv;
   const int n_tiles = (d.L + TT - 1) / TT;
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);  // logit scale * log2(e)
+  Timed tm(HSA_KERNEL_FWD, s);
   k_fwd_tile<D, TT, G><<<dim3(BG * n_tiles), 512, 0, s>>>(
       (const bf16*)Q, (const bf16*)K, (const bf16*)Vt, idx, w, (const uint32_t*)prep, (bf16*)O,
       d.L, d.Hq, d.Hkv, d.K, d.nC, BG, c2);
@@ -321,6 +323,7 @@ size_t fwd_mfma_ws(const Dims& d) { return 2 * chunk_ops_bytes(d) + tile_prep_by
 void launch_prep_ops(const Dims& d, const void* src, void* dst, bool trans, hipStream_t s) {
   if (d.nC == 0) return;
   dim3 grid(d.B * d.Hkv * d.nC);
+  Timed tm(HSA_KERNEL_PREP_OPS, s);
   if (trans)
     k_prep_ops<true><<<grid, 256, 0, s>>>((const bf16*)src, (bf16*)dst, d.L, d.Hkv, d.D, d.nC);
   else

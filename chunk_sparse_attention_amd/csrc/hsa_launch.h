@@ -5,7 +5,23 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "hsa.h"
+
 namespace hsa {
+
+// Brackets the launches made during its lifetime with HIP events when kernel timing is on
+// (kc is an hsa_kernel_t class); does nothing otherwise.
+class Timed {
+ public:
+  Timed(int kc, hipStream_t s);
+  ~Timed();
+  Timed(const Timed&) = delete;
+  Timed& operator=(const Timed&) = delete;
+
+ private:
+  int kc_, slot_;
+  hipStream_t s_;
+};
 
 // Validated problem, with derived sizes and the scales resolved in double.
 struct Dims {

@@ -36,6 +36,7 @@ hipError_t launch_pool(const Dims& d, const void* K, void* Kslc, hipStream_t s) 
   size_t total = (size_t)d.B * d.nC * d.Hkv * d.D;
   if (total == 0) return hipSuccess;
   dim3 grid((unsigned)((total + 255) / 256));
+  Timed tm(HSA_KERNEL_POOL, s);
   if (d.dtype == 1)
     k_pool<bf16><<<grid, 256, 0, s>>>((const bf16*)K, (bf16*)Kslc, d.L, d.Hkv, d.D, d.S, d.nC,
                                       total);
@@ -117,6 +118,7 @@ hipError_t launch_select_generic(const Dims& d, const void* Qs, const void* Kslc
                                  float* score, float* w, hipStream_t s) {
   size_t rows = (size_t)d.B * d.L * d.Hkv;
   if (rows == 0) return hipSuccess;
+  Timed tm(HSA_KERNEL_SELECT, s);
   if (d.dtype == 1)
     k_select_generic<bf16><<<dim3((unsigned)rows), 64, 0, s>>>(
         (const bf16*)Qs, (const bf16*)Kslc, idx, score, w, d.L, d.Hkv, d.D, d.S, d.K, d.nC,

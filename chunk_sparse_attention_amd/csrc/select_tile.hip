@@ -154,6 +154,7 @@ hipError_t launch_select_tile(const Dims& d, const void* Qs, const void* Kslc, i
   const int n_tiles = (d.L + 63) / 64;
   dim3 grid((unsigned)(BG * n_tiles));
   auto go = [&](auto kern, auto* qs, auto* ks) {
+    Timed tm(HSA_KERNEL_SELECT, s);
     kern<<<grid, 256, 0, s>>>(qs, ks, idx, score, w, d.L, d.Hkv, d.K, d.nC, BG, d.sel_scale);
   };
   if (d.dtype == 1) {

@@ -184,3 +184,18 @@ def decode(q, qs, Kc, Vc, Kslc, K_top, sm_scale=None, sel_scale=None, generic=Fa
                                 _ptr(Kslc), _ptr(O), _ptr(idx), _ptr(score), _ptr(w), wp, wn,
                                 _stream()), "hsa_decode")
     return O, idx, score, w
+
+
+def timer_enable(on: bool = True) -> None:
+    """Start (forgetting earlier records) or stop HIP-event timing of every kernel launch."""
+    check(_lib.lib().hsa_timer_enable(1 if on else 0), "hsa_timer_enable")
+
+
+def timer_read() -> dict:
+    """{kernel class: (recorded launches, total ms)} since the last timer_enable(True)."""
+    out = {}
+    for i, name in enumerate(_lib.KERNEL_CLASSES):
+        n, ms = ctypes.c_int(0), ctypes.c_double(0.0)
+        check(_lib.lib().hsa_timer_read(i, ctypes.byref(n), ctypes.byref(ms)), "hsa_timer_read")
+        out[name] = (int(n.value), float(ms.value))
+    return out

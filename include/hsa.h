@@ -158,6 +158,38 @@ hsa_status_t hsa_decode(const hsa_problem_t* p, const void* q, const void* qs,
                         int32_t* idx, float* score, float* w, void* ws, size_t ws_bytes,
                         hsa_stream_t stream);
 
+/* ---- Kernel timing (measurement aid; not part of the operation) ----------------------
+ * The entry points above each enqueue a short sequence of kernels.  To price one kernel
+ * against the device's roofline, the library can bracket every launch of a kernel class
+ * with a pair of HIP events recorded on that launch's stream.  Timing is off by default;
+ * when on, each recorded launch adds two event records to its stream and a little host
+ * work, and up to 4096 launches per class are recorded (later ones are not).  The state is
+ * process-wide and shared by all threads and devices; events come from the current device
+ * of the first launch that needs them, so time one device per enable. */
+typedef enum {
+  HSA_KERNEL_POOL = 0,       /* chunk-key mean pooling */
+  HSA_KERNEL_SELECT = 1,     /* scoring, top-K and stick-breaking weights */
+  HSA_KERNEL_TILE_PREP = 2,  /* per-token-tile job lists of the matrix-core kernels */
+  HSA_KERNEL_PREP_OPS = 3,   /* per-chunk operand copies of the matrix-core kernels */
+  HSA_KERNEL_FWD = 4,        /* token-level attention fused with the chunk weights */
+  HSA_KERNEL_INVIDX = 5,     /* chunk -> (token, slot) inverse index (count, scan, scatter) */
+  HSA_KERNEL_BWD_P1 = 6,     /* backward phase 1: per token dQ, dw, ds, dQs */
+  HSA_KERNEL_BWD_P2 = 7,     /* backward phase 2: per chunk dK, dV, dKslc partials */
+  HSA_KERNEL_BWD_REDUCE = 8, /* backward: fixed-order reduction of the phase-2 partials */
+  HSA_KERNEL_DECODE = 9,     /* decode step (scan and attend) */
+  HSA_KERNEL_COUNT = 10
+} hsa_kernel_t;
+
+/* enable != 0: forget earlier records and start recording; enable == 0: stop recording
+ * (records are kept for hsa_timer_read).  Always returns HSA_OK. */
+hsa_status_t hsa_timer_enable(int enable);
+
+/* Number of recorded launches of class `kernel` (hsa_kernel_t) since the last enable and
+ * the sum of their durations in milliseconds.  Waits for the recorded events to complete
+ * (the one call of this library that synchronises).  HSA_ERR_INVALID_ARG for an unknown
+ * class or NULL outputs; HSA_ERR_HIP if an event cannot be read. */
+hsa_status_t hsa_timer_read(int kernel, int* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

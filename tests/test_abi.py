@@ -102,3 +102,23 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros((1, 128, 1, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         hsa.select(x, x, 4)
+
+
+def test_kernel_timer_without_launches():
+    """The timing aid records nothing until a launch happens and validates its class."""
+    from chunk_sparse_attention_amd import _lib
+    L = _lib.lib()
+    assert L.hsa_timer_enable(1) == _lib.HSA_OK
+    n, ms = ctypes.c_int(-1), ctypes.c_double(-1.0)
+    for k in range(len(_lib.KERNEL_CLASSES)):
+        assert L.hsa_timer_read(k, ctypes.byref(n), ctypes.byref(ms)) == _lib.HSA_OK
+        assert (n.value, ms.value) == (0, 0.0)
+    assert L.hsa_timer_read(len(_lib.KERNEL_CLASSES), ctypes.byref(n),
+                            ctypes.byref(ms)) == _lib.HSA_ERR_INVALID_ARG
+    assert L.hsa_timer_read(-1, ctypes.byref(n), ctypes.byref(ms)) == _lib.HSA_ERR_INVALID_ARG
+    assert L.hsa_timer_read(0, None, ctypes.byref(ms)) == _lib.HSA_ERR_INVALID_ARG
+    assert L.hsa_timer_enable(0) == _lib.HSA_OK
+    with open(HEADER) as fh:
+        text = fh.read()
+    for i, name in enumerate(_lib.KERNEL_CLASSES):
+        assert f"HSA_KERNEL_{name.upper()} = {i}," in text
