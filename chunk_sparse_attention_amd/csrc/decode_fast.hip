@@ -1,0 +1,355 @@
+// decode_fast.hip -- one decode step per sequence, bandwidth-shaped (fp32 and bf16).
+//
+// At inference only the compact chunk-key table is scanned for selection, and each step
+// reads only the selected chunks' key/value rows ("Hardware-aligned Hierarchical Sparse
+// Attention ...", papernotes.org note, 方法详解 › 训练与推理优化, KV Cache Offloading).  The
+// step has two kernels:
+//   scan    streams the chunk-key table once.  Every lane scores kScanPer chunks with an
+//           fp64 dot product in dimension order (exact products, so each score is the
+//           correctly rounded definition); the block reduces its candidates to a ranked
+//           top-K that it writes to the workspace.
+//   attend  one block per (sequence, group) with one wave per kept slot.  Each wave merges
+//           the scan's candidates itself (so no wave waits on another), forms the
+//           stick-breaking weights, and runs softmax-off-by-one attention of the group's G
+//           query heads over its slot's chunk: lane j holds key row j for the logits, and the
+//           value rows are read as independent 16-byte pieces so that all of a chunk's loads
+//           are in flight at once.  The K weighted slot outputs meet in LDS and are summed in
+//           slot order.
+#include "hsa_common.h"
+#include "hsa_launch.h"
+#include "tile_common.h"
+
+namespace hsa {
+
+constexpr int kScanThreads = 256;
+constexpr int kScanPer = 1;                                   // chunks per lane
+constexpr int kScanChunks = kScanThreads * kScanPer;          // chunks per scan block
+constexpr int kScanWaves = kScanThreads / kWave;
+
+// Raw row of D elements kept as loaded (16-byte pieces), converted when used.
+template <typename T, int D>
+struct RawRow;
+template <int D>
+struct RawRow<bf16, D> {
+  uint4 v[D / 8];
+  __device__ __forceinline__ void load(const bf16* p) {
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) v[i] = reinterpret_cast<const uint4*>(p)[i];
+  }
+  __device__ __forceinline__ float get(int e) const {
+    const uint4 q = v[e / 8];
+    const uint32_t w = (e % 8) < 2 ? q.x : (e % 8) < 4 ? q.y : (e % 8) < 6 ? q.z : q.w;
+    return (e % 2) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+};
+template <int D>
+struct RawRow<float, D> {
+  float4 v[D / 4];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) v[i] = reinterpret_cast<const float4*>(p)[i];
+  }
+  __device__ __forceinline__ float get(int e) const {
+    const float4 q = v[e / 4];
+    return (e % 4) == 0 ? q.x : (e % 4) == 1 ? q.y : (e % 4) == 2 ? q.z : q.w;
+  }
+};
+
+// Maximum of a 64-bit key over the wave, in every lane: DPP inside each 16-lane row, then
+// the gfx950 row swaps across rows (the halves of a key travel together through each swap).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_key(uint64_t v) {
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), CTRL, 0xF, 0xF, true);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+  const uint64_t o = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint64_t swap_max_key(uint64_t v, bool rows32) {
+  const unsigned hi = (unsigned)(v >> 32), lo = (unsigned)v;
+  unsigned h0, h1, l0, l1;
+  if (rows32) {
+    auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    h0 = ph[0]; h1 = ph[1]; l0 = pl[0]; l1 = pl[1];
+  } else {
+    auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    h0 = ph[0]; h1 = ph[1]; l0 = pl[0]; l1 = pl[1];
+  }
+  asm volatile("" : "+v"(h0), "+v"(h1), "+v"(l0), "+v"(l1));  // keep the two results apart
+  const uint64_t a = ((uint64_t)h0 << 32) | l0, b = ((uint64_t)h1 << 32) | l1;
+  return a > b ? a : b;
+}
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  v = dpp_max_key<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_key<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_key<0x141>(v);  // row_half_mirror
+  v = dpp_max_key<0x140>(v);  // row_mirror
+  v = swap_max_key(v, false);
+  return swap_max_key(v, true);
+}
+
+size_t dec_fast_ws(const Dims& d) {
+  const int n_blocks = d.nC > 0 ? (d.nC + kScanChunks - 1) / kScanChunks : 0;
+  const size_t n = sizeof(uint64_t) * (size_t)d.B * d.Hkv * n_blocks * d.K;
+  return (n + 255) & ~(size_t)255;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(4)))
+k_dec_scan_fast(const T* __restrict__ qs,
+                                                                const T* __restrict__ Kslc,
+                                                                uint64_t* __restrict__ cand,
+                                                                int Hkv, int K, int nC,
+                                                                int n_blocks, double sel_scale) {
+  __shared__ double qsh[D];
+  const int blk = blockIdx.x % n_blocks;
+  const int bg = blockIdx.x / n_blocks;
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  for (int e = tid; e < D; e += kScanThreads)
+    qsh[e] = (double)to_f32(qs[((size_t)b * Hkv + g) * D + e]);
+
+  RawRow<T, D> row[kScanPer];
+  int cs[kScanPer];
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    cs[i] = blk * kScanChunks + i * kScanThreads + tid;
+    if (cs[i] < nC) row[i].load(Kslc + ((b * nC + cs[i]) * Hkv + g) * D);
+  }
+  __syncthreads();
+  // the dimension loop is outermost so that only eight query values are live at a time
+  double dot[kScanPer];
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) dot[i] = 0.0;
+#pragma unroll
+  for (int e0 = 0; e0 < D; e0 += 8) {
+    double qv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[e] = qsh[e0 + e];
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot[i] = fma(qv[e], (double)row[i].get(e0 + e), dot[i]);
+  }
+  uint64_t key[kScanPer];
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i)
+    key[i] = cs[i] < nC ? rank_key((float)(sel_scale * dot[i]), cs[i]) : 0;
+  // lane-local descending order, then K rounds of a wave maximum over the lane heads
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i)
+#pragma unroll
+    for (int j = i + 1; j < kScanPer; ++j)
+      if (key[j] > key[i]) {
+        const uint64_t t = key[i];
+        key[i] = key[j];
+        key[j] = t;
+      }
+  __shared__ uint64_t wtop[kScanWaves][kMaxK];
+  for (int k = 0; k < K; ++k) {
+    const uint64_t best = wave_max_key(key[0]);
+    if (best != 0 && key[0] == best) {
+#pragma unroll
+      for (int i = 0; i + 1 < kScanPer; ++i) key[i] = key[i + 1];
+      key[kScanPer - 1] = 0;
+    }
+    if (lane == 0) wtop[wave][k] = best;
+  }
+  __syncthreads();
+  // the block's ranked top-K from the waves' lists
+  if (wave == 0) {
+    uint64_t v = lane < kScanWaves * K ? wtop[lane / K][lane % K] : 0;
+    uint64_t* out = cand + ((size_t)bg * n_blocks + blk) * K;
+    for (int k = 0; k < K; ++k) {
+      const uint64_t best = wave_max_key(v);
+      if (v == best) v = 0;
+      if (lane == 0) out[k] = best;
+    }
+  }
+}
+
+// D elements per row = P pieces of 8; the 64 lanes of a wave form JG = 64/P groups of P
+// lanes, and group jg reads rows jg, jg+JG, ... of the chunk.  LDS: the group's queries, the
+// attention weights of four heads per wave, and the K weighted slot outputs (at most
+// 8 + 16 + 128 KB for D = 128, K = G = 16).
+template <typename T, int D>
+__global__ void __launch_bounds__(1024) k_dec_attend_fast(
+    const T* __restrict__ q, const T* __restrict__ Kc, const T* __restrict__ Vc,
+    const uint64_t* __restrict__ cand, T* __restrict__ O, int32_t* __restrict__ idx,
+    float* __restrict__ score, float* __restrict__ w, int ctx, int Hq, int Hkv, int K, int G,
+    int n_cand, float c2) {
+  constexpr int P = D / 8;
+  constexpr int JG = kWave / P;
+  constexpr int RPL = kChunk / JG;  // rows per lane in the value product
+  __shared__ float qsh[kMaxG][D];
+  __shared__ float ash[kMaxK][4][kChunk];
+  __shared__ float osh[kMaxK][kMaxG][D];
+  __shared__ int n_valid_sh;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int bg = blockIdx.x;
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const size_t qbase = ((size_t)b * Hq + (size_t)g * G) * D;
+  for (int i = tid; i < G * D; i += blockDim.x) qsh[i / D][i % D] = to_f32(q[qbase + i]);
+
+  // Every wave merges the candidates into the same ranked top-K and walks the stick-breaking
+  // recursion in rank order (in double): w_k = p_k * R, R <- R * (1 - p_k).
+  uint64_t top[kMaxK];
+#pragma unroll
+  for (int i = 0; i < kMaxK; ++i) top[i] = 0;
+  const uint64_t* cb = cand + (size_t)bg * n_cand;
+#pragma unroll 4
+  for (int i = lane; i < n_cand; i += kWave) topk_insert(top, cb[i], K);
+  uint64_t mine = 0;  // the key of this wave's slot
+  double wk = 0.0, rem = 1.0;
+  int n_valid = 0;
+  for (int k = 0; k < K; ++k) {
+    const uint64_t best = wave_max_key(top[0]);
+    if (best != 0 && top[0] == best) topk_pop(top);
+    if (best != 0) {
+      const double pk = sigmoid_d((double)key_score(best));
+      if (k == wave) {
+        mine = best;
+        wk = pk * rem;
+      }
+      rem *= 1.0 - pk;
+      ++n_valid;
+    }
+  }
+  if (lane == 0) {
+    const size_t o = (size_t)bg * K + wave;
+    if (mine == 0) {
+      idx[o] = -1;
+      if (score) score[o] = -__builtin_inff();
+      w[o] = 0.0f;
+    } else {
+      idx[o] = key_chunk(mine);
+      if (score) score[o] = key_score(mine);
+      w[o] = (float)wk;
+    }
+  }
+  if (tid == 0) n_valid_sh = n_valid;
+  __syncthreads();  // qsh ready
+
+  if (mine != 0) {
+    const int c = key_chunk(mine);
+    const float wf = (float)wk;
+    const size_t kvstride = (size_t)Hkv * D;
+    const size_t cbase = ((b * ctx + (size_t)c * kChunk) * Hkv + g) * D;
+    // logits: lane j owns key row j (products of stored values summed in fp32)
+    RawRow<T, D> kr;
+    kr.load(Kc + cbase + (size_t)lane * kvstride);
+    float z[kMaxG];
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+      z[h] = 0.0f;
+      if (h < G) {
+#pragma unroll
+        for (int e0 = 0; e0 < D; e0 += 8) {
+          int off = h * D + e0;  // pinned in the loop as in the scan
+          asm volatile("" : "+v"(off));
+          const float4 qa = *reinterpret_cast<const float4*>(&qsh[0][0] + off);
+          const float4 qb = *reinterpret_cast<const float4*>(&qsh[0][0] + off + 4);
+          const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) z[h] = fmaf(qv[e], kr.get(e0 + e), z[h]);
+        }
+      }
+    }
+    const int p = lane % P, jg = lane / P;
+#pragma unroll
+    for (int h0 = 0; h0 < kMaxG; h0 += 4) {
+      if (h0 >= G) break;
+      // softmax-off-by-one of four heads (log2 domain), scaled by the slot weight
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float aw = 0.0f;
+        if (h0 + a < G) {
+          const float zz = z[h0 + a] * c2;
+          const float m = fmaxf(0.0f, wave_max(zz));
+          const float ex = exp2f(zz - m);
+          aw = wf * ex / (exp2f(-m) + wave_sum(ex));
+        }
+        ash[wave][a][lane] = aw;
+      }
+      // value product: lane (jg, p) accumulates rows jg + JG*i of piece p
+      float acc[4][8];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[a][e] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        const int j = jg + JG * i;
+        float v[8];
+        load8(Vc + cbase + (size_t)j * kvstride + 8 * p, v);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float aw = ash[wave][a][j];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(aw, v[e], acc[a][e]);
+        }
+      }
+      // sum over the JG row groups: lanes p + P*jg
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float sum = acc[a][e];
+          if (P == 8) sum += dppc<0x128>(sum);  // row_ror:8 pairs lanes l and l^8 in a row
+          acc[a][e] = rows4_sum(sum);
+        }
+      if (jg == 0) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          if (h0 + a < G) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) osh[wave][h0 + a][8 * p + e] = acc[a][e];
+          }
+      }
+    }
+  }
+  __syncthreads();
+  // O = sum over the valid slots in rank order (valid slots come first)
+  const int nv = n_valid_sh;
+  for (int i = tid; i < G * D; i += blockDim.x) {
+    float sum = 0.0f;
+    for (int k = 0; k < nv; ++k) sum += osh[k][i / D][i % D];
+    O[qbase + i] = from_f32<T>(sum);
+  }
+}
+
+template <typename T, int D>
+static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, const void* Kc,
+                              const void* Vc, const void* Kslc, void* O, int32_t* idx,
+                              float* score, float* w, char* ws, hipStream_t s) {
+  const int bg = d.B * d.Hkv;
+  const int n_blocks = d.nC > 0 ? (d.nC + kScanChunks - 1) / kScanChunks : 0;
+  uint64_t* cand = (uint64_t*)ws;
+  if (n_blocks > 0)
+    k_dec_scan_fast<T, D><<<dim3(bg * n_blocks), kScanThreads, 0, s>>>(
+        (const T*)qs, (const T*)Kslc, cand, d.Hkv, d.K, d.nC, n_blocks, d.sel_scale);
+  const float c2 = (float)(d.sm_scale * 1.4426950408889634);
+  k_dec_attend_fast<T, D><<<dim3(bg), kWave * d.K, 0, s>>>(
+      (const T*)q, (const T*)Kc, (const T*)Vc, cand, (T*)O, idx, score, w, d.L, d.Hq, d.Hkv,
+      d.K, d.G, n_blocks * d.K, c2);
+}
+
+hipError_t launch_decode_fast(const Dims& d, const void* q, const void* qs, const void* Kc,
+                              const void* Vc, const void* Kslc, void* O, int32_t* idx,
+                              float* score, float* w, char* ws, hipStream_t s) {
+  if (d.B * d.Hkv == 0) return hipSuccess;
+  Timed tm(HSA_KERNEL_DECODE, s);
+  if (d.dtype == 1) {
+    if (d.D == 64) launch_dec_fast_t<bf16, 64>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w, ws, s);
+    else launch_dec_fast_t<bf16, 128>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w, ws, s);
+  } else {
+    if (d.D == 64) launch_dec_fast_t<float, 64>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w, ws, s);
+    else launch_dec_fast_t<float, 128>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w, ws, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hsa

@@ -96,7 +96,7 @@ size_t ws_bytes_for(int op, const hsa::Dims& d) {
     case HSA_OP_BWD:
       return hsa::bwd_layout(d).total;
     case HSA_OP_DECODE:
-      return hsa::dec_layout(d).total;
+      return (d.flags & HSA_FLAG_GENERIC) ? hsa::dec_layout(d).total : hsa::dec_fast_ws(d);
     case HSA_OP_FWD:
       return hsa::fwd_mfma_supported(d) ? hsa::fwd_mfma_ws(d) : 0;
     default:
@@ -264,6 +264,10 @@ HSA_EXPORT hsa_status_t hsa_decode(const hsa_problem_t* p, const void* q, const 
   TRY(check_ws(HSA_OP_DECODE, d, ws, ws_bytes));
   TRY(check_pending());
   hipStream_t s = (hipStream_t)stream;
+  if (!(d.flags & HSA_FLAG_GENERIC))
+    return launched(hsa::launch_decode_fast(d, q, qs, Kcache, Vcache, Kslc, O, idx, score, w,
+                                            (char*)ws, s),
+                    "decode");
   hsa::DecLayout lay = hsa::dec_layout(d);
   return launched(hsa::launch_decode_generic(d, lay, q, qs, Kcache, Vcache, Kslc, O, idx, score,
                                              w, (char*)ws, s),

@@ -98,6 +98,11 @@ size_t fwd_mfma_ws(const Dims& d);
 hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,
                            const int32_t* idx, const float* w, void* O, char* ws, hipStream_t s);
 
+// Decode with a bandwidth-shaped scan and one wave per kept slot (both dtypes).
+size_t dec_fast_ws(const Dims& d);
+hipError_t launch_decode_fast(const Dims& d, const void* q, const void* qs, const void* Kc,
+                              const void* Vc, const void* Kslc, void* O, int32_t* idx,
+                              float* score, float* w, char* ws, hipStream_t s);
 hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void* q,
                                  const void* qs, const void* Kc, const void* Vc,
                                  const void* Kslc, void* O, int32_t* idx, float* score,

@@ -207,6 +207,34 @@ def test_decode_small(hsa, dev, ctx, generic):
     assert max_abs(npy(O), d["O"]) <= 2e-2
 
 
+@pytest.mark.parametrize("shape", [
+    ("f32_d64_g4_k4", torch.float32, 64, 4, 1, 4, 1024 + 17),
+    ("bf16_d128_g16_k16", torch.bfloat16, 128, 32, 2, 16, 64 * 40 + 5),
+    ("bf16_d64_g1_k1", torch.bfloat16, 64, 8, 8, 1, 64 * 20),
+    ("f32_d128_g4_k3", torch.float32, 128, 16, 4, 3, 64 * 9),
+], ids=lambda s: s[0])
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
+def test_decode_shapes(hsa, dev, shape, generic):
+    name, dt, D, Hq, Hkv, K, ctx = shape
+    wl = W("decode_" + name, 2, ctx, Hq, Hkv, D, 64, K, dt)
+    say("case decode", name, ctx, generic)
+    x = workloads.make_decode_inputs(wl, seed=11, ctx=ctx)
+    q, qs, Kc, Vc = (x[k].to(dev) for k in ("q", "qs", "Kc", "Vc"))
+    Kslc = hsa.pool(Kc)
+    O, idx, score, w = hsa.decode(q, qs, Kc, Vc, Kslc, K, generic=generic)
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    ks = orc.pool(x["Kc"], 64)
+    d = orc.decode(x["q"], x["qs"], x["Kc"], x["Vc"], ks, 64, K)
+    assert np.array_equal(npy(idx), d["idx"])
+    sc = npy(score)
+    fin = np.isfinite(d["score"])
+    assert np.array_equal(np.isfinite(sc), fin)
+    assert max_abs(sc, d["score"], mask=fin) <= 1e-5
+    assert max_abs(npy(w), d["w"]) <= 1e-5
+    assert max_abs(npy(O), d["O"]) <= tol_for(dt)
+
+
 # ---- full-size workloads, sampled --------------------------------------------------------
 
 def _sample_rows(wl, n, seed):
