@@ -143,6 +143,53 @@ def cpu_baseline(wl, x, budget_s: float = 20.0) -> dict:
                        f"backward in {el:.1f} s")
 
 
+def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
+    """Time the 1M-context decode step (decode_1m), caches resident in HBM."""
+    import torch
+    wl3 = workloads.WORKLOADS["decode_1m"]
+    log(f"bench: decode {wl3.name} (generating caches)")
+    x3 = workloads.make_decode_inputs(wl3, seed=0, slab=4)
+    q, qs = x3["q"].to(dev), x3["qs"].to(dev)
+    Kc, Vc = x3["Kc"].to(dev), x3["Vc"].to(dev)
+    del x3
+    Kslc3 = hsa.pool(Kc)
+    prob3 = hsa.problem(wl3.B, wl3.L, wl3.Hq, wl3.Hkv, wl3.D, wl3.K, wl3.dtype, generic=gen)
+    ws3 = hsa.workspace(_lib.HSA_OP_DECODE, prob3, dev)
+    for _ in range(3):
+        hsa.decode(q, qs, Kc, Vc, Kslc3, wl3.K, generic=gen, ws=ws3)
+    torch.cuda.synchronize()
+    log("bench: decode timing")
+    # back-to-back steps without the kernel timer (its event records are not negligible at
+    # this scale), then the same with it for the per-kernel split
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        hsa.decode(q, qs, Kc, Vc, Kslc3, wl3.K, generic=gen, ws=ws3)
+    e1.record()
+    torch.cuda.synchronize()
+    dms = e0.elapsed_time(e1) / reps
+    hsa.timer_enable(True)
+    for _ in range(reps):
+        hsa.decode(q, qs, Kc, Vc, Kslc3, wl3.K, generic=gen, ws=ws3)
+    torch.cuda.synchronize()
+    hsa.timer_enable(False)
+    kt3 = hsa.timer_read()
+    n3 = kt3["decode_attend"][0]
+    tot3 = kt3["decode_scan"][1] + kt3["decode_attend"][1]
+    el = 2
+    # the chunk-key table, the selected chunks' K and V, q, qs and O
+    dbytes = (wl3.B * wl3.nC * wl3.Hkv * wl3.D * el
+              + 2 * wl3.B * wl3.Hkv * wl3.K * wl3.S * wl3.D * el
+              + 2 * wl3.B * wl3.Hq * wl3.D * el + wl3.B * wl3.Hkv * wl3.D * el)
+    return {"workload": f"{wl3.name}: B={wl3.B} ctx={wl3.L} Hq={wl3.Hq} Hkv={wl3.Hkv} "
+                        f"d={wl3.D} K={wl3.K}",
+            "ms": round(dms, 4), "new_tokens_per_s": round(wl3.B / (dms / 1e3), 1),
+            "roofline": roofline("decode_scan+decode_attend", dict(bytes=dbytes, flops=0),
+                                 tot3 / max(n3, 1), None),
+            "scan_ms": round(kt3["decode_scan"][1] / max(n3, 1), 4),
+            "attend_ms": round(kt3["decode_attend"][1] / max(n3, 1), 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,7 +203,7 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="profiling aid: with --only, first copy this many MiB once with a plain "
                          "device copy (the scale reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["select", "fwd", "bwd"], default=None,
+    ap.add_argument("--only", choices=["select", "fwd", "bwd", "decode"], default=None,
                     help="profiling aid: after one full step, run only this entry point "
                          "--steps times and print its mean time (no JSON line)")
     args = ap.parse_args()
@@ -172,6 +219,9 @@ def main() -> int:
 
     wl = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.only == "decode":
+        log("bench: only decode", run_decode(hsa, _lib, workloads, dev, args.generic, args.steps))
+        return 0
     log(f"bench: generating {wl.name} inputs")
     x = workloads.make_inputs(wl, seed=0)
     Q, K, V, Qs, dO = (x[k].to(dev) for k in ("Q", "K", "V", "Qs", "dO"))
@@ -210,12 +260,16 @@ def main() -> int:
                                       ws=ws_bwd)}[args.only]
         torch.cuda.synchronize()
         if args.copy_mib:
+            # the source is written first and then pushed out of the 256 MB last-level cache
+            # by writing 1 GiB elsewhere, so the copy reads it from HBM
             src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+            flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
             dst = torch.empty_like(src)
+            torch.cuda.synchronize()
             dst.copy_(src)
             torch.cuda.synchronize()
             log(f"bench: copied {args.copy_mib} MiB")
-            del src, dst
+            del src, dst, flush
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
@@ -320,41 +374,7 @@ def main() -> int:
         del Q2, K2, V2, Qs2, x2, O2, ws2
 
     if not args.no_decode:
-        wl3 = workloads.WORKLOADS["decode_1m"]
-        log(f"bench: decode {wl3.name} (generating caches)")
-        x3 = workloads.make_decode_inputs(wl3, seed=0, slab=4)
-        q, qs = x3["q"].to(dev), x3["qs"].to(dev)
-        Kc, Vc = x3["Kc"].to(dev), x3["Vc"].to(dev)
-        del x3
-        Kslc3 = hsa.pool(Kc)
-        prob3 = hsa.problem(wl3.B, wl3.L, wl3.Hq, wl3.Hkv, wl3.D, wl3.K, wl3.dtype, generic=gen)
-        ws3 = hsa.workspace(_lib.HSA_OP_DECODE, prob3, dev)
-        for _ in range(3):
-            hsa.decode(q, qs, Kc, Vc, Kslc3, wl3.K, generic=gen, ws=ws3)
-        torch.cuda.synchronize()
-        log("bench: decode timing")
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 50
-        hsa.timer_enable(True)
-        e0.record()
-        for _ in range(reps):
-            hsa.decode(q, qs, Kc, Vc, Kslc3, wl3.K, generic=gen, ws=ws3)
-        e1.record()
-        torch.cuda.synchronize()
-        hsa.timer_enable(False)
-        n3, tot3 = hsa.timer_read()["decode"]
-        dms = e0.elapsed_time(e1) / reps
-        el = 2
-        # the chunk-key table, the selected chunks' K and V, q, qs and O
-        dbytes = (wl3.B * wl3.nC * wl3.Hkv * wl3.D * el
-                  + 2 * wl3.B * wl3.Hkv * wl3.K * wl3.S * wl3.D * el
-                  + 2 * wl3.B * wl3.Hq * wl3.D * el + wl3.B * wl3.Hkv * wl3.D * el)
-        out["decode"] = {"workload": f"{wl3.name}: B={wl3.B} ctx={wl3.L} Hq={wl3.Hq} "
-                                     f"Hkv={wl3.Hkv} d={wl3.D} K={wl3.K}",
-                         "ms": round(dms, 4), "new_tokens_per_s": round(wl3.B / (dms / 1e3), 1),
-                         "roofline": roofline("decode", dict(bytes=dbytes, flops=0),
-                                              tot3 / max(n3, 1), None)}
-        del q, qs, Kc, Vc, Kslc3
+        out["decode"] = run_decode(hsa, _lib, workloads, dev, gen, reps=50)
 
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")

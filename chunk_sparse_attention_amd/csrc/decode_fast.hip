@@ -15,13 +15,15 @@
 //           value rows are read as independent 16-byte pieces so that all of a chunk's loads
 //           are in flight at once.  The K weighted slot outputs meet in LDS and are summed in
 //           slot order.
+#include <algorithm>
+
 #include "hsa_common.h"
 #include "hsa_launch.h"
 #include "tile_common.h"
 
 namespace hsa {
 
-constexpr int kScanThreads = 256;
+constexpr int kScanThreads = 1024;
 constexpr int kScanPer = 1;                                   // chunks per lane
 constexpr int kScanChunks = kScanThreads * kScanPer;          // chunks per scan block
 constexpr int kScanWaves = kScanThreads / kWave;
@@ -158,97 +160,155 @@ k_dec_scan_fast(const T* __restrict__ qs,
     if (lane == 0) wtop[wave][k] = best;
   }
   __syncthreads();
-  // the block's ranked top-K from the waves' lists
+  // the block's ranked top-K from the waves' lists (at most 16 * 16 keys: four per lane)
   if (wave == 0) {
-    uint64_t v = lane < kScanWaves * K ? wtop[lane / K][lane % K] : 0;
+    uint64_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = lane + kWave * i;
+      v[i] = j < kScanWaves * K ? wtop[j / K][j % K] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = i + 1; j < 4; ++j)
+        if (v[j] > v[i]) {
+          const uint64_t t = v[i];
+          v[i] = v[j];
+          v[j] = t;
+        }
     uint64_t* out = cand + ((size_t)bg * n_blocks + blk) * K;
     for (int k = 0; k < K; ++k) {
-      const uint64_t best = wave_max_key(v);
-      if (v == best) v = 0;
+      const uint64_t best = wave_max_key(v[0]);
+      if (best != 0 && v[0] == best) {
+        v[0] = v[1];
+        v[1] = v[2];
+        v[2] = v[3];
+        v[3] = 0;
+      }
       if (lane == 0) out[k] = best;
     }
   }
 }
 
+__device__ __forceinline__ float wave_sum_f(float v) { return rows4_sum(row16_sum(v)); }
+__device__ __forceinline__ float wave_max_f(float v) { return rows4_max(row16_max(v)); }
+
+// Ranked top-K of the scan's candidates in every wave; lane k < K returns slot k's key.
+__device__ __forceinline__ uint64_t rank_candidates(const uint64_t* __restrict__ cb, int n_cand,
+                                                    int K, int lane) {
+  uint64_t mykey = 0;
+  if (n_cand <= 2 * kWave) {
+    // at most two keys per lane: a sorted pair
+    uint64_t a = lane < n_cand ? cb[lane] : 0;
+    uint64_t c = lane + kWave < n_cand ? cb[lane + kWave] : 0;
+    if (c > a) {
+      const uint64_t t = a;
+      a = c;
+      c = t;
+    }
+    for (int k = 0; k < K; ++k) {
+      const uint64_t best = wave_max_key(a);
+      if (best != 0 && a == best) {
+        a = c;
+        c = 0;
+      }
+      if (lane == k) mykey = best;
+    }
+  } else {
+    uint64_t top[kMaxK];
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i) top[i] = 0;
+    for (int i = lane; i < n_cand; i += kWave) topk_insert(top, cb[i], K);
+    for (int k = 0; k < K; ++k) {
+      const uint64_t best = wave_max_key(top[0]);
+      if (best != 0 && top[0] == best) topk_pop(top);
+      if (lane == k) mykey = best;
+    }
+  }
+  return mykey;
+}
+
 // D elements per row = P pieces of 8; the 64 lanes of a wave form JG = 64/P groups of P
-// lanes, and group jg reads rows jg, jg+JG, ... of the chunk.  LDS: the group's queries, the
-// attention weights of four heads per wave, and the K weighted slot outputs (at most
-// 8 + 16 + 128 KB for D = 128, K = G = 16).
-template <typename T, int D>
-__global__ void __launch_bounds__(1024) k_dec_attend_fast(
+// lanes, and group jg reads rows jg, jg+JG, ... of the chunk.  The block has WS waves per
+// slot, each taking HW of the group's heads.  LDS: the group's queries, the attention weights
+// of four heads per wave, and the K weighted slot outputs (at most 8 + 64 + 128 KB for
+// D = 128, K = G = 16).
+template <typename T, int D, int NT, int ZH>
+__global__ void __launch_bounds__(NT) k_dec_attend_fast(
     const T* __restrict__ q, const T* __restrict__ Kc, const T* __restrict__ Vc,
     const uint64_t* __restrict__ cand, T* __restrict__ O, int32_t* __restrict__ idx,
     float* __restrict__ score, float* __restrict__ w, int ctx, int Hq, int Hkv, int K, int G,
-    int n_cand, float c2) {
+    int WS, int HW, int n_cand, float c2) {
   constexpr int P = D / 8;
   constexpr int JG = kWave / P;
   constexpr int RPL = kChunk / JG;  // rows per lane in the value product
   __shared__ float qsh[kMaxG][D];
-  __shared__ float ash[kMaxK][4][kChunk];
+  __shared__ float ash[NT / kWave][4][kChunk];
   __shared__ float osh[kMaxK][kMaxG][D];
-  __shared__ int n_valid_sh;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int slot = wave / WS, h_lo = (wave % WS) * HW, h_hi = min(G, h_lo + HW);
   const int bg = blockIdx.x;
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const size_t qbase = ((size_t)b * Hq + (size_t)g * G) * D;
   for (int i = tid; i < G * D; i += blockDim.x) qsh[i / D][i % D] = to_f32(q[qbase + i]);
 
-  // Every wave merges the candidates into the same ranked top-K and walks the stick-breaking
-  // recursion in rank order (in double): w_k = p_k * R, R <- R * (1 - p_k).
-  uint64_t top[kMaxK];
+  const uint64_t mykey = rank_candidates(cand + (size_t)bg * n_cand, n_cand, K, lane);
+  // stick-breaking in rank order: slot k needs p_k * prod_{j<k} (1 - p_j), a prefix
+  // product over lanes 0..K-1 (masked slots have p = 0 and come last)
+  const double p = mykey != 0 ? sigmoid_d((double)key_score(mykey)) : 0.0;
+  double keep = 1.0 - p;
 #pragma unroll
-  for (int i = 0; i < kMaxK; ++i) top[i] = 0;
-  const uint64_t* cb = cand + (size_t)bg * n_cand;
-#pragma unroll 4
-  for (int i = lane; i < n_cand; i += kWave) topk_insert(top, cb[i], K);
-  uint64_t mine = 0;  // the key of this wave's slot
-  double wk = 0.0, rem = 1.0;
-  int n_valid = 0;
-  for (int k = 0; k < K; ++k) {
-    const uint64_t best = wave_max_key(top[0]);
-    if (best != 0 && top[0] == best) topk_pop(top);
-    if (best != 0) {
-      const double pk = sigmoid_d((double)key_score(best));
-      if (k == wave) {
-        mine = best;
-        wk = pk * rem;
-      }
-      rem *= 1.0 - pk;
-      ++n_valid;
-    }
+  for (int o = 1; o < 16; o <<= 1) {
+    const double x = __shfl_up(keep, o, 16);
+    if ((lane & 15) >= o) keep *= x;
   }
-  if (lane == 0) {
-    const size_t o = (size_t)bg * K + wave;
-    if (mine == 0) {
+  double excl = __shfl_up(keep, 1, 16);
+  if ((lane & 15) == 0) excl = 1.0;
+  const double wslot = p * excl;
+  if (wave == 0 && lane < K) {
+    const size_t o = (size_t)bg * K + lane;
+    if (mykey == 0) {
       idx[o] = -1;
       if (score) score[o] = -__builtin_inff();
       w[o] = 0.0f;
     } else {
-      idx[o] = key_chunk(mine);
-      if (score) score[o] = key_score(mine);
-      w[o] = (float)wk;
+      idx[o] = key_chunk(mykey);
+      if (score) score[o] = key_score(mykey);
+      w[o] = (float)wslot;
     }
   }
-  if (tid == 0) n_valid_sh = n_valid;
+  const int n_valid = __popcll(__ballot(lane < K && mykey != 0));
+  // this wave's slot, read from lane `slot`
+  const uint32_t mhi = __builtin_amdgcn_readlane((uint32_t)(mykey >> 32), slot);
+  const uint32_t mlo = __builtin_amdgcn_readlane((uint32_t)mykey, slot);
+  const uint64_t mine = ((uint64_t)mhi << 32) | mlo;
+  const float wf = __shfl((float)wslot, slot);
   __syncthreads();  // qsh ready
 
   if (mine != 0) {
     const int c = key_chunk(mine);
-    const float wf = (float)wk;
     const size_t kvstride = (size_t)Hkv * D;
     const size_t cbase = ((b * ctx + (size_t)c * kChunk) * Hkv + g) * D;
-    // logits: lane j owns key row j (products of stored values summed in fp32)
+    const int p8 = lane % P, jg = lane / P;
+    // key row j in lane j; for D = 64 the value pieces are requested at the same time
     RawRow<T, D> kr;
     kr.load(Kc + cbase + (size_t)lane * kvstride);
-    float z[kMaxG];
+    RawRow<T, 8> vp[RPL];
+    if (D == 64) {
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
+      for (int i = 0; i < RPL; ++i)
+        vp[i].load(Vc + cbase + (size_t)(jg + JG * i) * kvstride + 8 * p8);
+    }
+    float z[ZH];  // ZH >= HW heads per wave
+#pragma unroll
+    for (int h = 0; h < ZH; ++h) {
       z[h] = 0.0f;
-      if (h < G) {
+      if (h < h_hi - h_lo) {
 #pragma unroll
         for (int e0 = 0; e0 < D; e0 += 8) {
-          int off = h * D + e0;  // pinned in the loop as in the scan
+          int off = (h_lo + h) * D + e0;  // the empty asm keeps the query reads in the loop
           asm volatile("" : "+v"(off));
           const float4 qa = *reinterpret_cast<const float4*>(&qsh[0][0] + off);
           const float4 qb = *reinterpret_cast<const float4*>(&qsh[0][0] + off + 4);
@@ -258,23 +318,27 @@ __global__ void __launch_bounds__(1024) k_dec_attend_fast(
         }
       }
     }
-    const int p = lane % P, jg = lane / P;
+    if (D != 64) {
 #pragma unroll
-    for (int h0 = 0; h0 < kMaxG; h0 += 4) {
-      if (h0 >= G) break;
+      for (int i = 0; i < RPL; ++i)
+        vp[i].load(Vc + cbase + (size_t)(jg + JG * i) * kvstride + 8 * p8);
+    }
+#pragma unroll
+    for (int h0 = 0; h0 < ZH; h0 += 4) {
+      if (h0 >= h_hi - h_lo) break;
       // softmax-off-by-one of four heads (log2 domain), scaled by the slot weight
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         float aw = 0.0f;
-        if (h0 + a < G) {
+        if (h0 + a < h_hi - h_lo) {
           const float zz = z[h0 + a] * c2;
-          const float m = fmaxf(0.0f, wave_max(zz));
+          const float m = fmaxf(0.0f, wave_max_f(zz));
           const float ex = exp2f(zz - m);
-          aw = wf * ex / (exp2f(-m) + wave_sum(ex));
+          aw = wf * ex / (exp2f(-m) + wave_sum_f(ex));
         }
         ash[wave][a][lane] = aw;
       }
-      // value product: lane (jg, p) accumulates rows jg + JG*i of piece p
+      // value product: lane (jg, p8) accumulates rows jg + JG*i of piece p8
       float acc[4][8];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -283,16 +347,14 @@ __global__ void __launch_bounds__(1024) k_dec_attend_fast(
 #pragma unroll
       for (int i = 0; i < RPL; ++i) {
         const int j = jg + JG * i;
-        float v[8];
-        load8(Vc + cbase + (size_t)j * kvstride + 8 * p, v);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const float aw = ash[wave][a][j];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(aw, v[e], acc[a][e]);
+          for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(aw, vp[i].get(e), acc[a][e]);
         }
       }
-      // sum over the JG row groups: lanes p + P*jg
+      // sum over the JG row groups: lanes p8 + P*jg
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -304,19 +366,18 @@ __global__ void __launch_bounds__(1024) k_dec_attend_fast(
       if (jg == 0) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
-          if (h0 + a < G) {
+          if (h0 + a < h_hi - h_lo) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) osh[wave][h0 + a][8 * p + e] = acc[a][e];
+            for (int e = 0; e < 8; ++e) osh[slot][h_lo + h0 + a][8 * p8 + e] = acc[a][e];
           }
       }
     }
   }
   __syncthreads();
   // O = sum over the valid slots in rank order (valid slots come first)
-  const int nv = n_valid_sh;
   for (int i = tid; i < G * D; i += blockDim.x) {
     float sum = 0.0f;
-    for (int k = 0; k < nv; ++k) sum += osh[k][i / D][i % D];
+    for (int k = 0; k < n_valid; ++k) sum += osh[k][i / D][i % D];
     O[qbase + i] = from_f32<T>(sum);
   }
 }
@@ -328,20 +389,32 @@ static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, cons
   const int bg = d.B * d.Hkv;
   const int n_blocks = d.nC > 0 ? (d.nC + kScanChunks - 1) / kScanChunks : 0;
   uint64_t* cand = (uint64_t*)ws;
-  if (n_blocks > 0)
+  if (n_blocks > 0) {
+    Timed tm(HSA_KERNEL_DECODE_SCAN, s);
     k_dec_scan_fast<T, D><<<dim3(bg * n_blocks), kScanThreads, 0, s>>>(
         (const T*)qs, (const T*)Kslc, cand, d.Hkv, d.K, d.nC, n_blocks, d.sel_scale);
+  }
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);
-  k_dec_attend_fast<T, D><<<dim3(bg), kWave * d.K, 0, s>>>(
-      (const T*)q, (const T*)Kc, (const T*)Vc, cand, (T*)O, idx, score, w, d.L, d.Hq, d.Hkv,
-      d.K, d.G, n_blocks * d.K, c2);
+  Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
+  // WS waves per slot (each HW heads), at most 16 waves; the launch bound sets the register
+  // budget (256 VGPRs up to 8 waves, 128 above)
+  const int WS = std::max(1, std::min((d.G + 3) / 4, 16 / d.K));
+  const int HW = (d.G + WS - 1) / WS;
+  const int nt = kWave * d.K * WS;
+  auto go = [&](auto kern) {
+    kern<<<dim3(bg), nt, 0, s>>>((const T*)q, (const T*)Kc, (const T*)Vc, cand, (T*)O, idx,
+                                 score, w, d.L, d.Hq, d.Hkv, d.K, d.G, WS, HW, n_blocks * d.K,
+                                 c2);
+  };
+  if (nt <= 512) go(k_dec_attend_fast<T, D, 512, 16>);
+  else if (HW <= 4) go(k_dec_attend_fast<T, D, 1024, 4>);
+  else go(k_dec_attend_fast<T, D, 1024, 16>);
 }
 
 hipError_t launch_decode_fast(const Dims& d, const void* q, const void* qs, const void* Kc,
                               const void* Vc, const void* Kslc, void* O, int32_t* idx,
                               float* score, float* w, char* ws, hipStream_t s) {
   if (d.B * d.Hkv == 0) return hipSuccess;
-  Timed tm(HSA_KERNEL_DECODE, s);
   if (d.dtype == 1) {
     if (d.D == 64) launch_dec_fast_t<bf16, 64>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w, ws, s);
     else launch_dec_fast_t<bf16, 128>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w, ws, s);

@@ -187,18 +187,25 @@ hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void
   uint64_t* cand = (uint64_t*)(ws + lay.cand);
   float sm = (float)d.sm_scale;
   // d.L is the context length; the new token may select every complete chunk.
-  Timed tm(HSA_KERNEL_DECODE, s);
   if (d.dtype == 1) {
-    k_dec_scan<bf16><<<dim3(bg * lay.n_blocks), 256, 0, s>>>(
-        (const bf16*)qs, (const bf16*)Kslc, cand, d.Hkv, d.D, d.K, d.nC, lay.n_blocks,
-        d.sel_scale);
+    {
+      Timed tm(HSA_KERNEL_DECODE_SCAN, s);
+      k_dec_scan<bf16><<<dim3(bg * lay.n_blocks), 256, 0, s>>>(
+          (const bf16*)qs, (const bf16*)Kslc, cand, d.Hkv, d.D, d.K, d.nC, lay.n_blocks,
+          d.sel_scale);
+    }
+    Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
     k_dec_attend<bf16><<<dim3(bg), 64, 0, s>>>((const bf16*)q, (const bf16*)Kc, (const bf16*)Vc,
                                                cand, (bf16*)O, idx, score, w, d.L, d.Hq, d.Hkv,
                                                d.D, d.S, d.K, d.G, d.nC, lay.n_blocks, sm);
   } else {
-    k_dec_scan<float><<<dim3(bg * lay.n_blocks), 256, 0, s>>>(
-        (const float*)qs, (const float*)Kslc, cand, d.Hkv, d.D, d.K, d.nC, lay.n_blocks,
-        d.sel_scale);
+    {
+      Timed tm(HSA_KERNEL_DECODE_SCAN, s);
+      k_dec_scan<float><<<dim3(bg * lay.n_blocks), 256, 0, s>>>(
+          (const float*)qs, (const float*)Kslc, cand, d.Hkv, d.D, d.K, d.nC, lay.n_blocks,
+          d.sel_scale);
+    }
+    Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
     k_dec_attend<float><<<dim3(bg), 64, 0, s>>>(
         (const float*)q, (const float*)Kc, (const float*)Vc, cand, (float*)O, idx, score, w,
         d.L, d.Hq, d.Hkv, d.D, d.S, d.K, d.G, d.nC, lay.n_blocks, sm);

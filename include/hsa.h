@@ -176,8 +176,9 @@ typedef enum {
   HSA_KERNEL_BWD_P1 = 6,     /* backward phase 1: per token dQ, dw, ds, dQs */
   HSA_KERNEL_BWD_P2 = 7,     /* backward phase 2: per chunk dK, dV, dKslc partials */
   HSA_KERNEL_BWD_REDUCE = 8, /* backward: fixed-order reduction of the phase-2 partials */
-  HSA_KERNEL_DECODE = 9,     /* decode step (scan and attend) */
-  HSA_KERNEL_COUNT = 10
+  HSA_KERNEL_DECODE_SCAN = 9,    /* decode: scan of the chunk-key table, per-block top-K */
+  HSA_KERNEL_DECODE_ATTEND = 10, /* decode: merge, weights and attention over the kept chunks */
+  HSA_KERNEL_COUNT = 11
 } hsa_kernel_t;
 
 /* enable != 0: forget earlier records and start recording; enable == 0: stop recording
