@@ -43,24 +43,48 @@ __device__ void block_bitonic_sort(uint32_t* keys, int N) {
   }
 }
 
-// Inclusive scan of N ints in LDS (Hillis-Steele), op 0 = sum, 1 = max.
+// Inclusive scan of N ints in LDS (N a power of two, at most 4*NT), op 0 = sum, 1 = max
+// (values >= -1).  Each thread scans up to four consecutive elements in registers, the
+// waves scan the thread totals with shuffles, and wtot (NT/64 ints) carries the wave totals.
 template <int NT>
-__device__ void block_inclusive_scan(int* a, int* tmp, int N, int op) {
-  for (int off = 1; off < N; off <<= 1) {
-    for (int i = threadIdx.x; i < N; i += NT) {
-      int v = a[i];
-      if (i >= off) v = op == 0 ? v + a[i - off] : max(v, a[i - off]);
-      tmp[i] = v;
+__device__ void block_inclusive_scan(int* a, int* wtot, int N, int op) {
+  const int ident = op == 0 ? 0 : -1;
+  const int P = N > NT ? N / NT : 1;
+  const int base = threadIdx.x * P;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  int v[4];
+  int acc = ident;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    v[p] = ident;
+    if (p < P && base + p < N) {
+      const int x = a[base + p];
+      acc = op == 0 ? acc + x : max(acc, x);
+      v[p] = acc;
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < N; i += NT) a[i] = tmp[i];
-    __syncthreads();
   }
+  int x = acc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x = op == 0 ? x + y : max(x, y);
+  }
+  if (lane == 63) wtot[wave] = x;
+  __syncthreads();
+  int pre = ident;
+  for (int w = 0; w < wave; ++w) pre = op == 0 ? pre + wtot[w] : max(pre, wtot[w]);
+  const int below = __shfl_up(x, 1, 64);
+  if (lane > 0) pre = op == 0 ? pre + below : max(pre, below);
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    if (p < P && base + p < N) a[base + p] = op == 0 ? pre + v[p] : max(pre, v[p]);
+  __syncthreads();
 }
 
 // From sorted keys[0..N): the number of valid edges and the job list.  A job is up to
 // `tpj` consecutive edges of one chunk; jobs[j] = first edge | (edge count << 16).
-// Scratch arrays rs and tmp hold N ints each.  Returns through *n_valid / *n_jobs (LDS).
+// Scratch arrays rs and tmp hold N ints each (tmp also holds the scan's wave totals).
+// Returns through *n_valid / *n_jobs (LDS).
 template <int NT>
 __device__ void build_jobs(const uint32_t* keys, int N, int tpj, int* rs, int* tmp,
                            uint32_t* jobs, int* n_valid, int* n_jobs) {
@@ -77,7 +101,7 @@ __device__ void build_jobs(const uint32_t* keys, int N, int tpj, int* rs, int* t
   }
   __syncthreads();
   block_inclusive_scan<NT>(rs, tmp, N, 1);  // rs[i] = first edge of i's chunk run
-  int* jf = tmp + N;                        // second scratch half
+  int* jf = tmp + 64;
   for (int i = threadIdx.x; i < N; i += NT) jf[i] = (i < nv && (i - rs[i]) % tpj == 0) ? 1 : 0;
   __syncthreads();
   block_inclusive_scan<NT>(jf, tmp, N, 0);
@@ -95,75 +119,153 @@ __device__ void build_jobs(const uint32_t* keys, int N, int tpj, int* rs, int* t
 
 // Conflict-free rounds.  Jobs of one round touch disjoint tokens, so the waves of a round
 // can update the tile's LDS accumulators with plain read-add-write (LDS float atomics are
-// slow on this part).  Greedy colouring in job order: a job takes the lowest round none of
-// its tokens is in yet.  A token has at most 16 edges and a job at most 4 tokens, so no job
-// needs a round above 4*15 = 60.  Wave 0 does the colouring with the per-token round masks
-// in registers (lane tl holds token tl's mask) so the sequential loop has no memory latency.
-// In: jobs[0..n_jobs), keys.  Out: order[] = jobs grouped by round (job order kept inside a
-// round), roff[0..n_rounds] = round offsets, *n_rounds.  Scratch: jround[n_jobs] (int).
-template <int NT>
-__device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, int n_jobs,
-                             int* jround, int* roff, uint32_t* order, int* n_rounds) {
+// slow on this part).  The rounds are the greedy colouring in job order -- a job takes the
+// lowest round that no earlier job sharing one of its tokens has -- computed in parallel: a
+// job picks its round as soon as all those earlier jobs have theirs, which gives the same
+// rounds as colouring the jobs one by one, in as many block-wide steps as the longest chain
+// of such dependencies (about 20 for random top-8 selections).  A token has at most 16 edges
+// and a job at most 4 tokens, so no round exceeds 4*15 = 60.
+// In: jobs[0..n_jobs), keys.  Out: order[] = jobs grouped by round, roff[0..n_rounds] =
+// round offsets, *n_rounds.  Within a round no token repeats, so the order inside a round
+// does not change any token's accumulation order.  Scratch: colour[n_jobs], jl[TT*16],
+// cnt[64] (ints), tmask[TT].
+template <int NT, int TT>
+__device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, int n_jobs, int Kt,
+                             int* colour, int* jl, int* cnt, unsigned long long* tmask,
+                             int* roff, uint32_t* order, int* n_rounds) {
+  constexpr int kNone = 0x7fffffff;
+  static_assert(TT * 16 % 4 == 0, "token lists are read as 16-byte words");
+  for (int i = threadIdx.x; i < TT * 16; i += NT) jl[i] = kNone;
+  for (int i = threadIdx.x; i < 64; i += NT) cnt[i] = 0;
+  for (int i = threadIdx.x; i < TT; i += NT) tmask[i] = 0;
+  __syncthreads();
+  // token -> its jobs (every (token, slot) edge lies in exactly one job)
+  for (int j = threadIdx.x; j < n_jobs; j += NT) {
+    const uint32_t job = jobs[j];
+    const int e0 = (int)(job & 0xffff), c = (int)(job >> 16);
+    for (int i = 0; i < c; ++i) {
+      const uint32_t k = keys[e0 + i];
+      jl[edge_token(k) * 16 + edge_slot(k)] = j;
+    }
+    colour[j] = -1;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < TT; t += NT) {  // ascending job order per token
+    int v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = q < Kt ? jl[t * 16 + q] : kNone;
+#pragma unroll
+    for (int a = 1; a < 16; ++a)
+#pragma unroll
+      for (int q = a; q > 0; --q)
+        if (v[q] < v[q - 1]) {
+          const int tmp = v[q];
+          v[q] = v[q - 1];
+          v[q - 1] = tmp;
+        }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) jl[t * 16 + q] = v[q];
+  }
+  __syncthreads();
+  // rounds: a job waits until every earlier job of its tokens has a round.  The earlier jobs
+  // of one token form a chain (each waits for the one before it), so a job is ready exactly
+  // when the latest earlier job of each of its tokens has a round.  Each lane takes its jobs
+  // (j = lane + s*NT) in ascending order and re-checks its current job until it is ready;
+  // the smallest job without a round is always some lane's current job and is ready, so the
+  // waves make progress without block barriers.  tmask[t] collects the rounds of t's jobs so
+  // far (its earlier jobs); a job adds its round there before it publishes the round.
+  {
+    constexpr int kJpt = 4;  // jobs per lane: n_jobs <= TT*16 <= 4*NT
+    const volatile int* vcol = colour;
+    int nts[kJpt], prevs[kJpt][4], tks[kJpt][4];
+#pragma unroll
+    for (int s = 0; s < kJpt; ++s) {  // every job's tokens and latest earlier jobs, up front
+      const int j = threadIdx.x + s * NT;
+      nts[s] = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        prevs[s][i] = -1;
+        tks[s][i] = 0;
+      }
+      if (j < n_jobs) {
+        const uint32_t job = jobs[j];
+        const int e0 = (int)(job & 0xffff);
+        nts[s] = (int)(job >> 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < nts[s]) {
+            tks[s][i] = edge_token(keys[e0 + i]);
+            const int4* l4 = reinterpret_cast<const int4*>(jl + tks[s][i] * 16);
+            int pv = -1;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const int4 x = l4[w];
+              pv = x.x < j ? max(pv, x.x) : pv;
+              pv = x.y < j ? max(pv, x.y) : pv;
+              pv = x.z < j ? max(pv, x.z) : pv;
+              pv = x.w < j ? max(pv, x.w) : pv;
+            }
+            prevs[s][i] = pv;
+          }
+        }
+      }
+    }
+    int cur = 0;
+    for (;;) {
+      int nt = 0, prev[4], tk[4];
+#pragma unroll
+      for (int s = 0; s < kJpt; ++s)
+        if (s == cur) {
+          nt = nts[s];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            prev[i] = prevs[s][i];
+            tk[i] = tks[s][i];
+          }
+        }
+      if (!__ballot(nt > 0)) break;
+      if (nt > 0) {
+        bool ready = true;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < nt && prev[i] >= 0 && vcol[prev[i]] < 0) ready = false;
+        if (ready) {
+          uint64_t u = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i < nt) u |= tmask[tk[i]];
+          const int r = __builtin_ctzll(~u);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i < nt) atomicOr(&tmask[tk[i]], 1ull << r);
+          __threadfence_block();
+          colour[threadIdx.x + cur * NT] = r;
+          ++cur;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // group by round: sizes, offsets (rounds used are 0..n_rounds-1), then placement
+  for (int j = threadIdx.x; j < n_jobs; j += NT) atomicAdd(&cnt[colour[j]], 1);
+  __syncthreads();
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    uint64_t tmask = 0;   // rounds used by token `lane`
-    uint32_t count = 0;   // jobs in round `lane`
-    int rmax = -1;
-    for (int jb = 0; jb < n_jobs; jb += 64) {
-      // lane i fetches job jb+i: its tokens packed 6 bits each, count in the top bits
-      uint32_t packed = 0;
-      if (jb + lane < n_jobs) {
-        const uint32_t job = jobs[jb + lane];
-        const int e0 = (int)(job & 0xffff), cnt = (int)(job >> 16);
-        packed = (uint32_t)cnt << 24;
-        for (int i = 0; i < cnt; ++i) packed |= (uint32_t)edge_token(keys[e0 + i]) << (6 * i);
-      }
-      int myr = 0;
-      const int nb = min(64, n_jobs - jb);
-      for (int i = 0; i < nb; ++i) {
-        const uint32_t pk = __builtin_amdgcn_readlane(packed, i);
-        const int cnt = (int)(pk >> 24);
-        uint64_t used = 0;
-        bool mine = false;
-        for (int q = 0; q < cnt; ++q) {
-          const int tl = (int)((pk >> (6 * q)) & 63);
-          used |= ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(tmask >> 32), tl) << 32) |
-                  (uint64_t)__builtin_amdgcn_readlane((uint32_t)tmask, tl);
-          mine |= lane == tl;
-        }
-        const int r = __builtin_ctzll(~used);
-        if (mine) tmask |= 1ull << r;
-        if (lane == r) ++count;
-        if (lane == i) myr = r;
-        rmax = max(rmax, r);
-      }
-      if (jb + lane < n_jobs) jround[jb + lane] = myr;
-    }
-    // exclusive scan of the round sizes (lane r holds round r's size)
-    uint32_t incl = count;
+    const int size = cnt[lane];
+    int incl = size;
+#pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
     }
-    uint32_t next = incl - count;  // start of round `lane`, advanced as jobs are placed
-    if (lane <= rmax) roff[lane] = (int)next;
-    if (lane == 0) {
-      roff[rmax + 1] = n_jobs;
-      *n_rounds = rmax + 1;
-    }
-    // stable placement in job order
-    for (int jb = 0; jb < n_jobs; jb += 64) {
-      const int myr = jb + lane < n_jobs ? jround[jb + lane] : 0;
-      const uint32_t myjob = jb + lane < n_jobs ? jobs[jb + lane] : 0u;
-      const int nb = min(64, n_jobs - jb);
-      for (int i = 0; i < nb; ++i) {
-        const int r = __builtin_amdgcn_readlane(myr, i);
-        const uint32_t pos = __builtin_amdgcn_readlane(next, r);
-        if (lane == r) ++next;
-        if (lane == i) order[pos] = myjob;
-      }
-    }
+    const uint64_t nz = __ballot(size > 0);
+    const int nr = nz ? 64 - __builtin_clzll(nz) : 0;
+    if (lane <= nr) roff[lane] = incl - size;
+    if (lane == 0) *n_rounds = nr;
+    cnt[lane] = incl - size;  // placement cursor of round `lane`
   }
+  __syncthreads();
+  for (int j = threadIdx.x; j < n_jobs; j += NT) order[atomicAdd(&cnt[colour[j]], 1)] = jobs[j];
   __syncthreads();
 }
 
@@ -182,6 +284,9 @@ __global__ void __launch_bounds__(NT) k_tile_prep(const int32_t* __restrict__ id
   __shared__ uint32_t keys[NMAX];
   __shared__ uint32_t jobs[NMAX];
   __shared__ int scratch[3 * NMAX];
+  __shared__ __attribute__((aligned(16))) int jl[TT * 16];
+  __shared__ int cnt[64];
+  __shared__ unsigned long long tmask[TT];
   __shared__ int n_valid_sh, n_jobs_sh, n_rounds_sh;
   const int bg = blockIdx.x % BG;
   const int tile = blockIdx.x / BG;
@@ -207,7 +312,8 @@ __global__ void __launch_bounds__(NT) k_tile_prep(const int32_t* __restrict__ id
   const int n_jobs = n_jobs_sh;
   uint32_t* order = reinterpret_cast<uint32_t*>(scratch + NMAX);
   int* roff = scratch + 2 * NMAX;
-  build_rounds<NT>(keys, jobs, n_jobs, scratch, roff, order, &n_rounds_sh);
+  build_rounds<NT, TT>(keys, jobs, n_jobs, Kt, scratch, jl, cnt, tmask, roff, order,
+                       &n_rounds_sh);
   uint32_t* out = prep + (size_t)blockIdx.x * prep_words(TT);
   const int nv = n_valid_sh, nr = n_rounds_sh;
   if (threadIdx.x == 0) {
