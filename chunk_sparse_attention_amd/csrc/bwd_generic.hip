@@ -46,6 +46,9 @@ BwdLayout bwd_layout(const Dims& d) {
   l.kop = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
   l.vop = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
   l.prep = take(tile_prep_bytes(d));
+  // per (token, group, slot, head): the softmax normaliser (log2 domain) and D = <dO, O_k>
+  l.lse = take(sizeof(float) * bg * E * d.G);
+  l.dd = take(sizeof(float) * bg * E * d.G);
   l.total = o;
   return l;
 }

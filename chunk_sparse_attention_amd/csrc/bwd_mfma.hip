@@ -13,7 +13,8 @@
 //   dw_edge = sum over the token's heads of D
 // then per token the stick-breaking chain rule gives ds and dQs.
 // Phase 2 (chunk segments over the chunk -> (token, slot) index): per job of 16 query rows
-//   S = Q K_c^T, dP = dO V_c^T, P, D, dS as above (rows = queries, columns = keys)
+//   S = Q K_c^T, dP = dO V_c^T; P from phase 1's softmax normaliser, D from phase 1, dS as
+//   above (rows = queries, columns = keys)
 //   dV^T += dO^T (w P),  dK^T += Q^T dS                  (MFMA 16x16x16, registers)
 //   dKslc += ds * Qs
 // and every segment writes fp32 partials that a fixed-order reduction sums per chunk.
@@ -33,6 +34,15 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c) {
 __device__ __forceinline__ s16x4 pack_bf16x4(f32x4 v) {
   return __builtin_bit_cast(s16x4, __builtin_convertvector(v, bf16x4));
 }
+// gfx950 transposing LDS read of four 16-bit elements: in each group of 16 lanes, lane j
+// receives element j%4 of the 8-byte word that lane 4*i + j/4 addresses, for i = 0..3.
+// With lane m of group `blk` addressing row 4*blk + m/4, column c0 + 4*(m%4) of a row-major
+// LDS matrix, lane j gets column c0 + j of rows 4*blk .. 4*blk+3: the 16x16x16 MFMA
+// A operand of the transposed matrix.  p must point into LDS.
+__device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+}
 
 
 // ---- phase 1 -------------------------------------------------------------------------------
@@ -43,8 +53,9 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
     const bf16* __restrict__ Kt, const bf16* __restrict__ Kslc, const int32_t* __restrict__ idx,
     const float* __restrict__ score, const float* __restrict__ w, const bf16* __restrict__ dO,
     const uint32_t* __restrict__ prep, bf16* __restrict__ dQ, bf16* __restrict__ dQs,
-    float* __restrict__ ds_out, float* __restrict__ dw_out, int L, int Hq, int Hkv, int Kn,
-    int nC, int BG, float c2, float sm_scale, float sel_scale) {
+    float* __restrict__ ds_out, float* __restrict__ dw_out, float* __restrict__ lse_out,
+    float* __restrict__ dd_out, int L, int Hq, int Hkv, int Kn, int nC, int BG, float c2,
+    float sm_scale, float sel_scale) {
   constexpr int NT = 512, NW = NT / 64;
   constexpr int DP = D + 1;
   constexpr int KS = D / 32;
@@ -78,39 +89,105 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int col = lane % 16, blk = lane / 16;
   const int slot = col / G, head = col % G;
-  bf16x8 ka[4][KS], vr[4][KS], kt[DT][2];
-  int cur = -1;
-  for (int r = 0; r < n_rounds; ++r) {
+  // this wave's share of round r: [rb(r), re(r)), and its next job after job j of round r
+  auto rb = [&](int r) {
     const int a = roff[r], n = roff[r + 1] - a;
-    const int jb = a + (int)((long)n * wv / NW), je = a + (int)((long)n * (wv + 1) / NW);
-    for (int j = jb; j < je; ++j) {
-      const uint32_t job = __builtin_amdgcn_readfirstlane(order[j]);
-      const int e0 = (int)(job & 0xffff), cnt = (int)(job >> 16);
-      const int c = __builtin_amdgcn_readfirstlane(edge_chunk(keys[e0]));
-      const bool valid = slot < cnt;
-      const uint32_t ek = keys[e0 + (valid ? slot : 0)];
-      const int tl = edge_token(ek), k = edge_slot(ek);
-      const size_t qoff = ((b * L + t0 + tl) * Hq + (size_t)g * G + head) * D;
-      bf16x8 qb[KS], db[KS];
+    return a + (int)((long)n * wv / NW);
+  };
+  auto re = [&](int r) {
+    const int a = roff[r], n = roff[r + 1] - a;
+    return a + (int)((long)n * (wv + 1) / NW);
+  };
+  auto next_job = [&](int r, int j) {
+    if (j + 1 < re(r)) return j + 1;
+    for (int r2 = r + 1; r2 < n_rounds; ++r2)
+      if (rb(r2) < re(r2)) return rb(r2);
+    return -1;
+  };
+  auto chunk_of = [&](int j) {
+    return __builtin_amdgcn_readfirstlane(edge_chunk(keys[order[j] & 0xffff]));
+  };
+  // D=64: the next job's chunk operands (K and V rows) are prefetched into a second register
+  // set like its query rows; the transposed K of the dQ product loads when the chunk changes
+  // and is first needed after the S, dP and softmax work of the job.
+  constexpr bool kPrefetchKV = (D == 64);
+  bf16x8 ka[4][KS], vr[4][KS], kt[DT][2], kn[4][KS], vn[4][KS];
+  bf16x8 qb[KS], db[KS], qn[KS], dn[KS];
+  int tl = 0, k = 0, tl_n = 0, k_n = 0;
+  bool valid = false, valid_n = false;
+  auto load_kv = [&](bf16x8 (&dk)[4][KS], bf16x8 (&dv)[4][KS], int c) {
+    const size_t co = ((size_t)bg * nC + c) * D * 64 + lane * 8;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        qb[ks] = ld_bf16x8(Q + qoff + 32 * ks + 8 * blk);
-        db[ks] = ld_bf16x8(dO + qoff + 32 * ks + 8 * blk);
+        dk[t4][ks] = ld_bf16x8(Kop + co + (t4 * KS + ks) * 512);
+        dv[t4][ks] = ld_bf16x8(Vop + co + (t4 * KS + ks) * 512);
       }
-      if (c != cur) {
-        cur = c;
-        const size_t co = ((size_t)bg * nC + c) * D * 64 + lane * 8;
+  };
+  auto load_kt = [&](int c) {
+    const size_t co = ((size_t)bg * nC + c) * D * 64 + lane * 8;
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            ka[t4][ks] = ld_bf16x8(Kop + co + (t4 * KS + ks) * 512);
-            vr[t4][ks] = ld_bf16x8(Vop + co + (t4 * KS + ks) * 512);
-          }
+      for (int s2 = 0; s2 < 2; ++s2) kt[dt][s2] = ld_bf16x8(Kt + co + (dt * 2 + s2) * 512);
+  };
+  auto load_qd = [&](int j, bf16x8 (&q)[KS], bf16x8 (&dd)[KS], int& tl_o, int& k_o,
+                     bool& valid_o) {
+    const uint32_t job = __builtin_amdgcn_readfirstlane(order[j]);
+    const int e0 = (int)(job & 0xffff), cnt = (int)(job >> 16);
+    valid_o = slot < cnt;
+    // a padding column reads the job's first token; its weight factor is 0 and it stores
+    // nothing, and the unconditional load keeps the prefetch free of branches
+    const uint32_t ek = keys[e0 + (valid_o ? slot : 0)];
+    tl_o = edge_token(ek);
+    k_o = edge_slot(ek);
+    const size_t qoff = ((b * L + t0 + tl_o) * Hq + (size_t)g * G + head) * D;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+    for (int ks = 0; ks < KS; ++ks) {
+      q[ks] = ld_bf16x8(Q + qoff + 32 * ks + 8 * blk);
+      dd[ks] = ld_bf16x8(dO + qoff + 32 * ks + 8 * blk);
+    }
+  };
+  int cur = -1, nxt = -1, jn = -1;
+  for (int r = 0; r < n_rounds && jn < 0; ++r)
+    if (rb(r) < re(r)) jn = rb(r);
+  if (jn >= 0) {
+    nxt = chunk_of(jn);
+    if (kPrefetchKV) load_kv(kn, vn, nxt);
+    load_qd(jn, qn, dn, tl_n, k_n, valid_n);
+  }
+  for (int r = 0; r < n_rounds; ++r) {
+    const int jr1 = re(r);
+    for (int j = rb(r); j < jr1; ++j) {
+      if (nxt != cur) {
+        if (kPrefetchKV) {
 #pragma unroll
-          for (int s = 0; s < 2; ++s) kt[dt][s] = ld_bf16x8(Kt + co + (dt * 2 + s) * 512);
+          for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              ka[t4][ks] = kn[t4][ks];
+              vr[t4][ks] = vn[t4][ks];
+            }
+        } else {
+          load_kv(ka, vr, nxt);
+        }
+        load_kt(nxt);
+        cur = nxt;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qb[ks] = qn[ks];
+        db[ks] = dn[ks];
+      }
+      tl = tl_n;
+      k = k_n;
+      valid = valid_n;
+      jn = next_job(r, j);
+      if (jn >= 0) {
+        nxt = chunk_of(jn);
+        if (kPrefetchKV && nxt != cur) load_kv(kn, vn, nxt);
+        load_qd(jn, qn, dn, tl_n, k_n, valid_n);
       }
       f32x4 sa[4], pa[4];
 #pragma unroll
@@ -148,6 +225,11 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
           dsum += sa[t4][i] * pa[t4][i];
         }
       dsum = rows4_sum(dsum);  // D of this column
+      if (valid && blk == 0) {  // kept for phase 2: normaliser (log2 domain) and D
+        const size_t so = (((b * L + t0 + tl) * Hkv + g) * Kn + k) * G + head;
+        __builtin_nontemporal_store(m + __builtin_amdgcn_logf(exp2_fast(-m) + sum), lse_out + so);
+        __builtin_nontemporal_store(dsum, dd_out + so);
+      }
       const float wk = valid ? wsh[tl * 16 + k] : 0.0f;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
@@ -155,7 +237,7 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
         for (int i = 0; i < 4; ++i) sa[t4][i] = wk * sa[t4][i] * (pa[t4][i] - dsum);  // dS
       bf16x8 sb[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) sb[s] = pack_bf16x8(sa[2 * s], sa[2 * s + 1]);
+      for (int s2 = 0; s2 < 2; ++s2) sb[s2] = pack_bf16x8(sa[2 * s2], sa[2 * s2 + 1]);
       // dw of this edge: sum of D over the token's G head columns (lanes of one slot)
       const float dw = group_sum<G>(dsum);
       if (valid && head == 0 && blk == 0) dwsh[tl * 16 + k] = dw;
@@ -234,7 +316,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 k_bwd_p2_mfma(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ Qs, const float* __restrict__ w, const bf16* __restrict__ dO,
-    const float* __restrict__ ds_in, const int32_t* __restrict__ offsets,
+    const float* __restrict__ ds_in, const float* __restrict__ lse_in,
+    const float* __restrict__ dd_in, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ seg_start,
     const int32_t* __restrict__ seg_chunk, const int32_t* __restrict__ n_seg,
     float* __restrict__ part_dk, float* __restrict__ part_dv, float* __restrict__ part_dks,
@@ -246,7 +329,7 @@ k_bwd_p2_mfma(
   __shared__ __attribute__((aligned(16))) uint16_t vl[64][D + 8];
   __shared__ __attribute__((aligned(16))) uint16_t ql[16][D + 8];
   __shared__ __attribute__((aligned(16))) uint16_t dl[16][D + 8];
-  __shared__ int tok_l[SEGMAX];
+  __shared__ int tok_l[SEGMAX], k_l[SEGMAX];
   __shared__ float w_l[SEGMAX], ds_l[SEGMAX];
   const int64_t sidx = blockIdx.x % max_seg;
   const int bg = (int)(blockIdx.x / max_seg);
@@ -268,6 +351,7 @@ k_bwd_p2_mfma(
     const int t = val / Kn, k = val % Kn;
     const size_t o = ((b * L + t) * Hkv + g) * Kn + k;
     tok_l[i] = t;
+    k_l[i] = k;
     w_l[i] = w[o];
     ds_l[i] = ds_in[o];
   }
@@ -288,8 +372,10 @@ k_bwd_p2_mfma(
   const int qs_sel = col / G, qs_head = col % G;  // this lane's A-operand row -> selector, head
   __syncthreads();
 
-  // this lane's query row of job j (a padding row repeats the job's first selector)
-  auto load_rows = [&](int ej, bf16x8 (&qa)[KS], bf16x8 (&da)[KS]) {
+  // this lane's query row of job j (a padding row repeats the job's first selector), and
+  // phase 1's normaliser and D of the lane's four output rows 4*blk + i
+  auto load_rows = [&](int ej, bf16x8 (&qa)[KS], bf16x8 (&da)[KS], float (&le)[4],
+                       float (&dd)[4]) {
     const int n_here = min(TPJ, ne - ej);
     const int t = tok_l[ej + (qs_sel < n_here ? qs_sel : 0)];
     const size_t qoff = ((b * L + t) * Hq + (size_t)g * G + qs_head) * D;
@@ -298,8 +384,16 @@ k_bwd_p2_mfma(
       qa[ks] = ld_bf16x8(Q + qoff + 32 * ks + 8 * blk);
       da[ks] = ld_bf16x8(dO + qoff + 32 * ks + 8 * blk);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * blk + i, s2 = r / G, e = ej + (s2 < n_here ? s2 : 0);
+      const size_t so = (((b * L + tok_l[e]) * Hkv + g) * Kn + k_l[e]) * G + r % G;
+      le[i] = lse_in[so];
+      dd[i] = dd_in[so];
+    }
   };
   bf16x8 qn[KS], dn[KS];
+  float len[4], ddn[4];
   float qsn = 0.0f;  // Qs of the next job's selectors, summed with their ds
   auto load_qs = [&](int ej) {
     float a = 0.0f;
@@ -309,20 +403,26 @@ k_bwd_p2_mfma(
     return a;
   };
   if (ne > 0) {
-    load_rows(0, qn, dn);
+    load_rows(0, qn, dn, len, ddn);
     qsn = load_qs(0);
   }
   for (int ej = 0; ej < ne; ej += TPJ) {
     const int n_here = min(TPJ, ne - ej);
     bf16x8 qa[KS], da[KS];
+    float lse[4], dr[4];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qa[ks] = qn[ks];
       da[ks] = dn[ks];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lse[i] = len[i];
+      dr[i] = ddn[i];
+    }
     dks += qsn;
     if (ej + TPJ < ne) {
-      load_rows(ej + TPJ, qn, dn);
+      load_rows(ej + TPJ, qn, dn, len, ddn);
       qsn = load_qs(ej + TPJ);
     }
 #pragma unroll
@@ -345,45 +445,23 @@ k_bwd_p2_mfma(
         pa[t4] = mfma_16x16x32(da[ks], vb, pa[t4]);
       }
     }
-    // per query row r = 4*blk + i: softmax1 over the 64 keys (4 tiles x 16 lanes)
-    float wr[4], dr[4];
+    // per query row r = 4*blk + i: softmax1 over the 64 keys from phase 1's normaliser
+    float wr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 4 * blk + i, s = r / G;
-      float m = 0.0f;
+      const int s = (4 * blk + i) / G;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) m = fmaxf(m, sa[t4][i] * c2);
-      m = row16_max(m);
-      float sum = 0.0f;
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        sa[t4][i] = exp2_fast(sa[t4][i] * c2 - m);
-        sum += sa[t4][i];
-      }
-      sum = row16_sum(sum);
-      const float inv = 1.0f / (exp2_fast(-m) + sum);
-      float dsum = 0.0f;
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        sa[t4][i] *= inv;
-        dsum += sa[t4][i] * pa[t4][i];
-      }
-      dsum = row16_sum(dsum);
+      for (int t4 = 0; t4 < 4; ++t4) sa[t4][i] = exp2_fast(sa[t4][i] * c2 - lse[i]);
       wr[i] = s < n_here ? w_l[ej + s] : 0.0f;
-      dr[i] = dsum;
     }
-    // dV^T += dO^T (w P), dK^T += Q^T dS  (k = the 16 query rows, 4 per lane block)
+    // dV^T += dO^T (w P), dK^T += Q^T dS  (k = the 16 query rows, 4 per lane block), the
+    // transposed operands read from LDS with the transposing read
     s16x4 doT[DT], qT[DT];
+    const int trow = 4 * blk + col / 4, tcol = 4 * (col % 4);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      s16x4 a, q;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = (short)dl[4 * blk + e][16 * dt + col];
-        q[e] = (short)ql[4 * blk + e][16 * dt + col];
-      }
-      doT[dt] = a;
-      qT[dt] = q;
+      doT[dt] = lds_read_tr4(&dl[trow][16 * dt + tcol]);
+      qT[dt] = lds_read_tr4(&ql[trow][16 * dt + tcol]);
     }
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
@@ -433,7 +511,8 @@ static void launch_p1(const Dims& d, const BwdLayout& lay, const void* Q, const 
       (const bf16*)(ws + lay.kt),
       (const bf16*)Kslc, idx, score, w, (const bf16*)dO, (const uint32_t*)(ws + lay.prep),
       (bf16*)dQ, (bf16*)dQs,
-      (float*)(ws + lay.ds), (float*)(ws + lay.dw), d.L, d.Hq, d.Hkv, d.K, d.nC, BG, c2,
+      (float*)(ws + lay.ds), (float*)(ws + lay.dw), (float*)(ws + lay.lse),
+      (float*)(ws + lay.dd), d.L, d.Hq, d.Hkv, d.K, d.nC, BG, c2,
       (float)d.sm_scale, (float)d.sel_scale);
 }
 
@@ -472,7 +551,8 @@ hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, c
         Timed tm(HSA_KERNEL_BWD_P2, s);
         kern<<<grid, 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)V,
                                  (const bf16*)Qs, w, (const bf16*)dO,
-                                 (const float*)(ws + lay.ds), (const int32_t*)(ws + lay.offsets),
+                                 (const float*)(ws + lay.ds), (const float*)(ws + lay.lse),
+                                 (const float*)(ws + lay.dd), (const int32_t*)(ws + lay.offsets),
                                  (const int32_t*)(ws + lay.entries),
                                  (const int32_t*)(ws + lay.seg_start),
                                  (const int32_t*)(ws + lay.seg_chunk),

@@ -40,7 +40,7 @@ struct BwdLayout {
   int seg;          // entries per backward-phase-2 segment
   int64_t max_seg;  // segment capacity per (b, g)
   size_t ds, dw, tile_counts, tile_base, offsets, entries, seg_start, seg_chunk, n_seg,
-      part_dk, part_dv, part_dks, kt, kop, vop, prep, total;
+      part_dk, part_dv, part_dks, kt, kop, vop, prep, lse, dd, total;
 };
 BwdLayout bwd_layout(const Dims& d);
 
