@@ -57,40 +57,6 @@ struct RawRow<float, D> {
   }
 };
 
-// Maximum of a 64-bit key over the wave, in every lane: DPP inside each 16-lane row, then
-// the gfx950 row swaps across rows (the halves of a key travel together through each swap).
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max_key(uint64_t v) {
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), CTRL, 0xF, 0xF, true);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
-  const uint64_t o = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-  return o > v ? o : v;
-}
-__device__ __forceinline__ uint64_t swap_max_key(uint64_t v, bool rows32) {
-  const unsigned hi = (unsigned)(v >> 32), lo = (unsigned)v;
-  unsigned h0, h1, l0, l1;
-  if (rows32) {
-    auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    h0 = ph[0]; h1 = ph[1]; l0 = pl[0]; l1 = pl[1];
-  } else {
-    auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    h0 = ph[0]; h1 = ph[1]; l0 = pl[0]; l1 = pl[1];
-  }
-  asm volatile("" : "+v"(h0), "+v"(h1), "+v"(l0), "+v"(l1));  // keep the two results apart
-  const uint64_t a = ((uint64_t)h0 << 32) | l0, b = ((uint64_t)h1 << 32) | l1;
-  return a > b ? a : b;
-}
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
-  v = dpp_max_key<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_max_key<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_max_key<0x141>(v);  // row_half_mirror
-  v = dpp_max_key<0x140>(v);  // row_mirror
-  v = swap_max_key(v, false);
-  return swap_max_key(v, true);
-}
-
 size_t dec_fast_ws(const Dims& d) {
   const int n_blocks = d.nC > 0 ? (d.nC + kScanChunks - 1) / kScanChunks : 0;
   const size_t n = sizeof(uint64_t) * (size_t)d.B * d.Hkv * n_blocks * d.K;

@@ -184,6 +184,8 @@ HSA_EXPORT hsa_status_t hsa_select(const hsa_problem_t* p, const void* Qs, const
     if (e != hipSuccess) return launched(e, "pool");
   }
   if (!Qs) return ok();
+  if (hsa::select_mfma_supported(d))
+    return launched(hsa::launch_select_mfma(d, Qs, Kslc, idx, score, w, s), "select");
   if (hsa::select_tile_supported(d))
     return launched(hsa::launch_select_tile(d, Qs, Kslc, idx, score, w, s), "select");
   return launched(hsa::launch_select_generic(d, Qs, Kslc, idx, score, w, s), "select");

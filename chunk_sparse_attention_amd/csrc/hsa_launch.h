@@ -78,6 +78,11 @@ bool select_tile_supported(const Dims& d);
 hipError_t launch_select_tile(const Dims& d, const void* Qs, const void* Kslc, int32_t* idx,
                               float* score, float* w, hipStream_t s);
 
+// Selection for bf16: matrix-core candidate filter, exact rescoring (same results).
+bool select_mfma_supported(const Dims& d);
+hipError_t launch_select_mfma(const Dims& d, const void* Qs, const void* Kslc, int32_t* idx,
+                              float* score, float* w, hipStream_t s);
+
 // Matrix-core (MFMA) kernels for bf16.
 // Per-chunk operand copies for the matrix-core kernels (layouts in fwd_mfma.hip):
 // trans = false: key rows in A-operand order; trans = true: transposed, P.V key order.

@@ -1,0 +1,313 @@
+// select_mfma.hip -- top-K chunk selection for bf16 inputs: a matrix-core candidate filter
+// followed by exact rescoring of the few candidates that can matter.
+//
+// Chunk selection ("Hardware-aligned Hierarchical Sparse Attention ...", papernotes.org note,
+// 方法详解 › 层次化稀疏注意力（HSA）, Chunk Selection): every token scores each earlier chunk's
+// pooled key with its selection query and keeps the top-K, per query group; the chunk
+// weights are stick-breaking over the sigmoid of the ranked scores (same section, 第二阶段).
+//
+// The result is the exact one: scores are the fp64 dot products of the stored values,
+// rounded once to fp32, ranked by (score desc, chunk asc).  Only the work is reduced.
+//   1. Every candidate score is computed approximately on the matrix cores (bf16 products
+//      are exact in fp32, so the fp32 sum is off by at most E = sel * |q| * max|k| * (D+8) *
+//      2^-24 including the scale's own rounding; a factor 2 of headroom is added).
+//   2. T = the K-th largest approximate score of the token.  Every chunk of the exact top-K
+//      has an approximate score >= T - 2E: if V is the exact K-th largest score, then T <=
+//      V + E (else K chunks would score above V exactly) and each member scores >= V - E.
+//   3. The chunks at or above T - 2E (about K per token) are rescored exactly in fp64 and
+//      ranked; a token with more than kSelCap such chunks, or any non-finite value, is
+//      scored exactly over all its candidates instead.
+#include "hsa_common.h"
+#include "hsa_launch.h"
+#include "mfma_common.h"
+#include "tile_common.h"
+
+namespace hsa {
+
+constexpr int kSelCap = 48;  // chunks rescored exactly per token
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Sum of squares of eight bf16 values.
+__device__ __forceinline__ float sq8(bf16x8 v) {
+  const uint4 u = __builtin_bit_cast(uint4, v);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
+    s = fmaf(a, a, s);
+    s = fmaf(b, b, s);
+  }
+  return s;
+}
+
+// Order-preserving 32-bit image of a float (NaN never reaches it).
+__device__ __forceinline__ uint32_t ord_f32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Stick-breaking over a ranked list and the output writes of one (token, group) row.
+__device__ __forceinline__ void write_row(const uint64_t (&top)[kMaxK], int Kt, size_t o,
+                                          int32_t* idx, float* score, float* w) {
+  double rem = 1.0;
+  for (int k = 0; k < Kt; ++k) {
+    const uint64_t key = top[k];
+    if (key == 0) {
+      idx[o + k] = -1;
+      score[o + k] = -__builtin_inff();
+      w[o + k] = 0.0f;
+    } else {
+      const float s = key_score(key);
+      const double p = sigmoid_d((double)s);
+      idx[o + k] = key_chunk(key);
+      score[o + k] = s;
+      w[o + k] = (float)(p * rem);
+      rem *= 1.0 - p;
+    }
+  }
+}
+
+template <int D, int KL>
+__global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs,
+                                                     const bf16* __restrict__ Kslc,
+                                                     int32_t* __restrict__ idx,
+                                                     float* __restrict__ score,
+                                                     float* __restrict__ w, int L, int Hkv,
+                                                     int Kt, int nC, int BG, double sel_scale) {
+  constexpr int KS = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t qraw[64][D + 8];  // the tile's Qs rows
+  __shared__ int cnt[64];
+  __shared__ int fall[64];
+  __shared__ int candl[64][kSelCap];
+  const int bg = blockIdx.x % BG;
+  const int q = blockIdx.x / BG;  // query chunk of the tile: its tokens see chunks < q
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const int t0 = q * 64;
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const int col = lane % 16, blk = lane / 16;
+  const int m = min(q, nC);
+  const int tl = 16 * wave + col;  // this lane's token in the tile (MFMA column)
+  const int t = t0 + tl;
+  const float sel_f = (float)sel_scale;
+  const bf16* kbase = Kslc + (b * nC * Hkv + g) * (size_t)D;  // chunk c row: + c * Hkv * D
+
+  for (int i = tid; i < 64 * D / 8; i += 256) {
+    const int r = i / (D / 8), e = (i % (D / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t0 + r < L) v = *reinterpret_cast<const uint4*>(Qs + ((b * L + t0 + r) * Hkv + g) * D + e);
+    *reinterpret_cast<uint4*>(&qraw[r][e]) = v;
+  }
+  if (tid < 64) {
+    cnt[tid] = 0;
+    fall[tid] = 0;
+  }
+  __syncthreads();
+
+  // B operand: this lane's token column, 8 dimensions per k-step; |q|^2 over the 4 lanes
+  bf16x8 qb[KS];
+  float q2 = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qb[ks] = *reinterpret_cast<const bf16x8*>(&qraw[tl][32 * ks + 8 * blk]);
+    q2 += sq8(qb[ks]);
+  }
+  q2 = rows4_sum(q2);
+
+  // approximate scores of chunks c0 .. c0+63 against the wave's 16 tokens: lane holds
+  // chunks c0 + 16*t4 + 4*blk + i of its token; k2 = |k|^2 of chunk c0 + 16*t4 + col
+  auto approx = [&](int c0, f32x4 (&sacc)[4], float& k2max) {
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      sacc[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int c = c0 + 16 * t4 + col;
+      float k2 = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = c < m ? ld_bf16x8(kbase + (size_t)c * Hkv * D + 32 * ks + 8 * blk)
+                                : zero_bf16x8();
+        k2 += sq8(ka);
+        sacc[t4] = mfma_16x16x32(ka, qb[ks], sacc[t4]);
+      }
+      k2max = fmaxf(k2max, rows4_sum(k2));
+    }
+  };
+
+  // 1. the KL >= K largest approximate scores of this lane's share, kept sorted by a
+  //    branch-free compare-exchange chain that the wave skips when no lane beats its last
+  //    entry; any non-finite value marks the token for the exact path
+  float top[KL];
+#pragma unroll
+  for (int i = 0; i < KL; ++i) top[i] = -__builtin_inff();
+  float k2max = 0.0f;
+  bool bad = (__float_as_uint(q2) & 0x7f800000u) == 0x7f800000u;
+  for (int c0 = 0; c0 < m; c0 += 64) {
+    f32x4 sacc[4];
+    approx(c0, sacc, k2max);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = c0 + 16 * t4 + 4 * blk + i;
+        float v = sacc[t4][i] * sel_f;
+        const bool fin = (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u;  // not inf or NaN
+        bad = bad || (c < m && !fin);
+        v = (c < m && fin) ? v : -__builtin_inff();
+        if (__ballot(v > top[KL - 1])) {
+#pragma unroll
+          for (int j = 0; j < KL; ++j) {
+            const float hi = fmaxf(top[j], v);
+            v = fminf(top[j], v);
+            top[j] = hi;
+          }
+        }
+      }
+  }
+  k2max = row16_max(k2max);  // over the wave's columns: every chunk was in some column
+  // T = K-th largest over the token's 4 lanes (lane order breaks equal values apart)
+  float T = -__builtin_inff();
+  for (int k = 0; k < Kt; ++k) {
+    const uint64_t key = ((uint64_t)ord_f32(top[0]) << 2) | (uint64_t)blk;
+    const uint64_t best = rows4_max_key(key);
+    if (best == key) {
+#pragma unroll
+      for (int j = 0; j + 1 < KL; ++j) top[j] = top[j + 1];
+      top[KL - 1] = -__builtin_inff();
+    }
+    const uint32_t bo = (uint32_t)(best >> 2);
+    T = __uint_as_float((bo & 0x80000000u) ? (bo ^ 0x80000000u) : ~bo);
+  }
+  const float E = 2.0f * sel_f * sqrtf(q2) * sqrtf(k2max) * (float)(D + 8) * 5.9604645e-8f;
+  bad = bad || (__float_as_uint(E) & 0x7f800000u) == 0x7f800000u;
+  const float thr = T == -__builtin_inff() ? -__builtin_inff() : T - 2.0f * E;
+  const uint64_t badmask = __ballot(bad);
+  if (blk == 0 && ((badmask >> col) & 0x0001000100010001ull)) fall[tl] = 1;
+
+  // 2. collect the chunks at or above the threshold
+  for (int c0 = 0; c0 < m; c0 += 64) {
+    f32x4 sacc[4];
+    float unused = 0.0f;
+    approx(c0, sacc, unused);
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = c0 + 16 * t4 + 4 * blk + i;
+        if (c < m && sacc[t4][i] * sel_f >= thr) {
+          const int pos = atomicAdd(&cnt[tl], 1);
+          if (pos < kSelCap) candl[tl][pos] = c;
+        }
+      }
+  }
+  __syncthreads();
+
+  // 3. exact scores of the candidates: four consecutive lanes per token, each rescoring
+  //    every fourth candidate into its own ranked list of KL >= K keys; the four lists merge
+  //    by quad maxima and the first lane writes each slot as it is ranked
+  {
+    const int tj = 16 * wave + lane / 4, sub = lane % 4, tt = t0 + tj;
+    const bool fb = fall[tj] || cnt[tj] > kSelCap;
+    const int n = fb ? 0 : cnt[tj];
+    uint64_t tk[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) tk[i] = 0;
+    for (int r = sub; r < n; r += 4) {
+      const int c = candl[tj][r];
+      const bf16* kr = kbase + (size_t)c * Hkv * D;
+      double dot = 0.0;
+#pragma unroll 2
+      for (int e = 0; e < D; e += 8) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(kr + e);
+        const uint4 qv = *reinterpret_cast<const uint4*>(&qraw[tj][e]);
+        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          dot = fma((double)bf16_lo(qw[h]), (double)bf16_lo(kw[h]), dot);
+          dot = fma((double)bf16_hi(qw[h]), (double)bf16_hi(kw[h]), dot);
+        }
+      }
+      uint64_t key = rank_key((float)(sel_scale * dot), c);
+#pragma unroll
+      for (int i = 0; i < KL; ++i)
+        if (key > tk[i]) {
+          const uint64_t x = tk[i];
+          tk[i] = key;
+          key = x;
+        }
+    }
+    const bool writer = sub == 0 && tt < L && !fb;  // a token without candidates: all masked
+    const size_t o = ((b * L + tt) * Hkv + g) * Kt;
+    double rem = 1.0;
+    for (int k = 0; k < Kt; ++k) {
+      const uint64_t best = dpp_max_key<0x4E>(dpp_max_key<0xB1>(tk[0]));  // over the quad
+      if (best != 0 && tk[0] == best) {
+#pragma unroll
+        for (int i = 0; i + 1 < KL; ++i) tk[i] = tk[i + 1];
+        tk[KL - 1] = 0;
+      }
+      if (writer) {
+        if (best == 0) {
+          idx[o + k] = -1;
+          score[o + k] = -__builtin_inff();
+          w[o + k] = 0.0f;
+        } else {
+          const float sc = key_score(best);
+          const double p = sigmoid_d((double)sc);
+          idx[o + k] = key_chunk(best);
+          score[o + k] = sc;
+          w[o + k] = (float)(p * rem);
+          rem *= 1.0 - p;
+        }
+      }
+    }
+  }
+  // tokens for the exact path over all their candidates, one token at a time per wave
+  for (int j = 0; j < 16; ++j) {
+    const int tj = 16 * wave + j, tt = t0 + tj;
+    if (tt >= L || !(fall[tj] || cnt[tj] > kSelCap)) continue;  // uniform over the wave
+    uint64_t tk[kMaxK];
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i) tk[i] = 0;
+    for (int c = lane; c < m; c += 64) {
+      const bf16* kr = kbase + (size_t)c * Hkv * D;
+      double dot = 0.0;
+      for (int e = 0; e < D; ++e)
+        dot = fma((double)to_f32(bf16{qraw[tj][e]}), (double)to_f32(kr[e]), dot);
+      topk_insert(tk, rank_key((float)(sel_scale * dot), c), Kt);
+    }
+    uint64_t merged[kMaxK];
+    for (int k = 0; k < Kt; ++k) {
+      const uint64_t best = wave_max_key(tk[0]);
+      if (best != 0 && tk[0] == best) topk_pop(tk);
+      merged[k] = best;
+    }
+    for (int k = Kt; k < kMaxK; ++k) merged[k] = 0;
+    if (lane == 0) write_row(merged, Kt, ((b * L + tt) * Hkv + g) * Kt, idx, score, w);
+  }
+}
+
+bool select_mfma_supported(const Dims& d) { return d.dtype == 1 && !(d.flags & 1u); }
+
+hipError_t launch_select_mfma(const Dims& d, const void* Qs, const void* Kslc, int32_t* idx,
+                              float* score, float* w, hipStream_t s) {
+  const int BG = d.B * d.Hkv;
+  const int n_tiles = (d.L + 63) / 64;
+  Timed tm(HSA_KERNEL_SELECT, s);
+  auto go = [&](auto kern) {
+    kern<<<dim3(BG * n_tiles), 256, 0, s>>>((const bf16*)Qs, (const bf16*)Kslc, idx, score, w,
+                                            d.L, d.Hkv, d.K, d.nC, BG, d.sel_scale);
+  };
+  if (d.D == 64) {
+    if (d.K <= 8) go(k_select_mfma<64, 8>);
+    else go(k_select_mfma<64, 16>);
+  } else {
+    if (d.K <= 8) go(k_select_mfma<128, 8>);
+    else go(k_select_mfma<128, 16>);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hsa

@@ -13,24 +13,9 @@
 // token over its chunks, and the 16 threads of a token merge their lists at the end.
 #include "hsa_common.h"
 #include "hsa_launch.h"
+#include "tile_common.h"
 
 namespace hsa {
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), CTRL, 0xF, 0xF, true);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
-  const uint64_t o = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-  return o > v ? o : v;
-}
-// Maximum over the 16 lanes of a row (DPP butterfly), result in every lane of the row.
-__device__ __forceinline__ uint64_t row16_max_u64(uint64_t v) {
-  v = dpp_max_u64<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_max_u64<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_max_u64<0x141>(v);  // row_half_mirror
-  v = dpp_max_u64<0x140>(v);  // row_mirror
-  return v;
-}
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256) k_select_tile(const T* __restrict__ Qs,
@@ -115,7 +100,7 @@ __global__ void __launch_bounds__(256) k_select_tile(const T* __restrict__ Qs,
     const int tl = 4 * tr + a, t = t0 + tl;
     uint64_t mine = 0;  // lane tc keeps the key of slot tc
     for (int k = 0; k < Kt; ++k) {
-      const uint64_t best = row16_max_u64(top[a][0]);
+      const uint64_t best = row16_max_key(top[a][0]);
       if (best != 0 && top[a][0] == best) topk_pop(top[a]);
       if (tc == k) mine = best;
     }

@@ -400,4 +400,46 @@ __device__ __forceinline__ float rows4_max(float v) {
   return fmaxf(a, b);
 }
 
+// ---- 64-bit rank keys across lanes ---------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_key(uint64_t v) {
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), CTRL, 0xF, 0xF, true);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+  const uint64_t o = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+  return o > v ? o : v;
+}
+// Maximum over the 16 lanes of a row, in every lane of the row.
+__device__ __forceinline__ uint64_t row16_max_key(uint64_t v) {
+  v = dpp_max_key<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_key<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_key<0x141>(v);  // row_half_mirror
+  return dpp_max_key<0x140>(v);  // row_mirror
+}
+// Maximum of v and its partner 16 (rows32 = false) or 32 (true) lanes away; the halves of a
+// key travel together through the swap, and the empty asm keeps the two results apart.
+__device__ __forceinline__ uint64_t swap_max_key(uint64_t v, bool rows32) {
+  const unsigned hi = (unsigned)(v >> 32), lo = (unsigned)v;
+  unsigned h0, h1, l0, l1;
+  if (rows32) {
+    auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    h0 = ph[0]; h1 = ph[1]; l0 = pl[0]; l1 = pl[1];
+  } else {
+    auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    h0 = ph[0]; h1 = ph[1]; l0 = pl[0]; l1 = pl[1];
+  }
+  asm volatile("" : "+v"(h0), "+v"(h1), "+v"(l0), "+v"(l1));
+  const uint64_t a = ((uint64_t)h0 << 32) | l0, b = ((uint64_t)h1 << 32) | l1;
+  return a > b ? a : b;
+}
+// Maximum over lanes l, l^16, l^32, l^48 (the four rows at one position).
+__device__ __forceinline__ uint64_t rows4_max_key(uint64_t v) {
+  return swap_max_key(swap_max_key(v, false), true);
+}
+// Maximum over the whole wave, in every lane.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  return rows4_max_key(row16_max_key(v));
+}
+
 }  // namespace hsa

@@ -188,6 +188,38 @@ def test_fold_flag(hsa, dev):
     assert torch.equal(a["dV"], b["dV"]) and torch.equal(a["dQ"], b["dQ"])
 
 
+@pytest.mark.parametrize("case", ["qs_zero", "qs_half_zero", "equal_chunks", "qs_large"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_select_degenerate(hsa, dev, case, d):
+    """Exact ties and extreme magnitudes: the ranking must still equal the oracle's bit for
+    bit (ties go to the lower chunk index), whatever path the kernel takes."""
+    wl = W("sel_" + case, 1, 64 * 70 + 7, 8, 2, d, 64, 8, torch.bfloat16)
+    say("case select", case, d)
+    x = workloads.make_inputs(wl, seed=5, with_grad=False)
+    Qs, K = x["Qs"].clone(), x["K"].clone()
+    if case == "qs_zero":
+        Qs.zero_()
+    elif case == "qs_half_zero":
+        Qs[:, ::2] = 0
+    elif case == "equal_chunks":
+        nC = wl.L // 64
+        K[:, :nC * 64] = K[:, :64].repeat(1, nC, 1, 1)
+    elif case == "qs_large":
+        Qs = (Qs.float() * 2.0 ** 100).to(torch.bfloat16)
+    Kslc, idx, score, w = hsa.select(Qs.to(dev), K.to(dev), wl.K)
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    ks = orc.pool(K, 64)
+    assert np.array_equal(npy(Kslc), ks)
+    oi, osc, ow = orc.select(Qs, ks, 64, wl.K)
+    assert np.array_equal(npy(idx), oi)
+    sc = npy(score)
+    fin = np.isfinite(osc)
+    assert np.array_equal(np.isfinite(sc), fin)
+    assert np.array_equal(sc[fin].astype(np.float32), osc[fin].astype(np.float32))
+    assert max_abs(npy(w), ow) <= 1e-5
+
+
 @pytest.mark.parametrize("ctx", [40, 64, 64 * 7 + 13, 64 * 33])
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
 def test_decode_small(hsa, dev, ctx, generic):
