@@ -81,28 +81,31 @@ __global__ void __launch_bounds__(256) k_inv_count(const int32_t* __restrict__ i
   for (int c = threadIdx.x; c < nC; c += blockDim.x) out[c] = cnt[c];
 }
 
-// Exclusive scan of n ints in place (one block of 1024 threads; thread-contiguous runs).
+// Exclusive scan of n ints in place (one block of 1024 threads; thread-contiguous runs):
+// per-thread run sums, a shuffle scan inside each wave, then the wave totals.
 __device__ void block_exclusive_scan(int32_t* a, int n, int32_t* total_out) {
-  __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int per = (n + 1023) / 1024;
   const int lo = min(n, tid * per);
   const int hi = min(n, lo + per);
   int32_t s = 0;
   for (int i = lo; i < hi; ++i) s += a[i];
-  part[tid] = s;
-  __syncthreads();
-  if (tid == 0) {
-    int32_t run = 0;
-    for (int i = 0; i < 1024; ++i) {
-      int32_t v = part[i];
-      part[i] = run;
-      run += v;
-    }
-    *total_out = run;
+  int32_t incl = s;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
   }
+  if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
-  int32_t run = part[tid];
+  int32_t run = incl - s;
+  int32_t total = 0;
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) run += wsum[w];
+    total += wsum[w];
+  }
+  if (tid == 0) *total_out = total;
   for (int i = lo; i < hi; ++i) {
     int32_t v = a[i];
     a[i] = run;
@@ -153,34 +156,42 @@ __global__ void __launch_bounds__(1024) k_inv_scan(const int32_t* __restrict__ t
 }
 
 // Per (b, g, tile), one wave: walk the tile's tokens in order; lane k places slot k.  A token's
-// chunks are distinct, so the lanes of one step never share a counter.
+// chunks are distinct, so the lanes of one step never share a counter.  The tile's selections
+// are first staged in LDS, 256 tokens at a time, so the serial walk waits on LDS only.
+constexpr int kScatterBatch = 256;
 __global__ void __launch_bounds__(64) k_inv_scatter(const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ tile_base,
                                                     int32_t* __restrict__ entries, int L,
                                                     int Hkv, int K, int nC, int tile_tokens,
                                                     int n_tiles) {
   extern __shared__ int32_t cnt[];
+  __shared__ int32_t sel[kScatterBatch * kMaxK];
   const int tile = blockIdx.x % n_tiles;
   const int bg = blockIdx.x / n_tiles;
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const int lane = threadIdx.x;
   for (int c = lane; c < nC; c += kWave) cnt[c] = 0;
-  __syncthreads();
   const int32_t* tb = tile_base + ((size_t)bg * n_tiles + tile) * nC;
   int32_t* ent = entries + (size_t)bg * L * K;
   const int t0 = tile * tile_tokens;
   const int t1 = min(L, t0 + tile_tokens);
-  for (int t = t0; t < t1; ++t) {
-    if (lane < K) {
-      int c = idx[((b * L + t) * Hkv + g) * K + lane];
-      if (c >= 0 && c < nC) {
-        int pos = tb[c] + cnt[c];
-        cnt[c] += 1;
-        ent[pos] = t * K + lane;
+  for (int tb0 = t0; tb0 < t1; tb0 += kScatterBatch) {
+    const int nt = min(kScatterBatch, t1 - tb0);
+    __syncthreads();
+    for (int i = lane; i < nt * K; i += kWave)
+      sel[i] = idx[((b * L + tb0 + i / K) * Hkv + g) * K + i % K];
+    __syncthreads();
+    for (int tt = 0; tt < nt; ++tt) {
+      if (lane < K) {
+        const int c = sel[tt * K + lane];
+        if (c >= 0 && c < nC) {
+          const int pos = tb[c] + cnt[c];
+          cnt[c] += 1;
+          ent[pos] = (tb0 + tt) * K + lane;
+        }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -480,16 +491,42 @@ __global__ void __launch_bounds__(256) k_bwd_p2_reduce(
     if (dKslc) dKslc[((b * nC + c) * Hkv + g) * D + e] = a;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kChunk * D; i += blockDim.x) {
-    int j = i / D, e = i % D;
-    float ak = 0.0f, av = 0.0f;
-    for (int s = s0; s < s1; ++s) {
-      ak += part_dk[((pb + s) * kChunk + j) * D + e];
-      av += part_dv[((pb + s) * kChunk + j) * D + e];
+  for (int i = threadIdx.x; i < kChunk * D / 4; i += blockDim.x) {
+    const int j = (4 * i) / D, e = (4 * i) % D;
+    float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak;
+    const float* pk = part_dk + ((pb + s0) * kChunk + j) * D + e;
+    const float* pv = part_dv + ((pb + s0) * kChunk + j) * D + e;
+    const size_t step = (size_t)kChunk * D;
+    int s = s0;
+    for (; s + 4 <= s1; s += 4) {  // four segments' loads in flight, summed in segment order
+      float4 k4[4], v4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        k4[u] = *reinterpret_cast<const float4*>(pk + (size_t)(s - s0 + u) * step);
+        v4[u] = *reinterpret_cast<const float4*>(pv + (size_t)(s - s0 + u) * step);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ak.x += k4[u].x; ak.y += k4[u].y; ak.z += k4[u].z; ak.w += k4[u].w;
+        av.x += v4[u].x; av.y += v4[u].y; av.z += v4[u].z; av.w += v4[u].w;
+      }
     }
-    if (fold) ak += dks[e] / (float)S;
-    dK[cbase + j * kvstride + e] = from_f32<T>(ak);
-    dV[cbase + j * kvstride + e] = from_f32<T>(av);
+    for (; s < s1; ++s) {
+      const float4 k1 = *reinterpret_cast<const float4*>(pk + (size_t)(s - s0) * step);
+      const float4 v1 = *reinterpret_cast<const float4*>(pv + (size_t)(s - s0) * step);
+      ak.x += k1.x; ak.y += k1.y; ak.z += k1.z; ak.w += k1.w;
+      av.x += v1.x; av.y += v1.y; av.z += v1.z; av.w += v1.w;
+    }
+    if (fold) {
+      ak.x += dks[e] / (float)S;
+      ak.y += dks[e + 1] / (float)S;
+      ak.z += dks[e + 2] / (float)S;
+      ak.w += dks[e + 3] / (float)S;
+    }
+    T* kd = dK + cbase + j * kvstride + e;
+    T* vd = dV + cbase + j * kvstride + e;
+    kd[0] = from_f32<T>(ak.x); kd[1] = from_f32<T>(ak.y); kd[2] = from_f32<T>(ak.z); kd[3] = from_f32<T>(ak.w);
+    vd[0] = from_f32<T>(av.x); vd[1] = from_f32<T>(av.y); vd[2] = from_f32<T>(av.z); vd[3] = from_f32<T>(av.w);
   }
 }
 
