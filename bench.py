@@ -235,10 +235,13 @@ def main() -> int:
         Kslc, idx, score, w = hsa.select(Qs, K, wl.K, generic=gen)
         if ev is not None:
             ev[1].record()
-        O = hsa.fwd(Q, K, V, idx, w, generic=gen)
+        # one workspace for both: the backward reuses the forward's tile job lists, key
+        # operand and softmax normalisers (HSA_BWD_AFTER_FWD)
+        O = hsa.fwd(Q, K, V, idx, w, generic=gen, ws=ws_bwd)
         if ev is not None:
             ev[2].record()
-        g = hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, generic=gen, ws=ws_bwd)
+        g = hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, generic=gen, ws=ws_bwd,
+                    after_fwd=True)
         if ev is not None:
             ev[3].record()
         return idx, O, g

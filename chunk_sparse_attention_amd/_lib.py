@@ -19,6 +19,7 @@ HSA_F32, HSA_BF16 = 0, 1
 HSA_OP_SELECT, HSA_OP_FWD, HSA_OP_BWD, HSA_OP_DECODE = range(4)
 HSA_FLAG_GENERIC = 0x1
 HSA_BWD_FOLD_KSLC = 0x1
+HSA_BWD_AFTER_FWD = 0x2
 
 EXPORTS = ("hsa_status_string", "hsa_last_error", "hsa_version", "hsa_workspace_size",
            "hsa_select", "hsa_fwd", "hsa_bwd", "hsa_decode", "hsa_timer_enable",

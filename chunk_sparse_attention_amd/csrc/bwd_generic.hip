@@ -24,7 +24,11 @@ BwdLayout bwd_layout(const Dims& d) {
   const int64_t bg = (int64_t)d.B * d.Hkv;
   const int64_t E = (int64_t)d.L * d.K;  // entry capacity per (b, g)
   l.max_seg = (E + l.seg - 1) / l.seg + d.nC;
-  size_t o = 0;
+  const FwdState st = fwd_state(d);  // the forward's state comes first
+  l.prep = st.prep;
+  l.kop = st.kop;
+  l.lse = st.lse;
+  size_t o = st.total;
   auto take = [&](size_t bytes) {
     size_t at = o;
     o = align256(o + bytes);
@@ -43,11 +47,8 @@ BwdLayout bwd_layout(const Dims& d) {
   l.part_dv = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
   l.part_dks = take(sizeof(float) * bg * l.max_seg * d.D);
   l.kt = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
-  l.kop = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
   l.vop = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
-  l.prep = take(tile_prep_bytes(d));
-  // per (token, group, slot, head): the softmax normaliser (log2 domain) and D = <dO, O_k>
-  l.lse = take(sizeof(float) * bg * E * d.G);
+  // per (token, group, slot, head): D = <dO, O_k> (the normaliser is in the state prefix)
   l.dd = take(sizeof(float) * bg * E * d.G);
   l.total = o;
   return l;

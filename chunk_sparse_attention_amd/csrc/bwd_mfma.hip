@@ -47,15 +47,17 @@ __device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p) {
 
 // ---- phase 1 -------------------------------------------------------------------------------
 
-template <int D, int TT, int G>
+template <int D, int TT, int G, bool HL>
 __global__ void __launch_bounds__(512) k_bwd_p1_tile(
     const bf16* __restrict__ Q, const bf16* __restrict__ Kop, const bf16* __restrict__ Vop,
     const bf16* __restrict__ Kt, const bf16* __restrict__ Kslc, const int32_t* __restrict__ idx,
     const float* __restrict__ score, const float* __restrict__ w, const bf16* __restrict__ dO,
     const uint32_t* __restrict__ prep, bf16* __restrict__ dQ, bf16* __restrict__ dQs,
-    float* __restrict__ ds_out, float* __restrict__ dw_out, float* __restrict__ lse_out,
+    float* __restrict__ ds_out, float* __restrict__ dw_out, float* __restrict__ lse,
     float* __restrict__ dd_out, int L, int Hq, int Hkv, int Kn, int nC, int BG, float c2,
     float sm_scale, float sel_scale) {
+  // HL: lse holds the forward's softmax normaliser of every (token, group, slot, head) and is
+  // read; otherwise it is computed here and written for phase 2.
   constexpr int NT = 512, NW = NT / 64;
   constexpr int DP = D + 1;
   constexpr int KS = D / 32;
@@ -115,6 +117,7 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
   bf16x8 qb[KS], db[KS], qn[KS], dn[KS];
   int tl = 0, k = 0, tl_n = 0, k_n = 0;
   bool valid = false, valid_n = false;
+  float le = 0.0f, le_n = 0.0f;  // the column's normaliser (HL)
   auto load_kv = [&](bf16x8 (&dk)[4][KS], bf16x8 (&dv)[4][KS], int c) {
     const size_t co = ((size_t)bg * nC + c) * D * 64 + lane * 8;
 #pragma unroll
@@ -133,7 +136,7 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
       for (int s2 = 0; s2 < 2; ++s2) kt[dt][s2] = ld_bf16x8(Kt + co + (dt * 2 + s2) * 512);
   };
   auto load_qd = [&](int j, bf16x8 (&q)[KS], bf16x8 (&dd)[KS], int& tl_o, int& k_o,
-                     bool& valid_o) {
+                     bool& valid_o, float& le_o) {
     const uint32_t job = __builtin_amdgcn_readfirstlane(order[j]);
     const int e0 = (int)(job & 0xffff), cnt = (int)(job >> 16);
     valid_o = slot < cnt;
@@ -148,6 +151,7 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
       q[ks] = ld_bf16x8(Q + qoff + 32 * ks + 8 * blk);
       dd[ks] = ld_bf16x8(dO + qoff + 32 * ks + 8 * blk);
     }
+    if (HL) le_o = lse[(((b * L + t0 + tl_o) * Hkv + g) * Kn + k_o) * G + head];
   };
   int cur = -1, nxt = -1, jn = -1;
   for (int r = 0; r < n_rounds && jn < 0; ++r)
@@ -155,7 +159,7 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
   if (jn >= 0) {
     nxt = chunk_of(jn);
     if (kPrefetchKV) load_kv(kn, vn, nxt);
-    load_qd(jn, qn, dn, tl_n, k_n, valid_n);
+    load_qd(jn, qn, dn, tl_n, k_n, valid_n, le_n);
   }
   for (int r = 0; r < n_rounds; ++r) {
     const int jr1 = re(r);
@@ -183,11 +187,12 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
       tl = tl_n;
       k = k_n;
       valid = valid_n;
+      le = le_n;
       jn = next_job(r, j);
       if (jn >= 0) {
         nxt = chunk_of(jn);
         if (kPrefetchKV && nxt != cur) load_kv(kn, vn, nxt);
-        load_qd(jn, qn, dn, tl_n, k_n, valid_n);
+        load_qd(jn, qn, dn, tl_n, k_n, valid_n, le_n);
       }
       f32x4 sa[4], pa[4];
 #pragma unroll
@@ -200,34 +205,46 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
           pa[t4] = mfma_16x16x32(vr[t4][ks], db[ks], pa[t4]);
         }
       }
-      float m = 0.0f;
+      float dsum = 0.0f, lse_w = 0.0f;
+      if (HL) {  // P from the forward's normaliser
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
+        for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, sa[t4][i] * c2);
-      m = rows4_max(m);
-      float sum = 0.0f;
+          for (int i = 0; i < 4; ++i) {
+            sa[t4][i] = exp2_fast(sa[t4][i] * c2 - le);
+            dsum += sa[t4][i] * pa[t4][i];
+          }
+      } else {
+        float m = 0.0f;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
+        for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sa[t4][i] = exp2_fast(sa[t4][i] * c2 - m);
-          sum += sa[t4][i];
-        }
-      sum = rows4_sum(sum);
-      const float inv = 1.0f / (exp2_fast(-m) + sum);
-      float dsum = 0.0f;
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, sa[t4][i] * c2);
+        m = rows4_max(m);
+        float sum = 0.0f;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
+        for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sa[t4][i] *= inv;  // P
-          dsum += sa[t4][i] * pa[t4][i];
-        }
+          for (int i = 0; i < 4; ++i) {
+            sa[t4][i] = exp2_fast(sa[t4][i] * c2 - m);
+            sum += sa[t4][i];
+          }
+        sum = rows4_sum(sum);
+        const float den = exp2_fast(-m) + sum;
+        const float inv = 1.0f / den;
+        lse_w = m + __builtin_amdgcn_logf(den);
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sa[t4][i] *= inv;  // P
+            dsum += sa[t4][i] * pa[t4][i];
+          }
+      }
       dsum = rows4_sum(dsum);  // D of this column
       if (valid && blk == 0) {  // kept for phase 2: normaliser (log2 domain) and D
         const size_t so = (((b * L + t0 + tl) * Hkv + g) * Kn + k) * G + head;
-        __builtin_nontemporal_store(m + __builtin_amdgcn_logf(exp2_fast(-m) + sum), lse_out + so);
+        if (!HL) __builtin_nontemporal_store(lse_w, lse + so);
         __builtin_nontemporal_store(dsum, dd_out + so);
       }
       const float wk = valid ? wsh[tl * 16 + k] : 0.0f;
@@ -500,49 +517,53 @@ bool bwd_mfma_supported(const Dims& d) {
 template <int D, int TT, int G>
 static void launch_p1(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
                       const void* V, const void* Kslc, const int32_t* idx, const float* score,
-                      const float* w, const void* dO, void* dQ, void* dQs, char* ws,
+                      const float* w, const void* dO, void* dQ, void* dQs, bool hl, char* ws,
                       hipStream_t s) {
   const int BG = d.B * d.Hkv;
   const int n_tiles = (d.L + TT - 1) / TT;
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);
   Timed tm(HSA_KERNEL_BWD_P1, s);
-  k_bwd_p1_tile<D, TT, G><<<dim3(BG * n_tiles), 512, 0, s>>>(
-      (const bf16*)Q, (const bf16*)(ws + lay.kop), (const bf16*)(ws + lay.vop),
-      (const bf16*)(ws + lay.kt),
-      (const bf16*)Kslc, idx, score, w, (const bf16*)dO, (const uint32_t*)(ws + lay.prep),
-      (bf16*)dQ, (bf16*)dQs,
-      (float*)(ws + lay.ds), (float*)(ws + lay.dw), (float*)(ws + lay.lse),
-      (float*)(ws + lay.dd), d.L, d.Hq, d.Hkv, d.K, d.nC, BG, c2,
-      (float)d.sm_scale, (float)d.sel_scale);
+  auto go = [&](auto kern) {
+    kern<<<dim3(BG * n_tiles), 512, 0, s>>>(
+        (const bf16*)Q, (const bf16*)(ws + lay.kop), (const bf16*)(ws + lay.vop),
+        (const bf16*)(ws + lay.kt), (const bf16*)Kslc, idx, score, w, (const bf16*)dO,
+        (const uint32_t*)(ws + lay.prep), (bf16*)dQ, (bf16*)dQs, (float*)(ws + lay.ds),
+        (float*)(ws + lay.dw), (float*)(ws + lay.lse), (float*)(ws + lay.dd), d.L, d.Hq, d.Hkv,
+        d.K, d.nC, BG, c2, (float)d.sm_scale, (float)d.sel_scale);
+  };
+  if (hl) go(k_bwd_p1_tile<D, TT, G, true>);
+  else go(k_bwd_p1_tile<D, TT, G, false>);
 }
 
 template <int D, int TT>
 static void launch_p1_g(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
                         const void* V, const void* Kslc, const int32_t* idx, const float* score,
-                        const float* w, const void* dO, void* dQ, void* dQs, char* ws,
+                        const float* w, const void* dO, void* dQ, void* dQs, bool hl, char* ws,
                         hipStream_t s) {
-  if (d.G == 4) launch_p1<D, TT, 4>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
-  else if (d.G == 8) launch_p1<D, TT, 8>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
-  else launch_p1<D, TT / 2, 16>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
+  if (d.G == 4) launch_p1<D, TT, 4>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, hl, ws, s);
+  else if (d.G == 8) launch_p1<D, TT, 8>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, hl, ws, s);
+  else launch_p1<D, TT / 2, 16>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, hl, ws, s);
 }
 
 
 hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
                            const void* V, const void* Qs, const void* Kslc, const int32_t* idx,
                            const float* score, const float* w, const void* dO, void* dQ,
-                           void* dK, void* dV, void* dQs, float* dKslc, bool fold, char* ws,
-                           hipStream_t s) {
+                           void* dK, void* dV, void* dQs, float* dKslc, bool fold,
+                           bool after_fwd, char* ws, hipStream_t s) {
   hipError_t e = launch_invidx(d, lay, idx, ws, s);
   if (e != hipSuccess) return e;
   const int BG = d.B * d.Hkv;
   launch_prep_ops(d, K, ws + lay.kt, true, s);
-  launch_prep_ops(d, K, ws + lay.kop, false, s);
   launch_prep_ops(d, V, ws + lay.vop, false, s);
-  launch_tile_prep(d, idx, ws + lay.prep, s);
+  if (!after_fwd) {  // else the forward's job lists and key operand are still in place
+    launch_prep_ops(d, K, ws + lay.kop, false, s);
+    launch_tile_prep(d, idx, ws + lay.prep, s);
+  }
   if (d.D == 64)
-    launch_p1_g<64, 64>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
+    launch_p1_g<64, 64>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, after_fwd, ws, s);
   else
-    launch_p1_g<128, 32>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, ws, s);
+    launch_p1_g<128, 32>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, after_fwd, ws, s);
   if (d.nC > 0) {
     if (d.D == 64) {
       const float c2 = (float)(d.sm_scale * 1.4426950408889634);

@@ -64,8 +64,8 @@ template <int D, int TT, int G>
 __global__ void __launch_bounds__(512) k_fwd_tile(
     const bf16* __restrict__ Q, const bf16* __restrict__ Kop, const bf16* __restrict__ Vt,
     const int32_t* __restrict__ idx, const float* __restrict__ w,
-    const uint32_t* __restrict__ prep, bf16* __restrict__ O, int L, int Hq, int Hkv, int Kt,
-    int nC, int BG, float c2) {
+    const uint32_t* __restrict__ prep, bf16* __restrict__ O, float* __restrict__ lse_out, int L,
+    int Hq, int Hkv, int Kt, int nC, int BG, float c2) {
   constexpr int NT = 512, NW = NT / 64;
   constexpr int DP = D + 1;    // padded accumulator row
   constexpr int KS = D / 32;   // k-steps of S^T
@@ -230,7 +230,11 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
         sum += s_acc[kt][i];
       }
     sum = rows4_sum(sum);
-    const float f = valid_c ? wsh[tl_c * 16 + k_c] / (exp2_fast(-m) + sum) : 0.0f;
+    const float den = exp2_fast(-m) + sum;
+    if (valid_c && blk == 0)  // the normaliser, kept for a backward over the same selection
+      __builtin_nontemporal_store(m + __builtin_amdgcn_logf(den),
+                                  lse_out + (((b * L + t0 + tl_c) * Hkv + g) * Kt + k_c) * G + head);
+    const float f = valid_c ? wsh[tl_c * 16 + k_c] / den : 0.0f;
     bf16x8 pb[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) pb[s] = pack_bf16x8(s_acc[2 * s] * f, s_acc[2 * s + 1] * f);
@@ -290,24 +294,24 @@ void launch_tile_prep(const Dims& d, const int32_t* idx, void* prep, hipStream_t
 template <int D, int TT, int G>
 static void launch_fwd_tile(const Dims& d, const void* Q, const void* K, const void* Vt,
                             const int32_t* idx, const float* w, const void* prep, void* O,
-                            hipStream_t s) {
+                            float* lse, hipStream_t s) {
   const int BG = d.B * d.Hkv;
   const int n_tiles = (d.L + TT - 1) / TT;
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);  // logit scale * log2(e)
   Timed tm(HSA_KERNEL_FWD, s);
   k_fwd_tile<D, TT, G><<<dim3(BG * n_tiles), 512, 0, s>>>(
       (const bf16*)Q, (const bf16*)K, (const bf16*)Vt, idx, w, (const uint32_t*)prep, (bf16*)O,
-      d.L, d.Hq, d.Hkv, d.K, d.nC, BG, c2);
+      lse, d.L, d.Hq, d.Hkv, d.K, d.nC, BG, c2);
 }
 
 template <int D, int TT>
 static bool launch_fwd_tile_g(const Dims& d, const void* Q, const void* K, const void* Vt,
                               const int32_t* idx, const float* w, const void* prep, void* O,
-                              hipStream_t s) {
+                              float* lse, hipStream_t s) {
   switch (d.G) {
-    case 4: launch_fwd_tile<D, TT, 4>(d, Q, K, Vt, idx, w, prep, O, s); return true;
-    case 8: launch_fwd_tile<D, TT, 8>(d, Q, K, Vt, idx, w, prep, O, s); return true;
-    case 16: launch_fwd_tile<D, TT / 2, 16>(d, Q, K, Vt, idx, w, prep, O, s); return true;
+    case 4: launch_fwd_tile<D, TT, 4>(d, Q, K, Vt, idx, w, prep, O, lse, s); return true;
+    case 8: launch_fwd_tile<D, TT, 8>(d, Q, K, Vt, idx, w, prep, O, lse, s); return true;
+    case 16: launch_fwd_tile<D, TT / 2, 16>(d, Q, K, Vt, idx, w, prep, O, lse, s); return true;
   }
   return false;
 }
@@ -318,7 +322,17 @@ bool fwd_mfma_supported(const Dims& d) {
          !(d.flags & 1u);
 }
 
-size_t fwd_mfma_ws(const Dims& d) { return 2 * chunk_ops_bytes(d) + tile_prep_bytes(d); }
+FwdState fwd_state(const Dims& d) {
+  FwdState st{};
+  st.prep = 0;
+  st.kop = tile_prep_bytes(d);
+  st.lse = st.kop + chunk_ops_bytes(d);
+  const size_t lse = sizeof(float) * (size_t)d.B * d.L * d.Hq * d.K;
+  st.total = st.lse + ((lse + 255) & ~(size_t)255);
+  return st;
+}
+
+size_t fwd_mfma_ws(const Dims& d) { return fwd_state(d).total + chunk_ops_bytes(d); }
 
 void launch_prep_ops(const Dims& d, const void* src, void* dst, bool trans, hipStream_t s) {
   if (d.nC == 0) return;
@@ -336,16 +350,18 @@ size_t chunk_ops_bytes(const Dims& d) {
 
 hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,
                            const int32_t* idx, const float* w, void* O, char* ws, hipStream_t s) {
-  char* kop = ws;
-  char* vt = ws + chunk_ops_bytes(d);
-  char* prep = ws + 2 * chunk_ops_bytes(d);
+  const FwdState st = fwd_state(d);
+  char* kop = ws + st.kop;
+  char* prep = ws + st.prep;
+  float* lse = (float*)(ws + st.lse);
+  char* vt = ws + st.total;
   launch_prep_ops(d, K, kop, false, s);
   launch_prep_ops(d, V, vt, true, s);
   launch_tile_prep(d, idx, prep, s);
   if (d.D == 64)
-    launch_fwd_tile_g<64, 64>(d, Q, kop, vt, idx, w, prep, O, s);
+    launch_fwd_tile_g<64, 64>(d, Q, kop, vt, idx, w, prep, O, lse, s);
   else
-    launch_fwd_tile_g<128, 32>(d, Q, kop, vt, idx, w, prep, O, s);
+    launch_fwd_tile_g<128, 32>(d, Q, kop, vt, idx, w, prep, O, lse, s);
   return hipGetLastError();
 }
 

@@ -232,7 +232,8 @@ HSA_EXPORT hsa_status_t hsa_bwd(const hsa_problem_t* p, const void* Q, const voi
   TRY(need_tensor(dV, "dV"));
   TRY(need_tensor(dQs, "dQs"));
   if (dKslc && !aligned(dKslc, 16)) return fail(HSA_ERR_INVALID_ARG, "dKslc is not 16-byte aligned");
-  if (flags & ~(uint32_t)HSA_BWD_FOLD_KSLC) return fail(HSA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (flags & ~(uint32_t)(HSA_BWD_FOLD_KSLC | HSA_BWD_AFTER_FWD))
+    return fail(HSA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   TRY(check_ws(HSA_OP_BWD, d, ws, ws_bytes));
   TRY(check_pending());
   hipStream_t s = (hipStream_t)stream;
@@ -240,6 +241,8 @@ HSA_EXPORT hsa_status_t hsa_bwd(const hsa_problem_t* p, const void* Q, const voi
   if (hsa::bwd_mfma_supported(d))
     return launched(hsa::launch_bwd_mfma(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK,
                                          dV, dQs, dKslc, (flags & HSA_BWD_FOLD_KSLC) != 0,
+                                         (flags & HSA_BWD_AFTER_FWD) != 0 &&
+                                             hsa::fwd_mfma_supported(d),
                                          (char*)ws, s),
                     "bwd");
   return launched(hsa::launch_bwd_generic(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK,

@@ -33,6 +33,15 @@ struct Dims {
   unsigned flags;
 };
 
+// State the forward leaves at the start of its workspace for a backward over the same
+// selection: the token-tile job lists, the key rows in MFMA operand order and, per (token,
+// group, slot, head), the softmax-off-by-one normaliser in the log2 domain.  The backward's
+// workspace starts with the same regions.
+struct FwdState {
+  size_t prep, kop, lse, total;
+};
+FwdState fwd_state(const Dims& d);
+
 // Backward workspace carve-up (byte offsets into the caller's workspace).
 struct BwdLayout {
   int tile_tokens;  // tokens per tile of the inverse-index build
@@ -93,11 +102,12 @@ int tile_tokens(const Dims& d);
 size_t tile_prep_bytes(const Dims& d);
 void launch_tile_prep(const Dims& d, const int32_t* idx, void* prep, hipStream_t s);
 bool bwd_mfma_supported(const Dims& d);
+// after_fwd: ws still holds the forward's state for this problem, idx and K (see FwdState).
 hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
                            const void* V, const void* Qs, const void* Kslc, const int32_t* idx,
                            const float* score, const float* w, const void* dO, void* dQ,
-                           void* dK, void* dV, void* dQs, float* dKslc, bool fold, char* ws,
-                           hipStream_t s);
+                           void* dK, void* dV, void* dQs, float* dKslc, bool fold,
+                           bool after_fwd, char* ws, hipStream_t s);
 bool fwd_mfma_supported(const Dims& d);
 size_t fwd_mfma_ws(const Dims& d);
 hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,

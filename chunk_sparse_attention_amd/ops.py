@@ -128,8 +128,12 @@ def fwd(Q, K, V, idx, w, sm_scale=None, generic=False, ws=None, out=None):
 
 
 def bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, fold=True, want_dkslc=True, sm_scale=None,
-        sel_scale=None, generic=False, ws=None):
-    """Gradients with the selection fixed.  Returns dict(dQ, dK, dV, dQs, dKslc)."""
+        sel_scale=None, generic=False, ws=None, after_fwd=False):
+    """Gradients with the selection fixed.  Returns dict(dQ, dK, dV, dQs, dKslc).
+
+    after_fwd=True: `ws` is the workspace that fwd() just used for the same Q, K, idx and w
+    (allocate it with workspace(HSA_OP_BWD, ...), which also fits the forward); the backward
+    then reuses the state the forward left in it (HSA_BWD_AFTER_FWD)."""
     _need(Q, "Q")
     B, L, Hq, D = Q.shape
     Hkv = K.shape[2]
@@ -150,9 +154,11 @@ def bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, fold=True, want_dkslc=True, sm_sca
     dKslc = (torch.empty((B, L // S_CHUNK, Hkv, D), dtype=torch.float32, device=dev)
              if want_dkslc else None)
     if ws is None:
+        if after_fwd:
+            raise ValueError("after_fwd needs the workspace the forward used")
         ws = workspace(_lib.HSA_OP_BWD, prob, dev)
     wp, wn = _ws_args(ws)
-    flags = _lib.HSA_BWD_FOLD_KSLC if fold else 0
+    flags = (_lib.HSA_BWD_FOLD_KSLC if fold else 0) | (_lib.HSA_BWD_AFTER_FWD if after_fwd else 0)
     check(_lib.lib().hsa_bwd(ctypes.byref(prob), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qs), _ptr(Kslc),
                              _ptr(idx), _ptr(score), _ptr(w), _ptr(dO), _ptr(dQ), _ptr(dK),
                              _ptr(dV), _ptr(dQs), _ptr(dKslc), flags, wp, wn, _stream()),

@@ -76,6 +76,8 @@ typedef enum { HSA_OP_SELECT = 0, HSA_OP_FWD = 1, HSA_OP_BWD = 2, HSA_OP_DECODE 
 
 /* hsa_bwd flags */
 #define HSA_BWD_FOLD_KSLC 0x1u /* add dKslc/S into every key row of the chunk (Kslc = mean K) */
+#define HSA_BWD_AFTER_FWD 0x2u /* ws holds what hsa_fwd left in it for this problem, Q, K, idx
+                                  and w: reuse it (see hsa_bwd) */
 
 typedef struct hsa_problem {
   int32_t B;        /* batch (decode: number of sequences) */
@@ -139,7 +141,16 @@ hsa_status_t hsa_fwd(const hsa_problem_t* p, const void* Q, const void* K, const
  *   dQ [B, L, Hq, D], dK, dV, dQs [B, L, Hkv, D] dtype
  *   dKslc [B, nC, Hkv, D] fp32, gradient with respect to Kslc (may be NULL)
  * flags: HSA_BWD_FOLD_KSLC adds dKslc[c]/S to dK of every row of chunk c, which is the
- * complete key gradient when Kslc was pooled from K. */
+ * complete key gradient when Kslc was pooled from K.
+ * HSA_BWD_AFTER_FWD: the caller ran hsa_fwd with the same problem, Q, K, idx and w on this
+ * same workspace (sized for hsa_bwd, which is at least the forward's size) and has not
+ * touched it since.  The forward leaves at the start of its workspace the per-tile job lists,
+ * the key rows in matrix-core operand order and every (token, head, slot)'s softmax
+ * normaliser; the backward then skips rebuilding them and takes its probabilities from the
+ * normaliser.  The results equal those without the flag up to fp32 rounding.  When the
+ * problem uses the plain kernels (fp32, HSA_FLAG_GENERIC, or shapes outside the matrix-core
+ * kernels) the flag has no effect.  Passing it without that forward call gives undefined
+ * results. */
 hsa_status_t hsa_bwd(const hsa_problem_t* p, const void* Q, const void* K, const void* V,
                      const void* Qs, const void* Kslc, const int32_t* idx, const float* score,
                      const float* w, const void* dO, void* dQ, void* dK, void* dV, void* dQs,

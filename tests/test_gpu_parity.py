@@ -133,6 +133,31 @@ def test_small_end_to_end(hsa, dev, wl, generic):
     compare_backward(orc, x, wl, g, f, diff, grads)
 
 
+@pytest.mark.parametrize("wl", [w for w in SMALL if w.dtype == torch.bfloat16],
+                         ids=lambda w: w.name)
+def test_backward_after_forward(hsa, dev, wl):
+    """Forward and backward on one workspace, the backward reusing the forward's state
+    (HSA_BWD_AFTER_FWD): parity with the oracle, and agreement with the stand-alone backward."""
+    from chunk_sparse_attention_amd import _lib
+    say("case after_fwd", wl)
+    orc = oracle.get()
+    x = workloads.make_inputs(wl, seed=0)
+    Q, K, V, Qs = (x[k].to(dev) for k in ("Q", "K", "V", "Qs"))
+    dO = x["dO"].to(dev)
+    Kslc, idx, score, w = hsa.select(Qs, K, wl.K)
+    prob = hsa.problem(wl.B, wl.L, wl.Hq, wl.Hkv, wl.D, wl.K, wl.dtype)
+    ws = hsa.workspace(_lib.HSA_OP_BWD, prob, dev)
+    O = hsa.fwd(Q, K, V, idx, w, ws=ws)
+    grads = hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, ws=ws, after_fwd=True)
+    alone = hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO)
+    torch.cuda.synchronize()
+    g = dict(Q=Q, K=K, V=V, Qs=Qs, Kslc=Kslc, idx=idx, score=score, w=w, O=O)
+    f, diff, _ = compare_forward(orc, x, wl, g)
+    compare_backward(orc, x, wl, g, f, diff, grads)
+    for k in ("dQ", "dK", "dV", "dQs"):
+        assert max_abs(npy(grads[k]), npy(alone[k])) <= 1e-2, k
+
+
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
 @pytest.mark.parametrize("wl", SMALL[1:4], ids=lambda w: w.name)
 def test_given_selection(hsa, dev, wl, generic):
