@@ -82,12 +82,15 @@ __device__ void block_inclusive_scan(int* a, int* wtot, int N, int op) {
 }
 
 // From sorted keys[0..N): the number of valid edges and the job list.  A job is up to
-// `tpj` consecutive edges of one chunk; jobs[j] = first edge | (edge count << 16).
+// `tpj` consecutive edges of one chunk; jobs[j] = first edge | (edge count << 16).  Up to
+// 4/tpj consecutive jobs of one chunk form a piece (at most four tokens) that is scheduled as
+// a unit, so one wave serves them with one load of the chunk's operands; phead[j] = the
+// piece's first job.
 // Scratch arrays rs and tmp hold N ints each (tmp also holds the scan's wave totals).
 // Returns through *n_valid / *n_jobs (LDS).
 template <int NT>
 __device__ void build_jobs(const uint32_t* keys, int N, int tpj, int* rs, int* tmp,
-                           uint32_t* jobs, int* n_valid, int* n_jobs) {
+                           uint32_t* jobs, int* phead, int* n_valid, int* n_jobs) {
   for (int i = threadIdx.x; i < N; i += NT) {
     bool v = keys[i] != kNoEdge;
     if (v && (i + 1 == N || keys[i + 1] == kNoEdge)) *n_valid = i + 1;
@@ -111,7 +114,11 @@ __device__ void build_jobs(const uint32_t* keys, int N, int tpj, int* rs, int* t
       int cnt = 1;
       const int c = edge_chunk(keys[i]);
       while (cnt < tpj && i + cnt < nv && edge_chunk(keys[i + cnt]) == c) ++cnt;
-      jobs[jf[i] - 1] = (uint32_t)i | ((uint32_t)cnt << 16);
+      const int j = jf[i] - 1;
+      const int pj = 4 / tpj;                       // jobs per piece
+      const int first = jf[rs[i]] - 1;              // first job of the chunk's run
+      jobs[j] = (uint32_t)i | ((uint32_t)cnt << 16);
+      phead[j] = first + (j - first) / pj * pj;
     }
   }
   __syncthreads();
@@ -119,38 +126,40 @@ __device__ void build_jobs(const uint32_t* keys, int N, int tpj, int* rs, int* t
 
 // Conflict-free rounds.  Jobs of one round touch disjoint tokens, so the waves of a round
 // can update the tile's LDS accumulators with plain read-add-write (LDS float atomics are
-// slow on this part).  The rounds are the greedy colouring in job order -- a job takes the
-// lowest round that no earlier job sharing one of its tokens has -- computed in parallel: a
-// job picks its round as soon as all those earlier jobs have theirs, which gives the same
-// rounds as colouring the jobs one by one, in as many block-wide steps as the longest chain
-// of such dependencies (about 20 for random top-8 selections).  A token has at most 16 edges
-// and a job at most 4 tokens, so no round exceeds 4*15 = 60.
-// In: jobs[0..n_jobs), keys.  Out: order[] = jobs grouped by round, roff[0..n_rounds] =
-// round offsets, *n_rounds.  Within a round no token repeats, so the order inside a round
+// slow on this part).  Pieces (see build_jobs) are coloured as units by the greedy rule in
+// piece order -- a piece takes the lowest round that no earlier piece sharing one of its
+// tokens has -- computed in parallel: a piece picks its round as soon as all those earlier
+// pieces have theirs, which gives the same rounds as colouring the pieces one by one, in as
+// many steps as the longest chain of such dependencies (about 20 for random top-8
+// selections).  A piece has at most 4 tokens and a token at most 16 edges, so no round
+// exceeds 4*15 = 60.  Every job takes its piece's round, and a piece's jobs stay adjacent.
+// In: jobs[0..n_jobs), phead, keys.  Out: order[] = jobs grouped by round, roff[0..n_rounds]
+// = round offsets, *n_rounds.  Within a round no token repeats, so the order inside a round
 // does not change any token's accumulation order.  Scratch: colour[n_jobs], jl[TT*16],
 // cnt[64] (ints), tmask[TT].
 template <int NT, int TT>
-__device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, int n_jobs, int Kt,
-                             int* colour, int* jl, int* cnt, unsigned long long* tmask,
-                             int* roff, uint32_t* order, int* n_rounds) {
+__device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, const int* phead,
+                             int n_jobs, int Kt, int* colour, int* jl, int* cnt,
+                             unsigned long long* tmask, int* roff, uint32_t* order,
+                             int* n_rounds) {
   constexpr int kNone = 0x7fffffff;
   static_assert(TT * 16 % 4 == 0, "token lists are read as 16-byte words");
   for (int i = threadIdx.x; i < TT * 16; i += NT) jl[i] = kNone;
   for (int i = threadIdx.x; i < 64; i += NT) cnt[i] = 0;
   for (int i = threadIdx.x; i < TT; i += NT) tmask[i] = 0;
   __syncthreads();
-  // token -> its jobs (every (token, slot) edge lies in exactly one job)
+  // token -> its pieces (every (token, slot) edge lies in exactly one job, hence one piece)
   for (int j = threadIdx.x; j < n_jobs; j += NT) {
     const uint32_t job = jobs[j];
     const int e0 = (int)(job & 0xffff), c = (int)(job >> 16);
     for (int i = 0; i < c; ++i) {
       const uint32_t k = keys[e0 + i];
-      jl[edge_token(k) * 16 + edge_slot(k)] = j;
+      jl[edge_token(k) * 16 + edge_slot(k)] = phead[j];
     }
     colour[j] = -1;
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < TT; t += NT) {  // ascending job order per token
+  for (int t = threadIdx.x; t < TT; t += NT) {  // ascending piece order per token
     int v[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) v[q] = q < Kt ? jl[t * 16 + q] : kNone;
@@ -167,19 +176,19 @@ __device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, int n_j
     for (int q = 0; q < 16; ++q) jl[t * 16 + q] = v[q];
   }
   __syncthreads();
-  // rounds: a job waits until every earlier job of its tokens has a round.  The earlier jobs
-  // of one token form a chain (each waits for the one before it), so a job is ready exactly
-  // when the latest earlier job of each of its tokens has a round.  Each lane takes its jobs
-  // (j = lane + s*NT) in ascending order and re-checks its current job until it is ready;
-  // the smallest job without a round is always some lane's current job and is ready, so the
-  // waves make progress without block barriers.  tmask[t] collects the rounds of t's jobs so
-  // far (its earlier jobs); a job adds its round there before it publishes the round.
+  // rounds of the piece heads.  The earlier pieces of one token form a chain (each waits
+  // for the one before it), so a piece is ready exactly when the latest earlier piece of
+  // each of its tokens has a round.  Each lane takes its heads (j = lane + s*NT) in
+  // ascending order and re-checks its current one until it is ready; the smallest head
+  // without a round is always some lane's current one and is ready, so the waves make
+  // progress without block barriers.  tmask[t] collects the rounds of t's pieces so far
+  // (its earlier pieces); a piece adds its round there before it publishes the round.
   {
     constexpr int kJpt = 4;  // jobs per lane: n_jobs <= TT*16 <= 4*NT
     const volatile int* vcol = colour;
     int nts[kJpt], prevs[kJpt][4], tks[kJpt][4];
 #pragma unroll
-    for (int s = 0; s < kJpt; ++s) {  // every job's tokens and latest earlier jobs, up front
+    for (int s = 0; s < kJpt; ++s) {  // every head's tokens and latest earlier pieces
       const int j = threadIdx.x + s * NT;
       nts[s] = 0;
 #pragma unroll
@@ -187,14 +196,23 @@ __device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, int n_j
         prevs[s][i] = -1;
         tks[s][i] = 0;
       }
-      if (j < n_jobs) {
-        const uint32_t job = jobs[j];
-        const int e0 = (int)(job & 0xffff);
-        nts[s] = (int)(job >> 16);
+      if (j < n_jobs && phead[j] == j) {
+        int n = 0;
+        for (int jj = j; jj < n_jobs && phead[jj] == j; ++jj) {
+          const uint32_t job = jobs[jj];
+          const int e0 = (int)(job & 0xffff), c = (int)(job >> 16);
+          for (int i = 0; i < c; ++i) {
+            const int t = edge_token(keys[e0 + i]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (q == n) tks[s][q] = t;
+            ++n;
+          }
+        }
+        nts[s] = n;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (i < nts[s]) {
-            tks[s][i] = edge_token(keys[e0 + i]);
+          if (i < n) {
             const int4* l4 = reinterpret_cast<const int4*>(jl + tks[s][i] * 16);
             int pv = -1;
 #pragma unroll
@@ -212,11 +230,13 @@ __device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, int n_j
     }
     int cur = 0;
     for (;;) {
-      int nt = 0, prev[4], tk[4];
+      // the current head: the next slot with a piece (slots without one are skipped)
+      int nt = 0, prev[4], tk[4], jcur = 0;
 #pragma unroll
-      for (int s = 0; s < kJpt; ++s)
-        if (s == cur) {
+      for (int s = kJpt - 1; s >= 0; --s)
+        if (s >= cur && nts[s] > 0) {
           nt = nts[s];
+          jcur = threadIdx.x + s * NT;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             prev[i] = prevs[s][i];
@@ -239,15 +259,19 @@ __device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, int n_j
           for (int i = 0; i < 4; ++i)
             if (i < nt) atomicOr(&tmask[tk[i]], 1ull << r);
           __threadfence_block();
-          colour[threadIdx.x + cur * NT] = r;
-          ++cur;
+          colour[jcur] = r;
+          cur = (jcur - threadIdx.x) / NT + 1;
         }
       }
     }
     __syncthreads();
   }
-  // group by round: sizes, offsets (rounds used are 0..n_rounds-1), then placement
-  for (int j = threadIdx.x; j < n_jobs; j += NT) atomicAdd(&cnt[colour[j]], 1);
+  // every job takes its piece's round; round sizes, offsets (rounds used are
+  // 0..n_rounds-1); then each head places its piece's jobs adjacently
+  for (int j = threadIdx.x; j < n_jobs; j += NT) {
+    const int r = colour[phead[j]];
+    atomicAdd(&cnt[r], 1);
+  }
   __syncthreads();
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -265,7 +289,13 @@ __device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, int n_j
     cnt[lane] = incl - size;  // placement cursor of round `lane`
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < n_jobs; j += NT) order[atomicAdd(&cnt[colour[j]], 1)] = jobs[j];
+  for (int j = threadIdx.x; j < n_jobs; j += NT) {
+    if (phead[j] != j) continue;
+    int sz = 1;
+    while (j + sz < n_jobs && phead[j + sz] == j) ++sz;
+    const int pos = atomicAdd(&cnt[colour[j]], sz);
+    for (int i = 0; i < sz; ++i) order[pos + i] = jobs[j + i];
+  }
   __syncthreads();
 }
 
@@ -285,6 +315,7 @@ __global__ void __launch_bounds__(NT) k_tile_prep(const int32_t* __restrict__ id
   __shared__ uint32_t jobs[NMAX];
   __shared__ int scratch[3 * NMAX];
   __shared__ __attribute__((aligned(16))) int jl[TT * 16];
+  __shared__ int phead[NMAX];
   __shared__ int cnt[64];
   __shared__ unsigned long long tmask[TT];
   __shared__ int n_valid_sh, n_jobs_sh, n_rounds_sh;
@@ -308,11 +339,11 @@ __global__ void __launch_bounds__(NT) k_tile_prep(const int32_t* __restrict__ id
   }
   __syncthreads();
   block_bitonic_sort<NT>(keys, N);
-  build_jobs<NT>(keys, N, tpj, scratch, scratch + NMAX, jobs, &n_valid_sh, &n_jobs_sh);
+  build_jobs<NT>(keys, N, tpj, scratch, scratch + NMAX, jobs, phead, &n_valid_sh, &n_jobs_sh);
   const int n_jobs = n_jobs_sh;
   uint32_t* order = reinterpret_cast<uint32_t*>(scratch + NMAX);
   int* roff = scratch + 2 * NMAX;
-  build_rounds<NT, TT>(keys, jobs, n_jobs, Kt, scratch, jl, cnt, tmask, roff, order,
+  build_rounds<NT, TT>(keys, jobs, phead, n_jobs, Kt, scratch, jl, cnt, tmask, roff, order,
                        &n_rounds_sh);
   uint32_t* out = prep + (size_t)blockIdx.x * prep_words(TT);
   const int nv = n_valid_sh, nr = n_rounds_sh;
