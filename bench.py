@@ -26,6 +26,7 @@ import hashlib
 import glob
 import json
 import os
+import re
 import sys
 import time
 
@@ -106,17 +107,163 @@ def roofline(name: str, counts: dict, avg_ms: float, traffic) -> dict:
     return r
 
 
-def measured_traffic(entry: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel sources; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{entry}.json")
+# kernel function name -> kernel class of the launch timer; the first matching prefix wins.
+# A class launch is one host call: the inverse index runs three kernels per launch, counted
+# by its scatter.
+KERNEL_CLASS_OF = (("k_bwd_p2_reduce", "bwd_reduce"), ("k_bwd_p2", "bwd_p2"),
+                   ("k_bwd_p1", "bwd_p1"), ("k_inv_", "invidx"), ("k_tile_prep", "tile_prep"),
+                   ("k_prep_ops", "prep_ops"), ("k_fwd_", "fwd"), ("k_select", "select"),
+                   ("k_pool", "pool"), ("k_dec_scan", "decode_scan"),
+                   ("k_dec_attend", "decode_attend"))
+LAUNCH_KERNEL = {"invidx": "k_inv_scatter"}
+
+
+def kernel_class(kernel_name: str):
+    m = re.search(r"hsa::(k_[a-z0-9_]+)", kernel_name)
+    if not m:
+        return None, None
+    for prefix, cls in KERNEL_CLASS_OF:
+        if m.group(1).startswith(prefix):
+            return cls, m.group(1)
+    return None, m.group(1)
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def measured_traffic(workload: str, cls: str):
+    """HBM bytes per launch of one kernel class, from the committed rocprofv3 counter summary
+    of the workload, if it was taken on the current kernel sources; otherwise None."""
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
     if t.get("source_sha") != source_sha():
         return None
-    return t.get("hbm_bytes_per_launch")
+    k = t.get("kernels", {}).get(cls)
+    return None if k is None else k["hbm_bytes_per_launch"]
+
+
+def summarize_counters(cdir: str, workload: str, copy_mib: int) -> int:
+    """Turn two rocprofv3 --pmc runs of `bench.py --only step --copy-mib M` (FETCH_SIZE under
+    cdir/fetch, WRITE_SIZE under cdir/write) into HBM bytes per launch of each kernel class.
+    Each counter is scaled by what it reads for the plain device copy of M MiB that the run
+    makes first (a copy reads M MiB and writes M MiB).  Writes profiles/traffic_<workload>.json
+    and prints a markdown table."""
+    import collections
+    import csv
+    vals = {}
+    for sub, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        files = glob.glob(os.path.join(cdir, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            log(f"bench: no counter_collection.csv under {cdir}/{sub}")
+            return 1
+        per = collections.defaultdict(list)
+        with open(files[0]) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    per[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)
+        vals[counter] = per
+    copies = [(max(v), k) for k, v in vals["FETCH_SIZE"].items() if "copy" in k.lower()]
+    if not copies:
+        log("bench: no copy kernel in the FETCH_SIZE run")
+        return 1
+    cf, ck = max(copies)
+    cw = max(vals["WRITE_SIZE"][ck])
+    ref = copy_mib * 2.0 ** 20
+    fs, wsc = ref / cf, ref / cw
+    acc = collections.defaultdict(lambda: dict(fetch=0.0, write=0.0, launches=0, names=set()))
+    for name, fv in vals["FETCH_SIZE"].items():
+        cls, fn = kernel_class(name)
+        if cls is None:
+            continue
+        a = acc[cls]
+        a["fetch"] += sum(fv) * fs
+        a["write"] += sum(vals["WRITE_SIZE"].get(name, [])) * wsc
+        if LAUNCH_KERNEL.get(cls, fn) == fn:
+            a["launches"] += len(fv)
+        a["names"].add(re.sub(r"\(.*", "", name).replace("void ", "").strip())
+    out = {"source_sha": source_sha(), "workload": workload,
+           "copy_reference": {"mib": copy_mib, "kernel": re.sub(r"\(.*", "", ck)[:100],
+                              "fetch_read_over_true": round(cf / ref, 4),
+                              "write_read_over_true": round(cw / ref, 4)},
+           "kernels": {}}
+    print(f"| kernel class | launches | FETCH MB/launch | WRITE MB/launch | HBM MB/launch | kernels |")
+    print("|---|---:|---:|---:|---:|---|")
+    for cls in sorted(acc, key=lambda c: -(acc[c]["fetch"] + acc[c]["write"])):
+        a = acc[cls]
+        n = max(a["launches"], 1)
+        f, w = a["fetch"] / n, a["write"] / n
+        out["kernels"][cls] = dict(launches=a["launches"], fetch_bytes_per_launch=round(f),
+                                   write_bytes_per_launch=round(w),
+                                   hbm_bytes_per_launch=round(f + w), kernels=sorted(a["names"]))
+        print(f"| {cls} | {a['launches']} | {f / 1e6:.1f} | {w / 1e6:.1f} | {(f + w) / 1e6:.1f} "
+              f"| {', '.join('`' + k + '`' for k in sorted(a['names']))} |")
+    print(f"\nCopy reference ({copy_mib} MiB, `{out['copy_reference']['kernel'][:60]}`): "
+          f"FETCH_SIZE reads {cf / ref:.3f} x and WRITE_SIZE {cw / ref:.3f} x the bytes moved; "
+          f"the figures above are scaled by {fs:.3f} and {wsc:.3f}.")
+    with open(traffic_path(workload), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    # optional runs of the same command with L2 (DIR/l2) and SQ (DIR/sq) counters
+    extra = collections.defaultdict(lambda: collections.defaultdict(list))
+    for sub in ("l2", "sq"):
+        for f in glob.glob(os.path.join(cdir, sub, "**", "*counter_collection.csv"),
+                           recursive=True)[:1]:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    cls, fn = kernel_class(r["Kernel_Name"])
+                    if cls:
+                        extra[fn][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if extra:
+        print("\n| kernel | L2 hit rate | waves | per wave: VALU | MFMA | LDS | VMEM rd | "
+              "wave cycles | waiting cycles |")
+        print("|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+        for fn, c in sorted(extra.items()):
+            m = {k: sum(v) / len(v) for k, v in c.items()}
+            hit = m.get("TCC_HIT_sum", 0.0)
+            tot = hit + m.get("TCC_MISS_sum", 0.0)
+            wv = m.get("SQ_WAVES", 0.0)
+
+            def pw(k):
+                return f"{m[k] / wv:.0f}" if wv and k in m else "-"
+            print(f"| `{fn}` | {hit / tot:.3f} | {wv:.0f} | {pw('SQ_INSTS_VALU')} | "
+                  f"{pw('SQ_INSTS_MFMA')} | {pw('SQ_INSTS_LDS')} | {pw('SQ_INSTS_VMEM_RD')} | "
+                  f"{pw('SQ_WAVE_CYCLES')} | {pw('SQ_WAIT_INST_ANY')} |" if tot else
+                  f"| `{fn}` | - | {wv:.0f} | - | - | - | - | - | - |")
+    return 0
+
+
+def summarize_trace(tdir: str, bench_json: str) -> int:
+    """Markdown table of a rocprofv3 --kernel-trace --stats run (run_kernel_stats.csv under
+    tdir) beside the per-launch averages the bench's own HIP-event timer printed."""
+    import csv
+    files = glob.glob(os.path.join(tdir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        log(f"bench: no kernel_stats.csv under {tdir}")
+        return 1
+    rows = list(csv.DictReader(open(files[0])))
+    print("| kernel | calls | avg µs | min µs | max µs | % of GPU time |")
+    print("|---|---:|---:|---:|---:|---:|")
+    by_cls = {}
+    for r in rows:
+        name = re.sub(r"\(.*", "", r["Name"]).replace("void ", "").strip()
+        calls = int(r["Calls"])
+        avg = float(r["AverageNs"]) / 1e3
+        print(f"| `{name[:90]}` | {calls} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+              f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+        cls, _ = kernel_class(r["Name"])
+        if cls:
+            by_cls.setdefault(cls, []).append(f"`{name}` {avg / 1e3:.4f}")
+    with open(bench_json) as fh:
+        b = json.loads(fh.read().strip().splitlines()[-1])
+    print("\n| kernel class | bench.py avg ms per launch | rocprofv3 avg ms per kernel |")
+    print("|---|---:|---|")
+    for cls, k in sorted(b["kernels"].items(), key=lambda kv: -kv[1]["ms_per_step"]):
+        print(f"| {cls} | {k['avg_ms']:.4f} | {'; '.join(by_cls.get(cls, []))} |")
+    return 0
 
 
 def cpu_baseline(wl, x, budget_s: float = 20.0) -> dict:
@@ -203,10 +350,20 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="profiling aid: with --only, first copy this many MiB once with a plain "
                          "device copy (the scale reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["select", "fwd", "bwd", "decode"], default=None,
-                    help="profiling aid: after one full step, run only this entry point "
-                         "--steps times and print its mean time (no JSON line)")
+    ap.add_argument("--only", choices=["step", "select", "fwd", "bwd", "decode"], default=None,
+                    help="profiling aid: after the warm-up, run only this entry point (or the "
+                         "whole step) --steps times and print its mean time (no JSON line)")
+    ap.add_argument("--summarize-counters", metavar="DIR", default=None,
+                    help="write profiles/traffic_<workload>.json from the FETCH_SIZE (DIR/fetch) "
+                         "and WRITE_SIZE (DIR/write) runs of --only step --copy-mib M; no GPU")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("DIR", "BENCH_JSON"), default=None,
+                    help="markdown table of a --kernel-trace --stats run beside the bench's "
+                         "own per-launch timing; no GPU")
     args = ap.parse_args()
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.workload, args.copy_mib)
+    if args.summarize_trace:
+        return summarize_trace(*args.summarize_trace)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build of the HSA operator has no multi-GPU "
               f"path (asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
@@ -257,7 +414,8 @@ def main() -> int:
         prob_fwd = hsa.problem(wl.B, wl.L, wl.Hq, wl.Hkv, wl.D, wl.K, wl.dtype, generic=gen)
         ws_fwd = hsa.workspace(_lib.HSA_OP_FWD, prob_fwd, dev)
         O = torch.empty_like(Q)
-        run = {"select": lambda: hsa.select(Qs, K, wl.K, generic=gen),
+        run = {"step": step,
+               "select": lambda: hsa.select(Qs, K, wl.K, generic=gen),
                "fwd": lambda: hsa.fwd(Q, K, V, idx, w, generic=gen, ws=ws_fwd, out=O),
                "bwd": lambda: hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, generic=gen,
                                       ws=ws_bwd)}[args.only]
@@ -303,7 +461,7 @@ def main() -> int:
     for name, (n, total) in ktimes.items():
         if n == 0:
             continue
-        r = roofline(name, counts[name], total / n, measured_traffic(name))
+        r = roofline(name, counts[name], total / n, measured_traffic(wl.name, name))
         r["launches_per_step"] = round(n / args.steps, 3)
         r["ms_per_step"] = round(total / args.steps, 4)
         kern[name] = r
