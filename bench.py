@@ -57,7 +57,14 @@ def causal_candidates(wl) -> int:
     return wl.B * wl.Hkv * per_seq
 
 
-def kernel_counts(wl, n_slots: int) -> dict:
+def fused_backward(wl, generic: bool) -> bool:
+    """The library's bf16 D=64 backward: chunk phase with per-edge dQ partials, then a token
+    phase (no token-tile phase)."""
+    return (not generic and str(wl.dtype).endswith("bfloat16") and wl.D == 64
+            and wl.G in (4, 8, 16))
+
+
+def kernel_counts(wl, n_slots: int, fused: bool = True) -> dict:
     """Algorithmic bytes (each input the kernel needs read once, each output it produces
     written once; workspace copies of the design are not counted) and flops per launch of
     each kernel class.  n_slots = valid (b, t, g, k) selections; every slot is attended by
@@ -69,7 +76,7 @@ def kernel_counts(wl, n_slots: int) -> dict:
     kslc = B * wl.nC * Hkv * D * el         # Kslc
     slot = B * L * Hkv * K * 4              # idx, score, w or ds
     eg = n_slots * wl.G
-    return {
+    c = {
         "pool": dict(bytes=kv + kslc, flops=B * wl.nC * Hkv * D * S),
         "select": dict(bytes=kv + kslc + 3 * slot, flops=2 * D * causal_candidates(wl),
                        alu=True),
@@ -78,9 +85,16 @@ def kernel_counts(wl, n_slots: int) -> dict:
         "fwd": dict(bytes=2 * q + 2 * kv + 2 * slot, flops=4 * S * D * eg),
         "invidx": dict(bytes=slot + 4 * n_slots, flops=0),
         "bwd_p1": dict(bytes=3 * q + 4 * kv + kslc + 4 * slot, flops=6 * S * D * eg),
-        "bwd_p2": dict(bytes=2 * q + 5 * kv + 2 * slot + 4 * n_slots + 2 * kslc, flops=8 * S * D * eg),
+        "bwd_p2": dict(bytes=2 * q + 5 * kv + 2 * slot + 4 * n_slots + 2 * kslc,
+                       flops=8 * S * D * eg),
         "bwd_reduce": dict(bytes=2 * kv + 2 * kslc, flops=0),
     }
+    if fused:
+        # token phase: dQ and dQs out, the slots and Kslc rows in; dKslc partials read Qs
+        c["bwd_p1"] = dict(bytes=q + 2 * kv + kslc + 3 * slot, flops=0)
+        # chunk phase: Q, dO, K, V and the weights in; S, dP, dV, dK and dQ products
+        c["bwd_p2"] = dict(bytes=2 * q + 2 * kv + slot, flops=10 * S * D * eg)
+    return c
 
 
 def roofline(name: str, counts: dict, avg_ms: float, traffic) -> dict:
@@ -456,7 +470,7 @@ def main() -> int:
     entry_ms = {n: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps, 4)
                 for j, n in enumerate(names)}
     log("bench: per-entry ms", entry_ms)
-    counts = kernel_counts(wl, n_slots)
+    counts = kernel_counts(wl, n_slots, fused_backward(wl, gen))
     kern = {}
     for name, (n, total) in ktimes.items():
         if n == 0:
@@ -522,7 +536,7 @@ def main() -> int:
         kt2 = hsa.timer_read()
         ts /= reps
         tf /= reps
-        c2 = kernel_counts(wl2, n2)
+        c2 = kernel_counts(wl2, n2, fused_backward(wl2, gen))
         k2 = {name: roofline(name, c2[name], total / n, None)
               for name, (n, total) in kt2.items() if n}
         out["secondary"] = {

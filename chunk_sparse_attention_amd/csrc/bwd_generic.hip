@@ -46,10 +46,15 @@ BwdLayout bwd_layout(const Dims& d) {
   l.part_dk = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
   l.part_dv = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
   l.part_dks = take(sizeof(float) * bg * l.max_seg * d.D);
-  l.kt = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
-  l.vop = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
-  // per (token, group, slot, head): D = <dO, O_k> (the normaliser is in the state prefix)
-  l.dd = take(sizeof(float) * bg * E * d.G);
+  if (bwd_fused(d)) {
+    // per (token, group, slot, head): the edge's dQ contribution (bf16, D values)
+    l.dq_part = take(sizeof(uint16_t) * bg * E * d.G * d.D);
+  } else {
+    l.kt = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
+    l.vop = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
+    // per (token, group, slot, head): D = <dO, O_k> (the normaliser is in the state prefix)
+    l.dd = take(sizeof(float) * bg * E * d.G);
+  }
   l.total = o;
   return l;
 }

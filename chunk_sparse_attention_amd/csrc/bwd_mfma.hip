@@ -6,18 +6,26 @@
 // selected it; the chunk weights pass gradient on into the selection scores (same note,
 // 层次化稀疏注意力（HSA）, 端到端学习).
 //
-// Phase 1 (token tiles, like the forward): per 16-column job of one chunk
+// The gradients of queries, keys, values, chunk weights and selection scores are the same as
+// that two-phase plan's; the order of the work differs with the head dimension.
+//
+// D = 64 (fused): the chunk phase does all the per-edge work.  Per segment of a chunk's
+// selector list (the chunk -> (token, slot) index) and job of 16 query rows:
+//   S = Q K_c^T, dP = dO V_c^T; P = softmax1(S); D = sum_keys P.dP; dS = w P (dP - D)
+//   dV^T += dO^T (w P), dK^T += Q^T dS     (MFMA, registers, fp32 partial per segment)
+//   dQ_k^T = K_c^T dS^T                     (MFMA, one bf16 partial per selection edge)
+//   dw_edge = sum over the edge's heads of D
+// A token phase sums each token's dQ partials in slot order and applies the stick-breaking
+// chain rule for ds and dQs; a segment pass forms dKslc = sum ds * Qs; a fixed-order
+// reduction sums the segments' partials per chunk.
+//
+// D = 128: phase 1 (token tiles, like the forward), per 16-column job of one chunk
 //   S^T = K_c Q^T, dP^T = V_c dO^T                     (MFMA)
 //   P = softmax1(S), D = sum_keys P.dP, dS = w P (dP - D)   (per column, fp32)
 //   dQ^T += K_c^T dS^T                                  (MFMA, into LDS by rounds)
 //   dw_edge = sum over the token's heads of D
-// then per token the stick-breaking chain rule gives ds and dQs.
-// Phase 2 (chunk segments over the chunk -> (token, slot) index): per job of 16 query rows
-//   S = Q K_c^T, dP = dO V_c^T; P from phase 1's softmax normaliser, D from phase 1, dS as
-//   above (rows = queries, columns = keys)
-//   dV^T += dO^T (w P),  dK^T += Q^T dS                  (MFMA 16x16x16, registers)
-//   dKslc += ds * Qs
-// and every segment writes fp32 partials that a fixed-order reduction sums per chunk.
+// then per token the stick-breaking chain rule gives ds and dQs; phase 2 is the vector-ALU
+// chunk phase with the same reduction.
 #include "hsa_common.h"
 #include "hsa_launch.h"
 #include "mfma_common.h"
@@ -323,31 +331,38 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
   }
 }
 
-// ---- phase 2 -------------------------------------------------------------------------------
+// ---- fused backward for D = 64: chunk phase, then token phase -------------------------------
 
-// One wave per segment of a chunk's selector list (D = 64).  The chunk's keys and values sit
-// in LDS; a job takes 16/G selectors (16 query rows).  dK^T and dV^T accumulate in registers
-// (MFMA accumulators) for the whole segment.
-template <int G>
+// Chunk phase: one wave per segment of a chunk's selector list.  The chunk's keys and values
+// sit in LDS; a job takes 16/G selectors (16 query rows, row q = selector * G + head):
+//   S = Q K_c^T, dP = dO V_c^T                               (MFMA 16x16x32)
+//   P = exp(S - lse), with lse the forward's normaliser (HL) or computed here over the
+//   chunk's 64 keys; D = rowsum(P * dP); dS = w P (dP - D)
+//   dV^T += dO^T (w P), dK^T += Q^T dS                       (MFMA 16x16x16, registers)
+//   dQ_k^T = K_c^T dS^T                                      (MFMA 16x16x16, per edge)
+//   dw_edge = sum over the edge's G heads of D
+// Every selection edge belongs to exactly one segment, so the edge's dQ contribution (bf16,
+// unscaled) and dw are stored once; the segment's dK/dV are fp32 partials that a fixed-order
+// reduction sums per chunk.
+template <int G, bool HL>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
-k_bwd_p2_mfma(
+k_bwd_chunk_mfma(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ Qs, const float* __restrict__ w, const bf16* __restrict__ dO,
-    const float* __restrict__ ds_in, const float* __restrict__ lse_in,
-    const float* __restrict__ dd_in, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ entries, const int32_t* __restrict__ seg_start,
-    const int32_t* __restrict__ seg_chunk, const int32_t* __restrict__ n_seg,
-    float* __restrict__ part_dk, float* __restrict__ part_dv, float* __restrict__ part_dks,
-    int L, int Hq, int Hkv, int Kn, int nC, int seg, int64_t max_seg, float c2, float sm_scale,
-    float sel_scale) {
+    const float* __restrict__ w, const bf16* __restrict__ dO, const float* __restrict__ lse_in,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries,
+    const int32_t* __restrict__ seg_start, const int32_t* __restrict__ seg_chunk,
+    const int32_t* __restrict__ n_seg, float* __restrict__ part_dk, float* __restrict__ part_dv,
+    bf16* __restrict__ dq_part, float* __restrict__ dw_out, int L, int Hq, int Hkv, int Kn,
+    int nC, int seg, int64_t max_seg, float c2, float sm_scale) {
   constexpr int D = 64, TPJ = 16 / G, KS = D / 32, DT = D / 16;
   constexpr int SEGMAX = 128;
   __shared__ __attribute__((aligned(16))) uint16_t kl[64][D + 8];
   __shared__ __attribute__((aligned(16))) uint16_t vl[64][D + 8];
   __shared__ __attribute__((aligned(16))) uint16_t ql[16][D + 8];
   __shared__ __attribute__((aligned(16))) uint16_t dl[16][D + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sdl[64][16];  // dS^T of the job
   __shared__ int tok_l[SEGMAX], k_l[SEGMAX];
-  __shared__ float w_l[SEGMAX], ds_l[SEGMAX];
+  __shared__ float w_l[SEGMAX];
   const int64_t sidx = blockIdx.x % max_seg;
   const int bg = (int)(blockIdx.x / max_seg);
   if (sidx >= n_seg[bg]) return;  // whole wave
@@ -362,15 +377,12 @@ k_bwd_p2_mfma(
   const int lane = threadIdx.x, col = lane % 16, blk = lane / 16;
   const size_t kvrow = (size_t)Hkv * D;
   const size_t cb = ((b * L + (size_t)c * 64) * Hkv + g) * D;
-  // the segment's selectors: token, weight, score gradient (one gather per entry)
   for (int i = lane; i < ne; i += 64) {
     const int val = ent[i];
     const int t = val / Kn, k = val % Kn;
-    const size_t o = ((b * L + t) * Hkv + g) * Kn + k;
     tok_l[i] = t;
     k_l[i] = k;
-    w_l[i] = w[o];
-    ds_l[i] = ds_in[o];
+    w_l[i] = w[((b * L + t) * Hkv + g) * Kn + k];
   }
   for (int i = lane; i < 64 * (D / 8); i += 64) {
     const int key = i / (D / 8), d = (i % (D / 8)) * 8;
@@ -385,14 +397,12 @@ k_bwd_p2_mfma(
       dk[dt][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
       dv[dt][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  float dks = 0.0f;
   const int qs_sel = col / G, qs_head = col % G;  // this lane's A-operand row -> selector, head
   __syncthreads();
 
-  // this lane's query row of job j (a padding row repeats the job's first selector), and
-  // phase 1's normaliser and D of the lane's four output rows 4*blk + i
-  auto load_rows = [&](int ej, bf16x8 (&qa)[KS], bf16x8 (&da)[KS], float (&le)[4],
-                       float (&dd)[4]) {
+  // this lane's query row of job j (a padding row repeats the job's first selector) and, with
+  // HL, the forward's normaliser of the lane's four output rows 4*blk + i
+  auto load_rows = [&](int ej, bf16x8 (&qa)[KS], bf16x8 (&da)[KS], float (&le)[4]) {
     const int n_here = min(TPJ, ne - ej);
     const int t = tok_l[ej + (qs_sel < n_here ? qs_sel : 0)];
     const size_t qoff = ((b * L + t) * Hq + (size_t)g * G + qs_head) * D;
@@ -401,47 +411,29 @@ k_bwd_p2_mfma(
       qa[ks] = ld_bf16x8(Q + qoff + 32 * ks + 8 * blk);
       da[ks] = ld_bf16x8(dO + qoff + 32 * ks + 8 * blk);
     }
+    if (HL) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * blk + i, s2 = r / G, e = ej + (s2 < n_here ? s2 : 0);
-      const size_t so = (((b * L + tok_l[e]) * Hkv + g) * Kn + k_l[e]) * G + r % G;
-      le[i] = lse_in[so];
-      dd[i] = dd_in[so];
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * blk + i, s2 = r / G, e = ej + (s2 < n_here ? s2 : 0);
+        le[i] = lse_in[(((b * L + tok_l[e]) * Hkv + g) * Kn + k_l[e]) * G + r % G];
+      }
     }
   };
   bf16x8 qn[KS], dn[KS];
-  float len[4], ddn[4];
-  float qsn = 0.0f;  // Qs of the next job's selectors, summed with their ds
-  auto load_qs = [&](int ej) {
-    float a = 0.0f;
-    const int n_here = min(TPJ, ne - ej);
-    for (int s2 = 0; s2 < n_here; ++s2)
-      a += ds_l[ej + s2] * to_f32(Qs[((b * L + tok_l[ej + s2]) * Hkv + g) * D + lane]);
-    return a;
-  };
-  if (ne > 0) {
-    load_rows(0, qn, dn, len, ddn);
-    qsn = load_qs(0);
-  }
+  float len[4] = {0.f, 0.f, 0.f, 0.f};
+  if (ne > 0) load_rows(0, qn, dn, len);
   for (int ej = 0; ej < ne; ej += TPJ) {
     const int n_here = min(TPJ, ne - ej);
     bf16x8 qa[KS], da[KS];
-    float lse[4], dr[4];
+    float lse[4];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qa[ks] = qn[ks];
       da[ks] = dn[ks];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lse[i] = len[i];
-      dr[i] = ddn[i];
-    }
-    dks += qsn;
-    if (ej + TPJ < ne) {
-      load_rows(ej + TPJ, qn, dn, len, ddn);
-      qsn = load_qs(ej + TPJ);
-    }
+    for (int i = 0; i < 4; ++i) lse[i] = len[i];
+    if (ej + TPJ < ne) load_rows(ej + TPJ, qn, dn, len);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       *reinterpret_cast<bf16x8*>(&ql[col][32 * ks + 8 * blk]) = qa[ks];
@@ -462,17 +454,45 @@ k_bwd_p2_mfma(
         pa[t4] = mfma_16x16x32(da[ks], vb, pa[t4]);
       }
     }
-    // per query row r = 4*blk + i: softmax1 over the 64 keys from phase 1's normaliser
-    float wr[4];
+    if (!HL) {  // softmax1 normaliser of each row over the chunk's 64 keys (log2 domain)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = 0.0f;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) m = fmaxf(m, sa[t4][i] * c2);
+        m = row16_max(m);
+        float sum = 0.0f;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) sum += exp2_fast(sa[t4][i] * c2 - m);
+        sum = row16_sum(sum);
+        lse[i] = m + __builtin_amdgcn_logf(exp2_fast(-m) + sum);
+      }
+    }
+    // P, and per row r = 4*blk + i: D = sum over keys of P dP, the selector's weight
+    float wr[4], dr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = (4 * blk + i) / G;
+      float dsum = 0.0f;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) sa[t4][i] = exp2_fast(sa[t4][i] * c2 - lse[i]);
+      for (int t4 = 0; t4 < 4; ++t4) {
+        sa[t4][i] = exp2_fast(sa[t4][i] * c2 - lse[i]);
+        dsum += sa[t4][i] * pa[t4][i];
+      }
+      dr[i] = row16_sum(dsum);
       wr[i] = s < n_here ? w_l[ej + s] : 0.0f;
     }
+    // dw of each edge: its G rows' D (rows 4*blk .. 4*blk+3 per lane block)
+    {
+      float dsel = (dr[0] + dr[1]) + (dr[2] + dr[3]);
+      if (G >= 8) dsel += __shfl_xor(dsel, 16);
+      if (G == 16) dsel += __shfl_xor(dsel, 32);
+      const int s = (4 * blk) / G;
+      if (col == 0 && (4 * blk) % G == 0 && s < n_here)
+        dw_out[((b * L + tok_l[ej + s]) * Hkv + g) * Kn + k_l[ej + s]] = dsel;
+    }
     // dV^T += dO^T (w P), dK^T += Q^T dS  (k = the 16 query rows, 4 per lane block), the
-    // transposed operands read from LDS with the transposing read
+    // transposed operands read from LDS with the transposing read; dS^T goes to LDS for dQ
     s16x4 doT[DT], qT[DT];
     const int trow = 4 * blk + col / 4, tcol = 4 * (col % 4);
 #pragma unroll
@@ -489,13 +509,33 @@ k_bwd_p2_mfma(
         dsv[i] = wr[i] * sa[t4][i] * (pa[t4][i] - dr[i]);
       }
       const s16x4 wpb = pack_bf16x4(wp), dsb = pack_bf16x4(dsv);
+      *reinterpret_cast<s16x4*>(&sdl[16 * t4 + col][4 * blk]) = dsb;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         dv[dt][t4] = mfma_16x16x16(doT[dt], wpb, dv[dt][t4]);
         dk[dt][t4] = mfma_16x16x16(qT[dt], dsb, dk[dt][t4]);
       }
     }
-    __syncthreads();  // ql/dl reuse by the next job
+    __syncthreads();  // sdl is read transposed below
+    // dQ^T (rows d, columns the 16 query rows) = K_c^T dS^T over the chunk's keys
+    f32x4 dq[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const s16x4 dsT = lds_read_tr4(&sdl[16 * kb + trow][tcol]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        dq[dt] = mfma_16x16x16(lds_read_tr4(&kl[16 * kb + trow][16 * dt + tcol]), dsT, dq[dt]);
+    }
+    if (qs_sel < n_here) {  // lane column = query row col: its edge's partial at d = 16*dt + 4*blk
+      const int e = ej + qs_sel;
+      bf16* dst = dq_part + ((((b * L + tok_l[e]) * Hkv + g) * Kn + k_l[e]) * G + qs_head) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<s16x4*>(dst + 16 * dt + 4 * blk) = pack_bf16x4(dq[dt]);
+    }
+    __syncthreads();  // ql/dl/sdl reuse by the next job
   }
   const size_t pb = (size_t)bg * max_seg + sidx;
 #pragma unroll
@@ -506,7 +546,161 @@ k_bwd_p2_mfma(
       *reinterpret_cast<f32x4*>(part_dk + (pb * 64 + key) * D + d) = dk[dt][t4] * sm_scale;
       *reinterpret_cast<f32x4*>(part_dv + (pb * 64 + key) * D + d) = dv[dt][t4];
     }
-  part_dks[pb * D + lane] = dks * sel_scale;
+}
+
+// E consecutive bf16 values (E = 4, 8 or 16; 2E-byte aligned) to fp32 and back (RNE)
+template <int E>
+__device__ __forceinline__ void load_row(const bf16* p, float (&v)[E]) {
+  uint32_t u[E / 2];
+  if constexpr (E == 4) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    u[0] = x.x;
+    u[1] = x.y;
+  } else {
+#pragma unroll
+    for (int h = 0; h < E / 8; ++h) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p + 8 * h);
+      u[4 * h] = x.x;
+      u[4 * h + 1] = x.y;
+      u[4 * h + 2] = x.z;
+      u[4 * h + 3] = x.w;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < E / 2; ++j) {
+    v[2 * j] = __uint_as_float(u[j] << 16);
+    v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+  }
+}
+template <int E>
+__device__ __forceinline__ void store_row(bf16* p, const float (&v)[E]) {
+#pragma unroll
+  for (int j = 0; j < E / 4; ++j)
+    *reinterpret_cast<s16x4*>(p + 4 * j) =
+        pack_bf16x4(f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]});
+}
+
+// Token phase: one wave per (b, t, g) row (D = 64).  dQ = sm_scale * the sum of the chunk
+// phase's partials over the token's valid slots in slot order; ds by the stick-breaking chain
+// rule from the edges' dw (fp64, newest slot first); dQs = sel_scale * sum_k ds_k Kslc[c_k].
+template <int G>
+__global__ void __launch_bounds__(256) k_bwd_tok(
+    const bf16* __restrict__ dq_part, const float* __restrict__ dw_in,
+    const int32_t* __restrict__ idx, const float* __restrict__ score,
+    const float* __restrict__ w, const bf16* __restrict__ Kslc, bf16* __restrict__ dQ,
+    bf16* __restrict__ dQs, float* __restrict__ ds_out, int L, int Hkv, int Kn, int nC,
+    int64_t rows, float sm_scale, float sel_scale) {
+  constexpr int D = 64, E = G;  // elements of the row's G x D block per lane
+  const int lane = threadIdx.x % 64;
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // (b * L + t) * Hkv + g
+  if (row >= rows) return;  // whole wave
+  const int g = (int)(row % Hkv);
+  const int64_t bt = row / Hkv;
+  const int64_t b = bt / L;
+  const size_t o = (size_t)row * Kn;
+  int c = -1;
+  float wk = 0.0f, sk = 0.0f, dwk = 0.0f;
+  if (lane < Kn) {
+    c = idx[o + lane];
+    if (c >= 0 && c < nC) {
+      wk = w[o + lane];
+      sk = score[o + lane];
+      dwk = dw_in[o + lane];
+    } else {
+      c = -1;
+    }
+  }
+  const uint64_t vmask = __ballot(c >= 0);
+  // dQ: partials of the valid slots, loads first, then the sum in slot order
+  float acc[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) acc[j] = 0.0f;
+  const bf16* src = dq_part + o * (size_t)(G * D) + (size_t)lane * E;
+  for (int k0 = 0; k0 < Kn; k0 += 8) {
+    float v[8][E];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + u;
+      if (k < Kn && ((vmask >> k) & 1)) {
+        load_row<E>(src + (size_t)k * G * D, v[u]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) v[u][j] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int j = 0; j < E; ++j) acc[j] += v[u][j];
+  }
+#pragma unroll
+  for (int j = 0; j < E; ++j) acc[j] *= sm_scale;
+  store_row<E>(dQ + bt * (int64_t)Hkv * G * D + (size_t)g * G * D + (size_t)lane * E, acc);
+  // ds_k = dw_k w_k (1 - p_k) - p_k * sum_{k' > k} dw_k' w_k'  (fp64, suffix from the last slot)
+  const double dww = (double)dwk * (double)wk;
+  double suffix = 0.0;
+  for (int k2 = Kn - 1; k2 >= 0; --k2) {
+    const double v = __shfl(dww, k2);
+    if (k2 > lane) suffix += v;
+  }
+  float dsk = 0.0f;
+  if (c >= 0) {
+    const double p = sigmoid_d((double)sk);
+    dsk = (float)(dww * (1.0 - p) - p * suffix);
+  }
+  if (lane < Kn) ds_out[o + lane] = dsk;
+  // dQs (one feature per lane), slots in order
+  float a = 0.0f;
+  for (int k = 0; k < Kn; ++k) {
+    const int ck = __shfl(c, k);
+    const float dsv = __shfl(dsk, k);
+    if (ck >= 0) a += dsv * to_f32(Kslc[((b * nC + ck) * Hkv + g) * D + lane]);
+  }
+  dQs[row * D + lane] = from_f32<bf16>(a * sel_scale);
+}
+
+// dKslc partial of one segment of a chunk's selector list (D = 64, one feature per lane):
+// sel_scale * sum over the segment's selectors, in list order, of ds * Qs.
+__global__ void __launch_bounds__(64) k_bwd_dks(
+    const bf16* __restrict__ Qs, const float* __restrict__ ds, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ entries, const int32_t* __restrict__ seg_start,
+    const int32_t* __restrict__ seg_chunk, const int32_t* __restrict__ n_seg,
+    float* __restrict__ part_dks, int L, int Hkv, int Kn, int nC, int seg, int64_t max_seg,
+    float sel_scale) {
+  constexpr int D = 64, SEGMAX = 128;
+  __shared__ int tok_l[SEGMAX];
+  __shared__ float ds_l[SEGMAX];
+  const int64_t sidx = blockIdx.x % max_seg;
+  const int bg = (int)(blockIdx.x / max_seg);
+  if (sidx >= n_seg[bg]) return;
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const int c = seg_chunk[(size_t)bg * max_seg + sidx];
+  const int32_t* off = offsets + (size_t)bg * (nC + 1);
+  const int32_t* ss = seg_start + (size_t)bg * (nC + 1);
+  const int e0 = off[c] + (int)(sidx - ss[c]) * seg;
+  const int ne = min(off[c + 1], e0 + seg) - e0;
+  const int32_t* ent = entries + (size_t)bg * L * Kn + e0;
+  const int lane = threadIdx.x;
+  for (int i = lane; i < ne; i += 64) {
+    const int val = ent[i];
+    const int t = val / Kn, k = val % Kn;
+    tok_l[i] = t;
+    ds_l[i] = ds[((b * L + t) * Hkv + g) * Kn + k];
+  }
+  __syncthreads();
+  float a = 0.0f;
+  int i = 0;
+  for (; i + 8 <= ne; i += 8) {  // eight rows in flight, summed in list order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = to_f32(Qs[((b * L + tok_l[i + u]) * Hkv + g) * D + lane]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a += ds_l[i + u] * v[u];
+  }
+  for (; i < ne; ++i) a += ds_l[i] * to_f32(Qs[((b * L + tok_l[i]) * Hkv + g) * D + lane]);
+  part_dks[((size_t)bg * max_seg + sidx) * D + lane] = a * sel_scale;
 }
 
 bool bwd_mfma_supported(const Dims& d) {
@@ -546,6 +740,61 @@ static void launch_p1_g(const Dims& d, const BwdLayout& lay, const void* Q, cons
 }
 
 
+bool bwd_fused(const Dims& d) { return bwd_mfma_supported(d) && d.D == 64; }
+
+// D = 64: chunk phase, token phase (+ dKslc partials), reduction.
+static hipError_t launch_bwd_fused(const Dims& d, const BwdLayout& lay, const void* Q,
+                                   const void* K, const void* V, const void* Qs,
+                                   const void* Kslc, const int32_t* idx, const float* score,
+                                   const float* w, const void* dO, void* dQ, void* dK, void* dV,
+                                   void* dQs, float* dKslc, bool fold, bool after_fwd, char* ws,
+                                   hipStream_t s) {
+  const int BG = d.B * d.Hkv;
+  const float c2 = (float)(d.sm_scale * 1.4426950408889634);
+  if (d.nC > 0) {
+    dim3 grid((unsigned)(BG * lay.max_seg));
+    auto go = [&](auto kern) {
+      Timed tm(HSA_KERNEL_BWD_P2, s);
+      kern<<<grid, 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)V, w,
+                               (const bf16*)dO, (const float*)(ws + lay.lse),
+                               (const int32_t*)(ws + lay.offsets),
+                               (const int32_t*)(ws + lay.entries),
+                               (const int32_t*)(ws + lay.seg_start),
+                               (const int32_t*)(ws + lay.seg_chunk),
+                               (const int32_t*)(ws + lay.n_seg), (float*)(ws + lay.part_dk),
+                               (float*)(ws + lay.part_dv), (bf16*)(ws + lay.dq_part),
+                               (float*)(ws + lay.dw), d.L, d.Hq, d.Hkv, d.K, d.nC, lay.seg,
+                               lay.max_seg, c2, (float)d.sm_scale);
+    };
+    if (d.G == 4) after_fwd ? go(k_bwd_chunk_mfma<4, true>) : go(k_bwd_chunk_mfma<4, false>);
+    else if (d.G == 8) after_fwd ? go(k_bwd_chunk_mfma<8, true>) : go(k_bwd_chunk_mfma<8, false>);
+    else after_fwd ? go(k_bwd_chunk_mfma<16, true>) : go(k_bwd_chunk_mfma<16, false>);
+  }
+  {
+    Timed tm(HSA_KERNEL_BWD_P1, s);
+    const int64_t rows = (int64_t)d.B * d.L * d.Hkv;
+    auto go = [&](auto kern) {
+      kern<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(
+          (const bf16*)(ws + lay.dq_part), (const float*)(ws + lay.dw), idx, score, w,
+          (const bf16*)Kslc, (bf16*)dQ, (bf16*)dQs, (float*)(ws + lay.ds), d.L, d.Hkv, d.K,
+          d.nC, rows, (float)d.sm_scale, (float)d.sel_scale);
+    };
+    if (d.G == 4) go(k_bwd_tok<4>);
+    else if (d.G == 8) go(k_bwd_tok<8>);
+    else go(k_bwd_tok<16>);
+    if (d.nC > 0)
+      k_bwd_dks<<<dim3((unsigned)(BG * lay.max_seg)), 64, 0, s>>>(
+          (const bf16*)Qs, (const float*)(ws + lay.ds), (const int32_t*)(ws + lay.offsets),
+          (const int32_t*)(ws + lay.entries), (const int32_t*)(ws + lay.seg_start),
+          (const int32_t*)(ws + lay.seg_chunk), (const int32_t*)(ws + lay.n_seg),
+          (float*)(ws + lay.part_dks), d.L, d.Hkv, d.K, d.nC, lay.seg, lay.max_seg,
+          (float)d.sel_scale);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_bwd_reduce(d, lay, dK, dV, dKslc, fold, ws, s);
+}
+
 hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
                            const void* V, const void* Qs, const void* Kslc, const int32_t* idx,
                            const float* score, const float* w, const void* dO, void* dQ,
@@ -553,43 +802,19 @@ hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, c
                            bool after_fwd, char* ws, hipStream_t s) {
   hipError_t e = launch_invidx(d, lay, idx, ws, s);
   if (e != hipSuccess) return e;
-  const int BG = d.B * d.Hkv;
+  if (bwd_fused(d))
+    return launch_bwd_fused(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK, dV, dQs,
+                            dKslc, fold, after_fwd, ws, s);
+  // D = 128: token tiles on the matrix cores, then the vector-ALU chunk phase
   launch_prep_ops(d, K, ws + lay.kt, true, s);
   launch_prep_ops(d, V, ws + lay.vop, false, s);
   if (!after_fwd) {  // else the forward's job lists and key operand are still in place
     launch_prep_ops(d, K, ws + lay.kop, false, s);
     launch_tile_prep(d, idx, ws + lay.prep, s);
   }
-  if (d.D == 64)
-    launch_p1_g<64, 64>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, after_fwd, ws, s);
-  else
-    launch_p1_g<128, 32>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, after_fwd, ws, s);
-  if (d.nC > 0) {
-    if (d.D == 64) {
-      const float c2 = (float)(d.sm_scale * 1.4426950408889634);
-      dim3 grid((unsigned)(BG * lay.max_seg));
-      auto go = [&](auto kern) {
-        Timed tm(HSA_KERNEL_BWD_P2, s);
-        kern<<<grid, 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)V,
-                                 (const bf16*)Qs, w, (const bf16*)dO,
-                                 (const float*)(ws + lay.ds), (const float*)(ws + lay.lse),
-                                 (const float*)(ws + lay.dd), (const int32_t*)(ws + lay.offsets),
-                                 (const int32_t*)(ws + lay.entries),
-                                 (const int32_t*)(ws + lay.seg_start),
-                                 (const int32_t*)(ws + lay.seg_chunk),
-                                 (const int32_t*)(ws + lay.n_seg), (float*)(ws + lay.part_dk),
-                                 (float*)(ws + lay.part_dv), (float*)(ws + lay.part_dks), d.L,
-                                 d.Hq, d.Hkv, d.K, d.nC, lay.seg, lay.max_seg, c2,
-                                 (float)d.sm_scale, (float)d.sel_scale);
-      };
-      if (d.G == 4) go(k_bwd_p2_mfma<4>);
-      else if (d.G == 8) go(k_bwd_p2_mfma<8>);
-      else go(k_bwd_p2_mfma<16>);
-    } else {
-      e = launch_bwd_generic_p2(d, lay, Q, K, V, Qs, w, dO, ws, s);
-      if (e != hipSuccess) return e;
-    }
-  }
+  launch_p1_g<128, 32>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, after_fwd, ws, s);
+  e = launch_bwd_generic_p2(d, lay, Q, K, V, Qs, w, dO, ws, s);
+  if (e != hipSuccess) return e;
   return launch_bwd_reduce(d, lay, dK, dV, dKslc, fold, ws, s);
 }
 

@@ -49,7 +49,7 @@ struct BwdLayout {
   int seg;          // entries per backward-phase-2 segment
   int64_t max_seg;  // segment capacity per (b, g)
   size_t ds, dw, tile_counts, tile_base, offsets, entries, seg_start, seg_chunk, n_seg,
-      part_dk, part_dv, part_dks, kt, kop, vop, prep, lse, dd, total;
+      part_dk, part_dv, part_dks, kt, kop, vop, prep, lse, dd, dq_part, total;
 };
 BwdLayout bwd_layout(const Dims& d);
 
@@ -102,6 +102,9 @@ int tile_tokens(const Dims& d);
 size_t tile_prep_bytes(const Dims& d);
 void launch_tile_prep(const Dims& d, const int32_t* idx, void* prep, hipStream_t s);
 bool bwd_mfma_supported(const Dims& d);
+// D = 64 on the matrix cores: the chunk phase also yields per-edge dQ partials, which a
+// token phase sums (no token-tile phase).
+bool bwd_fused(const Dims& d);
 // after_fwd: ws still holds the forward's state for this problem, idx and K (see FwdState).
 hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
                            const void* V, const void* Qs, const void* Kslc, const int32_t* idx,

@@ -146,8 +146,8 @@ hsa_status_t hsa_fwd(const hsa_problem_t* p, const void* Q, const void* K, const
  * same workspace (sized for hsa_bwd, which is at least the forward's size) and has not
  * touched it since.  The forward leaves at the start of its workspace the per-tile job lists,
  * the key rows in matrix-core operand order and every (token, head, slot)'s softmax
- * normaliser; the backward then skips rebuilding them and takes its probabilities from the
- * normaliser.  The results equal those without the flag up to fp32 rounding.  When the
+ * normaliser; the backward then skips rebuilding those it uses and takes its probabilities
+ * from the normaliser.  The results equal those without the flag up to fp32 rounding.  When the
  * problem uses the plain kernels (fp32, HSA_FLAG_GENERIC, or shapes outside the matrix-core
  * kernels) the flag has no effect.  Passing it without that forward call gives undefined
  * results. */
@@ -184,9 +184,13 @@ typedef enum {
   HSA_KERNEL_PREP_OPS = 3,   /* per-chunk operand copies of the matrix-core kernels */
   HSA_KERNEL_FWD = 4,        /* token-level attention fused with the chunk weights */
   HSA_KERNEL_INVIDX = 5,     /* chunk -> (token, slot) inverse index (count, scan, scatter) */
-  HSA_KERNEL_BWD_P1 = 6,     /* backward phase 1: per token dQ, dw, ds, dQs */
-  HSA_KERNEL_BWD_P2 = 7,     /* backward phase 2: per chunk dK, dV, dKslc partials */
-  HSA_KERNEL_BWD_REDUCE = 8, /* backward: fixed-order reduction of the phase-2 partials */
+  HSA_KERNEL_BWD_P1 = 6,     /* backward, token phase: per token dQ, ds, dQs (bf16 D=64: the sum
+                                of the chunk phase's per-edge dQ partials, then the dKslc
+                                partials per segment; otherwise token tiles that also form
+                                dw) */
+  HSA_KERNEL_BWD_P2 = 7,     /* backward, chunk phase: per chunk segment dK, dV partials (bf16
+                                D=64: also the per-edge dQ partials and dw; runs first) */
+  HSA_KERNEL_BWD_REDUCE = 8, /* backward: fixed-order reduction of the segment partials */
   HSA_KERNEL_DECODE_SCAN = 9,    /* decode: scan of the chunk-key table, per-block top-K */
   HSA_KERNEL_DECODE_ATTEND = 10, /* decode: merge, weights and attention over the kept chunks */
   HSA_KERNEL_COUNT = 11
