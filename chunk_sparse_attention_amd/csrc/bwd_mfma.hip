@@ -42,6 +42,11 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c) {
 __device__ __forceinline__ s16x4 pack_bf16x4(f32x4 v) {
   return __builtin_bit_cast(s16x4, __builtin_convertvector(v, bf16x4));
 }
+__device__ __forceinline__ bf16x8 cat_bf16x8(s16x4 lo, s16x4 hi) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
 // gfx950 transposing LDS read of four 16-bit elements: in each group of 16 lanes, lane j
 // receives element j%4 of the 8-byte word that lane 4*i + j/4 addresses, for i = 0..3.
 // With lane m of group `blk` addressing row 4*blk + m/4, column c0 + 4*(m%4) of a row-major
@@ -517,16 +522,21 @@ k_bwd_chunk_mfma(
       }
     }
     __syncthreads();  // sdl is read transposed below
-    // dQ^T (rows d, columns the 16 query rows) = K_c^T dS^T over the chunk's keys
+    // dQ^T (rows d, columns the 16 query rows) = K_c^T dS^T over the chunk's keys, 32 keys
+    // per product: lane block blk takes keys 32*kk + 4*blk + i and 32*kk + 16 + 4*blk + i in
+    // both operands
     f32x4 dq[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const s16x4 dsT = lds_read_tr4(&sdl[16 * kb + trow][tcol]);
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 dsT = cat_bf16x8(lds_read_tr4(&sdl[32 * kk + trow][tcol]),
+                                    lds_read_tr4(&sdl[32 * kk + 16 + trow][tcol]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        dq[dt] = mfma_16x16x16(lds_read_tr4(&kl[16 * kb + trow][16 * dt + tcol]), dsT, dq[dt]);
+        dq[dt] = mfma_16x16x32(cat_bf16x8(lds_read_tr4(&kl[32 * kk + trow][16 * dt + tcol]),
+                                          lds_read_tr4(&kl[32 * kk + 16 + trow][16 * dt + tcol])),
+                               dsT, dq[dt]);
     }
     if (qs_sel < n_here) {  // lane column = query row col: its edge's partial at d = 16*dt + 4*blk
       const int e = ej + qs_sel;
@@ -583,6 +593,8 @@ __device__ __forceinline__ void store_row(bf16* p, const float (&v)[E]) {
 // Token phase: one wave per (b, t, g) row (D = 64).  dQ = sm_scale * the sum of the chunk
 // phase's partials over the token's valid slots in slot order; ds by the stick-breaking chain
 // rule from the edges' dw (fp64, newest slot first); dQs = sel_scale * sum_k ds_k Kslc[c_k].
+// The slot data and every slot's partial are loaded together: a slot that is not valid has no
+// partial or dw (its workspace bytes are stale) and is masked out by selection.
 template <int G>
 __global__ void __launch_bounds__(256) k_bwd_tok(
     const bf16* __restrict__ dq_part, const float* __restrict__ dw_in,
@@ -602,59 +614,71 @@ __global__ void __launch_bounds__(256) k_bwd_tok(
   float wk = 0.0f, sk = 0.0f, dwk = 0.0f;
   if (lane < Kn) {
     c = idx[o + lane];
-    if (c >= 0 && c < nC) {
-      wk = w[o + lane];
-      sk = score[o + lane];
-      dwk = dw_in[o + lane];
-    } else {
-      c = -1;
-    }
+    wk = w[o + lane];
+    sk = score[o + lane];
+    dwk = dw_in[o + lane];
   }
-  const uint64_t vmask = __ballot(c >= 0);
-  // dQ: partials of the valid slots, loads first, then the sum in slot order
+  const bool valid = c >= 0 && c < nC;
+  const bf16* src = dq_part + o * (size_t)(G * D) + (size_t)lane * E;
   float acc[E];
 #pragma unroll
   for (int j = 0; j < E; ++j) acc[j] = 0.0f;
-  const bf16* src = dq_part + o * (size_t)(G * D) + (size_t)lane * E;
+  const uint64_t vmask = __ballot(valid);
   for (int k0 = 0; k0 < Kn; k0 += 8) {
     float v[8][E];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int k = k0 + u;
-      if (k < Kn && ((vmask >> k) & 1)) {
-        load_row<E>(src + (size_t)k * G * D, v[u]);
+      if (k0 + u < Kn) {
+        load_row<E>(src + (size_t)(k0 + u) * G * D, v[u]);
       } else {
 #pragma unroll
         for (int j = 0; j < E; ++j) v[u][j] = 0.0f;
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 8; ++u) {
+      const bool on = k0 + u < Kn && ((vmask >> (k0 + u)) & 1);
 #pragma unroll
-      for (int j = 0; j < E; ++j) acc[j] += v[u][j];
+      for (int j = 0; j < E; ++j) acc[j] += on ? v[u][j] : 0.0f;
+    }
   }
 #pragma unroll
   for (int j = 0; j < E; ++j) acc[j] *= sm_scale;
   store_row<E>(dQ + bt * (int64_t)Hkv * G * D + (size_t)g * G * D + (size_t)lane * E, acc);
   // ds_k = dw_k w_k (1 - p_k) - p_k * sum_{k' > k} dw_k' w_k'  (fp64, suffix from the last slot)
-  const double dww = (double)dwk * (double)wk;
+  const double dww = valid ? (double)dwk * (double)wk : 0.0;
+  const int2 dwi = __builtin_bit_cast(int2, dww);
   double suffix = 0.0;
   for (int k2 = Kn - 1; k2 >= 0; --k2) {
-    const double v = __shfl(dww, k2);
-    if (k2 > lane) suffix += v;
+    const int2 vi = make_int2(__builtin_amdgcn_readlane(dwi.x, k2),
+                              __builtin_amdgcn_readlane(dwi.y, k2));
+    if (k2 > lane) suffix += __builtin_bit_cast(double, vi);
   }
   float dsk = 0.0f;
-  if (c >= 0) {
+  if (valid) {
     const double p = sigmoid_d((double)sk);
     dsk = (float)(dww * (1.0 - p) - p * suffix);
   }
   if (lane < Kn) ds_out[o + lane] = dsk;
-  // dQs (one feature per lane), slots in order
+  // dQs (one feature per lane), slots in order; the rows of the valid slots load together
   float a = 0.0f;
-  for (int k = 0; k < Kn; ++k) {
-    const int ck = __shfl(c, k);
-    const float dsv = __shfl(dsk, k);
-    if (ck >= 0) a += dsv * to_f32(Kslc[((b * nC + ck) * Hkv + g) * D + lane]);
+  if (nC > 0) {
+    const int cv = valid ? c : 0;
+    for (int k0 = 0; k0 < Kn; k0 += 8) {
+      float kv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int ck = __builtin_amdgcn_readlane(cv, min(k0 + u, Kn - 1));
+        kv[u] = to_f32(Kslc[((b * nC + ck) * Hkv + g) * D + lane]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u;
+        const float dsv = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dsk), min(k, Kn - 1)));
+        if (k < Kn && ((vmask >> k) & 1)) a += dsv * kv[u];
+      }
+    }
   }
   dQs[row * D + lane] = from_f32<bf16>(a * sel_scale);
 }
@@ -691,13 +715,13 @@ __global__ void __launch_bounds__(64) k_bwd_dks(
   __syncthreads();
   float a = 0.0f;
   int i = 0;
-  for (; i + 8 <= ne; i += 8) {  // eight rows in flight, summed in list order
-    float v[8];
+  for (; i + 16 <= ne; i += 16) {  // sixteen rows in flight, summed in list order
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 16; ++u)
       v[u] = to_f32(Qs[((b * L + tok_l[i + u]) * Hkv + g) * D + lane]);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a += ds_l[i + u] * v[u];
+    for (int u = 0; u < 16; ++u) a += ds_l[i + u] * v[u];
   }
   for (; i < ne; ++i) a += ds_l[i] * to_f32(Qs[((b * L + tok_l[i]) * Hkv + g) * D + lane]);
   part_dks[((size_t)bg * max_seg + sidx) * D + lane] = a * sel_scale;
