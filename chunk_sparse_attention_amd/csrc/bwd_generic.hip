@@ -20,7 +20,7 @@ BwdLayout bwd_layout(const Dims& d) {
   while ((d.L + tt - 1) / tt > 256) tt *= 2;
   l.tile_tokens = tt;
   l.n_tiles = (d.L + tt - 1) / tt;
-  l.seg = 128;
+  l.seg = bwd_fused(d) ? kBwdSeg : 128;
   const int64_t bg = (int64_t)d.B * d.Hkv;
   const int64_t E = (int64_t)d.L * d.K;  // entry capacity per (b, g)
   l.max_seg = (E + l.seg - 1) / l.seg + d.nC;

@@ -42,6 +42,14 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c) {
 __device__ __forceinline__ s16x4 pack_bf16x4(f32x4 v) {
   return __builtin_bit_cast(s16x4, __builtin_convertvector(v, bf16x4));
 }
+// Orders this wave's earlier LDS accesses before its later ones that touch other lanes' data
+// (the LDS serves one wave's instructions in order; the wait and the compiler barrier keep
+// both the hardware and the compiler from moving accesses across this point).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ bf16x8 cat_bf16x8(s16x4 lo, s16x4 hi) {
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -350,7 +358,7 @@ __global__ void __launch_bounds__(512) k_bwd_p1_tile(
 // unscaled) and dw are stored once; the segment's dK/dV are fp32 partials that a fixed-order
 // reduction sums per chunk.
 template <int G, bool HL>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
 k_bwd_chunk_mfma(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const float* __restrict__ w, const bf16* __restrict__ dO, const float* __restrict__ lse_in,
@@ -359,37 +367,42 @@ k_bwd_chunk_mfma(
     const int32_t* __restrict__ n_seg, float* __restrict__ part_dk, float* __restrict__ part_dv,
     bf16* __restrict__ dq_part, float* __restrict__ dw_out, int L, int Hq, int Hkv, int Kn,
     int nC, int seg, int64_t max_seg, float c2, float sm_scale) {
-  constexpr int D = 64, TPJ = 16 / G, KS = D / 32, DT = D / 16;
-  constexpr int SEGMAX = 128;
-  __shared__ __attribute__((aligned(16))) uint16_t kl[64][D + 8];
-  __shared__ __attribute__((aligned(16))) uint16_t vl[64][D + 8];
-  __shared__ __attribute__((aligned(16))) uint16_t ql[16][D + 8];
-  __shared__ __attribute__((aligned(16))) uint16_t dl[16][D + 8];
-  __shared__ __attribute__((aligned(16))) uint16_t sdl[64][16];  // dS^T of the job
-  __shared__ int tok_l[SEGMAX], k_l[SEGMAX];
-  __shared__ float w_l[SEGMAX];
+  // two waves share the segment's chunk in LDS and take alternate jobs; their dK/dV sums
+  // meet in LDS at the end
+  constexpr int D = 64, TPJ = 16 / G, KS = D / 32, DT = D / 16, NW = 2, NT = 64 * NW;
+  constexpr int KROW = D + 8, WREGION = 2 * 16 * KROW + 64 * 16;
+  __shared__ __attribute__((aligned(16))) uint16_t sm[2 * 64 * KROW + NW * WREGION];
+  __shared__ int tok_l[kBwdSeg], k_l[kBwdSeg];
+  __shared__ float w_l[kBwdSeg];
   const int64_t sidx = blockIdx.x % max_seg;
   const int bg = (int)(blockIdx.x / max_seg);
-  if (sidx >= n_seg[bg]) return;  // whole wave
+  if (sidx >= n_seg[bg]) return;  // whole block
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const int c = seg_chunk[(size_t)bg * max_seg + sidx];
   const int32_t* off = offsets + (size_t)bg * (nC + 1);
   const int32_t* ss = seg_start + (size_t)bg * (nC + 1);
   const int e0 = off[c] + (int)(sidx - ss[c]) * seg;
-  const int ne = min(off[c + 1], e0 + seg) - e0;  // <= seg <= SEGMAX
+  const int ne = min(off[c + 1], e0 + seg) - e0;  // <= seg = kBwdSeg
   const int32_t* ent = entries + (size_t)bg * L * Kn + e0;
-  const int lane = threadIdx.x, col = lane % 16, blk = lane / 16;
+  const int tid = threadIdx.x, lane = tid % 64, col = lane % 16, blk = lane / 16;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
+  uint16_t (*kl)[KROW] = reinterpret_cast<uint16_t (*)[KROW]>(sm);
+  uint16_t (*vl)[KROW] = reinterpret_cast<uint16_t (*)[KROW]>(sm + 64 * KROW);
+  uint16_t* wreg = sm + 2 * 64 * KROW + wv * WREGION;  // this wave's job staging
+  uint16_t (*ql)[KROW] = reinterpret_cast<uint16_t (*)[KROW]>(wreg);
+  uint16_t (*dl)[KROW] = reinterpret_cast<uint16_t (*)[KROW]>(wreg + 16 * KROW);
+  uint16_t (*sdl)[16] = reinterpret_cast<uint16_t (*)[16]>(wreg + 32 * KROW);  // dS^T
   const size_t kvrow = (size_t)Hkv * D;
   const size_t cb = ((b * L + (size_t)c * 64) * Hkv + g) * D;
-  for (int i = lane; i < ne; i += 64) {
+  for (int i = tid; i < ne; i += NT) {
     const int val = ent[i];
     const int t = val / Kn, k = val % Kn;
     tok_l[i] = t;
     k_l[i] = k;
     w_l[i] = w[((b * L + t) * Hkv + g) * Kn + k];
   }
-  for (int i = lane; i < 64 * (D / 8); i += 64) {
+  for (int i = tid; i < 64 * (D / 8); i += NT) {
     const int key = i / (D / 8), d = (i % (D / 8)) * 8;
     *reinterpret_cast<uint4*>(&kl[key][d]) = *reinterpret_cast<const uint4*>(K + cb + key * kvrow + d);
     *reinterpret_cast<uint4*>(&vl[key][d]) = *reinterpret_cast<const uint4*>(V + cb + key * kvrow + d);
@@ -426,8 +439,8 @@ k_bwd_chunk_mfma(
   };
   bf16x8 qn[KS], dn[KS];
   float len[4] = {0.f, 0.f, 0.f, 0.f};
-  if (ne > 0) load_rows(0, qn, dn, len);
-  for (int ej = 0; ej < ne; ej += TPJ) {
+  if (wv * TPJ < ne) load_rows(wv * TPJ, qn, dn, len);
+  for (int ej = wv * TPJ; ej < ne; ej += NW * TPJ) {
     const int n_here = min(TPJ, ne - ej);
     bf16x8 qa[KS], da[KS];
     float lse[4];
@@ -438,13 +451,13 @@ k_bwd_chunk_mfma(
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) lse[i] = len[i];
-    if (ej + TPJ < ne) load_rows(ej + TPJ, qn, dn, len);
+    if (ej + NW * TPJ < ne) load_rows(ej + NW * TPJ, qn, dn, len);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       *reinterpret_cast<bf16x8*>(&ql[col][32 * ks + 8 * blk]) = qa[ks];
       *reinterpret_cast<bf16x8*>(&dl[col][32 * ks + 8 * blk]) = da[ks];
     }
-    __syncthreads();  // ql/dl are read transposed below
+    wave_lds_sync();  // ql/dl are read transposed below
     // S = Q K_c^T, dP = dO V_c^T (rows: the 16 query rows; columns: keys 16*t4 + col)
     f32x4 sa[4], pa[4];
 #pragma unroll
@@ -521,7 +534,7 @@ k_bwd_chunk_mfma(
         dk[dt][t4] = mfma_16x16x16(qT[dt], dsb, dk[dt][t4]);
       }
     }
-    __syncthreads();  // sdl is read transposed below
+    wave_lds_sync();  // sdl is read transposed below
     // dQ^T (rows d, columns the 16 query rows) = K_c^T dS^T over the chunk's keys, 32 keys
     // per product: lane block blk takes keys 32*kk + 4*blk + i and 32*kk + 16 + 4*blk + i in
     // both operands
@@ -545,17 +558,47 @@ k_bwd_chunk_mfma(
       for (int dt = 0; dt < DT; ++dt)
         *reinterpret_cast<s16x4*>(dst + 16 * dt + 4 * blk) = pack_bf16x4(dq[dt]);
     }
-    __syncthreads();  // ql/dl/sdl reuse by the next job
+    wave_lds_sync();  // ql/dl/sdl reuse by the next job
   }
+  // wave 1's sums meet wave 0's in LDS (dK, then dV); wave 0 stores the segment's partials
+  __syncthreads();  // every job is done: the chunk and staging areas are free
+  f32x4* xs = reinterpret_cast<f32x4*>(sm);  // 16 x 64 lanes x 16 bytes
   const size_t pb = (size_t)bg * max_seg + sidx;
+  if (wv == 1) {
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const int key = 16 * t4 + col, d = 16 * dt + 4 * blk;
-      *reinterpret_cast<f32x4*>(part_dk + (pb * 64 + key) * D + d) = dk[dt][t4] * sm_scale;
-      *reinterpret_cast<f32x4*>(part_dv + (pb * 64 + key) * D + d) = dv[dt][t4];
-    }
+      for (int t4 = 0; t4 < 4; ++t4) xs[(dt * 4 + t4) * 64 + lane] = dk[dt][t4];
+  }
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int key = 16 * t4 + col, d = 16 * dt + 4 * blk;
+        *reinterpret_cast<f32x4*>(part_dk + (pb * 64 + key) * D + d) =
+            (dk[dt][t4] + xs[(dt * 4 + t4) * 64 + lane]) * sm_scale;
+      }
+  }
+  __syncthreads();
+  if (wv == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) xs[(dt * 4 + t4) * 64 + lane] = dv[dt][t4];
+  }
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int key = 16 * t4 + col, d = 16 * dt + 4 * blk;
+        *reinterpret_cast<f32x4*>(part_dv + (pb * 64 + key) * D + d) =
+            dv[dt][t4] + xs[(dt * 4 + t4) * 64 + lane];
+      }
+  }
 }
 
 // E consecutive bf16 values (E = 4, 8 or 16; 2E-byte aligned) to fp32 and back (RNE)
@@ -691,9 +734,9 @@ __global__ void __launch_bounds__(64) k_bwd_dks(
     const int32_t* __restrict__ seg_chunk, const int32_t* __restrict__ n_seg,
     float* __restrict__ part_dks, int L, int Hkv, int Kn, int nC, int seg, int64_t max_seg,
     float sel_scale) {
-  constexpr int D = 64, SEGMAX = 128;
-  __shared__ int tok_l[SEGMAX];
-  __shared__ float ds_l[SEGMAX];
+  constexpr int D = 64;
+  __shared__ int tok_l[kBwdSeg];
+  __shared__ float ds_l[kBwdSeg];
   const int64_t sidx = blockIdx.x % max_seg;
   const int bg = (int)(blockIdx.x / max_seg);
   if (sidx >= n_seg[bg]) return;
@@ -779,7 +822,7 @@ static hipError_t launch_bwd_fused(const Dims& d, const BwdLayout& lay, const vo
     dim3 grid((unsigned)(BG * lay.max_seg));
     auto go = [&](auto kern) {
       Timed tm(HSA_KERNEL_BWD_P2, s);
-      kern<<<grid, 64, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)V, w,
+      kern<<<grid, 128, 0, s>>>((const bf16*)Q, (const bf16*)K, (const bf16*)V, w,
                                (const bf16*)dO, (const float*)(ws + lay.lse),
                                (const int32_t*)(ws + lay.offsets),
                                (const int32_t*)(ws + lay.entries),

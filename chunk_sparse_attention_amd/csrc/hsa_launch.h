@@ -43,6 +43,8 @@ struct FwdState {
 FwdState fwd_state(const Dims& d);
 
 // Backward workspace carve-up (byte offsets into the caller's workspace).
+// Entries per chunk segment of the fused backward (two waves of 16-row jobs per segment).
+constexpr int kBwdSeg = 256;
 struct BwdLayout {
   int tile_tokens;  // tokens per tile of the inverse-index build
   int n_tiles;      // tiles per (b, g)
