@@ -601,10 +601,10 @@ k_bwd_chunk_mfma(
   }
 }
 
-// E consecutive bf16 values (E = 4, 8 or 16; 2E-byte aligned) to fp32 and back (RNE)
+// E consecutive bf16 values (E = 4, 8 or 16; 2E-byte aligned): raw load, fp32 accumulation,
+// and the RNE store of E fp32 values
 template <int E>
-__device__ __forceinline__ void load_row(const bf16* p, float (&v)[E]) {
-  uint32_t u[E / 2];
+__device__ __forceinline__ void load_raw(const bf16* p, uint32_t (&u)[E / 2]) {
   if constexpr (E == 4) {
     const uint2 x = *reinterpret_cast<const uint2*>(p);
     u[0] = x.x;
@@ -619,10 +619,13 @@ __device__ __forceinline__ void load_row(const bf16* p, float (&v)[E]) {
       u[4 * h + 3] = x.w;
     }
   }
+}
+template <int E>
+__device__ __forceinline__ void add_raw(float (&acc)[E], const uint32_t (&u)[E / 2], bool on) {
 #pragma unroll
   for (int j = 0; j < E / 2; ++j) {
-    v[2 * j] = __uint_as_float(u[j] << 16);
-    v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+    acc[2 * j] += on ? __uint_as_float(u[j] << 16) : 0.0f;
+    acc[2 * j + 1] += on ? __uint_as_float(u[j] & 0xffff0000u) : 0.0f;
   }
 }
 template <int E>
@@ -668,22 +671,18 @@ __global__ void __launch_bounds__(256) k_bwd_tok(
   for (int j = 0; j < E; ++j) acc[j] = 0.0f;
   const uint64_t vmask = __ballot(valid);
   for (int k0 = 0; k0 < Kn; k0 += 8) {
-    float v[8][E];
+    uint32_t v[8][E / 2];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (k0 + u < Kn) {
-        load_row<E>(src + (size_t)(k0 + u) * G * D, v[u]);
+        load_raw<E>(src + (size_t)(k0 + u) * G * D, v[u]);
       } else {
 #pragma unroll
-        for (int j = 0; j < E; ++j) v[u][j] = 0.0f;
+        for (int j = 0; j < E / 2; ++j) v[u][j] = 0u;
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool on = k0 + u < Kn && ((vmask >> (k0 + u)) & 1);
-#pragma unroll
-      for (int j = 0; j < E; ++j) acc[j] += on ? v[u][j] : 0.0f;
-    }
+    for (int u = 0; u < 8; ++u) add_raw<E>(acc, v[u], k0 + u < Kn && ((vmask >> (k0 + u)) & 1));
   }
 #pragma unroll
   for (int j = 0; j < E; ++j) acc[j] *= sm_scale;

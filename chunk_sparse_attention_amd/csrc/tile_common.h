@@ -12,6 +12,9 @@
 namespace hsa {
 
 constexpr uint32_t kNoEdge = 0xffffffffu;
+// Tokens per scheduling piece (see build_jobs); a piece of one job when equal to the jobs'
+// tokens.
+constexpr int kPieceTokens = 2;
 
 // Edge key: chunk in the high 16 bits, then token-in-tile (6 bits) and slot (4 bits), so an
 // ascending sort groups edges by chunk and keeps token order inside a chunk.
@@ -115,7 +118,7 @@ __device__ void build_jobs(const uint32_t* keys, int N, int tpj, int* rs, int* t
       const int c = edge_chunk(keys[i]);
       while (cnt < tpj && i + cnt < nv && edge_chunk(keys[i + cnt]) == c) ++cnt;
       const int j = jf[i] - 1;
-      const int pj = 4 / tpj;                       // jobs per piece
+      const int pj = max(1, kPieceTokens / tpj);    // jobs per piece
       const int first = jf[rs[i]] - 1;              // first job of the chunk's run
       jobs[j] = (uint32_t)i | ((uint32_t)cnt << 16);
       phead[j] = first + (j - first) / pj * pj;
