@@ -90,6 +90,9 @@ def kernel_counts(wl, n_slots: int, fused: bool = True) -> dict:
         "bwd_reduce": dict(bytes=2 * kv + 2 * kslc, flops=0),
     }
     if fused:
+        # chunk-major forward: Q, K, V and the slots in (the token phase writes O)
+        c["fwd"] = dict(bytes=q + 2 * kv + 2 * slot, flops=4 * S * D * eg)
+        c["fwd_token"] = dict(bytes=q + slot, flops=0)
         # token phase: dQ and dQs out, the slots and Kslc rows in; dKslc partials read Qs
         c["bwd_p1"] = dict(bytes=q + 2 * kv + kslc + 3 * slot, flops=0)
         # chunk phase: Q, dO, K, V and the weights in; S, dP, dV, dK and dQ products
@@ -122,14 +125,17 @@ def roofline(name: str, counts: dict, avg_ms: float, traffic) -> dict:
 
 
 # kernel function name -> kernel class of the launch timer; the first matching prefix wins.
-# A class launch is one host call: the inverse index runs three kernels per launch, counted
-# by its scatter.
+# A class launch is one host call: the inverse index runs three kernels per launch and the
+# fused backward's token phase two; the others are one kernel each.
 KERNEL_CLASS_OF = (("k_bwd_p2_reduce", "bwd_reduce"), ("k_bwd_p2", "bwd_p2"),
-                   ("k_bwd_p1", "bwd_p1"), ("k_inv_", "invidx"), ("k_tile_prep", "tile_prep"),
-                   ("k_prep_ops", "prep_ops"), ("k_fwd_", "fwd"), ("k_select", "select"),
+                   ("k_bwd_chunk", "bwd_p2"), ("k_bwd_p1", "bwd_p1"), ("k_bwd_tok", "bwd_p1"),
+                   ("k_bwd_dks", "bwd_p1"), ("k_inv_", "invidx"), ("k_tile_prep", "tile_prep"),
+                   ("k_prep_ops", "prep_ops"), ("k_fwd_tok", "fwd_token"), ("k_fwd_", "fwd"),
+                   ("k_select", "select"),
                    ("k_pool", "pool"), ("k_dec_scan", "decode_scan"),
                    ("k_dec_attend", "decode_attend"))
-LAUNCH_KERNEL = {"invidx": "k_inv_scatter"}
+# kernels that run inside another kernel's class launch (not counted as launches)
+SECONDARY_KERNELS = {"k_inv_count", "k_inv_scan", "k_bwd_dks"}
 
 
 def kernel_class(kernel_name: str):
@@ -196,7 +202,7 @@ def summarize_counters(cdir: str, workload: str, copy_mib: int) -> int:
         a = acc[cls]
         a["fetch"] += sum(fv) * fs
         a["write"] += sum(vals["WRITE_SIZE"].get(name, [])) * wsc
-        if LAUNCH_KERNEL.get(cls, fn) == fn:
+        if fn not in SECONDARY_KERNELS:
             a["launches"] += len(fv)
         a["names"].add(re.sub(r"\(.*", "", name).replace("void ", "").strip())
     out = {"source_sha": source_sha(), "workload": workload,

@@ -26,7 +26,7 @@ EXPORTS = ("hsa_status_string", "hsa_last_error", "hsa_version", "hsa_workspace_
            "hsa_timer_read")
 # hsa_kernel_t: kernel classes of the timing aid
 KERNEL_CLASSES = ("pool", "select", "tile_prep", "prep_ops", "fwd", "invidx", "bwd_p1", "bwd_p2",
-                  "bwd_reduce", "decode_scan", "decode_attend")
+                  "bwd_reduce", "decode_scan", "decode_attend", "fwd_token")
 
 
 class Problem(ctypes.Structure):

@@ -14,16 +14,33 @@ namespace hsa {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-BwdLayout bwd_layout(const Dims& d) {
-  BwdLayout l{};
+IndexLayout index_layout(const Dims& d, size_t& o) {
+  IndexLayout x{};
   int tt = 256;
   while ((d.L + tt - 1) / tt > 256) tt *= 2;
-  l.tile_tokens = tt;
-  l.n_tiles = (d.L + tt - 1) / tt;
-  l.seg = bwd_fused(d) ? kBwdSeg : 128;
+  x.tile_tokens = tt;
+  x.n_tiles = (d.L + tt - 1) / tt;
+  x.seg = bwd_fused(d) ? kBwdSeg : 128;
   const int64_t bg = (int64_t)d.B * d.Hkv;
   const int64_t E = (int64_t)d.L * d.K;  // entry capacity per (b, g)
-  l.max_seg = (E + l.seg - 1) / l.seg + d.nC;
+  x.max_seg = (E + x.seg - 1) / x.seg + d.nC;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  x.tile_counts = take(sizeof(int32_t) * bg * x.n_tiles * d.nC);
+  x.tile_base = take(sizeof(int32_t) * bg * x.n_tiles * d.nC);
+  x.offsets = take(sizeof(int32_t) * bg * (d.nC + 1));
+  x.entries = take(sizeof(int32_t) * bg * E);
+  x.seg_start = take(sizeof(int32_t) * bg * (d.nC + 1));
+  x.seg_chunk = take(sizeof(int32_t) * bg * x.max_seg);
+  x.n_seg = take(sizeof(int32_t) * bg);
+  return x;
+}
+
+BwdLayout bwd_layout(const Dims& d) {
+  BwdLayout l{};
   const FwdState st = fwd_state(d);  // the forward's state comes first
   l.prep = st.prep;
   l.kop = st.kop;
@@ -34,21 +51,20 @@ BwdLayout bwd_layout(const Dims& d) {
     o = align256(o + bytes);
     return at;
   };
+  const bool fused = bwd_fused(d), chunked = fwd_chunked(d);
+  // the chunk-major forward builds the index in its state; otherwise it follows the state
+  static_cast<IndexLayout&>(l) = chunked ? st.ix : index_layout(d, o);
+  const int64_t bg = (int64_t)d.B * d.Hkv;
+  const int64_t E = (int64_t)d.L * d.K;
   l.ds = take(sizeof(float) * bg * E);
   l.dw = take(sizeof(float) * bg * E);
-  l.tile_counts = take(sizeof(int32_t) * bg * l.n_tiles * d.nC);
-  l.tile_base = take(sizeof(int32_t) * bg * l.n_tiles * d.nC);
-  l.offsets = take(sizeof(int32_t) * bg * (d.nC + 1));
-  l.entries = take(sizeof(int32_t) * bg * E);
-  l.seg_start = take(sizeof(int32_t) * bg * (d.nC + 1));
-  l.seg_chunk = take(sizeof(int32_t) * bg * l.max_seg);
-  l.n_seg = take(sizeof(int32_t) * bg);
   l.part_dk = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
   l.part_dv = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
   l.part_dks = take(sizeof(float) * bg * l.max_seg * d.D);
-  if (bwd_fused(d)) {
-    // per (token, group, slot, head): the edge's dQ contribution (bf16, D values)
-    l.dq_part = take(sizeof(uint16_t) * bg * E * d.G * d.D);
+  if (fused) {
+    // per (token, group, slot, head): the edge's dQ contribution (the chunk-major forward's
+    // partials' buffer, free once the forward has summed them)
+    l.dq_part = chunked ? st.part : take(sizeof(uint16_t) * bg * E * d.G * d.D);
   } else {
     l.kt = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
     l.vop = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
@@ -201,7 +217,7 @@ __global__ void __launch_bounds__(64) k_inv_scatter(const int32_t* __restrict__ 
   }
 }
 
-hipError_t launch_invidx(const Dims& d, const BwdLayout& lay, const int32_t* idx, char* ws,
+hipError_t launch_invidx(const Dims& d, const IndexLayout& lay, const int32_t* idx, char* ws,
                          hipStream_t s) {
   const int bg = d.B * d.Hkv;
   if (bg == 0 || d.nC == 0) return hipSuccess;

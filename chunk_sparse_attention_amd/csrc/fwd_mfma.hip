@@ -266,6 +266,202 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
   }
 }
 
+// ---- chunk-major forward (D = 64) ----------------------------------------------------------
+// One block of two waves per segment of a chunk's selector list (the chunk -> (token, slot)
+// index); the chunk's keys and values sit in LDS and the waves take alternate jobs of 16
+// query rows (16/G selectors x G heads, row q = selector * G + head):
+//   S = Q K_c^T                                  (MFMA; lane: key column, four query rows)
+//   softmax-off-by-one over the chunk's 64 keys  (row statistics across 16 lanes)
+//   P~ = w P, packed to bf16, to LDS as P~^T
+//   O_k^T = V_c^T P~^T                           (MFMA, both operands by transposing reads)
+// Each selection edge lies in exactly one segment: its weighted output (bf16, G x D) and the
+// normaliser of each of its heads are stored once; a token phase sums the edges of a token.
+template <int G, int NW>
+__global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const float* __restrict__ w, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ entries, const int32_t* __restrict__ seg_start,
+    const int32_t* __restrict__ seg_chunk, const int32_t* __restrict__ n_seg,
+    bf16* __restrict__ o_part, float* __restrict__ lse_out, int L, int Hq, int Hkv, int Kn,
+    int nC, int seg, int64_t max_seg, float c2) {
+  constexpr int D = 64, TPJ = 16 / G, KS = D / 32, DT = D / 16, NT = 64 * NW;
+  constexpr int KROW = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t kl[64][KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t vl[64][KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t pl[NW][64][16];  // P~^T of a wave's job
+  __shared__ int tok_l[kBwdSeg];
+  __shared__ int64_t eo_l[kBwdSeg];  // the entry's (b, t, g, slot) index
+  __shared__ float w_l[kBwdSeg];
+  const int64_t sidx = blockIdx.x % max_seg;
+  const int bg = (int)(blockIdx.x / max_seg);
+  if (sidx >= n_seg[bg]) return;  // whole block
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const int c = seg_chunk[(size_t)bg * max_seg + sidx];
+  const int32_t* off = offsets + (size_t)bg * (nC + 1);
+  const int32_t* ss = seg_start + (size_t)bg * (nC + 1);
+  const int e0 = off[c] + (int)(sidx - ss[c]) * seg;
+  const int ne = min(off[c + 1], e0 + seg) - e0;  // <= seg = kBwdSeg
+  const int32_t* ent = entries + (size_t)bg * L * Kn + e0;
+  const int tid = threadIdx.x, lane = tid % 64, col = lane % 16, blk = lane / 16;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
+  const size_t kvrow = (size_t)Hkv * D;
+  const size_t cb = ((b * L + (size_t)c * 64) * Hkv + g) * D;
+  for (int i = tid; i < ne; i += NT) {
+    const int val = ent[i];
+    const int t = val / Kn, k = val % Kn;
+    const int64_t eo = ((int64_t)(b * L + t) * Hkv + g) * Kn + k;
+    tok_l[i] = t;
+    eo_l[i] = eo;
+    w_l[i] = w[eo];
+  }
+  for (int i = tid; i < 64 * (D / 8); i += NT) {
+    const int key = i / (D / 8), d = (i % (D / 8)) * 8;
+    *reinterpret_cast<uint4*>(&kl[key][d]) = *reinterpret_cast<const uint4*>(K + cb + key * kvrow + d);
+    *reinterpret_cast<uint4*>(&vl[key][d]) = *reinterpret_cast<const uint4*>(V + cb + key * kvrow + d);
+  }
+  __syncthreads();
+  const int qs_sel = col / G, qs_head = col % G;  // this lane's A-operand row -> selector, head
+  const int trow = 4 * blk + col / 4, tcol = 4 * (col % 4);
+  const bf16* qbase = Q + ((b * L * Hq + (size_t)g * G + qs_head) * D + 8 * blk);
+  const size_t qstride = (size_t)Hq * D;  // per token
+  // this lane's query row of job j (a padding row repeats the job's first selector)
+  auto load_q = [&](int ej, bf16x8 (&qa)[KS]) {
+    const int n_here = min(TPJ, ne - ej);
+    const bf16* qr = qbase + (size_t)tok_l[ej + (qs_sel < n_here ? qs_sel : 0)] * qstride;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qa[ks] = ld_bf16x8(qr + 32 * ks);
+  };
+  bf16x8 qn[KS];
+  if (wv * TPJ < ne) load_q(wv * TPJ, qn);
+  for (int ej = wv * TPJ; ej < ne; ej += NW * TPJ) {
+    const int n_here = min(TPJ, ne - ej);
+    bf16x8 qa[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qa[ks] = qn[ks];
+    if (ej + NW * TPJ < ne) load_q(ej + NW * TPJ, qn);
+    f32x4 sa[4];
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      sa[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sa[t4] = mfma_16x16x32(
+            qa[ks], *reinterpret_cast<const bf16x8*>(&kl[16 * t4 + col][32 * ks + 8 * blk]),
+            sa[t4]);
+    }
+    // z = logit * log2(e).  Softmax-off-by-one of a row: P = exp2(z - lse) with
+    // lse = log2(1 + sum exp2(z)), evaluated with a shift m as m + log2(exp2(-m) + sum
+    // exp2(z - m)).  Any m gives the same value; m = max(0, max z) is needed only when some
+    // exp2(z) could overflow, so m = 0 unless a logit of the job exceeds 64.
+    float lmax = 0.0f;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa[t4][i] *= c2;
+        lmax = fmaxf(lmax, sa[t4][i]);
+      }
+    float m[4] = {0.f, 0.f, 0.f, 0.f};
+    if (__ballot(lmax > 64.0f)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mi = 0.0f;
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) mi = fmaxf(mi, sa[t4][i]);
+        m[i] = row16_max(mi);
+      }
+    }
+    float lse[4], f[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = (4 * blk + i) / G;
+      float sum = 0.0f;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        sa[t4][i] = exp2_fast(sa[t4][i] - m[i]);
+        sum += sa[t4][i];
+      }
+      const float den = exp2_fast(-m[i]) + row16_sum(sum);
+      lse[i] = m[i] + __builtin_amdgcn_logf(den);
+      f[i] = s < n_here ? w_l[ej + s] * __builtin_amdgcn_rcpf(den) : 0.0f;
+    }
+    {  // the normaliser of row 4*blk + col (lanes col < 4), kept for a backward
+      const int r = 4 * blk + col, s = r / G;
+      const float v = col == 0 ? lse[0] : col == 1 ? lse[1] : col == 2 ? lse[2] : lse[3];
+      if (col < 4 && s < n_here)
+        __builtin_nontemporal_store(v, lse_out + eo_l[ej + s] * G + r % G);
+    }
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[t4][i] *= f[i];
+      *reinterpret_cast<s16x4*>(&pl[wv][16 * t4 + col][4 * blk]) = pack_bf16x4(sa[t4]);
+    }
+    wave_lds_sync();  // P~^T is read transposed below
+    // O^T (rows d, columns the 16 query rows) = V_c^T P~^T, 32 keys per product: lane block
+    // blk takes keys 32*kk + 4*blk + i and 32*kk + 16 + 4*blk + i in both operands
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 pT = cat_bf16x8(lds_read_tr4(&pl[wv][32 * kk + trow][tcol]),
+                                   lds_read_tr4(&pl[wv][32 * kk + 16 + trow][tcol]));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        o[dt] = mfma_16x16x32(cat_bf16x8(lds_read_tr4(&vl[32 * kk + trow][16 * dt + tcol]),
+                                         lds_read_tr4(&vl[32 * kk + 16 + trow][16 * dt + tcol])),
+                              pT, o[dt]);
+    }
+    if (qs_sel < n_here) {  // lane column = query row col: its edge's output at d = 16*dt + 4*blk
+      bf16* dst = o_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 4 * blk;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<s16x4*>(dst + 16 * dt) = pack_bf16x4(o[dt]);
+    }
+    wave_lds_sync();  // pl reuse by the next job
+  }
+}
+
+// Token phase of the chunk-major forward: one wave per (b, t, g) row; O = the sum of the
+// row's valid slots' weighted outputs in slot order (fp32), rounded once.  Slots that are not
+// valid have no partial (their workspace bytes are stale) and are masked out by selection.
+template <int G>
+__global__ void __launch_bounds__(256) k_fwd_tok(const bf16* __restrict__ o_part,
+                                                 const int32_t* __restrict__ idx,
+                                                 bf16* __restrict__ O, int L, int Hkv, int Kn,
+                                                 int nC, int64_t rows) {
+  constexpr int D = 64, E = G;  // elements of the row's G x D block per lane
+  const int lane = threadIdx.x % 64;
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // (b * L + t) * Hkv + g
+  if (row >= rows) return;  // whole wave
+  const int g = (int)(row % Hkv);
+  const int64_t bt = row / Hkv;
+  const size_t o = (size_t)row * Kn;
+  const int c = lane < Kn ? idx[o + lane] : -1;
+  const uint64_t vmask = __ballot(c >= 0 && c < nC);
+  const bf16* src = o_part + o * (size_t)(G * D) + (size_t)lane * E;
+  float acc[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) acc[j] = 0.0f;
+  for (int k0 = 0; k0 < Kn; k0 += 8) {
+    uint32_t v[8][E / 2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (k0 + u < Kn) {
+        load_raw<E>(src + (size_t)(k0 + u) * G * D, v[u]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < E / 2; ++j) v[u][j] = 0u;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add_raw<E>(acc, v[u], k0 + u < Kn && ((vmask >> (k0 + u)) & 1));
+  }
+  store_row<E>(O + bt * (int64_t)Hkv * G * D + (size_t)g * G * D + (size_t)lane * E, acc);
+}
+
 int tile_tokens(const Dims& d) { return (d.D == 64 ? 64 : 32) / (d.G == 16 ? 2 : 1); }
 
 size_t tile_prep_bytes(const Dims& d) {
@@ -322,17 +518,33 @@ bool fwd_mfma_supported(const Dims& d) {
          !(d.flags & 1u);
 }
 
+bool fwd_chunked(const Dims& d) { return bwd_fused(d) && d.nC <= 16384; }
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 FwdState fwd_state(const Dims& d) {
   FwdState st{};
-  st.prep = 0;
-  st.kop = tile_prep_bytes(d);
-  st.lse = st.kop + chunk_ops_bytes(d);
-  const size_t lse = sizeof(float) * (size_t)d.B * d.L * d.Hq * d.K;
-  st.total = st.lse + ((lse + 255) & ~(size_t)255);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  st.lse = take(sizeof(float) * (size_t)d.B * d.L * d.Hq * d.K);
+  if (fwd_chunked(d)) {
+    st.ix = index_layout(d, o);
+    st.part = take(sizeof(uint16_t) * (size_t)d.B * d.L * d.Hq * d.K * d.D);
+  } else {
+    st.prep = take(tile_prep_bytes(d));
+    st.kop = take(chunk_ops_bytes(d));
+  }
+  st.total = o;
   return st;
 }
 
-size_t fwd_mfma_ws(const Dims& d) { return fwd_state(d).total + chunk_ops_bytes(d); }
+size_t fwd_mfma_ws(const Dims& d) {
+  return fwd_chunked(d) ? fwd_state(d).total : fwd_state(d).total + chunk_ops_bytes(d);
+}
 
 void launch_prep_ops(const Dims& d, const void* src, void* dst, bool trans, hipStream_t s) {
   if (d.nC == 0) return;
@@ -348,9 +560,48 @@ size_t chunk_ops_bytes(const Dims& d) {
   return ((size_t)d.B * d.Hkv * d.nC * 64 * d.D * sizeof(uint16_t) + 255) & ~(size_t)255;
 }
 
+// waves per segment block of the chunk-major forward (they share the chunk in LDS)
+constexpr int kFwdWaves = 8;
+
+static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const void* Q,
+                                     const void* K, const void* V, const int32_t* idx,
+                                     const float* w, void* O, char* ws, hipStream_t s) {
+  hipError_t e = launch_invidx(d, st.ix, idx, ws, s);
+  if (e != hipSuccess) return e;
+  const int BG = d.B * d.Hkv;
+  const float c2 = (float)(d.sm_scale * 1.4426950408889634);  // logit scale * log2(e)
+  if (d.nC > 0) {
+    Timed tm(HSA_KERNEL_FWD, s);
+    auto go = [&](auto kern) {
+      kern<<<dim3((unsigned)(BG * st.ix.max_seg)), 64 * kFwdWaves, 0, s>>>(
+          (const bf16*)Q, (const bf16*)K, (const bf16*)V, w,
+          (const int32_t*)(ws + st.ix.offsets), (const int32_t*)(ws + st.ix.entries),
+          (const int32_t*)(ws + st.ix.seg_start), (const int32_t*)(ws + st.ix.seg_chunk),
+          (const int32_t*)(ws + st.ix.n_seg), (bf16*)(ws + st.part), (float*)(ws + st.lse),
+          d.L, d.Hq, d.Hkv, d.K, d.nC, st.ix.seg, st.ix.max_seg, c2);
+    };
+    if (d.G == 4) go(k_fwd_chunk<4, kFwdWaves>);
+    else if (d.G == 8) go(k_fwd_chunk<8, kFwdWaves>);
+    else go(k_fwd_chunk<16, kFwdWaves>);
+  }
+  {
+    Timed tm(HSA_KERNEL_FWD_TOKEN, s);
+    const int64_t rows = (int64_t)d.B * d.L * d.Hkv;
+    auto go = [&](auto kern) {
+      kern<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(
+          (const bf16*)(ws + st.part), idx, (bf16*)O, d.L, d.Hkv, d.K, d.nC, rows);
+    };
+    if (d.G == 4) go(k_fwd_tok<4>);
+    else if (d.G == 8) go(k_fwd_tok<8>);
+    else go(k_fwd_tok<16>);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,
                            const int32_t* idx, const float* w, void* O, char* ws, hipStream_t s) {
   const FwdState st = fwd_state(d);
+  if (fwd_chunked(d)) return launch_fwd_chunked(d, st, Q, K, V, idx, w, O, ws, s);
   char* kop = ws + st.kop;
   char* prep = ws + st.prep;
   float* lse = (float*)(ws + st.lse);

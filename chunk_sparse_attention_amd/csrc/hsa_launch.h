@@ -33,25 +33,37 @@ struct Dims {
   unsigned flags;
 };
 
+// The chunk -> (token, slot) inverse index: per (b, g), entries grouped by chunk and cut into
+// segments of `seg` entries (byte offsets into a workspace).
+struct IndexLayout {
+  int tile_tokens;  // tokens per tile of the index build
+  int n_tiles;      // tiles per (b, g)
+  int seg;          // entries per segment
+  int64_t max_seg;  // segment capacity per (b, g)
+  size_t tile_counts, tile_base, offsets, entries, seg_start, seg_chunk, n_seg;
+};
+// Entries per chunk segment of the chunk-major kernels (two waves of 16-row jobs).
+constexpr int kBwdSeg = 256;
+// Lays the index out from byte offset o (advanced past it).
+IndexLayout index_layout(const Dims& d, size_t& o);
+
 // State the forward leaves at the start of its workspace for a backward over the same
-// selection: the token-tile job lists, the key rows in MFMA operand order and, per (token,
-// group, slot, head), the softmax-off-by-one normaliser in the log2 domain.  The backward's
-// workspace starts with the same regions.
+// selection: per (token, group, slot, head) the softmax-off-by-one normaliser in the log2
+// domain, and either (chunk-major forward) the inverse index and the per-edge partials'
+// buffer, or (token-tile forward) the tiles' job lists and the key rows in MFMA operand
+// order.  The backward's workspace starts with the same regions.
 struct FwdState {
-  size_t prep, kop, lse, total;
+  size_t lse;
+  IndexLayout ix;      // chunk-major forward
+  size_t part;         // chunk-major forward: per-edge bf16 partials, G*D per (t, g, slot)
+  size_t prep, kop;    // token-tile forward
+  size_t total;
 };
 FwdState fwd_state(const Dims& d);
 
 // Backward workspace carve-up (byte offsets into the caller's workspace).
-// Entries per chunk segment of the fused backward (two waves of 16-row jobs per segment).
-constexpr int kBwdSeg = 256;
-struct BwdLayout {
-  int tile_tokens;  // tokens per tile of the inverse-index build
-  int n_tiles;      // tiles per (b, g)
-  int seg;          // entries per backward-phase-2 segment
-  int64_t max_seg;  // segment capacity per (b, g)
-  size_t ds, dw, tile_counts, tile_base, offsets, entries, seg_start, seg_chunk, n_seg,
-      part_dk, part_dv, part_dks, kt, kop, vop, prep, lse, dd, dq_part, total;
+struct BwdLayout : IndexLayout {
+  size_t ds, dw, part_dk, part_dv, part_dks, kt, kop, vop, prep, lse, dd, dq_part, total;
 };
 BwdLayout bwd_layout(const Dims& d);
 
@@ -71,7 +83,7 @@ hipError_t launch_select_generic(const Dims& d, const void* Qs, const void* Kslc
                                  float* score, float* w, hipStream_t s);
 hipError_t launch_fwd_generic(const Dims& d, const void* Q, const void* K, const void* V,
                               const int32_t* idx, const float* w, void* O, hipStream_t s);
-hipError_t launch_invidx(const Dims& d, const BwdLayout& lay, const int32_t* idx, char* ws,
+hipError_t launch_invidx(const Dims& d, const IndexLayout& lay, const int32_t* idx, char* ws,
                          hipStream_t s);
 hipError_t launch_bwd_generic(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
                               const void* V, const void* Qs, const void* Kslc,
@@ -114,6 +126,8 @@ hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, c
                            void* dK, void* dV, void* dQs, float* dKslc, bool fold,
                            bool after_fwd, char* ws, hipStream_t s);
 bool fwd_mfma_supported(const Dims& d);
+// bf16 D = 64: the forward runs chunk-major (inverse index, per-edge partials, token sums).
+bool fwd_chunked(const Dims& d);
 size_t fwd_mfma_ws(const Dims& d);
 hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,
                            const int32_t* idx, const float* w, void* O, char* ws, hipStream_t s);

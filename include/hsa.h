@@ -193,7 +193,9 @@ typedef enum {
   HSA_KERNEL_BWD_REDUCE = 8, /* backward: fixed-order reduction of the segment partials */
   HSA_KERNEL_DECODE_SCAN = 9,    /* decode: scan of the chunk-key table, per-block top-K */
   HSA_KERNEL_DECODE_ATTEND = 10, /* decode: merge, weights and attention over the kept chunks */
-  HSA_KERNEL_COUNT = 11
+  HSA_KERNEL_FWD_TOKEN = 11, /* chunk-major forward (bf16 D=64): per token sum of the edges'
+                                weighted outputs */
+  HSA_KERNEL_COUNT = 12
 } hsa_kernel_t;
 
 /* enable != 0: forget earlier records and start recording; enable == 0: stop recording

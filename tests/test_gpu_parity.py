@@ -116,6 +116,8 @@ SMALL = [
     W("fp32_k1", 2, 64 * 9 + 1, 4, 2, 64, 64, 1, torch.float32, 1.0, 1.0),
     W("bf16_no_chunk", 1, 50, 8, 2, 64, 64, 4, torch.bfloat16),
     W("planted_d128", 1, 64 * 100, 16, 2, 128, 64, 8, torch.bfloat16, planted=True),
+    W("bf16_d64_g4_ragged", 1, 64 * 17 + 9, 8, 2, 64, 64, 6, torch.bfloat16),
+    W("bf16_d64_g16_k16", 1, 64 * 19 + 3, 16, 1, 64, 64, 16, torch.bfloat16),
 ]
 
 
