@@ -64,7 +64,13 @@ def fused_backward(wl, generic: bool) -> bool:
             and wl.G in (4, 8, 16))
 
 
-def kernel_counts(wl, n_slots: int, fused: bool = True) -> dict:
+def chunked_forward(wl, generic: bool) -> bool:
+    """The library's bf16 chunk-major forward (inverse index, per-edge partials, token sums)."""
+    return (not generic and str(wl.dtype).endswith("bfloat16") and wl.D in (64, 128)
+            and wl.G in (4, 8, 16) and wl.nC <= 16384)
+
+
+def kernel_counts(wl, n_slots: int, fused: bool = True, chunked: bool = True) -> dict:
     """Algorithmic bytes (each input the kernel needs read once, each output it produces
     written once; workspace copies of the design are not counted) and flops per launch of
     each kernel class.  n_slots = valid (b, t, g, k) selections; every slot is attended by
@@ -89,10 +95,11 @@ def kernel_counts(wl, n_slots: int, fused: bool = True) -> dict:
                        flops=8 * S * D * eg),
         "bwd_reduce": dict(bytes=2 * kv + 2 * kslc, flops=0),
     }
-    if fused:
+    if chunked:
         # chunk-major forward: Q, K, V and the slots in (the token phase writes O)
         c["fwd"] = dict(bytes=q + 2 * kv + 2 * slot, flops=4 * S * D * eg)
         c["fwd_token"] = dict(bytes=q + slot, flops=0)
+    if fused:
         # token phase: dQ and dQs out, the slots and Kslc rows in; dKslc partials read Qs
         c["bwd_p1"] = dict(bytes=q + 2 * kv + kslc + 3 * slot, flops=0)
         # chunk phase: Q, dO, K, V and the weights in; S, dP, dV, dK and dQ products
@@ -476,7 +483,7 @@ def main() -> int:
     entry_ms = {n: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps, 4)
                 for j, n in enumerate(names)}
     log("bench: per-entry ms", entry_ms)
-    counts = kernel_counts(wl, n_slots, fused_backward(wl, gen))
+    counts = kernel_counts(wl, n_slots, fused_backward(wl, gen), chunked_forward(wl, gen))
     kern = {}
     for name, (n, total) in ktimes.items():
         if n == 0:
@@ -542,7 +549,7 @@ def main() -> int:
         kt2 = hsa.timer_read()
         ts /= reps
         tf /= reps
-        c2 = kernel_counts(wl2, n2, fused_backward(wl2, gen))
+        c2 = kernel_counts(wl2, n2, fused_backward(wl2, gen), chunked_forward(wl2, gen))
         k2 = {name: roofline(name, c2[name], total / n, None)
               for name, (n, total) in kt2.items() if n}
         out["secondary"] = {

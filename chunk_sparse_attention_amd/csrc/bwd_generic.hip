@@ -20,7 +20,7 @@ IndexLayout index_layout(const Dims& d, size_t& o) {
   while ((d.L + tt - 1) / tt > 256) tt *= 2;
   x.tile_tokens = tt;
   x.n_tiles = (d.L + tt - 1) / tt;
-  x.seg = bwd_fused(d) ? kBwdSeg : 128;
+  x.seg = (fwd_chunked(d) || bwd_fused(d)) ? kBwdSeg : 128;
   const int64_t bg = (int64_t)d.B * d.Hkv;
   const int64_t E = (int64_t)d.L * d.K;  // entry capacity per (b, g)
   x.max_seg = (E + x.seg - 1) / x.seg + d.nC;
@@ -66,6 +66,10 @@ BwdLayout bwd_layout(const Dims& d) {
     // partials' buffer, free once the forward has summed them)
     l.dq_part = chunked ? st.part : take(sizeof(uint16_t) * bg * E * d.G * d.D);
   } else {
+    if (chunked && bwd_mfma_supported(d)) {  // the token-tile backward's own job lists
+      l.prep = take(tile_prep_bytes(d));
+      l.kop = take(chunk_ops_bytes(d));
+    }
     l.kt = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
     l.vop = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
     // per (token, group, slot, head): D = <dO, O_k> (the normaliser is in the state prefix)

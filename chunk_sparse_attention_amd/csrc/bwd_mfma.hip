@@ -810,7 +810,8 @@ hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, c
   // D = 128: token tiles on the matrix cores, then the vector-ALU chunk phase
   launch_prep_ops(d, K, ws + lay.kt, true, s);
   launch_prep_ops(d, V, ws + lay.vop, false, s);
-  if (!after_fwd) {  // else the forward's job lists and key operand are still in place
+  // after a token-tile forward its job lists and key operand are still in place
+  if (!after_fwd || fwd_chunked(d)) {
     launch_prep_ops(d, K, ws + lay.kop, false, s);
     launch_tile_prep(d, idx, ws + lay.prep, s);
   }

@@ -4,7 +4,10 @@
 // stick-breaking chunk weights ("Hardware-aligned Hierarchical Sparse Attention ...",
 // papernotes.org note, 方法详解 › 层次化稀疏注意力（HSA） 第一阶段/第二阶段, 硬件对齐 Kernel).
 //
-// One workgroup owns a tile of TT consecutive tokens of one (batch, group) and keeps their
+// Two designs.  The chunk-major one (below k_fwd_tile) runs whenever the inverse index fits
+// (at most 16384 chunks); the token-tile one covers longer sequences.
+//
+// Token tiles: one workgroup owns a tile of TT consecutive tokens of one (batch, group) and keeps their
 // fp32 outputs in LDS.  The tile's (token, slot) edges are sorted by chunk; each wave takes a
 // contiguous range of 16-column jobs (16/G tokens of one chunk, G heads each), holds that
 // chunk's key and transposed value operands in registers while its jobs share the chunk, and
@@ -266,9 +269,9 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
   }
 }
 
-// ---- chunk-major forward (D = 64) ----------------------------------------------------------
-// One block of two waves per segment of a chunk's selector list (the chunk -> (token, slot)
-// index); the chunk's keys and values sit in LDS and the waves take alternate jobs of 16
+// ---- chunk-major forward ------------------------------------------------------------------
+// One block of NW waves per segment of a chunk's selector list (the chunk -> (token, slot)
+// index); the chunk's keys and values sit in LDS and the waves take turns at jobs of 16
 // query rows (16/G selectors x G heads, row q = selector * G + head):
 //   S = Q K_c^T                                  (MFMA; lane: key column, four query rows)
 //   softmax-off-by-one over the chunk's 64 keys  (row statistics across 16 lanes)
@@ -276,7 +279,7 @@ __global__ void __launch_bounds__(512) k_fwd_tile(
 //   O_k^T = V_c^T P~^T                           (MFMA, both operands by transposing reads)
 // Each selection edge lies in exactly one segment: its weighted output (bf16, G x D) and the
 // normaliser of each of its heads are stored once; a token phase sums the edges of a token.
-template <int G, int NW>
+template <int D, int G, int NW>
 __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const float* __restrict__ w, const int32_t* __restrict__ offsets,
@@ -284,7 +287,7 @@ __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
     const int32_t* __restrict__ seg_chunk, const int32_t* __restrict__ n_seg,
     bf16* __restrict__ o_part, float* __restrict__ lse_out, int L, int Hq, int Hkv, int Kn,
     int nC, int seg, int64_t max_seg, float c2) {
-  constexpr int D = 64, TPJ = 16 / G, KS = D / 32, DT = D / 16, NT = 64 * NW;
+  constexpr int TPJ = 16 / G, KS = D / 32, DT = D / 16, NT = 64 * NW;
   constexpr int KROW = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t kl[64][KROW];
   __shared__ __attribute__((aligned(16))) uint16_t vl[64][KROW];
@@ -427,12 +430,12 @@ __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
 // Token phase of the chunk-major forward: one wave per (b, t, g) row; O = the sum of the
 // row's valid slots' weighted outputs in slot order (fp32), rounded once.  Slots that are not
 // valid have no partial (their workspace bytes are stale) and are masked out by selection.
-template <int G>
+template <int D, int G>
 __global__ void __launch_bounds__(256) k_fwd_tok(const bf16* __restrict__ o_part,
                                                  const int32_t* __restrict__ idx,
                                                  bf16* __restrict__ O, int L, int Hkv, int Kn,
                                                  int nC, int64_t rows) {
-  constexpr int D = 64, E = G;  // elements of the row's G x D block per lane
+  constexpr int E = G * D / 64;  // elements of the row's G x D block per lane
   const int lane = threadIdx.x % 64;
   const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // (b * L + t) * Hkv + g
   if (row >= rows) return;  // whole wave
@@ -518,7 +521,7 @@ bool fwd_mfma_supported(const Dims& d) {
          !(d.flags & 1u);
 }
 
-bool fwd_chunked(const Dims& d) { return bwd_fused(d) && d.nC <= 16384; }
+bool fwd_chunked(const Dims& d) { return fwd_mfma_supported(d) && d.nC <= 16384; }
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -580,9 +583,15 @@ static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const vo
           (const int32_t*)(ws + st.ix.n_seg), (bf16*)(ws + st.part), (float*)(ws + st.lse),
           d.L, d.Hq, d.Hkv, d.K, d.nC, st.ix.seg, st.ix.max_seg, c2);
     };
-    if (d.G == 4) go(k_fwd_chunk<4, kFwdWaves>);
-    else if (d.G == 8) go(k_fwd_chunk<8, kFwdWaves>);
-    else go(k_fwd_chunk<16, kFwdWaves>);
+    if (d.D == 64) {
+      if (d.G == 4) go(k_fwd_chunk<64, 4, kFwdWaves>);
+      else if (d.G == 8) go(k_fwd_chunk<64, 8, kFwdWaves>);
+      else go(k_fwd_chunk<64, 16, kFwdWaves>);
+    } else {
+      if (d.G == 4) go(k_fwd_chunk<128, 4, kFwdWaves>);
+      else if (d.G == 8) go(k_fwd_chunk<128, 8, kFwdWaves>);
+      else go(k_fwd_chunk<128, 16, kFwdWaves>);
+    }
   }
   {
     Timed tm(HSA_KERNEL_FWD_TOKEN, s);
@@ -591,9 +600,15 @@ static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const vo
       kern<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(
           (const bf16*)(ws + st.part), idx, (bf16*)O, d.L, d.Hkv, d.K, d.nC, rows);
     };
-    if (d.G == 4) go(k_fwd_tok<4>);
-    else if (d.G == 8) go(k_fwd_tok<8>);
-    else go(k_fwd_tok<16>);
+    if (d.D == 64) {
+      if (d.G == 4) go(k_fwd_tok<64, 4>);
+      else if (d.G == 8) go(k_fwd_tok<64, 8>);
+      else go(k_fwd_tok<64, 16>);
+    } else {
+      if (d.G == 4) go(k_fwd_tok<128, 4>);
+      else if (d.G == 8) go(k_fwd_tok<128, 8>);
+      else go(k_fwd_tok<128, 16>);
+    }
   }
   return hipGetLastError();
 }
