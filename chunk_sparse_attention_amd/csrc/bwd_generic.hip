@@ -16,7 +16,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 IndexLayout index_layout(const Dims& d, size_t& o) {
   IndexLayout x{};
-  int tt = 256;
+  int tt = 64;
   while ((d.L + tt - 1) / tt > 256) tt *= 2;
   x.tile_tokens = tt;
   x.n_tiles = (d.L + tt - 1) / tt;
@@ -29,8 +29,8 @@ IndexLayout index_layout(const Dims& d, size_t& o) {
     o = align256(o + bytes);
     return at;
   };
+  // per (b, g, chunk, tile): the tile's count of the chunk, then its exclusive prefix
   x.tile_counts = take(sizeof(int32_t) * bg * x.n_tiles * d.nC);
-  x.tile_base = take(sizeof(int32_t) * bg * x.n_tiles * d.nC);
   x.offsets = take(sizeof(int32_t) * bg * (d.nC + 1));
   x.entries = take(sizeof(int32_t) * bg * E);
   x.seg_start = take(sizeof(int32_t) * bg * (d.nC + 1));
@@ -81,7 +81,8 @@ BwdLayout bwd_layout(const Dims& d) {
 
 // ---- inverse index ---------------------------------------------------------------------
 
-// Per (b, g, tile): how many of the tile's (token, slot) entries chose each chunk.
+// Per (b, g, tile): how many of the tile's (token, slot) entries chose each chunk, stored
+// chunk-major: tile_counts[(bg * nC + c) * n_tiles + tile].
 __global__ void __launch_bounds__(256) k_inv_count(const int32_t* __restrict__ idx,
                                                    int32_t* __restrict__ tile_counts, int L,
                                                    int Hkv, int K, int nC, int tile_tokens,
@@ -94,17 +95,53 @@ __global__ void __launch_bounds__(256) k_inv_count(const int32_t* __restrict__ i
   for (int c = threadIdx.x; c < nC; c += blockDim.x) cnt[c] = 0;
   __syncthreads();
   const int t0 = tile * tile_tokens;
-  const int t1 = min(L, t0 + tile_tokens);
-  for (int t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
-    const int32_t* ir = idx + ((b * L + t) * Hkv + g) * K;
-    for (int k = 0; k < K; ++k) {
-      int c = ir[k];
-      if (c >= 0 && c < nC) atomicAdd(&cnt[c], 1);
-    }
+  const int n = (min(L, t0 + tile_tokens) - t0) * K;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int t = t0 + i / K, k = i % K;
+    const int c = idx[((b * L + t) * Hkv + g) * K + k];
+    if (c >= 0 && c < nC) atomicAdd(&cnt[c], 1);
   }
   __syncthreads();
-  int32_t* out = tile_counts + ((size_t)bg * n_tiles + tile) * nC;
-  for (int c = threadIdx.x; c < nC; c += blockDim.x) out[c] = cnt[c];
+  int32_t* out = tile_counts + (size_t)bg * nC * n_tiles + tile;
+  for (int c = threadIdx.x; c < nC; c += blockDim.x) out[(size_t)c * n_tiles] = cnt[c];
+}
+
+// One wave per (b, g, chunk): exclusive prefix of the chunk's tile counts over the tiles
+// (n_tiles <= 256, four per lane), written in place; the chunk's total entries go to
+// offsets[c] and its segment count to seg_start[c] (both scanned over chunks next).
+__global__ void __launch_bounds__(256) k_inv_colscan(int32_t* __restrict__ tile_counts,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ seg_start, int nC,
+                                                     int n_tiles, int seg, int n_rows) {
+  const int row = blockIdx.x * 4 + threadIdx.x / kWave;  // bg * nC + c
+  if (row >= n_rows) return;  // whole wave
+  const int lane = threadIdx.x % kWave;
+  const int bg = row / nC, c = row % nC;
+  int32_t* tc = tile_counts + (size_t)row * n_tiles;
+  int32_t v[4], s = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // lane takes tiles 4*lane .. 4*lane+3
+    const int tile = 4 * lane + j;
+    v[j] = tile < n_tiles ? tc[tile] : 0;
+    s += v[j];
+  }
+  int32_t incl = s;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  int32_t run = incl - s;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tile = 4 * lane + j;
+    if (tile < n_tiles) tc[tile] = run;
+    run += v[j];
+  }
+  if (lane == kWave - 1) {
+    offsets[(size_t)bg * (nC + 1) + c] = incl;
+    seg_start[(size_t)bg * (nC + 1) + c] = (incl + seg - 1) / seg;
+  }
 }
 
 // Exclusive scan of n ints in place (one block of 1024 threads; thread-contiguous runs):
@@ -140,28 +177,17 @@ __device__ void block_exclusive_scan(int32_t* a, int n, int32_t* total_out) {
   __syncthreads();
 }
 
-// Per (b, g): chunk offsets, each tile's base position per chunk, and the phase-2 segments
-// (ceil(n_c / seg) per chunk) with their chunk ids.
-__global__ void __launch_bounds__(1024) k_inv_scan(const int32_t* __restrict__ tile_counts,
-                                                   int32_t* __restrict__ tile_base,
-                                                   int32_t* __restrict__ offsets,
+// Per (b, g): chunk offsets and the segments (ceil(n_c / seg) per chunk) with their chunk
+// ids, from the per-chunk totals and segment counts.
+__global__ void __launch_bounds__(1024) k_inv_scan(int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ seg_start,
                                                    int32_t* __restrict__ seg_chunk,
                                                    int32_t* __restrict__ n_seg, int nC,
-                                                   int n_tiles, int seg, int64_t max_seg) {
+                                                   int64_t max_seg) {
   __shared__ int32_t total_e, total_s;
   const int bg = blockIdx.x;
-  const int32_t* tc = tile_counts + (size_t)bg * n_tiles * nC;
-  int32_t* tb = tile_base + (size_t)bg * n_tiles * nC;
   int32_t* off = offsets + (size_t)bg * (nC + 1);
   int32_t* ss = seg_start + (size_t)bg * (nC + 1);
-  for (int c = threadIdx.x; c < nC; c += blockDim.x) {
-    int32_t col = 0;
-    for (int tile = 0; tile < n_tiles; ++tile) col += tc[(size_t)tile * nC + c];
-    off[c] = col;
-    ss[c] = (col + seg - 1) / seg;
-  }
-  __syncthreads();
   block_exclusive_scan(off, nC, &total_e);
   block_exclusive_scan(ss, nC, &total_s);
   if (threadIdx.x == 0) {
@@ -170,23 +196,19 @@ __global__ void __launch_bounds__(1024) k_inv_scan(const int32_t* __restrict__ t
     n_seg[bg] = total_s;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < nC; c += blockDim.x) {
-    int32_t run = off[c];
-    for (int tile = 0; tile < n_tiles; ++tile) {
-      tb[(size_t)tile * nC + c] = run;
-      run += tc[(size_t)tile * nC + c];
-    }
-    int32_t* sc = seg_chunk + (size_t)bg * max_seg;
+  int32_t* sc = seg_chunk + (size_t)bg * max_seg;
+  for (int c = threadIdx.x; c < nC; c += blockDim.x)
     for (int s = ss[c]; s < ss[c + 1]; ++s) sc[s] = c;
-  }
 }
 
 // Per (b, g, tile), one wave: walk the tile's tokens in order; lane k places slot k.  A token's
 // chunks are distinct, so the lanes of one step never share a counter.  The tile's selections
-// are first staged in LDS, 256 tokens at a time, so the serial walk waits on LDS only.
+// are first staged in LDS, 256 tokens at a time, so the serial walk waits on LDS only.  A
+// chunk's entries from this tile start at offsets[c] + the tile's prefix for c.
 constexpr int kScatterBatch = 256;
 __global__ void __launch_bounds__(64) k_inv_scatter(const int32_t* __restrict__ idx,
-                                                    const int32_t* __restrict__ tile_base,
+                                                    const int32_t* __restrict__ tile_prefix,
+                                                    const int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ entries, int L,
                                                     int Hkv, int K, int nC, int tile_tokens,
                                                     int n_tiles) {
@@ -197,8 +219,9 @@ __global__ void __launch_bounds__(64) k_inv_scatter(const int32_t* __restrict__ 
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const int lane = threadIdx.x;
-  for (int c = lane; c < nC; c += kWave) cnt[c] = 0;
-  const int32_t* tb = tile_base + ((size_t)bg * n_tiles + tile) * nC;
+  const int32_t* tp = tile_prefix + (size_t)bg * nC * n_tiles + tile;
+  const int32_t* off = offsets + (size_t)bg * (nC + 1);
+  for (int c = lane; c < nC; c += kWave) cnt[c] = off[c] + tp[(size_t)c * n_tiles];
   int32_t* ent = entries + (size_t)bg * L * K;
   const int t0 = tile * tile_tokens;
   const int t1 = min(L, t0 + tile_tokens);
@@ -212,8 +235,8 @@ __global__ void __launch_bounds__(64) k_inv_scatter(const int32_t* __restrict__ 
       if (lane < K) {
         const int c = sel[tt * K + lane];
         if (c >= 0 && c < nC) {
-          const int pos = tb[c] + cnt[c];
-          cnt[c] += 1;
+          const int pos = cnt[c];
+          cnt[c] = pos + 1;
           ent[pos] = (tb0 + tt) * K + lane;
         }
       }
@@ -226,18 +249,21 @@ hipError_t launch_invidx(const Dims& d, const IndexLayout& lay, const int32_t* i
   const int bg = d.B * d.Hkv;
   if (bg == 0 || d.nC == 0) return hipSuccess;
   int32_t* tc = (int32_t*)(ws + lay.tile_counts);
-  int32_t* tb = (int32_t*)(ws + lay.tile_base);
   size_t lds = sizeof(int32_t) * d.nC;
   Timed tm(HSA_KERNEL_INVIDX, s);
   k_inv_count<<<dim3(bg * lay.n_tiles), 256, lds, s>>>(idx, tc, d.L, d.Hkv, d.K, d.nC,
                                                         lay.tile_tokens, lay.n_tiles);
-  k_inv_scan<<<dim3(bg), 1024, 0, s>>>(tc, tb, (int32_t*)(ws + lay.offsets),
+  const int rows = bg * d.nC;
+  k_inv_colscan<<<dim3((rows + 3) / 4), 256, 0, s>>>(tc, (int32_t*)(ws + lay.offsets),
+                                                     (int32_t*)(ws + lay.seg_start), d.nC,
+                                                     lay.n_tiles, lay.seg, rows);
+  k_inv_scan<<<dim3(bg), 1024, 0, s>>>((int32_t*)(ws + lay.offsets),
                                        (int32_t*)(ws + lay.seg_start),
                                        (int32_t*)(ws + lay.seg_chunk),
-                                       (int32_t*)(ws + lay.n_seg), d.nC, lay.n_tiles, lay.seg,
-                                       lay.max_seg);
-  k_inv_scatter<<<dim3(bg * lay.n_tiles), 64, lds, s>>>(idx, tb, (int32_t*)(ws + lay.entries),
-                                                         d.L, d.Hkv, d.K, d.nC, lay.tile_tokens,
+                                       (int32_t*)(ws + lay.n_seg), d.nC, lay.max_seg);
+  k_inv_scatter<<<dim3(bg * lay.n_tiles), 64, lds, s>>>(idx, tc, (const int32_t*)(ws + lay.offsets),
+                                                         (int32_t*)(ws + lay.entries), d.L,
+                                                         d.Hkv, d.K, d.nC, lay.tile_tokens,
                                                          lay.n_tiles);
   return hipGetLastError();
 }

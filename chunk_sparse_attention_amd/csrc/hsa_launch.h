@@ -40,7 +40,7 @@ struct IndexLayout {
   int n_tiles;      // tiles per (b, g)
   int seg;          // entries per segment
   int64_t max_seg;  // segment capacity per (b, g)
-  size_t tile_counts, tile_base, offsets, entries, seg_start, seg_chunk, n_seg;
+  size_t tile_counts, offsets, entries, seg_start, seg_chunk, n_seg;
 };
 // Entries per chunk segment of the chunk-major kernels (two waves of 16-row jobs).
 constexpr int kBwdSeg = 256;
