@@ -8,13 +8,14 @@
 //           fp64 dot product in dimension order (exact products, so each score is the
 //           correctly rounded definition); the block reduces its candidates to a ranked
 //           top-K that it writes to the workspace.
-//   attend  one block per (sequence, group) with one wave per kept slot.  Each wave merges
+//   attend  one block per (sequence, group, quarter of the group's heads) with one wave per
+//           kept slot, so a (sequence, group) spreads over up to four CUs.  Each wave merges
 //           the scan's candidates itself (so no wave waits on another), forms the
-//           stick-breaking weights, and runs softmax-off-by-one attention of the group's G
-//           query heads over its slot's chunk: lane j holds key row j for the logits, and the
-//           value rows are read as independent 16-byte pieces so that all of a chunk's loads
-//           are in flight at once.  The K weighted slot outputs meet in LDS and are summed in
-//           slot order.
+//           stick-breaking weights, and runs softmax-off-by-one attention of the block's heads
+//           over its slot's chunk: lane j holds key row j for the logits, and the value rows
+//           are read as independent 16-byte pieces so that all of a chunk's loads are in
+//           flight at once.  The K weighted slot outputs meet in LDS and are summed in slot
+//           order.
 #include <algorithm>
 
 #include "hsa_common.h"
@@ -57,19 +58,25 @@ struct RawRow<float, D> {
   }
 };
 
-size_t dec_fast_ws(const Dims& d) {
-  const int n_blocks = d.nC > 0 ? (d.nC + kScanChunks - 1) / kScanChunks : 0;
-  const size_t n = sizeof(uint64_t) * (size_t)d.B * d.Hkv * n_blocks * d.K;
-  return (n + 255) & ~(size_t)255;
+// Workspace: the scan blocks' candidate keys.
+struct DecFastLayout {
+  int n_blocks;
+  size_t cand, total;
+};
+static DecFastLayout dec_fast_layout(const Dims& d) {
+  DecFastLayout l{};
+  l.n_blocks = d.nC > 0 ? (d.nC + kScanChunks - 1) / kScanChunks : 0;
+  l.cand = 0;
+  l.total = (sizeof(uint64_t) * (size_t)d.B * d.Hkv * l.n_blocks * d.K + 255) & ~(size_t)255;
+  return l;
 }
+size_t dec_fast_ws(const Dims& d) { return dec_fast_layout(d).total; }
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(4)))
-k_dec_scan_fast(const T* __restrict__ qs,
-                                                                const T* __restrict__ Kslc,
-                                                                uint64_t* __restrict__ cand,
-                                                                int Hkv, int K, int nC,
-                                                                int n_blocks, double sel_scale) {
+k_dec_scan_fast(const T* __restrict__ qs, const T* __restrict__ Kslc,
+                uint64_t* __restrict__ cand, int Hkv, int K, int nC, int n_blocks,
+                double sel_scale) {
   __shared__ double qsh[D];
   const int blk = blockIdx.x % n_blocks;
   const int bg = blockIdx.x / n_blocks;
@@ -195,32 +202,34 @@ __device__ __forceinline__ uint64_t rank_candidates(const uint64_t* __restrict__
   return mykey;
 }
 
-// D elements per row = P pieces of 8; the 64 lanes of a wave form JG = 64/P groups of P
-// lanes, and group jg reads rows jg, jg+JG, ... of the chunk.  The block has WS waves per
-// slot, each taking HW of the group's heads.  LDS: the group's queries, the attention weights
-// of four heads per wave, and the K weighted slot outputs (at most 8 + 64 + 128 KB for
-// D = 128, K = G = 16).
-template <typename T, int D, int NT, int ZH>
-__global__ void __launch_bounds__(NT) k_dec_attend_fast(
+// One block per (b, g, head group): a head group is HW of the group's G query heads, and the
+// block has one wave per kept slot.  D elements per row = P pieces of 8; the 64 lanes of a
+// wave form JG = 64/P groups of P lanes, and group jg reads rows jg, jg+JG, ... of the chunk
+// in the value product.  Every wave merges the scan's candidates itself (so no wave waits on
+// another) and forms the stick-breaking weights; the slots' weighted outputs meet in LDS and
+// are summed in rank order.
+template <typename T, int D, int ZH, int NT>
+__global__ void __launch_bounds__(NT) k_dec_attend_heads(
     const T* __restrict__ q, const T* __restrict__ Kc, const T* __restrict__ Vc,
     const uint64_t* __restrict__ cand, T* __restrict__ O, int32_t* __restrict__ idx,
     float* __restrict__ score, float* __restrict__ w, int ctx, int Hq, int Hkv, int K, int G,
-    int WS, int HW, int n_cand, float c2) {
+    int HW, int n_hg, int n_cand, float c2) {
   constexpr int P = D / 8;
   constexpr int JG = kWave / P;
   constexpr int RPL = kChunk / JG;  // rows per lane in the value product
-  __shared__ float qsh[kMaxG][D];
-  __shared__ float ash[NT / kWave][4][kChunk];
-  __shared__ float osh[kMaxK][kMaxG][D];
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int slot = wave / WS, h_lo = (wave % WS) * HW, h_hi = min(G, h_lo + HW);
-  const int bg = blockIdx.x;
+  __shared__ float qsh[ZH][D];
+  __shared__ float ash[kMaxK][ZH][kChunk];
+  __shared__ float osh[kMaxK][ZH][D];
+  const int tid = threadIdx.x, lane = tid % kWave, slot = tid / kWave;
+  const int hg = blockIdx.x % n_hg, bg = blockIdx.x / n_hg;
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
-  const size_t qbase = ((size_t)b * Hq + (size_t)g * G) * D;
-  for (int i = tid; i < G * D; i += blockDim.x) qsh[i / D][i % D] = to_f32(q[qbase + i]);
+  const int h_lo = hg * HW, nh = min(G, h_lo + HW) - h_lo;
+  const size_t qbase = ((size_t)b * Hq + (size_t)g * G + h_lo) * D;
+  for (int i = tid; i < nh * D; i += blockDim.x) qsh[i / D][i % D] = to_f32(q[qbase + i]);
 
-  const uint64_t mykey = rank_candidates(cand + (size_t)bg * n_cand, n_cand, K, lane);
+  const uint64_t mykey =
+      n_cand > 0 ? rank_candidates(cand + (size_t)bg * n_cand, n_cand, K, lane) : 0;
   // stick-breaking in rank order: slot k needs p_k * prod_{j<k} (1 - p_j), a prefix
   // product over lanes 0..K-1 (masked slots have p = 0 and come last)
   const double p = mykey != 0 ? sigmoid_d((double)key_score(mykey)) : 0.0;
@@ -233,7 +242,7 @@ __global__ void __launch_bounds__(NT) k_dec_attend_fast(
   double excl = __shfl_up(keep, 1, 16);
   if ((lane & 15) == 0) excl = 1.0;
   const double wslot = p * excl;
-  if (wave == 0 && lane < K) {
+  if (hg == 0 && slot == 0 && lane < K) {
     const size_t o = (size_t)bg * K + lane;
     if (mykey == 0) {
       idx[o] = -1;
@@ -258,23 +267,21 @@ __global__ void __launch_bounds__(NT) k_dec_attend_fast(
     const size_t kvstride = (size_t)Hkv * D;
     const size_t cbase = ((b * ctx + (size_t)c * kChunk) * Hkv + g) * D;
     const int p8 = lane % P, jg = lane / P;
-    // key row j in lane j; for D = 64 the value pieces are requested at the same time
+    // key row j in lane j; the value pieces are requested at the same time
     RawRow<T, D> kr;
     kr.load(Kc + cbase + (size_t)lane * kvstride);
     RawRow<T, 8> vp[RPL];
-    if (D == 64) {
 #pragma unroll
-      for (int i = 0; i < RPL; ++i)
-        vp[i].load(Vc + cbase + (size_t)(jg + JG * i) * kvstride + 8 * p8);
-    }
-    float z[ZH];  // ZH >= HW heads per wave
+    for (int i = 0; i < RPL; ++i)
+      vp[i].load(Vc + cbase + (size_t)(jg + JG * i) * kvstride + 8 * p8);
+    float z[ZH];
 #pragma unroll
     for (int h = 0; h < ZH; ++h) {
       z[h] = 0.0f;
-      if (h < h_hi - h_lo) {
+      if (h < nh) {
 #pragma unroll
         for (int e0 = 0; e0 < D; e0 += 8) {
-          int off = (h_lo + h) * D + e0;  // the empty asm keeps the query reads in the loop
+          int off = h * D + e0;  // the empty asm keeps the query reads in the loop
           asm volatile("" : "+v"(off));
           const float4 qa = *reinterpret_cast<const float4*>(&qsh[0][0] + off);
           const float4 qb = *reinterpret_cast<const float4*>(&qsh[0][0] + off + 4);
@@ -284,64 +291,55 @@ __global__ void __launch_bounds__(NT) k_dec_attend_fast(
         }
       }
     }
-    if (D != 64) {
+    // softmax-off-by-one of each head (log2 domain), scaled by the slot weight
 #pragma unroll
-      for (int i = 0; i < RPL; ++i)
-        vp[i].load(Vc + cbase + (size_t)(jg + JG * i) * kvstride + 8 * p8);
+    for (int h = 0; h < ZH; ++h) {
+      float aw = 0.0f;
+      if (h < nh) {
+        const float zz = z[h] * c2;
+        const float m = fmaxf(0.0f, wave_max_f(zz));
+        const float ex = exp2f(zz - m);
+        aw = wf * ex / (exp2f(-m) + wave_sum_f(ex));
+      }
+      ash[slot][h][lane] = aw;
     }
+    // value product: lane (jg, p8) accumulates rows jg + JG*i of piece p8
+    float acc[ZH][8];
 #pragma unroll
-    for (int h0 = 0; h0 < ZH; h0 += 4) {
-      if (h0 >= h_hi - h_lo) break;
-      // softmax-off-by-one of four heads (log2 domain), scaled by the slot weight
+    for (int h = 0; h < ZH; ++h)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        float aw = 0.0f;
-        if (h0 + a < h_hi - h_lo) {
-          const float zz = z[h0 + a] * c2;
-          const float m = fmaxf(0.0f, wave_max_f(zz));
-          const float ex = exp2f(zz - m);
-          aw = wf * ex / (exp2f(-m) + wave_sum_f(ex));
-        }
-        ash[wave][a][lane] = aw;
+      for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int j = jg + JG * i;
+#pragma unroll
+      for (int h = 0; h < ZH; ++h) {
+        const float aw = ash[slot][h][j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(aw, vp[i].get(e), acc[h][e]);
       }
-      // value product: lane (jg, p8) accumulates rows jg + JG*i of piece p8
-      float acc[4][8];
+    }
+    // sum over the JG row groups: lanes p8 + P*jg
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+    for (int h = 0; h < ZH; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[a][e] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < RPL; ++i) {
-        const int j = jg + JG * i;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const float aw = ash[wave][a][j];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[a][e] = fmaf(aw, vp[i].get(e), acc[a][e]);
-        }
+      for (int e = 0; e < 8; ++e) {
+        float sum = acc[h][e];
+        if (P == 8) sum += dppc<0x128>(sum);  // row_ror:8 pairs lanes l and l^8 in a row
+        acc[h][e] = rows4_sum(sum);
       }
-      // sum over the JG row groups: lanes p8 + P*jg
+    if (jg == 0) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int h = 0; h < ZH; ++h)
+        if (h < nh) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float sum = acc[a][e];
-          if (P == 8) sum += dppc<0x128>(sum);  // row_ror:8 pairs lanes l and l^8 in a row
-          acc[a][e] = rows4_sum(sum);
+          for (int e = 0; e < 8; ++e) osh[slot][h][8 * p8 + e] = acc[h][e];
         }
-      if (jg == 0) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          if (h0 + a < h_hi - h_lo) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) osh[slot][h_lo + h0 + a][8 * p8 + e] = acc[a][e];
-          }
-      }
     }
   }
   __syncthreads();
   // O = sum over the valid slots in rank order (valid slots come first)
-  for (int i = tid; i < G * D; i += blockDim.x) {
+  for (int i = tid; i < nh * D; i += blockDim.x) {
     float sum = 0.0f;
     for (int k = 0; k < n_valid; ++k) sum += osh[k][i / D][i % D];
     O[qbase + i] = from_f32<T>(sum);
@@ -353,8 +351,9 @@ static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, cons
                               const void* Vc, const void* Kslc, void* O, int32_t* idx,
                               float* score, float* w, char* ws, hipStream_t s) {
   const int bg = d.B * d.Hkv;
-  const int n_blocks = d.nC > 0 ? (d.nC + kScanChunks - 1) / kScanChunks : 0;
-  uint64_t* cand = (uint64_t*)ws;
+  const DecFastLayout lay = dec_fast_layout(d);
+  const int n_blocks = lay.n_blocks;
+  uint64_t* cand = (uint64_t*)(ws + lay.cand);
   if (n_blocks > 0) {
     Timed tm(HSA_KERNEL_DECODE_SCAN, s);
     k_dec_scan_fast<T, D><<<dim3(bg * n_blocks), kScanThreads, 0, s>>>(
@@ -362,19 +361,17 @@ static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, cons
   }
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);
   Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
-  // WS waves per slot (each HW heads), at most 16 waves; the launch bound sets the register
-  // budget (256 VGPRs up to 8 waves, 128 above)
-  const int WS = std::max(1, std::min((d.G + 3) / 4, 16 / d.K));
-  const int HW = (d.G + WS - 1) / WS;
-  const int nt = kWave * d.K * WS;
+  // one block per (b, g, head group) of HW <= 4 heads, one wave per kept slot
+  const int HW = (d.G + 3) / 4;
+  const int n_hg = (d.G + HW - 1) / HW;
+  // the launch bound sets the register budget: 256 VGPRs up to 8 slots, 128 above
   auto go = [&](auto kern) {
-    kern<<<dim3(bg), nt, 0, s>>>((const T*)q, (const T*)Kc, (const T*)Vc, cand, (T*)O, idx,
-                                 score, w, d.L, d.Hq, d.Hkv, d.K, d.G, WS, HW, n_blocks * d.K,
-                                 c2);
+    kern<<<dim3(bg * n_hg), kWave * d.K, 0, s>>>((const T*)q, (const T*)Kc, (const T*)Vc, cand,
+                                                 (T*)O, idx, score, w, d.L, d.Hq, d.Hkv, d.K,
+                                                 d.G, HW, n_hg, n_blocks * d.K, c2);
   };
-  if (nt <= 512) go(k_dec_attend_fast<T, D, 512, 16>);
-  else if (HW <= 4) go(k_dec_attend_fast<T, D, 1024, 4>);
-  else go(k_dec_attend_fast<T, D, 1024, 16>);
+  if (d.K <= 8) go(k_dec_attend_heads<T, D, 4, 512>);
+  else go(k_dec_attend_heads<T, D, 4, 1024>);
 }
 
 hipError_t launch_decode_fast(const Dims& d, const void* q, const void* qs, const void* Kc,

@@ -144,10 +144,11 @@ hsa_status_t hsa_fwd(const hsa_problem_t* p, const void* Q, const void* K, const
  * complete key gradient when Kslc was pooled from K.
  * HSA_BWD_AFTER_FWD: the caller ran hsa_fwd with the same problem, Q, K, idx and w on this
  * same workspace (sized for hsa_bwd, which is at least the forward's size) and has not
- * touched it since.  The forward leaves at the start of its workspace the per-tile job lists,
- * the key rows in matrix-core operand order and every (token, head, slot)'s softmax
- * normaliser; the backward then skips rebuilding those it uses and takes its probabilities
- * from the normaliser.  The results equal those without the flag up to fp32 rounding.  When the
+ * touched it since.  The forward leaves at the start of its workspace every (token, head,
+ * slot)'s softmax normaliser and either the chunk -> (token, slot) inverse index (up to 16384
+ * chunks) or the token tiles' job lists and the key rows in matrix-core operand order; the
+ * backward then skips rebuilding those it uses and takes its probabilities from the
+ * normaliser.  The results equal those without the flag up to fp32 rounding.  When the
  * problem uses the plain kernels (fp32, HSA_FLAG_GENERIC, or shapes outside the matrix-core
  * kernels) the flag has no effect.  Passing it without that forward call gives undefined
  * results. */
