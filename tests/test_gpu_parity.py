@@ -336,6 +336,33 @@ def test_full_backward_sampled(hsa, dev):
     compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=tm, chunk_mask=cm)
 
 
+def test_full_step_sampled(hsa, dev):
+    """The bench's step at its full size and launch configuration (fwd_16k: select, forward
+    and backward on one workspace with HSA_BWD_AFTER_FWD), on sampled tokens and chunks."""
+    from chunk_sparse_attention_amd import _lib
+    wl = workloads.WORKLOADS["fwd_16k"]
+    say("case full step fwd_16k")
+    x = workloads.make_inputs(wl, seed=0)
+    Q, K, V, Qs = (x[k].to(dev) for k in ("Q", "K", "V", "Qs"))
+    dO = x["dO"].to(dev)
+    prob = hsa.problem(wl.B, wl.L, wl.Hq, wl.Hkv, wl.D, wl.K, wl.dtype)
+    ws = hsa.workspace(_lib.HSA_OP_BWD, prob, dev)
+    Kslc, idx, score, w = hsa.select(Qs, K, wl.K)
+    O = hsa.fwd(Q, K, V, idx, w, ws=ws)
+    grads = hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, ws=ws, after_fwd=True)
+    torch.cuda.synchronize()
+    g = dict(Q=Q, K=K, V=V, Qs=Qs, Kslc=Kslc, idx=idx, score=score, w=w, O=O)
+    orc = oracle.get()
+    f, diff, _ = compare_forward(orc, x, wl, g)
+    tm = _sample_rows(wl, 32, seed=4)
+    rng = np.random.default_rng(5)
+    cm = np.zeros((wl.B, wl.nC), np.uint8)
+    for b in range(wl.B):
+        cm[b, rng.choice(wl.nC, size=4, replace=False)] = 1
+        cm[b, [0, wl.nC - 1]] = 1
+    compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=tm, chunk_mask=cm)
+
+
 def test_full_decode(hsa, dev):
     wl = workloads.WORKLOADS["decode_1m"]
     say("case full decode decode_1m")
