@@ -339,7 +339,8 @@ k_bwd_chunk_mfma(
   constexpr int D = 64, TPJ = 16 / G, KS = D / 32, DT = D / 16, NW = 2, NT = 64 * NW;
   constexpr int KROW = D + 8, WREGION = 2 * 16 * KROW + 64 * 16;
   __shared__ __attribute__((aligned(16))) uint16_t sm[2 * 64 * KROW + NW * WREGION];
-  __shared__ int tok_l[kBwdSeg], k_l[kBwdSeg];
+  __shared__ int tok_l[kBwdSeg];
+  __shared__ int64_t eo_l[kBwdSeg];  // the entry's (b, t, g, slot) index
   __shared__ float w_l[kBwdSeg];
   const int64_t sidx = blockIdx.x % max_seg;
   const int bg = (int)(blockIdx.x / max_seg);
@@ -365,9 +366,10 @@ k_bwd_chunk_mfma(
   for (int i = tid; i < ne; i += NT) {
     const int val = ent[i];
     const int t = val / Kn, k = val % Kn;
+    const int64_t eo = ((int64_t)(b * L + t) * Hkv + g) * Kn + k;
     tok_l[i] = t;
-    k_l[i] = k;
-    w_l[i] = w[((b * L + t) * Hkv + g) * Kn + k];
+    eo_l[i] = eo;
+    w_l[i] = w[eo];
   }
   for (int i = tid; i < 64 * (D / 8); i += NT) {
     const int key = i / (D / 8), d = (i % (D / 8)) * 8;
@@ -386,22 +388,25 @@ k_bwd_chunk_mfma(
   __syncthreads();
 
   // this lane's query row of job j (a padding row repeats the job's first selector) and, with
-  // HL, the forward's normaliser of the lane's four output rows 4*blk + i
+  // HL, the forward's normaliser of the lane's four output rows 4*blk + i: four consecutive
+  // heads of one selector (G >= 4), one 16-byte load
+  const size_t row_off = (b * L * Hq + (size_t)g * G + qs_head) * D + 8 * blk;
+  const size_t tok_stride = (size_t)Hq * D;
   auto load_rows = [&](int ej, bf16x8 (&qa)[KS], bf16x8 (&da)[KS], float (&le)[4]) {
     const int n_here = min(TPJ, ne - ej);
-    const int t = tok_l[ej + (qs_sel < n_here ? qs_sel : 0)];
-    const size_t qoff = ((b * L + t) * Hq + (size_t)g * G + qs_head) * D;
+    const size_t qoff = row_off + (size_t)tok_l[ej + (qs_sel < n_here ? qs_sel : 0)] * tok_stride;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qa[ks] = ld_bf16x8(Q + qoff + 32 * ks + 8 * blk);
-      da[ks] = ld_bf16x8(dO + qoff + 32 * ks + 8 * blk);
+      qa[ks] = ld_bf16x8(Q + qoff + 32 * ks);
+      da[ks] = ld_bf16x8(dO + qoff + 32 * ks);
     }
     if (HL) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * blk + i, s2 = r / G, e = ej + (s2 < n_here ? s2 : 0);
-        le[i] = lse_in[(((b * L + tok_l[e]) * Hkv + g) * Kn + k_l[e]) * G + r % G];
-      }
+      const int s2 = (4 * blk) / G, e = ej + (s2 < n_here ? s2 : 0);
+      const float4 v = *reinterpret_cast<const float4*>(lse_in + eo_l[e] * G + (4 * blk) % G);
+      le[0] = v.x;
+      le[1] = v.y;
+      le[2] = v.z;
+      le[3] = v.w;
     }
   };
   bf16x8 qn[KS], dn[KS];
@@ -473,8 +478,7 @@ k_bwd_chunk_mfma(
       if (G >= 8) dsel += __shfl_xor(dsel, 16);
       if (G == 16) dsel += __shfl_xor(dsel, 32);
       const int s = (4 * blk) / G;
-      if (col == 0 && (4 * blk) % G == 0 && s < n_here)
-        dw_out[((b * L + tok_l[ej + s]) * Hkv + g) * Kn + k_l[ej + s]] = dsel;
+      if (col == 0 && (4 * blk) % G == 0 && s < n_here) dw_out[eo_l[ej + s]] = dsel;
     }
     // dV^T += dO^T (w P), dK^T += Q^T dS  (k = the 16 query rows, 4 per lane block), the
     // transposed operands read from LDS with the transposing read; dS^T goes to LDS for dQ
@@ -519,11 +523,10 @@ k_bwd_chunk_mfma(
                                dsT, dq[dt]);
     }
     if (qs_sel < n_here) {  // lane column = query row col: its edge's partial at d = 16*dt + 4*blk
-      const int e = ej + qs_sel;
-      bf16* dst = dq_part + ((((b * L + tok_l[e]) * Hkv + g) * Kn + k_l[e]) * G + qs_head) * D;
+      bf16* dst = dq_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 4 * blk;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<s16x4*>(dst + 16 * dt + 4 * blk) = pack_bf16x4(dq[dt]);
+        *reinterpret_cast<s16x4*>(dst + 16 * dt) = pack_bf16x4(dq[dt]);
     }
     wave_lds_sync();  // ql/dl/sdl reuse by the next job
   }
