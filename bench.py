@@ -132,7 +132,7 @@ def roofline(name: str, counts: dict, avg_ms: float, traffic) -> dict:
 
 
 # kernel function name -> kernel class of the launch timer; the first matching prefix wins.
-# A class launch is one host call: the inverse index runs three kernels per launch and the
+# A class launch is one host call: the inverse index runs four kernels per launch and the
 # fused backward's token phase two; the others are one kernel each.
 KERNEL_CLASS_OF = (("k_bwd_p2_reduce", "bwd_reduce"), ("k_bwd_p2", "bwd_p2"),
                    ("k_bwd_chunk", "bwd_p2"), ("k_bwd_p1", "bwd_p1"), ("k_bwd_tok", "bwd_p1"),
@@ -142,7 +142,7 @@ KERNEL_CLASS_OF = (("k_bwd_p2_reduce", "bwd_reduce"), ("k_bwd_p2", "bwd_p2"),
                    ("k_pool", "pool"), ("k_dec_scan", "decode_scan"),
                    ("k_dec_attend", "decode_attend"))
 # kernels that run inside another kernel's class launch (not counted as launches)
-SECONDARY_KERNELS = {"k_inv_count", "k_inv_scan", "k_bwd_dks"}
+SECONDARY_KERNELS = {"k_inv_count", "k_inv_colscan", "k_inv_scan", "k_bwd_dks"}
 
 
 def kernel_class(kernel_name: str):
