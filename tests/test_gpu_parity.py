@@ -317,6 +317,18 @@ def test_full_forward_sampled(hsa, dev, name):
     compare_forward(oracle.get(), x, wl, g, row_mask=mask)
 
 
+def test_long_sequence_token_tile_forward(hsa, dev):
+    """Past 16384 chunks the forward uses its token-tile kernels (job lists per token tile,
+    rounds of jobs, LDS accumulation): parity on sampled rows of a sequence of 16400 chunks."""
+    wl = W("bf16_16400_chunks", 1, 64 * 16400 + 17, 8, 2, 64, 64, 4, torch.bfloat16)
+    say("case token-tile forward", wl)
+    x = workloads.make_inputs(wl, seed=6, with_grad=False)
+    g = gpu_forward(hsa, x, wl, dev)
+    torch.cuda.synchronize()
+    mask = _sample_rows(wl, 96, seed=7)
+    compare_forward(oracle.get(), x, wl, g, row_mask=mask)
+
+
 def test_full_backward_sampled(hsa, dev):
     wl = workloads.WORKLOADS["bwd_16k"]
     say("case full backward bwd_16k")
