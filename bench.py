@@ -12,8 +12,9 @@ timed region starts.  value = B*L tokens per step / seconds per step.
                     [--no-decode]
 
 The roofline object describes the kernel that takes the most time per step.  Its duration is
-the average launch time over the timed steps, from the HIP events libhsa.so records around
-each of its launches on the launch's own stream (hsa_timer_enable / hsa_timer_read); its
+the average launch time over a second pass of as many steps, run after the timed ones, from
+the HIP events libhsa.so records around each of its launches on the launch's own stream
+(hsa_timer_enable / hsa_timer_read); its
 algorithmic bytes and flops per launch are the workload's, from kernel_counts().  "kernels"
 holds the same for every kernel class, "secondary" the select+fwd pass of the L=65536, d=128
 workload, "decode" the 1M-context decode step.  cpu_baseline times the CPU oracle (test
@@ -468,17 +469,23 @@ def main() -> int:
         return 0
 
     log(f"bench: timing {args.steps} steps")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    hsa.timer_enable(True)
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # the same number of steps again, outside the timed region, for the per-entry and
+    # per-kernel split (their event records take a little time of their own)
+    log("bench: per-kernel pass")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    hsa.timer_enable(True)
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     hsa.timer_enable(False)
     ktimes = hsa.timer_read()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
     names = ["hsa_select", "hsa_fwd", "hsa_bwd"]
     entry_ms = {n: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps, 4)
                 for j, n in enumerate(names)}
