@@ -661,19 +661,21 @@ __global__ void __launch_bounds__(256) k_bwd_tok(
 }
 
 // dKslc partial of one segment of a chunk's selector list (D = 64, one feature per lane):
-// sel_scale * sum over the segment's selectors, in list order, of ds * Qs.
-__global__ void __launch_bounds__(64) k_bwd_dks(
+// sel_scale * sum over the segment's selectors of ds * Qs.  Four waves take a quarter of the
+// list each, in list order; their sums are added in wave order.
+__global__ void __launch_bounds__(256) k_bwd_dks(
     const bf16* __restrict__ Qs, const float* __restrict__ ds, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ seg_start,
     const int32_t* __restrict__ seg_chunk, const int32_t* __restrict__ n_seg,
     float* __restrict__ part_dks, int L, int Hkv, int Kn, int nC, int seg, int64_t max_seg,
     float sel_scale) {
-  constexpr int D = 64;
+  constexpr int D = 64, NW = 4;
   __shared__ int tok_l[kBwdSeg];
   __shared__ float ds_l[kBwdSeg];
+  __shared__ float wsum[NW][D];
   const int64_t sidx = blockIdx.x % max_seg;
   const int bg = (int)(blockIdx.x / max_seg);
-  if (sidx >= n_seg[bg]) return;
+  if (sidx >= n_seg[bg]) return;  // whole block
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const int c = seg_chunk[(size_t)bg * max_seg + sidx];
@@ -682,26 +684,32 @@ __global__ void __launch_bounds__(64) k_bwd_dks(
   const int e0 = off[c] + (int)(sidx - ss[c]) * seg;
   const int ne = min(off[c + 1], e0 + seg) - e0;
   const int32_t* ent = entries + (size_t)bg * L * Kn + e0;
-  const int lane = threadIdx.x;
-  for (int i = lane; i < ne; i += 64) {
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  for (int i = tid; i < ne; i += 64 * NW) {
     const int val = ent[i];
     const int t = val / Kn, k = val % Kn;
     tok_l[i] = t;
     ds_l[i] = ds[((b * L + t) * Hkv + g) * Kn + k];
   }
   __syncthreads();
+  const bf16* qs = Qs + (b * L * Hkv + g) * D + lane;
+  const size_t tstride = (size_t)Hkv * D;
+  const int i0 = ne * wave / NW, i1 = ne * (wave + 1) / NW;
   float a = 0.0f;
-  int i = 0;
-  for (; i + 16 <= ne; i += 16) {  // sixteen rows in flight, summed in list order
-    float v[16];
+  int i = i0;
+  for (; i + 8 <= i1; i += 8) {  // eight rows in flight, summed in list order
+    float v[8];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      v[u] = to_f32(Qs[((b * L + tok_l[i + u]) * Hkv + g) * D + lane]);
+    for (int u = 0; u < 8; ++u) v[u] = to_f32(qs[(size_t)tok_l[i + u] * tstride]);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) a += ds_l[i + u] * v[u];
+    for (int u = 0; u < 8; ++u) a += ds_l[i + u] * v[u];
   }
-  for (; i < ne; ++i) a += ds_l[i] * to_f32(Qs[((b * L + tok_l[i]) * Hkv + g) * D + lane]);
-  part_dks[((size_t)bg * max_seg + sidx) * D + lane] = a * sel_scale;
+  for (; i < i1; ++i) a += ds_l[i] * to_f32(qs[(size_t)tok_l[i] * tstride]);
+  wsum[wave][lane] = a;
+  __syncthreads();
+  if (wave == 0)
+    part_dks[((size_t)bg * max_seg + sidx) * D + lane] =
+        (((wsum[0][lane] + wsum[1][lane]) + wsum[2][lane]) + wsum[3][lane]) * sel_scale;
 }
 
 bool bwd_mfma_supported(const Dims& d) {
@@ -784,7 +792,7 @@ static hipError_t launch_bwd_fused(const Dims& d, const BwdLayout& lay, const vo
     else if (d.G == 8) go(k_bwd_tok<8>);
     else go(k_bwd_tok<16>);
     if (d.nC > 0)
-      k_bwd_dks<<<dim3((unsigned)(BG * lay.max_seg)), 64, 0, s>>>(
+      k_bwd_dks<<<dim3((unsigned)(BG * lay.max_seg)), 256, 0, s>>>(
           (const bf16*)Qs, (const float*)(ws + lay.ds), (const int32_t*)(ws + lay.offsets),
           (const int32_t*)(ws + lay.entries), (const int32_t*)(ws + lay.seg_start),
           (const int32_t*)(ws + lay.seg_chunk), (const int32_t*)(ws + lay.n_seg),
