@@ -508,15 +508,30 @@ __global__ void __launch_bounds__(128) k_bwd_p2_seg(
   }
 }
 
-// One block per chunk (including the incomplete tail chunk, whose rows get zero): sum the
-// chunk's segment partials in segment order, fold dKslc/S into dK if asked, store.
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float4 v) {
+  *reinterpret_cast<float4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float4 v) {
+  const uint32_t lo = (uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+
+// One block per (b, g, chunk), the incomplete tail chunk included (its rows get zero): dK and
+// dV = the sums of the chunk's segment partials in segment order, dKslc the same over the
+// dKslc partials; with fold, dK rows also get dKslc / S.  Each thread
+// owns four features of one key row and sums the dKslc partials of its features itself, so no
+// phase waits for another.
 template <typename T>
 __global__ void __launch_bounds__(256) k_bwd_p2_reduce(
     const float* __restrict__ part_dk, const float* __restrict__ part_dv,
     const float* __restrict__ part_dks, const int32_t* __restrict__ seg_start, T* __restrict__ dK,
     T* __restrict__ dV, float* __restrict__ dKslc, int L, int Hkv, int D, int S, int nC,
     int n_chunks_all, int64_t max_seg, int fold) {
-  __shared__ float dks[128];
   const int c = blockIdx.x % n_chunks_all;
   const int bg = blockIdx.x / n_chunks_all;
   const int g = bg % Hkv;
@@ -536,49 +551,47 @@ __global__ void __launch_bounds__(256) k_bwd_p2_reduce(
   const int32_t* ss = seg_start + (size_t)bg * (nC + 1);
   const int s0 = ss[c], s1 = ss[c + 1];
   const size_t pb = (size_t)bg * max_seg;
-  for (int e = threadIdx.x; e < D; e += blockDim.x) {
-    float a = 0.0f;
-    for (int s = s0; s < s1; ++s) a += part_dks[(pb + s) * D + e];
-    dks[e] = a;
-    if (dKslc) dKslc[((b * nC + c) * Hkv + g) * D + e] = a;
-  }
-  __syncthreads();
   for (int i = threadIdx.x; i < kChunk * D / 4; i += blockDim.x) {
     const int j = (4 * i) / D, e = (4 * i) % D;
-    float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak;
+    float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak, as = ak;
     const float* pk = part_dk + ((pb + s0) * kChunk + j) * D + e;
     const float* pv = part_dv + ((pb + s0) * kChunk + j) * D + e;
+    const float* ps = part_dks + (pb + s0) * D + e;
     const size_t step = (size_t)kChunk * D;
     int s = s0;
     for (; s + 4 <= s1; s += 4) {  // four segments' loads in flight, summed in segment order
-      float4 k4[4], v4[4];
+      float4 k4[4], v4[4], d4[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         k4[u] = *reinterpret_cast<const float4*>(pk + (size_t)(s - s0 + u) * step);
         v4[u] = *reinterpret_cast<const float4*>(pv + (size_t)(s - s0 + u) * step);
+        d4[u] = *reinterpret_cast<const float4*>(ps + (size_t)(s - s0 + u) * D);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         ak.x += k4[u].x; ak.y += k4[u].y; ak.z += k4[u].z; ak.w += k4[u].w;
         av.x += v4[u].x; av.y += v4[u].y; av.z += v4[u].z; av.w += v4[u].w;
+        as.x += d4[u].x; as.y += d4[u].y; as.z += d4[u].z; as.w += d4[u].w;
       }
     }
     for (; s < s1; ++s) {
       const float4 k1 = *reinterpret_cast<const float4*>(pk + (size_t)(s - s0) * step);
       const float4 v1 = *reinterpret_cast<const float4*>(pv + (size_t)(s - s0) * step);
+      const float4 d1 = *reinterpret_cast<const float4*>(ps + (size_t)(s - s0) * D);
       ak.x += k1.x; ak.y += k1.y; ak.z += k1.z; ak.w += k1.w;
       av.x += v1.x; av.y += v1.y; av.z += v1.z; av.w += v1.w;
+      as.x += d1.x; as.y += d1.y; as.z += d1.z; as.w += d1.w;
     }
+    if (j == 0 && dKslc)
+      *reinterpret_cast<float4*>(dKslc + ((b * nC + c) * Hkv + g) * D + e) = as;
     if (fold) {
-      ak.x += dks[e] / (float)S;
-      ak.y += dks[e + 1] / (float)S;
-      ak.z += dks[e + 2] / (float)S;
-      ak.w += dks[e + 3] / (float)S;
+      ak.x += as.x / (float)S;
+      ak.y += as.y / (float)S;
+      ak.z += as.z / (float)S;
+      ak.w += as.w / (float)S;
     }
-    T* kd = dK + cbase + j * kvstride + e;
-    T* vd = dV + cbase + j * kvstride + e;
-    kd[0] = from_f32<T>(ak.x); kd[1] = from_f32<T>(ak.y); kd[2] = from_f32<T>(ak.z); kd[3] = from_f32<T>(ak.w);
-    vd[0] = from_f32<T>(av.x); vd[1] = from_f32<T>(av.y); vd[2] = from_f32<T>(av.z); vd[3] = from_f32<T>(av.w);
+    store4<T>(dK + cbase + j * kvstride + e, ak);
+    store4<T>(dV + cbase + j * kvstride + e, av);
   }
 }
 
