@@ -10,9 +10,10 @@
 
 namespace hsa {
 
-// Kslc[b,c,g,e] = mean_j K[b, c*S+j, g, e]: one thread per output element; the sum runs in
-// fp64 in row order so the result is the exact mean for any bf16/fp32 chunk in practice,
-// rounded once to the storage type.  Consecutive threads read consecutive e (coalesced).
+// Kslc[b,c,g,e] = mean_j K[b, c*S+j, g, e] (S = 64): one thread per output element; the sum
+// runs in fp64 in row order so the result is the exact mean for any bf16/fp32 chunk in
+// practice, rounded once to the storage type.  Consecutive threads read consecutive e
+// (coalesced), and sixteen rows' loads are in flight at a time.
 template <typename T>
 __global__ void __launch_bounds__(256) k_pool(const T* __restrict__ K, T* __restrict__ Kslc,
                                               int L, int Hkv, int D, int S, int nC,
@@ -25,11 +26,18 @@ __global__ void __launch_bounds__(256) k_pool(const T* __restrict__ K, T* __rest
   r /= Hkv;
   int c = (int)(r % nC);
   size_t b = r / nC;
-  const T* src = K + ((b * L + (size_t)c * S) * Hkv + g) * D + e;
-  size_t stride = (size_t)Hkv * D;
+  const T* src = K + ((b * L + (size_t)c * kChunk) * Hkv + g) * D + e;
+  const size_t stride = (size_t)Hkv * D;
+  // sixteen rows' loads in flight at a time; the sum stays in row order
   double sum = 0.0;
-  for (int j = 0; j < S; ++j) sum += (double)to_f32(src[j * stride]);
-  Kslc[i] = from_f64<T>(sum / S);
+  for (int j0 = 0; j0 < kChunk; j0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = to_f32(src[(size_t)(j0 + u) * stride]);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) sum += (double)v[u];
+  }
+  Kslc[i] = from_f64<T>(sum / kChunk);
 }
 
 hipError_t launch_pool(const Dims& d, const void* K, void* Kslc, hipStream_t s) {
