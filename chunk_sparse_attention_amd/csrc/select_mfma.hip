@@ -79,6 +79,7 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
                                                      int Kt, int nC, int BG, double sel_scale) {
   constexpr int KS = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t qraw[64][D + 8];  // the tile's Qs rows
+  __shared__ __attribute__((aligned(16))) uint16_t kl[64][D + 8];    // a group of 64 chunks
   __shared__ int cnt[64];
   __shared__ int fall[64];
   __shared__ int candl[64][kSelCap];
@@ -117,18 +118,36 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
   }
   q2 = rows4_sum(q2);
 
-  // approximate scores of chunks c0 .. c0+63 against the wave's 16 tokens: lane holds
-  // chunks c0 + 16*t4 + 4*blk + i of its token; k2 = |k|^2 of chunk c0 + 16*t4 + col
-  auto approx = [&](int c0, f32x4 (&sacc)[4], float& k2max) {
+  // The block stages each group of 64 chunk keys in LDS; every thread holds D/32 16-byte
+  // pieces of the next group in registers while the current one is scored.
+  constexpr int NP = D / 32;
+  uint4 pre[NP];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int i = tid + 256 * u, r = i / (D / 8), e = (i % (D / 8)) * 8;
+      pre[u] = c0 + r < m ? *reinterpret_cast<const uint4*>(kbase + (size_t)(c0 + r) * Hkv * D + e)
+                          : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stage = [&]() {  // between two block barriers
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int i = tid + 256 * u, r = i / (D / 8), e = (i % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(&kl[r][e]) = pre[u];
+    }
+  };
+
+  // approximate scores of chunks c0 .. c0+63 (staged) against the wave's 16 tokens: lane
+  // holds chunks c0 + 16*t4 + 4*blk + i of its token; k2 = |k|^2 of chunk c0 + 16*t4 + col
+  auto approx = [&](f32x4 (&sacc)[4], float& k2max) {
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       sacc[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int c = c0 + 16 * t4 + col;
       float k2 = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = c < m ? ld_bf16x8(kbase + (size_t)c * Hkv * D + 32 * ks + 8 * blk)
-                                : zero_bf16x8();
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kl[16 * t4 + col][32 * ks + 8 * blk]);
         k2 += sq8(ka);
         sacc[t4] = mfma_16x16x32(ka, qb[ks], sacc[t4]);
       }
@@ -144,9 +163,14 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
   for (int i = 0; i < KL; ++i) top[i] = -__builtin_inff();
   float k2max = 0.0f;
   bool bad = (__float_as_uint(q2) & 0x7f800000u) == 0x7f800000u;
+  if (m > 0) fetch(0);
   for (int c0 = 0; c0 < m; c0 += 64) {
+    __syncthreads();  // the previous group is no longer read
+    stage();
+    __syncthreads();
+    if (c0 + 64 < m) fetch(c0 + 64);
     f32x4 sacc[4];
-    approx(c0, sacc, k2max);
+    approx(sacc, k2max);
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
@@ -187,10 +211,15 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
   if (blk == 0 && ((badmask >> col) & 0x0001000100010001ull)) fall[tl] = 1;
 
   // 2. collect the chunks at or above the threshold
+  if (m > 0) fetch(0);
   for (int c0 = 0; c0 < m; c0 += 64) {
+    __syncthreads();  // the previous group is no longer read
+    stage();
+    __syncthreads();
+    if (c0 + 64 < m) fetch(c0 + 64);
     f32x4 sacc[4];
     float unused = 0.0f;
-    approx(c0, sacc, unused);
+    approx(sacc, unused);
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
