@@ -375,6 +375,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the 1M-context decode step")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step (an informational figure)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="profiling aid: with --only, first copy this many MiB once with a plain "
                          "device copy (the scale reference for HBM byte counters)")
@@ -476,6 +478,27 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # the same step captured once in a HIP graph and replayed as many times: how much of the
+    # step is launch overhead (reported beside the eager figure, not as it)
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        del graph
+        log(f"bench: graph replay {graph_ms:.4f} ms per step")
     # the same number of steps again, outside the timed region, for the per-entry and
     # per-kernel split (their event records take a little time of their own)
     log("bench: per-kernel pass")
@@ -522,6 +545,7 @@ def main() -> int:
                    "global_batch": wl.B, "seq_len": wl.L, "parallelism": "single GPU",
                    "kernels": "generic" if gen else "default"},
         "roofline": roof,
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "entry_ms": entry_ms,
         "kernels": kern,
     }

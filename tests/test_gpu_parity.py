@@ -186,6 +186,41 @@ def test_given_selection(hsa, dev, wl, generic):
         assert v <= tol, (k, v)
 
 
+def test_graph_replay_matches_eager(hsa, dev):
+    """The whole step (select, forward, backward after forward on one workspace) captured in a
+    HIP graph: every replay, with eager work between replays, equals the eager step bitwise."""
+    from chunk_sparse_attention_amd import _lib
+    wl = SMALL[1]
+    say("case graph replay", wl)
+    x = workloads.make_inputs(wl, seed=8)
+    Q, K, V, Qs, dO = (x[k].to(dev) for k in ("Q", "K", "V", "Qs", "dO"))
+    prob = hsa.problem(wl.B, wl.L, wl.Hq, wl.Hkv, wl.D, wl.K, wl.dtype)
+    ws = hsa.workspace(_lib.HSA_OP_BWD, prob, dev)
+
+    def step():
+        Kslc, idx, score, w = hsa.select(Qs, K, wl.K)
+        O = hsa.fwd(Q, K, V, idx, w, ws=ws)
+        g = hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, ws=ws, after_fwd=True)
+        return [idx, score, w, O] + [g[k] for k in ("dQ", "dK", "dV", "dQs", "dKslc")]
+
+    eager = [t.clone() for t in step()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        static = step()
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(static, eager):
+            assert torch.equal(a, b)
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_backward_bitwise_reproducible(hsa, dev):
     wl = SMALL[1]
     x = workloads.make_inputs(wl, seed=5)
