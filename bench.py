@@ -16,8 +16,9 @@ the average launch time over a second pass of as many steps, run after the timed
 the HIP events libhsa.so records around each of its launches on the launch's own stream
 (hsa_timer_enable / hsa_timer_read); its
 algorithmic bytes and flops per launch are the workload's, from kernel_counts().  "kernels"
-holds the same for every kernel class, "secondary" the select+fwd pass of the L=65536, d=128
-workload, "decode" the 1M-context decode step.  cpu_baseline times the CPU oracle (test
+holds the same for every kernel class, "secondary" the select+fwd+bwd pass of the L=65536,
+d=128 workload (tokens/s of the whole pass and of select+fwd), "decode" the 1M-context decode
+step.  cpu_baseline times the CPU oracle (test
 infrastructure) on the same workload; it is a reported baseline, not the target.
 """
 from __future__ import annotations
@@ -59,10 +60,10 @@ def causal_candidates(wl) -> int:
 
 
 def fused_backward(wl, generic: bool) -> bool:
-    """The library's bf16 D=64 backward: chunk phase with per-edge dQ partials, then a token
-    phase (no token-tile phase)."""
-    return (not generic and str(wl.dtype).endswith("bfloat16") and wl.D == 64
-            and wl.G in (4, 8, 16))
+    """The library's bf16 matrix-core backward: chunk phase with per-edge dQ partials, then a
+    token phase."""
+    return (not generic and str(wl.dtype).endswith("bfloat16") and wl.D in (64, 128)
+            and wl.G in (4, 8, 16) and wl.nC < 32768)
 
 
 def chunked_forward(wl, generic: bool) -> bool:
@@ -552,45 +553,55 @@ def main() -> int:
 
     if not args.no_secondary:
         wl2 = workloads.WORKLOADS["fwd_64k"]
-        log(f"bench: secondary {wl2.name} select+fwd")
-        x2 = workloads.make_inputs(wl2, seed=0, with_grad=False)
-        Q2, K2, V2, Qs2 = (x2[k].to(dev) for k in ("Q", "K", "V", "Qs"))
+        log(f"bench: secondary {wl2.name} select+fwd+bwd")
+        x2 = workloads.make_inputs(wl2, seed=0)
+        Q2, K2, V2, Qs2, dO2 = (x2[k].to(dev) for k in ("Q", "K", "V", "Qs", "dO"))
         prob2 = hsa.problem(wl2.B, wl2.L, wl2.Hq, wl2.Hkv, wl2.D, wl2.K, wl2.dtype, generic=gen)
-        ws2 = hsa.workspace(_lib.HSA_OP_FWD, prob2, dev)
+        ws2 = hsa.workspace(_lib.HSA_OP_BWD, prob2, dev)
         O2 = torch.empty_like(Q2)
-        for _ in range(2):
-            _, i2, _, w2 = hsa.select(Qs2, K2, wl2.K, generic=gen)
-            hsa.fwd(Q2, K2, V2, i2, w2, generic=gen, ws=ws2, out=O2)
-        torch.cuda.synchronize()
-        n2 = int((i2 >= 0).sum().item())
-        reps = max(3, args.steps // 4)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        ts, tf = 0.0, 0.0
-        hsa.timer_enable(True)
-        for _ in range(reps):
-            e[0].record()
-            _, i2, _, w2 = hsa.select(Qs2, K2, wl2.K, generic=gen)
+
+        def step2():
+            Kslc2, i2, sc2, w2 = hsa.select(Qs2, K2, wl2.K, generic=gen)
             e[1].record()
             hsa.fwd(Q2, K2, V2, i2, w2, generic=gen, ws=ws2, out=O2)
             e[2].record()
+            hsa.bwd(Q2, K2, V2, Qs2, Kslc2, i2, sc2, w2, dO2, generic=gen, ws=ws2,
+                    after_fwd=True)
+            return i2
+
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for _ in range(2):
+            i2 = step2()
+        torch.cuda.synchronize()
+        n2 = int((i2 >= 0).sum().item())
+        reps = max(3, args.steps // 4)
+        ts, tf, tb = 0.0, 0.0, 0.0
+        hsa.timer_enable(True)
+        for _ in range(reps):
+            e[0].record()
+            step2()
+            e[3].record()
             torch.cuda.synchronize()
             ts += e[0].elapsed_time(e[1])
             tf += e[1].elapsed_time(e[2])
+            tb += e[2].elapsed_time(e[3])
         hsa.timer_enable(False)
         kt2 = hsa.timer_read()
         ts /= reps
         tf /= reps
+        tb /= reps
         c2 = kernel_counts(wl2, n2, fused_backward(wl2, gen), chunked_forward(wl2, gen))
         k2 = {name: roofline(name, c2[name], total / n, None)
               for name, (n, total) in kt2.items() if n}
         out["secondary"] = {
-            "workload": f"{wl2.name}: select+fwd B={wl2.B} L={wl2.L} Hq={wl2.Hq} "
+            "workload": f"{wl2.name}: select+fwd+bwd B={wl2.B} L={wl2.L} Hq={wl2.Hq} "
                         f"Hkv={wl2.Hkv} d={wl2.D} K={wl2.K}",
-            "select_ms": round(ts, 4), "fwd_ms": round(tf, 4),
-            "tokens_per_s": round(wl2.B * wl2.L / ((ts + tf) / 1e3), 1),
+            "select_ms": round(ts, 4), "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4),
+            "tokens_per_s": round(wl2.B * wl2.L / ((ts + tf + tb) / 1e3), 1),
+            "fwd_tokens_per_s": round(wl2.B * wl2.L / ((ts + tf) / 1e3), 1),
             "kernels": k2,
         }
-        del Q2, K2, V2, Qs2, x2, O2, ws2
+        del Q2, K2, V2, Qs2, dO2, x2, O2, ws2
 
     if not args.no_decode:
         out["decode"] = run_decode(hsa, _lib, workloads, dev, gen, reps=50)

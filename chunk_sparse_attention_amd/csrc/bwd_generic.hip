@@ -20,7 +20,7 @@ IndexLayout index_layout(const Dims& d, size_t& o) {
   while ((d.L + tt - 1) / tt > 256) tt *= 2;
   x.tile_tokens = tt;
   x.n_tiles = (d.L + tt - 1) / tt;
-  x.seg = (fwd_chunked(d) || bwd_fused(d)) ? kBwdSeg : 128;
+  x.seg = (fwd_chunked(d) || bwd_mfma_supported(d)) ? kBwdSeg : 128;
   const int64_t bg = (int64_t)d.B * d.Hkv;
   const int64_t E = (int64_t)d.L * d.K;  // entry capacity per (b, g)
   x.max_seg = (E + x.seg - 1) / x.seg + d.nC;
@@ -42,8 +42,6 @@ IndexLayout index_layout(const Dims& d, size_t& o) {
 BwdLayout bwd_layout(const Dims& d) {
   BwdLayout l{};
   const FwdState st = fwd_state(d);  // the forward's state comes first
-  l.prep = st.prep;
-  l.kop = st.kop;
   l.lse = st.lse;
   size_t o = st.total;
   auto take = [&](size_t bytes) {
@@ -51,7 +49,7 @@ BwdLayout bwd_layout(const Dims& d) {
     o = align256(o + bytes);
     return at;
   };
-  const bool fused = bwd_fused(d), chunked = fwd_chunked(d);
+  const bool chunked = fwd_chunked(d);
   // the chunk-major forward builds the index in its state; otherwise it follows the state
   static_cast<IndexLayout&>(l) = chunked ? st.ix : index_layout(d, o);
   const int64_t bg = (int64_t)d.B * d.Hkv;
@@ -61,19 +59,10 @@ BwdLayout bwd_layout(const Dims& d) {
   l.part_dk = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
   l.part_dv = take(sizeof(float) * bg * l.max_seg * kChunk * d.D);
   l.part_dks = take(sizeof(float) * bg * l.max_seg * d.D);
-  if (fused) {
+  if (bwd_mfma_supported(d)) {
     // per (token, group, slot, head): the edge's dQ contribution (the chunk-major forward's
     // partials' buffer, free once the forward has summed them)
     l.dq_part = chunked ? st.part : take(sizeof(uint16_t) * bg * E * d.G * d.D);
-  } else {
-    if (chunked && bwd_mfma_supported(d)) {  // the token-tile backward's own job lists
-      l.prep = take(tile_prep_bytes(d));
-      l.kop = take(chunk_ops_bytes(d));
-    }
-    l.kt = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
-    l.vop = take(sizeof(uint16_t) * bg * d.nC * kChunk * d.D);
-    // per (token, group, slot, head): D = <dO, O_k> (the normaliser is in the state prefix)
-    l.dd = take(sizeof(float) * bg * E * d.G);
   }
   l.total = o;
   return l;

@@ -7,319 +7,34 @@
 // 层次化稀疏注意力（HSA）, 端到端学习).
 //
 // The gradients of queries, keys, values, chunk weights and selection scores are the same as
-// that two-phase plan's; the order of the work differs with the head dimension.
-//
-// D = 64 (fused): the chunk phase does all the per-edge work.  Per segment of a chunk's
-// selector list (the chunk -> (token, slot) index) and job of 16 query rows:
+// that two-phase plan's; the order of the work differs.  The chunk phase does all the per-edge
+// work.  Per segment of a chunk's selector list (the chunk -> (token, slot) index) and job of
+// 16 query rows:
 //   S = Q K_c^T, dP = dO V_c^T; P = softmax1(S); D = sum_keys P.dP; dS = w P (dP - D)
 //   dV^T += dO^T (w P), dK^T += Q^T dS     (MFMA, registers, fp32 partial per segment)
 //   dQ_k^T = K_c^T dS^T                     (MFMA, one bf16 partial per selection edge)
 //   dw_edge = sum over the edge's heads of D
-// A token phase sums each token's dQ partials in slot order and applies the stick-breaking
-// chain rule for ds and dQs; a segment pass forms dKslc = sum ds * Qs; a fixed-order
-// reduction sums the segments' partials per chunk.
-//
-// D = 128: phase 1 (token tiles, like the forward), per 16-column job of one chunk
-//   S^T = K_c Q^T, dP^T = V_c dO^T                     (MFMA)
-//   P = softmax1(S), D = sum_keys P.dP, dS = w P (dP - D)   (per column, fp32)
-//   dQ^T += K_c^T dS^T                                  (MFMA, into LDS by rounds)
-//   dw_edge = sum over the token's heads of D
-// then per token the stick-breaking chain rule gives ds and dQs; phase 2 is the vector-ALU
-// chunk phase with the same reduction.
+// For D = 64 the two waves of a segment take alternate jobs over all 64 keys; for D = 128
+// they split the keys and share each job.  A token phase sums each token's dQ partials in
+// slot order and applies the stick-breaking chain rule for ds and dQs; a segment pass forms
+// dKslc = sum ds * Qs; a fixed-order reduction sums the segments' partials per chunk.
 #include "hsa_common.h"
 #include "hsa_launch.h"
 #include "mfma_common.h"
-#include "tile_common.h"
+#include "tile_common.h"  // row reductions
 
 namespace hsa {
 
-// ---- phase 1 -------------------------------------------------------------------------------
+// ---- chunk phase, then token phase ----------------------------------------------------------
 
-template <int D, int TT, int G, bool HL>
-__global__ void __launch_bounds__(512) k_bwd_p1_tile(
-    const bf16* __restrict__ Q, const bf16* __restrict__ Kop, const bf16* __restrict__ Vop,
-    const bf16* __restrict__ Kt, const bf16* __restrict__ Kslc, const int32_t* __restrict__ idx,
-    const float* __restrict__ score, const float* __restrict__ w, const bf16* __restrict__ dO,
-    const uint32_t* __restrict__ prep, bf16* __restrict__ dQ, bf16* __restrict__ dQs,
-    float* __restrict__ ds_out, float* __restrict__ dw_out, float* __restrict__ lse,
-    float* __restrict__ dd_out, int L, int Hq, int Hkv, int Kn, int nC, int BG, float c2,
-    float sm_scale, float sel_scale) {
-  // HL: lse holds the forward's softmax normaliser of every (token, group, slot, head) and is
-  // read; otherwise it is computed here and written for phase 2.
-  constexpr int NT = 512, NW = NT / 64;
-  constexpr int DP = D + 1;
-  constexpr int KS = D / 32;
-  constexpr int DT = D / 16;
-  constexpr int NMAX = TT * 16;
-  __shared__ float acc[TT * G * DP];  // dQ (without the logit scale)
-  __shared__ uint32_t keys[NMAX];
-  __shared__ uint32_t order[NMAX];    // later: ds per (token, slot)
-  __shared__ int roff[65];
-  __shared__ float wsh[TT * 16];
-  __shared__ float dwsh[TT * 16];
-  __shared__ int hdr[3];
-
-  const int bg = blockIdx.x % BG;
-  const int tile = blockIdx.x / BG;
-  const int g = bg % Hkv;
-  const size_t b = bg / Hkv;
-  const int t0 = tile * TT;
-  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-
-  load_prep<NT, TT>(prep + (size_t)blockIdx.x * prep_words(TT), keys, order, roff, hdr);
-  for (int i = tid; i < TT * Kn; i += NT) {
-    const int tl = i / Kn, k = i % Kn, t = t0 + tl;
-    if (t < L) wsh[tl * 16 + k] = w[((b * L + t) * Hkv + g) * Kn + k];
-  }
-  for (int i = tid; i < TT * 16; i += NT) dwsh[i] = 0.0f;
-  for (int i = tid; i < TT * G * DP; i += NT) acc[i] = 0.0f;
-  __syncthreads();
-  const int n_rounds = hdr[2];
-
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int col = lane % 16, blk = lane / 16;
-  const int slot = col / G, head = col % G;
-  // this wave's share of round r: [rb(r), re(r)), and its next job after job j of round r
-  auto rb = [&](int r) {
-    const int a = roff[r], n = roff[r + 1] - a;
-    return a + (int)((long)n * wv / NW);
-  };
-  auto re = [&](int r) {
-    const int a = roff[r], n = roff[r + 1] - a;
-    return a + (int)((long)n * (wv + 1) / NW);
-  };
-  auto next_job = [&](int r, int j) {
-    if (j + 1 < re(r)) return j + 1;
-    for (int r2 = r + 1; r2 < n_rounds; ++r2)
-      if (rb(r2) < re(r2)) return rb(r2);
-    return -1;
-  };
-  auto chunk_of = [&](int j) {
-    return __builtin_amdgcn_readfirstlane(edge_chunk(keys[order[j] & 0xffff]));
-  };
-  // D=64: the next job's chunk operands (K and V rows) are prefetched into a second register
-  // set like its query rows; the transposed K of the dQ product loads when the chunk changes
-  // and is first needed after the S, dP and softmax work of the job.
-  constexpr bool kPrefetchKV = (D == 64);
-  bf16x8 ka[4][KS], vr[4][KS], kt[DT][2], kn[4][KS], vn[4][KS];
-  bf16x8 qb[KS], db[KS], qn[KS], dn[KS];
-  int tl = 0, k = 0, tl_n = 0, k_n = 0;
-  bool valid = false, valid_n = false;
-  float le = 0.0f, le_n = 0.0f;  // the column's normaliser (HL)
-  auto load_kv = [&](bf16x8 (&dk)[4][KS], bf16x8 (&dv)[4][KS], int c) {
-    const size_t co = ((size_t)bg * nC + c) * D * 64 + lane * 8;
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        dk[t4][ks] = ld_bf16x8(Kop + co + (t4 * KS + ks) * 512);
-        dv[t4][ks] = ld_bf16x8(Vop + co + (t4 * KS + ks) * 512);
-      }
-  };
-  auto load_kt = [&](int c) {
-    const size_t co = ((size_t)bg * nC + c) * D * 64 + lane * 8;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) kt[dt][s2] = ld_bf16x8(Kt + co + (dt * 2 + s2) * 512);
-  };
-  auto load_qd = [&](int j, bf16x8 (&q)[KS], bf16x8 (&dd)[KS], int& tl_o, int& k_o,
-                     bool& valid_o, float& le_o) {
-    const uint32_t job = __builtin_amdgcn_readfirstlane(order[j]);
-    const int e0 = (int)(job & 0xffff), cnt = (int)(job >> 16);
-    valid_o = slot < cnt;
-    // a padding column reads the job's first token; its weight factor is 0 and it stores
-    // nothing, and the unconditional load keeps the prefetch free of branches
-    const uint32_t ek = keys[e0 + (valid_o ? slot : 0)];
-    tl_o = edge_token(ek);
-    k_o = edge_slot(ek);
-    const size_t qoff = ((b * L + t0 + tl_o) * Hq + (size_t)g * G + head) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      q[ks] = ld_bf16x8(Q + qoff + 32 * ks + 8 * blk);
-      dd[ks] = ld_bf16x8(dO + qoff + 32 * ks + 8 * blk);
-    }
-    if (HL) le_o = lse[(((b * L + t0 + tl_o) * Hkv + g) * Kn + k_o) * G + head];
-  };
-  int cur = -1, nxt = -1, jn = -1;
-  for (int r = 0; r < n_rounds && jn < 0; ++r)
-    if (rb(r) < re(r)) jn = rb(r);
-  if (jn >= 0) {
-    nxt = chunk_of(jn);
-    if (kPrefetchKV) load_kv(kn, vn, nxt);
-    load_qd(jn, qn, dn, tl_n, k_n, valid_n, le_n);
-  }
-  for (int r = 0; r < n_rounds; ++r) {
-    const int jr1 = re(r);
-    for (int j = rb(r); j < jr1; ++j) {
-      if (nxt != cur) {
-        if (kPrefetchKV) {
-#pragma unroll
-          for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-              ka[t4][ks] = kn[t4][ks];
-              vr[t4][ks] = vn[t4][ks];
-            }
-        } else {
-          load_kv(ka, vr, nxt);
-        }
-        load_kt(nxt);
-        cur = nxt;
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        qb[ks] = qn[ks];
-        db[ks] = dn[ks];
-      }
-      tl = tl_n;
-      k = k_n;
-      valid = valid_n;
-      le = le_n;
-      jn = next_job(r, j);
-      if (jn >= 0) {
-        nxt = chunk_of(jn);
-        if (kPrefetchKV && nxt != cur) load_kv(kn, vn, nxt);
-        load_qd(jn, qn, dn, tl_n, k_n, valid_n, le_n);
-      }
-      f32x4 sa[4], pa[4];
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        sa[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
-        pa[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          sa[t4] = mfma_16x16x32(ka[t4][ks], qb[ks], sa[t4]);
-          pa[t4] = mfma_16x16x32(vr[t4][ks], db[ks], pa[t4]);
-        }
-      }
-      float dsum = 0.0f, lse_w = 0.0f;
-      if (HL) {  // P from the forward's normaliser
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sa[t4][i] = exp2_fast(sa[t4][i] * c2 - le);
-            dsum += sa[t4][i] * pa[t4][i];
-          }
-      } else {
-        float m = 0.0f;
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) m = fmaxf(m, sa[t4][i] * c2);
-        m = rows4_max(m);
-        float sum = 0.0f;
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sa[t4][i] = exp2_fast(sa[t4][i] * c2 - m);
-            sum += sa[t4][i];
-          }
-        sum = rows4_sum(sum);
-        const float den = exp2_fast(-m) + sum;
-        const float inv = 1.0f / den;
-        lse_w = m + __builtin_amdgcn_logf(den);
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sa[t4][i] *= inv;  // P
-            dsum += sa[t4][i] * pa[t4][i];
-          }
-      }
-      dsum = rows4_sum(dsum);  // D of this column
-      if (valid && blk == 0) {  // kept for phase 2: normaliser (log2 domain) and D
-        const size_t so = (((b * L + t0 + tl) * Hkv + g) * Kn + k) * G + head;
-        if (!HL) __builtin_nontemporal_store(lse_w, lse + so);
-        __builtin_nontemporal_store(dsum, dd_out + so);
-      }
-      const float wk = valid ? wsh[tl * 16 + k] : 0.0f;
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sa[t4][i] = wk * sa[t4][i] * (pa[t4][i] - dsum);  // dS
-      bf16x8 sb[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) sb[s2] = pack_bf16x8(sa[2 * s2], sa[2 * s2 + 1]);
-      // dw of this edge: sum of D over the token's G head columns (lanes of one slot)
-      const float dw = group_sum<G>(dsum);
-      if (valid && head == 0 && blk == 0) dwsh[tl * 16 + k] = dw;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-        o = mfma_16x16x32(kt[dt][0], sb[0], o);
-        o = mfma_16x16x32(kt[dt][1], sb[1], o);
-        if (valid) {
-          float* dst = acc + (tl * G + head) * DP + 16 * dt + 4 * blk;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i] += o[i];
-        }
-      }
-    }
-    __syncthreads();  // end of round r
-  }
-
-  // per token: ds by the stick-breaking chain rule (newest slot first)
-  float* dssh = reinterpret_cast<float*>(order);
-  if (tid < TT) {
-    const int tl = tid, t = t0 + tl;
-    if (t < L) {
-      const size_t o = ((b * L + t) * Hkv + g) * Kn;
-      double suffix = 0.0;
-      for (int k = Kn - 1; k >= 0; --k) {
-        const int c = idx[o + k];
-        double dsk = 0.0, dwk = 0.0;
-        if (c >= 0 && c < nC) {
-          const double p = sigmoid_d((double)score[o + k]);
-          const double wk = (double)wsh[tl * 16 + k];
-          dwk = (double)dwsh[tl * 16 + k];
-          dsk = dwk * wk * (1.0 - p) - p * suffix;
-          suffix += dwk * wk;
-        }
-        dssh[tl * 16 + k] = (float)dsk;
-        ds_out[o + k] = (float)dsk;
-        dw_out[o + k] = (float)dwk;
-      }
-    }
-  }
-  __syncthreads();
-  // dQs = sel_scale * sum_k ds_k Kslc[c_k]
-  for (int i = tid; i < TT * D; i += NT) {
-    const int tl = i / D, e = i % D, t = t0 + tl;
-    if (t >= L) continue;
-    const size_t o = ((b * L + t) * Hkv + g) * Kn;
-    float a = 0.0f;
-    for (int k = 0; k < Kn; ++k) {
-      const int c = idx[o + k];
-      if (c >= 0 && c < nC) a += dssh[tl * 16 + k] * to_f32(Kslc[((b * nC + c) * Hkv + g) * D + e]);
-    }
-    dQs[((b * L + t) * Hkv + g) * D + e] = from_f32<bf16>(a * sel_scale);
-  }
-  // dQ
-  for (int i = tid; i < TT * G * D / 8; i += NT) {
-    const int e = i * 8;
-    const int tl = e / (G * D), h = (e / D) % G, d = e % D;
-    const int t = t0 + tl;
-    if (t >= L) continue;
-    const float* src = acc + (tl * G + h) * DP + d;
-    f32x4 lo = {src[0], src[1], src[2], src[3]};
-    f32x4 hi = {src[4], src[5], src[6], src[7]};
-    *reinterpret_cast<bf16x8*>(dQ + ((b * L + t) * Hq + (size_t)g * G + h) * D + d) =
-        pack_bf16x8(lo * sm_scale, hi * sm_scale);
-  }
-}
-
-// ---- fused backward for D = 64: chunk phase, then token phase -------------------------------
-
-// Chunk phase: one wave per segment of a chunk's selector list.  The chunk's keys and values
-// sit in LDS; a job takes 16/G selectors (16 query rows, row q = selector * G + head):
+// Chunk phase for D = 64: one block of two waves per segment of a chunk's selector list.  The
+// chunk's keys and values sit in LDS; a job takes 16/G selectors (16 query rows, row
+// q = selector * G + head), and the two waves take alternate jobs:
 //   S = Q K_c^T, dP = dO V_c^T                               (MFMA 16x16x32)
 //   P = exp(S - lse), with lse the forward's normaliser (HL) or computed here over the
 //   chunk's 64 keys; D = rowsum(P * dP); dS = w P (dP - D)
 //   dV^T += dO^T (w P), dK^T += Q^T dS                       (MFMA 16x16x16, registers)
-//   dQ_k^T = K_c^T dS^T                                      (MFMA 16x16x16, per edge)
+//   dQ_k^T = K_c^T dS^T                                      (MFMA 16x16x32, per edge)
 //   dw_edge = sum over the edge's G heads of D
 // Every selection edge belongs to exactly one segment, so the edge's dQ contribution (bf16,
 // unscaled) and dw are stored once; the segment's dK/dV are fp32 partials that a fixed-order
@@ -571,19 +286,262 @@ k_bwd_chunk_mfma(
   }
 }
 
-// Token phase: one wave per (b, t, g) row (D = 64).  dQ = sm_scale * the sum of the chunk
+// Chunk phase for D = 128: two waves per segment split the chunk's 64 keys (wave w owns keys
+// 32w .. 32w+31 and their dK/dV sums, 128 registers each) and work through the jobs together.
+// Per job of 16 query rows (16/G selectors x G heads):
+//   the rows of Q and dO are staged once in LDS for both waves;
+//   each wave: S and dP over its 32 keys, P (from the forward's normaliser, or its own over
+//   the chunk's keys: the row maxima and sums of the two halves meet in LDS), its half of
+//   D = sum over keys of P dP (the halves meet in LDS, added in key order), dS over its keys,
+//   dV^T and dK^T of its keys, dS^T of its keys to a shared LDS tile;
+//   then each wave forms dQ^T = K_c^T dS^T for half of the 128 dimensions, over all 64 keys.
+// Each wave stores its keys' segment partials of dK and dV at the end.
+template <int G, bool HL>
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
+k_bwd_chunk_keys(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const float* __restrict__ w, const bf16* __restrict__ dO, const float* __restrict__ lse_in,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries,
+    const int32_t* __restrict__ seg_start, const int32_t* __restrict__ seg_chunk,
+    const int32_t* __restrict__ n_seg, float* __restrict__ part_dk, float* __restrict__ part_dv,
+    bf16* __restrict__ dq_part, float* __restrict__ dw_out, int L, int Hq, int Hkv, int Kn,
+    int nC, int seg, int64_t max_seg, float c2, float sm_scale) {
+  constexpr int D = 128, TPJ = 16 / G, KS = D / 32, DT = D / 16, NT = 128;
+  constexpr int KROW = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t kl[64][KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t vl[64][KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t ql[16][KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t dl[16][KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sdl[64][16];  // dS^T of the job
+  __shared__ float xl[3][2][16];  // per wave and row: D half; without HL also max, sum
+  __shared__ int tok_l[kBwdSeg];
+  __shared__ int64_t eo_l[kBwdSeg];  // the entry's (b, t, g, slot) index
+  __shared__ float w_l[kBwdSeg];
+  const int64_t sidx = blockIdx.x % max_seg;
+  const int bg = (int)(blockIdx.x / max_seg);
+  if (sidx >= n_seg[bg]) return;  // whole block
+  const int g = bg % Hkv;
+  const size_t b = bg / Hkv;
+  const int c = seg_chunk[(size_t)bg * max_seg + sidx];
+  const int32_t* off = offsets + (size_t)bg * (nC + 1);
+  const int32_t* ss = seg_start + (size_t)bg * (nC + 1);
+  const int e0 = off[c] + (int)(sidx - ss[c]) * seg;
+  const int ne = min(off[c + 1], e0 + seg) - e0;  // <= seg = kBwdSeg
+  const int32_t* ent = entries + (size_t)bg * L * Kn + e0;
+  const int tid = threadIdx.x, lane = tid % 64, col = lane % 16, blk = lane / 16;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / 64);
+  const size_t kvrow = (size_t)Hkv * D;
+  const size_t cb = ((b * L + (size_t)c * 64) * Hkv + g) * D;
+  for (int i = tid; i < ne; i += NT) {
+    const int val = ent[i];
+    const int t = val / Kn, k = val % Kn;
+    const int64_t eo = ((int64_t)(b * L + t) * Hkv + g) * Kn + k;
+    tok_l[i] = t;
+    eo_l[i] = eo;
+    w_l[i] = w[eo];
+  }
+  for (int i = tid; i < 64 * (D / 8); i += NT) {
+    const int key = i / (D / 8), d = (i % (D / 8)) * 8;
+    *reinterpret_cast<uint4*>(&kl[key][d]) = *reinterpret_cast<const uint4*>(K + cb + key * kvrow + d);
+    *reinterpret_cast<uint4*>(&vl[key][d]) = *reinterpret_cast<const uint4*>(V + cb + key * kvrow + d);
+  }
+  f32x4 dk[DT][2], dv[DT][2];  // keys 32*wv + 16*t2 + col, d = 16*dt + 4*blk + i
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      dk[dt][t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dv[dt][t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  const int qs_sel = col / G, qs_head = col % G;  // this lane's query row -> selector, head
+  const int trow = 4 * blk + col / 4, tcol = 4 * (col % 4);
+  // staging of job j: thread tid copies 32 bytes of row tid/8 of Q and of dO (a padding row
+  // repeats the job's first selector)
+  const int srow = tid / 8, spc = tid % 8;
+  const size_t srow_off = (b * L * Hq + (size_t)g * G + srow % G) * D + 16 * spc;
+  const size_t tok_stride = (size_t)Hq * D;
+  auto fetch = [&](int ej, uint4 (&pf)[4], float (&le)[4]) {
+    const int n_here = min(TPJ, ne - ej);
+    const int s2 = srow / G;
+    const size_t qoff = srow_off + (size_t)tok_l[ej + (s2 < n_here ? s2 : 0)] * tok_stride;
+    pf[0] = *reinterpret_cast<const uint4*>(Q + qoff);
+    pf[1] = *reinterpret_cast<const uint4*>(Q + qoff + 8);
+    pf[2] = *reinterpret_cast<const uint4*>(dO + qoff);
+    pf[3] = *reinterpret_cast<const uint4*>(dO + qoff + 8);
+    if (HL) {  // the normaliser of this lane's four output rows 4*blk .. 4*blk+3
+      const int s3 = (4 * blk) / G, e = ej + (s3 < n_here ? s3 : 0);
+      const float4 v = *reinterpret_cast<const float4*>(lse_in + eo_l[e] * G + (4 * blk) % G);
+      le[0] = v.x;
+      le[1] = v.y;
+      le[2] = v.z;
+      le[3] = v.w;
+    }
+  };
+  __syncthreads();
+  uint4 pf[4];
+  float len[4] = {0.f, 0.f, 0.f, 0.f};
+  if (ne > 0) fetch(0, pf, len);
+  for (int ej = 0; ej < ne; ej += TPJ) {
+    const int n_here = min(TPJ, ne - ej);
+    float lse[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lse[i] = len[i];
+    *reinterpret_cast<uint4*>(&ql[srow][16 * spc]) = pf[0];
+    *reinterpret_cast<uint4*>(&ql[srow][16 * spc + 8]) = pf[1];
+    *reinterpret_cast<uint4*>(&dl[srow][16 * spc]) = pf[2];
+    *reinterpret_cast<uint4*>(&dl[srow][16 * spc + 8]) = pf[3];
+    __syncthreads();  // the job's rows are staged
+    if (ej + TPJ < ne) fetch(ej + TPJ, pf, len);
+    // S = Q K^T, dP = dO V^T over this wave's keys 32*wv + 16*t2 + col (rows: the 16 query
+    // rows, four per lane block)
+    f32x4 sa[2], pa[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      sa[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pa[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&ql[col][32 * ks + 8 * blk]);
+      const bf16x8 da = *reinterpret_cast<const bf16x8*>(&dl[col][32 * ks + 8 * blk]);
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int key = 32 * wv + 16 * t2 + col;
+        sa[t2] = mfma_16x16x32(qa, *reinterpret_cast<const bf16x8*>(&kl[key][32 * ks + 8 * blk]),
+                               sa[t2]);
+        pa[t2] = mfma_16x16x32(da, *reinterpret_cast<const bf16x8*>(&vl[key][32 * ks + 8 * blk]),
+                               pa[t2]);
+      }
+    }
+    if (!HL) {  // softmax1 normaliser of each row over the chunk's 64 keys (log2 domain)
+      float mh[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = 0.0f;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) m = fmaxf(m, sa[t2][i] * c2);
+        mh[i] = row16_max(m);
+        if (col == 0) xl[1][wv][4 * blk + i] = mh[i];
+      }
+      __syncthreads();
+      float sh[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mh[i] = fmaxf(xl[1][0][4 * blk + i], xl[1][1][4 * blk + i]);
+        float sum = 0.0f;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) sum += exp2_fast(sa[t2][i] * c2 - mh[i]);
+        sh[i] = row16_sum(sum);
+        if (col == 0) xl[2][wv][4 * blk + i] = sh[i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sum = xl[2][0][4 * blk + i] + xl[2][1][4 * blk + i];
+        lse[i] = mh[i] + __builtin_amdgcn_logf(exp2_fast(-mh[i]) + sum);
+      }
+    }
+    // P; this wave's half of D = sum over keys of P dP per row r = 4*blk + i
+    float wr[4], dr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = (4 * blk + i) / G;
+      float dsum = 0.0f;
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        sa[t2][i] = exp2_fast(sa[t2][i] * c2 - lse[i]);
+        dsum += sa[t2][i] * pa[t2][i];
+      }
+      dsum = row16_sum(dsum);
+      if (col == 0) xl[0][wv][4 * blk + i] = dsum;
+      wr[i] = s < n_here ? w_l[ej + s] : 0.0f;
+    }
+    __syncthreads();  // both halves of D
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dr[i] = xl[0][0][4 * blk + i] + xl[0][1][4 * blk + i];
+    if (wv == 0) {  // dw of each edge: its G rows' D
+      float dsel = (dr[0] + dr[1]) + (dr[2] + dr[3]);
+      if (G >= 8) dsel += __shfl_xor(dsel, 16);
+      if (G == 16) dsel += __shfl_xor(dsel, 32);
+      const int s = (4 * blk) / G;
+      if (col == 0 && (4 * blk) % G == 0 && s < n_here) dw_out[eo_l[ej + s]] = dsel;
+    }
+    // dV^T += dO^T (w P), dK^T += Q^T dS over this wave's keys (k = the 16 query rows); dS^T
+    // of its keys to the shared tile
+    s16x4 wpb[2], dsb[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      f32x4 wp, dsv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wp[i] = wr[i] * sa[t2][i];
+        dsv[i] = wr[i] * sa[t2][i] * (pa[t2][i] - dr[i]);
+      }
+      wpb[t2] = pack_bf16x4(wp);
+      dsb[t2] = pack_bf16x4(dsv);
+      *reinterpret_cast<s16x4*>(&sdl[32 * wv + 16 * t2 + col][4 * blk]) = dsb[t2];
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const s16x4 doT = lds_read_tr4(&dl[trow][16 * dt + tcol]);
+      const s16x4 qT = lds_read_tr4(&ql[trow][16 * dt + tcol]);
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        dv[dt][t2] = mfma_16x16x16(doT, wpb[t2], dv[dt][t2]);
+        dk[dt][t2] = mfma_16x16x16(qT, dsb[t2], dk[dt][t2]);
+      }
+    }
+    __syncthreads();  // the shared dS^T tile is complete
+    // dQ^T rows d = 64*wv .. 64*wv+63 (columns: the 16 query rows) = K_c^T dS^T over the 64
+    // keys, 32 keys per product: lane block blk takes keys 32*kk + 4*blk + i and
+    // 32*kk + 16 + 4*blk + i in both operands
+    f32x4 dq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 dsT = cat_bf16x8(lds_read_tr4(&sdl[32 * kk + trow][tcol]),
+                                    lds_read_tr4(&sdl[32 * kk + 16 + trow][tcol]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 64 * wv + 16 * j;
+        dq[j] = mfma_16x16x32(cat_bf16x8(lds_read_tr4(&kl[32 * kk + trow][d0 + tcol]),
+                                         lds_read_tr4(&kl[32 * kk + 16 + trow][d0 + tcol])),
+                              dsT, dq[j]);
+      }
+    }
+    if (qs_sel < n_here) {  // lane column = query row col: its edge's partial, this wave's half
+      bf16* dst = dq_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 64 * wv + 4 * blk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<s16x4*>(dst + 16 * j) = pack_bf16x4(dq[j]);
+    }
+    __syncthreads();  // staging, dS^T and the row exchange are reused by the next job
+  }
+  const size_t pb = (size_t)bg * max_seg + sidx;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int key = 32 * wv + 16 * t2 + col, d = 16 * dt + 4 * blk;
+      *reinterpret_cast<f32x4*>(part_dk + (pb * 64 + key) * D + d) = dk[dt][t2] * sm_scale;
+      *reinterpret_cast<f32x4*>(part_dv + (pb * 64 + key) * D + d) = dv[dt][t2];
+    }
+}
+
+// Token phase: one wave per (b, t, g) row.  dQ = sm_scale * the sum of the chunk
 // phase's partials over the token's valid slots in slot order; ds by the stick-breaking chain
 // rule from the edges' dw (fp64, newest slot first); dQs = sel_scale * sum_k ds_k Kslc[c_k].
 // The slot data and every slot's partial are loaded together: a slot that is not valid has no
 // partial or dw (its workspace bytes are stale) and is masked out by selection.
-template <int G>
+template <int D, int G>
 __global__ void __launch_bounds__(256) k_bwd_tok(
     const bf16* __restrict__ dq_part, const float* __restrict__ dw_in,
     const int32_t* __restrict__ idx, const float* __restrict__ score,
     const float* __restrict__ w, const bf16* __restrict__ Kslc, bf16* __restrict__ dQ,
     bf16* __restrict__ dQs, float* __restrict__ ds_out, int L, int Hkv, int Kn, int nC,
     int64_t rows, float sm_scale, float sel_scale) {
-  constexpr int D = 64, E = G;  // elements of the row's G x D block per lane
+  constexpr int E = G * D / 64;  // elements of the row's G x D block per lane
+  constexpr int F = D / 64;      // features of dQs per lane: lane + 64 f
   const int lane = threadIdx.x % 64;
   const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // (b * L + t) * Hkv + g
   if (row >= rows) return;  // whole wave
@@ -637,39 +595,48 @@ __global__ void __launch_bounds__(256) k_bwd_tok(
     dsk = (float)(dww * (1.0 - p) - p * suffix);
   }
   if (lane < Kn) ds_out[o + lane] = dsk;
-  // dQs (one feature per lane), slots in order; the rows of the valid slots load together
-  float a = 0.0f;
+  // dQs (features lane + 64 f), slots in order; the rows of the valid slots load together
+  float a[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) a[f] = 0.0f;
   if (nC > 0) {
     const int cv = valid ? c : 0;
     for (int k0 = 0; k0 < Kn; k0 += 8) {
-      float kv[8];
+      float kv[8][F];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int ck = __builtin_amdgcn_readlane(cv, min(k0 + u, Kn - 1));
-        kv[u] = to_f32(Kslc[((b * nC + ck) * Hkv + g) * D + lane]);
+#pragma unroll
+        for (int f = 0; f < F; ++f)
+          kv[u][f] = to_f32(Kslc[((b * nC + ck) * Hkv + g) * D + lane + 64 * f]);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int k = k0 + u;
         const float dsv = __builtin_bit_cast(
             float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dsk), min(k, Kn - 1)));
-        if (k < Kn && ((vmask >> k) & 1)) a += dsv * kv[u];
+        if (k < Kn && ((vmask >> k) & 1)) {
+#pragma unroll
+          for (int f = 0; f < F; ++f) a[f] += dsv * kv[u][f];
+        }
       }
     }
   }
-  dQs[row * D + lane] = from_f32<bf16>(a * sel_scale);
+#pragma unroll
+  for (int f = 0; f < F; ++f) dQs[row * D + lane + 64 * f] = from_f32<bf16>(a[f] * sel_scale);
 }
 
-// dKslc partial of one segment of a chunk's selector list (D = 64, one feature per lane):
+// dKslc partial of one segment of a chunk's selector list (features lane + 64 f per lane):
 // sel_scale * sum over the segment's selectors of ds * Qs.  Four waves take a quarter of the
 // list each, in list order; their sums are added in wave order.
+template <int D>
 __global__ void __launch_bounds__(256) k_bwd_dks(
     const bf16* __restrict__ Qs, const float* __restrict__ ds, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ seg_start,
     const int32_t* __restrict__ seg_chunk, const int32_t* __restrict__ n_seg,
     float* __restrict__ part_dks, int L, int Hkv, int Kn, int nC, int seg, int64_t max_seg,
     float sel_scale) {
-  constexpr int D = 64, NW = 4;
+  constexpr int NW = 4, F = D / 64;
   __shared__ int tok_l[kBwdSeg];
   __shared__ float ds_l[kBwdSeg];
   __shared__ float wsum[NW][D];
@@ -695,21 +662,34 @@ __global__ void __launch_bounds__(256) k_bwd_dks(
   const bf16* qs = Qs + (b * L * Hkv + g) * D + lane;
   const size_t tstride = (size_t)Hkv * D;
   const int i0 = ne * wave / NW, i1 = ne * (wave + 1) / NW;
-  float a = 0.0f;
+  float a[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) a[f] = 0.0f;
   int i = i0;
   for (; i + 8 <= i1; i += 8) {  // eight rows in flight, summed in list order
-    float v[8];
+    float v[8][F];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = to_f32(qs[(size_t)tok_l[i + u] * tstride]);
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a += ds_l[i + u] * v[u];
+      for (int f = 0; f < F; ++f) v[u][f] = to_f32(qs[(size_t)tok_l[i + u] * tstride + 64 * f]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int f = 0; f < F; ++f) a[f] += ds_l[i + u] * v[u][f];
   }
-  for (; i < i1; ++i) a += ds_l[i] * to_f32(qs[(size_t)tok_l[i] * tstride]);
-  wsum[wave][lane] = a;
+  for (; i < i1; ++i)
+#pragma unroll
+    for (int f = 0; f < F; ++f) a[f] += ds_l[i] * to_f32(qs[(size_t)tok_l[i] * tstride + 64 * f]);
+#pragma unroll
+  for (int f = 0; f < F; ++f) wsum[wave][lane + 64 * f] = a[f];
   __syncthreads();
   if (wave == 0)
-    part_dks[((size_t)bg * max_seg + sidx) * D + lane] =
-        (((wsum[0][lane] + wsum[1][lane]) + wsum[2][lane]) + wsum[3][lane]) * sel_scale;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      const int e = lane + 64 * f;
+      part_dks[((size_t)bg * max_seg + sidx) * D + e] =
+          (((wsum[0][e] + wsum[1][e]) + wsum[2][e]) + wsum[3][e]) * sel_scale;
+    }
 }
 
 bool bwd_mfma_supported(const Dims& d) {
@@ -717,41 +697,7 @@ bool bwd_mfma_supported(const Dims& d) {
          d.nC < 32768 && !(d.flags & 1u);
 }
 
-template <int D, int TT, int G>
-static void launch_p1(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
-                      const void* V, const void* Kslc, const int32_t* idx, const float* score,
-                      const float* w, const void* dO, void* dQ, void* dQs, bool hl, char* ws,
-                      hipStream_t s) {
-  const int BG = d.B * d.Hkv;
-  const int n_tiles = (d.L + TT - 1) / TT;
-  const float c2 = (float)(d.sm_scale * 1.4426950408889634);
-  Timed tm(HSA_KERNEL_BWD_P1, s);
-  auto go = [&](auto kern) {
-    kern<<<dim3(BG * n_tiles), 512, 0, s>>>(
-        (const bf16*)Q, (const bf16*)(ws + lay.kop), (const bf16*)(ws + lay.vop),
-        (const bf16*)(ws + lay.kt), (const bf16*)Kslc, idx, score, w, (const bf16*)dO,
-        (const uint32_t*)(ws + lay.prep), (bf16*)dQ, (bf16*)dQs, (float*)(ws + lay.ds),
-        (float*)(ws + lay.dw), (float*)(ws + lay.lse), (float*)(ws + lay.dd), d.L, d.Hq, d.Hkv,
-        d.K, d.nC, BG, c2, (float)d.sm_scale, (float)d.sel_scale);
-  };
-  if (hl) go(k_bwd_p1_tile<D, TT, G, true>);
-  else go(k_bwd_p1_tile<D, TT, G, false>);
-}
-
-template <int D, int TT>
-static void launch_p1_g(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
-                        const void* V, const void* Kslc, const int32_t* idx, const float* score,
-                        const float* w, const void* dO, void* dQ, void* dQs, bool hl, char* ws,
-                        hipStream_t s) {
-  if (d.G == 4) launch_p1<D, TT, 4>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, hl, ws, s);
-  else if (d.G == 8) launch_p1<D, TT, 8>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, hl, ws, s);
-  else launch_p1<D, TT / 2, 16>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, hl, ws, s);
-}
-
-
-bool bwd_fused(const Dims& d) { return bwd_mfma_supported(d) && d.D == 64; }
-
-// D = 64: chunk phase, token phase (+ dKslc partials), reduction.
+// Chunk phase, token phase (+ dKslc partials), reduction.
 static hipError_t launch_bwd_fused(const Dims& d, const BwdLayout& lay, const void* Q,
                                    const void* K, const void* V, const void* Qs,
                                    const void* Kslc, const int32_t* idx, const float* score,
@@ -775,9 +721,15 @@ static hipError_t launch_bwd_fused(const Dims& d, const BwdLayout& lay, const vo
                                (float*)(ws + lay.dw), d.L, d.Hq, d.Hkv, d.K, d.nC, lay.seg,
                                lay.max_seg, c2, (float)d.sm_scale);
     };
-    if (d.G == 4) after_fwd ? go(k_bwd_chunk_mfma<4, true>) : go(k_bwd_chunk_mfma<4, false>);
-    else if (d.G == 8) after_fwd ? go(k_bwd_chunk_mfma<8, true>) : go(k_bwd_chunk_mfma<8, false>);
-    else after_fwd ? go(k_bwd_chunk_mfma<16, true>) : go(k_bwd_chunk_mfma<16, false>);
+    if (d.D == 64) {
+      if (d.G == 4) after_fwd ? go(k_bwd_chunk_mfma<4, true>) : go(k_bwd_chunk_mfma<4, false>);
+      else if (d.G == 8) after_fwd ? go(k_bwd_chunk_mfma<8, true>) : go(k_bwd_chunk_mfma<8, false>);
+      else after_fwd ? go(k_bwd_chunk_mfma<16, true>) : go(k_bwd_chunk_mfma<16, false>);
+    } else {
+      if (d.G == 4) after_fwd ? go(k_bwd_chunk_keys<4, true>) : go(k_bwd_chunk_keys<4, false>);
+      else if (d.G == 8) after_fwd ? go(k_bwd_chunk_keys<8, true>) : go(k_bwd_chunk_keys<8, false>);
+      else after_fwd ? go(k_bwd_chunk_keys<16, true>) : go(k_bwd_chunk_keys<16, false>);
+    }
   }
   {
     Timed tm(HSA_KERNEL_BWD_P1, s);
@@ -788,11 +740,18 @@ static hipError_t launch_bwd_fused(const Dims& d, const BwdLayout& lay, const vo
           (const bf16*)Kslc, (bf16*)dQ, (bf16*)dQs, (float*)(ws + lay.ds), d.L, d.Hkv, d.K,
           d.nC, rows, (float)d.sm_scale, (float)d.sel_scale);
     };
-    if (d.G == 4) go(k_bwd_tok<4>);
-    else if (d.G == 8) go(k_bwd_tok<8>);
-    else go(k_bwd_tok<16>);
+    if (d.D == 64) {
+      if (d.G == 4) go(k_bwd_tok<64, 4>);
+      else if (d.G == 8) go(k_bwd_tok<64, 8>);
+      else go(k_bwd_tok<64, 16>);
+    } else {
+      if (d.G == 4) go(k_bwd_tok<128, 4>);
+      else if (d.G == 8) go(k_bwd_tok<128, 8>);
+      else go(k_bwd_tok<128, 16>);
+    }
+    auto dks = d.D == 64 ? k_bwd_dks<64> : k_bwd_dks<128>;
     if (d.nC > 0)
-      k_bwd_dks<<<dim3((unsigned)(BG * lay.max_seg)), 256, 0, s>>>(
+      dks<<<dim3((unsigned)(BG * lay.max_seg)), 256, 0, s>>>(
           (const bf16*)Qs, (const float*)(ws + lay.ds), (const int32_t*)(ws + lay.offsets),
           (const int32_t*)(ws + lay.entries), (const int32_t*)(ws + lay.seg_start),
           (const int32_t*)(ws + lay.seg_chunk), (const int32_t*)(ws + lay.n_seg),
@@ -814,22 +773,8 @@ hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, c
     hipError_t e = launch_invidx(d, lay, idx, ws, s);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = hipSuccess;
-  if (bwd_fused(d))
-    return launch_bwd_fused(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK, dV, dQs,
-                            dKslc, fold, after_fwd, ws, s);
-  // D = 128: token tiles on the matrix cores, then the vector-ALU chunk phase
-  launch_prep_ops(d, K, ws + lay.kt, true, s);
-  launch_prep_ops(d, V, ws + lay.vop, false, s);
-  // after a token-tile forward its job lists and key operand are still in place
-  if (!after_fwd || fwd_chunked(d)) {
-    launch_prep_ops(d, K, ws + lay.kop, false, s);
-    launch_tile_prep(d, idx, ws + lay.prep, s);
-  }
-  launch_p1_g<128, 32>(d, lay, Q, K, V, Kslc, idx, score, w, dO, dQ, dQs, after_fwd, ws, s);
-  e = launch_bwd_generic_p2(d, lay, Q, K, V, Qs, w, dO, ws, s);
-  if (e != hipSuccess) return e;
-  return launch_bwd_reduce(d, lay, dK, dV, dKslc, fold, ws, s);
+  return launch_bwd_fused(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK, dV, dQs, dKslc,
+                          fold, after_fwd, ws, s);
 }
 
 }  // namespace hsa

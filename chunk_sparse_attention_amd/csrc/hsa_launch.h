@@ -63,7 +63,7 @@ FwdState fwd_state(const Dims& d);
 
 // Backward workspace carve-up (byte offsets into the caller's workspace).
 struct BwdLayout : IndexLayout {
-  size_t ds, dw, part_dk, part_dv, part_dks, kt, kop, vop, prep, lse, dd, dq_part, total;
+  size_t ds, dw, part_dk, part_dv, part_dks, lse, dq_part, total;
 };
 BwdLayout bwd_layout(const Dims& d);
 
@@ -115,10 +115,9 @@ size_t chunk_ops_bytes(const Dims& d);
 int tile_tokens(const Dims& d);
 size_t tile_prep_bytes(const Dims& d);
 void launch_tile_prep(const Dims& d, const int32_t* idx, void* prep, hipStream_t s);
+// On the matrix cores the chunk phase also yields per-edge dQ partials, which a token phase
+// sums.
 bool bwd_mfma_supported(const Dims& d);
-// D = 64 on the matrix cores: the chunk phase also yields per-edge dQ partials, which a
-// token phase sums (no token-tile phase).
-bool bwd_fused(const Dims& d);
 // after_fwd: ws still holds the forward's state for this problem, idx and K (see FwdState).
 hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
                            const void* V, const void* Qs, const void* Kslc, const int32_t* idx,
@@ -126,7 +125,8 @@ hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, c
                            void* dK, void* dV, void* dQs, float* dKslc, bool fold,
                            bool after_fwd, char* ws, hipStream_t s);
 bool fwd_mfma_supported(const Dims& d);
-// bf16 D = 64: the forward runs chunk-major (inverse index, per-edge partials, token sums).
+// bf16 up to 16384 chunks: the forward runs chunk-major (inverse index, per-edge partials,
+// token sums); beyond, on token tiles.
 bool fwd_chunked(const Dims& d);
 size_t fwd_mfma_ws(const Dims& d);
 hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,

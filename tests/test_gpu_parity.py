@@ -55,15 +55,24 @@ def gpu_forward(hsa, x, wl, dev, generic=False):
     return dict(Q=Q, K=K, V=V, Qs=Qs, Kslc=Kslc, idx=idx, score=score, w=w, O=O)
 
 
-def compare_forward(orc, x, wl, g, row_mask=None):
-    f = orc.forward(x["Q"], x["K"], x["V"], x["Qs"], wl.S, wl.K, row_mask=row_mask)
+def compare_forward(orc, x, wl, g, row_mask=None, out_mask=None):
+    """Selection on the rows of row_mask (default: all), outputs on those of out_mask
+    (default: row_mask)."""
+    if out_mask is None:
+        f = orc.forward(x["Q"], x["K"], x["V"], x["Qs"], wl.S, wl.K, row_mask=row_mask)
+    else:
+        Kslc = orc.pool(x["K"], wl.S)
+        idx, score, w = orc.select(x["Qs"], Kslc, wl.S, wl.K, row_mask=row_mask)
+        O = orc.attend(x["Q"], x["K"], x["V"], idx, w, wl.S, row_mask=out_mask)
+        f = dict(Kslc=Kslc, idx=idx, score=score, w=w, O=O)
     near = near_tie_rows(orc, x["Qs"], f["Kslc"], wl.S, wl.K, row_mask=row_mask)
     assert np.array_equal(npy(g["Kslc"]), f["Kslc"]), "pooled chunk keys differ"
     gpu = dict(idx=npy(g["idx"]), score=npy(g["score"]), w=npy(g["w"]))
     diff, rep = check_selection(gpu, f, near, x["Qs"], f["Kslc"], wl.S, 1.0 / np.sqrt(wl.D),
                                 row_mask)
-    rows = np.ones(diff.shape, bool) if row_mask is None else np.broadcast_to(
-        np.asarray(row_mask, bool).reshape(wl.B, wl.L, 1), diff.shape)
+    om = row_mask if out_mask is None else out_mask
+    rows = np.ones(diff.shape, bool) if om is None else np.broadcast_to(
+        np.asarray(om, bool).reshape(wl.B, wl.L, 1), diff.shape)
     keep = head_mask(rows & ~diff, wl.G)
     err = max_abs(npy(g["O"]), f["O"], keep)
     rep["O_max_abs"] = err
@@ -383,12 +392,14 @@ def test_full_backward_sampled(hsa, dev):
     compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=tm, chunk_mask=cm)
 
 
-def test_full_step_sampled(hsa, dev):
-    """The bench's step at its full size and launch configuration (fwd_16k: select, forward
-    and backward on one workspace with HSA_BWD_AFTER_FWD), on sampled tokens and chunks."""
+@pytest.mark.parametrize("name", ["fwd_16k", "fwd_64k"])
+def test_full_step_sampled(hsa, dev, name):
+    """The bench's step at its full size and launch configuration (select, forward and
+    backward on one workspace with HSA_BWD_AFTER_FWD), on sampled tokens and chunks; the
+    selection is compared on every row (the chunk gradients need every selector)."""
     from chunk_sparse_attention_amd import _lib
-    wl = workloads.WORKLOADS["fwd_16k"]
-    say("case full step fwd_16k")
+    wl = workloads.WORKLOADS[name]
+    say("case full step", name)
     x = workloads.make_inputs(wl, seed=0)
     Q, K, V, Qs = (x[k].to(dev) for k in ("Q", "K", "V", "Qs"))
     dO = x["dO"].to(dev)
@@ -400,7 +411,8 @@ def test_full_step_sampled(hsa, dev):
     torch.cuda.synchronize()
     g = dict(Q=Q, K=K, V=V, Qs=Qs, Kslc=Kslc, idx=idx, score=score, w=w, O=O)
     orc = oracle.get()
-    f, diff, _ = compare_forward(orc, x, wl, g)
+    om = None if name == "fwd_16k" else _sample_rows(wl, 384, seed=8)
+    f, diff, _ = compare_forward(orc, x, wl, g, out_mask=om)
     tm = _sample_rows(wl, 32, seed=4)
     rng = np.random.default_rng(5)
     cm = np.zeros((wl.B, wl.nC), np.uint8)
