@@ -185,17 +185,18 @@ typedef enum {
   HSA_KERNEL_PREP_OPS = 3,   /* per-chunk operand copies of the matrix-core kernels */
   HSA_KERNEL_FWD = 4,        /* token-level attention fused with the chunk weights */
   HSA_KERNEL_INVIDX = 5,     /* chunk -> (token, slot) inverse index (count, scan, scatter) */
-  HSA_KERNEL_BWD_P1 = 6,     /* backward, token phase: per token dQ, ds, dQs (bf16 D=64: the sum
-                                of the chunk phase's per-edge dQ partials, then the dKslc
-                                partials per segment; otherwise token tiles that also form
-                                dw) */
-  HSA_KERNEL_BWD_P2 = 7,     /* backward, chunk phase: per chunk segment dK, dV partials (bf16
-                                D=64: also the per-edge dQ partials and dw; runs first) */
+  HSA_KERNEL_BWD_P1 = 6,     /* backward, token phase: per token dQ, ds, dQs (matrix-core
+                                path: the sum of the chunk phase's per-edge dQ partials, then
+                                the dKslc partials per segment; plain kernels: one wave per
+                                token row that also forms dw) */
+  HSA_KERNEL_BWD_P2 = 7,     /* backward, chunk phase: per chunk segment dK, dV partials
+                                (matrix-core path: also the per-edge dQ partials and dw; runs
+                                first) */
   HSA_KERNEL_BWD_REDUCE = 8, /* backward: fixed-order reduction of the segment partials */
   HSA_KERNEL_DECODE_SCAN = 9,    /* decode: scan of the chunk-key table, per-block top-K */
   HSA_KERNEL_DECODE_ATTEND = 10, /* decode: merge, weights and attention over the kept chunks */
-  HSA_KERNEL_FWD_TOKEN = 11, /* chunk-major forward (bf16 D=64): per token sum of the edges'
-                                weighted outputs */
+  HSA_KERNEL_FWD_TOKEN = 11, /* chunk-major forward (bf16, up to 16384 chunks): per token sum
+                                of the edges' weighted outputs */
   HSA_KERNEL_COUNT = 12
 } hsa_kernel_t;
 
