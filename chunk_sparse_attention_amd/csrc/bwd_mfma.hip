@@ -287,7 +287,8 @@ k_bwd_chunk_mfma(
 }
 
 // Chunk phase for D = 128: two waves per segment split the chunk's 64 keys (wave w owns keys
-// 32w .. 32w+31 and their dK/dV sums, 128 registers each) and work through the jobs together.
+// 32w .. 32w+31, their dK/dV sums in 128 registers and their value rows as dP's B operand in
+// 32 more) and work through the jobs together.
 // Per job of 16 query rows (16/G selectors x G heads):
 //   the rows of Q and dO are staged once in LDS for both waves;
 //   each wave: S and dP over its 32 keys, P (from the forward's normaliser, or its own over
@@ -309,7 +310,6 @@ k_bwd_chunk_keys(
   constexpr int D = 128, TPJ = 16 / G, KS = D / 32, DT = D / 16, NT = 128;
   constexpr int KROW = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t kl[64][KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vl[64][KROW];
   __shared__ __attribute__((aligned(16))) uint16_t ql[16][KROW];
   __shared__ __attribute__((aligned(16))) uint16_t dl[16][KROW];
   __shared__ __attribute__((aligned(16))) uint16_t sdl[64][16];  // dS^T of the job
@@ -343,8 +343,14 @@ k_bwd_chunk_keys(
   for (int i = tid; i < 64 * (D / 8); i += NT) {
     const int key = i / (D / 8), d = (i % (D / 8)) * 8;
     *reinterpret_cast<uint4*>(&kl[key][d]) = *reinterpret_cast<const uint4*>(K + cb + key * kvrow + d);
-    *reinterpret_cast<uint4*>(&vl[key][d]) = *reinterpret_cast<const uint4*>(V + cb + key * kvrow + d);
   }
+  // the value rows of this wave's keys stay in registers as dP's B operand
+  bf16x8 vb[2][KS];
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      vb[t2][ks] = ld_bf16x8(V + cb + (32 * wv + 16 * t2 + col) * kvrow + 32 * ks + 8 * blk);
   f32x4 dk[DT][2], dv[DT][2];  // keys 32*wv + 16*t2 + col, d = 16*dt + 4*blk + i
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -360,38 +366,39 @@ k_bwd_chunk_keys(
   const int srow = tid / 8, spc = tid % 8;
   const size_t srow_off = (b * L * Hq + (size_t)g * G + srow % G) * D + 16 * spc;
   const size_t tok_stride = (size_t)Hq * D;
-  auto fetch = [&](int ej, uint4 (&pf)[4], float (&le)[4]) {
+  // the rows of job ej, returned by value so that they stay in registers
+  struct JobRows {
+    uint4 q0, q1, d0, d1;
+    float4 le;
+  };
+  auto fetch = [&](int ej) {
+    JobRows r;
     const int n_here = min(TPJ, ne - ej);
     const int s2 = srow / G;
     const size_t qoff = srow_off + (size_t)tok_l[ej + (s2 < n_here ? s2 : 0)] * tok_stride;
-    pf[0] = *reinterpret_cast<const uint4*>(Q + qoff);
-    pf[1] = *reinterpret_cast<const uint4*>(Q + qoff + 8);
-    pf[2] = *reinterpret_cast<const uint4*>(dO + qoff);
-    pf[3] = *reinterpret_cast<const uint4*>(dO + qoff + 8);
+    r.q0 = *reinterpret_cast<const uint4*>(Q + qoff);
+    r.q1 = *reinterpret_cast<const uint4*>(Q + qoff + 8);
+    r.d0 = *reinterpret_cast<const uint4*>(dO + qoff);
+    r.d1 = *reinterpret_cast<const uint4*>(dO + qoff + 8);
+    r.le = float4{0.f, 0.f, 0.f, 0.f};
     if (HL) {  // the normaliser of this lane's four output rows 4*blk .. 4*blk+3
       const int s3 = (4 * blk) / G, e = ej + (s3 < n_here ? s3 : 0);
-      const float4 v = *reinterpret_cast<const float4*>(lse_in + eo_l[e] * G + (4 * blk) % G);
-      le[0] = v.x;
-      le[1] = v.y;
-      le[2] = v.z;
-      le[3] = v.w;
+      r.le = *reinterpret_cast<const float4*>(lse_in + eo_l[e] * G + (4 * blk) % G);
     }
+    return r;
   };
   __syncthreads();
-  uint4 pf[4];
-  float len[4] = {0.f, 0.f, 0.f, 0.f};
-  if (ne > 0) fetch(0, pf, len);
+  JobRows nxt = {};
+  if (ne > 0) nxt = fetch(0);
   for (int ej = 0; ej < ne; ej += TPJ) {
     const int n_here = min(TPJ, ne - ej);
-    float lse[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lse[i] = len[i];
-    *reinterpret_cast<uint4*>(&ql[srow][16 * spc]) = pf[0];
-    *reinterpret_cast<uint4*>(&ql[srow][16 * spc + 8]) = pf[1];
-    *reinterpret_cast<uint4*>(&dl[srow][16 * spc]) = pf[2];
-    *reinterpret_cast<uint4*>(&dl[srow][16 * spc + 8]) = pf[3];
+    float lse[4] = {nxt.le.x, nxt.le.y, nxt.le.z, nxt.le.w};
+    *reinterpret_cast<uint4*>(&ql[srow][16 * spc]) = nxt.q0;
+    *reinterpret_cast<uint4*>(&ql[srow][16 * spc + 8]) = nxt.q1;
+    *reinterpret_cast<uint4*>(&dl[srow][16 * spc]) = nxt.d0;
+    *reinterpret_cast<uint4*>(&dl[srow][16 * spc + 8]) = nxt.d1;
     __syncthreads();  // the job's rows are staged
-    if (ej + TPJ < ne) fetch(ej + TPJ, pf, len);
+    if (ej + TPJ < ne) nxt = fetch(ej + TPJ);
     // S = Q K^T, dP = dO V^T over this wave's keys 32*wv + 16*t2 + col (rows: the 16 query
     // rows, four per lane block)
     f32x4 sa[2], pa[2];
@@ -409,8 +416,7 @@ k_bwd_chunk_keys(
         const int key = 32 * wv + 16 * t2 + col;
         sa[t2] = mfma_16x16x32(qa, *reinterpret_cast<const bf16x8*>(&kl[key][32 * ks + 8 * blk]),
                                sa[t2]);
-        pa[t2] = mfma_16x16x32(da, *reinterpret_cast<const bf16x8*>(&vl[key][32 * ks + 8 * blk]),
-                               pa[t2]);
+        pa[t2] = mfma_16x16x32(da, vb[t2][ks], pa[t2]);
       }
     }
     if (!HL) {  // softmax1 normaliser of each row over the chunk's 64 keys (log2 domain)
@@ -515,7 +521,8 @@ k_bwd_chunk_keys(
 #pragma unroll
       for (int j = 0; j < 4; ++j) *reinterpret_cast<s16x4*>(dst + 16 * j) = pack_bf16x4(dq[j]);
     }
-    __syncthreads();  // staging, dS^T and the row exchange are reused by the next job
+    // no barrier here: the next job restages Q and dO after the dK/dV barrier above, and
+    // rewrites dS^T and the row exchange only after its own exchange barrier
   }
   const size_t pb = (size_t)bg * max_seg + sidx;
 #pragma unroll
