@@ -510,78 +510,78 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, float4 v) {
   *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
 }
 
-// One block per (b, g, chunk), the incomplete tail chunk included (its rows get zero): dK and
-// dV = the sums of the chunk's segment partials in segment order, dKslc the same over the
-// dKslc partials; with fold, dK rows also get dKslc / S.  Each thread
-// owns four features of one key row and sums the dKslc partials of its features itself, so no
-// phase waits for another.
+// One block per (b, g, chunk, group of 1024/D key rows), the incomplete tail chunk included
+// (its rows get zero): dK and dV = the sums of the chunk's segment partials in segment order,
+// dKslc the same over the dKslc partials; with fold, dK rows also get dKslc / S.  Each thread
+// owns four features of one key row, keeps eight segments' loads in flight and sums the dKslc
+// partials of its features itself, so no phase waits for another.
 template <typename T>
 __global__ void __launch_bounds__(256) k_bwd_p2_reduce(
     const float* __restrict__ part_dk, const float* __restrict__ part_dv,
     const float* __restrict__ part_dks, const int32_t* __restrict__ seg_start, T* __restrict__ dK,
     T* __restrict__ dV, float* __restrict__ dKslc, int L, int Hkv, int D, int S, int nC,
     int n_chunks_all, int64_t max_seg, int fold) {
-  const int c = blockIdx.x % n_chunks_all;
-  const int bg = blockIdx.x / n_chunks_all;
+  const int n_rg = D / 16;  // row groups per chunk: 64 rows / (1024 / D)
+  const int rg = blockIdx.x % n_rg;
+  const int c = (blockIdx.x / n_rg) % n_chunks_all;
+  const int bg = blockIdx.x / (n_rg * n_chunks_all);
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const size_t kvstride = (size_t)Hkv * D;
   const size_t cbase = ((b * L + (size_t)c * S) * Hkv + g) * D;
+  const int j = rg * (1024 / D) + threadIdx.x / (D / 4), e = 4 * (threadIdx.x % (D / 4));
   if (c >= nC) {  // incomplete tail chunk: never selectable
-    for (int i = threadIdx.x; i < kChunk * D; i += blockDim.x) {
-      int j = i / D, e = i % D;
-      if ((size_t)c * S + j < (size_t)L) {
-        dK[cbase + j * kvstride + e] = from_f32<T>(0.0f);
-        dV[cbase + j * kvstride + e] = from_f32<T>(0.0f);
-      }
+    if ((size_t)c * S + j < (size_t)L) {
+      store4<T>(dK + cbase + j * kvstride + e, make_float4(0.f, 0.f, 0.f, 0.f));
+      store4<T>(dV + cbase + j * kvstride + e, make_float4(0.f, 0.f, 0.f, 0.f));
     }
     return;
   }
   const int32_t* ss = seg_start + (size_t)bg * (nC + 1);
-  const int s0 = ss[c], s1 = ss[c + 1];
+  const int s0 = ss[c], s1 = ss[c + 1], ns = s1 - s0;
   const size_t pb = (size_t)bg * max_seg;
-  for (int i = threadIdx.x; i < kChunk * D / 4; i += blockDim.x) {
-    const int j = (4 * i) / D, e = (4 * i) % D;
-    float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak, as = ak;
-    const float* pk = part_dk + ((pb + s0) * kChunk + j) * D + e;
-    const float* pv = part_dv + ((pb + s0) * kChunk + j) * D + e;
-    const float* ps = part_dks + (pb + s0) * D + e;
-    const size_t step = (size_t)kChunk * D;
-    int s = s0;
-    for (; s + 4 <= s1; s += 4) {  // four segments' loads in flight, summed in segment order
-      float4 k4[4], v4[4], d4[4];
+  const size_t step = (size_t)kChunk * D;
+  const float* pk = part_dk + ((pb + s0) * kChunk + j) * D + e;
+  const float* pv = part_dv + ((pb + s0) * kChunk + j) * D + e;
+  const float* ps = part_dks + (pb + s0) * D + e;
+  auto add = [](float4& a, const float4& v) {
+    a.x += v.x;
+    a.y += v.y;
+    a.z += v.z;
+    a.w += v.w;
+  };
+  float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), av = ak, as = ak;
+  int s = 0;
+  for (; s + 8 <= ns; s += 8) {  // eight segments' loads in flight, summed in segment order
+    float4 k8[8], v8[8], d8[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        k4[u] = *reinterpret_cast<const float4*>(pk + (size_t)(s - s0 + u) * step);
-        v4[u] = *reinterpret_cast<const float4*>(pv + (size_t)(s - s0 + u) * step);
-        d4[u] = *reinterpret_cast<const float4*>(ps + (size_t)(s - s0 + u) * D);
-      }
+    for (int u = 0; u < 8; ++u) {
+      k8[u] = *reinterpret_cast<const float4*>(pk + (size_t)(s + u) * step);
+      v8[u] = *reinterpret_cast<const float4*>(pv + (size_t)(s + u) * step);
+      d8[u] = *reinterpret_cast<const float4*>(ps + (size_t)(s + u) * D);
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        ak.x += k4[u].x; ak.y += k4[u].y; ak.z += k4[u].z; ak.w += k4[u].w;
-        av.x += v4[u].x; av.y += v4[u].y; av.z += v4[u].z; av.w += v4[u].w;
-        as.x += d4[u].x; as.y += d4[u].y; as.z += d4[u].z; as.w += d4[u].w;
-      }
+    for (int u = 0; u < 8; ++u) {
+      add(ak, k8[u]);
+      add(av, v8[u]);
+      add(as, d8[u]);
     }
-    for (; s < s1; ++s) {
-      const float4 k1 = *reinterpret_cast<const float4*>(pk + (size_t)(s - s0) * step);
-      const float4 v1 = *reinterpret_cast<const float4*>(pv + (size_t)(s - s0) * step);
-      const float4 d1 = *reinterpret_cast<const float4*>(ps + (size_t)(s - s0) * D);
-      ak.x += k1.x; ak.y += k1.y; ak.z += k1.z; ak.w += k1.w;
-      av.x += v1.x; av.y += v1.y; av.z += v1.z; av.w += v1.w;
-      as.x += d1.x; as.y += d1.y; as.z += d1.z; as.w += d1.w;
-    }
-    if (j == 0 && dKslc)
-      *reinterpret_cast<float4*>(dKslc + ((b * nC + c) * Hkv + g) * D + e) = as;
-    if (fold) {
-      ak.x += as.x / (float)S;
-      ak.y += as.y / (float)S;
-      ak.z += as.z / (float)S;
-      ak.w += as.w / (float)S;
-    }
-    store4<T>(dK + cbase + j * kvstride + e, ak);
-    store4<T>(dV + cbase + j * kvstride + e, av);
   }
+  for (; s < ns; ++s) {
+    add(ak, *reinterpret_cast<const float4*>(pk + (size_t)s * step));
+    add(av, *reinterpret_cast<const float4*>(pv + (size_t)s * step));
+    add(as, *reinterpret_cast<const float4*>(ps + (size_t)s * D));
+  }
+  if (j == 0 && dKslc)
+    *reinterpret_cast<float4*>(dKslc + ((b * nC + c) * Hkv + g) * D + e) = as;
+  if (fold) {
+    ak.x += as.x / (float)S;
+    ak.y += as.y / (float)S;
+    ak.z += as.z / (float)S;
+    ak.w += as.w / (float)S;
+  }
+  store4<T>(dK + cbase + j * kvstride + e, ak);
+  store4<T>(dV + cbase + j * kvstride + e, av);
 }
 
 template <typename T>
@@ -639,7 +639,7 @@ hipError_t launch_bwd_reduce(const Dims& d, const BwdLayout& lay, void* dK, void
   const int n_all = (d.L + d.S - 1) / d.S;
   auto go = [&](auto kern, auto* dk, auto* dv) {
     Timed tm(HSA_KERNEL_BWD_REDUCE, s);
-    kern<<<dim3((unsigned)(bg * n_all)), 256, 0, s>>>(
+    kern<<<dim3((unsigned)(bg * n_all * (d.D / 16))), 256, 0, s>>>(
         (const float*)(ws + lay.part_dk), (const float*)(ws + lay.part_dv),
         (const float*)(ws + lay.part_dks), (const int32_t*)(ws + lay.seg_start), dk, dv, dKslc,
         d.L, d.Hkv, d.D, d.S, d.nC, n_all, lay.max_seg, fold ? 1 : 0);
