@@ -591,7 +591,7 @@ def main() -> int:
         tf /= reps
         tb /= reps
         c2 = kernel_counts(wl2, n2, fused_backward(wl2, gen), chunked_forward(wl2, gen))
-        k2 = {name: roofline(name, c2[name], total / n, None)
+        k2 = {name: roofline(name, c2[name], total / n, measured_traffic(wl2.name, name))
               for name, (n, total) in kt2.items() if n}
         out["secondary"] = {
             "workload": f"{wl2.name}: select+fwd+bwd B={wl2.B} L={wl2.L} Hq={wl2.Hq} "

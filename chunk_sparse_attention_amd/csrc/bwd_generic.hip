@@ -36,6 +36,7 @@ IndexLayout index_layout(const Dims& d, size_t& o) {
   x.seg_start = take(sizeof(int32_t) * bg * (d.nC + 1));
   x.seg_chunk = take(sizeof(int32_t) * bg * x.max_seg);
   x.n_seg = take(sizeof(int32_t) * bg);
+  x.seg_order = take(sizeof(int32_t) * bg * x.max_seg);
   return x;
 }
 
@@ -190,6 +191,41 @@ __global__ void __launch_bounds__(1024) k_inv_scan(int32_t* __restrict__ offsets
     for (int s = ss[c]; s < ss[c + 1]; ++s) sc[s] = c;
 }
 
+// Per (b, g), one block: the segments ordered by the token of their first entry (a counting
+// sort over kOrderBuckets token ranges; the order inside a range is whatever the LDS atomics
+// give, which no result depends on: every segment writes its own partials).  Blocks of the
+// chunk-major kernels that run together then gather the Q (and dO) rows of nearby tokens,
+// which the last-level cache can hold, instead of rows from the whole sequence.
+constexpr int kOrderBuckets = 1024;
+__global__ void __launch_bounds__(1024) k_inv_order(const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ seg_start,
+                                                    const int32_t* __restrict__ seg_chunk,
+                                                    const int32_t* __restrict__ n_seg,
+                                                    const int32_t* __restrict__ entries,
+                                                    int32_t* __restrict__ seg_order, int L,
+                                                    int K, int nC, int seg, int64_t max_seg) {
+  __shared__ int32_t hist[kOrderBuckets];
+  __shared__ int32_t total;
+  const int bg = blockIdx.x;
+  const int ns = n_seg[bg];
+  const int32_t* off = offsets + (size_t)bg * (nC + 1);
+  const int32_t* ss = seg_start + (size_t)bg * (nC + 1);
+  const int32_t* sc = seg_chunk + (size_t)bg * max_seg;
+  const int32_t* ent = entries + (size_t)bg * L * K;
+  int32_t* order = seg_order + (size_t)bg * max_seg;
+  auto bucket = [&](int s) {
+    const int c = sc[s];
+    const int t = ent[off[c] + (s - ss[c]) * seg] / K;
+    return (int)((int64_t)t * kOrderBuckets / L);
+  };
+  for (int i = threadIdx.x; i < kOrderBuckets; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  for (int s = threadIdx.x; s < ns; s += blockDim.x) atomicAdd(&hist[bucket(s)], 1);
+  __syncthreads();
+  block_exclusive_scan(hist, kOrderBuckets, &total);
+  for (int s = threadIdx.x; s < ns; s += blockDim.x) order[atomicAdd(&hist[bucket(s)], 1)] = s;
+}
+
 // Per (b, g, tile), one wave: walk the tile's tokens in order; lane k places slot k.  A token's
 // chunks are distinct, so the lanes of one step never share a counter.  The tile's selections
 // are first staged in LDS, 256 tokens at a time, so the serial walk waits on LDS only.  A
@@ -254,6 +290,13 @@ hipError_t launch_invidx(const Dims& d, const IndexLayout& lay, const int32_t* i
                                                          (int32_t*)(ws + lay.entries), d.L,
                                                          d.Hkv, d.K, d.nC, lay.tile_tokens,
                                                          lay.n_tiles);
+  k_inv_order<<<dim3(bg), 1024, 0, s>>>((const int32_t*)(ws + lay.offsets),
+                                        (const int32_t*)(ws + lay.seg_start),
+                                        (const int32_t*)(ws + lay.seg_chunk),
+                                        (const int32_t*)(ws + lay.n_seg),
+                                        (const int32_t*)(ws + lay.entries),
+                                        (int32_t*)(ws + lay.seg_order), d.L, d.K, d.nC, lay.seg,
+                                        lay.max_seg);
   return hipGetLastError();
 }
 

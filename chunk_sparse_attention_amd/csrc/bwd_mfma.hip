@@ -46,7 +46,8 @@ k_bwd_chunk_mfma(
     const float* __restrict__ w, const bf16* __restrict__ dO, const float* __restrict__ lse_in,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries,
     const int32_t* __restrict__ seg_start, const int32_t* __restrict__ seg_chunk,
-    const int32_t* __restrict__ n_seg, float* __restrict__ part_dk, float* __restrict__ part_dv,
+    const int32_t* __restrict__ n_seg,
+    const int32_t* __restrict__ seg_order, float* __restrict__ part_dk, float* __restrict__ part_dv,
     bf16* __restrict__ dq_part, float* __restrict__ dw_out, int L, int Hq, int Hkv, int Kn,
     int nC, int seg, int64_t max_seg, float c2, float sm_scale) {
   // two waves share the segment's chunk in LDS and take alternate jobs; their dK/dV sums
@@ -57,9 +58,10 @@ k_bwd_chunk_mfma(
   __shared__ int tok_l[kBwdSeg];
   __shared__ int64_t eo_l[kBwdSeg];  // the entry's (b, t, g, slot) index
   __shared__ float w_l[kBwdSeg];
-  const int64_t sidx = blockIdx.x % max_seg;
+  const int64_t slot = blockIdx.x % max_seg;
   const int bg = (int)(blockIdx.x / max_seg);
-  if (sidx >= n_seg[bg]) return;  // whole block
+  if (slot >= n_seg[bg]) return;  // whole block
+  const int64_t sidx = seg_order[(size_t)bg * max_seg + slot];  // segments in token order
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const int c = seg_chunk[(size_t)bg * max_seg + sidx];
@@ -304,7 +306,8 @@ k_bwd_chunk_keys(
     const float* __restrict__ w, const bf16* __restrict__ dO, const float* __restrict__ lse_in,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries,
     const int32_t* __restrict__ seg_start, const int32_t* __restrict__ seg_chunk,
-    const int32_t* __restrict__ n_seg, float* __restrict__ part_dk, float* __restrict__ part_dv,
+    const int32_t* __restrict__ n_seg,
+    const int32_t* __restrict__ seg_order, float* __restrict__ part_dk, float* __restrict__ part_dv,
     bf16* __restrict__ dq_part, float* __restrict__ dw_out, int L, int Hq, int Hkv, int Kn,
     int nC, int seg, int64_t max_seg, float c2, float sm_scale) {
   constexpr int D = 128, TPJ = 16 / G, KS = D / 32, DT = D / 16, NT = 128;
@@ -317,9 +320,10 @@ k_bwd_chunk_keys(
   __shared__ int tok_l[kBwdSeg];
   __shared__ int64_t eo_l[kBwdSeg];  // the entry's (b, t, g, slot) index
   __shared__ float w_l[kBwdSeg];
-  const int64_t sidx = blockIdx.x % max_seg;
+  const int64_t slot = blockIdx.x % max_seg;
   const int bg = (int)(blockIdx.x / max_seg);
-  if (sidx >= n_seg[bg]) return;  // whole block
+  if (slot >= n_seg[bg]) return;  // whole block
+  const int64_t sidx = seg_order[(size_t)bg * max_seg + slot];  // segments in token order
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const int c = seg_chunk[(size_t)bg * max_seg + sidx];
@@ -723,7 +727,8 @@ static hipError_t launch_bwd_fused(const Dims& d, const BwdLayout& lay, const vo
                                (const int32_t*)(ws + lay.entries),
                                (const int32_t*)(ws + lay.seg_start),
                                (const int32_t*)(ws + lay.seg_chunk),
-                               (const int32_t*)(ws + lay.n_seg), (float*)(ws + lay.part_dk),
+                               (const int32_t*)(ws + lay.n_seg),
+                               (const int32_t*)(ws + lay.seg_order), (float*)(ws + lay.part_dk),
                                (float*)(ws + lay.part_dv), (bf16*)(ws + lay.dq_part),
                                (float*)(ws + lay.dw), d.L, d.Hq, d.Hkv, d.K, d.nC, lay.seg,
                                lay.max_seg, c2, (float)d.sm_scale);

@@ -285,6 +285,7 @@ __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
     const float* __restrict__ w, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ entries, const int32_t* __restrict__ seg_start,
     const int32_t* __restrict__ seg_chunk, const int32_t* __restrict__ n_seg,
+    const int32_t* __restrict__ seg_order,
     bf16* __restrict__ o_part, float* __restrict__ lse_out, int L, int Hq, int Hkv, int Kn,
     int nC, int seg, int64_t max_seg, float c2) {
   constexpr int TPJ = 16 / G, KS = D / 32, DT = D / 16, NT = 64 * NW;
@@ -295,9 +296,10 @@ __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
   __shared__ int tok_l[kBwdSeg];
   __shared__ int64_t eo_l[kBwdSeg];  // the entry's (b, t, g, slot) index
   __shared__ float w_l[kBwdSeg];
-  const int64_t sidx = blockIdx.x % max_seg;
+  const int64_t slot = blockIdx.x % max_seg;
   const int bg = (int)(blockIdx.x / max_seg);
-  if (sidx >= n_seg[bg]) return;  // whole block
+  if (slot >= n_seg[bg]) return;  // whole block
+  const int64_t sidx = seg_order[(size_t)bg * max_seg + slot];  // segments in token order
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const int c = seg_chunk[(size_t)bg * max_seg + sidx];
@@ -580,7 +582,8 @@ static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const vo
           (const bf16*)Q, (const bf16*)K, (const bf16*)V, w,
           (const int32_t*)(ws + st.ix.offsets), (const int32_t*)(ws + st.ix.entries),
           (const int32_t*)(ws + st.ix.seg_start), (const int32_t*)(ws + st.ix.seg_chunk),
-          (const int32_t*)(ws + st.ix.n_seg), (bf16*)(ws + st.part), (float*)(ws + st.lse),
+          (const int32_t*)(ws + st.ix.n_seg), (const int32_t*)(ws + st.ix.seg_order),
+          (bf16*)(ws + st.part), (float*)(ws + st.lse),
           d.L, d.Hq, d.Hkv, d.K, d.nC, st.ix.seg, st.ix.max_seg, c2);
     };
     if (d.D == 64) {

@@ -41,6 +41,9 @@ struct IndexLayout {
   int seg;          // entries per segment
   int64_t max_seg;  // segment capacity per (b, g)
   size_t tile_counts, offsets, entries, seg_start, seg_chunk, n_seg;
+  // the segments of each (b, g) in the order the chunk-major kernels take them: by the token
+  // of their first entry, so that the blocks in flight gather the rows of nearby tokens
+  size_t seg_order;
 };
 // Entries per chunk segment of the chunk-major kernels (two waves of 16-row jobs).
 constexpr int kBwdSeg = 256;
