@@ -320,13 +320,16 @@ def cpu_baseline(wl, x, budget_s: float = 20.0) -> dict:
 
 
 def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
-    """Time the 1M-context decode step (decode_1m), caches resident in HBM."""
+    """Time the 1M-context decode step (decode_1m), caches resident in HBM, and the same step
+    with the caches in pinned host memory (hsa_decode_host_kv)."""
     import torch
     wl3 = workloads.WORKLOADS["decode_1m"]
     log(f"bench: decode {wl3.name} (generating caches)")
     x3 = workloads.make_decode_inputs(wl3, seed=0, slab=4)
     q, qs = x3["q"].to(dev), x3["qs"].to(dev)
     Kc, Vc = x3["Kc"].to(dev), x3["Vc"].to(dev)
+    # the same caches in pinned host memory for the offloaded step
+    Kh, Vh = x3["Kc"].pin_memory(), x3["Vc"].pin_memory()
     del x3
     Kslc3 = hsa.pool(Kc)
     prob3 = hsa.problem(wl3.B, wl3.L, wl3.Hq, wl3.Hkv, wl3.D, wl3.K, wl3.dtype, generic=gen)
@@ -352,6 +355,17 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
     kt3 = hsa.timer_read()
     n3 = kt3["decode_attend"][0]
     tot3 = kt3["decode_scan"][1] + kt3["decode_attend"][1]
+    # the step with the caches left in host memory: only the selected chunks cross the link
+    for _ in range(3):
+        hsa.decode_host_kv(q, qs, Kh, Vh, Kslc3, wl3.K, generic=gen, ws=ws3)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        hsa.decode_host_kv(q, qs, Kh, Vh, Kslc3, wl3.K, generic=gen, ws=ws3)
+    e1.record()
+    torch.cuda.synchronize()
+    hms = e0.elapsed_time(e1) / reps
+    del Kh, Vh
     el = 2
     # the chunk-key table, the selected chunks' K and V, q, qs and O
     dbytes = (wl3.B * wl3.nC * wl3.Hkv * wl3.D * el
@@ -363,7 +377,9 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
             "roofline": roofline("decode_scan+decode_attend", dict(bytes=dbytes, flops=0),
                                  tot3 / max(n3, 1), None),
             "scan_ms": round(kt3["decode_scan"][1] / max(n3, 1), 4),
-            "attend_ms": round(kt3["decode_attend"][1] / max(n3, 1), 4)}
+            "attend_ms": round(kt3["decode_attend"][1] / max(n3, 1), 4),
+            "host_kv": {"ms": round(hms, 4), "vs_device_kv": round(hms / dms, 3),
+                        "link_bytes_per_step": 2 * wl3.B * wl3.Hkv * wl3.K * wl3.S * wl3.D * el}}
 
 
 def main() -> int:

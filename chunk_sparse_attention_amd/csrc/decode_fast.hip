@@ -17,6 +17,7 @@
 //           flight at once.  The K weighted slot outputs meet in LDS and are summed in slot
 //           order.
 #include <algorithm>
+#include <type_traits>
 
 #include "hsa_common.h"
 #include "hsa_launch.h"
@@ -86,27 +87,34 @@ k_dec_scan_fast(const T* __restrict__ qs, const T* __restrict__ Kslc,
   for (int e = tid; e < D; e += kScanThreads)
     qsh[e] = (double)to_f32(qs[((size_t)b * Hkv + g) * D + e]);
 
-  RawRow<T, D> row[kScanPer];
+  // bf16 rows are taken whole; fp32 rows in parts of 32 values, one after the other and
+  // still summed in dimension order, so that the 1024-thread block stays within 128
+  // registers per lane
+  constexpr int DP = sizeof(T) == 2 ? D : 32;
   int cs[kScanPer];
 #pragma unroll
-  for (int i = 0; i < kScanPer; ++i) {
-    cs[i] = blk * kScanChunks + i * kScanThreads + tid;
-    if (cs[i] < nC) row[i].load(Kslc + ((b * nC + cs[i]) * Hkv + g) * D);
-  }
-  __syncthreads();
-  // the dimension loop is outermost so that only eight query values are live at a time
+  for (int i = 0; i < kScanPer; ++i) cs[i] = blk * kScanChunks + i * kScanThreads + tid;
   double dot[kScanPer];
 #pragma unroll
   for (int i = 0; i < kScanPer; ++i) dot[i] = 0.0;
-#pragma unroll
-  for (int e0 = 0; e0 < D; e0 += 8) {
-    double qv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[e] = qsh[e0 + e];
+#pragma unroll 1
+  for (int d0 = 0; d0 < D; d0 += DP) {
+    RawRow<T, DP> row[kScanPer];
 #pragma unroll
     for (int i = 0; i < kScanPer; ++i)
+      if (cs[i] < nC) row[i].load(Kslc + ((b * nC + cs[i]) * Hkv + g) * D + d0);
+    if (d0 == 0) __syncthreads();  // qsh ready
+    // the dimension loop is outermost so that only eight query values are live at a time
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dot[i] = fma(qv[e], (double)row[i].get(e0 + e), dot[i]);
+    for (int e0 = 0; e0 < DP; e0 += 8) {
+      double qv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = qsh[d0 + e0 + e];
+#pragma unroll
+      for (int i = 0; i < kScanPer; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot[i] = fma(qv[e], (double)row[i].get(e0 + e), dot[i]);
+    }
   }
   uint64_t key[kScanPer];
 #pragma unroll
@@ -217,9 +225,10 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
   constexpr int P = D / 8;
   constexpr int JG = kWave / P;
   constexpr int RPL = kChunk / JG;  // rows per lane in the value product
+  constexpr int NS = NT / kWave;    // slots (waves) per block
   __shared__ float qsh[ZH][D];
-  __shared__ float ash[kMaxK][ZH][kChunk];
-  __shared__ float osh[kMaxK][ZH][D];
+  __shared__ float ash[NS][ZH][kChunk];
+  __shared__ float osh[NS][ZH][D];
   const int tid = threadIdx.x, lane = tid % kWave, slot = tid / kWave;
   const int hg = blockIdx.x % n_hg, bg = blockIdx.x / n_hg;
   const int g = bg % Hkv;
@@ -267,27 +276,40 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
     const size_t kvstride = (size_t)Hkv * D;
     const size_t cbase = ((b * ctx + (size_t)c * kChunk) * Hkv + g) * D;
     const int p8 = lane % P, jg = lane / P;
-    // key row j in lane j; the value pieces are requested at the same time
-    RawRow<T, D> kr;
-    kr.load(Kc + cbase + (size_t)lane * kvstride);
+    // key row j in lane j; the value pieces are requested at the same time where the
+    // register budget holds both (otherwise after the logits)
+    constexpr bool kEarlyV = sizeof(T) == 2 && (NT <= 512 || D == 64);
+    // with 128 registers per lane a D = 128 key row is taken in two halves, one after the
+    // other (the logits still accumulate in dimension order)
+    constexpr int KP = (NT > 512 && D == 128) ? 2 : 1;
+    constexpr int DK = D / KP;
     RawRow<T, 8> vp[RPL];
+    auto load_v = [&]() {
 #pragma unroll
-    for (int i = 0; i < RPL; ++i)
-      vp[i].load(Vc + cbase + (size_t)(jg + JG * i) * kvstride + 8 * p8);
+      for (int i = 0; i < RPL; ++i)
+        vp[i].load(Vc + cbase + (size_t)(jg + JG * i) * kvstride + 8 * p8);
+    };
     float z[ZH];
 #pragma unroll
-    for (int h = 0; h < ZH; ++h) {
-      z[h] = 0.0f;
-      if (h < nh) {
+    for (int h = 0; h < ZH; ++h) z[h] = 0.0f;
+#pragma unroll 1
+    for (int kp = 0; kp < KP; ++kp) {
+      RawRow<T, DK> kr;
+      kr.load(Kc + cbase + (size_t)lane * kvstride + kp * DK);
+      if (kEarlyV && kp == 0) load_v();
 #pragma unroll
-        for (int e0 = 0; e0 < D; e0 += 8) {
-          int off = h * D + e0;  // the empty asm keeps the query reads in the loop
-          asm volatile("" : "+v"(off));
-          const float4 qa = *reinterpret_cast<const float4*>(&qsh[0][0] + off);
-          const float4 qb = *reinterpret_cast<const float4*>(&qsh[0][0] + off + 4);
-          const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+      for (int h = 0; h < ZH; ++h) {
+        if (h < nh) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) z[h] = fmaf(qv[e], kr.get(e0 + e), z[h]);
+          for (int e0 = 0; e0 < DK; e0 += 8) {
+            int off = h * D + kp * DK + e0;  // the empty asm keeps the query reads in the loop
+            asm volatile("" : "+v"(off));
+            const float4 qa = *reinterpret_cast<const float4*>(&qsh[0][0] + off);
+            const float4 qb = *reinterpret_cast<const float4*>(&qsh[0][0] + off + 4);
+            const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[h] = fmaf(qv[e], kr.get(e0 + e), z[h]);
+          }
         }
       }
     }
@@ -303,6 +325,7 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
       }
       ash[slot][h][lane] = aw;
     }
+    if (!kEarlyV) load_v();
     // value product: lane (jg, p8) accumulates rows jg + JG*i of piece p8
     float acc[ZH][8];
 #pragma unroll
@@ -349,7 +372,7 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
 template <typename T, int D>
 static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, const void* Kc,
                               const void* Vc, const void* Kslc, void* O, int32_t* idx,
-                              float* score, float* w, char* ws, hipStream_t s) {
+                              float* score, float* w, bool host_kv, char* ws, hipStream_t s) {
   const int bg = d.B * d.Hkv;
   const DecFastLayout lay = dec_fast_layout(d);
   const int n_blocks = lay.n_blocks;
@@ -361,29 +384,42 @@ static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, cons
   }
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);
   Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
-  // one block per (b, g, head group) of HW <= 4 heads, one wave per kept slot
-  const int HW = (d.G + 3) / 4;
-  const int n_hg = (d.G + HW - 1) / HW;
-  // the launch bound sets the register budget: 256 VGPRs up to 8 slots, 128 above
-  auto go = [&](auto kern) {
+  // one block per (b, g, head group) of HW <= ZH heads, one wave per kept slot.  With the
+  // caches in device memory a group's heads spread over up to four blocks (more CUs); with
+  // them in host memory one block takes up to eight heads, so that each selected chunk
+  // crosses the host link once per eight heads.
+  // The launch bound sets the register budget: 256 VGPRs up to 8 slots, 128 above.
+  auto go = [&](auto kern, int zh) {
+    const int n_hg0 = (d.G + zh - 1) / zh;
+    const int HW = host_kv ? (d.G + n_hg0 - 1) / n_hg0 : (d.G + 3) / 4;
+    const int n_hg = (d.G + HW - 1) / HW;
     kern<<<dim3(bg * n_hg), kWave * d.K, 0, s>>>((const T*)q, (const T*)Kc, (const T*)Vc, cand,
                                                  (T*)O, idx, score, w, d.L, d.Hq, d.Hkv, d.K,
                                                  d.G, HW, n_hg, n_blocks * d.K, c2);
   };
-  if (d.K <= 8) go(k_dec_attend_heads<T, D, 4, 512>);
-  else go(k_dec_attend_heads<T, D, 4, 1024>);
+  constexpr int ZW = 8;  // heads per block for host caches, up to 8 slots
+  if (d.K > 8) go(k_dec_attend_heads<T, D, 4, 1024>, 4);
+  else if (host_kv) go(k_dec_attend_heads<T, D, ZW, 512>, ZW);
+  else go(k_dec_attend_heads<T, D, 4, 512>, 4);
 }
 
 hipError_t launch_decode_fast(const Dims& d, const void* q, const void* qs, const void* Kc,
                               const void* Vc, const void* Kslc, void* O, int32_t* idx,
-                              float* score, float* w, char* ws, hipStream_t s) {
+                              float* score, float* w, bool host_kv, char* ws, hipStream_t s) {
   if (d.B * d.Hkv == 0) return hipSuccess;
+  auto go = [&](auto tag, auto dim) {
+    using T = decltype(tag);
+    launch_dec_fast_t<T, decltype(dim)::value>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w,
+                                               host_kv, ws, s);
+  };
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
   if (d.dtype == 1) {
-    if (d.D == 64) launch_dec_fast_t<bf16, 64>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w, ws, s);
-    else launch_dec_fast_t<bf16, 128>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w, ws, s);
+    if (d.D == 64) go(bf16{}, D64{});
+    else go(bf16{}, D128{});
   } else {
-    if (d.D == 64) launch_dec_fast_t<float, 64>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w, ws, s);
-    else launch_dec_fast_t<float, 128>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w, ws, s);
+    if (d.D == 64) go(float{}, D64{});
+    else go(float{}, D128{});
   }
   return hipGetLastError();
 }

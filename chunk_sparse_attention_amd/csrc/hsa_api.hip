@@ -251,10 +251,31 @@ HSA_EXPORT hsa_status_t hsa_bwd(const hsa_problem_t* p, const void* Q, const voi
                   "bwd");
 }
 
-HSA_EXPORT hsa_status_t hsa_decode(const hsa_problem_t* p, const void* q, const void* qs,
-                                   const void* Kcache, const void* Vcache, const void* Kslc,
-                                   void* O, int32_t* idx, float* score, float* w, void* ws,
-                                   size_t ws_bytes, hsa_stream_t stream) {
+namespace {
+
+// The device's view of page-locked host memory, or an error for anything else.
+hsa_status_t host_view(const void* p, const char* name, const void** dev) {
+  hipPointerAttribute_t a{};
+  const hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // the query's own error is not a failure of enqueued work
+    return fail(HSA_ERR_INVALID_ARG, "%s is not page-locked host memory (%s)", name,
+                hipGetErrorString(e));
+  }
+  if (a.type != hipMemoryTypeHost || !a.devicePointer)
+    return fail(HSA_ERR_INVALID_ARG, "%s is not host memory mapped for the device", name);
+  *dev = a.devicePointer;
+  return HSA_OK;
+}
+
+}  // namespace
+
+namespace {
+
+hsa_status_t decode_impl(const hsa_problem_t* p, const void* q, const void* qs,
+                         const void* Kcache, const void* Vcache, const void* Kslc, void* O,
+                         int32_t* idx, float* score, float* w, void* ws, size_t ws_bytes,
+                         hsa_stream_t stream, bool host_kv) {
   hsa::Dims d;
   TRY(check_problem(HSA_OP_DECODE, p, &d));
   TRY(need_tensor(q, "q"));
@@ -271,10 +292,37 @@ HSA_EXPORT hsa_status_t hsa_decode(const hsa_problem_t* p, const void* q, const 
   hipStream_t s = (hipStream_t)stream;
   if (!(d.flags & HSA_FLAG_GENERIC))
     return launched(hsa::launch_decode_fast(d, q, qs, Kcache, Vcache, Kslc, O, idx, score, w,
-                                            (char*)ws, s),
+                                            host_kv, (char*)ws, s),
                     "decode");
   hsa::DecLayout lay = hsa::dec_layout(d);
   return launched(hsa::launch_decode_generic(d, lay, q, qs, Kcache, Vcache, Kslc, O, idx, score,
                                              w, (char*)ws, s),
                   "decode");
+}
+
+}  // namespace
+
+HSA_EXPORT hsa_status_t hsa_decode(const hsa_problem_t* p, const void* q, const void* qs,
+                                   const void* Kcache, const void* Vcache, const void* Kslc,
+                                   void* O, int32_t* idx, float* score, float* w, void* ws,
+                                   size_t ws_bytes, hsa_stream_t stream) {
+  return decode_impl(p, q, qs, Kcache, Vcache, Kslc, O, idx, score, w, ws, ws_bytes, stream,
+                     false);
+}
+
+HSA_EXPORT hsa_status_t hsa_decode_host_kv(const hsa_problem_t* p, const void* q,
+                                           const void* qs, const void* Kcache,
+                                           const void* Vcache, const void* Kslc, void* O,
+                                           int32_t* idx, float* score, float* w, void* ws,
+                                           size_t ws_bytes, hsa_stream_t stream) {
+  hsa::Dims d;
+  TRY(check_problem(HSA_OP_DECODE, p, &d));
+  TRY(need_tensor(Kcache, "Kcache"));
+  TRY(need_tensor(Vcache, "Vcache"));
+  const void *kd = nullptr, *vd = nullptr;
+  TRY(host_view(Kcache, "Kcache", &kd));
+  TRY(host_view(Vcache, "Vcache", &vd));
+  if (!aligned(kd, 16) || !aligned(vd, 16))
+    return fail(HSA_ERR_INVALID_ARG, "the device view of the caches is not 16-byte aligned");
+  return decode_impl(p, q, qs, kd, vd, Kslc, O, idx, score, w, ws, ws_bytes, stream, true);
 }

@@ -137,9 +137,10 @@ hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const vo
 
 // Decode with a bandwidth-shaped scan and one wave per kept slot (both dtypes).
 size_t dec_fast_ws(const Dims& d);
+// host_kv: Kc and Vc are the device's view of page-locked host memory.
 hipError_t launch_decode_fast(const Dims& d, const void* q, const void* qs, const void* Kc,
                               const void* Vc, const void* Kslc, void* O, int32_t* idx,
-                              float* score, float* w, char* ws, hipStream_t s);
+                              float* score, float* w, bool host_kv, char* ws, hipStream_t s);
 hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void* q,
                                  const void* qs, const void* Kc, const void* Vc,
                                  const void* Kslc, void* O, int32_t* idx, float* score,

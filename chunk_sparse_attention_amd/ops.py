@@ -192,6 +192,40 @@ def decode(q, qs, Kc, Vc, Kslc, K_top, sm_scale=None, sel_scale=None, generic=Fa
     return O, idx, score, w
 
 
+def decode_host_kv(q, qs, Kc, Vc, Kslc, K_top, sm_scale=None, sel_scale=None, generic=False,
+                   ws=None):
+    """decode() with the caches Kc, Vc [B,ctx,Hkv,D] in pinned host memory (CPU tensors made
+    with pin_memory); the step reads only the selected chunks' rows of them.  q, qs and Kslc
+    are GPU tensors.  Returns (O [B,Hq,D], idx, score, w [B,Hkv,K])."""
+    for t, name in ((Kc, "Kcache"), (Vc, "Vcache")):
+        if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned():
+            raise ValueError(f"{name} must be a pinned host tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, ctx, Hkv, D = Kc.shape
+    if Vc.dtype != Kc.dtype or tuple(Vc.shape) != tuple(Kc.shape):
+        raise ValueError("Vcache must match Kcache in dtype and shape")
+    _need(q, "q", Kc.dtype)
+    dev = q.device
+    Hq = q.shape[1]
+    _need(q, "q", Kc.dtype, (B, Hq, D), dev)
+    _need(qs, "qs", Kc.dtype, (B, Hkv, D), dev)
+    _need(Kslc, "Kslc", Kc.dtype, (B, ctx // S_CHUNK, Hkv, D), dev)
+    prob = problem(B, ctx, Hq, Hkv, D, K_top, Kc.dtype, sm_scale=sm_scale, sel_scale=sel_scale,
+                   generic=generic)
+    O = torch.empty((B, Hq, D), dtype=Kc.dtype, device=dev)
+    idx = torch.empty((B, Hkv, K_top), dtype=torch.int32, device=dev)
+    score = torch.empty((B, Hkv, K_top), dtype=torch.float32, device=dev)
+    w = torch.empty((B, Hkv, K_top), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(_lib.HSA_OP_DECODE, prob, dev)
+    wp, wn = _ws_args(ws)
+    check(_lib.lib().hsa_decode_host_kv(ctypes.byref(prob), _ptr(q), _ptr(qs), _ptr(Kc),
+                                        _ptr(Vc), _ptr(Kslc), _ptr(O), _ptr(idx), _ptr(score),
+                                        _ptr(w), wp, wn, _stream()), "hsa_decode_host_kv")
+    return O, idx, score, w
+
+
 def timer_enable(on: bool = True) -> None:
     """Start (forgetting earlier records) or stop HIP-event timing of every kernel launch."""
     check(_lib.lib().hsa_timer_enable(1 if on else 0), "hsa_timer_enable")

@@ -170,6 +170,23 @@ hsa_status_t hsa_decode(const hsa_problem_t* p, const void* q, const void* qs,
                         int32_t* idx, float* score, float* w, void* ws, size_t ws_bytes,
                         hsa_stream_t stream);
 
+/* One decode step with the token K/V cache left in host memory (note section 训练与推理优化,
+ * KV cache offloading: the chunk-key table stays on the device for selection and each step
+ * moves only the selected chunks; 局限与展望: that exchange is g x dh x K x S values per
+ * sequence and group).  Arguments, results and errors are those of hsa_decode, except:
+ *   Kcache, Vcache [B, ctx, Hkv, D] dtype: page-locked host memory mapped for the device
+ *   (hipHostMalloc, or a pinned torch tensor), owned by the caller and read in place: the
+ *   step reads the K selected chunks' 64 rows of K and V per (sequence, group) across the
+ *   host link and nothing else of them.  q, qs, Kslc, O, idx, score, w and ws are device
+ *   memory as for hsa_decode.
+ * Each cache pointer is checked with hipPointerGetAttributes before anything is enqueued:
+ * memory that is not host memory mapped for the device (pageable host memory, or device
+ * memory, which hsa_decode takes) gives HSA_ERR_INVALID_ARG. */
+hsa_status_t hsa_decode_host_kv(const hsa_problem_t* p, const void* q, const void* qs,
+                                const void* Kcache, const void* Vcache, const void* Kslc,
+                                void* O, int32_t* idx, float* score, float* w, void* ws,
+                                size_t ws_bytes, hsa_stream_t stream);
+
 /* ---- Kernel timing (measurement aid; not part of the operation) ----------------------
  * The entry points above each enqueue a short sequence of kernels.  To price one kernel
  * against the device's roofline, the library can bracket every launch of a kernel class

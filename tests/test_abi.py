@@ -94,6 +94,12 @@ def test_entry_points_reject_before_launch():
     st = lib.hsa_decode(ctypes.byref(_prob(D=80)), fake, fake, fake, fake, fake, fake, fake, None,
                         fake, fake, 1 << 30, None)
     assert st == 2
+    st = lib.hsa_decode_host_kv(ctypes.byref(_prob(D=80)), fake, fake, fake, fake, fake, fake,
+                                fake, None, fake, fake, 1 << 30, None)
+    assert st == 2
+    st = lib.hsa_decode_host_kv(ctypes.byref(_prob()), fake, fake, None, fake, fake, fake, fake,
+                                None, fake, fake, 1 << 30, None)
+    assert st == 1 and b"Kcache is NULL" in lib.hsa_last_error()
 
 
 def test_binding_refuses_cpu_tensors():
@@ -102,6 +108,16 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros((1, 128, 1, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         hsa.select(x, x, 4)
+
+
+def test_binding_host_kv_needs_pinned_caches():
+    """The host-cache decode takes pinned host tensors only (checked before any GPU call)."""
+    import torch
+    import chunk_sparse_attention_amd as hsa
+    x = torch.zeros((1, 128, 1, 64), dtype=torch.bfloat16)
+    q = torch.zeros((1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="pinned host tensor"):
+        hsa.decode_host_kv(q, q[:, :1], x, x, x[:, :2], 2)
 
 
 def test_kernel_timer_without_launches():

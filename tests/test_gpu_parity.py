@@ -7,6 +7,8 @@ for bf16 and 1e-4 for fp32.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -308,6 +310,56 @@ def test_decode_small(hsa, dev, ctx, generic):
     assert np.array_equal(npy(idx), d["idx"])
     assert max_abs(npy(w), d["w"]) <= 1e-5
     assert max_abs(npy(O), d["O"]) <= 2e-2
+
+
+@pytest.mark.parametrize("ctx", [64 * 7 + 13, 64 * 33])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_decode_host_kv(hsa, dev, ctx, dtype):
+    """The caches in pinned host memory: the same kernels read the selected chunks across the
+    host link, so the results equal those with device caches bit for bit, and the oracle's."""
+    wl = W("decode_host_kv", 3, ctx, 16, 2, 64, 64, 8, dtype)
+    say("case decode host kv", ctx, dtype)
+    x = workloads.make_decode_inputs(wl, seed=9, ctx=ctx)
+    q, qs, Kc, Vc = (x[k].to(dev) for k in ("q", "qs", "Kc", "Vc"))
+    Kh, Vh = x["Kc"].pin_memory(), x["Vc"].pin_memory()
+    Kslc = hsa.pool(Kc)
+    ref = hsa.decode(q, qs, Kc, Vc, Kslc, wl.K)
+    got = hsa.decode_host_kv(q, qs, Kh, Vh, Kslc, wl.K)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    orc = oracle.get()
+    ks = orc.pool(x["Kc"], 64)
+    d = orc.decode(x["q"], x["qs"], x["Kc"], x["Vc"], ks, 64, wl.K)
+    assert np.array_equal(npy(got[1]), d["idx"])
+    assert max_abs(npy(got[3]), d["w"]) <= 1e-5
+    assert max_abs(npy(got[0]), d["O"]) <= tol_for(dtype)
+
+
+def test_decode_host_kv_rejects_other_memory(hsa, dev):
+    """Pageable host memory and device memory are refused before anything is enqueued."""
+    from chunk_sparse_attention_amd import _lib
+    wl = W("decode_host_kv", 1, 256, 8, 2, 64, 64, 2, torch.bfloat16)
+    x = workloads.make_decode_inputs(wl, seed=1)
+    q, qs, Kc = (x[k].to(dev) for k in ("q", "qs", "Kc"))
+    Kslc = hsa.pool(Kc)
+    prob = hsa.problem(1, 256, 8, 2, 64, 2, torch.bfloat16)
+    out = torch.empty((1, 8, 64), dtype=torch.bfloat16, device=dev)
+    small = torch.empty((1, 2, 2), dtype=torch.float32, device=dev)
+    idx = torch.empty((1, 2, 2), dtype=torch.int32, device=dev)
+    ws = hsa.workspace(_lib.HSA_OP_DECODE, prob, dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    L = _lib.lib()
+    for kc in (x["Kc"], Kc):  # pageable host memory, then device memory
+        st = L.hsa_decode_host_kv(ctypes.byref(prob), P(q), P(qs), P(kc), P(kc), P(Kslc),
+                                  P(out), P(idx), None, P(small), P(ws), ws.numel(),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == _lib.HSA_ERR_INVALID_ARG, L.hsa_last_error()
+        assert b"Kcache" in L.hsa_last_error()
+    # the library still works afterwards
+    O, i2, _, _ = hsa.decode(q, qs, Kc, x["Vc"].to(dev), Kslc, 2)
+    torch.cuda.synchronize()
+    assert O.shape == (1, 8, 64)
 
 
 @pytest.mark.parametrize("shape", [
