@@ -103,6 +103,14 @@ def _i32(x):
     return np.ascontiguousarray(x, dtype=np.int32)
 
 
+def _wmode(weights: str) -> int:
+    """Chunk-weight mode of the C oracle: 0 stick-breaking, 1 softmax."""
+    modes = {"stick": 0, "softmax": 1}
+    if weights not in modes:
+        raise ValueError(f"weights must be one of {sorted(modes)}")
+    return modes[weights]
+
+
 def _mask(x):
     if x is None:
         return None
@@ -120,16 +128,17 @@ class Oracle:
         lib.oracle_pool.restype = None
         lib.oracle_pool.argtypes = [_P, _I, _I, _I, _I, _I, _I, _I, _P]
         lib.oracle_select.restype = None
-        lib.oracle_select.argtypes = [_P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I, _P, _P, _P, _P]
+        lib.oracle_select.argtypes = [_P, _I, _P, _I, _I, _I, _I, _I, _I, _D, _I, _I, _P, _P, _P,
+                                      _P]
         lib.oracle_attend.restype = None
         lib.oracle_attend.argtypes = [_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D,
                                       _P, _P, _P]
         lib.oracle_bwd.restype = None
         lib.oracle_bwd.argtypes = [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
-                                   _I, _I, _D, _D, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+                                   _I, _I, _D, _D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         lib.oracle_decode.restype = None
         lib.oracle_decode.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _D, _D,
-                                      _I, _P, _P, _P, _P]
+                                      _I, _I, _P, _P, _P, _P]
         self.lib = lib
 
     # -- elementwise -------------------------------------------------------------------
@@ -151,9 +160,10 @@ class Oracle:
 
     # -- F2-F4 ---------------------------------------------------------------------------
     def select(self, Qs, Kslc, S: int, K: int, sel_scale: float | None = None,
-               score_dt: int = F32, row_mask=None):
-        """Top-K chunk selection + stick-breaking weights.
-        Returns (idx int32, score f64, w f64), each [B, L, Hkv, K]."""
+               score_dt: int = F32, row_mask=None, weights: str = "stick"):
+        """Top-K chunk selection + chunk weights (weights="stick": stick-breaking, "softmax":
+        softmax of the valid slots' scores).  Returns (idx int32, score f64, w f64), each
+        [B, L, Hkv, K]."""
         qs, dt = _as_storage(Qs)
         B, L, Hkv, D = qs.shape
         ks = _f64(Kslc)
@@ -165,7 +175,8 @@ class Oracle:
         w = np.zeros((B, L, Hkv, K), np.float64)
         m = _mask(row_mask)
         self.lib.oracle_select(_ptr(qs), dt, _ptr(ks), B, L, Hkv, D, S, K, float(sel_scale),
-                               score_dt, _ptr(m), _ptr(idx), _ptr(score), _ptr(w))
+                               score_dt, _wmode(weights), _ptr(m), _ptr(idx), _ptr(score),
+                               _ptr(w))
         return idx, score, w
 
     # -- F5-F6 ---------------------------------------------------------------------------
@@ -192,16 +203,17 @@ class Oracle:
         return (O, Ok) if per_slot else O
 
     def forward(self, Q, Kmat, V, Qs, S: int, K: int, sm_scale=None, sel_scale=None,
-                score_dt: int = F32, row_mask=None):
+                score_dt: int = F32, row_mask=None, weights: str = "stick"):
         """pool -> select -> attend.  Returns dict(Kslc, idx, score, w, O)."""
         Kslc = self.pool(Kmat, S)
-        idx, score, w = self.select(Qs, Kslc, S, K, sel_scale, score_dt, row_mask)
+        idx, score, w = self.select(Qs, Kslc, S, K, sel_scale, score_dt, row_mask, weights)
         O = self.attend(Q, Kmat, V, idx, w, S, sm_scale, row_mask)
         return dict(Kslc=Kslc, idx=idx, score=score, w=w, O=O)
 
     # -- B1-B5 ---------------------------------------------------------------------------
     def backward(self, Q, Kmat, V, Qs, Kslc, idx, score, w, dO, S: int, sm_scale=None,
-                 sel_scale=None, fold: bool = True, tok_mask=None, chunk_mask=None):
+                 sel_scale=None, fold: bool = True, tok_mask=None, chunk_mask=None,
+                 weights: str = "stick"):
         """Gradients with the selection held fixed.  Returns dict(dQ, dK, dV, dQs, dKslc, dw,
         ds) as float64 arrays."""
         q, dt = _as_storage(Q)
@@ -229,14 +241,15 @@ class Oracle:
         cm = _mask(chunk_mask)
         self.lib.oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(qs), dt, _ptr(ks), _ptr(idx_),
                             _ptr(sc), _ptr(w_), _ptr(do), B, L, Hq, Hkv, D, S, Kt,
-                            float(sm_scale), float(sel_scale), int(bool(fold)), _ptr(tm), _ptr(cm),
+                            float(sm_scale), float(sel_scale), int(bool(fold)), _wmode(weights),
+                            _ptr(tm), _ptr(cm),
                             _ptr(out["dQ"]), _ptr(out["dK"]), _ptr(out["dV"]), _ptr(out["dQs"]),
                             _ptr(out["dKslc"]), _ptr(out["dw"]), _ptr(out["ds"]))
         return out
 
     # -- decode --------------------------------------------------------------------------
     def decode(self, q, qs, Kc, Vc, Kslc, S: int, K: int, sm_scale=None, sel_scale=None,
-               score_dt: int = F32):
+               score_dt: int = F32, weights: str = "stick"):
         """One new query per sequence at position ctx.  Returns dict(O, idx, score, w)."""
         q_, dt = _as_storage(q)
         qs_, _ = _as_storage(qs)
@@ -255,7 +268,8 @@ class Oracle:
         score = np.full((B, Hkv, K), -np.inf)
         w = np.zeros((B, Hkv, K))
         self.lib.oracle_decode(_ptr(q_), _ptr(qs_), _ptr(kc), _ptr(vc), dt, _ptr(ks), B, ctx, Hq,
-                               Hkv, D, S, K, float(sm_scale), float(sel_scale), score_dt, _ptr(O),
+                               Hkv, D, S, K, float(sm_scale), float(sel_scale), score_dt,
+                               _wmode(weights), _ptr(O),
                                _ptr(idx), _ptr(score), _ptr(w))
         return dict(O=O, idx=idx, score=score, w=w)
 

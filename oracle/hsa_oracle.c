@@ -28,6 +28,8 @@
  *     remaining slots masked (idx -1, score -inf, weight 0).
  *   - ranking is by score descending, ties toward the lower chunk index; stick-breaking
  *     runs over the slots in that rank order; a NaN score ranks as -inf.
+ *   - the softmax variant of the chunk weights is a plain softmax of the valid slots'
+ *     selection scores (no temperature), masked slots 0.
  *   - the chunk key is the plain mean of the chunk's S key rows, rounded once (to nearest,
  *     ties to even) to the storage type of the inputs; selection scores are rounded to fp32
  *     before ranking, the precision in which the GPU library takes the same decision.
@@ -128,6 +130,23 @@ static void stick_breaking(const double* s, int n_valid, double* w) {
   }
 }
 
+/* The softmax variant of the chunk weights: w_k = exp(s_k) / sum_j exp(s_j) over the valid
+ * slots, evaluated with the shift m = max_j s_j (all weights 0 if every score is -inf)
+ * [HSA-atlas, "Measured effects reported in the paper": the ablation that replaces the
+ * stick-breaking weights with a softmax; HSA-note 亮点: softmax vs stick-breaking]. */
+enum { ORC_W_STICK = 0, ORC_W_SOFTMAX = 1 };
+static void softmax_weights(const double* s, int n_valid, double* w) {
+  double m = -INFINITY;
+  for (int k = 0; k < n_valid; ++k)
+    if (s[k] > m) m = s[k];
+  double den = 0.0;
+  for (int k = 0; k < n_valid; ++k) {
+    w[k] = m == -INFINITY ? 0.0 : exp(s[k] - m);
+    den += w[k];
+  }
+  for (int k = 0; k < n_valid; ++k) w[k] = den > 0.0 ? w[k] / den : 0.0;
+}
+
 /* Number of chunks token t may select (causal: strictly earlier, complete chunks). */
 static int n_available(int t, int S, int nC) {
   int n = MUT(4) ? t / S + 1 : t / S;
@@ -145,8 +164,8 @@ static double sel_score(const void* Qs, int dt, size_t qoff, const double* krow,
 }
 
 /* Fill one row's K slots from an array of scored candidates. */
-static void select_row(cand_t* cand, int n_avail, int Kt, int32_t* idx, double* score,
-                       double* w) {
+static void select_row(cand_t* cand, int n_avail, int Kt, int wmode, int32_t* idx,
+                       double* score, double* w) {
   qsort(cand, (size_t)n_avail, sizeof(cand_t), cand_cmp);
   int n_valid = n_avail < Kt ? n_avail : Kt;
   double sv[64];
@@ -156,7 +175,10 @@ static void select_row(cand_t* cand, int n_avail, int Kt, int32_t* idx, double* 
     sv[k] = cand[k].s;
   }
   double wv[64];
-  stick_breaking(sv, n_valid, wv);
+  if (wmode == ORC_W_SOFTMAX)
+    softmax_weights(sv, n_valid, wv);
+  else
+    stick_breaking(sv, n_valid, wv);
   for (int k = 0; k < Kt; ++k) {
     if (k < n_valid) {
       w[k] = wv[k];
@@ -173,8 +195,8 @@ static void select_row(cand_t* cand, int n_avail, int Kt, int32_t* idx, double* 
  * [HSA-note 层次化稀疏注意力（HSA）, "Chunk Selection"]: every token scores each chunk's
  * pooled key with its selection query and keeps the top-K, separately per query group. */
 void oracle_select(const void* Qs, int dt, const double* Kslc, int B, int L, int Hkv, int D,
-                   int S, int Kt, double sel_scale, int score_dt, const uint8_t* row_mask,
-                   int32_t* idx, double* score, double* w) {
+                   int S, int Kt, double sel_scale, int score_dt, int wmode,
+                   const uint8_t* row_mask, int32_t* idx, double* score, double* w) {
   int nC = L / S;
 #pragma omp parallel
   {
@@ -192,7 +214,7 @@ void oracle_select(const void* Qs, int dt, const double* Kslc, int B, int L, int
             cand[c].c = c;
           }
           size_t o = (((size_t)b * L + t) * Hkv + g) * Kt;
-          select_row(cand, n_avail, Kt, idx + o, score + o, w + o);
+          select_row(cand, n_avail, Kt, wmode, idx + o, score + o, w + o);
         }
       }
     free(cand);
@@ -281,6 +303,7 @@ void oracle_attend(const void* Q, const void* K, const void* V, int dt, const in
  *   dQ_h += sm_scale sum_j dz_j k_j;   dK_j += sm_scale dz_j q_h;   dV_j += w_k a_j dO_h
  *   dw_k = sum_{h in g} D_hk
  *   ds_k = dw_k w_k (1 - p_k) - p_k sum_{k'>k} dw_{k'} w_{k'}   (stick-breaking chain rule)
+ *   ds_k = w_k (dw_k - sum_j w_j dw_j)                           (softmax weights, wmode 1)
  *   dQs += sel_scale ds_k Kslc_c;  dKslc_c += sel_scale ds_k Qs_t
  * With fold != 0 the pooled-key gradient flows on into the keys: dK_j += dKslc_c / S for
  * every row j of chunk c (the chunk key is the mean of those rows).
@@ -295,9 +318,9 @@ void oracle_attend(const void* Q, const void* K, const void* V, int dt, const in
 void oracle_bwd(const void* Q, const void* K, const void* V, const void* Qs, int dt,
                 const double* Kslc, const int32_t* idx, const double* score,
                 const double* w, const void* dO, int B, int L, int Hq, int Hkv, int D, int S,
-                int Kt, double sm_scale, double sel_scale, int fold, const uint8_t* tok_mask,
-                const uint8_t* chunk_mask, double* dQ, double* dK, double* dV, double* dQs,
-                double* dKslc, double* dw, double* ds) {
+                int Kt, double sm_scale, double sel_scale, int fold, int wmode,
+                const uint8_t* tok_mask, const uint8_t* chunk_mask, double* dQ, double* dK,
+                double* dV, double* dQs, double* dKslc, double* dw, double* ds) {
   int nC = L / S;
   int G = Hq / Hkv;
   size_t kstride = (size_t)Hkv * D;
@@ -347,16 +370,26 @@ void oracle_bwd(const void* Q, const void* K, const void* V, const void* Qs, int
             }
           }
         }
-        /* stick-breaking backward over the valid slots (they are a prefix) */
-        double suffix = 0.0; /* sum_{k'>k} dw_k' w_k' */
-        for (int k = Kt - 1; k >= 0; --k) {
-          if (idx[so + k] < 0) {
-            ds[so + k] = 0.0;
-            continue;
+        if (wmode == ORC_W_SOFTMAX) {
+          /* softmax backward over the valid slots */
+          double mean = 0.0; /* sum_j w_j dw_j */
+          for (int k = 0; k < Kt; ++k)
+            if (idx[so + k] >= 0) mean += w[so + k] * dw[so + k];
+          for (int k = 0; k < Kt; ++k)
+            ds[so + k] = idx[so + k] < 0 ? 0.0
+                                         : w[so + k] * (dw[so + k] - (MUT(11) ? 0.0 : mean));
+        } else {
+          /* stick-breaking backward over the valid slots (they are a prefix) */
+          double suffix = 0.0; /* sum_{k'>k} dw_k' w_k' */
+          for (int k = Kt - 1; k >= 0; --k) {
+            if (idx[so + k] < 0) {
+              ds[so + k] = 0.0;
+              continue;
+            }
+            double p = sigmoid(score[so + k]);
+            ds[so + k] = dw[so + k] * w[so + k] * (1.0 - p) - (MUT(6) ? 0.0 : p * suffix);
+            suffix += dw[so + k] * w[so + k];
           }
-          double p = sigmoid(score[so + k]);
-          ds[so + k] = dw[so + k] * w[so + k] * (1.0 - p) - (MUT(6) ? 0.0 : p * suffix);
-          suffix += dw[so + k] * w[so + k];
         }
         if (want_q) {
           double* dqs = dQs + (((size_t)b * L + t) * Hkv + g) * D;
@@ -438,8 +471,8 @@ void oracle_bwd(const void* Q, const void* K, const void* V, const void* Qs, int
  * Out: O [B, Hq, D], idx/score/w [B, Hkv, Kt]. */
 void oracle_decode(const void* q, const void* qs, const void* Kc, const void* Vc, int dt,
                    const double* Kslc, int B, int ctx, int Hq, int Hkv, int D, int S, int Kt,
-                   double sm_scale, double sel_scale, int score_dt, double* O, int32_t* idx,
-                   double* score, double* w) {
+                   double sm_scale, double sel_scale, int score_dt, int wmode, double* O,
+                   int32_t* idx, double* score, double* w) {
   int nC = ctx / S;
   int n_avail = n_available(ctx, S, nC);
   size_t kstride = (size_t)Hkv * D;
@@ -454,7 +487,7 @@ void oracle_decode(const void* q, const void* qs, const void* Kc, const void* Vc
         cand[c].c = c;
       }
       size_t so = ((size_t)b * Hkv + g) * Kt;
-      select_row(cand, n_avail, Kt, idx + so, score + so, w + so);
+      select_row(cand, n_avail, Kt, wmode, idx + so, score + so, w + so);
       free(cand);
       double a[1024];
       for (int h = 0; h < Hq; ++h) {

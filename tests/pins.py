@@ -169,6 +169,41 @@ def pin_stick_breaking_identities(orc):
     assert np.array_equal(idx, idx2)
 
 
+def pin_softmax_weights_identities(orc):
+    """The softmax variant of the chunk weights: the same selection as stick-breaking, every
+    row's valid weights positive and summing to 1, and closed forms: Qs = 0 gives each of a
+    row's n valid slots 1/n; K = 1 gives weight 1."""
+    gen = torch.Generator().manual_seed(21)
+    S, K, D = 8, 6, 16
+    L = 12 * S
+    Kmat = _rand(gen, (2, L, 2, D), 1.0, torch.float32)
+    Qs = _rand(gen, (2, L, 2, D), 3.0, torch.float32)
+    ks = orc.pool(Kmat, S)
+    idx, score, w = orc.select(Qs, ks, S, K, weights="softmax")
+    idx_sb, _, _ = orc.select(Qs, ks, S, K)
+    assert np.array_equal(idx, idx_sb)
+    valid = idx >= 0
+    assert np.all(w[valid] > 0) and np.all(w[~valid] == 0)
+    rows = valid.any(-1)
+    assert np.allclose(w.sum(-1)[rows], 1.0, rtol=0, atol=1e-14)
+    # the log-weights of a row differ by the score differences (base e, increasing in s)
+    both = valid[..., 1:] & valid[..., :1]
+    dlog = np.log(np.where(valid, w, 1.0))
+    sv = np.where(valid, score, 0.0)
+    gap = (dlog[..., 1:] - dlog[..., :1]) - (sv[..., 1:] - sv[..., :1])
+    assert np.allclose(np.where(both, gap, 0.0), 0.0, rtol=0, atol=1e-12)
+    assert np.all(w.sum(-1)[~rows] == 0)
+    # Qs = 0: every score 0, uniform weights over the n_avail = min(K, t // S) slots
+    _, _, w0 = orc.select(torch.zeros_like(Qs), ks, S, K, weights="softmax")
+    for t in range(L):
+        n = min(K, t // S)
+        expect = np.array([1.0 / n] * n + [0.0] * (K - n)) if n else np.zeros(K)
+        assert np.allclose(w0[:, t], expect, rtol=0, atol=1e-15), t
+    # K = 1: the single slot takes all the weight
+    idx1, _, w1 = orc.select(Qs, ks, S, 1, weights="softmax")
+    assert np.all(w1[idx1 >= 0] == 1.0) and np.all(w1[idx1 < 0] == 0.0)
+
+
 # ----------------------------------------------------------------------------------------
 # F5-F6 attention
 # ----------------------------------------------------------------------------------------
@@ -295,8 +330,9 @@ def pin_permutation_within_chunk(orc):
 # ----------------------------------------------------------------------------------------
 # B1-B5 backward
 # ----------------------------------------------------------------------------------------
-def _loss_and_grads(orc, Q, Km, V, Qs, dO, S, K, sm, sel):
-    f = orc.forward(Q, Km, V, Qs, S, K, sm_scale=sm, sel_scale=sel, score_dt=F64)
+def _loss_and_grads(orc, Q, Km, V, Qs, dO, S, K, sm, sel, weights="stick"):
+    f = orc.forward(Q, Km, V, Qs, S, K, sm_scale=sm, sel_scale=sel, score_dt=F64,
+                    weights=weights)
     loss = float((f["O"] * dO.numpy()).sum())
     return f, loss
 
@@ -306,7 +342,17 @@ def pin_backward_finite_differences(orc):
     forward (pool -> select -> attend, in float64 with no score rounding), for directional
     derivatives along random directions in Q, K, V and Qs.  The chosen inputs have no
     near-ties, so the ranking is constant over the step."""
-    gen = torch.Generator().manual_seed(10)
+    _finite_differences(orc, "stick", 10)
+
+
+def pin_backward_finite_differences_softmax(orc):
+    """The same check with the softmax chunk weights: it pins their chain rule into the
+    selection scores (and so dQs and the pooled-key gradient)."""
+    _finite_differences(orc, "softmax", 11)
+
+
+def _finite_differences(orc, weights, seed):
+    gen = torch.Generator().manual_seed(seed)
     B, S, Hq, Hkv, D, K = 1, 8, 4, 2, 8, 3
     L = 7 * S
     Q = _rand(gen, (B, L, Hq, D), 1.0)
@@ -315,9 +361,9 @@ def pin_backward_finite_differences(orc):
     Qs = _rand(gen, (B, L, Hkv, D), 2.0)
     dO = _rand(gen, (B, L, Hq, D), 1.0)
     sm, sel = 0.35, 0.5
-    f, _ = _loss_and_grads(orc, Q, Km, V, Qs, dO, S, K, sm, sel)
+    f, _ = _loss_and_grads(orc, Q, Km, V, Qs, dO, S, K, sm, sel, weights)
     g = orc.backward(Q, Km, V, Qs, f["Kslc"], f["idx"], f["score"], f["w"], dO, S, sm, sel,
-                     fold=True)
+                     fold=True, weights=weights)
     eps = 1e-6
     for name in ("Q", "K", "V", "Qs"):
         for trial in range(3):
@@ -327,8 +373,10 @@ def pin_backward_finite_differences(orc):
             minus = dict(args)
             plus[name] = args[name] + eps * d
             minus[name] = args[name] - eps * d
-            fp, lp = _loss_and_grads(orc, plus["Q"], plus["K"], plus["V"], plus["Qs"], dO, S, K, sm, sel)
-            fm, lm = _loss_and_grads(orc, minus["Q"], minus["K"], minus["V"], minus["Qs"], dO, S, K, sm, sel)
+            fp, lp = _loss_and_grads(orc, plus["Q"], plus["K"], plus["V"], plus["Qs"], dO, S, K,
+                                     sm, sel, weights)
+            fm, lm = _loss_and_grads(orc, minus["Q"], minus["K"], minus["V"], minus["Qs"], dO, S,
+                                     K, sm, sel, weights)
             assert np.array_equal(fp["idx"], f["idx"]) and np.array_equal(fm["idx"], f["idx"])
             fd = (lp - lm) / (2 * eps)
             grad = {"Q": g["dQ"], "K": g["dK"], "V": g["dV"], "Qs": g["dQs"]}[name]
@@ -424,14 +472,15 @@ def pin_decode_equals_forward_row(orc):
     Km = _rand(gen, (1, L, Hkv, D), 0.5, torch.bfloat16)
     V = _rand(gen, (1, L, Hkv, D), 0.5, torch.bfloat16)
     Qs = _rand(gen, (1, L, Hkv, D), 1.0, torch.bfloat16)
-    f = orc.forward(Q, Km, V, Qs, S, K)
-    for t in (S - 1, S, 3 * S + 2, 7 * S, L - 1):
-        ctx = t
-        ks = orc.pool(Km[:, :ctx], S)
-        d = orc.decode(Q[:, t], Qs[:, t], Km[:, :ctx], V[:, :ctx], ks, S, K)
-        assert np.array_equal(d["idx"], f["idx"][:, t]), t
-        assert np.allclose(d["w"], f["w"][:, t], rtol=0, atol=0), t
-        assert np.allclose(d["O"], f["O"][:, t], rtol=1e-13, atol=1e-14), t
+    for weights in ("stick", "softmax"):
+        f = orc.forward(Q, Km, V, Qs, S, K, weights=weights)
+        for t in (S - 1, S, 3 * S + 2, 7 * S, L - 1):
+            ctx = t
+            ks = orc.pool(Km[:, :ctx], S)
+            d = orc.decode(Q[:, t], Qs[:, t], Km[:, :ctx], V[:, :ctx], ks, S, K, weights=weights)
+            assert np.array_equal(d["idx"], f["idx"][:, t]), t
+            assert np.allclose(d["w"], f["w"][:, t], rtol=0, atol=0), t
+            assert np.allclose(d["O"], f["O"][:, t], rtol=1e-13, atol=1e-14), t
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -17,6 +17,7 @@ MUTATIONS = {
     8: "selection-query gradient uses Qs instead of the chunk key",
     9: "query head mapped to group h % Hkv",
     10: "logit scale dropped",
+    11: "softmax-weight backward drops the weighted mean of dw",
 }
 
 
