@@ -16,7 +16,8 @@ the average launch time over a second pass of as many steps, run after the timed
 the HIP events libhsa.so records around each of its launches on the launch's own stream
 (hsa_timer_enable / hsa_timer_read); its
 algorithmic bytes and flops per launch are the workload's, from kernel_counts().  "kernels"
-holds the same for every kernel class, "secondary" the select+fwd+bwd pass of the L=65536,
+holds the same for every kernel class, "softmax_weights" the step with the softmax chunk
+weights (HSA_FLAG_SOFTMAX_WEIGHTS), "secondary" the select+fwd+bwd pass of the L=65536,
 d=128 workload (tokens/s of the whole pass and of select+fwd), "decode" the 1M-context decode
 step.  cpu_baseline times the CPU oracle (test
 infrastructure) on the same workload; it is a reported baseline, not the target.
@@ -543,6 +544,23 @@ def main() -> int:
     dominant = max(kern, key=lambda k: kern[k]["ms_per_step"])
     roof = {k: v for k, v in kern[dominant].items() if k not in ("launches_per_step",)}
 
+    # the same step with the softmax chunk weights (HSA_FLAG_SOFTMAX_WEIGHTS): select's extra
+    # weight pass and the backward's other chain rule
+    def step_softmax():
+        Kslc, idx, score, w = hsa.select(Qs, K, wl.K, generic=gen, weights="softmax")
+        hsa.fwd(Q, K, V, idx, w, generic=gen, ws=ws_bwd)
+        hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, generic=gen, ws=ws_bwd, after_fwd=True,
+                weights="softmax")
+
+    for _ in range(2):
+        step_softmax()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_softmax()
+    torch.cuda.synchronize()
+    sm_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
     tokens = wl.B * wl.L
     out = {
         "metric": METRIC,
@@ -565,6 +583,8 @@ def main() -> int:
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "entry_ms": entry_ms,
         "kernels": kern,
+        "softmax_weights": {"ms_per_step": round(sm_ms, 4),
+                            "tokens_per_s": round(tokens / (sm_ms / 1e3), 1)},
     }
 
     if not args.no_secondary:

@@ -18,6 +18,7 @@ HSA_OK, HSA_ERR_INVALID_ARG, HSA_ERR_UNSUPPORTED, HSA_ERR_WORKSPACE, HSA_ERR_HIP
 HSA_F32, HSA_BF16 = 0, 1
 HSA_OP_SELECT, HSA_OP_FWD, HSA_OP_BWD, HSA_OP_DECODE = range(4)
 HSA_FLAG_GENERIC = 0x1
+HSA_FLAG_SOFTMAX_WEIGHTS = 0x2
 HSA_BWD_FOLD_KSLC = 0x1
 HSA_BWD_AFTER_FWD = 0x2
 

@@ -312,7 +312,7 @@ __global__ void __launch_bounds__(64) k_bwd_p1_generic(
     const float* __restrict__ score, const float* __restrict__ w, const T* __restrict__ dO,
     T* __restrict__ dQ, T* __restrict__ dQs, float* __restrict__ ds_out,
     float* __restrict__ dw_out, int L, int Hq, int Hkv, int D, int S, int Kt, int G, int nC,
-    float sm_scale, float sel_scale) {
+    float sm_scale, float sel_scale, int softmax_w) {
   __shared__ float qsh[kMaxG][128];
   __shared__ float dosh[kMaxG][128];
   __shared__ float dzsh[kMaxG][kChunk];
@@ -399,9 +399,25 @@ __global__ void __launch_bounds__(64) k_bwd_p1_generic(
       if (D > 64) dQ[qbase + (size_t)h * D + 64 + lane] = from_f32<T>(dq[h][1] * sm_scale);
     }
   }
+  // softmax weights: ds_k = w_k (dw_k - sum_j w_j dw_j) over the valid slots (slot order)
+  if (lane == 0 && softmax_w) {
+    double mean = 0.0;
+    for (int k = 0; k < Kt; ++k) {
+      const int c = idx[row * Kt + k];
+      if (c >= 0 && c < nC) mean += (double)dwsh[k] * (double)w[row * Kt + k];
+    }
+    for (int k = 0; k < Kt; ++k) {
+      const int c = idx[row * Kt + k];
+      const bool ok = c >= 0 && c < nC;
+      const double dsk = ok ? (double)w[row * Kt + k] * ((double)dwsh[k] - mean) : 0.0;
+      dssh[k] = (float)dsk;
+      ds_out[row * Kt + k] = (float)dsk;
+      dw_out[row * Kt + k] = ok ? dwsh[k] : 0.0f;
+    }
+  }
   // stick-breaking chain rule over the valid prefix, newest slot first:
   // ds_k = dw_k w_k (1 - p_k) - p_k * sum_{k' > k} dw_k' w_k'
-  if (lane == 0) {
+  if (lane == 0 && !softmax_w) {
     double suffix = 0.0;
     for (int k = Kt - 1; k >= 0; --k) {
       int c = idx[row * Kt + k];
@@ -637,7 +653,7 @@ static void launch_p1_generic(const Dims& d, const BwdLayout& lay, const void* Q
   k_bwd_p1_generic<T><<<dim3((unsigned)rows), 64, 0, s>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)Kslc, idx, score, w, (const T*)dO,
       (T*)dQ, (T*)dQs, (float*)(ws + lay.ds), (float*)(ws + lay.dw), d.L, d.Hq, d.Hkv, d.D, d.S,
-      d.K, d.G, d.nC, (float)d.sm_scale, (float)d.sel_scale);
+      d.K, d.G, d.nC, (float)d.sm_scale, (float)d.sel_scale, softmax_w(d));
 }
 
 template <typename T>

@@ -550,7 +550,7 @@ __global__ void __launch_bounds__(256) k_bwd_tok(
     const int32_t* __restrict__ idx, const float* __restrict__ score,
     const float* __restrict__ w, const bf16* __restrict__ Kslc, bf16* __restrict__ dQ,
     bf16* __restrict__ dQs, float* __restrict__ ds_out, int L, int Hkv, int Kn, int nC,
-    int64_t rows, float sm_scale, float sel_scale) {
+    int64_t rows, float sm_scale, float sel_scale, int softmax_w) {
   constexpr int E = G * D / 64;  // elements of the row's G x D block per lane
   constexpr int F = D / 64;      // features of dQs per lane: lane + 64 f
   const int lane = threadIdx.x % 64;
@@ -591,19 +591,30 @@ __global__ void __launch_bounds__(256) k_bwd_tok(
 #pragma unroll
   for (int j = 0; j < E; ++j) acc[j] *= sm_scale;
   store_row<E>(dQ + bt * (int64_t)Hkv * G * D + (size_t)g * G * D + (size_t)lane * E, acc);
-  // ds_k = dw_k w_k (1 - p_k) - p_k * sum_{k' > k} dw_k' w_k'  (fp64, suffix from the last slot)
+  // stick-breaking: ds_k = dw_k w_k (1 - p_k) - p_k * sum_{k' > k} dw_k' w_k'  (fp64, suffix
+  // from the last slot); softmax weights: ds_k = w_k (dw_k - sum_j w_j dw_j)  (fp64, slot order)
   const double dww = valid ? (double)dwk * (double)wk : 0.0;
   const int2 dwi = __builtin_bit_cast(int2, dww);
-  double suffix = 0.0;
-  for (int k2 = Kn - 1; k2 >= 0; --k2) {
-    const int2 vi = make_int2(__builtin_amdgcn_readlane(dwi.x, k2),
-                              __builtin_amdgcn_readlane(dwi.y, k2));
-    if (k2 > lane) suffix += __builtin_bit_cast(double, vi);
+  double suffix = 0.0, mean = 0.0;
+  if (softmax_w) {
+    for (int k2 = 0; k2 < Kn; ++k2)
+      mean += __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readlane(dwi.x, k2),
+                                                   __builtin_amdgcn_readlane(dwi.y, k2)));
+  } else {
+    for (int k2 = Kn - 1; k2 >= 0; --k2) {
+      const int2 vi = make_int2(__builtin_amdgcn_readlane(dwi.x, k2),
+                                __builtin_amdgcn_readlane(dwi.y, k2));
+      if (k2 > lane) suffix += __builtin_bit_cast(double, vi);
+    }
   }
   float dsk = 0.0f;
   if (valid) {
-    const double p = sigmoid_d((double)sk);
-    dsk = (float)(dww * (1.0 - p) - p * suffix);
+    if (softmax_w) {
+      dsk = (float)((double)wk * ((double)dwk - mean));
+    } else {
+      const double p = sigmoid_d((double)sk);
+      dsk = (float)(dww * (1.0 - p) - p * suffix);
+    }
   }
   if (lane < Kn) ds_out[o + lane] = dsk;
   // dQs (features lane + 64 f), slots in order; the rows of the valid slots load together
@@ -750,7 +761,7 @@ static hipError_t launch_bwd_fused(const Dims& d, const BwdLayout& lay, const vo
       kern<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(
           (const bf16*)(ws + lay.dq_part), (const float*)(ws + lay.dw), idx, score, w,
           (const bf16*)Kslc, (bf16*)dQ, (bf16*)dQs, (float*)(ws + lay.ds), d.L, d.Hkv, d.K,
-          d.nC, rows, (float)d.sm_scale, (float)d.sel_scale);
+          d.nC, rows, (float)d.sm_scale, (float)d.sel_scale, softmax_w(d));
     };
     if (d.D == 64) {
       if (d.G == 4) go(k_bwd_tok<64, 4>);

@@ -221,7 +221,7 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
     const T* __restrict__ q, const T* __restrict__ Kc, const T* __restrict__ Vc,
     const uint64_t* __restrict__ cand, T* __restrict__ O, int32_t* __restrict__ idx,
     float* __restrict__ score, float* __restrict__ w, int ctx, int Hq, int Hkv, int K, int G,
-    int HW, int n_hg, int n_cand, float c2) {
+    int HW, int n_hg, int n_cand, float c2, int softmax_w) {
   constexpr int P = D / 8;
   constexpr int JG = kWave / P;
   constexpr int RPL = kChunk / JG;  // rows per lane in the value product
@@ -239,18 +239,31 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
 
   const uint64_t mykey =
       n_cand > 0 ? rank_candidates(cand + (size_t)bg * n_cand, n_cand, K, lane) : 0;
-  // stick-breaking in rank order: slot k needs p_k * prod_{j<k} (1 - p_j), a prefix
-  // product over lanes 0..K-1 (masked slots have p = 0 and come last)
-  const double p = mykey != 0 ? sigmoid_d((double)key_score(mykey)) : 0.0;
-  double keep = 1.0 - p;
+  double wslot;
+  if (softmax_w) {
+    // softmax of the valid slots' scores (lanes 0..K-1), shifted by their maximum and
+    // summed in slot order
+    const double sc = mykey != 0 ? (double)key_score(mykey) : -__builtin_inf();
+    double m = -__builtin_inf();
+    for (int j = 0; j < K; ++j) m = fmax(m, __shfl(sc, j));
+    const double e = (mykey != 0 && m != -__builtin_inf()) ? exp(sc - m) : 0.0;
+    double den = 0.0;
+    for (int j = 0; j < K; ++j) den += __shfl(e, j);
+    wslot = den > 0.0 ? e / den : 0.0;
+  } else {
+    // stick-breaking in rank order: slot k needs p_k * prod_{j<k} (1 - p_j), a prefix
+    // product over lanes 0..K-1 (masked slots have p = 0 and come last)
+    const double p = mykey != 0 ? sigmoid_d((double)key_score(mykey)) : 0.0;
+    double keep = 1.0 - p;
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    const double x = __shfl_up(keep, o, 16);
-    if ((lane & 15) >= o) keep *= x;
+    for (int o = 1; o < 16; o <<= 1) {
+      const double x = __shfl_up(keep, o, 16);
+      if ((lane & 15) >= o) keep *= x;
+    }
+    double excl = __shfl_up(keep, 1, 16);
+    if ((lane & 15) == 0) excl = 1.0;
+    wslot = p * excl;
   }
-  double excl = __shfl_up(keep, 1, 16);
-  if ((lane & 15) == 0) excl = 1.0;
-  const double wslot = p * excl;
   if (hg == 0 && slot == 0 && lane < K) {
     const size_t o = (size_t)bg * K + lane;
     if (mykey == 0) {
@@ -395,7 +408,8 @@ static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, cons
     const int n_hg = (d.G + HW - 1) / HW;
     kern<<<dim3(bg * n_hg), kWave * d.K, 0, s>>>((const T*)q, (const T*)Kc, (const T*)Vc, cand,
                                                  (T*)O, idx, score, w, d.L, d.Hq, d.Hkv, d.K,
-                                                 d.G, HW, n_hg, n_blocks * d.K, c2);
+                                                 d.G, HW, n_hg, n_blocks * d.K, c2,
+                                                 softmax_w(d));
   };
   constexpr int ZW = 8;  // heads per block for host caches, up to 8 slots
   if (d.K > 8) go(k_dec_attend_heads<T, D, 4, 1024>, 4);

@@ -74,7 +74,7 @@ __global__ void __launch_bounds__(64) k_dec_attend(
     const T* __restrict__ q, const T* __restrict__ Kc, const T* __restrict__ Vc,
     const uint64_t* __restrict__ cand, T* __restrict__ O, int32_t* __restrict__ idx,
     float* __restrict__ score, float* __restrict__ w, int ctx, int Hq, int Hkv, int D, int S,
-    int K, int G, int nC, int n_blocks, float sm_scale) {
+    int K, int G, int nC, int n_blocks, float sm_scale, int softmax_w) {
   __shared__ float qsh[kMaxG][128];
   __shared__ float ash[kMaxG][kChunk];
   __shared__ int sidx[kMaxK];
@@ -96,6 +96,14 @@ __global__ void __launch_bounds__(64) k_dec_attend(
   }
   __syncthreads();
   if (lane == 0) {
+    // softmax weights: the valid slots' largest score and the sum of their exponentials
+    double m = -__builtin_inf(), den = 0.0;
+    if (softmax_w) {
+      for (int k = 0; k < K; ++k)
+        if (skey[k] != 0) m = fmax(m, (double)key_score(skey[k]));
+      for (int k = 0; k < K; ++k)
+        if (skey[k] != 0 && m != -__builtin_inf()) den += exp((double)key_score(skey[k]) - m);
+    }
     double remaining = 1.0;
     for (int k = 0; k < K; ++k) {
       const uint64_t key = skey[k];
@@ -108,9 +116,14 @@ __global__ void __launch_bounds__(64) k_dec_attend(
         w[o] = 0.0f;
       } else {
         const float s = key_score(key);
-        const double p = sigmoid_d((double)s);
-        const float wk = (float)(p * remaining);
-        remaining *= 1.0 - p;
+        float wk;
+        if (softmax_w) {
+          wk = den > 0.0 ? (float)(exp((double)s - m) / den) : 0.0f;
+        } else {
+          const double p = sigmoid_d((double)s);
+          wk = (float)(p * remaining);
+          remaining *= 1.0 - p;
+        }
         sidx[k] = key_chunk(key);
         sw[k] = wk;
         idx[o] = key_chunk(key);
@@ -197,7 +210,8 @@ hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void
     Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
     k_dec_attend<bf16><<<dim3(bg), 64, 0, s>>>((const bf16*)q, (const bf16*)Kc, (const bf16*)Vc,
                                                cand, (bf16*)O, idx, score, w, d.L, d.Hq, d.Hkv,
-                                               d.D, d.S, d.K, d.G, d.nC, lay.n_blocks, sm);
+                                               d.D, d.S, d.K, d.G, d.nC, lay.n_blocks, sm,
+                                               softmax_w(d));
   } else {
     {
       Timed tm(HSA_KERNEL_DECODE_SCAN, s);
@@ -208,7 +222,7 @@ hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void
     Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
     k_dec_attend<float><<<dim3(bg), 64, 0, s>>>(
         (const float*)q, (const float*)Kc, (const float*)Vc, cand, (float*)O, idx, score, w,
-        d.L, d.Hq, d.Hkv, d.D, d.S, d.K, d.G, d.nC, lay.n_blocks, sm);
+        d.L, d.Hq, d.Hkv, d.D, d.S, d.K, d.G, d.nC, lay.n_blocks, sm, softmax_w(d));
   }
   return hipGetLastError();
 }

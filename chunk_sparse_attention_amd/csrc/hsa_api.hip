@@ -58,6 +58,8 @@ hsa_status_t check_problem(int op, const hsa_problem_t* p, hsa::Dims* d) {
     return fail(HSA_ERR_UNSUPPORTED, "L*K=%lld does not fit int32", (long long)p->L * p->K);
   if ((int64_t)p->B * p->L * p->Hkv >= ((int64_t)1 << 31))
     return fail(HSA_ERR_UNSUPPORTED, "B*L*Hkv rows exceed the grid limit");
+  if (p->flags & ~(HSA_FLAG_GENERIC | HSA_FLAG_SOFTMAX_WEIGHTS))
+    return fail(HSA_ERR_INVALID_ARG, "unknown problem flags 0x%x", p->flags);
   if (!isfinite(p->sm_scale) || !isfinite(p->sel_scale))
     return fail(HSA_ERR_INVALID_ARG, "scales must be finite");
   const int nC = p->L / p->S;
@@ -184,11 +186,15 @@ HSA_EXPORT hsa_status_t hsa_select(const hsa_problem_t* p, const void* Qs, const
     if (e != hipSuccess) return launched(e, "pool");
   }
   if (!Qs) return ok();
+  hipError_t e;
   if (hsa::select_mfma_supported(d))
-    return launched(hsa::launch_select_mfma(d, Qs, Kslc, idx, score, w, s), "select");
-  if (hsa::select_tile_supported(d))
-    return launched(hsa::launch_select_tile(d, Qs, Kslc, idx, score, w, s), "select");
-  return launched(hsa::launch_select_generic(d, Qs, Kslc, idx, score, w, s), "select");
+    e = hsa::launch_select_mfma(d, Qs, Kslc, idx, score, w, s);
+  else if (hsa::select_tile_supported(d))
+    e = hsa::launch_select_tile(d, Qs, Kslc, idx, score, w, s);
+  else
+    e = hsa::launch_select_generic(d, Qs, Kslc, idx, score, w, s);
+  if (e == hipSuccess && hsa::softmax_w(d)) e = hsa::launch_softmax_weights(d, idx, score, w, s);
+  return launched(e, "select");
 }
 
 HSA_EXPORT hsa_status_t hsa_fwd(const hsa_problem_t* p, const void* Q, const void* K,

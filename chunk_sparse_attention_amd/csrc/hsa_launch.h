@@ -78,6 +78,12 @@ struct DecLayout {
 };
 DecLayout dec_layout(const Dims& d);
 
+// 1 when the chunk weights are the softmax of the selected scores (HSA_FLAG_SOFTMAX_WEIGHTS).
+inline int softmax_w(const Dims& d) { return (d.flags & HSA_FLAG_SOFTMAX_WEIGHTS) ? 1 : 0; }
+// Rewrites w of every (token, group) row as the softmax of its valid slots' scores.
+hipError_t launch_softmax_weights(const Dims& d, const int32_t* idx, const float* score,
+                                  float* w, hipStream_t s);
+
 // F1 pooling (both dtypes).
 hipError_t launch_pool(const Dims& d, const void* K, void* Kslc, hipStream_t s);
 

@@ -122,6 +122,38 @@ __global__ void __launch_bounds__(64) k_select_generic(const T* __restrict__ Qs,
   }
 }
 
+// Softmax chunk weights of one (token, group) row per thread from its written scores: with
+// m the largest valid score, w_k = exp(s_k - m) / sum_j exp(s_j - m) over the valid slots
+// (fp64, summed in slot order); masked slots, and rows whose scores are all -inf, get 0.
+__global__ void __launch_bounds__(256) k_softmax_weights(const int32_t* __restrict__ idx,
+                                                         const float* __restrict__ score,
+                                                         float* __restrict__ w, int64_t rows,
+                                                         int K) {
+  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  const int64_t o = row * K;
+  double m = -__builtin_inf();
+  for (int k = 0; k < K; ++k)
+    if (idx[o + k] >= 0) m = fmax(m, (double)score[o + k]);
+  const bool any = m != -__builtin_inf();
+  double den = 0.0;
+  for (int k = 0; k < K; ++k)
+    if (idx[o + k] >= 0 && any) den += exp((double)score[o + k] - m);
+  for (int k = 0; k < K; ++k)
+    w[o + k] = (idx[o + k] >= 0 && den > 0.0) ? (float)(exp((double)score[o + k] - m) / den)
+                                              : 0.0f;
+}
+
+hipError_t launch_softmax_weights(const Dims& d, const int32_t* idx, const float* score,
+                                  float* w, hipStream_t s) {
+  const int64_t rows = (int64_t)d.B * d.L * d.Hkv;
+  if (rows == 0) return hipSuccess;
+  Timed tm(HSA_KERNEL_SELECT, s);
+  k_softmax_weights<<<dim3((unsigned)((rows + 255) / 256)), 256, 0, s>>>(idx, score, w, rows,
+                                                                          d.K);
+  return hipGetLastError();
+}
+
 hipError_t launch_select_generic(const Dims& d, const void* Qs, const void* Kslc, int32_t* idx,
                                  float* score, float* w, hipStream_t s) {
   size_t rows = (size_t)d.B * d.L * d.Hkv;

@@ -47,13 +47,18 @@ def _need(t, name, dtype=None, shape=None, device=None):
 
 
 def problem(B, L, Hq, Hkv, D, K, dtype, sm_scale=None, sel_scale=None, generic=False,
-            S=S_CHUNK) -> Problem:
+            S=S_CHUNK, weights="stick") -> Problem:
+    """weights: "stick" (stick-breaking chunk weights) or "softmax" (a softmax of the
+    selected chunks' scores, HSA_FLAG_SOFTMAX_WEIGHTS)."""
     if dtype not in _DT:
         raise TypeError(f"unsupported dtype {dtype}")
+    if weights not in ("stick", "softmax"):
+        raise ValueError(f"weights must be 'stick' or 'softmax', not {weights!r}")
+    flags = (_lib.HSA_FLAG_GENERIC if generic else 0) | (
+        _lib.HSA_FLAG_SOFTMAX_WEIGHTS if weights == "softmax" else 0)
     return Problem(int(B), int(L), int(Hq), int(Hkv), int(D), int(S), int(K),
                    0.0 if sm_scale is None else float(sm_scale),
-                   0.0 if sel_scale is None else float(sel_scale), _DT[dtype],
-                   _lib.HSA_FLAG_GENERIC if generic else 0)
+                   0.0 if sel_scale is None else float(sel_scale), _DT[dtype], flags)
 
 
 def workspace_size(op: int, prob: Problem) -> int:
@@ -88,12 +93,14 @@ def pool(K: torch.Tensor, K_top: int = 1, generic=False) -> torch.Tensor:
 
 
 def select(Qs: torch.Tensor, K: torch.Tensor, K_top: int, sel_scale=None, generic=False,
-           ws=None):
-    """Pool + top-K selection + stick-breaking weights.  Returns (Kslc, idx, score, w)."""
+           ws=None, weights="stick"):
+    """Pool + top-K selection + chunk weights (stick-breaking, or softmax with
+    weights="softmax").  Returns (Kslc, idx, score, w)."""
     _need(K, "K")
     B, L, Hkv, D = K.shape
     _need(Qs, "Qs", K.dtype, (B, L, Hkv, D), K.device)
-    prob = problem(B, L, Hkv, Hkv, D, K_top, K.dtype, sel_scale=sel_scale, generic=generic)
+    prob = problem(B, L, Hkv, Hkv, D, K_top, K.dtype, sel_scale=sel_scale, generic=generic,
+                   weights=weights)
     dev = K.device
     Kslc = torch.empty((B, L // S_CHUNK, Hkv, D), dtype=K.dtype, device=dev)
     idx = torch.empty((B, L, Hkv, K_top), dtype=torch.int32, device=dev)
@@ -128,8 +135,9 @@ def fwd(Q, K, V, idx, w, sm_scale=None, generic=False, ws=None, out=None):
 
 
 def bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, fold=True, want_dkslc=True, sm_scale=None,
-        sel_scale=None, generic=False, ws=None, after_fwd=False):
+        sel_scale=None, generic=False, ws=None, after_fwd=False, weights="stick"):
     """Gradients with the selection fixed.  Returns dict(dQ, dK, dV, dQs, dKslc).
+    weights: the chunk-weight rule select() used ("stick" or "softmax").
 
     after_fwd=True: `ws` is the workspace that fwd() just used for the same Q, K, idx and w
     (allocate it with workspace(HSA_OP_BWD, ...), which also fits the forward); the backward
@@ -146,7 +154,7 @@ def bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, fold=True, want_dkslc=True, sm_sca
     _need(score, "score", torch.float32, (B, L, Hkv, Kt), dev)
     _need(w, "w", torch.float32, (B, L, Hkv, Kt), dev)
     prob = problem(B, L, Hq, Hkv, D, Kt, Q.dtype, sm_scale=sm_scale, sel_scale=sel_scale,
-                   generic=generic)
+                   generic=generic, weights=weights)
     dQ = torch.empty_like(Q)
     dK = torch.empty_like(K)
     dV = torch.empty_like(V)
@@ -166,7 +174,8 @@ def bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, fold=True, want_dkslc=True, sm_sca
     return dict(dQ=dQ, dK=dK, dV=dV, dQs=dQs, dKslc=dKslc)
 
 
-def decode(q, qs, Kc, Vc, Kslc, K_top, sm_scale=None, sel_scale=None, generic=False, ws=None):
+def decode(q, qs, Kc, Vc, Kslc, K_top, sm_scale=None, sel_scale=None, generic=False, ws=None,
+           weights="stick"):
     """One decode step: q [B,Hq,D], qs [B,Hkv,D], caches [B,ctx,Hkv,D], Kslc [B,ctx//64,Hkv,D].
     Returns (O [B,Hq,D], idx, score, w [B,Hkv,K])."""
     _need(Kc, "Kcache")
@@ -178,7 +187,7 @@ def decode(q, qs, Kc, Vc, Kslc, K_top, sm_scale=None, sel_scale=None, generic=Fa
     _need(Vc, "Vcache", Kc.dtype, (B, ctx, Hkv, D), dev)
     _need(Kslc, "Kslc", Kc.dtype, (B, ctx // S_CHUNK, Hkv, D), dev)
     prob = problem(B, ctx, Hq, Hkv, D, K_top, Kc.dtype, sm_scale=sm_scale, sel_scale=sel_scale,
-                   generic=generic)
+                   generic=generic, weights=weights)
     O = torch.empty((B, Hq, D), dtype=Kc.dtype, device=dev)
     idx = torch.empty((B, Hkv, K_top), dtype=torch.int32, device=dev)
     score = torch.empty((B, Hkv, K_top), dtype=torch.float32, device=dev)
@@ -193,7 +202,7 @@ def decode(q, qs, Kc, Vc, Kslc, K_top, sm_scale=None, sel_scale=None, generic=Fa
 
 
 def decode_host_kv(q, qs, Kc, Vc, Kslc, K_top, sm_scale=None, sel_scale=None, generic=False,
-                   ws=None):
+                   ws=None, weights="stick"):
     """decode() with the caches Kc, Vc [B,ctx,Hkv,D] in pinned host memory (CPU tensors made
     with pin_memory); the step reads only the selected chunks' rows of them.  q, qs and Kslc
     are GPU tensors.  Returns (O [B,Hq,D], idx, score, w [B,Hkv,K])."""
@@ -212,7 +221,7 @@ def decode_host_kv(q, qs, Kc, Vc, Kslc, K_top, sm_scale=None, sel_scale=None, ge
     _need(qs, "qs", Kc.dtype, (B, Hkv, D), dev)
     _need(Kslc, "Kslc", Kc.dtype, (B, ctx // S_CHUNK, Hkv, D), dev)
     prob = problem(B, ctx, Hq, Hkv, D, K_top, Kc.dtype, sm_scale=sm_scale, sel_scale=sel_scale,
-                   generic=generic)
+                   generic=generic, weights=weights)
     O = torch.empty((B, Hq, D), dtype=Kc.dtype, device=dev)
     idx = torch.empty((B, Hkv, K_top), dtype=torch.int32, device=dev)
     score = torch.empty((B, Hkv, K_top), dtype=torch.float32, device=dev)

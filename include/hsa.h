@@ -73,6 +73,12 @@ typedef enum { HSA_OP_SELECT = 0, HSA_OP_FWD = 1, HSA_OP_BWD = 2, HSA_OP_DECODE 
 
 /* hsa_problem_t.flags */
 #define HSA_FLAG_GENERIC 0x1u /* use the plain vector-ALU kernels even where MFMA kernels exist */
+/* Chunk weights as a softmax of the valid slots' selection scores instead of stick-breaking
+ * (the variant of the pages' weights ablation: atlas summary, measured effects; note
+ * section 亮点): hsa_select and hsa_decode write them, hsa_bwd differentiates them
+ * (ds_k = w_k (dw_k - sum_j w_j dw_j)); hsa_fwd takes whatever w it is given.  Give the same
+ * flag to the select and the backward of one step. */
+#define HSA_FLAG_SOFTMAX_WEIGHTS 0x2u
 
 /* hsa_bwd flags */
 #define HSA_BWD_FOLD_KSLC 0x1u /* add dKslc/S into every key row of the chunk (Kslc = mean K) */
@@ -115,7 +121,8 @@ hsa_status_t hsa_workspace_size(int op, const hsa_problem_t* p, size_t* bytes);
  *   Kslc  [B, nC, Hkv, D] dtype out: chunk keys (mean of each chunk's key rows)
  *   idx   [B, L, Hkv, K] int32 out: selected chunks in rank order, -1 = masked
  *   score [B, L, Hkv, K] fp32  out: their scores, -inf = masked
- *   w     [B, L, Hkv, K] fp32  out: stick-breaking weights, 0 = masked
+ *   w     [B, L, Hkv, K] fp32  out: stick-breaking weights (softmax weights with
+ *                                 HSA_FLAG_SOFTMAX_WEIGHTS), 0 = masked
  * With Qs == NULL only Kslc is written and idx/score/w may be NULL (used to build the
  * resident chunk table for decode); otherwise all must be non-NULL. */
 hsa_status_t hsa_select(const hsa_problem_t* p, const void* Qs, const void* K, void* Kslc,

@@ -94,6 +94,10 @@ def test_entry_points_reject_before_launch():
     st = lib.hsa_decode(ctypes.byref(_prob(D=80)), fake, fake, fake, fake, fake, fake, fake, None,
                         fake, fake, 1 << 30, None)
     assert st == 2
+    bad = _prob()
+    bad.flags = 0x4  # no such problem flag
+    st = lib.hsa_select(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, 0, None)
+    assert st == 1 and b"unknown problem flags" in lib.hsa_last_error()
     st = lib.hsa_decode_host_kv(ctypes.byref(_prob(D=80)), fake, fake, fake, fake, fake, fake,
                                 fake, None, fake, fake, 1 << 30, None)
     assert st == 2

@@ -50,21 +50,23 @@ def head_mask(row_mask_bLg, G):
     return np.repeat(row_mask_bLg, G, axis=2)
 
 
-def gpu_forward(hsa, x, wl, dev, generic=False):
+def gpu_forward(hsa, x, wl, dev, generic=False, weights="stick"):
     Q, K, V, Qs = (x[k].to(dev) for k in ("Q", "K", "V", "Qs"))
-    Kslc, idx, score, w = hsa.select(Qs, K, wl.K, generic=generic)
+    Kslc, idx, score, w = hsa.select(Qs, K, wl.K, generic=generic, weights=weights)
     O = hsa.fwd(Q, K, V, idx, w, generic=generic)
     return dict(Q=Q, K=K, V=V, Qs=Qs, Kslc=Kslc, idx=idx, score=score, w=w, O=O)
 
 
-def compare_forward(orc, x, wl, g, row_mask=None, out_mask=None):
+def compare_forward(orc, x, wl, g, row_mask=None, out_mask=None, weights="stick"):
     """Selection on the rows of row_mask (default: all), outputs on those of out_mask
     (default: row_mask)."""
     if out_mask is None:
-        f = orc.forward(x["Q"], x["K"], x["V"], x["Qs"], wl.S, wl.K, row_mask=row_mask)
+        f = orc.forward(x["Q"], x["K"], x["V"], x["Qs"], wl.S, wl.K, row_mask=row_mask,
+                        weights=weights)
     else:
         Kslc = orc.pool(x["K"], wl.S)
-        idx, score, w = orc.select(x["Qs"], Kslc, wl.S, wl.K, row_mask=row_mask)
+        idx, score, w = orc.select(x["Qs"], Kslc, wl.S, wl.K, row_mask=row_mask,
+                                   weights=weights)
         O = orc.attend(x["Q"], x["K"], x["V"], idx, w, wl.S, row_mask=out_mask)
         f = dict(Kslc=Kslc, idx=idx, score=score, w=w, O=O)
     near = near_tie_rows(orc, x["Qs"], f["Kslc"], wl.S, wl.K, row_mask=row_mask)
@@ -83,9 +85,10 @@ def compare_forward(orc, x, wl, g, row_mask=None, out_mask=None):
     return f, diff, rep
 
 
-def compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=None, chunk_mask=None):
+def compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=None, chunk_mask=None,
+                     weights="stick"):
     o = orc.backward(x["Q"], x["K"], x["V"], x["Qs"], f["Kslc"], f["idx"], f["score"], f["w"],
-                     x["dO"], wl.S, tok_mask=tok_mask, chunk_mask=chunk_mask)
+                     x["dO"], wl.S, tok_mask=tok_mask, chunk_mask=chunk_mask, weights=weights)
     tol = tol_for(wl.dtype)
     B, L, nC = wl.B, wl.L, wl.nC
     tm = np.ones((B, L), bool) if tok_mask is None else np.asarray(tok_mask, bool).reshape(B, L)
@@ -307,6 +310,47 @@ def test_decode_small(hsa, dev, ctx, generic):
     ks = orc.pool(x["Kc"], 64)
     assert np.array_equal(npy(Kslc), ks)
     d = orc.decode(x["q"], x["qs"], x["Kc"], x["Vc"], ks, 64, wl.K)
+    assert np.array_equal(npy(idx), d["idx"])
+    assert max_abs(npy(w), d["w"]) <= 1e-5
+    assert max_abs(npy(O), d["O"]) <= 2e-2
+
+
+SOFTMAX_CASES = [w for w in SMALL if w.name in ("tiny_fp32", "bf16_d64_ragged", "bf16_d128_ragged",
+                                               "bf16_g1_k3", "fp32_k1", "bf16_d64_g16_k16")]
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
+@pytest.mark.parametrize("wl", SOFTMAX_CASES, ids=lambda w: w.name)
+def test_softmax_weights_end_to_end(hsa, dev, wl, generic):
+    """HSA_FLAG_SOFTMAX_WEIGHTS: selection, softmax chunk weights, attention and the
+    backward through the softmax chain rule against the oracle's softmax mode."""
+    say("case softmax weights", wl, "generic" if generic else "default")
+    orc = oracle.get()
+    x = workloads.make_inputs(wl, seed=3)
+    g = gpu_forward(hsa, x, wl, dev, generic, weights="softmax")
+    grads = hsa.bwd(g["Q"], g["K"], g["V"], g["Qs"], g["Kslc"], g["idx"], g["score"], g["w"],
+                    x["dO"].to(dev), generic=generic, weights="softmax")
+    torch.cuda.synchronize()
+    f, diff, _ = compare_forward(orc, x, wl, g, weights="softmax")
+    w = npy(g["w"])
+    rows = (npy(g["idx"]) >= 0).any(-1)
+    assert np.allclose(w.sum(-1)[rows], 1.0, atol=1e-5)
+    compare_backward(orc, x, wl, g, f, diff, grads, weights="softmax")
+
+
+@pytest.mark.parametrize("ctx", [40, 64 * 7 + 13, 64 * 33])
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
+def test_decode_softmax_weights(hsa, dev, ctx, generic):
+    wl = W("decode_softmax", 3, ctx, 16, 2, 64, 64, 8, torch.bfloat16)
+    say("case decode softmax", ctx, generic)
+    x = workloads.make_decode_inputs(wl, seed=8, ctx=ctx)
+    q, qs, Kc, Vc = (x[k].to(dev) for k in ("q", "qs", "Kc", "Vc"))
+    Kslc = hsa.pool(Kc)
+    O, idx, score, w = hsa.decode(q, qs, Kc, Vc, Kslc, wl.K, generic=generic, weights="softmax")
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    ks = orc.pool(x["Kc"], 64)
+    d = orc.decode(x["q"], x["qs"], x["Kc"], x["Vc"], ks, 64, wl.K, weights="softmax")
     assert np.array_equal(npy(idx), d["idx"])
     assert max_abs(npy(w), d["w"]) <= 1e-5
     assert max_abs(npy(O), d["O"]) <= 2e-2
