@@ -367,6 +367,20 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
     torch.cuda.synchronize()
     hms = e0.elapsed_time(e1) / reps
     del Kh, Vh
+    # sequences of different lengths in the same cache (hsa_decode_ragged): lengths drawn
+    # uniformly from [ctx/2, ctx] with a fixed seed
+    g = torch.Generator().manual_seed(1)
+    lens = torch.randint(wl3.L // 2, wl3.L + 1, (wl3.B,), generator=g, dtype=torch.int32)
+    ctx_lens = lens.to(dev)
+    for _ in range(3):
+        hsa.decode_ragged(q, qs, Kc, Vc, Kslc3, ctx_lens, wl3.K, generic=gen, ws=ws3)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        hsa.decode_ragged(q, qs, Kc, Vc, Kslc3, ctx_lens, wl3.K, generic=gen, ws=ws3)
+    e1.record()
+    torch.cuda.synchronize()
+    rms = e0.elapsed_time(e1) / reps
     el = 2
     # the chunk-key table, the selected chunks' K and V, q, qs and O
     dbytes = (wl3.B * wl3.nC * wl3.Hkv * wl3.D * el
@@ -380,7 +394,9 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
             "scan_ms": round(kt3["decode_scan"][1] / max(n3, 1), 4),
             "attend_ms": round(kt3["decode_attend"][1] / max(n3, 1), 4),
             "host_kv": {"ms": round(hms, 4), "vs_device_kv": round(hms / dms, 3),
-                        "link_bytes_per_step": 2 * wl3.B * wl3.Hkv * wl3.K * wl3.S * wl3.D * el}}
+                        "link_bytes_per_step": 2 * wl3.B * wl3.Hkv * wl3.K * wl3.S * wl3.D * el},
+            "ragged": {"ms": round(rms, 4), "mean_ctx": round(float(lens.double().mean()), 1),
+                       "lengths": "uniform in [ctx/2, ctx], seed 1"}}
 
 
 def main() -> int:

@@ -77,13 +77,15 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(4)))
 k_dec_scan_fast(const T* __restrict__ qs, const T* __restrict__ Kslc,
                 uint64_t* __restrict__ cand, int Hkv, int K, int nC, int n_blocks,
-                double sel_scale) {
+                double sel_scale, const int32_t* __restrict__ ctx_lens) {
   __shared__ double qsh[D];
   const int blk = blockIdx.x % n_blocks;
   const int bg = blockIdx.x / n_blocks;
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  // chunks this sequence may select: all nC of the table, or those below its own length
+  const int nCb = ctx_lens ? min(nC, max(0, ctx_lens[b]) / kChunk) : nC;
   for (int e = tid; e < D; e += kScanThreads)
     qsh[e] = (double)to_f32(qs[((size_t)b * Hkv + g) * D + e]);
 
@@ -102,7 +104,7 @@ k_dec_scan_fast(const T* __restrict__ qs, const T* __restrict__ Kslc,
     RawRow<T, DP> row[kScanPer];
 #pragma unroll
     for (int i = 0; i < kScanPer; ++i)
-      if (cs[i] < nC) row[i].load(Kslc + ((b * nC + cs[i]) * Hkv + g) * D + d0);
+      if (cs[i] < nCb) row[i].load(Kslc + ((b * nC + cs[i]) * Hkv + g) * D + d0);
     if (d0 == 0) __syncthreads();  // qsh ready
     // the dimension loop is outermost so that only eight query values are live at a time
 #pragma unroll
@@ -119,7 +121,7 @@ k_dec_scan_fast(const T* __restrict__ qs, const T* __restrict__ Kslc,
   uint64_t key[kScanPer];
 #pragma unroll
   for (int i = 0; i < kScanPer; ++i)
-    key[i] = cs[i] < nC ? rank_key((float)(sel_scale * dot[i]), cs[i]) : 0;
+    key[i] = cs[i] < nCb ? rank_key((float)(sel_scale * dot[i]), cs[i]) : 0;
   // lane-local descending order, then K rounds of a wave maximum over the lane heads
 #pragma unroll
   for (int i = 0; i < kScanPer; ++i)
@@ -385,7 +387,8 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
 template <typename T, int D>
 static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, const void* Kc,
                               const void* Vc, const void* Kslc, void* O, int32_t* idx,
-                              float* score, float* w, bool host_kv, char* ws, hipStream_t s) {
+                              float* score, float* w, bool host_kv, const int32_t* ctx_lens,
+                              char* ws, hipStream_t s) {
   const int bg = d.B * d.Hkv;
   const DecFastLayout lay = dec_fast_layout(d);
   const int n_blocks = lay.n_blocks;
@@ -393,7 +396,7 @@ static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, cons
   if (n_blocks > 0) {
     Timed tm(HSA_KERNEL_DECODE_SCAN, s);
     k_dec_scan_fast<T, D><<<dim3(bg * n_blocks), kScanThreads, 0, s>>>(
-        (const T*)qs, (const T*)Kslc, cand, d.Hkv, d.K, d.nC, n_blocks, d.sel_scale);
+        (const T*)qs, (const T*)Kslc, cand, d.Hkv, d.K, d.nC, n_blocks, d.sel_scale, ctx_lens);
   }
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);
   Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
@@ -419,12 +422,13 @@ static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, cons
 
 hipError_t launch_decode_fast(const Dims& d, const void* q, const void* qs, const void* Kc,
                               const void* Vc, const void* Kslc, void* O, int32_t* idx,
-                              float* score, float* w, bool host_kv, char* ws, hipStream_t s) {
+                              float* score, float* w, bool host_kv, const int32_t* ctx_lens,
+                              char* ws, hipStream_t s) {
   if (d.B * d.Hkv == 0) return hipSuccess;
   auto go = [&](auto tag, auto dim) {
     using T = decltype(tag);
     launch_dec_fast_t<T, decltype(dim)::value>(d, q, qs, Kc, Vc, Kslc, O, idx, score, w,
-                                               host_kv, ws, s);
+                                               host_kv, ctx_lens, ws, s);
   };
   using D64 = std::integral_constant<int, 64>;
   using D128 = std::integral_constant<int, 128>;

@@ -29,7 +29,8 @@ __global__ void __launch_bounds__(256) k_dec_scan(const T* __restrict__ qs,
                                                   const T* __restrict__ Kslc,
                                                   uint64_t* __restrict__ cand, int Hkv, int D,
                                                   int K, int nC, int n_blocks,
-                                                  double sel_scale) {
+                                                  double sel_scale,
+                                                  const int32_t* __restrict__ ctx_lens) {
   __shared__ double qsh[128];
   __shared__ uint64_t wbest[4][kMaxK];
   const int blk = blockIdx.x % n_blocks;
@@ -40,8 +41,10 @@ __global__ void __launch_bounds__(256) k_dec_scan(const T* __restrict__ qs,
   for (int e = tid; e < D; e += blockDim.x) qsh[e] = (double)to_f32(qs[((size_t)b * Hkv + g) * D + e]);
   __syncthreads();
   const int c = blk * kDecChunksPerBlock + tid;
+  // chunks this sequence may select: all nC of the table, or those below its own length
+  const int nCb = ctx_lens ? min(nC, max(0, ctx_lens[b]) / kChunk) : nC;
   uint64_t key = 0;
-  if (c < nC) {
+  if (c < nCb) {
     const T* kr = Kslc + ((b * nC + c) * Hkv + g) * D;
     double dot = 0.0;
     for (int e = 0; e < D; e += 8) {
@@ -194,7 +197,7 @@ __global__ void __launch_bounds__(64) k_dec_attend(
 hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void* q,
                                  const void* qs, const void* Kc, const void* Vc,
                                  const void* Kslc, void* O, int32_t* idx, float* score,
-                                 float* w, char* ws, hipStream_t s) {
+                                 float* w, const int32_t* ctx_lens, char* ws, hipStream_t s) {
   const int bg = d.B * d.Hkv;
   if (bg == 0) return hipSuccess;
   uint64_t* cand = (uint64_t*)(ws + lay.cand);
@@ -205,7 +208,7 @@ hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void
       Timed tm(HSA_KERNEL_DECODE_SCAN, s);
       k_dec_scan<bf16><<<dim3(bg * lay.n_blocks), 256, 0, s>>>(
           (const bf16*)qs, (const bf16*)Kslc, cand, d.Hkv, d.D, d.K, d.nC, lay.n_blocks,
-          d.sel_scale);
+          d.sel_scale, ctx_lens);
     }
     Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
     k_dec_attend<bf16><<<dim3(bg), 64, 0, s>>>((const bf16*)q, (const bf16*)Kc, (const bf16*)Vc,
@@ -217,7 +220,7 @@ hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void
       Timed tm(HSA_KERNEL_DECODE_SCAN, s);
       k_dec_scan<float><<<dim3(bg * lay.n_blocks), 256, 0, s>>>(
           (const float*)qs, (const float*)Kslc, cand, d.Hkv, d.D, d.K, d.nC, lay.n_blocks,
-          d.sel_scale);
+          d.sel_scale, ctx_lens);
     }
     Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
     k_dec_attend<float><<<dim3(bg), 64, 0, s>>>(

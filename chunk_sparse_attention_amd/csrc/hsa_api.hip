@@ -281,7 +281,7 @@ namespace {
 hsa_status_t decode_impl(const hsa_problem_t* p, const void* q, const void* qs,
                          const void* Kcache, const void* Vcache, const void* Kslc, void* O,
                          int32_t* idx, float* score, float* w, void* ws, size_t ws_bytes,
-                         hsa_stream_t stream, bool host_kv) {
+                         hsa_stream_t stream, bool host_kv, const int32_t* ctx_lens) {
   hsa::Dims d;
   TRY(check_problem(HSA_OP_DECODE, p, &d));
   TRY(need_tensor(q, "q"));
@@ -298,11 +298,11 @@ hsa_status_t decode_impl(const hsa_problem_t* p, const void* q, const void* qs,
   hipStream_t s = (hipStream_t)stream;
   if (!(d.flags & HSA_FLAG_GENERIC))
     return launched(hsa::launch_decode_fast(d, q, qs, Kcache, Vcache, Kslc, O, idx, score, w,
-                                            host_kv, (char*)ws, s),
+                                            host_kv, ctx_lens, (char*)ws, s),
                     "decode");
   hsa::DecLayout lay = hsa::dec_layout(d);
   return launched(hsa::launch_decode_generic(d, lay, q, qs, Kcache, Vcache, Kslc, O, idx, score,
-                                             w, (char*)ws, s),
+                                             w, ctx_lens, (char*)ws, s),
                   "decode");
 }
 
@@ -313,7 +313,7 @@ HSA_EXPORT hsa_status_t hsa_decode(const hsa_problem_t* p, const void* q, const 
                                    void* O, int32_t* idx, float* score, float* w, void* ws,
                                    size_t ws_bytes, hsa_stream_t stream) {
   return decode_impl(p, q, qs, Kcache, Vcache, Kslc, O, idx, score, w, ws, ws_bytes, stream,
-                     false);
+                     false, nullptr);
 }
 
 HSA_EXPORT hsa_status_t hsa_decode_host_kv(const hsa_problem_t* p, const void* q,
@@ -330,5 +330,31 @@ HSA_EXPORT hsa_status_t hsa_decode_host_kv(const hsa_problem_t* p, const void* q
   TRY(host_view(Vcache, "Vcache", &vd));
   if (!aligned(kd, 16) || !aligned(vd, 16))
     return fail(HSA_ERR_INVALID_ARG, "the device view of the caches is not 16-byte aligned");
-  return decode_impl(p, q, qs, kd, vd, Kslc, O, idx, score, w, ws, ws_bytes, stream, true);
+  return decode_impl(p, q, qs, kd, vd, Kslc, O, idx, score, w, ws, ws_bytes, stream, true,
+                     nullptr);
+}
+
+HSA_EXPORT hsa_status_t hsa_decode_ragged(const hsa_problem_t* p, const int32_t* ctx_lens,
+                                          const void* q, const void* qs, const void* Kcache,
+                                          const void* Vcache, const void* Kslc, void* O,
+                                          int32_t* idx, float* score, float* w, void* ws,
+                                          size_t ws_bytes, hsa_stream_t stream) {
+  TRY(need_small(ctx_lens, "ctx_lens"));
+  return decode_impl(p, q, qs, Kcache, Vcache, Kslc, O, idx, score, w, ws, ws_bytes, stream,
+                     false, ctx_lens);
+}
+
+HSA_EXPORT hsa_status_t hsa_pool_chunks(const hsa_problem_t* p, const void* K, void* Kslc,
+                                        const int32_t* chunk_ids, int n_ids,
+                                        hsa_stream_t stream) {
+  hsa::Dims d;
+  TRY(check_problem(HSA_OP_SELECT, p, &d));
+  TRY(need_tensor(K, "K"));
+  if (d.nC > 0) TRY(need_tensor(Kslc, "Kslc"));
+  TRY(need_small(chunk_ids, "chunk_ids"));
+  if (n_ids < 1 || n_ids > (d.nC > 1 ? d.nC : 1))
+    return fail(HSA_ERR_INVALID_ARG, "n_ids=%d is outside [1, max(nC, 1)]", n_ids);
+  TRY(check_pending());
+  return launched(hsa::launch_pool_chunks(d, K, Kslc, chunk_ids, n_ids, (hipStream_t)stream),
+                  "pool_chunks");
 }

@@ -86,6 +86,9 @@ hipError_t launch_softmax_weights(const Dims& d, const int32_t* idx, const float
 
 // F1 pooling (both dtypes).
 hipError_t launch_pool(const Dims& d, const void* K, void* Kslc, hipStream_t s);
+// Pooling of listed chunks only: chunk_ids [B, n_ids] (device); entries outside [0, nC) skip.
+hipError_t launch_pool_chunks(const Dims& d, const void* K, void* Kslc, const int32_t* chunk_ids,
+                              int n_ids, hipStream_t s);
 
 // Generic vector-ALU kernels (fp32 and bf16).
 hipError_t launch_select_generic(const Dims& d, const void* Qs, const void* Kslc, int32_t* idx,
@@ -143,13 +146,15 @@ hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const vo
 
 // Decode with a bandwidth-shaped scan and one wave per kept slot (both dtypes).
 size_t dec_fast_ws(const Dims& d);
-// host_kv: Kc and Vc are the device's view of page-locked host memory.
+// host_kv: Kc and Vc are the device's view of page-locked host memory.  ctx_lens (device,
+// [B], or NULL): sequence b may select only chunks below ctx_lens[b] / S.
 hipError_t launch_decode_fast(const Dims& d, const void* q, const void* qs, const void* Kc,
                               const void* Vc, const void* Kslc, void* O, int32_t* idx,
-                              float* score, float* w, bool host_kv, char* ws, hipStream_t s);
+                              float* score, float* w, bool host_kv, const int32_t* ctx_lens,
+                              char* ws, hipStream_t s);
 hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void* q,
                                  const void* qs, const void* Kc, const void* Vc,
                                  const void* Kslc, void* O, int32_t* idx, float* score,
-                                 float* w, char* ws, hipStream_t s);
+                                 float* w, const int32_t* ctx_lens, char* ws, hipStream_t s);
 
 }  // namespace hsa

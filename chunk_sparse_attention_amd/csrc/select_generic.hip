@@ -14,6 +14,25 @@ namespace hsa {
 // runs in fp64 in row order so the result is the exact mean for any bf16/fp32 chunk in
 // practice, rounded once to the storage type.  Consecutive threads read consecutive e
 // (coalesced), and sixteen rows' loads are in flight at a time.
+// Feature e of the chunk key of (b, chunk c, group g): the mean of the chunk's S key rows,
+// summed in row order in fp64 and rounded once.
+template <typename T>
+__device__ __forceinline__ T pool_one(const T* __restrict__ K, int L, int Hkv, int D, size_t b,
+                                      int c, int g, int e) {
+  const T* src = K + ((b * L + (size_t)c * kChunk) * Hkv + g) * D + e;
+  const size_t stride = (size_t)Hkv * D;
+  // sixteen rows' loads in flight at a time; the sum stays in row order
+  double sum = 0.0;
+  for (int j0 = 0; j0 < kChunk; j0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = to_f32(src[(size_t)(j0 + u) * stride]);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) sum += (double)v[u];
+  }
+  return from_f64<T>(sum / kChunk);
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) k_pool(const T* __restrict__ K, T* __restrict__ Kslc,
                                               int L, int Hkv, int D, int S, int nC,
@@ -26,18 +45,7 @@ __global__ void __launch_bounds__(256) k_pool(const T* __restrict__ K, T* __rest
   r /= Hkv;
   int c = (int)(r % nC);
   size_t b = r / nC;
-  const T* src = K + ((b * L + (size_t)c * kChunk) * Hkv + g) * D + e;
-  const size_t stride = (size_t)Hkv * D;
-  // sixteen rows' loads in flight at a time; the sum stays in row order
-  double sum = 0.0;
-  for (int j0 = 0; j0 < kChunk; j0 += 16) {
-    float v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = to_f32(src[(size_t)(j0 + u) * stride]);
-#pragma unroll
-    for (int u = 0; u < 16; ++u) sum += (double)v[u];
-  }
-  Kslc[i] = from_f64<T>(sum / kChunk);
+  Kslc[i] = pool_one(K, L, Hkv, D, b, c, g, e);
 }
 
 hipError_t launch_pool(const Dims& d, const void* K, void* Kslc, hipStream_t s) {
@@ -51,6 +59,40 @@ hipError_t launch_pool(const Dims& d, const void* K, void* Kslc, hipStream_t s) 
   else
     k_pool<float><<<grid, 256, 0, s>>>((const float*)K, (float*)Kslc, d.L, d.Hkv, d.D, d.S,
                                        d.nC, total);
+  return hipGetLastError();
+}
+
+// The chunk keys of listed chunks only (a decoder appends the chunk its sequence just
+// completed): one thread per (b, listed entry, g, feature), the same arithmetic as k_pool.
+template <typename T>
+__global__ void __launch_bounds__(256) k_pool_chunks(const T* __restrict__ K, T* __restrict__ Kslc,
+                                                     const int32_t* __restrict__ chunk_ids,
+                                                     int n_ids, int L, int Hkv, int D, int nC,
+                                                     size_t total) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int e = (int)(i % D);
+  size_t r = i / D;
+  const int g = (int)(r % Hkv);
+  r /= Hkv;  // b * n_ids + j
+  const size_t b = r / n_ids;
+  const int c = chunk_ids[r];
+  if (c < 0 || c >= nC) return;
+  Kslc[((b * nC + c) * Hkv + g) * D + e] = pool_one(K, L, Hkv, D, b, c, g, e);
+}
+
+hipError_t launch_pool_chunks(const Dims& d, const void* K, void* Kslc, const int32_t* chunk_ids,
+                              int n_ids, hipStream_t s) {
+  const size_t total = (size_t)d.B * n_ids * d.Hkv * d.D;
+  if (total == 0 || d.nC == 0) return hipSuccess;
+  dim3 grid((unsigned)((total + 255) / 256));
+  Timed tm(HSA_KERNEL_POOL, s);
+  if (d.dtype == 1)
+    k_pool_chunks<bf16><<<grid, 256, 0, s>>>((const bf16*)K, (bf16*)Kslc, chunk_ids, n_ids, d.L,
+                                             d.Hkv, d.D, d.nC, total);
+  else
+    k_pool_chunks<float><<<grid, 256, 0, s>>>((const float*)K, (float*)Kslc, chunk_ids, n_ids,
+                                              d.L, d.Hkv, d.D, d.nC, total);
   return hipGetLastError();
 }
 

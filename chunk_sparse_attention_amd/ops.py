@@ -235,6 +235,50 @@ def decode_host_kv(q, qs, Kc, Vc, Kslc, K_top, sm_scale=None, sel_scale=None, ge
     return O, idx, score, w
 
 
+def decode_ragged(q, qs, Kc, Vc, Kslc, ctx_lens, K_top, sm_scale=None, sel_scale=None,
+                  generic=False, ws=None, weights="stick"):
+    """decode() for sequences of different lengths in one cache: ctx_lens [B] int32 (GPU),
+    caches [B,L,Hkv,D] with L the capacity.  Returns (O [B,Hq,D], idx, score, w [B,Hkv,K])."""
+    _need(Kc, "Kcache")
+    B, ctx, Hkv, D = Kc.shape
+    dev = Kc.device
+    Hq = q.shape[1]
+    _need(q, "q", Kc.dtype, (B, Hq, D), dev)
+    _need(qs, "qs", Kc.dtype, (B, Hkv, D), dev)
+    _need(Vc, "Vcache", Kc.dtype, (B, ctx, Hkv, D), dev)
+    _need(Kslc, "Kslc", Kc.dtype, (B, ctx // S_CHUNK, Hkv, D), dev)
+    _need(ctx_lens, "ctx_lens", torch.int32, (B,), dev)
+    prob = problem(B, ctx, Hq, Hkv, D, K_top, Kc.dtype, sm_scale=sm_scale, sel_scale=sel_scale,
+                   generic=generic, weights=weights)
+    O = torch.empty((B, Hq, D), dtype=Kc.dtype, device=dev)
+    idx = torch.empty((B, Hkv, K_top), dtype=torch.int32, device=dev)
+    score = torch.empty((B, Hkv, K_top), dtype=torch.float32, device=dev)
+    w = torch.empty((B, Hkv, K_top), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(_lib.HSA_OP_DECODE, prob, dev)
+    wp, wn = _ws_args(ws)
+    check(_lib.lib().hsa_decode_ragged(ctypes.byref(prob), _ptr(ctx_lens), _ptr(q), _ptr(qs),
+                                       _ptr(Kc), _ptr(Vc), _ptr(Kslc), _ptr(O), _ptr(idx),
+                                       _ptr(score), _ptr(w), wp, wn, _stream()),
+          "hsa_decode_ragged")
+    return O, idx, score, w
+
+
+def pool_chunks(K, Kslc, chunk_ids):
+    """Recompute Kslc[b, c] in place for the chunks c listed in chunk_ids [B, n] int32 (GPU;
+    entries outside [0, nC) are skipped).  K [B,L,Hkv,D], Kslc [B,L//64,Hkv,D]."""
+    _need(K, "K")
+    B, L, Hkv, D = K.shape
+    _need(Kslc, "Kslc", K.dtype, (B, L // S_CHUNK, Hkv, D), K.device)
+    _need(chunk_ids, "chunk_ids", torch.int32, None, K.device)
+    if chunk_ids.dim() != 2 or chunk_ids.shape[0] != B:
+        raise ValueError(f"chunk_ids must be [B={B}, n], not {tuple(chunk_ids.shape)}")
+    prob = problem(B, L, Hkv, Hkv, D, 1, K.dtype)
+    check(_lib.lib().hsa_pool_chunks(ctypes.byref(prob), _ptr(K), _ptr(Kslc), _ptr(chunk_ids),
+                                     int(chunk_ids.shape[1]), _stream()), "hsa_pool_chunks")
+    return Kslc
+
+
 def timer_enable(on: bool = True) -> None:
     """Start (forgetting earlier records) or stop HIP-event timing of every kernel launch."""
     check(_lib.lib().hsa_timer_enable(1 if on else 0), "hsa_timer_enable")

@@ -194,6 +194,28 @@ hsa_status_t hsa_decode_host_kv(const hsa_problem_t* p, const void* q, const voi
                                 void* O, int32_t* idx, float* score, float* w, void* ws,
                                 size_t ws_bytes, hsa_stream_t stream);
 
+/* One decode step for B sequences of different lengths in one cache (note section
+ * 训练与推理优化: decode scans the chunk-key table and reads only the selected chunks).
+ * p->L is the cache capacity: Kcache, Vcache [B, L, Hkv, D], Kslc [B, floor(L/S), Hkv, D],
+ * as for hsa_decode.  ctx_lens [B] int32 (device memory): sequence b's new token sits at
+ * position ctx_lens[b] and may select chunks c < min(floor(ctx_lens[b]/S), floor(L/S))
+ * (values below 0 count as 0), so its result equals hsa_decode's on that sequence's first
+ * ctx_lens[b] tokens.  Other arguments, results and errors as for hsa_decode. */
+hsa_status_t hsa_decode_ragged(const hsa_problem_t* p, const int32_t* ctx_lens, const void* q,
+                               const void* qs, const void* Kcache, const void* Vcache,
+                               const void* Kslc, void* O, int32_t* idx, float* score, float* w,
+                               void* ws, size_t ws_bytes, hsa_stream_t stream);
+
+/* Chunk keys of listed chunks only, for a decoder that appends the chunk its sequence has
+ * just completed (note section 训练与推理优化: the chunk-key table stays resident and grows by
+ * one chunk every S tokens).  p->L is the cache capacity; K [B, L, Hkv, D] dtype.
+ * chunk_ids [B, n_ids] int32 (device memory): for every entry c with 0 <= c < floor(L/S),
+ * Kslc[b, c] is recomputed from rows cS .. cS+S-1 of sequence b, with the same arithmetic
+ * as hsa_select's pooling (so the result equals a full pooling bit for bit); other entries
+ * (e.g. -1) are skipped.  1 <= n_ids <= max(floor(L/S), 1), else HSA_ERR_INVALID_ARG. */
+hsa_status_t hsa_pool_chunks(const hsa_problem_t* p, const void* K, void* Kslc,
+                             const int32_t* chunk_ids, int n_ids, hsa_stream_t stream);
+
 /* ---- Kernel timing (measurement aid; not part of the operation) ----------------------
  * The entry points above each enqueue a short sequence of kernels.  To price one kernel
  * against the device's roofline, the library can bracket every launch of a kernel class

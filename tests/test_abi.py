@@ -94,6 +94,11 @@ def test_entry_points_reject_before_launch():
     st = lib.hsa_decode(ctypes.byref(_prob(D=80)), fake, fake, fake, fake, fake, fake, fake, None,
                         fake, fake, 1 << 30, None)
     assert st == 2
+    st = lib.hsa_decode_ragged(ctypes.byref(_prob()), None, fake, fake, fake, fake, fake, fake,
+                               fake, None, fake, fake, 1 << 30, None)
+    assert st == 1 and b"ctx_lens is NULL" in lib.hsa_last_error()
+    st = lib.hsa_pool_chunks(ctypes.byref(_prob()), fake, fake, fake, 0, None)
+    assert st == 1 and b"n_ids" in lib.hsa_last_error()
     bad = _prob()
     bad.flags = 0x4  # no such problem flag
     st = lib.hsa_select(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, 0, None)

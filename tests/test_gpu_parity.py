@@ -356,6 +356,83 @@ def test_decode_softmax_weights(hsa, dev, ctx, generic):
     assert max_abs(npy(O), d["O"]) <= 2e-2
 
 
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
+def test_decode_ragged(hsa, dev, generic):
+    """Sequences of different lengths in one cache: each sequence's result equals hsa_decode
+    on its own prefix bit for bit, and the oracle's."""
+    cap = 64 * 40 + 5
+    lens = [40, 64 * 7 + 13, 64 * 33, cap]
+    wl = W("decode_ragged", len(lens), cap, 16, 2, 64, 64, 8, torch.bfloat16)
+    say("case decode ragged", lens, generic)
+    x = workloads.make_decode_inputs(wl, seed=12)
+    q, qs, Kc, Vc = (x[k].to(dev) for k in ("q", "qs", "Kc", "Vc"))
+    Kslc = hsa.pool(Kc)
+    ctx_lens = torch.tensor(lens, dtype=torch.int32, device=dev)
+    got = hsa.decode_ragged(q, qs, Kc, Vc, Kslc, ctx_lens, wl.K, generic=generic)
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    for b, n in enumerate(lens):
+        Kb, Vb = Kc[b:b + 1, :n].contiguous(), Vc[b:b + 1, :n].contiguous()
+        ref = hsa.decode(q[b:b + 1], qs[b:b + 1], Kb, Vb, hsa.pool(Kb), wl.K, generic=generic)
+        torch.cuda.synchronize()
+        for a, r in zip(got, ref):
+            assert torch.equal(a[b:b + 1], r), (b, n)
+        xb = {k: x[k][b:b + 1] for k in ("q", "qs")}
+        kb, vb = x["Kc"][b:b + 1, :n], x["Vc"][b:b + 1, :n]
+        d = orc.decode(xb["q"], xb["qs"], kb, vb, orc.pool(kb, 64), 64, wl.K)
+        assert np.array_equal(npy(got[1][b:b + 1]), d["idx"]), (b, n)
+        assert max_abs(npy(got[3][b:b + 1]), d["w"]) <= 1e-5
+        assert max_abs(npy(got[0][b:b + 1]), d["O"]) <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_pool_chunks(hsa, dev, dtype):
+    """Pooling listed chunks only reproduces the full pooling of those chunks bit for bit and
+    leaves the others alone."""
+    gen = torch.Generator().manual_seed(4)
+    B, L, Hkv, D = 3, 64 * 20 + 7, 2, 64
+    K = (torch.randn((B, L, Hkv, D), generator=gen) * 0.5).to(dtype).to(dev)
+    full = hsa.pool(K)
+    ids = torch.tensor([[3, -1, 19], [0, 7, 25], [-1, -1, 12]], dtype=torch.int32)
+    Kslc = full.clone()
+    for b in range(B):
+        for c in ids[b].tolist():
+            if 0 <= c < L // 64:
+                Kslc[b, c] = 0
+    hsa.pool_chunks(K, Kslc, ids.to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(Kslc, full)
+
+
+def test_decode_incremental(hsa, dev):
+    """A decoder loop: sequences grow one token per step; when one completes a chunk, that
+    chunk's key is pooled into the resident table (hsa_pool_chunks) and the next step may
+    select it.  Every step equals the oracle's decode on each sequence's prefix."""
+    cap = 64 * 12
+    lens = [64 * 5 + 62, 64 * 3 + 63]
+    wl = W("decode_incremental", len(lens), cap, 8, 2, 64, 64, 4, torch.bfloat16)
+    x = workloads.make_decode_inputs(wl, seed=13)
+    q, qs, Kc, Vc = (x[k].to(dev) for k in ("q", "qs", "Kc", "Vc"))
+    Kslc = hsa.pool(Kc)
+    for b, n in enumerate(lens):  # only the chunks complete at the start are in the table
+        Kslc[b, n // 64:] = 0
+    orc = oracle.get()
+    for step in range(4):
+        ctx_lens = torch.tensor(lens, dtype=torch.int32, device=dev)
+        O, idx, _, w = hsa.decode_ragged(q, qs, Kc, Vc, Kslc, ctx_lens, wl.K)
+        torch.cuda.synchronize()
+        for b, n in enumerate(lens):
+            kb, vb = x["Kc"][b:b + 1, :n], x["Vc"][b:b + 1, :n]
+            d = orc.decode(x["q"][b:b + 1], x["qs"][b:b + 1], kb, vb, orc.pool(kb, 64), 64, wl.K)
+            assert np.array_equal(npy(idx[b:b + 1]), d["idx"]), (step, b, n)
+            assert max_abs(npy(w[b:b + 1]), d["w"]) <= 1e-5
+            assert max_abs(npy(O[b:b + 1]), d["O"]) <= 2e-2
+        # one more token per sequence; a completed chunk joins the table
+        lens = [n + 1 for n in lens]
+        done = [[n // 64 - 1 if n % 64 == 0 else -1] for n in lens]
+        hsa.pool_chunks(Kc, Kslc, torch.tensor(done, dtype=torch.int32, device=dev))
+
+
 @pytest.mark.parametrize("ctx", [64 * 7 + 13, 64 * 33])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 def test_decode_host_kv(hsa, dev, ctx, dtype):
