@@ -381,6 +381,40 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
     e1.record()
     torch.cuda.synchronize()
     rms = e0.elapsed_time(e1) / reps
+    del Kc, Vc
+    # four layers at a 16K context sharing one selection (hsa_decode for the first layer,
+    # hsa_decode_shared for the other three) against four independent decode steps
+    nl, ctx4 = 4, 16384
+    wl4 = workloads.Workload("decode_16k_layers", wl3.B, ctx4, wl3.Hq, wl3.Hkv, wl3.D, wl3.S,
+                             wl3.K, wl3.dtype, decode=True)
+    xs = [workloads.make_decode_inputs(wl4, seed=10 + l) for l in range(nl)]
+    q4 = torch.stack([x["q"] for x in xs]).to(dev)
+    K4 = torch.stack([x["Kc"] for x in xs]).to(dev)
+    V4 = torch.stack([x["Vc"] for x in xs]).to(dev)
+    qs4 = [x["qs"].to(dev) for x in xs]
+    del xs
+    ks4 = [hsa.pool(K4[l]) for l in range(nl)]
+
+    def shared():
+        _, i4, _, w4 = hsa.decode(q4[0], qs4[0], K4[0], V4[0], ks4[0], wl4.K, generic=gen)
+        hsa.decode_shared(q4[1:], K4[1:], V4[1:], i4, w4)
+
+    def unshared():
+        for l in range(nl):
+            hsa.decode(q4[l], qs4[l], K4[l], V4[l], ks4[l], wl4.K, generic=gen)
+
+    lay = {}
+    for name, fn in (("shared_ms", shared), ("unshared_ms", unshared)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        lay[name] = round(e0.elapsed_time(e1) / reps, 4)
+    del q4, K4, V4, qs4, ks4
     el = 2
     # the chunk-key table, the selected chunks' K and V, q, qs and O
     dbytes = (wl3.B * wl3.nC * wl3.Hkv * wl3.D * el
@@ -396,7 +430,9 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
             "host_kv": {"ms": round(hms, 4), "vs_device_kv": round(hms / dms, 3),
                         "link_bytes_per_step": 2 * wl3.B * wl3.Hkv * wl3.K * wl3.S * wl3.D * el},
             "ragged": {"ms": round(rms, 4), "mean_ctx": round(float(lens.double().mean()), 1),
-                       "lengths": "uniform in [ctx/2, ctx], seed 1"}}
+                       "lengths": "uniform in [ctx/2, ctx], seed 1"},
+            "shared_selection": {"workload": f"{nl} layers, B={wl4.B} ctx={ctx4} Hq={wl4.Hq} "
+                                             f"Hkv={wl4.Hkv} d={wl4.D} K={wl4.K}", **lay}}
 
 
 def main() -> int:

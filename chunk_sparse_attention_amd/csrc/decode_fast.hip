@@ -223,7 +223,8 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
     const T* __restrict__ q, const T* __restrict__ Kc, const T* __restrict__ Vc,
     const uint64_t* __restrict__ cand, T* __restrict__ O, int32_t* __restrict__ idx,
     float* __restrict__ score, float* __restrict__ w, int ctx, int Hq, int Hkv, int K, int G,
-    int HW, int n_hg, int n_cand, float c2, int softmax_w) {
+    int HW, int n_hg, int n_cand, float c2, int softmax_w, const int32_t* __restrict__ sel_idx,
+    const float* __restrict__ sel_w, size_t q_lstride, size_t kv_lstride) {
   constexpr int P = D / 8;
   constexpr int JG = kWave / P;
   constexpr int RPL = kChunk / JG;  // rows per lane in the value product
@@ -233,61 +234,76 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
   __shared__ float osh[NS][ZH][D];
   const int tid = threadIdx.x, lane = tid % kWave, slot = tid / kWave;
   const int hg = blockIdx.x % n_hg, bg = blockIdx.x / n_hg;
+  // layer blockIdx.y of a stack of layers that share one selection (strides 0 otherwise)
+  const size_t layer = blockIdx.y;
+  q += layer * q_lstride;
+  O += layer * q_lstride;
+  Kc += layer * kv_lstride;
+  Vc += layer * kv_lstride;
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const int h_lo = hg * HW, nh = min(G, h_lo + HW) - h_lo;
   const size_t qbase = ((size_t)b * Hq + (size_t)g * G + h_lo) * D;
   for (int i = tid; i < nh * D; i += blockDim.x) qsh[i / D][i % D] = to_f32(q[qbase + i]);
 
-  const uint64_t mykey =
-      n_cand > 0 ? rank_candidates(cand + (size_t)bg * n_cand, n_cand, K, lane) : 0;
-  double wslot;
-  if (softmax_w) {
-    // softmax of the valid slots' scores (lanes 0..K-1), shifted by their maximum and
-    // summed in slot order
-    const double sc = mykey != 0 ? (double)key_score(mykey) : -__builtin_inf();
-    double m = -__builtin_inf();
-    for (int j = 0; j < K; ++j) m = fmax(m, __shfl(sc, j));
-    const double e = (mykey != 0 && m != -__builtin_inf()) ? exp(sc - m) : 0.0;
-    double den = 0.0;
-    for (int j = 0; j < K; ++j) den += __shfl(e, j);
-    wslot = den > 0.0 ? e / den : 0.0;
+  int my_c = -1;       // lane k < K: slot k's chunk (-1 = masked)
+  double wslot = 0.0;  // and its weight
+  if (sel_idx) {
+    // a selection made before (an earlier layer's): the slots' chunks and weights as given
+    if (lane < K) {
+      my_c = sel_idx[(size_t)bg * K + lane];
+      wslot = my_c >= 0 ? (double)sel_w[(size_t)bg * K + lane] : 0.0;
+    }
   } else {
-    // stick-breaking in rank order: slot k needs p_k * prod_{j<k} (1 - p_j), a prefix
-    // product over lanes 0..K-1 (masked slots have p = 0 and come last)
-    const double p = mykey != 0 ? sigmoid_d((double)key_score(mykey)) : 0.0;
-    double keep = 1.0 - p;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const double x = __shfl_up(keep, o, 16);
-      if ((lane & 15) >= o) keep *= x;
-    }
-    double excl = __shfl_up(keep, 1, 16);
-    if ((lane & 15) == 0) excl = 1.0;
-    wslot = p * excl;
-  }
-  if (hg == 0 && slot == 0 && lane < K) {
-    const size_t o = (size_t)bg * K + lane;
-    if (mykey == 0) {
-      idx[o] = -1;
-      if (score) score[o] = -__builtin_inff();
-      w[o] = 0.0f;
+    const uint64_t mykey =
+        n_cand > 0 ? rank_candidates(cand + (size_t)bg * n_cand, n_cand, K, lane) : 0;
+    if (softmax_w) {
+      // softmax of the valid slots' scores (lanes 0..K-1), shifted by their maximum and
+      // summed in slot order
+      const double sc = mykey != 0 ? (double)key_score(mykey) : -__builtin_inf();
+      double m = -__builtin_inf();
+      for (int j = 0; j < K; ++j) m = fmax(m, __shfl(sc, j));
+      const double e = (mykey != 0 && m != -__builtin_inf()) ? exp(sc - m) : 0.0;
+      double den = 0.0;
+      for (int j = 0; j < K; ++j) den += __shfl(e, j);
+      wslot = den > 0.0 ? e / den : 0.0;
     } else {
-      idx[o] = key_chunk(mykey);
-      if (score) score[o] = key_score(mykey);
-      w[o] = (float)wslot;
+      // stick-breaking in rank order: slot k needs p_k * prod_{j<k} (1 - p_j), a prefix
+      // product over lanes 0..K-1 (masked slots have p = 0 and come last)
+      const double p = mykey != 0 ? sigmoid_d((double)key_score(mykey)) : 0.0;
+      double keep = 1.0 - p;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const double x = __shfl_up(keep, o, 16);
+        if ((lane & 15) >= o) keep *= x;
+      }
+      double excl = __shfl_up(keep, 1, 16);
+      if ((lane & 15) == 0) excl = 1.0;
+      wslot = p * excl;
     }
+    if (hg == 0 && slot == 0 && lane < K) {
+      const size_t o = (size_t)bg * K + lane;
+      if (mykey == 0) {
+        idx[o] = -1;
+        if (score) score[o] = -__builtin_inff();
+        w[o] = 0.0f;
+      } else {
+        idx[o] = key_chunk(mykey);
+        if (score) score[o] = key_score(mykey);
+        w[o] = (float)wslot;
+      }
+    }
+    my_c = mykey != 0 ? key_chunk(mykey) : -1;
   }
-  const int n_valid = __popcll(__ballot(lane < K && mykey != 0));
+  // the valid slots come first
+  const int n_valid = __popcll(__ballot(lane < K && my_c >= 0));
   // this wave's slot, read from lane `slot`
-  const uint32_t mhi = __builtin_amdgcn_readlane((uint32_t)(mykey >> 32), slot);
-  const uint32_t mlo = __builtin_amdgcn_readlane((uint32_t)mykey, slot);
-  const uint64_t mine = ((uint64_t)mhi << 32) | mlo;
+  const int mine = __builtin_amdgcn_readlane(my_c, slot);
   const float wf = __shfl((float)wslot, slot);
   __syncthreads();  // qsh ready
 
-  if (mine != 0) {
-    const int c = key_chunk(mine);
+  if (mine >= 0) {
+    const int c = mine;
     const size_t kvstride = (size_t)Hkv * D;
     const size_t cbase = ((b * ctx + (size_t)c * kChunk) * Hkv + g) * D;
     const int p8 = lane % P, jg = lane / P;
@@ -412,12 +428,46 @@ static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, cons
     kern<<<dim3(bg * n_hg), kWave * d.K, 0, s>>>((const T*)q, (const T*)Kc, (const T*)Vc, cand,
                                                  (T*)O, idx, score, w, d.L, d.Hq, d.Hkv, d.K,
                                                  d.G, HW, n_hg, n_blocks * d.K, c2,
-                                                 softmax_w(d));
+                                                 softmax_w(d), nullptr, nullptr, 0, 0);
   };
   constexpr int ZW = 8;  // heads per block for host caches, up to 8 slots
   if (d.K > 8) go(k_dec_attend_heads<T, D, 4, 1024>, 4);
   else if (host_kv) go(k_dec_attend_heads<T, D, ZW, 512>, ZW);
   else go(k_dec_attend_heads<T, D, 4, 512>, 4);
+}
+
+// A stack of n_layers layers attending with one given selection (attend kernel only).
+template <typename T, int D>
+static void launch_dec_shared_t(const Dims& d, int n_layers, const void* q, const void* Kc,
+                                const void* Vc, const int32_t* sel_idx, const float* sel_w,
+                                void* O, hipStream_t s) {
+  const int bg = d.B * d.Hkv;
+  const float c2 = (float)(d.sm_scale * 1.4426950408889634);
+  const int HW = (d.G + 3) / 4;
+  const int n_hg = (d.G + HW - 1) / HW;
+  const size_t q_ls = (size_t)d.B * d.Hq * D, kv_ls = (size_t)d.B * d.L * d.Hkv * D;
+  Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
+  auto go = [&](auto kern) {
+    kern<<<dim3(bg * n_hg, n_layers), kWave * d.K, 0, s>>>(
+        (const T*)q, (const T*)Kc, (const T*)Vc, nullptr, (T*)O, nullptr, nullptr, nullptr,
+        d.L, d.Hq, d.Hkv, d.K, d.G, HW, n_hg, 0, c2, 0, sel_idx, sel_w, q_ls, kv_ls);
+  };
+  if (d.K > 8) go(k_dec_attend_heads<T, D, 4, 1024>);
+  else go(k_dec_attend_heads<T, D, 4, 512>);
+}
+
+hipError_t launch_decode_shared(const Dims& d, int n_layers, const void* q, const void* Kc,
+                                const void* Vc, const int32_t* sel_idx, const float* sel_w,
+                                void* O, hipStream_t s) {
+  if (d.B * d.Hkv == 0) return hipSuccess;
+  if (d.dtype == 1) {
+    if (d.D == 64) launch_dec_shared_t<bf16, 64>(d, n_layers, q, Kc, Vc, sel_idx, sel_w, O, s);
+    else launch_dec_shared_t<bf16, 128>(d, n_layers, q, Kc, Vc, sel_idx, sel_w, O, s);
+  } else {
+    if (d.D == 64) launch_dec_shared_t<float, 64>(d, n_layers, q, Kc, Vc, sel_idx, sel_w, O, s);
+    else launch_dec_shared_t<float, 128>(d, n_layers, q, Kc, Vc, sel_idx, sel_w, O, s);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_fast(const Dims& d, const void* q, const void* qs, const void* Kc,

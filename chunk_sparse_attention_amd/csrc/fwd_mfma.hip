@@ -570,9 +570,12 @@ constexpr int kFwdWaves = 8;
 
 static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const void* Q,
                                      const void* K, const void* V, const int32_t* idx,
-                                     const float* w, void* O, char* ws, hipStream_t s) {
-  hipError_t e = launch_invidx(d, st.ix, idx, ws, s);
-  if (e != hipSuccess) return e;
+                                     const float* w, void* O, char* ws, hipStream_t s,
+                                     bool index_ready = false) {
+  if (!index_ready) {  // the index of this selection is not in ws yet
+    hipError_t e = launch_invidx(d, st.ix, idx, ws, s);
+    if (e != hipSuccess) return e;
+  }
   const int BG = d.B * d.Hkv;
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);  // logit scale * log2(e)
   if (d.nC > 0) {
@@ -617,16 +620,17 @@ static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const vo
 }
 
 hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,
-                           const int32_t* idx, const float* w, void* O, char* ws, hipStream_t s) {
+                           const int32_t* idx, const float* w, void* O, char* ws, hipStream_t s,
+                           bool index_ready) {
   const FwdState st = fwd_state(d);
-  if (fwd_chunked(d)) return launch_fwd_chunked(d, st, Q, K, V, idx, w, O, ws, s);
+  if (fwd_chunked(d)) return launch_fwd_chunked(d, st, Q, K, V, idx, w, O, ws, s, index_ready);
   char* kop = ws + st.kop;
   char* prep = ws + st.prep;
   float* lse = (float*)(ws + st.lse);
   char* vt = ws + st.total;
   launch_prep_ops(d, K, kop, false, s);
   launch_prep_ops(d, V, vt, true, s);
-  launch_tile_prep(d, idx, prep, s);
+  if (!index_ready) launch_tile_prep(d, idx, prep, s);
   if (d.D == 64)
     launch_fwd_tile_g<64, 64>(d, Q, kop, vt, idx, w, prep, O, lse, s);
   else

@@ -358,3 +358,57 @@ HSA_EXPORT hsa_status_t hsa_pool_chunks(const hsa_problem_t* p, const void* K, v
   return launched(hsa::launch_pool_chunks(d, K, Kslc, chunk_ids, n_ids, (hipStream_t)stream),
                   "pool_chunks");
 }
+
+HSA_EXPORT hsa_status_t hsa_fwd_layers(const hsa_problem_t* p, int n_layers, const void* Q,
+                                       const void* K, const void* V, const int32_t* idx,
+                                       const float* w, void* O, void* ws, size_t ws_bytes,
+                                       hsa_stream_t stream) {
+  hsa::Dims d;
+  TRY(check_problem(HSA_OP_FWD, p, &d));
+  if (n_layers < 1) return fail(HSA_ERR_INVALID_ARG, "n_layers=%d must be positive", n_layers);
+  TRY(need_tensor(Q, "Q"));
+  TRY(need_tensor(K, "K"));
+  TRY(need_tensor(V, "V"));
+  TRY(need_small(idx, "idx"));
+  TRY(need_small(w, "w"));
+  TRY(need_tensor(O, "O"));
+  TRY(check_ws(HSA_OP_FWD, d, ws, ws_bytes));
+  TRY(check_pending());
+  hipStream_t s = (hipStream_t)stream;
+  const size_t el = d.dtype == HSA_BF16 ? 2 : 4;
+  const size_t q_ls = (size_t)d.B * d.L * d.Hq * d.D * el;
+  const size_t kv_ls = (size_t)d.B * d.L * d.Hkv * d.D * el;
+  const bool mfma = hsa::fwd_mfma_supported(d);
+  for (int l = 0; l < n_layers; ++l) {
+    const char* Ql = (const char*)Q + l * q_ls;
+    const char* Kl = (const char*)K + l * kv_ls;
+    const char* Vl = (const char*)V + l * kv_ls;
+    char* Ol = (char*)O + l * q_ls;
+    // the layers share the selection: its index is built for the first layer only
+    const hipError_t e =
+        mfma ? hsa::launch_fwd_mfma(d, Ql, Kl, Vl, idx, w, Ol, (char*)ws, s, l > 0)
+             : hsa::launch_fwd_generic(d, Ql, Kl, Vl, idx, w, Ol, s);
+    if (e != hipSuccess) return launched(e, "fwd_layers");
+  }
+  return ok();
+}
+
+HSA_EXPORT hsa_status_t hsa_decode_shared(const hsa_problem_t* p, int n_layers, const void* q,
+                                          const void* Kcache, const void* Vcache,
+                                          const int32_t* idx, const float* w, void* O,
+                                          hsa_stream_t stream) {
+  hsa::Dims d;
+  TRY(check_problem(HSA_OP_DECODE, p, &d));
+  if (n_layers < 1 || n_layers > 65535)
+    return fail(HSA_ERR_INVALID_ARG, "n_layers=%d is outside [1, 65535]", n_layers);
+  TRY(need_tensor(q, "q"));
+  TRY(need_tensor(Kcache, "Kcache"));
+  TRY(need_tensor(Vcache, "Vcache"));
+  TRY(need_small(idx, "idx"));
+  TRY(need_small(w, "w"));
+  TRY(need_tensor(O, "O"));
+  TRY(check_pending());
+  return launched(hsa::launch_decode_shared(d, n_layers, q, Kcache, Vcache, idx, w, O,
+                                            (hipStream_t)stream),
+                  "decode_shared");
+}

@@ -141,8 +141,11 @@ bool fwd_mfma_supported(const Dims& d);
 // token sums); beyond, on token tiles.
 bool fwd_chunked(const Dims& d);
 size_t fwd_mfma_ws(const Dims& d);
+// index_ready: ws already holds the inverse index (or the token tiles' job lists) of this
+// selection, built by the previous call on the same workspace and idx.
 hipError_t launch_fwd_mfma(const Dims& d, const void* Q, const void* K, const void* V,
-                           const int32_t* idx, const float* w, void* O, char* ws, hipStream_t s);
+                           const int32_t* idx, const float* w, void* O, char* ws, hipStream_t s,
+                           bool index_ready = false);
 
 // Decode with a bandwidth-shaped scan and one wave per kept slot (both dtypes).
 size_t dec_fast_ws(const Dims& d);
@@ -152,6 +155,11 @@ hipError_t launch_decode_fast(const Dims& d, const void* q, const void* qs, cons
                               const void* Vc, const void* Kslc, void* O, int32_t* idx,
                               float* score, float* w, bool host_kv, const int32_t* ctx_lens,
                               char* ws, hipStream_t s);
+// n_layers layers attending with one given selection (idx/w [B, Hkv, K], valid slots
+// first); q, O [n_layers, B, Hq, D], caches [n_layers, B, L, Hkv, D].
+hipError_t launch_decode_shared(const Dims& d, int n_layers, const void* q, const void* Kc,
+                                const void* Vc, const int32_t* sel_idx, const float* sel_w,
+                                void* O, hipStream_t s);
 hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void* q,
                                  const void* qs, const void* Kc, const void* Vc,
                                  const void* Kslc, void* O, int32_t* idx, float* score,

@@ -279,6 +279,48 @@ def pool_chunks(K, Kslc, chunk_ids):
     return Kslc
 
 
+def fwd_layers(Q, K, V, idx, w, sm_scale=None, generic=False, ws=None, out=None):
+    """fwd() for a stack of layers sharing one selection: Q [n,B,L,Hq,D], K, V [n,B,L,Hkv,D],
+    idx/w [B,L,Hkv,K].  Returns O [n,B,L,Hq,D]."""
+    _need(Q, "Q")
+    n, B, L, Hq, D = Q.shape
+    Hkv = K.shape[3]
+    Kt = idx.shape[-1]
+    _need(K, "K", Q.dtype, (n, B, L, Hkv, D), Q.device)
+    _need(V, "V", Q.dtype, (n, B, L, Hkv, D), Q.device)
+    _need(idx, "idx", torch.int32, (B, L, Hkv, Kt), Q.device)
+    _need(w, "w", torch.float32, (B, L, Hkv, Kt), Q.device)
+    prob = problem(B, L, Hq, Hkv, D, Kt, Q.dtype, sm_scale=sm_scale, generic=generic)
+    O = torch.empty_like(Q) if out is None else _need(out, "out", Q.dtype, Q.shape, Q.device)
+    if ws is None:
+        ws = workspace(_lib.HSA_OP_FWD, prob, Q.device)
+    wp, wn = _ws_args(ws)
+    check(_lib.lib().hsa_fwd_layers(ctypes.byref(prob), n, _ptr(Q), _ptr(K), _ptr(V),
+                                    _ptr(idx), _ptr(w), _ptr(O), wp, wn, _stream()),
+          "hsa_fwd_layers")
+    return O
+
+
+def decode_shared(q, Kc, Vc, idx, w, sm_scale=None):
+    """Decode attention of a stack of layers with a selection made before (idx/w [B,Hkv,K]
+    from decode()): q [n,B,Hq,D], caches [n,B,ctx,Hkv,D].  Returns O [n,B,Hq,D]."""
+    _need(Kc, "Kcache")
+    n, B, ctx, Hkv, D = Kc.shape
+    dev = Kc.device
+    Hq = q.shape[2]
+    K_top = idx.shape[-1]
+    _need(q, "q", Kc.dtype, (n, B, Hq, D), dev)
+    _need(Vc, "Vcache", Kc.dtype, (n, B, ctx, Hkv, D), dev)
+    _need(idx, "idx", torch.int32, (B, Hkv, K_top), dev)
+    _need(w, "w", torch.float32, (B, Hkv, K_top), dev)
+    prob = problem(B, ctx, Hq, Hkv, D, K_top, Kc.dtype, sm_scale=sm_scale)
+    O = torch.empty((n, B, Hq, D), dtype=Kc.dtype, device=dev)
+    check(_lib.lib().hsa_decode_shared(ctypes.byref(prob), n, _ptr(q), _ptr(Kc), _ptr(Vc),
+                                       _ptr(idx), _ptr(w), _ptr(O), _stream()),
+          "hsa_decode_shared")
+    return O
+
+
 def timer_enable(on: bool = True) -> None:
     """Start (forgetting earlier records) or stop HIP-event timing of every kernel launch."""
     check(_lib.lib().hsa_timer_enable(1 if on else 0), "hsa_timer_enable")

@@ -216,6 +216,30 @@ hsa_status_t hsa_decode_ragged(const hsa_problem_t* p, const int32_t* ctx_lens, 
 hsa_status_t hsa_pool_chunks(const hsa_problem_t* p, const void* K, void* Kslc,
                              const int32_t* chunk_ids, int n_ids, hsa_stream_t stream);
 
+/* ---- Layers that share one selection ------------------------------------------------
+ * The pages' model shares the chunk selection across its HSA layers (atlas summary,
+ * measured effects: removing that sharing slows offloaded decoding): the selection is made
+ * once and the layers attend with it.  Both calls take a stack of n_layers layers in one
+ * contiguous tensor per operand, layer-major.
+ *
+ * hsa_fwd for each layer: Q, O [n_layers, B, L, Hq, D], K, V [n_layers, B, L, Hkv, D], one
+ * idx/w [B, L, Hkv, K] for all layers (as for hsa_fwd).  The inverse index (or the token
+ * tiles' job lists) is built once for the stack.  ws as for hsa_fwd with the same problem
+ * (the layers run one after the other on it).  n_layers >= 1. */
+hsa_status_t hsa_fwd_layers(const hsa_problem_t* p, int n_layers, const void* Q, const void* K,
+                            const void* V, const int32_t* idx, const float* w, void* O,
+                            void* ws, size_t ws_bytes, hsa_stream_t stream);
+
+/* Decode attention of a stack of layers with a selection made before (by hsa_decode,
+ * hsa_decode_ragged or hsa_decode_host_kv for one layer): nothing is scanned.
+ *   q [n_layers, B, Hq, D];  Kcache, Vcache [n_layers, B, L, Hkv, D] (L = context length);
+ *   idx [B, Hkv, K] int32, w [B, Hkv, K] fp32 as those calls write them (valid slots
+ *   first, -1 after);  O [n_layers, B, Hq, D] out.
+ * All device memory; one launch covers the stack.  1 <= n_layers <= 65535. */
+hsa_status_t hsa_decode_shared(const hsa_problem_t* p, int n_layers, const void* q,
+                               const void* Kcache, const void* Vcache, const int32_t* idx,
+                               const float* w, void* O, hsa_stream_t stream);
+
 /* ---- Kernel timing (measurement aid; not part of the operation) ----------------------
  * The entry points above each enqueue a short sequence of kernels.  To price one kernel
  * against the device's roofline, the library can bracket every launch of a kernel class

@@ -99,6 +99,11 @@ def test_entry_points_reject_before_launch():
     assert st == 1 and b"ctx_lens is NULL" in lib.hsa_last_error()
     st = lib.hsa_pool_chunks(ctypes.byref(_prob()), fake, fake, fake, 0, None)
     assert st == 1 and b"n_ids" in lib.hsa_last_error()
+    st = lib.hsa_fwd_layers(ctypes.byref(_prob()), 0, fake, fake, fake, fake, fake, fake, fake,
+                            1 << 30, None)
+    assert st == 1 and b"n_layers" in lib.hsa_last_error()
+    st = lib.hsa_decode_shared(ctypes.byref(_prob()), 0, fake, fake, fake, fake, fake, fake, None)
+    assert st == 1 and b"n_layers" in lib.hsa_last_error()
     bad = _prob()
     bad.flags = 0x4  # no such problem flag
     st = lib.hsa_select(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, 0, None)

@@ -356,6 +356,84 @@ def test_decode_softmax_weights(hsa, dev, ctx, generic):
     assert max_abs(npy(O), d["O"]) <= 2e-2
 
 
+LAYER_CASES = [w for w in SMALL if w.name in ("tiny_fp32", "bf16_d64_ragged", "bf16_d128_ragged")]
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
+@pytest.mark.parametrize("wl", LAYER_CASES, ids=lambda w: w.name)
+def test_fwd_layers(hsa, dev, wl, generic):
+    """Three layers sharing one selection: each layer's output equals hsa_fwd's on that layer
+    bit for bit (the index is built once) and the oracle's."""
+    say("case fwd layers", wl, generic)
+    n = 3
+    xs = [workloads.make_inputs(wl, seed=20 + l, with_grad=False) for l in range(n)]
+    Q = torch.stack([x["Q"] for x in xs]).to(dev)
+    K = torch.stack([x["K"] for x in xs]).to(dev)
+    V = torch.stack([x["V"] for x in xs]).to(dev)
+    _, idx, _, w = hsa.select(xs[0]["Qs"].to(dev), K[0], wl.K, generic=generic)
+    O = hsa.fwd_layers(Q, K, V, idx, w, generic=generic)
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    for l in range(n):
+        ref = hsa.fwd(Q[l], K[l], V[l], idx, w, generic=generic)
+        torch.cuda.synchronize()
+        assert torch.equal(O[l], ref), l
+        o = orc.attend(xs[l]["Q"], xs[l]["K"], xs[l]["V"], npy(idx), npy(w), wl.S)
+        assert max_abs(npy(O[l]), o) <= tol_for(wl.dtype), l
+
+
+def test_fwd_layers_token_tiles(hsa, dev):
+    """Past 16384 chunks the forward runs on token tiles; their job lists are built once for
+    the stack: each layer equals hsa_fwd's (whose parity the token-tile test checks)."""
+    wl = W("bf16_16400_chunks", 1, 64 * 16400 + 17, 8, 2, 64, 64, 4, torch.bfloat16)
+    say("case fwd layers token tiles", wl)
+    xs = [workloads.make_inputs(wl, seed=30 + l, with_grad=False) for l in range(2)]
+    Q = torch.stack([x["Q"] for x in xs]).to(dev)
+    K = torch.stack([x["K"] for x in xs]).to(dev)
+    V = torch.stack([x["V"] for x in xs]).to(dev)
+    _, idx, _, w = hsa.select(xs[0]["Qs"].to(dev), K[0], wl.K)
+    O = hsa.fwd_layers(Q, K, V, idx, w)
+    for l in range(2):
+        ref = hsa.fwd(Q[l], K[l], V[l], idx, w)
+        torch.cuda.synchronize()
+        assert torch.equal(O[l], ref), l
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_decode_shared(hsa, dev, dtype):
+    """Layers reusing layer 0's decode selection: layer 0 reproduces its own decode bit for
+    bit, and every layer equals the oracle's attention of its query over the given chunks."""
+    ctx, n = 64 * 21 + 9, 3
+    wl = W("decode_shared", 2, ctx, 16, 2, 64, 64, 8, dtype)
+    say("case decode shared", dtype)
+    xs = [workloads.make_decode_inputs(wl, seed=40 + l) for l in range(n)]
+    q = torch.stack([x["q"] for x in xs]).to(dev)
+    Kc = torch.stack([x["Kc"] for x in xs]).to(dev)
+    Vc = torch.stack([x["Vc"] for x in xs]).to(dev)
+    qs = xs[0]["qs"].to(dev)
+    O0, idx, _, w = hsa.decode(q[0], qs, Kc[0], Vc[0], hsa.pool(Kc[0]), wl.K)
+    O = hsa.decode_shared(q, Kc, Vc, idx, w)
+    torch.cuda.synchronize()
+    assert torch.equal(O[0], O0)
+    orc = oracle.get()
+    B, Hkv, K = idx.shape
+    # the decode row as row ctx of a sequence of ctx + 1 tokens, the only row computed
+    for l in range(n):
+        Qf = torch.zeros((B, ctx + 1, wl.Hq, wl.D), dtype=dtype)
+        Qf[:, ctx] = xs[l]["q"]
+        pad = torch.zeros((B, 1, Hkv, wl.D), dtype=dtype)
+        Kf = torch.cat([xs[l]["Kc"], pad], 1)
+        Vf = torch.cat([xs[l]["Vc"], pad], 1)
+        idf = np.full((B, ctx + 1, Hkv, K), -1, np.int32)
+        wf = np.zeros((B, ctx + 1, Hkv, K))
+        idf[:, ctx] = npy(idx)
+        wf[:, ctx] = npy(w)
+        mask = np.zeros((B, ctx + 1), np.uint8)
+        mask[:, ctx] = 1
+        o = orc.attend(Qf, Kf, Vf, idf, wf, 64, row_mask=mask)
+        assert max_abs(npy(O[l]), o[:, ctx]) <= tol_for(dtype), l
+
+
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
 def test_decode_ragged(hsa, dev, generic):
     """Sequences of different lengths in one cache: each sequence's result equals hsa_decode
