@@ -239,11 +239,13 @@ k_bwd_chunk_mfma(
                                           lds_read_tr4(&kl[32 * kk + 16 + trow][16 * dt + tcol])),
                                dsT, dq[dt]);
     }
+    // the per-edge partials are stored non-temporally: they are read once, by the token
+    // phase, and measured faster that way (for the forward's partials it was slower)
     if (qs_sel < n_here) {  // lane column = query row col: its edge's partial at d = 16*dt + 4*blk
       bf16* dst = dq_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 4 * blk;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<s16x4*>(dst + 16 * dt) = pack_bf16x4(dq[dt]);
+        __builtin_nontemporal_store(pack_bf16x4(dq[dt]), reinterpret_cast<s16x4*>(dst + 16 * dt));
     }
     wave_lds_sync();  // ql/dl/sdl reuse by the next job
   }
@@ -521,9 +523,11 @@ k_bwd_chunk_keys(
       }
     }
     if (qs_sel < n_here) {  // lane column = query row col: its edge's partial, this wave's half
+      // (stored non-temporally, as in the d = 64 chunk phase)
       bf16* dst = dq_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 64 * wv + 4 * blk;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<s16x4*>(dst + 16 * j) = pack_bf16x4(dq[j]);
+      for (int j = 0; j < 4; ++j)
+        __builtin_nontemporal_store(pack_bf16x4(dq[j]), reinterpret_cast<s16x4*>(dst + 16 * j));
     }
     // no barrier here: the next job restages Q and dO after the dK/dV barrier above, and
     // rewrites dS^T and the row exchange only after its own exchange barrier
