@@ -225,7 +225,8 @@ hsa_status_t hsa_pool_chunks(const hsa_problem_t* p, const void* K, void* Kslc,
  * hsa_fwd for each layer: Q, O [n_layers, B, L, Hq, D], K, V [n_layers, B, L, Hkv, D], one
  * idx/w [B, L, Hkv, K] for all layers (as for hsa_fwd).  The inverse index (or the token
  * tiles' job lists) is built once for the stack.  ws as for hsa_fwd with the same problem
- * (the layers run one after the other on it).  n_layers >= 1. */
+ * (the layers run one after the other on it); afterwards it holds the last layer's forward
+ * state, so HSA_BWD_AFTER_FWD applies to a backward of the last layer only.  n_layers >= 1. */
 hsa_status_t hsa_fwd_layers(const hsa_problem_t* p, int n_layers, const void* Q, const void* K,
                             const void* V, const int32_t* idx, const float* w, void* O,
                             void* ws, size_t ws_bytes, hsa_stream_t stream);
