@@ -252,6 +252,7 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
     // a selection made before (an earlier layer's): the slots' chunks and weights as given
     if (lane < K) {
       my_c = sel_idx[(size_t)bg * K + lane];
+      if (my_c >= ctx / kChunk) my_c = -1;  // an index past the cache is a masked slot
       wslot = my_c >= 0 ? (double)sel_w[(size_t)bg * K + lane] : 0.0;
     }
   } else {
@@ -295,8 +296,8 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
     }
     my_c = mykey != 0 ? key_chunk(mykey) : -1;
   }
-  // the valid slots come first
-  const int n_valid = __popcll(__ballot(lane < K && my_c >= 0));
+  // the valid slots (the first ones, in what the scan ranks; in a given selection, any)
+  const uint64_t vmask = __ballot(lane < K && my_c >= 0);
   // this wave's slot, read from lane `slot`
   const int mine = __builtin_amdgcn_readlane(my_c, slot);
   const float wf = __shfl((float)wslot, slot);
@@ -392,10 +393,11 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
     }
   }
   __syncthreads();
-  // O = sum over the valid slots in rank order (valid slots come first)
+  // O = sum over the valid slots in slot order
   for (int i = tid; i < nh * D; i += blockDim.x) {
     float sum = 0.0f;
-    for (int k = 0; k < n_valid; ++k) sum += osh[k][i / D][i % D];
+    for (int k = 0; k < K; ++k)
+      if ((vmask >> k) & 1) sum += osh[k][i / D][i % D];
     O[qbase + i] = from_f32<T>(sum);
   }
 }

@@ -234,8 +234,8 @@ hsa_status_t hsa_fwd_layers(const hsa_problem_t* p, int n_layers, const void* Q,
 /* Decode attention of a stack of layers with a selection made before (by hsa_decode,
  * hsa_decode_ragged or hsa_decode_host_kv for one layer): nothing is scanned.
  *   q [n_layers, B, Hq, D];  Kcache, Vcache [n_layers, B, L, Hkv, D] (L = context length);
- *   idx [B, Hkv, K] int32, w [B, Hkv, K] fp32 as those calls write them (valid slots
- *   first, -1 after);  O [n_layers, B, Hq, D] out.
+ *   idx [B, Hkv, K] int32, w [B, Hkv, K] fp32 as those calls write them (a slot whose
+ *   index is -1, or not below floor(L/S), adds nothing);  O [n_layers, B, Hq, D] out.
  * All device memory; one launch covers the stack.  1 <= n_layers <= 65535. */
 hsa_status_t hsa_decode_shared(const hsa_problem_t* p, int n_layers, const void* q,
                                const void* Kcache, const void* Vcache, const int32_t* idx,

@@ -434,6 +434,35 @@ def test_decode_shared(hsa, dev, dtype):
         assert max_abs(npy(O[l]), o[:, ctx]) <= tol_for(dtype), l
 
 
+def test_decode_shared_masked_slots(hsa, dev):
+    """A given selection with a masked slot between valid ones and an index past the cache:
+    both slots add nothing, the others are summed in slot order."""
+    ctx = 64 * 9 + 5
+    wl = W("decode_shared_masks", 2, ctx, 8, 2, 64, 64, 4, torch.bfloat16)
+    x = workloads.make_decode_inputs(wl, seed=50)
+    q, Kc, Vc = (x[k].to(dev) for k in ("q", "Kc", "Vc"))
+    idx = torch.tensor([[[3, -1, 7, 2], [0, 8, 99, 5]], [[1, 2, -1, -1], [6, 4, 3, 0]]],
+                       dtype=torch.int32)
+    w = torch.tensor([[[0.4, 0.3, 0.2, 0.1], [0.25, 0.25, 0.3, 0.2]],
+                      [[0.5, 0.5, 0.0, 0.0], [0.1, 0.2, 0.3, 0.4]]], dtype=torch.float32)
+    O = hsa.decode_shared(q[None], Kc[None], Vc[None], idx.to(dev), w.to(dev))
+    torch.cuda.synchronize()
+    eff = torch.where(idx < ctx // 64, idx, torch.full_like(idx, -1))  # 99 is past the cache
+    B, Hkv, K = idx.shape
+    Qf = torch.zeros((B, ctx + 1, wl.Hq, wl.D), dtype=wl.dtype)
+    Qf[:, ctx] = x["q"]
+    pad = torch.zeros((B, 1, Hkv, wl.D), dtype=wl.dtype)
+    idf = np.full((B, ctx + 1, Hkv, K), -1, np.int32)
+    wf = np.zeros((B, ctx + 1, Hkv, K))
+    idf[:, ctx] = eff.numpy()
+    wf[:, ctx] = np.where(eff.numpy() >= 0, w.numpy(), 0.0)
+    mask = np.zeros((B, ctx + 1), np.uint8)
+    mask[:, ctx] = 1
+    o = oracle.get().attend(Qf, torch.cat([x["Kc"], pad], 1), torch.cat([x["Vc"], pad], 1), idf,
+                            wf, 64, row_mask=mask)
+    assert max_abs(npy(O[0]), o[:, ctx]) <= 2e-2
+
+
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
 def test_decode_ragged(hsa, dev, generic):
     """Sequences of different lengths in one cache: each sequence's result equals hsa_decode
