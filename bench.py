@@ -321,8 +321,8 @@ def cpu_baseline(wl, x, budget_s: float = 20.0) -> dict:
 
 
 def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
-    """Time the 1M-context decode step (decode_1m), caches resident in HBM, and the same step
-    with the caches in pinned host memory (hsa_decode_host_kv)."""
+    """Time the 1M-context decode step (decode_1m), caches resident in HBM (back to back, and
+    cold: the median step after the last-level cache was flushed), and its variants."""
     import torch
     wl3 = workloads.WORKLOADS["decode_1m"]
     log(f"bench: decode {wl3.name} (generating caches)")
@@ -348,6 +348,20 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
     e1.record()
     torch.cuda.synchronize()
     dms = e0.elapsed_time(e1) / reps
+    # cold: 512 MiB read before every step pushes the chunk-key table out of the 256 MB
+    # last-level cache (a read, so that no write-back overlaps the step); only the step
+    # itself is timed
+    flush = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+    cold = []
+    for r in range(reps // 2):
+        flush.sum()
+        e0.record()
+        hsa.decode(q, qs, Kc, Vc, Kslc3, wl3.K, generic=gen, ws=ws3)
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    cms = sorted(cold)[len(cold) // 2]
     hsa.timer_enable(True)
     for _ in range(reps):
         hsa.decode(q, qs, Kc, Vc, Kslc3, wl3.K, generic=gen, ws=ws3)
@@ -423,6 +437,7 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
     return {"workload": f"{wl3.name}: B={wl3.B} ctx={wl3.L} Hq={wl3.Hq} Hkv={wl3.Hkv} "
                         f"d={wl3.D} K={wl3.K}",
             "ms": round(dms, 4), "new_tokens_per_s": round(wl3.B / (dms / 1e3), 1),
+            "cold_ms_median": round(cms, 4),
             "roofline": roofline("decode_scan+decode_attend", dict(bytes=dbytes, flops=0),
                                  tot3 / max(n3, 1), None),
             "scan_ms": round(kt3["decode_scan"][1] / max(n3, 1), 4),
@@ -582,6 +597,10 @@ def main() -> int:
     names = ["hsa_select", "hsa_fwd", "hsa_bwd"]
     entry_ms = {n: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps, 4)
                 for j, n in enumerate(names)}
+    # per-step spread (this pass records events, which adds a little to every step)
+    per_step = sorted(e[0].elapsed_time(e[3]) for e in evs)
+    pct = {f"p{p}": round(per_step[min(len(per_step) - 1, int(p / 100 * len(per_step)))], 4)
+           for p in (10, 50, 90)}
     log("bench: per-entry ms", entry_ms)
     counts = kernel_counts(wl, n_slots, fused_backward(wl, gen), chunked_forward(wl, gen))
     kern = {}
@@ -634,6 +653,7 @@ def main() -> int:
         "roofline": roof,
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "entry_ms": entry_ms,
+        "step_ms_spread": pct,
         "kernels": kern,
         "softmax_weights": {"ms_per_step": round(sm_ms, 4),
                             "tokens_per_s": round(tokens / (sm_ms / 1e3), 1)},
