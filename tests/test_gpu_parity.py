@@ -235,6 +235,45 @@ def test_graph_replay_matches_eager(hsa, dev):
         torch.cuda.synchronize()
 
 
+def test_graph_replay_decode(hsa, dev):
+    """The decode calls (stick-breaking and softmax weights, ragged lengths, a shared
+    selection) captured in one HIP graph: every replay equals the eager calls bitwise."""
+    from chunk_sparse_attention_amd import _lib
+    ctx = 64 * 40 + 5
+    wl = W("decode_graph", 3, ctx, 16, 2, 64, 64, 8, torch.bfloat16)
+    x = workloads.make_decode_inputs(wl, seed=60)
+    q, qs, Kc, Vc = (x[k].to(dev) for k in ("q", "qs", "Kc", "Vc"))
+    Kslc = hsa.pool(Kc)
+    lens = torch.tensor([ctx, 64 * 7 + 1, 100], dtype=torch.int32, device=dev)
+    prob = hsa.problem(wl.B, ctx, wl.Hq, wl.Hkv, wl.D, wl.K, wl.dtype)
+    ws = [hsa.workspace(_lib.HSA_OP_DECODE, prob, dev) for _ in range(3)]
+    q2, K2, V2 = torch.stack([q, q.flip(0)]), torch.stack([Kc, Kc]), torch.stack([Vc, Vc])
+
+    def calls():
+        O, idx, score, w = hsa.decode(q, qs, Kc, Vc, Kslc, wl.K, ws=ws[0])
+        Os, _, _, ws_ = hsa.decode(q, qs, Kc, Vc, Kslc, wl.K, ws=ws[1], weights="softmax")
+        Or, ir, _, _ = hsa.decode_ragged(q, qs, Kc, Vc, Kslc, lens, wl.K, ws=ws[2])
+        Osh = hsa.decode_shared(q2, K2, V2, idx, w)
+        return [O, idx, score, w, Os, ws_, Or, ir, Osh]
+
+    eager = [t.clone() for t in calls()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        static = calls()
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(static, eager):
+            assert torch.equal(a, b)
+        calls()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_backward_bitwise_reproducible(hsa, dev):
     wl = SMALL[1]
     x = workloads.make_inputs(wl, seed=5)
