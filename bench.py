@@ -498,7 +498,7 @@ def main() -> int:
     if args.summarize_trace:
         return summarize_trace(*args.summarize_trace)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build of the HSA operator has no multi-GPU "
+        print(f"bench.py runs on one GPU only: the HSA library has no multi-GPU "
               f"path (asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         return 2
 
