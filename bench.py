@@ -435,8 +435,21 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
         for l in range(nl):
             hsa.decode(q4[l], qs4[l], K4[l], V4[l], ks4[l], wl4.K, generic=gen)
 
+    # the same with every layer's caches in pinned host memory
+    Kh4, Vh4 = K4.cpu().pin_memory(), V4.cpu().pin_memory()
+
+    def shared_host():
+        _, i4, _, w4 = hsa.decode_host_kv(q4[0], qs4[0], Kh4[0], Vh4[0], ks4[0], wl4.K,
+                                          generic=gen)
+        hsa.decode_shared(q4[1:], Kh4[1:], Vh4[1:], i4, w4)
+
+    def unshared_host():
+        for l in range(nl):
+            hsa.decode_host_kv(q4[l], qs4[l], Kh4[l], Vh4[l], ks4[l], wl4.K, generic=gen)
+
     lay = {}
-    for name, fn in (("shared_ms", shared), ("unshared_ms", unshared)):
+    for name, fn in (("shared_ms", shared), ("unshared_ms", unshared),
+                     ("host_kv_shared_ms", shared_host), ("host_kv_unshared_ms", unshared_host)):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -446,7 +459,7 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
         e1.record()
         torch.cuda.synchronize()
         lay[name] = round(e0.elapsed_time(e1) / reps, 4)
-    del q4, K4, V4, qs4, ks4
+    del q4, K4, V4, qs4, ks4, Kh4, Vh4
     el = 2
     # the chunk-key table, the selected chunks' K and V, q, qs and O
     dbytes = (wl3.B * wl3.nC * wl3.Hkv * wl3.D * el

@@ -25,7 +25,7 @@ HSA_BWD_AFTER_FWD = 0x2
 EXPORTS = ("hsa_status_string", "hsa_last_error", "hsa_version", "hsa_workspace_size",
            "hsa_select", "hsa_fwd", "hsa_bwd", "hsa_decode", "hsa_decode_host_kv",
            "hsa_decode_ragged", "hsa_pool_chunks", "hsa_fwd_layers", "hsa_decode_shared",
-           "hsa_timer_enable", "hsa_timer_read")
+           "hsa_decode_shared_host_kv", "hsa_timer_enable", "hsa_timer_read")
 # hsa_kernel_t: kernel classes of the timing aid
 KERNEL_CLASSES = ("pool", "select", "tile_prep", "prep_ops", "fwd", "invidx", "bwd_p1", "bwd_p2",
                   "bwd_reduce", "decode_scan", "decode_attend", "fwd_token")
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.hsa_fwd_layers.argtypes = [PP, I, P, P, P, P, P, P, P, Z, P]
     L.hsa_decode_shared.restype = I
     L.hsa_decode_shared.argtypes = [PP, I, P, P, P, P, P, P, P]
+    L.hsa_decode_shared_host_kv.restype = I
+    L.hsa_decode_shared_host_kv.argtypes = [PP, I, P, P, P, P, P, P, P]
     L.hsa_timer_enable.restype = I
     L.hsa_timer_enable.argtypes = [I]
     L.hsa_timer_read.restype = I

@@ -442,32 +442,43 @@ static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, cons
 template <typename T, int D>
 static void launch_dec_shared_t(const Dims& d, int n_layers, const void* q, const void* Kc,
                                 const void* Vc, const int32_t* sel_idx, const float* sel_w,
-                                void* O, hipStream_t s) {
+                                void* O, bool host_kv, hipStream_t s) {
   const int bg = d.B * d.Hkv;
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);
-  const int HW = (d.G + 3) / 4;
-  const int n_hg = (d.G + HW - 1) / HW;
   const size_t q_ls = (size_t)d.B * d.Hq * D, kv_ls = (size_t)d.B * d.L * d.Hkv * D;
   Timed tm(HSA_KERNEL_DECODE_ATTEND, s);
-  auto go = [&](auto kern) {
+  // head groups as in launch_dec_fast_t: quarters of the group's heads for device caches,
+  // up to eight heads per block for host caches
+  auto go = [&](auto kern, int zh) {
+    const int n_hg0 = (d.G + zh - 1) / zh;
+    const int HW = host_kv ? (d.G + n_hg0 - 1) / n_hg0 : (d.G + 3) / 4;
+    const int n_hg = (d.G + HW - 1) / HW;
     kern<<<dim3(bg * n_hg, n_layers), kWave * d.K, 0, s>>>(
         (const T*)q, (const T*)Kc, (const T*)Vc, nullptr, (T*)O, nullptr, nullptr, nullptr,
         d.L, d.Hq, d.Hkv, d.K, d.G, HW, n_hg, 0, c2, 0, sel_idx, sel_w, q_ls, kv_ls);
   };
-  if (d.K > 8) go(k_dec_attend_heads<T, D, 4, 1024>);
-  else go(k_dec_attend_heads<T, D, 4, 512>);
+  if (d.K > 8) go(k_dec_attend_heads<T, D, 4, 1024>, 4);
+  else if (host_kv) go(k_dec_attend_heads<T, D, 8, 512>, 8);
+  else go(k_dec_attend_heads<T, D, 4, 512>, 4);
 }
 
 hipError_t launch_decode_shared(const Dims& d, int n_layers, const void* q, const void* Kc,
                                 const void* Vc, const int32_t* sel_idx, const float* sel_w,
-                                void* O, hipStream_t s) {
+                                void* O, bool host_kv, hipStream_t s) {
   if (d.B * d.Hkv == 0) return hipSuccess;
+  auto go = [&](auto tag, auto dim) {
+    using T = decltype(tag);
+    launch_dec_shared_t<T, decltype(dim)::value>(d, n_layers, q, Kc, Vc, sel_idx, sel_w, O,
+                                                 host_kv, s);
+  };
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
   if (d.dtype == 1) {
-    if (d.D == 64) launch_dec_shared_t<bf16, 64>(d, n_layers, q, Kc, Vc, sel_idx, sel_w, O, s);
-    else launch_dec_shared_t<bf16, 128>(d, n_layers, q, Kc, Vc, sel_idx, sel_w, O, s);
+    if (d.D == 64) go(bf16{}, D64{});
+    else go(bf16{}, D128{});
   } else {
-    if (d.D == 64) launch_dec_shared_t<float, 64>(d, n_layers, q, Kc, Vc, sel_idx, sel_w, O, s);
-    else launch_dec_shared_t<float, 128>(d, n_layers, q, Kc, Vc, sel_idx, sel_w, O, s);
+    if (d.D == 64) go(float{}, D64{});
+    else go(float{}, D128{});
   }
   return hipGetLastError();
 }

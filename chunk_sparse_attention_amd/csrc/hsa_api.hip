@@ -393,10 +393,11 @@ HSA_EXPORT hsa_status_t hsa_fwd_layers(const hsa_problem_t* p, int n_layers, con
   return ok();
 }
 
-HSA_EXPORT hsa_status_t hsa_decode_shared(const hsa_problem_t* p, int n_layers, const void* q,
-                                          const void* Kcache, const void* Vcache,
-                                          const int32_t* idx, const float* w, void* O,
-                                          hsa_stream_t stream) {
+namespace {
+
+hsa_status_t decode_shared_impl(const hsa_problem_t* p, int n_layers, const void* q,
+                                const void* Kcache, const void* Vcache, const int32_t* idx,
+                                const float* w, void* O, hsa_stream_t stream, bool host_kv) {
   hsa::Dims d;
   TRY(check_problem(HSA_OP_DECODE, p, &d));
   if (n_layers < 1 || n_layers > 65535)
@@ -407,8 +408,34 @@ HSA_EXPORT hsa_status_t hsa_decode_shared(const hsa_problem_t* p, int n_layers, 
   TRY(need_small(idx, "idx"));
   TRY(need_small(w, "w"));
   TRY(need_tensor(O, "O"));
+  if (host_kv) {
+    const void *kd = nullptr, *vd = nullptr;
+    TRY(host_view(Kcache, "Kcache", &kd));
+    TRY(host_view(Vcache, "Vcache", &vd));
+    if (!aligned(kd, 16) || !aligned(vd, 16))
+      return fail(HSA_ERR_INVALID_ARG, "the device view of the caches is not 16-byte aligned");
+    Kcache = kd;
+    Vcache = vd;
+  }
   TRY(check_pending());
-  return launched(hsa::launch_decode_shared(d, n_layers, q, Kcache, Vcache, idx, w, O,
+  return launched(hsa::launch_decode_shared(d, n_layers, q, Kcache, Vcache, idx, w, O, host_kv,
                                             (hipStream_t)stream),
                   "decode_shared");
+}
+
+}  // namespace
+
+HSA_EXPORT hsa_status_t hsa_decode_shared(const hsa_problem_t* p, int n_layers, const void* q,
+                                          const void* Kcache, const void* Vcache,
+                                          const int32_t* idx, const float* w, void* O,
+                                          hsa_stream_t stream) {
+  return decode_shared_impl(p, n_layers, q, Kcache, Vcache, idx, w, O, stream, false);
+}
+
+HSA_EXPORT hsa_status_t hsa_decode_shared_host_kv(const hsa_problem_t* p, int n_layers,
+                                                  const void* q, const void* Kcache,
+                                                  const void* Vcache, const int32_t* idx,
+                                                  const float* w, void* O,
+                                                  hsa_stream_t stream) {
+  return decode_shared_impl(p, n_layers, q, Kcache, Vcache, idx, w, O, stream, true);
 }

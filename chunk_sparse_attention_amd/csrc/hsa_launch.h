@@ -155,11 +155,12 @@ hipError_t launch_decode_fast(const Dims& d, const void* q, const void* qs, cons
                               const void* Vc, const void* Kslc, void* O, int32_t* idx,
                               float* score, float* w, bool host_kv, const int32_t* ctx_lens,
                               char* ws, hipStream_t s);
-// n_layers layers attending with one given selection (idx/w [B, Hkv, K], valid slots
-// first); q, O [n_layers, B, Hq, D], caches [n_layers, B, L, Hkv, D].
+// n_layers layers attending with one given selection (idx/w [B, Hkv, K]); q, O
+// [n_layers, B, Hq, D], caches [n_layers, B, L, Hkv, D] (host_kv: the device's view of
+// page-locked host memory).
 hipError_t launch_decode_shared(const Dims& d, int n_layers, const void* q, const void* Kc,
                                 const void* Vc, const int32_t* sel_idx, const float* sel_w,
-                                void* O, hipStream_t s);
+                                void* O, bool host_kv, hipStream_t s);
 hipError_t launch_decode_generic(const Dims& d, const DecLayout& lay, const void* q,
                                  const void* qs, const void* Kc, const void* Vc,
                                  const void* Kslc, void* O, int32_t* idx, float* score,

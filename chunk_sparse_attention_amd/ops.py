@@ -303,21 +303,34 @@ def fwd_layers(Q, K, V, idx, w, sm_scale=None, generic=False, ws=None, out=None)
 
 def decode_shared(q, Kc, Vc, idx, w, sm_scale=None):
     """Decode attention of a stack of layers with a selection made before (idx/w [B,Hkv,K]
-    from decode()): q [n,B,Hq,D], caches [n,B,ctx,Hkv,D].  Returns O [n,B,Hq,D]."""
-    _need(Kc, "Kcache")
+    from decode()): q [n,B,Hq,D], caches [n,B,ctx,Hkv,D] on the GPU, or pinned host tensors
+    (the host-cache variant).  Returns O [n,B,Hq,D]."""
+    host = not Kc.is_cuda
+    if host:
+        for t, name in ((Kc, "Kcache"), (Vc, "Vcache")):
+            if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned():
+                raise ValueError(f"{name} must be a GPU tensor or a pinned host tensor")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+    else:
+        _need(Kc, "Kcache")
     n, B, ctx, Hkv, D = Kc.shape
-    dev = Kc.device
+    dev = q.device
     Hq = q.shape[2]
     K_top = idx.shape[-1]
     _need(q, "q", Kc.dtype, (n, B, Hq, D), dev)
-    _need(Vc, "Vcache", Kc.dtype, (n, B, ctx, Hkv, D), dev)
+    if host:
+        if Vc.dtype != Kc.dtype or tuple(Vc.shape) != tuple(Kc.shape):
+            raise ValueError("Vcache must match Kcache in dtype and shape")
+    else:
+        _need(Vc, "Vcache", Kc.dtype, (n, B, ctx, Hkv, D), dev)
     _need(idx, "idx", torch.int32, (B, Hkv, K_top), dev)
     _need(w, "w", torch.float32, (B, Hkv, K_top), dev)
     prob = problem(B, ctx, Hq, Hkv, D, K_top, Kc.dtype, sm_scale=sm_scale)
     O = torch.empty((n, B, Hq, D), dtype=Kc.dtype, device=dev)
-    check(_lib.lib().hsa_decode_shared(ctypes.byref(prob), n, _ptr(q), _ptr(Kc), _ptr(Vc),
-                                       _ptr(idx), _ptr(w), _ptr(O), _stream()),
-          "hsa_decode_shared")
+    fn = _lib.lib().hsa_decode_shared_host_kv if host else _lib.lib().hsa_decode_shared
+    check(fn(ctypes.byref(prob), n, _ptr(q), _ptr(Kc), _ptr(Vc), _ptr(idx), _ptr(w), _ptr(O),
+             _stream()), "hsa_decode_shared_host_kv" if host else "hsa_decode_shared")
     return O
 
 

@@ -241,6 +241,15 @@ hsa_status_t hsa_decode_shared(const hsa_problem_t* p, int n_layers, const void*
                                const void* Kcache, const void* Vcache, const int32_t* idx,
                                const float* w, void* O, hsa_stream_t stream);
 
+/* hsa_decode_shared with the layers' token K/V caches in page-locked host memory (as for
+ * hsa_decode_host_kv: each cache pointer is checked with hipPointerGetAttributes first, and
+ * memory that is not host memory mapped for the device gives HSA_ERR_INVALID_ARG); only the
+ * selected chunks' rows cross the host link, once per layer and eight heads. */
+hsa_status_t hsa_decode_shared_host_kv(const hsa_problem_t* p, int n_layers, const void* q,
+                                       const void* Kcache, const void* Vcache,
+                                       const int32_t* idx, const float* w, void* O,
+                                       hsa_stream_t stream);
+
 /* ---- Kernel timing (measurement aid; not part of the operation) ----------------------
  * The entry points above each enqueue a short sequence of kernels.  To price one kernel
  * against the device's roofline, the library can bracket every launch of a kernel class

@@ -104,6 +104,12 @@ def test_entry_points_reject_before_launch():
     assert st == 1 and b"n_layers" in lib.hsa_last_error()
     st = lib.hsa_decode_shared(ctypes.byref(_prob()), 0, fake, fake, fake, fake, fake, fake, None)
     assert st == 1 and b"n_layers" in lib.hsa_last_error()
+    st = lib.hsa_decode_shared_host_kv(ctypes.byref(_prob()), 0, fake, fake, fake, fake, fake,
+                                       fake, None)
+    assert st == 1 and b"n_layers" in lib.hsa_last_error()
+    st = lib.hsa_decode_shared_host_kv(ctypes.byref(_prob()), 1, fake, None, fake, fake, fake,
+                                       fake, None)
+    assert st == 1 and b"Kcache" in lib.hsa_last_error()
     bad = _prob()
     bad.flags = 0x4  # no such problem flag
     st = lib.hsa_select(ctypes.byref(bad), fake, fake, fake, fake, fake, fake, None, 0, None)

@@ -502,6 +502,41 @@ def test_decode_shared_masked_slots(hsa, dev):
     assert max_abs(npy(O[0]), o[:, ctx]) <= 2e-2
 
 
+@pytest.mark.parametrize("K", [8, 12], ids=["k8", "k12"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_decode_shared_host_kv(hsa, dev, dtype, K):
+    """Shared-selection decode over pinned host caches: each head's sums are taken as with
+    device caches (only the grouping of heads into blocks differs), so the results are equal
+    bit for bit; pageable memory is refused."""
+    ctx, n = 64 * 30 + 17, 3
+    wl = W("decode_shared_host", 2, ctx, 16, 2, 64, 64, K, dtype)
+    say("case decode shared host kv", dtype, K)
+    xs = [workloads.make_decode_inputs(wl, seed=60 + l) for l in range(n)]
+    q = torch.stack([x["q"] for x in xs]).to(dev)
+    Kh = torch.stack([x["Kc"] for x in xs]).pin_memory()
+    Vh = torch.stack([x["Vc"] for x in xs]).pin_memory()
+    Kc, Vc = Kh.to(dev), Vh.to(dev)
+    _, idx, _, w = hsa.decode(q[0], xs[0]["qs"].to(dev), Kc[0], Vc[0], hsa.pool(Kc[0]), K)
+    ref = hsa.decode_shared(q, Kc, Vc, idx, w)
+    got = hsa.decode_shared(q, Kh, Vh, idx, w)
+    # views that start inside the pinned allocations
+    tail = hsa.decode_shared(q[1:], Kh[1:], Vh[1:], idx, w)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert torch.equal(tail, ref[1:])
+    from chunk_sparse_attention_amd import _lib
+    prob = hsa.problem(2, ctx, 16, 2, 64, K, dtype)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    Kp = Kh.clone()  # pageable host memory
+    for kc in (Kp, Kc):  # pageable host memory, then device memory
+        st = _lib.lib().hsa_decode_shared_host_kv(
+            ctypes.byref(prob), n, P(q), P(kc), P(kc), P(idx), P(w), P(got),
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == _lib.HSA_ERR_INVALID_ARG, _lib.lib().hsa_last_error()
+    with pytest.raises(ValueError):
+        hsa.decode_shared(q, Kp, Vh.clone(), idx, w)
+
+
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
 def test_decode_ragged(hsa, dev, generic):
     """Sequences of different lengths in one cache: each sequence's result equals hsa_decode
