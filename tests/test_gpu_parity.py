@@ -95,8 +95,9 @@ def compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=None, chunk_mask=No
     cm = np.ones((B, nC), bool) if chunk_mask is None else np.asarray(chunk_mask, bool).reshape(B, nC)
     # chunks whose selector sets differ between the two sides are not comparable
     touched = np.zeros((B, nC), bool)
+    gidx = npy(g["idx"])
     for (b, t, gg) in np.argwhere(diff):
-        for arr in (npy(g["idx"])[b, t, gg], f["idx"][b, t, gg]):
+        for arr in (gidx[b, t, gg], f["idx"][b, t, gg]):
             for c in arr:
                 if c >= 0:
                     touched[b, c] = True
@@ -774,6 +775,46 @@ def test_full_step_sampled(hsa, dev, name):
         cm[b, rng.choice(wl.nC, size=4, replace=False)] = 1
         cm[b, [0, wl.nC - 1]] = 1
     compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=tm, chunk_mask=cm)
+
+
+@pytest.mark.parametrize("D,Hq", [(64, 8), (128, 4)], ids=["d64", "d128"])
+def test_max_chunks_step_sampled(hsa, dev, D, Hq):
+    """The largest sequence the backward takes (16384 chunks and a ragged tail of 37 tokens):
+    select, forward and backward on one workspace.  dO is zero except on a sample T of rows,
+    so that the rows outside T add exact zeros to every gradient; the oracle then needs only
+    T's selection (its other rows select nothing), and dK, dV, dKslc are compared on the
+    chunks T selected plus others that must stay zero, dQ and dQs on T and rows outside it."""
+    from chunk_sparse_attention_amd import _lib
+    wl = W(f"max_chunks_d{D}", 1, 64 * 16384 + 37, Hq, 2, D, 64, 8, torch.bfloat16)
+    say("case max chunks step", wl)
+    x = workloads.make_inputs(wl, seed=11)
+    T = _sample_rows(wl, 40, seed=12)
+    x["dO"][torch.from_numpy(T == 0)] = 0
+    Q, K, V, Qs, dO = (x[k].to(dev) for k in ("Q", "K", "V", "Qs", "dO"))
+    prob = hsa.problem(wl.B, wl.L, wl.Hq, wl.Hkv, wl.D, wl.K, wl.dtype)
+    ws = hsa.workspace(_lib.HSA_OP_BWD, prob, dev)
+    Kslc, idx, score, w = hsa.select(Qs, K, wl.K)
+    O = hsa.fwd(Q, K, V, idx, w, ws=ws)
+    grads = hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, ws=ws, after_fwd=True)
+    torch.cuda.synchronize()
+    g = dict(Q=Q, K=K, V=V, Qs=Qs, Kslc=Kslc, idx=idx, score=score, w=w, O=O)
+    del Q, K, V, Qs, dO
+    orc = oracle.get()
+    f, diff, _ = compare_forward(orc, x, wl, g, row_mask=T)
+    rng = np.random.default_rng(13)
+    tm = T.copy()
+    tm[0, rng.choice(wl.L, size=64, replace=False)] = 1  # rows whose gradients must be zero
+    cm = np.zeros((wl.B, wl.nC), np.uint8)
+    sel = f["idx"][T.astype(bool)]
+    cm[0, np.unique(sel[sel >= 0])] = 1
+    picked = int(cm.sum())
+    cm[0, rng.choice(wl.nC, size=16, replace=False)] = 1
+    cm[0, [0, wl.nC - 1]] = 1
+    say("chunks selected by the sample:", picked, "compared:", int(cm.sum()))
+    compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=tm, chunk_mask=cm)
+    tail = slice(wl.nC * wl.S, wl.L)
+    assert torch.count_nonzero(grads["dK"][:, tail]).item() == 0
+    assert torch.count_nonzero(grads["dV"][:, tail]).item() == 0
 
 
 def test_full_decode(hsa, dev):
