@@ -40,6 +40,10 @@ METRIC = "HSA fwd+bwd tokens/sec at L=16K/64K bf16; % HBM roofline / MFMA util"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP64_VALU_PEAK_TFLOPS = 78.6   # 256 CUs x 4 SIMD x 16 lanes x 2 (FMA) x 2.4 GHz
+# v_exp_f32 results per second, measured on MI355X with a loop of eight independent exp2
+# chains per lane at 64 waves per CU (the same loop with fp32 FMA gives 57.2 T/s); the
+# attention's exponentials are priced against it as a third floor beside HBM and MFMA
+EXP_PEAK_PER_S = 17.9e12
 
 
 def log(*a):
@@ -77,7 +81,8 @@ def kernel_counts(wl, n_slots: int, fused: bool = True, chunked: bool = True) ->
     """Algorithmic bytes (each input the kernel needs read once, each output it produces
     written once; workspace copies of the design are not counted) and flops per launch of
     each kernel class.  n_slots = valid (b, t, g, k) selections; every slot is attended by
-    G query heads over S keys."""
+    G query heads over S keys.  "exps" counts the exponentials: one per logit in the forward
+    and one per logit again where the backward recomputes the probabilities."""
     el = 2 if str(wl.dtype).endswith("bfloat16") else 4
     B, L, Hq, Hkv, D, K, S = wl.B, wl.L, wl.Hq, wl.Hkv, wl.D, wl.K, wl.S
     q = B * L * Hq * D * el                 # Q, dO, O or dQ
@@ -91,22 +96,23 @@ def kernel_counts(wl, n_slots: int, fused: bool = True, chunked: bool = True) ->
                        alu=True),
         "tile_prep": dict(bytes=slot, flops=0),
         "prep_ops": dict(bytes=2 * kv, flops=0),
-        "fwd": dict(bytes=2 * q + 2 * kv + 2 * slot, flops=4 * S * D * eg),
+        "fwd": dict(bytes=2 * q + 2 * kv + 2 * slot, flops=4 * S * D * eg, exps=S * eg),
         "invidx": dict(bytes=slot + 4 * n_slots, flops=0),
-        "bwd_p1": dict(bytes=3 * q + 4 * kv + kslc + 4 * slot, flops=6 * S * D * eg),
+        "bwd_p1": dict(bytes=3 * q + 4 * kv + kslc + 4 * slot, flops=6 * S * D * eg,
+                       exps=S * eg),
         "bwd_p2": dict(bytes=2 * q + 5 * kv + 2 * slot + 4 * n_slots + 2 * kslc,
-                       flops=8 * S * D * eg),
+                       flops=8 * S * D * eg, exps=S * eg),
         "bwd_reduce": dict(bytes=2 * kv + 2 * kslc, flops=0),
     }
     if chunked:
         # chunk-major forward: Q, K, V and the slots in (the token phase writes O)
-        c["fwd"] = dict(bytes=q + 2 * kv + 2 * slot, flops=4 * S * D * eg)
+        c["fwd"] = dict(bytes=q + 2 * kv + 2 * slot, flops=4 * S * D * eg, exps=S * eg)
         c["fwd_token"] = dict(bytes=q + slot, flops=0)
     if fused:
         # token phase: dQ and dQs out, the slots and Kslc rows in; dKslc partials read Qs
         c["bwd_p1"] = dict(bytes=q + 2 * kv + kslc + 3 * slot, flops=0)
         # chunk phase: Q, dO, K, V and the weights in; S, dP, dV, dK and dQ products
-        c["bwd_p2"] = dict(bytes=2 * q + 2 * kv + slot, flops=10 * S * D * eg)
+        c["bwd_p2"] = dict(bytes=2 * q + 2 * kv + slot, flops=10 * S * D * eg, exps=S * eg)
     return c
 
 
@@ -131,6 +137,9 @@ def roofline(name: str, counts: dict, avg_ms: float, traffic) -> dict:
     r["avg_ms"] = round(avg_ms, 4)
     r["alg_bytes"] = int(counts["bytes"])
     r["alg_flops"] = int(counts["flops"])
+    if counts.get("exps"):
+        r["exps"] = int(counts["exps"])
+        r["exp_floor_ms"] = round(counts["exps"] / EXP_PEAK_PER_S * 1e3, 4)
     return r
 
 

@@ -43,6 +43,11 @@ def test_kernel_counts_follow_the_per_unit_figures():
     # chunk-major forward: Q, K, V and the slots in; the token phase writes O
     assert c["fwd"]["bytes"] == q + 2 * kv + 2 * slot
     assert c["fwd_token"]["bytes"] == q + slot
+    # one exponential per logit: S per (token, head, slot), again in the backward's recompute
+    assert c["fwd"]["exps"] == c["bwd_p2"]["exps"] == wl.S * eg
+    assert "exps" not in c["bwd_p1"]
+    r = bench.roofline("fwd", c["fwd"], 0.5, None)
+    assert r["exp_floor_ms"] == pytest.approx(wl.S * eg / bench.EXP_PEAK_PER_S * 1e3, abs=1e-4)
 
 
 def test_roofline_picks_the_binding_peak():
