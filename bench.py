@@ -133,6 +133,9 @@ def roofline(name: str, counts: dict, avg_ms: float, traffic) -> dict:
         r = dict(bound="hbm", achieved=round(ach, 2), peak=HBM_PEAK_GBS, unit="GB/s")
     r["frac"] = round(r["achieved"] / r["peak"], 5)
     r["traffic"] = traffic
+    # measured HBM bytes over the algorithmic bytes (re-reads and the design's workspace)
+    r["amplification"] = (round(traffic / counts["bytes"], 2)
+                          if traffic is not None and counts["bytes"] else None)
     r["kernel"] = name
     r["avg_ms"] = round(avg_ms, 4)
     r["alg_bytes"] = int(counts["bytes"])
@@ -246,9 +249,10 @@ def summarize_counters(cdir: str, workload: str, copy_mib: int) -> int:
     with open(traffic_path(workload), "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
-    # optional runs of the same command with L2 (DIR/l2) and SQ (DIR/sq) counters
+    # optional runs of the same command with L2 (DIR/l2), SQ (DIR/sq) and matrix-core / LDS
+    # (DIR/mx) counters
     extra = collections.defaultdict(lambda: collections.defaultdict(list))
-    for sub in ("l2", "sq"):
+    for sub in ("l2", "sq", "mx"):
         for f in glob.glob(os.path.join(cdir, sub, "**", "*counter_collection.csv"),
                            recursive=True)[:1]:
             with open(f) as fh:
@@ -256,11 +260,12 @@ def summarize_counters(cdir: str, workload: str, copy_mib: int) -> int:
                     cls, fn = kernel_class(r["Kernel_Name"])
                     if cls:
                         extra[fn][r["Counter_Name"]].append(float(r["Counter_Value"]))
-    if extra:
+    l2sq = {fn: c for fn, c in extra.items() if "TCC_HIT_sum" in c or "SQ_WAVES" in c}
+    if l2sq:
         print("\n| kernel | L2 hit rate | waves | per wave: VALU | MFMA | LDS | VMEM rd | "
               "wave cycles | waiting cycles |")
         print("|---|---:|---:|---:|---:|---:|---:|---:|---:|")
-        for fn, c in sorted(extra.items()):
+        for fn, c in sorted(l2sq.items()):
             m = {k: sum(v) / len(v) for k, v in c.items()}
             hit = m.get("TCC_HIT_sum", 0.0)
             tot = hit + m.get("TCC_MISS_sum", 0.0)
@@ -272,6 +277,20 @@ def summarize_counters(cdir: str, workload: str, copy_mib: int) -> int:
                   f"{pw('SQ_INSTS_MFMA')} | {pw('SQ_INSTS_LDS')} | {pw('SQ_INSTS_VMEM_RD')} | "
                   f"{pw('SQ_WAVE_CYCLES')} | {pw('SQ_WAIT_INST_ANY')} |" if tot else
                   f"| `{fn}` | - | {wv:.0f} | - | - | - | - | - | - |")
+    mx = {fn: {k: sum(v) / len(v) for k, v in c.items()} for fn, c in extra.items()
+          if "MfmaUtil" in c}
+    if mx:
+        # rocprofv3's derived metrics: MfmaUtil = matrix-core busy cycles over (GPU active
+        # cycles x SIMDs), in %; LdsBankConflict = bank-conflict stall cycles per LDS active
+        # cycle that was not a stall; LDSBankConflict = those stalls in % of GPU time.
+        # SQ_INSTS_VALU_MFMA_MOPS_BF16 counts executed bf16 matrix flops / 512.
+        print("\n| kernel | MFMA busy % | bf16 MFMA GFLOP executed per dispatch | "
+              "LDS bank-conflict cycles per access cycle | LDS bank-conflict % of time |")
+        print("|---|---:|---:|---:|---:|")
+        for fn, m in sorted(mx.items()):
+            print(f"| `{fn}` | {m.get('MfmaUtil', 0.0):.1f} | "
+                  f"{m.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0.0) * 512 / 1e9:.1f} | "
+                  f"{m.get('LdsBankConflict', 0.0):.3f} | {m.get('LDSBankConflict', 0.0):.2f} |")
     return 0
 
 

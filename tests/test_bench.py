@@ -55,11 +55,12 @@ def test_roofline_picks_the_binding_peak():
     units, for ALU-bound selection) its algorithmic counts make the longer."""
     # 8 GB at 8 TB/s = 1 ms beats 1 TFLOP at 2.5 PFLOP/s = 0.4 ms: HBM-bound
     r = bench.roofline("x", dict(bytes=8e9, flops=1e12), 2.0, None)
-    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["amplification"] is None
     assert r["achieved"] == pytest.approx(4000.0) and r["frac"] == pytest.approx(0.5)
     # 1 GB (0.125 ms) against 5 TFLOP (2 ms): MFMA-bound
-    r = bench.roofline("y", dict(bytes=1e9, flops=5e12), 4.0, 123)
-    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["traffic"] == 123
+    r = bench.roofline("y", dict(bytes=1e9, flops=5e12), 4.0, 2.5e9)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["traffic"] == 2.5e9
+    assert r["amplification"] == pytest.approx(2.5)  # measured over algorithmic bytes
     assert r["achieved"] == pytest.approx(1250.0) and r["frac"] == pytest.approx(0.5)
     r = bench.roofline("z", dict(bytes=1e6, flops=78.6e9, alu=True), 2.0, None)
     assert r["bound"] == "alu" and r["peak"] == 78.6 and r["frac"] == pytest.approx(0.5)

@@ -777,15 +777,16 @@ def test_full_step_sampled(hsa, dev, name):
     compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=tm, chunk_mask=cm)
 
 
-@pytest.mark.parametrize("D,Hq", [(64, 8), (128, 4)], ids=["d64", "d128"])
-def test_max_chunks_step_sampled(hsa, dev, D, Hq):
+@pytest.mark.parametrize("D,Hq,Hkv", [(64, 8, 2), (128, 4, 1)], ids=["d64", "d128"])
+def test_max_chunks_step_sampled(hsa, dev, D, Hq, Hkv):
     """The largest sequence the backward takes (16384 chunks and a ragged tail of 37 tokens):
     select, forward and backward on one workspace.  dO is zero except on a sample T of rows,
     so that the rows outside T add exact zeros to every gradient; the oracle then needs only
     T's selection (its other rows select nothing), and dK, dV, dKslc are compared on the
     chunks T selected plus others that must stay zero, dQ and dQs on T and rows outside it."""
     from chunk_sparse_attention_amd import _lib
-    wl = W(f"max_chunks_d{D}", 1, 64 * 16384 + 37, Hq, 2, D, 64, 8, torch.bfloat16)
+    wl = W(f"max_chunks_d{D}", 1, 64 * 16384 + 37, Hq, Hkv, D, 64, 8, torch.bfloat16)
+    assert wl.G == 4  # the matrix-core forward and backward
     say("case max chunks step", wl)
     x = workloads.make_inputs(wl, seed=11)
     T = _sample_rows(wl, 40, seed=12)
