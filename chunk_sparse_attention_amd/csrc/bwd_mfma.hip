@@ -53,7 +53,9 @@ k_bwd_chunk_mfma(
   // two waves share the segment's chunk in LDS and take alternate jobs; their dK/dV sums
   // meet in LDS at the end
   constexpr int D = 64, TPJ = 16 / G, KS = D / 32, DT = D / 16, NW = 2, NT = 64 * NW;
-  constexpr int KROW = D + 8, WREGION = 2 * 16 * KROW + 64 * 16;
+  // rows of D + 16 elements keep the 16-byte operand reads and the transposing reads free
+  // of LDS bank conflicts; the dS^T tile is swizzled as the forward's P~^T tile
+  constexpr int KROW = D + 16, WREGION = 2 * 16 * KROW + 64 * 16;
   __shared__ __attribute__((aligned(16))) uint16_t sm[2 * 64 * KROW + NW * WREGION];
   __shared__ int tok_l[kBwdSeg];
   __shared__ int64_t eo_l[kBwdSeg];  // the entry's (b, t, g, slot) index
@@ -201,6 +203,7 @@ k_bwd_chunk_mfma(
     // transposed operands read from LDS with the transposing read; dS^T goes to LDS for dQ
     s16x4 doT[DT], qT[DT];
     const int trow = 4 * blk + col / 4, tcol = 4 * (col % 4);
+    const int pcol = 4 * ((col % 4) ^ blk);  // tcol in the swizzled dS^T rows 4*blk + col/4
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       doT[dt] = lds_read_tr4(&dl[trow][16 * dt + tcol]);
@@ -215,7 +218,7 @@ k_bwd_chunk_mfma(
         dsv[i] = wr[i] * sa[t4][i] * (pa[t4][i] - dr[i]);
       }
       const s16x4 wpb = pack_bf16x4(wp), dsb = pack_bf16x4(dsv);
-      *reinterpret_cast<s16x4*>(&sdl[16 * t4 + col][4 * blk]) = dsb;
+      *reinterpret_cast<s16x4*>(&sdl[16 * t4 + col][4 * (blk ^ (col / 4))]) = dsb;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         dv[dt][t4] = mfma_16x16x16(doT[dt], wpb, dv[dt][t4]);
@@ -231,8 +234,8 @@ k_bwd_chunk_mfma(
     for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 dsT = cat_bf16x8(lds_read_tr4(&sdl[32 * kk + trow][tcol]),
-                                    lds_read_tr4(&sdl[32 * kk + 16 + trow][tcol]));
+      const bf16x8 dsT = cat_bf16x8(lds_read_tr4(&sdl[32 * kk + trow][pcol]),
+                                    lds_read_tr4(&sdl[32 * kk + 16 + trow][pcol]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
         dq[dt] = mfma_16x16x32(cat_bf16x8(lds_read_tr4(&kl[32 * kk + trow][16 * dt + tcol]),
@@ -313,11 +316,14 @@ k_bwd_chunk_keys(
     bf16* __restrict__ dq_part, float* __restrict__ dw_out, int L, int Hq, int Hkv, int Kn,
     int nC, int seg, int64_t max_seg, float c2, float sm_scale) {
   constexpr int D = 128, TPJ = 16 / G, KS = D / 32, DT = D / 16, NT = 128;
-  constexpr int KROW = D + 8;
+  // rows of D + 16 elements: no LDS bank conflicts in the operand and transposing reads
+  constexpr int KROW = D + 16;
   __shared__ __attribute__((aligned(16))) uint16_t kl[64][KROW];
   __shared__ __attribute__((aligned(16))) uint16_t ql[16][KROW];
   __shared__ __attribute__((aligned(16))) uint16_t dl[16][KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sdl[64][16];  // dS^T of the job
+  // dS^T of the job; column group j of row r sits at group j ^ ((r / 4) % 4), so that the
+  // 8-byte stores and the transposing reads both spread over the banks
+  __shared__ __attribute__((aligned(16))) uint16_t sdl[64][16];
   __shared__ float xl[3][2][16];  // per wave and row: D half; without HL also max, sum
   __shared__ int tok_l[kBwdSeg];
   __shared__ int64_t eo_l[kBwdSeg];  // the entry's (b, t, g, slot) index
@@ -367,6 +373,7 @@ k_bwd_chunk_keys(
     }
   const int qs_sel = col / G, qs_head = col % G;  // this lane's query row -> selector, head
   const int trow = 4 * blk + col / 4, tcol = 4 * (col % 4);
+  const int pcol = 4 * ((col % 4) ^ blk);  // tcol in the swizzled dS^T rows 4*blk + col/4
   // staging of job j: thread tid copies 32 bytes of row tid/8 of Q and of dO (a padding row
   // repeats the job's first selector)
   const int srow = tid / 8, spc = tid % 8;
@@ -491,7 +498,7 @@ k_bwd_chunk_keys(
       }
       wpb[t2] = pack_bf16x4(wp);
       dsb[t2] = pack_bf16x4(dsv);
-      *reinterpret_cast<s16x4*>(&sdl[32 * wv + 16 * t2 + col][4 * blk]) = dsb[t2];
+      *reinterpret_cast<s16x4*>(&sdl[32 * wv + 16 * t2 + col][4 * (blk ^ (col / 4))]) = dsb[t2];
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -512,8 +519,8 @@ k_bwd_chunk_keys(
     for (int j = 0; j < 4; ++j) dq[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 dsT = cat_bf16x8(lds_read_tr4(&sdl[32 * kk + trow][tcol]),
-                                    lds_read_tr4(&sdl[32 * kk + 16 + trow][tcol]));
+      const bf16x8 dsT = cat_bf16x8(lds_read_tr4(&sdl[32 * kk + trow][pcol]),
+                                    lds_read_tr4(&sdl[32 * kk + 16 + trow][pcol]));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d0 = 64 * wv + 16 * j;

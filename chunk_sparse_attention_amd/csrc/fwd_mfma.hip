@@ -289,10 +289,15 @@ __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
     bf16* __restrict__ o_part, float* __restrict__ lse_out, int L, int Hq, int Hkv, int Kn,
     int nC, int seg, int64_t max_seg, float c2) {
   constexpr int TPJ = 16 / G, KS = D / 32, DT = D / 16, NT = 64 * NW;
-  constexpr int KROW = D + 8;
+  // Rows of D + 16 elements (a stride of 8 banks) keep both the 16-byte key reads and the
+  // transposing value reads free of LDS bank conflicts.
+  constexpr int KROW = D + 16;
   __shared__ __attribute__((aligned(16))) uint16_t kl[64][KROW];
   __shared__ __attribute__((aligned(16))) uint16_t vl[64][KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t pl[NW][64][16];  // P~^T of a wave's job
+  // P~^T of a wave's job, 64 key rows of 16 query columns.  Column group j (four columns,
+  // 8 bytes) of row r sits at group j ^ ((r / 4) % 4): the 8-byte stores (16 rows at one
+  // group) and the transposing reads (4 rows at all groups) then both spread over the banks.
+  __shared__ __attribute__((aligned(16))) uint16_t pl[NW][64][16];
   __shared__ int tok_l[kBwdSeg];
   __shared__ int64_t eo_l[kBwdSeg];  // the entry's (b, t, g, slot) index
   __shared__ float w_l[kBwdSeg];
@@ -328,6 +333,7 @@ __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
   __syncthreads();
   const int qs_sel = col / G, qs_head = col % G;  // this lane's A-operand row -> selector, head
   const int trow = 4 * blk + col / 4, tcol = 4 * (col % 4);
+  const int pcol = 4 * ((col % 4) ^ blk);  // tcol in the swizzled P~^T rows 4*blk + col/4
   const bf16* qbase = Q + ((b * L * Hq + (size_t)g * G + qs_head) * D + 8 * blk);
   const size_t qstride = (size_t)Hq * D;  // per token
   // this lane's query row of job j (a padding row repeats the job's first selector)
@@ -401,7 +407,8 @@ __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
     for (int t4 = 0; t4 < 4; ++t4) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sa[t4][i] *= f[i];
-      *reinterpret_cast<s16x4*>(&pl[wv][16 * t4 + col][4 * blk]) = pack_bf16x4(sa[t4]);
+      *reinterpret_cast<s16x4*>(&pl[wv][16 * t4 + col][4 * (blk ^ (col / 4))]) =
+          pack_bf16x4(sa[t4]);
     }
     wave_lds_sync();  // P~^T is read transposed below
     // O^T (rows d, columns the 16 query rows) = V_c^T P~^T, 32 keys per product: lane block
@@ -411,8 +418,8 @@ __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 pT = cat_bf16x8(lds_read_tr4(&pl[wv][32 * kk + trow][tcol]),
-                                   lds_read_tr4(&pl[wv][32 * kk + 16 + trow][tcol]));
+      const bf16x8 pT = cat_bf16x8(lds_read_tr4(&pl[wv][32 * kk + trow][pcol]),
+                                   lds_read_tr4(&pl[wv][32 * kk + 16 + trow][pcol]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
         o[dt] = mfma_16x16x32(cat_bf16x8(lds_read_tr4(&vl[32 * kk + trow][16 * dt + tcol]),
