@@ -343,9 +343,18 @@ def cpu_baseline(wl, x, budget_s: float = 20.0) -> dict:
     # OpenMP uses OMP_NUM_THREADS threads when it is set, else one per CPU of the affinity mask
     env = os.environ.get("OMP_NUM_THREADS", "")
     cores = int(env) if env.isdigit() else len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return dict(value=round(done * wl.L / el, 2), unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"{done} of {wl.B} sequences x {wl.L} tokens: pool+select+attend+"
-                       f"backward in {el:.1f} s")
+                       f"backward in {el:.1f} s", cpu=model)
 
 
 def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
