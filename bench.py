@@ -71,17 +71,25 @@ def fused_backward(wl, generic: bool) -> bool:
             and wl.G in (4, 8, 16) and wl.nC < 32768)
 
 
+def mfma_select(wl, generic: bool) -> bool:
+    """The library's bf16 selection: matrix-core scores of every candidate, fp64 rescoring."""
+    return not generic and str(wl.dtype).endswith("bfloat16")
+
+
 def chunked_forward(wl, generic: bool) -> bool:
     """The library's bf16 chunk-major forward (inverse index, per-edge partials, token sums)."""
     return (not generic and str(wl.dtype).endswith("bfloat16") and wl.D in (64, 128)
             and wl.G in (4, 8, 16) and wl.nC <= 16384)
 
 
-def kernel_counts(wl, n_slots: int, fused: bool = True, chunked: bool = True) -> dict:
+def kernel_counts(wl, n_slots: int, fused: bool = True, chunked: bool = True,
+                  mfma_select: bool = True) -> dict:
     """Algorithmic bytes (each input the kernel needs read once, each output it produces
     written once; workspace copies of the design are not counted) and flops per launch of
     each kernel class.  n_slots = valid (b, t, g, k) selections; every slot is attended by
-    G query heads over S keys.  "exps" counts the exponentials: one per logit in the forward
+    G query heads over S keys.  Selection scores every candidate on the matrix cores when
+    mfma_select (bf16: the products are exact there, and only about K candidates per token
+    are rescored in fp64), else on the fp64 vector units.  "exps" counts the exponentials: one per logit in the forward
     and one per logit again where the backward recomputes the probabilities."""
     el = 2 if str(wl.dtype).endswith("bfloat16") else 4
     B, L, Hq, Hkv, D, K, S = wl.B, wl.L, wl.Hq, wl.Hkv, wl.D, wl.K, wl.S
@@ -93,7 +101,7 @@ def kernel_counts(wl, n_slots: int, fused: bool = True, chunked: bool = True) ->
     c = {
         "pool": dict(bytes=kv + kslc, flops=B * wl.nC * Hkv * D * S),
         "select": dict(bytes=kv + kslc + 3 * slot, flops=2 * D * causal_candidates(wl),
-                       alu=True),
+                       alu=not mfma_select),
         "tile_prep": dict(bytes=slot, flops=0),
         "prep_ops": dict(bytes=2 * kv, flops=0),
         "fwd": dict(bytes=2 * q + 2 * kv + 2 * slot, flops=4 * S * D * eg, exps=S * eg),
@@ -118,7 +126,7 @@ def kernel_counts(wl, n_slots: int, fused: bool = True, chunked: bool = True) ->
 
 def roofline(name: str, counts: dict, avg_ms: float, traffic) -> dict:
     """Price one kernel's average launch against MI355X's peaks: HBM bandwidth, dense bf16
-    MFMA or, for the fp64 vector-ALU scoring, the fp64 vector rate."""
+    MFMA or, for scoring on the fp64 vector units, the fp64 vector rate."""
     t_hbm = counts["bytes"] / (HBM_PEAK_GBS * 1e9)
     alu = counts.get("alu", False)
     peak_f = FP64_VALU_PEAK_TFLOPS if alu else BF16_PEAK_TFLOPS
@@ -670,7 +678,8 @@ def main() -> int:
     pct = {f"p{p}": round(per_step[min(len(per_step) - 1, int(p / 100 * len(per_step)))], 4)
            for p in (10, 50, 90)}
     log("bench: per-entry ms", entry_ms)
-    counts = kernel_counts(wl, n_slots, fused_backward(wl, gen), chunked_forward(wl, gen))
+    counts = kernel_counts(wl, n_slots, fused_backward(wl, gen), chunked_forward(wl, gen),
+                           mfma_select(wl, gen))
     kern = {}
     for name, (n, total) in ktimes.items():
         if n == 0:
@@ -766,7 +775,8 @@ def main() -> int:
         ts /= reps
         tf /= reps
         tb /= reps
-        c2 = kernel_counts(wl2, n2, fused_backward(wl2, gen), chunked_forward(wl2, gen))
+        c2 = kernel_counts(wl2, n2, fused_backward(wl2, gen), chunked_forward(wl2, gen),
+                           mfma_select(wl2, gen))
         k2 = {name: roofline(name, c2[name], total / n, measured_traffic(wl2.name, name))
               for name, (n, total) in kt2.items() if n}
         out["secondary"] = {

@@ -84,7 +84,9 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
   __shared__ int fall[64];
   __shared__ int candl[64][kSelCap];
   const int bg = blockIdx.x % BG;
-  const int q = blockIdx.x / BG;  // query chunk of the tile: its tokens see chunks < q
+  // query chunk of the tile (its tokens see chunks < q); a tile's work grows with q, so the
+  // grid hands out the last tiles first and the short ones fill in behind them
+  const int q = (int)(gridDim.x / BG) - 1 - (int)(blockIdx.x / BG);
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const int t0 = q * 64;

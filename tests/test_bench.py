@@ -35,6 +35,9 @@ def test_kernel_counts_follow_the_per_unit_figures():
     assert c["fwd"]["flops"] == 4 * wl.S * wl.D * eg
     assert c["bwd_p2"]["flops"] == 10 * wl.S * wl.D * eg
     assert c["select"]["flops"] == 2 * wl.D * bench.causal_candidates(wl)
+    # bf16 selection scores on the matrix cores; fp32 selection on the fp64 vector units
+    assert not c["select"]["alu"]
+    assert bench.kernel_counts(wl, n_slots, mfma_select=False)["select"]["alu"]
     kv = wl.B * wl.L * wl.Hkv * wl.D * 2
     kslc = wl.B * wl.nC * wl.Hkv * wl.D * 2
     assert c["pool"]["bytes"] == kv + kslc
