@@ -14,6 +14,10 @@
 //   2. T = the K-th largest approximate score of the token.  Every chunk of the exact top-K
 //      has an approximate score >= T - 2E: if V is the exact K-th largest score, then T <=
 //      V + E (else K chunks would score above V exactly) and each member scores >= V - E.
+//      The four lanes of a token keep only their KP largest approximate scores, and T is
+//      taken as the K-th largest of those 4 KP values: a subset's K-th largest is at most
+//      the whole set's, so the bound still holds (a lane holding more than KP of the top-K
+//      only lowers T and adds candidates).
 //   3. The chunks at or above T - 2E (about K per token) are rescored exactly in fp64 and
 //      ranked; a token with more than kSelCap such chunks, or any non-finite value, is
 //      scored exactly over all its candidates instead.
@@ -49,28 +53,37 @@ __device__ __forceinline__ uint32_t ord_f32(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Stick-breaking over a ranked list and the output writes of one (token, group) row.
-__device__ __forceinline__ void write_row(const uint64_t (&top)[kMaxK], int Kt, size_t o,
-                                          int32_t* idx, float* score, float* w) {
-  double rem = 1.0;
-  for (int k = 0; k < Kt; ++k) {
-    const uint64_t key = top[k];
-    if (key == 0) {
-      idx[o + k] = -1;
-      score[o + k] = -__builtin_inff();
-      w[o + k] = 0.0f;
-    } else {
-      const float s = key_score(key);
-      const double p = sigmoid_d((double)s);
-      idx[o + k] = key_chunk(key);
-      score[o + k] = s;
-      w[o + k] = (float)(p * rem);
-      rem *= 1.0 - p;
-    }
+// Output slot k of one (token, group) row from its ranked key (0: a masked slot), with the
+// stick-breaking weight: the sigmoid of the score times the stick left by slots < k.
+__device__ __forceinline__ void write_slot(uint64_t key, int k, size_t o, double& rem,
+                                           int32_t* idx, float* score, float* w) {
+  if (key == 0) {
+    idx[o + k] = -1;
+    score[o + k] = -__builtin_inff();
+    w[o + k] = 0.0f;
+  } else {
+    const float sc = key_score(key);
+    const double p = sigmoid_d((double)sc);
+    idx[o + k] = key_chunk(key);
+    score[o + k] = sc;
+    w[o + k] = (float)(p * rem);
+    rem *= 1.0 - p;
   }
 }
 
-template <int D, int KL>
+// Inserts key into a descending list of N keys (the smallest falls off).
+template <int N>
+__device__ __forceinline__ void insert_key(uint64_t (&tk)[N], uint64_t key) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (key > tk[i]) {
+      const uint64_t x = tk[i];
+      tk[i] = key;
+      key = x;
+    }
+}
+
+template <int D, int KL, int KP>
 __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs,
                                                      const bf16* __restrict__ Kslc,
                                                      int32_t* __restrict__ idx,
@@ -157,12 +170,13 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
     }
   };
 
-  // 1. the KL >= K largest approximate scores of this lane's share, kept sorted by a
+  // 1. the KP largest approximate scores of this lane's share (4 KP >= K), kept sorted by a
   //    branch-free compare-exchange chain that the wave skips when no lane beats its last
   //    entry; any non-finite value marks the token for the exact path
-  float top[KL];
+  static_assert(4 * KP >= KL, "the token's four lists must hold K scores");
+  float top[KP];
 #pragma unroll
-  for (int i = 0; i < KL; ++i) top[i] = -__builtin_inff();
+  for (int i = 0; i < KP; ++i) top[i] = -__builtin_inff();
   float k2max = 0.0f;
   bool bad = (__float_as_uint(q2) & 0x7f800000u) == 0x7f800000u;
   if (m > 0) fetch(0);
@@ -182,9 +196,9 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
         const bool fin = (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u;  // not inf or NaN
         bad = bad || (c < m && !fin);
         v = (c < m && fin) ? v : -__builtin_inff();
-        if (__ballot(v > top[KL - 1])) {
+        if (__ballot(v > top[KP - 1])) {
 #pragma unroll
-          for (int j = 0; j < KL; ++j) {
+          for (int j = 0; j < KP; ++j) {
             const float hi = fmaxf(top[j], v);
             v = fminf(top[j], v);
             top[j] = hi;
@@ -200,8 +214,8 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
     const uint64_t best = rows4_max_key(key);
     if (best == key) {
 #pragma unroll
-      for (int j = 0; j + 1 < KL; ++j) top[j] = top[j + 1];
-      top[KL - 1] = -__builtin_inff();
+      for (int j = 0; j + 1 < KP; ++j) top[j] = top[j + 1];
+      top[KP - 1] = -__builtin_inff();
     }
     const uint32_t bo = (uint32_t)(best >> 2);
     T = __uint_as_float((bo & 0x80000000u) ? (bo ^ 0x80000000u) : ~bo);
@@ -260,14 +274,7 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
           dot = fma((double)bf16_hi(qw[h]), (double)bf16_hi(kw[h]), dot);
         }
       }
-      uint64_t key = rank_key((float)(sel_scale * dot), c);
-#pragma unroll
-      for (int i = 0; i < KL; ++i)
-        if (key > tk[i]) {
-          const uint64_t x = tk[i];
-          tk[i] = key;
-          key = x;
-        }
+      insert_key(tk, rank_key((float)(sel_scale * dot), c));
     }
     const bool writer = sub == 0 && tt < L && !fb;  // a token without candidates: all masked
     const size_t o = ((b * L + tt) * Hkv + g) * Kt;
@@ -279,44 +286,35 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
         for (int i = 0; i + 1 < KL; ++i) tk[i] = tk[i + 1];
         tk[KL - 1] = 0;
       }
-      if (writer) {
-        if (best == 0) {
-          idx[o + k] = -1;
-          score[o + k] = -__builtin_inff();
-          w[o + k] = 0.0f;
-        } else {
-          const float sc = key_score(best);
-          const double p = sigmoid_d((double)sc);
-          idx[o + k] = key_chunk(best);
-          score[o + k] = sc;
-          w[o + k] = (float)(p * rem);
-          rem *= 1.0 - p;
-        }
-      }
+      if (writer) write_slot(best, k, o, rem, idx, score, w);
     }
   }
   // tokens for the exact path over all their candidates, one token at a time per wave
   for (int j = 0; j < 16; ++j) {
     const int tj = 16 * wave + j, tt = t0 + tj;
     if (tt >= L || !(fall[tj] || cnt[tj] > kSelCap)) continue;  // uniform over the wave
-    uint64_t tk[kMaxK];
+    uint64_t tk[KL];
 #pragma unroll
-    for (int i = 0; i < kMaxK; ++i) tk[i] = 0;
+    for (int i = 0; i < KL; ++i) tk[i] = 0;
     for (int c = lane; c < m; c += 64) {
       const bf16* kr = kbase + (size_t)c * Hkv * D;
       double dot = 0.0;
       for (int e = 0; e < D; ++e)
         dot = fma((double)to_f32(bf16{qraw[tj][e]}), (double)to_f32(kr[e]), dot);
-      topk_insert(tk, rank_key((float)(sel_scale * dot), c), Kt);
+      insert_key(tk, rank_key((float)(sel_scale * dot), c));
     }
-    uint64_t merged[kMaxK];
+    // the wave's ranked top-K: K rounds of the maximum over the lanes' list heads
+    const size_t o = ((b * L + tt) * Hkv + g) * Kt;
+    double rem = 1.0;
     for (int k = 0; k < Kt; ++k) {
       const uint64_t best = wave_max_key(tk[0]);
-      if (best != 0 && tk[0] == best) topk_pop(tk);
-      merged[k] = best;
+      if (best != 0 && tk[0] == best) {
+#pragma unroll
+        for (int i = 0; i + 1 < KL; ++i) tk[i] = tk[i + 1];
+        tk[KL - 1] = 0;
+      }
+      if (lane == 0) write_slot(best, k, o, rem, idx, score, w);
     }
-    for (int k = Kt; k < kMaxK; ++k) merged[k] = 0;
-    if (lane == 0) write_row(merged, Kt, ((b * L + tt) * Hkv + g) * Kt, idx, score, w);
   }
 }
 
@@ -331,12 +329,13 @@ hipError_t launch_select_mfma(const Dims& d, const void* Qs, const void* Kslc, i
     kern<<<dim3(BG * n_tiles), 256, 0, s>>>((const bf16*)Qs, (const bf16*)Kslc, idx, score, w,
                                             d.L, d.Hkv, d.K, d.nC, BG, d.sel_scale);
   };
+  // KP = K/4 + 2 scores per lane in the filter's first pass
   if (d.D == 64) {
-    if (d.K <= 8) go(k_select_mfma<64, 8>);
-    else go(k_select_mfma<64, 16>);
+    if (d.K <= 8) go(k_select_mfma<64, 8, 4>);
+    else go(k_select_mfma<64, 16, 6>);
   } else {
-    if (d.K <= 8) go(k_select_mfma<128, 8>);
-    else go(k_select_mfma<128, 16>);
+    if (d.K <= 8) go(k_select_mfma<128, 8, 4>);
+    else go(k_select_mfma<128, 16, 6>);
   }
   return hipGetLastError();
 }
