@@ -541,9 +541,10 @@ def test_decode_shared_host_kv(hsa, dev, dtype, K):
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
 def test_decode_ragged(hsa, dev, generic):
     """Sequences of different lengths in one cache: each sequence's result equals hsa_decode
-    on its own prefix bit for bit, and the oracle's."""
+    on its own prefix bit for bit, and the oracle's; a sequence of length 0 (or a negative
+    length, which counts as 0) selects nothing: every slot masked, O zero."""
     cap = 64 * 40 + 5
-    lens = [40, 64 * 7 + 13, 64 * 33, cap]
+    lens = [0, 40, 64 * 7 + 13, -7, 64 * 33, cap]
     wl = W("decode_ragged", len(lens), cap, 16, 2, 64, 64, 8, torch.bfloat16)
     say("case decode ragged", lens, generic)
     x = workloads.make_decode_inputs(wl, seed=12)
@@ -554,6 +555,10 @@ def test_decode_ragged(hsa, dev, generic):
     torch.cuda.synchronize()
     orc = oracle.get()
     for b, n in enumerate(lens):
+        if n <= 0:
+            assert torch.all(got[1][b] == -1) and torch.all(got[3][b] == 0)
+            assert torch.all(torch.isneginf(got[2][b])) and torch.all(got[0][b] == 0)
+            continue
         Kb, Vb = Kc[b:b + 1, :n].contiguous(), Vc[b:b + 1, :n].contiguous()
         ref = hsa.decode(q[b:b + 1], qs[b:b + 1], Kb, Vb, hsa.pool(Kb), wl.K, generic=generic)
         torch.cuda.synchronize()
