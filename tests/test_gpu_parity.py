@@ -422,6 +422,33 @@ def test_fwd_layers(hsa, dev, wl, generic):
         assert max_abs(npy(O[l]), o) <= tol_for(wl.dtype), l
 
 
+@pytest.mark.parametrize("wl", [w for w in LAYER_CASES if w.dtype == torch.bfloat16],
+                         ids=lambda w: w.name)
+def test_fwd_layers_then_backward(hsa, dev, wl):
+    """After hsa_fwd_layers the workspace holds the last layer's forward state: a backward of
+    that layer with HSA_BWD_AFTER_FWD equals, bit for bit, the one after hsa_fwd of that
+    layer alone."""
+    from chunk_sparse_attention_amd import _lib
+    say("case fwd_layers then backward", wl)
+    n = 3
+    xs = [workloads.make_inputs(wl, seed=70 + l) for l in range(n)]
+    Q = torch.stack([x["Q"] for x in xs]).to(dev)
+    K = torch.stack([x["K"] for x in xs]).to(dev)
+    V = torch.stack([x["V"] for x in xs]).to(dev)
+    Qs, dO = xs[0]["Qs"].to(dev), xs[-1]["dO"].to(dev)
+    Kslc, idx, score, w = hsa.select(Qs, K[0], wl.K)
+    prob = hsa.problem(wl.B, wl.L, wl.Hq, wl.Hkv, wl.D, wl.K, wl.dtype)
+    ws = hsa.workspace(_lib.HSA_OP_BWD, prob, dev)
+    hsa.fwd_layers(Q, K, V, idx, w, ws=ws)
+    got = hsa.bwd(Q[-1], K[-1], V[-1], Qs, Kslc, idx, score, w, dO, ws=ws, after_fwd=True)
+    ws2 = hsa.workspace(_lib.HSA_OP_BWD, prob, dev)
+    hsa.fwd(Q[-1], K[-1], V[-1], idx, w, ws=ws2)
+    ref = hsa.bwd(Q[-1], K[-1], V[-1], Qs, Kslc, idx, score, w, dO, ws=ws2, after_fwd=True)
+    torch.cuda.synchronize()
+    for k in ("dQ", "dK", "dV", "dQs"):
+        assert torch.equal(got[k], ref[k]), k
+
+
 def test_fwd_layers_token_tiles(hsa, dev):
     """Past 16384 chunks the forward runs on token tiles; their job lists are built once for
     the stack: each layer equals hsa_fwd's (whose parity the token-tile test checks)."""
