@@ -91,8 +91,7 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
                                                      float* __restrict__ w, int L, int Hkv,
                                                      int Kt, int nC, int BG, double sel_scale) {
   constexpr int KS = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t qraw[64][D + 8];  // the tile's Qs rows
-  __shared__ __attribute__((aligned(16))) uint16_t kl[64][D + 8];    // a group of 64 chunks
+  __shared__ __attribute__((aligned(16))) uint16_t kl[64][D + 8];  // a group of 64 chunks
   __shared__ int cnt[64];
   __shared__ int fall[64];
   __shared__ int candl[64][kSelCap];
@@ -111,24 +110,20 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
   const float sel_f = (float)sel_scale;
   const bf16* kbase = Kslc + (b * nC * Hkv + g) * (size_t)D;  // chunk c row: + c * Hkv * D
 
-  for (int i = tid; i < 64 * D / 8; i += 256) {
-    const int r = i / (D / 8), e = (i % (D / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t0 + r < L) v = *reinterpret_cast<const uint4*>(Qs + ((b * L + t0 + r) * Hkv + g) * D + e);
-    *reinterpret_cast<uint4*>(&qraw[r][e]) = v;
-  }
   if (tid < 64) {
     cnt[tid] = 0;
     fall[tid] = 0;
   }
   __syncthreads();
 
-  // B operand: this lane's token column, 8 dimensions per k-step; |q|^2 over the 4 lanes
+  // B operand: this lane's token column, 8 dimensions per k-step, read from the token's
+  // Qs row (zero past the sequence); |q|^2 over the 4 lanes
   bf16x8 qb[KS];
   float q2 = 0.0f;
+  const bf16* qrow = Qs + ((b * L + (size_t)t) * Hkv + g) * D;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qb[ks] = *reinterpret_cast<const bf16x8*>(&qraw[tl][32 * ks + 8 * blk]);
+    qb[ks] = t < L ? ld_bf16x8(qrow + 32 * ks + 8 * blk) : zero_bf16x8();
     q2 += sq8(qb[ks]);
   }
   q2 = rows4_sum(q2);
@@ -255,7 +250,8 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
   {
     const int tj = 16 * wave + lane / 4, sub = lane % 4, tt = t0 + tj;
     const bool fb = fall[tj] || cnt[tj] > kSelCap;
-    const int n = fb ? 0 : cnt[tj];
+    const int n = (fb || tt >= L) ? 0 : cnt[tj];  // rows past the sequence read nothing
+    const bf16* qr = Qs + ((b * L + (size_t)tt) * Hkv + g) * D;
     uint64_t tk[KL];
 #pragma unroll
     for (int i = 0; i < KL; ++i) tk[i] = 0;
@@ -266,7 +262,7 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
 #pragma unroll 2
       for (int e = 0; e < D; e += 8) {
         const uint4 kv = *reinterpret_cast<const uint4*>(kr + e);
-        const uint4 qv = *reinterpret_cast<const uint4*>(&qraw[tj][e]);
+        const uint4 qv = *reinterpret_cast<const uint4*>(qr + e);
         const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, qw[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
@@ -296,11 +292,11 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
     uint64_t tk[KL];
 #pragma unroll
     for (int i = 0; i < KL; ++i) tk[i] = 0;
+    const bf16* qr = Qs + ((b * L + (size_t)tt) * Hkv + g) * D;
     for (int c = lane; c < m; c += 64) {
       const bf16* kr = kbase + (size_t)c * Hkv * D;
       double dot = 0.0;
-      for (int e = 0; e < D; ++e)
-        dot = fma((double)to_f32(bf16{qraw[tj][e]}), (double)to_f32(kr[e]), dot);
+      for (int e = 0; e < D; ++e) dot = fma((double)to_f32(qr[e]), (double)to_f32(kr[e]), dot);
       insert_key(tk, rank_key((float)(sel_scale * dot), c));
     }
     // the wave's ranked top-K: K rounds of the maximum over the lanes' list heads
