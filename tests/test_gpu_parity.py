@@ -748,6 +748,19 @@ def test_full_forward_sampled(hsa, dev, name):
     compare_forward(oracle.get(), x, wl, g, row_mask=mask)
 
 
+@pytest.mark.parametrize("D,Hq,Hkv", [(64, 16, 4), (128, 16, 1)], ids=["d64", "d128"])
+def test_select_k16_many_chunks(hsa, dev, D, Hq, Hkv):
+    """K = 16 over up to 260 earlier chunks: the selection filter keeps only K/4 + 2 scores
+    per lane for its threshold, so its bound is loosest here; selection is compared on every
+    row, outputs on sampled rows."""
+    wl = W(f"bf16_k16_d{D}", 1, 64 * 260 + 11, Hq, Hkv, D, 64, 16, torch.bfloat16)
+    say("case select K=16", wl)
+    x = workloads.make_inputs(wl, seed=21, with_grad=False)
+    g = gpu_forward(hsa, x, wl, dev)
+    torch.cuda.synchronize()
+    compare_forward(oracle.get(), x, wl, g, out_mask=_sample_rows(wl, 256, seed=22))
+
+
 def test_long_sequence_token_tile_forward(hsa, dev):
     """Past 16384 chunks the forward uses its token-tile kernels (job lists per token tile,
     rounds of jobs, LDS accumulation): parity on sampled rows of a sequence of 16400 chunks."""
