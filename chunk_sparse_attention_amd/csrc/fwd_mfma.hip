@@ -574,6 +574,7 @@ size_t chunk_ops_bytes(const Dims& d) {
 
 // waves per segment block of the chunk-major forward (they share the chunk in LDS)
 constexpr int kFwdWaves = 8;
+constexpr int kFwdWaves128 = 6;  // d = 128: three blocks of six waves fit a CU's LDS
 
 static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const void* Q,
                                      const void* K, const void* V, const int32_t* idx,
@@ -587,8 +588,8 @@ static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const vo
   const float c2 = (float)(d.sm_scale * 1.4426950408889634);  // logit scale * log2(e)
   if (d.nC > 0) {
     Timed tm(HSA_KERNEL_FWD, s);
-    auto go = [&](auto kern) {
-      kern<<<dim3((unsigned)(BG * st.ix.max_seg)), 64 * kFwdWaves, 0, s>>>(
+    auto go = [&](auto kern, int nw) {
+      kern<<<dim3((unsigned)(BG * st.ix.max_seg)), 64 * nw, 0, s>>>(
           (const bf16*)Q, (const bf16*)K, (const bf16*)V, w,
           (const int32_t*)(ws + st.ix.offsets), (const int32_t*)(ws + st.ix.entries),
           (const int32_t*)(ws + st.ix.seg_start), (const int32_t*)(ws + st.ix.seg_chunk),
@@ -597,13 +598,13 @@ static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const vo
           d.L, d.Hq, d.Hkv, d.K, d.nC, st.ix.seg, st.ix.max_seg, c2);
     };
     if (d.D == 64) {
-      if (d.G == 4) go(k_fwd_chunk<64, 4, kFwdWaves>);
-      else if (d.G == 8) go(k_fwd_chunk<64, 8, kFwdWaves>);
-      else go(k_fwd_chunk<64, 16, kFwdWaves>);
+      if (d.G == 4) go(k_fwd_chunk<64, 4, kFwdWaves>, kFwdWaves);
+      else if (d.G == 8) go(k_fwd_chunk<64, 8, kFwdWaves>, kFwdWaves);
+      else go(k_fwd_chunk<64, 16, kFwdWaves>, kFwdWaves);
     } else {
-      if (d.G == 4) go(k_fwd_chunk<128, 4, kFwdWaves>);
-      else if (d.G == 8) go(k_fwd_chunk<128, 8, kFwdWaves>);
-      else go(k_fwd_chunk<128, 16, kFwdWaves>);
+      if (d.G == 4) go(k_fwd_chunk<128, 4, kFwdWaves128>, kFwdWaves128);
+      else if (d.G == 8) go(k_fwd_chunk<128, 8, kFwdWaves128>, kFwdWaves128);
+      else go(k_fwd_chunk<128, 16, kFwdWaves128>, kFwdWaves128);
     }
   }
   {
