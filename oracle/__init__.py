@@ -132,7 +132,7 @@ class Oracle:
                                       _P]
         lib.oracle_attend.restype = None
         lib.oracle_attend.argtypes = [_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D,
-                                      _P, _P, _P]
+                                      _P, _P, _P, _P]
         lib.oracle_bwd.restype = None
         lib.oracle_bwd.argtypes = [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                    _I, _I, _D, _D, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]
@@ -181,9 +181,11 @@ class Oracle:
 
     # -- F5-F6 ---------------------------------------------------------------------------
     def attend(self, Q, Kmat, V, idx, w, S: int, sm_scale: float | None = None,
-               row_mask=None, per_slot: bool = False):
+               row_mask=None, per_slot: bool = False, want_lse: bool = False):
         """O = sum_k w_k softmax1-attention over the selected chunks.
-        Returns O float64 [B, L, Hq, D] (and per-slot outputs [B, L, Hq, K, D] if asked)."""
+        Returns O float64 [B, L, Hq, D], followed, when asked, by the per-slot outputs
+        [B, L, Hq, K, D] and by lse [B, L, Hq, K] = log(1 + sum_j exp(z_j)) of every
+        (token, head, slot) (0 for masked slots)."""
         q, dt = _as_storage(Q)
         k, dtk = _as_storage(Kmat)
         v, dtv = _as_storage(V)
@@ -197,10 +199,13 @@ class Oracle:
             sm_scale = 1.0 / math.sqrt(D)
         O = np.zeros((B, L, Hq, D), np.float64)
         Ok = np.zeros((B, L, Hq, Kt, D), np.float64) if per_slot else None
+        lse = np.zeros((B, L, Hq, Kt), np.float64) if want_lse else None
         m = _mask(row_mask)
         self.lib.oracle_attend(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(idx_), _ptr(w_), B, L, Hq,
-                               Hkv, D, S, Kt, float(sm_scale), _ptr(m), _ptr(O), _ptr(Ok))
-        return (O, Ok) if per_slot else O
+                               Hkv, D, S, Kt, float(sm_scale), _ptr(m), _ptr(O), _ptr(Ok),
+                               _ptr(lse))
+        out = (O,) + ((Ok,) if per_slot else ()) + ((lse,) if want_lse else ())
+        return out if len(out) > 1 else O
 
     def forward(self, Q, Kmat, V, Qs, S: int, K: int, sm_scale=None, sel_scale=None,
                 score_dt: int = F32, row_mask=None, weights: str = "stick"):

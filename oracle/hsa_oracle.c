@@ -159,7 +159,7 @@ static double sel_score(const void* Qs, int dt, size_t qoff, const double* krow,
   double dot = 0.0;
   for (int e = 0; e < D; ++e) dot += ld(Qs, qoff + e, dt) * krow[e];
   double s = oracle_round(sel_scale * dot, score_dt);
-  if (isnan(s)) s = -INFINITY; /* a NaN score ranks last and carries no weight */
+  if (isnan(s) && !MUT(12)) s = -INFINITY; /* a NaN score ranks last and carries no weight */
   return s;
 }
 
@@ -227,8 +227,9 @@ void oracle_select(const void* Qs, int dt, const double* Kslc, int B, int L, int
  * softmax-off-by-one so that a token can give the chunk little total weight.
  * z_j = sm_scale <q, k_j>;  a_j = exp(z_j) / (1 + sum_i exp(z_i)), evaluated with the
  * shift m = max(0, max_j z_j) so no exponential overflows.
- * a: out [S] probabilities; returns nothing. */
-static void softmax1_probs(const void* Q, int dtq, size_t qoff, const void* K, int dtk,
+ * a: out [S] probabilities; returns the normaliser's log, log(1 + sum_j exp(z_j)) =
+ * m + log(exp(-m) + sum_j exp(z_j - m)). */
+static double softmax1_probs(const void* Q, int dtq, size_t qoff, const void* K, int dtk,
                            size_t k0, size_t kstride, int D, int S, double sm_scale,
                            double* a) {
   double z[1024];
@@ -245,6 +246,7 @@ static void softmax1_probs(const void* Q, int dtq, size_t qoff, const void* K, i
     den += a[j];
   }
   for (int j = 0; j < S; ++j) a[j] /= den;
+  return m + log(den);
 }
 
 /* Query head h -> KV group. */
@@ -257,10 +259,13 @@ static int group_of(int h, int Hq, int Hkv) {
  * [HSA-note 层次化稀疏注意力（HSA）, 第二阶段] and [HSA-note 硬件对齐 Kernel, forward]:
  * O_t = sum_k w_k * O_{t,k}; a token with no valid slot gets O_t = 0.
  * Q: [B, L, Hq, D]; K, V: [B, L, Hkv, D]; idx/w: [B, L, Hkv, Kt].  O out: [B, L, Hq, D].
- * Ok (optional): per-slot unweighted outputs [B, L, Hq, Kt, D] (0 for masked slots). */
+ * Ok (optional): per-slot unweighted outputs [B, L, Hq, Kt, D] (0 for masked slots).
+ * lse (optional): per (token, head, slot) the normaliser's log, log(1 + sum_j exp(z_j)),
+ * [B, L, Hq, Kt] (0 for masked slots). */
 void oracle_attend(const void* Q, const void* K, const void* V, int dt, const int32_t* idx,
                    const double* w, int B, int L, int Hq, int Hkv, int D, int S, int Kt,
-                   double sm_scale, const uint8_t* row_mask, double* O, double* Ok) {
+                   double sm_scale, const uint8_t* row_mask, double* O, double* Ok,
+                   double* lse) {
 #pragma omp parallel for collapse(2) schedule(dynamic, 16)
   for (int b = 0; b < B; ++b)
     for (int t = 0; t < L; ++t) {
@@ -275,12 +280,15 @@ void oracle_attend(const void* Q, const void* K, const void* V, int dt, const in
           size_t so = (((size_t)b * L + t) * Hkv + g) * Kt + k;
           int c = idx[so];
           double* ok = Ok ? Ok + ((((size_t)b * L + t) * Hq + h) * Kt + k) * D : NULL;
+          double* lk = lse ? lse + (((size_t)b * L + t) * Hq + h) * Kt + k : NULL;
           if (ok)
             for (int e = 0; e < D; ++e) ok[e] = 0.0;
+          if (lk) *lk = 0.0;
           if (c < 0) continue;
           size_t k0 = (((size_t)b * L + (size_t)c * S) * Hkv + g) * D;
           size_t kstride = (size_t)Hkv * D;
-          softmax1_probs(Q, dt, qoff, K, dt, k0, kstride, D, S, sm_scale, a);
+          double lz = softmax1_probs(Q, dt, qoff, K, dt, k0, kstride, D, S, sm_scale, a);
+          if (lk) *lk = lz;
           for (int e = 0; e < D; ++e) {
             double acc = 0.0;
             for (int j = 0; j < S; ++j) acc += a[j] * ld(V, k0 + j * kstride + e, dt);

@@ -148,6 +148,68 @@ def pin_select_ties_and_causality(orc):
         assert idx[0, t, 0, 0] == 2 and idx[0, t, 0, 1] == 5, idx[0, t, 0]
 
 
+def pin_select_nonfinite_and_signed_zero(orc):
+    """The ranking rule on values that are not ordinary numbers: a NaN score ranks as -inf
+    (last, ties among such chunks to the lower index, weight 0); +inf and -inf rank as the
+    extremes they are (an +inf slot takes all of the remaining stick); -0 ranks equal to +0,
+    so a row whose scores all round to a signed zero keeps chunk index order.  Checked
+    against a brute-force sort that applies exactly that rule to scores computed with numpy.
+    Inputs are small dyadic integers and the scale a power of two, so every finite score is
+    exact whatever the summation order and the comparison can demand equality."""
+    gen = torch.Generator().manual_seed(31)
+    S, K, D, Hkv = 4, 3, 8, 2
+    L = 12 * S + 2
+    nC = L // S
+    Kmat = torch.randint(-4, 5, (1, L, Hkv, D), generator=gen).to(torch.float32) * 0.25
+    Qs = torch.randint(-3, 4, (1, L, Hkv, D), generator=gen).to(torch.float32)
+    nan, inf = float("nan"), float("inf")
+    Qs[0, 17, 0, :] = nan           # every score NaN: chunks in index order, weight 0
+    Qs[0, 21, 1, 2] = nan           # one NaN component: same
+    Qs[0, 23, 1, 0] = inf           # scores +inf, -inf or NaN (0 * inf) by the key's sign
+    Qs[0, 30, 0, 5] = -inf
+    Kmat[0, 3 * S + 1, 0, 4] = nan  # chunk 3 of group 0: NaN for every token of group 0
+    Kmat[0, 5 * S + 2, 1, 6] = inf  # chunk 5 of group 1: +-inf or NaN scores
+    tiny = 2.0 ** -140              # rows whose every score rounds to a signed zero in fp32
+    Qs[0, 38, 1, :] = torch.tensor([tiny, -tiny, tiny, 0, 0, 0, 0, 0])
+    Qs[0, 41, 0, :] = -tiny
+    sel = 2.0 ** -20
+    ks = orc.pool(Kmat, S)
+    idx, score, w = orc.select(Qs, ks, S, K, sel)
+
+    q = Qs.double().numpy()
+    ref_idx = np.full((1, L, Hkv, K), -1, np.int32)
+    ref_sc = np.full((1, L, Hkv, K), -np.inf)
+    for g in range(Hkv):
+        with np.errstate(invalid="ignore", over="ignore"):
+            s_all = (q[0, :, g, :] @ ks[0, :, g, :].T) * sel
+        s_all = s_all.astype(np.float32).astype(np.float64)
+        s_all[np.isnan(s_all)] = -np.inf   # the rule: NaN ranks as -inf
+        s_all[s_all == 0] = 0.0            # the rule: -0 ranks as +0
+        for t in range(L):
+            n = min(t // S, nC)
+            if n == 0:
+                continue
+            s = s_all[t, :n]
+            order = np.lexsort((np.arange(n), -s))[:K]
+            ref_idx[0, t, g, :len(order)] = order
+            ref_sc[0, t, g, :len(order)] = s[order]
+    assert np.array_equal(idx, ref_idx), np.argwhere(idx != ref_idx)[:5]
+    assert not np.isnan(score).any() and not np.isnan(w).any()
+    assert np.array_equal(score, ref_sc), np.argwhere(score != ref_sc)[:5]
+    # the planted rows do what the rule says
+    assert list(idx[0, 17, 0]) == [0, 1, 2] and np.all(np.isneginf(score[0, 17, 0]))
+    assert np.all(w[0, 17, 0] == 0) and np.all(w[0, 21, 1] == 0)
+    assert list(idx[0, 38, 1]) == [0, 1, 2] and list(idx[0, 41, 0]) == [0, 1, 2]
+    assert np.all(score[0, 38, 1] == 0) and np.all(score[0, 41, 0] == 0)
+    assert 3 not in idx[0, 4 * S:, 0, :2]  # chunk 3 of group 0 never beats a finite score
+    row = score[0, 23, 1]
+    assert np.isposinf(row[0]) and w[0, 23, 1, 0] == 1.0 and np.all(w[0, 23, 1, 1:] == 0)
+    # stick-breaking on the other rows is untouched by the rule
+    valid = np.isfinite(score)
+    p = 1.0 / (1.0 + np.exp(-np.where(valid, score, 0.0)))
+    assert np.allclose(w[..., 0][valid[..., 0]], p[..., 0][valid[..., 0]], rtol=1e-14, atol=0)
+
+
 def pin_stick_breaking_identities(orc):
     """For any scores: w >= 0, w_0 = sigmoid(s_0), and sum_k w_k = 1 - prod_k (1 - sigmoid(s_k))
     (the telescoping identity of stick-breaking), so sum_k w_k <= 1."""
@@ -235,6 +297,36 @@ def pin_softmax1_equals_sdpa(orc):
                 Q[0, t, h].double()[None, None, None], kk[None, None], vv[None, None], scale=scale)
             assert np.allclose(out[0, t, h], ref.reshape(-1).numpy(), rtol=1e-12, atol=1e-13)
     assert np.all(out[0, :S] == 0)
+
+
+def pin_lse_equals_logsumexp(orc):
+    """The normaliser the oracle reports for every (token, head, slot) is torch's logsumexp
+    over the chunk's S scaled logits plus one zero logit; Q = 0 gives log(S + 1) exactly; a
+    masked slot reports 0."""
+    gen = torch.Generator().manual_seed(16)
+    S, D, Hq, Hkv, K = 8, 8, 4, 2, 3
+    L = 6 * S + 3
+    Q = _rand(gen, (1, L, Hq, D), 2.0, torch.float32)
+    Km = _rand(gen, (1, L, Hkv, D), 2.0, torch.float32)
+    V = _rand(gen, (1, L, Hkv, D), 1.0, torch.float32)
+    sel = workloads.make_selection(1, L, Hkv, S, K, seed=17)
+    sm = 0.45
+    _, lse = orc.attend(Q, Km, V, sel["idx"], sel["w"], S, sm_scale=sm, want_lse=True)
+    G = Hq // Hkv
+    idx = np.asarray(sel["idx"])
+    for t in range(L):
+        for h in range(Hq):
+            for k in range(K):
+                c = int(idx[0, t, h // G, k])
+                if c < 0:
+                    assert lse[0, t, h, k] == 0.0
+                    continue
+                z = (Km[0, c * S:(c + 1) * S, h // G].double() @ Q[0, t, h].double()) * sm
+                ref = torch.logsumexp(torch.cat([z, torch.zeros(1, dtype=torch.float64)]), 0)
+                assert abs(lse[0, t, h, k] - float(ref)) <= 1e-13 * max(1.0, abs(float(ref)))
+    _, lse0 = orc.attend(torch.zeros_like(Q), Km, V, sel["idx"], sel["w"], S, want_lse=True)
+    valid = np.repeat(idx >= 0, G, axis=2)
+    assert np.all(lse0[valid] == math.log(S + 1.0)) and np.all(lse0[~valid] == 0.0)
 
 
 def pin_zero_query_closed_form(orc):

@@ -18,6 +18,7 @@ MUTATIONS = {
     9: "query head mapped to group h % Hkv",
     10: "logit scale dropped",
     11: "softmax-weight backward drops the weighted mean of dw",
+    12: "a NaN selection score is not ranked as -inf",
 }
 
 
