@@ -74,9 +74,9 @@ def lib() -> ctypes.CDLL:
     L.hsa_select.restype = I
     L.hsa_select.argtypes = [PP, P, P, P, P, P, P, P, Z, P]
     L.hsa_fwd.restype = I
-    L.hsa_fwd.argtypes = [PP, P, P, P, P, P, P, P, Z, P]
+    L.hsa_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, Z, P]
     L.hsa_bwd.restype = I
-    L.hsa_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, U, P, Z, P]
+    L.hsa_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, U, P, Z, P]
     L.hsa_decode.restype = I
     L.hsa_decode.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, Z, P]
     L.hsa_decode_host_kv.restype = I

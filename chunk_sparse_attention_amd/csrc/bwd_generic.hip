@@ -226,10 +226,13 @@ __global__ void __launch_bounds__(1024) k_inv_order(const int32_t* __restrict__ 
   for (int s = threadIdx.x; s < ns; s += blockDim.x) order[atomicAdd(&hist[bucket(s)], 1)] = s;
 }
 
-// Per (b, g, tile), one wave: walk the tile's tokens in order; lane k places slot k.  A token's
-// chunks are distinct, so the lanes of one step never share a counter.  The tile's selections
-// are first staged in LDS, 256 tokens at a time, so the serial walk waits on LDS only.  A
-// chunk's entries from this tile start at offsets[c] + the tile's prefix for c.
+// Per (b, g, tile), one wave: walk the tile's tokens in order; lane k places slot k.  The
+// tile's selections are first staged in LDS, 256 tokens at a time, so the serial walk waits on
+// LDS only.  A chunk's entries from this tile start at offsets[c] + the tile's prefix for c.
+// A selection from hsa_select never repeats a chunk within a row, but a caller's may: such
+// slots are given consecutive entries in slot order (rank r among the row's equal slots goes
+// to the counter's value + r, and the first of them advances the counter past all), which is
+// the count k_inv_count made for them, so every entry is written exactly once.
 constexpr int kScatterBatch = 256;
 __global__ void __launch_bounds__(64) k_inv_scatter(const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ tile_prefix,
@@ -239,6 +242,7 @@ __global__ void __launch_bounds__(64) k_inv_scatter(const int32_t* __restrict__ 
                                                     int n_tiles) {
   extern __shared__ int32_t cnt[];
   __shared__ int32_t sel[kScatterBatch * kMaxK];
+  __shared__ uint16_t dup[kScatterBatch * kMaxK];  // rank among equal slots | their number << 8
   const int tile = blockIdx.x % n_tiles;
   const int bg = blockIdx.x / n_tiles;
   const int g = bg % Hkv;
@@ -256,12 +260,32 @@ __global__ void __launch_bounds__(64) k_inv_scatter(const int32_t* __restrict__ 
     for (int i = lane; i < nt * K; i += kWave)
       sel[i] = idx[((b * L + tb0 + i / K) * Hkv + g) * K + i % K];
     __syncthreads();
+    for (int tt = lane; tt < nt; tt += kWave) {  // one token per lane: its slots' repeats
+      int cv[kMaxK];
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) cv[j] = j < K ? sel[tt * K + j] : 0;
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k) {
+        if (k < K) {
+          int rank = 0, n = 0;
+#pragma unroll
+          for (int j = 0; j < kMaxK; ++j) {
+            const bool eq = j < K && cv[j] == cv[k];
+            rank += (j < k && eq) ? 1 : 0;
+            n += eq ? 1 : 0;
+          }
+          dup[tt * K + k] = (uint16_t)(rank | (n << 8));
+        }
+      }
+    }
+    __syncthreads();
     for (int tt = 0; tt < nt; ++tt) {
       if (lane < K) {
         const int c = sel[tt * K + lane];
         if (c >= 0 && c < nC) {
-          const int pos = cnt[c];
-          cnt[c] = pos + 1;
+          const int r = dup[tt * K + lane];
+          const int pos = cnt[c] + (r & 0xff);  // every lane reads before any lane writes
+          if ((r & 0xff) == 0) cnt[c] = pos + (r >> 8);
           ent[pos] = (tb0 + tt) * K + lane;
         }
       }

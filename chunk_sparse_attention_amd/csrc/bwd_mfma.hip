@@ -799,16 +799,20 @@ static hipError_t launch_bwd_fused(const Dims& d, const BwdLayout& lay, const vo
 
 hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
                            const void* V, const void* Qs, const void* Kslc, const int32_t* idx,
-                           const float* score, const float* w, const void* dO, void* dQ,
-                           void* dK, void* dV, void* dQs, float* dKslc, bool fold,
-                           bool after_fwd, char* ws, hipStream_t s) {
+                           const float* score, const float* w, const float* lse,
+                           const void* dO, void* dQ, void* dK, void* dV, void* dQs,
+                           float* dKslc, bool fold, bool after_fwd, char* ws, hipStream_t s) {
   // after the chunk-major forward the index of this selection is in place
   if (!(after_fwd && fwd_chunked(d))) {
     hipError_t e = launch_invidx(d, lay, idx, ws, s);
     if (e != hipSuccess) return e;
   }
+  if (lse) {  // the caller's normalisers replace whatever the state holds
+    hipError_t e = launch_lse_import(d, lse, (float*)(ws + lay.lse), s);
+    if (e != hipSuccess) return e;
+  }
   return launch_bwd_fused(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK, dV, dQs, dKslc,
-                          fold, after_fwd, ws, s);
+                          fold, after_fwd || lse != nullptr, ws, s);
 }
 
 }  // namespace hsa

@@ -14,8 +14,9 @@ namespace hsa {
 template <typename T>
 __global__ void __launch_bounds__(64) k_fwd_generic(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const int32_t* __restrict__ idx, const float* __restrict__ w, T* __restrict__ O, int L,
-    int Hq, int Hkv, int D, int S, int Kt, int G, int nC, float sm_scale) {
+    const int32_t* __restrict__ idx, const float* __restrict__ w, T* __restrict__ O,
+    float* __restrict__ lse, int L, int Hq, int Hkv, int D, int S, int Kt, int G, int nC,
+    float sm_scale) {
   __shared__ float qsh[kMaxG][128];
   __shared__ float ash[kMaxG][kChunk];
   const int lane = threadIdx.x;
@@ -34,7 +35,11 @@ __global__ void __launch_bounds__(64) k_fwd_generic(
   const size_t kvstride = (size_t)Hkv * D;
   for (int k = 0; k < Kt; ++k) {
     const int c = idx[row * Kt + k];
-    if (c < 0 || c >= nC) continue;  // masked slot (or out-of-range index): adds nothing
+    if (c < 0 || c >= nC) {  // masked slot (or out-of-range index): adds nothing
+      if (lse)
+        for (int h = lane; h < G; h += kWave) lse[(bt * Hq + (size_t)g * G + h) * Kt + k] = 0.0f;
+      continue;
+    }
     const float wk = w[row * Kt + k];
     const size_t cbase = ((b * L + (size_t)c * S) * Hkv + g) * D;
     // logits of lane j's key for every head of the group
@@ -61,6 +66,7 @@ __global__ void __launch_bounds__(64) k_fwd_generic(
         float ex = __expf(zz - m);
         float den = __expf(-m) + wave_sum(ex);
         ash[h][lane] = wk * ex / den;
+        if (lse && lane == 0) lse[(bt * Hq + (size_t)g * G + h) * Kt + k] = m + logf(den);
       }
     }
     __syncthreads();
@@ -89,18 +95,19 @@ __global__ void __launch_bounds__(64) k_fwd_generic(
 }
 
 hipError_t launch_fwd_generic(const Dims& d, const void* Q, const void* K, const void* V,
-                              const int32_t* idx, const float* w, void* O, hipStream_t s) {
+                              const int32_t* idx, const float* w, void* O, float* lse,
+                              hipStream_t s) {
   size_t rows = (size_t)d.B * d.L * d.Hkv;
   if (rows == 0) return hipSuccess;
   float sm = (float)d.sm_scale;
   Timed tm(HSA_KERNEL_FWD, s);
   if (d.dtype == 1)
     k_fwd_generic<bf16><<<dim3((unsigned)rows), 64, 0, s>>>(
-        (const bf16*)Q, (const bf16*)K, (const bf16*)V, idx, w, (bf16*)O, d.L, d.Hq, d.Hkv, d.D,
+        (const bf16*)Q, (const bf16*)K, (const bf16*)V, idx, w, (bf16*)O, lse, d.L, d.Hq, d.Hkv, d.D,
         d.S, d.K, d.G, d.nC, sm);
   else
     k_fwd_generic<float><<<dim3((unsigned)rows), 64, 0, s>>>(
-        (const float*)Q, (const float*)K, (const float*)V, idx, w, (float*)O, d.L, d.Hq, d.Hkv,
+        (const float*)Q, (const float*)K, (const float*)V, idx, w, (float*)O, lse, d.L, d.Hq, d.Hkv,
         d.D, d.S, d.K, d.G, d.nC, sm);
   return hipGetLastError();
 }

@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "hsa.h"
@@ -135,6 +136,86 @@ hsa_status_t launched(hipError_t e, const char* what) {
     if (st_ != HSA_OK) return st_;      \
   } while (0)
 
+// ---- forward-state records ------------------------------------------------------------
+// The forward leaves, at the start of its workspace, state a backward over the same
+// selection can reuse (the inverse index or token-tile job lists, and the normalisers).  The
+// library records, per (workspace pointer, device), which forward filled it; any other call
+// that writes into a workspace drops that workspace's record.  hsa_bwd reuses the state
+// only when the record names this very problem and these Q, K, idx and w.
+struct FwdRecord {
+  const void* ws;
+  int device;
+  hsa_problem_t p;
+  const void *Q, *K, *idx, *w;
+};
+constexpr int kMaxRecords = 64;
+std::mutex g_rec_mu;
+FwdRecord g_rec[kMaxRecords];
+int g_n_rec = 0, g_next_rec = 0;
+
+int current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    dev = -1;
+  }
+  return dev;
+}
+
+// The fields the forward's state depends on (the selection scale and the weighting rule
+// do not enter it).
+bool same_problem(const hsa_problem_t& a, const hsa_problem_t& b) {
+  return a.B == b.B && a.L == b.L && a.Hq == b.Hq && a.Hkv == b.Hkv && a.D == b.D &&
+         a.S == b.S && a.K == b.K && a.sm_scale == b.sm_scale && a.dtype == b.dtype &&
+         (a.flags & HSA_FLAG_GENERIC) == (b.flags & HSA_FLAG_GENERIC);
+}
+
+int find_record(const void* ws, int dev) {
+  for (int i = 0; i < g_n_rec; ++i)
+    if (g_rec[i].ws == ws && g_rec[i].device == dev) return i;
+  return -1;
+}
+
+void forget_state(const void* ws) {
+  if (!ws) return;
+  const int dev = current_device();
+  std::lock_guard<std::mutex> lk(g_rec_mu);
+  const int i = find_record(ws, dev);
+  if (i >= 0) g_rec[i].ws = nullptr;
+}
+
+void record_state(const void* ws, const hsa_problem_t* p, const void* Q, const void* K,
+                  const void* idx, const void* w) {
+  if (!ws) return;
+  const int dev = current_device();
+  std::lock_guard<std::mutex> lk(g_rec_mu);
+  int i = find_record(ws, dev);
+  if (i < 0) {
+    for (int j = 0; j < g_n_rec && i < 0; ++j)
+      if (!g_rec[j].ws) i = j;  // a dropped record's place
+  }
+  if (i < 0) {
+    if (g_n_rec < kMaxRecords) {
+      i = g_n_rec++;
+    } else {
+      i = g_next_rec;
+      g_next_rec = (g_next_rec + 1) % kMaxRecords;
+    }
+  }
+  g_rec[i] = FwdRecord{ws, dev, *p, Q, K, idx, w};
+}
+
+bool state_matches(const void* ws, const hsa_problem_t* p, const void* Q, const void* K,
+                   const void* idx, const void* w) {
+  if (!ws) return false;
+  const int dev = current_device();
+  std::lock_guard<std::mutex> lk(g_rec_mu);
+  const int i = find_record(ws, dev);
+  if (i < 0) return false;
+  const FwdRecord& r = g_rec[i];
+  return same_problem(r.p, *p) && r.Q == Q && r.K == K && r.idx == idx && r.w == w;
+}
+
 }  // namespace
 
 HSA_EXPORT const char* hsa_status_string(hsa_status_t s) {
@@ -180,6 +261,7 @@ HSA_EXPORT hsa_status_t hsa_select(const hsa_problem_t* p, const void* Qs, const
   }
   TRY(check_ws(HSA_OP_SELECT, d, ws, ws_bytes));
   TRY(check_pending());
+  forget_state(ws);
   hipStream_t s = (hipStream_t)stream;
   if (d.nC > 0) {
     hipError_t e = hsa::launch_pool(d, K, Kslc, s);
@@ -199,7 +281,7 @@ HSA_EXPORT hsa_status_t hsa_select(const hsa_problem_t* p, const void* Qs, const
 
 HSA_EXPORT hsa_status_t hsa_fwd(const hsa_problem_t* p, const void* Q, const void* K,
                                 const void* V, const int32_t* idx, const float* w, void* O,
-                                void* ws, size_t ws_bytes, hsa_stream_t stream) {
+                                float* lse, void* ws, size_t ws_bytes, hsa_stream_t stream) {
   hsa::Dims d;
   TRY(check_problem(HSA_OP_FWD, p, &d));
   TRY(need_tensor(Q, "Q"));
@@ -208,20 +290,27 @@ HSA_EXPORT hsa_status_t hsa_fwd(const hsa_problem_t* p, const void* Q, const voi
   TRY(need_small(idx, "idx"));
   TRY(need_small(w, "w"));
   TRY(need_tensor(O, "O"));
+  if (lse && !aligned(lse, 4)) return fail(HSA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   TRY(check_ws(HSA_OP_FWD, d, ws, ws_bytes));
   TRY(check_pending());
   hipStream_t s = (hipStream_t)stream;
-  if (hsa::fwd_mfma_supported(d))
-    return launched(hsa::launch_fwd_mfma(d, Q, K, V, idx, w, O, (char*)ws, s), "fwd");
-  return launched(hsa::launch_fwd_generic(d, Q, K, V, idx, w, O, s), "fwd");
+  forget_state(ws);
+  if (!hsa::fwd_mfma_supported(d))
+    return launched(hsa::launch_fwd_generic(d, Q, K, V, idx, w, O, lse, s), "fwd");
+  hipError_t e = hsa::launch_fwd_mfma(d, Q, K, V, idx, w, O, (char*)ws, s);
+  if (e == hipSuccess && lse)
+    e = hsa::launch_lse_export(d, (const float*)((const char*)ws + hsa::fwd_state(d).lse), idx,
+                               lse, s);
+  if (e == hipSuccess) record_state(ws, p, Q, K, idx, w);
+  return launched(e, "fwd");
 }
 
 HSA_EXPORT hsa_status_t hsa_bwd(const hsa_problem_t* p, const void* Q, const void* K,
                                 const void* V, const void* Qs, const void* Kslc,
                                 const int32_t* idx, const float* score, const float* w,
-                                const void* dO, void* dQ, void* dK, void* dV, void* dQs,
-                                float* dKslc, uint32_t flags, void* ws, size_t ws_bytes,
-                                hsa_stream_t stream) {
+                                const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                                void* dQs, float* dKslc, uint32_t flags, void* ws,
+                                size_t ws_bytes, hsa_stream_t stream) {
   hsa::Dims d;
   TRY(check_problem(HSA_OP_BWD, p, &d));
   TRY(need_tensor(Q, "Q"));
@@ -232,6 +321,7 @@ HSA_EXPORT hsa_status_t hsa_bwd(const hsa_problem_t* p, const void* Q, const voi
   TRY(need_small(idx, "idx"));
   TRY(need_small(score, "score"));
   TRY(need_small(w, "w"));
+  if (lse && !aligned(lse, 4)) return fail(HSA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   TRY(need_tensor(dO, "dO"));
   TRY(need_tensor(dQ, "dQ"));
   TRY(need_tensor(dK, "dK"));
@@ -244,16 +334,21 @@ HSA_EXPORT hsa_status_t hsa_bwd(const hsa_problem_t* p, const void* Q, const voi
   TRY(check_pending());
   hipStream_t s = (hipStream_t)stream;
   hsa::BwdLayout lay = hsa::bwd_layout(d);
-  if (hsa::bwd_mfma_supported(d))
-    return launched(hsa::launch_bwd_mfma(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK,
-                                         dV, dQs, dKslc, (flags & HSA_BWD_FOLD_KSLC) != 0,
-                                         (flags & HSA_BWD_AFTER_FWD) != 0 &&
-                                             hsa::fwd_mfma_supported(d),
-                                         (char*)ws, s),
+  const bool fold = (flags & HSA_BWD_FOLD_KSLC) != 0;
+  if (!hsa::bwd_mfma_supported(d)) {
+    forget_state(ws);
+    return launched(hsa::launch_bwd_generic(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ,
+                                            dK, dV, dQs, dKslc, fold, (char*)ws, s),
                     "bwd");
-  return launched(hsa::launch_bwd_generic(d, lay, Q, K, V, Qs, Kslc, idx, score, w, dO, dQ, dK,
-                                          dV, dQs, dKslc, (flags & HSA_BWD_FOLD_KSLC) != 0,
-                                          (char*)ws, s),
+  }
+  // the forward's state is reused only when the record of this workspace confirms it
+  const bool reuse = (flags & HSA_BWD_AFTER_FWD) && hsa::fwd_mfma_supported(d) &&
+                     state_matches(ws, p, Q, K, idx, w);
+  // a backward that rebuilds the index or copies the caller's normalisers into the state
+  // leaves a state that no forward made
+  if (!reuse || lse) forget_state(ws);
+  return launched(hsa::launch_bwd_mfma(d, lay, Q, K, V, Qs, Kslc, idx, score, w, lse, dO, dQ,
+                                       dK, dV, dQs, dKslc, fold, reuse, (char*)ws, s),
                   "bwd");
 }
 
@@ -295,6 +390,7 @@ hsa_status_t decode_impl(const hsa_problem_t* p, const void* q, const void* qs,
   if (score && !aligned(score, 4)) return fail(HSA_ERR_INVALID_ARG, "score is not 4-byte aligned");
   TRY(check_ws(HSA_OP_DECODE, d, ws, ws_bytes));
   TRY(check_pending());
+  forget_state(ws);
   hipStream_t s = (hipStream_t)stream;
   if (!(d.flags & HSA_FLAG_GENERIC))
     return launched(hsa::launch_decode_fast(d, q, qs, Kcache, Vcache, Kslc, O, idx, score, w,
@@ -374,6 +470,7 @@ HSA_EXPORT hsa_status_t hsa_fwd_layers(const hsa_problem_t* p, int n_layers, con
   TRY(need_tensor(O, "O"));
   TRY(check_ws(HSA_OP_FWD, d, ws, ws_bytes));
   TRY(check_pending());
+  forget_state(ws);
   hipStream_t s = (hipStream_t)stream;
   const size_t el = d.dtype == HSA_BF16 ? 2 : 4;
   const size_t q_ls = (size_t)d.B * d.L * d.Hq * d.D * el;
@@ -387,8 +484,9 @@ HSA_EXPORT hsa_status_t hsa_fwd_layers(const hsa_problem_t* p, int n_layers, con
     // the layers share the selection: its index is built for the first layer only
     const hipError_t e =
         mfma ? hsa::launch_fwd_mfma(d, Ql, Kl, Vl, idx, w, Ol, (char*)ws, s, l > 0)
-             : hsa::launch_fwd_generic(d, Ql, Kl, Vl, idx, w, Ol, s);
+             : hsa::launch_fwd_generic(d, Ql, Kl, Vl, idx, w, Ol, nullptr, s);
     if (e != hipSuccess) return launched(e, "fwd_layers");
+    if (mfma && l == n_layers - 1) record_state(ws, p, Ql, Kl, idx, w);
   }
   return ok();
 }

@@ -93,8 +93,15 @@ hipError_t launch_pool_chunks(const Dims& d, const void* K, void* Kslc, const in
 // Generic vector-ALU kernels (fp32 and bf16).
 hipError_t launch_select_generic(const Dims& d, const void* Qs, const void* Kslc, int32_t* idx,
                                  float* score, float* w, hipStream_t s);
+// lse (optional, [B, L, Hq, K], natural log, 0 for masked slots): the normalisers.
 hipError_t launch_fwd_generic(const Dims& d, const void* Q, const void* K, const void* V,
-                              const int32_t* idx, const float* w, void* O, hipStream_t s);
+                              const int32_t* idx, const float* w, void* O, float* lse,
+                              hipStream_t s);
+// The forward state's normalisers (log2 domain, [B, L, Hkv, K, G]) to the ABI's lse
+// ([B, L, Hq, K], natural log, 0 for masked slots) and back.
+hipError_t launch_lse_export(const Dims& d, const float* state, const int32_t* idx, float* lse,
+                             hipStream_t s);
+hipError_t launch_lse_import(const Dims& d, const float* lse, float* state, hipStream_t s);
 hipError_t launch_invidx(const Dims& d, const IndexLayout& lay, const int32_t* idx, char* ws,
                          hipStream_t s);
 hipError_t launch_bwd_generic(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
@@ -130,12 +137,14 @@ void launch_tile_prep(const Dims& d, const int32_t* idx, void* prep, hipStream_t
 // On the matrix cores the chunk phase also yields per-edge dQ partials, which a token phase
 // sums.
 bool bwd_mfma_supported(const Dims& d);
-// after_fwd: ws still holds the forward's state for this problem, idx and K (see FwdState).
+// after_fwd: ws still holds the forward's state for this problem, Q, K, idx and w (see
+// FwdState): its index and normalisers are reused.  lse (optional, the ABI layout): the
+// normalisers to use, copied into the state first.
 hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, const void* K,
                            const void* V, const void* Qs, const void* Kslc, const int32_t* idx,
-                           const float* score, const float* w, const void* dO, void* dQ,
-                           void* dK, void* dV, void* dQs, float* dKslc, bool fold,
-                           bool after_fwd, char* ws, hipStream_t s);
+                           const float* score, const float* w, const float* lse,
+                           const void* dO, void* dQ, void* dK, void* dV, void* dQs,
+                           float* dKslc, bool fold, bool after_fwd, char* ws, hipStream_t s);
 bool fwd_mfma_supported(const Dims& d);
 // bf16 up to 16384 chunks: the forward runs chunk-major (inverse index, per-edge partials,
 // token sums); beyond, on token tiles.

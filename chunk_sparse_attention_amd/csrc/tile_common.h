@@ -188,7 +188,11 @@ __device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, const i
   // (its earlier pieces); a piece adds its round there before it publishes the round.
   {
     constexpr int kJpt = 4;  // jobs per lane: n_jobs <= TT*16 <= 4*NT
+    // colour and tmask are written by other waves while this loop spins: both are read
+    // through volatile pointers, so every read is a fresh LDS load issued in program order
+    // (a piece's tmask reads come after the colour reads that found it ready)
     const volatile int* vcol = colour;
+    const volatile unsigned long long* vmask = tmask;
     int nts[kJpt], prevs[kJpt][4], tks[kJpt][4];
 #pragma unroll
     for (int s = 0; s < kJpt; ++s) {  // every head's tokens and latest earlier pieces
@@ -256,7 +260,7 @@ __device__ void build_rounds(const uint32_t* keys, const uint32_t* jobs, const i
           uint64_t u = 0;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (i < nt) u |= tmask[tk[i]];
+            if (i < nt) u |= vmask[tk[i]];
           const int r = __builtin_ctzll(~u);
 #pragma unroll
           for (int i = 0; i < 4; ++i)

@@ -114,8 +114,10 @@ def select(Qs: torch.Tensor, K: torch.Tensor, K_top: int, sel_scale=None, generi
     return Kslc, idx, score, w
 
 
-def fwd(Q, K, V, idx, w, sm_scale=None, generic=False, ws=None, out=None):
-    """O = sum_k w_k softmax1-attention of Q over the selected chunks of K/V."""
+def fwd(Q, K, V, idx, w, sm_scale=None, generic=False, ws=None, out=None, want_lse=False):
+    """O = sum_k w_k softmax1-attention of Q over the selected chunks of K/V.
+    want_lse=True returns (O, lse) with lse [B, L, Hq, K] fp32: every (token, head, slot)'s
+    softmax-off-by-one normaliser log(1 + sum_j exp(z_j)), 0 for masked slots."""
     _need(Q, "Q")
     B, L, Hq, D = Q.shape
     Hkv = K.shape[2]
@@ -126,22 +128,26 @@ def fwd(Q, K, V, idx, w, sm_scale=None, generic=False, ws=None, out=None):
     _need(w, "w", torch.float32, (B, L, Hkv, Kt), Q.device)
     prob = problem(B, L, Hq, Hkv, D, Kt, Q.dtype, sm_scale=sm_scale, generic=generic)
     O = torch.empty_like(Q) if out is None else _need(out, "out", Q.dtype, Q.shape, Q.device)
+    lse = (torch.empty((B, L, Hq, Kt), dtype=torch.float32, device=Q.device)
+           if want_lse else None)
     if ws is None:
         ws = workspace(_lib.HSA_OP_FWD, prob, Q.device)
     wp, wn = _ws_args(ws)
     check(_lib.lib().hsa_fwd(ctypes.byref(prob), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(w),
-                             _ptr(O), wp, wn, _stream()), "hsa_fwd")
-    return O
+                             _ptr(O), _ptr(lse), wp, wn, _stream()), "hsa_fwd")
+    return (O, lse) if want_lse else O
 
 
 def bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, fold=True, want_dkslc=True, sm_scale=None,
-        sel_scale=None, generic=False, ws=None, after_fwd=False, weights="stick"):
+        sel_scale=None, generic=False, ws=None, after_fwd=False, weights="stick", lse=None):
     """Gradients with the selection fixed.  Returns dict(dQ, dK, dV, dQs, dKslc).
     weights: the chunk-weight rule select() used ("stick" or "softmax").
+    lse: the normalisers fwd(want_lse=True) returned for the same Q, K and idx (optional).
 
     after_fwd=True: `ws` is the workspace that fwd() just used for the same Q, K, idx and w
     (allocate it with workspace(HSA_OP_BWD, ...), which also fits the forward); the backward
-    then reuses the state the forward left in it (HSA_BWD_AFTER_FWD)."""
+    then reuses the state the forward left in it (HSA_BWD_AFTER_FWD) when the library's
+    record of that workspace confirms it, and rebuilds it otherwise."""
     _need(Q, "Q")
     B, L, Hq, D = Q.shape
     Hkv = K.shape[2]
@@ -153,6 +159,8 @@ def bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, fold=True, want_dkslc=True, sm_sca
     _need(idx, "idx", torch.int32, (B, L, Hkv, Kt), dev)
     _need(score, "score", torch.float32, (B, L, Hkv, Kt), dev)
     _need(w, "w", torch.float32, (B, L, Hkv, Kt), dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, L, Hq, Kt), dev)
     prob = problem(B, L, Hq, Hkv, D, Kt, Q.dtype, sm_scale=sm_scale, sel_scale=sel_scale,
                    generic=generic, weights=weights)
     dQ = torch.empty_like(Q)
@@ -168,8 +176,9 @@ def bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, fold=True, want_dkslc=True, sm_sca
     wp, wn = _ws_args(ws)
     flags = (_lib.HSA_BWD_FOLD_KSLC if fold else 0) | (_lib.HSA_BWD_AFTER_FWD if after_fwd else 0)
     check(_lib.lib().hsa_bwd(ctypes.byref(prob), _ptr(Q), _ptr(K), _ptr(V), _ptr(Qs), _ptr(Kslc),
-                             _ptr(idx), _ptr(score), _ptr(w), _ptr(dO), _ptr(dQ), _ptr(dK),
-                             _ptr(dV), _ptr(dQs), _ptr(dKslc), flags, wp, wn, _stream()),
+                             _ptr(idx), _ptr(score), _ptr(w), _ptr(lse), _ptr(dO), _ptr(dQ),
+                             _ptr(dK), _ptr(dV), _ptr(dQs), _ptr(dKslc), flags, wp, wn,
+                             _stream()),
           "hsa_bwd")
     return dict(dQ=dQ, dK=dK, dV=dV, dQs=dQs, dKslc=dKslc)
 

@@ -82,8 +82,8 @@ typedef enum { HSA_OP_SELECT = 0, HSA_OP_FWD = 1, HSA_OP_BWD = 2, HSA_OP_DECODE 
 
 /* hsa_bwd flags */
 #define HSA_BWD_FOLD_KSLC 0x1u /* add dKslc/S into every key row of the chunk (Kslc = mean K) */
-#define HSA_BWD_AFTER_FWD 0x2u /* ws holds what hsa_fwd left in it for this problem, Q, K, idx
-                                  and w: reuse it (see hsa_bwd) */
+#define HSA_BWD_AFTER_FWD 0x2u /* reuse what hsa_fwd left in ws for this problem, Q, K, idx
+                                  and w, when the library can confirm it (see hsa_bwd) */
 
 typedef struct hsa_problem {
   int32_t B;        /* batch (decode: number of sequences) */
@@ -133,37 +133,49 @@ hsa_status_t hsa_select(const hsa_problem_t* p, const void* Qs, const void* K, v
  * chunk weights (note sections 层次化稀疏注意力（HSA） 第一阶段/第二阶段 and 硬件对齐 Kernel).
  *   Q   [B, L, Hq, D] dtype;  K, V [B, L, Hkv, D] dtype
  *   idx [B, L, Hkv, K] int32 and w [B, L, Hkv, K] fp32 as written by hsa_select (any valid
- *       selection works: valid slots first, each chunk < min(floor(t/S), nC), -1 after)
- *   O   [B, L, Hq, D] dtype out */
+ *       selection works: valid slots first, each chunk < min(floor(t/S), nC), -1 after, the
+ *       chunks of one row distinct).  A slot whose chunk is negative or not below nC adds
+ *       nothing.  A row that repeats a chunk is outside that contract; up to 16384 chunks
+ *       each repeated slot still adds its own term (as hsa_bwd differentiates it), beyond
+ *       (the token-tile kernels) only one of a row's equal slots adds its term.
+ *   O   [B, L, Hq, D] dtype out
+ *   lse [B, L, Hq, K] fp32 out, optional (NULL: not written): the softmax-off-by-one
+ *       normaliser of every (token, head, slot), lse = log(1 + sum_j exp(z_j)) in the natural
+ *       log, with z_j the slot's S logits; 0 for a masked slot.  hsa_bwd can take it back.
+ * The forward also leaves state in ws that a backward over the same problem, Q, K, idx and
+ * w can reuse (HSA_BWD_AFTER_FWD). */
 hsa_status_t hsa_fwd(const hsa_problem_t* p, const void* Q, const void* K, const void* V,
-                     const int32_t* idx, const float* w, void* O, void* ws, size_t ws_bytes,
-                     hsa_stream_t stream);
+                     const int32_t* idx, const float* w, void* O, float* lse, void* ws,
+                     size_t ws_bytes, hsa_stream_t stream);
 
 /* Backward of hsa_select's scores/weights and hsa_fwd with the selection held fixed
  * (note section 硬件对齐 Kernel: two phases; section 层次化稀疏注意力（HSA）: end-to-end
  * gradients through the chunk weights).  Inputs as in hsa_select / hsa_fwd plus
  *   Kslc [B, nC, Hkv, D] dtype (the chunk keys the scores were computed from)
+ *   lse  [B, L, Hq, K] fp32, optional: the normalisers hsa_fwd wrote for this problem, Q, K
+ *        and idx; NULL => recomputed (from the workspace state under HSA_BWD_AFTER_FWD, see
+ *        below, else from Q and K).  The plain vector-ALU kernels (fp32, HSA_FLAG_GENERIC, or
+ *        shapes outside the matrix-core kernels) always recompute it.
  *   dO   [B, L, Hq, D] dtype  upstream gradient of O
  * Outputs (all fully written):
  *   dQ [B, L, Hq, D], dK, dV, dQs [B, L, Hkv, D] dtype
  *   dKslc [B, nC, Hkv, D] fp32, gradient with respect to Kslc (may be NULL)
  * flags: HSA_BWD_FOLD_KSLC adds dKslc[c]/S to dK of every row of chunk c, which is the
  * complete key gradient when Kslc was pooled from K.
- * HSA_BWD_AFTER_FWD: the caller ran hsa_fwd with the same problem, Q, K, idx and w on this
- * same workspace (sized for hsa_bwd, which is at least the forward's size) and has not
- * touched it since.  The forward leaves at the start of its workspace every (token, head,
- * slot)'s softmax normaliser and either the chunk -> (token, slot) inverse index (up to 16384
- * chunks) or the token tiles' job lists and the key rows in matrix-core operand order; the
- * backward then skips rebuilding those it uses and takes its probabilities from the
- * normaliser.  The results equal those without the flag up to fp32 rounding.  When the
- * problem uses the plain kernels (fp32, HSA_FLAG_GENERIC, or shapes outside the matrix-core
- * kernels) the flag has no effect.  Passing it without that forward call gives undefined
- * results. */
+ * HSA_BWD_AFTER_FWD asks to reuse the state the last hsa_fwd (or hsa_fwd_layers, for its last
+ * layer) left in this same workspace (sized for hsa_bwd, which is at least the forward's
+ * size): the chunk -> (token, slot) inverse index, or the token tiles' job lists, and every
+ * softmax normaliser.  The library keeps, per workspace pointer and device, a record of the
+ * forward that last filled it (problem, Q, K, idx, w); the state is reused only when that
+ * record matches this call and no other entry point has used the workspace since (hsa_bwd
+ * calls that reused it leave it intact).  Otherwise the backward rebuilds what it needs, so
+ * the flag never changes the result beyond fp32 rounding.  The record cannot see the
+ * contents: the caller must not change Q, K, idx, w or the workspace bytes in between. */
 hsa_status_t hsa_bwd(const hsa_problem_t* p, const void* Q, const void* K, const void* V,
                      const void* Qs, const void* Kslc, const int32_t* idx, const float* score,
-                     const float* w, const void* dO, void* dQ, void* dK, void* dV, void* dQs,
-                     float* dKslc, uint32_t flags, void* ws, size_t ws_bytes,
-                     hsa_stream_t stream);
+                     const float* w, const float* lse, const void* dO, void* dQ, void* dK,
+                     void* dV, void* dQs, float* dKslc, uint32_t flags, void* ws,
+                     size_t ws_bytes, hsa_stream_t stream);
 
 /* One decode step for B sequences with L = ctx tokens already cached (note section
  * 训练与推理优化: only the chunk-key table is scanned; only the selected chunks' K/V are read).

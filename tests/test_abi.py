@@ -83,13 +83,18 @@ def test_entry_points_reject_before_launch():
     assert st == 1
     st = lib.hsa_select(ctypes.byref(p), fake, None, fake, fake, fake, fake, None, 0, None)
     assert st == 1 and b"K is NULL" in lib.hsa_last_error()
-    st = lib.hsa_fwd(ctypes.byref(p), odd, fake, fake, fake, fake, fake, None, 0, None)
+    st = lib.hsa_fwd(ctypes.byref(p), odd, fake, fake, fake, fake, fake, None, None, 0, None)
     assert st == 1 and b"aligned" in lib.hsa_last_error()
-    st = lib.hsa_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
-                     fake, fake, fake, None, 1, None, 0, None)
+    st = lib.hsa_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, odd, None, 0, None)
+    assert st == 1 and b"lse is not 4-byte aligned" in lib.hsa_last_error()
+    st = lib.hsa_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, None, fake,
+                     fake, fake, fake, fake, None, 1, None, 0, None)
     assert st == 3, lib.hsa_last_error()
+    st = lib.hsa_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, odd, fake,
+                     fake, fake, fake, fake, None, 1, fake, 1 << 40, None)
+    assert st == 1 and b"lse is not 4-byte aligned" in lib.hsa_last_error()
     st = lib.hsa_bwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
-                     fake, fake, fake, None, 0x80, fake, 1 << 40, None)
+                     fake, fake, fake, fake, None, 0x80, fake, 1 << 40, None)
     assert st == 1 and b"flags" in lib.hsa_last_error()
     st = lib.hsa_decode(ctypes.byref(_prob(D=80)), fake, fake, fake, fake, fake, fake, fake, None,
                         fake, fake, 1 << 30, None)

@@ -15,15 +15,11 @@ import torch
 
 import oracle
 import workloads
-from hsa_compare import check_selection, max_abs, near_tie_rows, tol_for
+from hsa_compare import compare_backward, compare_forward, head_mask, max_abs, npy, say, tol_for
 
 pytestmark = pytest.mark.gpu
 
 W = workloads.Workload
-
-
-def say(*a):
-    print(*a, flush=True)
 
 
 @pytest.fixture(scope="module")
@@ -38,88 +34,11 @@ def hsa():
     return m
 
 
-def npy(t):
-    t = t.detach()
-    if t.dtype == torch.bfloat16:
-        t = t.float()
-    return t.cpu().numpy().astype(np.float64) if t.is_floating_point() else t.cpu().numpy()
-
-
-def head_mask(row_mask_bLg, G):
-    """[B, L, Hkv] -> [B, L, Hkv*G] (query head h belongs to group h // G)."""
-    return np.repeat(row_mask_bLg, G, axis=2)
-
-
 def gpu_forward(hsa, x, wl, dev, generic=False, weights="stick"):
     Q, K, V, Qs = (x[k].to(dev) for k in ("Q", "K", "V", "Qs"))
     Kslc, idx, score, w = hsa.select(Qs, K, wl.K, generic=generic, weights=weights)
     O = hsa.fwd(Q, K, V, idx, w, generic=generic)
     return dict(Q=Q, K=K, V=V, Qs=Qs, Kslc=Kslc, idx=idx, score=score, w=w, O=O)
-
-
-def compare_forward(orc, x, wl, g, row_mask=None, out_mask=None, weights="stick"):
-    """Selection on the rows of row_mask (default: all), outputs on those of out_mask
-    (default: row_mask)."""
-    if out_mask is None:
-        f = orc.forward(x["Q"], x["K"], x["V"], x["Qs"], wl.S, wl.K, row_mask=row_mask,
-                        weights=weights)
-    else:
-        Kslc = orc.pool(x["K"], wl.S)
-        idx, score, w = orc.select(x["Qs"], Kslc, wl.S, wl.K, row_mask=row_mask,
-                                   weights=weights)
-        O = orc.attend(x["Q"], x["K"], x["V"], idx, w, wl.S, row_mask=out_mask)
-        f = dict(Kslc=Kslc, idx=idx, score=score, w=w, O=O)
-    near = near_tie_rows(orc, x["Qs"], f["Kslc"], wl.S, wl.K, row_mask=row_mask)
-    assert np.array_equal(npy(g["Kslc"]), f["Kslc"]), "pooled chunk keys differ"
-    gpu = dict(idx=npy(g["idx"]), score=npy(g["score"]), w=npy(g["w"]))
-    diff, rep = check_selection(gpu, f, near, x["Qs"], f["Kslc"], wl.S, 1.0 / np.sqrt(wl.D),
-                                row_mask)
-    om = row_mask if out_mask is None else out_mask
-    rows = np.ones(diff.shape, bool) if om is None else np.broadcast_to(
-        np.asarray(om, bool).reshape(wl.B, wl.L, 1), diff.shape)
-    keep = head_mask(rows & ~diff, wl.G)
-    err = max_abs(npy(g["O"]), f["O"], keep)
-    rep["O_max_abs"] = err
-    say("forward", wl.name, rep)
-    assert err <= tol_for(wl.dtype), err
-    return f, diff, rep
-
-
-def compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=None, chunk_mask=None,
-                     weights="stick"):
-    o = orc.backward(x["Q"], x["K"], x["V"], x["Qs"], f["Kslc"], f["idx"], f["score"], f["w"],
-                     x["dO"], wl.S, tok_mask=tok_mask, chunk_mask=chunk_mask, weights=weights)
-    tol = tol_for(wl.dtype)
-    B, L, nC = wl.B, wl.L, wl.nC
-    tm = np.ones((B, L), bool) if tok_mask is None else np.asarray(tok_mask, bool).reshape(B, L)
-    cm = np.ones((B, nC), bool) if chunk_mask is None else np.asarray(chunk_mask, bool).reshape(B, nC)
-    # chunks whose selector sets differ between the two sides are not comparable
-    touched = np.zeros((B, nC), bool)
-    gidx = npy(g["idx"])
-    for (b, t, gg) in np.argwhere(diff):
-        for arr in (gidx[b, t, gg], f["idx"][b, t, gg]):
-            for c in arr:
-                if c >= 0:
-                    touched[b, c] = True
-    trow = tm[:, :, None] & ~diff  # [B, L, Hkv]
-    rep = {}
-    rep["dQ"] = max_abs(npy(grads["dQ"]), o["dQ"], head_mask(trow, wl.G))
-    rep["dQs"] = max_abs(npy(grads["dQs"]), o["dQs"], trow)
-    crow = np.repeat(cm & ~touched, wl.S, axis=1)  # [B, nC*S]
-    crow = np.concatenate([crow, np.zeros((B, L - nC * wl.S), bool)], axis=1)[:, :, None]
-    crow = np.broadcast_to(crow, (B, L, wl.Hkv))
-    rep["dK"] = max_abs(npy(grads["dK"]), o["dK"], crow)
-    rep["dV"] = max_abs(npy(grads["dV"]), o["dV"], crow)
-    ck = np.broadcast_to((cm & ~touched)[:, :, None], (B, nC, wl.Hkv))
-    rep["dKslc"] = max_abs(npy(grads["dKslc"]), o["dKslc"], ck)
-    if chunk_mask is None:  # the incomplete tail chunk's rows must be exactly zero
-        assert np.all(npy(grads["dK"])[:, nC * wl.S:] == 0)
-        assert np.all(npy(grads["dV"])[:, nC * wl.S:] == 0)
-    rep["touched_chunks"] = int(touched.sum())
-    say("backward", wl.name, rep)
-    for k in ("dQ", "dQs", "dK", "dV", "dKslc"):
-        assert rep[k] <= tol, (k, rep[k])
-    return rep
 
 
 SMALL = [
@@ -304,15 +223,18 @@ def test_fold_flag(hsa, dev):
     assert torch.equal(a["dV"], b["dV"]) and torch.equal(a["dQ"], b["dQ"])
 
 
-@pytest.mark.parametrize("case", ["qs_zero", "qs_half_zero", "equal_chunks", "qs_large"])
+@pytest.mark.parametrize("case", ["qs_zero", "qs_half_zero", "equal_chunks", "qs_large",
+                                  "qs_nan", "qs_inf", "k_nan", "signed_zero"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_select_degenerate(hsa, dev, case, d):
-    """Exact ties and extreme magnitudes: the ranking must still equal the oracle's bit for
-    bit (ties go to the lower chunk index), whatever path the kernel takes."""
+    """Exact ties, extreme magnitudes and values that are not ordinary numbers: the ranking
+    must still equal the oracle's bit for bit (ties go to the lower chunk index, a NaN score
+    ranks as -inf, -0 as +0), whatever path the kernel takes."""
     wl = W("sel_" + case, 1, 64 * 70 + 7, 8, 2, d, 64, 8, torch.bfloat16)
     say("case select", case, d)
     x = workloads.make_inputs(wl, seed=5, with_grad=False)
     Qs, K = x["Qs"].clone(), x["K"].clone()
+    nan, inf = float("nan"), float("inf")
     if case == "qs_zero":
         Qs.zero_()
     elif case == "qs_half_zero":
@@ -322,16 +244,38 @@ def test_select_degenerate(hsa, dev, case, d):
         K[:, :nC * 64] = K[:, :64].repeat(1, nC, 1, 1)
     elif case == "qs_large":
         Qs = (Qs.float() * 2.0 ** 100).to(torch.bfloat16)
-    Kslc, idx, score, w = hsa.select(Qs.to(dev), K.to(dev), wl.K)
+    elif case == "qs_nan":  # whole rows and single components
+        Qs[0, 300:4000:37, 0, :] = nan
+        Qs[0, 150:4400:23, 1, 5] = nan
+    elif case == "qs_inf":  # scores +-inf, or NaN where a key component is 0
+        Qs[0, 200:4400:29, 0, 3] = inf
+        Qs[0, 180:4400:31, 1, 7] = -inf
+        K[0, 64 * 11:64 * 12, 0, 3] = 0  # chunk 11's key is 0 there: inf * 0
+    elif case == "k_nan":  # chunk keys with NaN or inf components
+        K[0, 64 * 5 + 7, 0, 10] = nan
+        K[0, 64 * 9 + 1, 1, 3] = inf
+        K[0, 64 * 30 + 2, 0, 1] = -inf
+    elif case == "signed_zero":  # rows whose every score rounds to +0 or -0 in fp32
+        Qs[0, 500:4000:13, :, :] = 0
+        Qs[0, 500:4000:13, :, 0] = 2.0 ** -133
+    sel = 2.0 ** -20 if case == "signed_zero" else None
+    Kslc, idx, score, w = hsa.select(Qs.to(dev), K.to(dev), wl.K, sel_scale=sel)
     torch.cuda.synchronize()
     orc = oracle.get()
     ks = orc.pool(K, 64)
-    assert np.array_equal(npy(Kslc), ks)
-    oi, osc, ow = orc.select(Qs, ks, 64, wl.K)
+    assert np.array_equal(npy(Kslc), ks, equal_nan=True)
+    oi, osc, ow = orc.select(Qs, ks, 64, wl.K, sel_scale=sel)
+    if case == "signed_zero":  # the planted rows rank their chunks in index order
+        t = np.arange(500, 4000, 13)
+        valid = oi[0, t] >= 0
+        assert np.all(osc[0, t][valid] == 0) and np.any(np.signbit(osc[0, t][valid]))
+        assert np.array_equal(oi[0, t, :, 0], np.zeros_like(oi[0, t, :, 0]))
     assert np.array_equal(npy(idx), oi)
     sc = npy(score)
     fin = np.isfinite(osc)
     assert np.array_equal(np.isfinite(sc), fin)
+    assert not np.isnan(sc).any() and not np.isnan(npy(w)).any()
+    assert np.array_equal(sc[~fin], osc[~fin])  # the same infinities
     assert np.array_equal(sc[fin].astype(np.float32), osc[fin].astype(np.float32))
     assert max_abs(npy(w), ow) <= 1e-5
 
@@ -353,6 +297,36 @@ def test_decode_small(hsa, dev, ctx, generic):
     assert np.array_equal(npy(idx), d["idx"])
     assert max_abs(npy(w), d["w"]) <= 1e-5
     assert max_abs(npy(O), d["O"]) <= 2e-2
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
+def test_decode_nonfinite_scores(hsa, dev, generic):
+    """Decode with selection queries that are not ordinary numbers: a NaN score ranks as -inf
+    (the slots take chunks in index order with weight 0, so the heads' output is 0) and an
+    +inf score takes all of the stick."""
+    ctx = 64 * 33 + 5
+    wl = W("decode_nonfinite", 3, ctx, 16, 2, 64, 64, 8, torch.bfloat16)
+    say("case decode nonfinite", generic)
+    x = workloads.make_decode_inputs(wl, seed=9, ctx=ctx)
+    qs = x["qs"].clone()
+    qs[1, 0, :] = float("nan")
+    qs[2, 1, 4] = float("inf")
+    q, Kc, Vc = (x[k].to(dev) for k in ("q", "Kc", "Vc"))
+    Kslc = hsa.pool(Kc)
+    O, idx, score, w = hsa.decode(q, qs.to(dev), Kc, Vc, Kslc, wl.K, generic=generic)
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    ks = orc.pool(x["Kc"], 64)
+    d = orc.decode(x["q"], qs, x["Kc"], x["Vc"], ks, 64, wl.K)
+    assert list(d["idx"][1, 0]) == list(range(8)) and np.all(d["w"][1, 0] == 0)
+    assert np.isposinf(d["score"][2, 1, 0]) and d["w"][2, 1, 0] == 1.0
+    assert np.array_equal(npy(idx), d["idx"])
+    sc = npy(score)
+    assert not np.isnan(sc).any()
+    assert np.array_equal(sc[~np.isfinite(d["score"])], d["score"][~np.isfinite(d["score"])])
+    assert max_abs(npy(w), d["w"]) <= 1e-5
+    assert max_abs(npy(O), d["O"]) <= 2e-2
+    assert np.all(npy(O)[1, :8] == 0)
 
 
 SOFTMAX_CASES = [w for w in SMALL if w.name in ("tiny_fp32", "bf16_d64_ragged", "bf16_d128_ragged",
@@ -782,7 +756,7 @@ def test_full_backward_sampled(hsa, dev):
                     x["dO"].to(dev))
     torch.cuda.synchronize()
     orc = oracle.get()
-    f, diff, _ = compare_forward(orc, x, wl, g)  # full oracle selection (needed for phase 2)
+    f, diff, _ = compare_forward(orc, x, wl, g)  # the selection on every row
     tm = _sample_rows(wl, 48, seed=2)
     rng = np.random.default_rng(3)
     cm = np.zeros((wl.B, wl.nC), np.uint8)
@@ -851,13 +825,13 @@ def test_max_chunks_step_sampled(hsa, dev, D, Hq, Hkv):
     tm = T.copy()
     tm[0, rng.choice(wl.L, size=64, replace=False)] = 1  # rows whose gradients must be zero
     cm = np.zeros((wl.B, wl.nC), np.uint8)
-    sel = f["idx"][T.astype(bool)]
+    sel = npy(g["idx"])[T.astype(bool)].astype(np.int64)
     cm[0, np.unique(sel[sel >= 0])] = 1
     picked = int(cm.sum())
     cm[0, rng.choice(wl.nC, size=16, replace=False)] = 1
     cm[0, [0, wl.nC - 1]] = 1
     say("chunks selected by the sample:", picked, "compared:", int(cm.sum()))
-    compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=tm, chunk_mask=cm)
+    compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=tm, chunk_mask=cm, sel_rows=T)
     tail = slice(wl.nC * wl.S, wl.L)
     assert torch.count_nonzero(grads["dK"][:, tail]).item() == 0
     assert torch.count_nonzero(grads["dV"][:, tail]).item() == 0
@@ -880,3 +854,133 @@ def test_full_decode(hsa, dev):
     assert np.array_equal(npy(idx), d["idx"])
     assert max_abs(npy(w), d["w"]) <= 1e-5
     assert max_abs(npy(O), d["O"]) <= 2e-2
+
+
+# ---- the normalisers at the boundary, and the forward state's records ----------------------
+
+LSE_CASES = [w for w in SMALL if w.name in ("tiny_fp32", "bf16_d64_ragged", "bf16_d128_ragged",
+                                           "bf16_g1_k3", "bf16_d64_g16_k16")]
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
+@pytest.mark.parametrize("wl", LSE_CASES, ids=lambda w: w.name)
+def test_lse_out_and_in(hsa, dev, wl, generic):
+    """hsa_fwd's optional lse equals the oracle's normaliser log(1 + sum_j exp(z_j)) of every
+    (token, head, slot) (0 on masked slots); hsa_bwd given that lse (and no forward state)
+    matches the oracle's gradients."""
+    say("case lse", wl, generic)
+    orc = oracle.get()
+    x = workloads.make_inputs(wl, seed=12)
+    Q, K, V, Qs, dO = (x[k].to(dev) for k in ("Q", "K", "V", "Qs", "dO"))
+    Kslc, idx, score, w = hsa.select(Qs, K, wl.K, generic=generic)
+    O, lse = hsa.fwd(Q, K, V, idx, w, generic=generic, want_lse=True)
+    grads = hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, generic=generic, lse=lse)
+    torch.cuda.synchronize()
+    gi, gw = npy(idx).astype(np.int32), npy(w)
+    Oo, lo = orc.attend(x["Q"], x["K"], x["V"], gi, gw, wl.S, want_lse=True)
+    assert max_abs(npy(O), Oo) <= tol_for(wl.dtype)
+    valid = np.repeat(gi >= 0, wl.G, axis=2)  # [B, L, Hq, K]
+    gl = npy(lse)
+    assert np.all(gl[~valid] == 0)
+    err = max_abs(gl, lo)
+    say("lse max abs", err)
+    assert err <= (1e-4 if wl.dtype == torch.float32 else 1e-3), err
+    g = dict(Q=Q, K=K, V=V, Qs=Qs, Kslc=Kslc, idx=idx, score=score, w=w, O=O)
+    f, diff, _ = compare_forward(orc, x, wl, g)
+    compare_backward(orc, x, wl, g, f, diff, grads)
+
+
+def _invidx_launches(hsa, fn):
+    hsa.timer_enable(True)
+    out = fn()
+    torch.cuda.synchronize()
+    n = hsa.timer_read()["invidx"][0]
+    hsa.timer_enable(False)
+    return out, n
+
+
+def test_after_fwd_stale_workspace(hsa, dev):
+    """HSA_BWD_AFTER_FWD reuses the forward's state only when the library's record of the
+    workspace names the same problem, Q, K, idx and w: after a forward of another selection
+    on the workspace, or a backward of another problem that rebuilt it, the flagged backward
+    rebuilds its index (one index launch instead of none) and equals, bit for bit, the
+    backward without the flag, and the oracle."""
+    from chunk_sparse_attention_amd import _lib
+    wl = SMALL[1]  # bf16_d64_ragged: the chunk-major forward and the matrix-core backward
+    say("case stale workspace", wl)
+    orc = oracle.get()
+    x = workloads.make_inputs(wl, seed=14)
+    Q, K, V, Qs, dO = (x[k].to(dev) for k in ("Q", "K", "V", "Qs", "dO"))
+    Kslc, idx, score, w = hsa.select(Qs, K, wl.K)
+    other = workloads.make_selection(wl.B, wl.L, wl.Hkv, wl.S, wl.K, seed=15)
+    idx2, w2 = other["idx"].to(dev), other["w"].to(dev)
+    prob = hsa.problem(wl.B, wl.L, wl.Hq, wl.Hkv, wl.D, wl.K, wl.dtype)
+    ws = hsa.workspace(_lib.HSA_OP_BWD, prob, dev)
+    alone = hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO)
+
+    def flagged():
+        return hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, ws=ws, after_fwd=True)
+
+    # 1. the matching forward: the state is reused (no index launch)
+    O = hsa.fwd(Q, K, V, idx, w, ws=ws)
+    fresh, n = _invidx_launches(hsa, flagged)
+    assert n == 0, n
+    # 2. a forward of another selection on the same workspace: rebuilt
+    hsa.fwd(Q, K, V, idx2, w2, ws=ws)
+    stale, n = _invidx_launches(hsa, flagged)
+    assert n == 1, n
+    for k in ("dQ", "dK", "dV", "dQs", "dKslc"):
+        assert torch.equal(stale[k], alone[k]), k
+    # 3. the matching forward, then a backward of another problem (smaller K) without the
+    #    flag on the same workspace, which rebuilds the index there: rebuilt again
+    hsa.fwd(Q, K, V, idx, w, ws=ws)
+    small = hsa.bwd(Q, K, V, Qs, Kslc, idx[..., :4].contiguous(), score[..., :4].contiguous(),
+                    w[..., :4].contiguous(), dO, ws=ws)
+    stale2, n = _invidx_launches(hsa, flagged)
+    assert n == 1, n
+    for k in ("dQ", "dK", "dV", "dQs", "dKslc"):
+        assert torch.equal(stale2[k], alone[k]), k
+    # 4. no forward ever ran on a fresh workspace: rebuilt
+    ws3 = hsa.workspace(_lib.HSA_OP_BWD, prob, dev)
+    never = hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, ws=ws3, after_fwd=True)
+    torch.cuda.synchronize()
+    for k in ("dQ", "dK", "dV", "dQs", "dKslc"):
+        assert torch.equal(never[k], alone[k]), k
+    del small
+    g = dict(Q=Q, K=K, V=V, Qs=Qs, Kslc=Kslc, idx=idx, score=score, w=w, O=O)
+    f, diff, _ = compare_forward(orc, x, wl, g)
+    compare_backward(orc, x, wl, g, f, diff, stale)
+    compare_backward(orc, x, wl, g, f, diff, fresh)
+
+
+@pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
+def test_repeated_chunks_in_a_row(hsa, dev, generic):
+    """A caller's selection that repeats a chunk within a row (outside hsa_fwd's contract, and
+    never produced by hsa_select): up to 16384 chunks every repeated slot still adds its own
+    term, as in the oracle, and the backward differentiates each slot; the inverse index
+    gives the repeated slots their own entries."""
+    wl = SMALL[1]
+    say("case repeated chunks", generic)
+    orc = oracle.get()
+    x = workloads.make_inputs(wl, seed=16)
+    sel = workloads.make_selection(wl.B, wl.L, wl.Hkv, wl.S, wl.K, seed=17)
+    idx = sel["idx"].clone()
+    rows = torch.arange(3 * 64, wl.L, 7)
+    idx[0, rows, 0, 1] = idx[0, rows, 0, 0]           # slot 1 repeats slot 0
+    idx[1, rows, 1, 3] = idx[1, rows, 1, 2]           # slot 3 repeats slot 2
+    idx[1, rows[::3], 0, 2] = idx[1, rows[::3], 0, 0]  # slots 0 and 2 agree
+    Q, K, V, Qs, dO = (x[k].to(dev) for k in ("Q", "K", "V", "Qs", "dO"))
+    d_idx, score, w = idx.to(dev), sel["score"].to(dev), sel["w"].to(dev)
+    Kslc = hsa.pool(K)
+    O = hsa.fwd(Q, K, V, d_idx, w, generic=generic)
+    grads = hsa.bwd(Q, K, V, Qs, Kslc, d_idx, score, w, dO, generic=generic)
+    torch.cuda.synchronize()
+    tol = tol_for(wl.dtype)
+    Oo = orc.attend(x["Q"], x["K"], x["V"], idx, sel["w"], wl.S)
+    assert max_abs(npy(O), Oo) <= tol
+    o = orc.backward(x["Q"], x["K"], x["V"], x["Qs"], orc.pool(x["K"], wl.S), idx,
+                     sel["score"], sel["w"], x["dO"], wl.S)
+    rep = {k: max_abs(npy(grads[k]), o[k]) for k in ("dQ", "dK", "dV", "dQs", "dKslc")}
+    say("repeated chunks", rep)
+    for k, v in rep.items():
+        assert v <= tol, (k, v)
