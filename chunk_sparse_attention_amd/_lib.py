@@ -25,7 +25,8 @@ HSA_BWD_AFTER_FWD = 0x2
 EXPORTS = ("hsa_status_string", "hsa_last_error", "hsa_version", "hsa_workspace_size",
            "hsa_select", "hsa_fwd", "hsa_bwd", "hsa_decode", "hsa_decode_host_kv",
            "hsa_decode_ragged", "hsa_pool_chunks", "hsa_fwd_layers", "hsa_decode_shared",
-           "hsa_decode_shared_host_kv", "hsa_timer_enable", "hsa_timer_read")
+           "hsa_decode_shared_host_kv", "hsa_timer_enable", "hsa_timer_read",
+           "hsa_decode_noalloc")
 # hsa_kernel_t: kernel classes of the timing aid
 KERNEL_CLASSES = ("pool", "select", "tile_prep", "prep_ops", "fwd", "invidx", "bwd_p1", "bwd_p2",
                   "bwd_reduce", "decode_scan", "decode_attend", "fwd_token")
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.hsa_bwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, U, P, Z, P]
     L.hsa_decode.restype = I
     L.hsa_decode.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, Z, P]
+    L.hsa_decode_noalloc.restype = I
+    L.hsa_decode_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P]
     L.hsa_decode_host_kv.restype = I
     L.hsa_decode_host_kv.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, Z, P]
     L.hsa_decode_ragged.restype = I

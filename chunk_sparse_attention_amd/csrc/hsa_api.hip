@@ -412,6 +412,61 @@ HSA_EXPORT hsa_status_t hsa_decode(const hsa_problem_t* p, const void* q, const 
                      false, nullptr);
 }
 
+// ---- decode without a caller workspace ---------------------------------------------------
+// Scratch of hsa_decode_noalloc: the scan blocks' candidate keys, in a file-scope device
+// array.  Each device that runs the library holds its own copy until the process ends.  In
+// host code the array's name is not a device address: the address of this device's copy
+// comes from hipGetSymbolAddress, taken once per device and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch` (nullptr and a message on failure).
+hsa_status_t scratch_for_current_device(void** out) {
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HSA_ERR_HIP, "no current HIP device in [0, %d) (got %d)", kMaxDevices, dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(HSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HSA_OK;
+}
+
+}  // namespace
+
+HSA_EXPORT hsa_status_t hsa_decode_noalloc(const hsa_problem_t* p, const void* q,
+                                           const void* qs, const void* Kcache,
+                                           const void* Vcache, const void* Kslc, void* O,
+                                           int32_t* idx, float* score, float* w,
+                                           hsa_stream_t stream) {
+  hsa::Dims d;
+  TRY(check_problem(HSA_OP_DECODE, p, &d));
+  const size_t need = ws_bytes_for(HSA_OP_DECODE, d);
+  if (need > kNoAllocScratchBytes)
+    return fail(HSA_ERR_UNSUPPORTED,
+                "decode needs %zu bytes of scratch, more than the %zu hsa_decode_noalloc holds "
+                "(use hsa_decode with a workspace)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) TRY(scratch_for_current_device(&ws));
+  return decode_impl(p, q, qs, Kcache, Vcache, Kslc, O, idx, score, w, ws,
+                     ws ? kNoAllocScratchBytes : 0, stream, false, nullptr);
+}
+
 HSA_EXPORT hsa_status_t hsa_decode_host_kv(const hsa_problem_t* p, const void* q,
                                            const void* qs, const void* Kcache,
                                            const void* Vcache, const void* Kslc, void* O,

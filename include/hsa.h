@@ -189,6 +189,21 @@ hsa_status_t hsa_decode(const hsa_problem_t* p, const void* q, const void* qs,
                         int32_t* idx, float* score, float* w, void* ws, size_t ws_bytes,
                         hsa_stream_t stream);
 
+/* hsa_decode for callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments, results and errors without
+ * `ws`.  Its scratch (the scan blocks' candidate keys, 8 * B * Hkv * ceil(ctx/(64*1024)) * K
+ * bytes on the default kernels) lives in a device array of 4 MiB inside the library, one
+ * copy per device, held until the process ends; a
+ * problem that needs more returns HSA_ERR_UNSUPPORTED before anything is enqueued.  The call
+ * allocates nothing and frees nothing.  Every call on one device uses that device's copy,
+ * and each call rewrites all of the scratch it reads, so successive calls need no clearing;
+ * calls that overlap in time on one device (other streams, other threads) race on it and
+ * must be ordered by the caller. */
+hsa_status_t hsa_decode_noalloc(const hsa_problem_t* p, const void* q, const void* qs,
+                                const void* Kcache, const void* Vcache, const void* Kslc,
+                                void* O, int32_t* idx, float* score, float* w,
+                                hsa_stream_t stream);
+
 /* One decode step with the token K/V cache left in host memory (note section 训练与推理优化,
  * KV cache offloading: the chunk-key table stays on the device for selection and each step
  * moves only the selected chunks; 局限与展望: that exchange is g x dh x K x S values per

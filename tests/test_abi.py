@@ -163,3 +163,18 @@ def test_kernel_timer_without_launches():
         text = fh.read()
     for i, name in enumerate(_lib.KERNEL_CLASSES):
         assert f"HSA_KERNEL_{name.upper()} = {i}," in text
+
+
+def test_decode_noalloc_refuses_oversized_scratch():
+    """hsa_decode_noalloc keeps its scratch in a 4 MiB device array: a problem that needs more
+    is refused with HSA_ERR_UNSUPPORTED before anything touches the GPU."""
+    from chunk_sparse_attention_amd import _lib
+    lib = _lib.lib()
+    fake = ctypes.c_void_p(0x10000)  # never dereferenced: the size check comes first
+    # 8 bytes * B * Hkv * one scan block * K = 64 MiB of candidate keys
+    p = _prob(B=1 << 16, L=64, Hq=8, Hkv=8, K=16)
+    st = lib.hsa_decode_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, None,
+                                fake, None)
+    assert st == 2 and b"scratch" in lib.hsa_last_error(), lib.hsa_last_error()
+    st = lib.hsa_decode_noalloc(None, fake, fake, fake, fake, fake, fake, fake, None, fake, None)
+    assert st == 1
