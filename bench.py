@@ -40,10 +40,11 @@ METRIC = "HSA fwd+bwd tokens/sec at L=16K/64K bf16; % HBM roofline / MFMA util"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP64_VALU_PEAK_TFLOPS = 78.6   # 256 CUs x 4 SIMD x 16 lanes x 2 (FMA) x 2.4 GHz
-# v_exp_f32 results per second, measured on MI355X with a loop of eight independent exp2
-# chains per lane at 64 waves per CU (the same loop with fp32 FMA gives 57.2 T/s); the
-# attention's exponentials are priced against it as a third floor beside HBM and MFMA
-EXP_PEAK_PER_S = 17.9e12
+# v_exp_f32 results per second: the transcendental unit takes a quarter of the fp32 lane
+# rate, 256 CUs x 4 SIMDs x 32 fp32 lanes per clock / 4 x 2.4 GHz (the fp32 vector peak,
+# 157.3 TFLOP/s, is the same 32 lanes x 2 flops); the attention's exponentials are priced
+# against it as a third floor beside HBM and MFMA
+EXP_PEAK_PER_S = 256 * 4 * 32 / 4 * 2.4e9
 
 
 def log(*a):
@@ -196,6 +197,14 @@ def measured_traffic(workload: str, cls: str):
     return None if k is None else k["hbm_bytes_per_launch"]
 
 
+def decode_traffic():
+    """Measured HBM bytes of one decode_1m step (scan + attend), from the committed counter
+    summary of `bench.py --only decode_step`, if taken on the current sources."""
+    a = measured_traffic("decode_1m", "decode_scan")
+    b = measured_traffic("decode_1m", "decode_attend")
+    return None if a is None or b is None else a + b
+
+
 def summarize_counters(cdir: str, workload: str, copy_mib: int) -> int:
     """Turn two rocprofv3 --pmc runs of `bench.py --only step --copy-mib M` (FETCH_SIZE under
     cdir/fetch, WRITE_SIZE under cdir/write) into HBM bytes per launch of each kernel class.
@@ -332,42 +341,96 @@ def summarize_trace(tdir: str, bench_json: str) -> int:
     return 0
 
 
-def cpu_baseline(wl, x, budget_s: float = 20.0) -> dict:
-    """The oracle (pool, select, attend, backward) over the workload's sequences, one at a
-    time, until all are done or budget_s has passed."""
-    import oracle
-    orc = oracle.get()
-    t0 = time.perf_counter()
-    done = 0
-    for b in range(wl.B):
-        sl = {k: x[k][b:b + 1] for k in ("Q", "K", "V", "Qs", "dO")}
-        f = orc.forward(sl["Q"], sl["K"], sl["V"], sl["Qs"], wl.S, wl.K)
-        orc.backward(sl["Q"], sl["K"], sl["V"], sl["Qs"], f["Kslc"], f["idx"], f["score"],
-                     f["w"], sl["dO"], wl.S)
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    el = time.perf_counter() - t0
-    # OpenMP uses OMP_NUM_THREADS threads when it is set, else one per CPU of the affinity mask
-    env = os.environ.get("OMP_NUM_THREADS", "")
-    cores = int(env) if env.isdigit() else len(os.sched_getaffinity(0))
-    model = "unknown"
+def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
                 if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return dict(value=round(done * wl.L / el, 2), unit="tokens/s", cores=cores, kind="oracle",
-                sample=f"{done} of {wl.B} sequences x {wl.L} tokens: pool+select+attend+"
-                       f"backward in {el:.1f} s", cpu=model)
+    return "unknown"
 
 
-def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
+def cpu_threads() -> int:
+    """Threads the oracle's OpenMP loops use by default: OMP_NUM_THREADS when set, else one
+    per CPU of the affinity mask."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return int(env) if env.isdigit() else len(os.sched_getaffinity(0))
+
+
+def median_seconds(fn, reps: int = 3) -> float:
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2]
+
+
+def oracle_rates(orc, tokens: int, fn, threads: int) -> dict:
+    """Median of three timed runs of fn at `threads` and at one thread; tokens/s of each."""
+    out = {}
+    for n in (threads, 1):
+        orc.set_threads(n)
+        sec = median_seconds(fn)
+        out["threads_%d" % n] = dict(seconds=round(sec, 3), tokens_per_s=round(tokens / sec, 2))
+    orc.set_threads(threads)
+    return out
+
+
+def cpu_baseline(wl, x, wl2, x2, every: int = 16, every2: int = 64) -> dict:
+    """The oracle (test infrastructure, untuned) on the host cores, on bounded samples of the
+    workloads: median of three runs at all threads and at one thread.
+      step (fwd_16k): sequence 0, every `every`-th token: pooling of the whole sequence, then
+        selection, attention and the whole backward for the sampled tokens only (the other
+        rows select nothing, so both backward phases do the sampled tokens' work);
+      select+fwd (fwd_64k): every `every2`-th token, pooling of the whole sequence.
+    Per-token work does not depend on the token's position except selection, which grows
+    with the number of earlier chunks; every k-th token samples those positions evenly, so
+    tokens/s = sampled tokens / seconds is the rate of the whole workload."""
+    import numpy as np
+    import oracle
+    orc = oracle.get()
+    threads = cpu_threads()
+    sl = {k: x[k][0:1] for k in ("Q", "K", "V", "Qs", "dO")}
+    rows = np.zeros((1, wl.L), np.uint8)
+    rows[0, ::every] = 1
+    n_rows = int(rows.sum())
+
+    def step():
+        Kslc = orc.pool(sl["K"], wl.S)
+        idx, score, w = orc.select(sl["Qs"], Kslc, wl.S, wl.K, row_mask=rows)
+        orc.attend(sl["Q"], sl["K"], sl["V"], idx, w, wl.S, row_mask=rows)
+        orc.backward(sl["Q"], sl["K"], sl["V"], sl["Qs"], Kslc, idx, score, w, sl["dO"], wl.S)
+
+    rows2 = np.zeros((wl2.B, wl2.L), np.uint8)
+    rows2[:, ::every2] = 1
+    n_rows2 = int(rows2.sum())
+
+    def select_fwd():
+        Kslc = orc.pool(x2["K"], wl2.S)
+        idx, _, w = orc.select(x2["Qs"], Kslc, wl2.S, wl2.K, row_mask=rows2)
+        orc.attend(x2["Q"], x2["K"], x2["V"], idx, w, wl2.S, row_mask=rows2)
+
+    r1 = oracle_rates(orc, n_rows, step, threads)
+    r2 = oracle_rates(orc, n_rows2, select_fwd, threads)
+    head = r1["threads_%d" % threads]
+    return dict(value=head["tokens_per_s"], unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{wl.name} step (pool+select+attend+backward), sequence 0, every "
+                       f"{every}th token ({n_rows} tokens); median of 3",
+                cpu=cpu_model(),
+                configs={f"{wl.name}_step": dict(sample=f"sequence 0, every {every}th token",
+                                                 **r1),
+                         f"{wl2.name}_select_fwd": dict(sample=f"every {every2}th token",
+                                                        **r2)})
+
+
+def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int, cpu: bool = False) -> dict:
     """Time the 1M-context decode step (decode_1m), caches resident in HBM (back to back, and
-    cold: the median step after the last-level cache was flushed), and its variants."""
+    cold: the median step after the last-level cache was flushed), and its variants.  cpu:
+    also time the oracle's decode step on the host (median of three, all threads and one
+    thread; its chunk-key table is pooled first and not timed, as on the GPU)."""
     import torch
     wl3 = workloads.WORKLOADS["decode_1m"]
     log(f"bench: decode {wl3.name} (generating caches)")
@@ -443,6 +506,17 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
     e1.record()
     torch.cuda.synchronize()
     hms = e0.elapsed_time(e1) / reps
+    cpu_dec = None
+    if cpu:
+        import oracle
+        orc = oracle.get()
+        log("bench: cpu baseline of the decode step (oracle)")
+        qh, qsh = q.cpu(), qs.cpu()
+        ksh = orc.pool(Kh, wl3.S)
+        cpu_dec = dict(sample=f"the whole step, {wl3.B} sequences", cores=cpu_threads(),
+                       **oracle_rates(orc, wl3.B, lambda: orc.decode(qh, qsh, Kh, Vh, ksh, wl3.S,
+                                                                     wl3.K), cpu_threads()))
+        del ksh
     del Kh, Vh
     # sequences of different lengths in the same cache (hsa_decode_ragged): lengths drawn
     # uniformly from [ctx/2, ctx] with a fixed seed
@@ -515,7 +589,7 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
             "ms": round(dms, 4), "new_tokens_per_s": round(wl3.B / (dms / 1e3), 1),
             "cold_ms_median": round(cms, 4), "graph_ms": round(gms, 4),
             "roofline": roofline("decode_scan+decode_attend", dict(bytes=dbytes, flops=0),
-                                 tot3 / max(n3, 1), None),
+                                 tot3 / max(n3, 1), decode_traffic()),
             "scan_ms": round(kt3["decode_scan"][1] / max(n3, 1), 4),
             "attend_ms": round(kt3["decode_attend"][1] / max(n3, 1), 4),
             "host_kv": {"ms": round(hms, 4), "vs_device_kv": round(hms / dms, 3),
@@ -523,7 +597,62 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int) -> dict:
             "ragged": {"ms": round(rms, 4), "mean_ctx": round(float(lens.double().mean()), 1),
                        "lengths": "uniform in [ctx/2, ctx], seed 1"},
             "shared_selection": {"workload": f"{nl} layers, B={wl4.B} ctx={ctx4} Hq={wl4.Hq} "
-                                             f"Hkv={wl4.Hkv} d={wl4.D} K={wl4.K}", **lay}}
+                                             f"Hkv={wl4.Hkv} d={wl4.D} K={wl4.K}", **lay},
+            "cpu_baseline": cpu_dec}
+
+
+def copy_reference(dev, mib: int) -> None:
+    """Profiling aid: one plain device copy of `mib` MiB whose source was first pushed out of
+    the 256 MB last-level cache (by writing 1 GiB elsewhere), so the copy reads it from HBM;
+    its byte counters scale the counters of the kernels that follow."""
+    if not mib:
+        return
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"bench: copied {mib} MiB")
+    del src, dst, flush
+
+
+def ceilings(dev, reps: int = 20) -> dict:
+    """Streaming rates of plain device kernels (torch's own): a read (sum of 2 GiB of fp32), a
+    write (fill of 2 GiB) and a copy (1 GiB to 1 GiB), each far larger than the 256 MB
+    last-level cache, and a read of 128 MiB that was just written (served by that cache).
+    The practical ceilings the kernels' measured traffic is compared with."""
+    import torch
+    big = torch.ones(1 << 29, dtype=torch.float32, device=dev)   # 2 GiB
+    half = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    small = torch.ones(1 << 25, dtype=torch.float32, device=dev)  # 128 MiB
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, nbytes, prep=None):
+        for _ in range(2):
+            if prep:
+                prep()
+            fn()
+        torch.cuda.synchronize()
+        t = 0.0
+        for _ in range(reps):
+            if prep:
+                prep()
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t += e0.elapsed_time(e1)
+        return round(nbytes / (t / reps / 1e3) / 1e9, 1)
+
+    out = {"read_2GiB_GBs": rate(lambda: big.sum(), big.numel() * 4),
+           "write_2GiB_GBs": rate(lambda: big.fill_(1.0), big.numel() * 4),
+           "copy_1GiB_GBs": rate(lambda: half.copy_(big[:1 << 28]), 2 * half.numel() * 4),
+           "read_128MiB_after_write_GBs": rate(lambda: small.sum(), small.numel() * 4,
+                                               prep=lambda: small.fill_(2.0))}
+    del big, half, small
+    return out
 
 
 def main() -> int:
@@ -541,7 +670,11 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="profiling aid: with --only, first copy this many MiB once with a plain "
                          "device copy (the scale reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["step", "select", "fwd", "bwd", "decode"], default=None,
+    ap.add_argument("--ceilings", action="store_true",
+                    help="print the streaming rates of plain device kernels (read, write, copy, "
+                         "a cache-resident read) as one JSON line and exit")
+    ap.add_argument("--only", choices=["step", "select", "fwd", "bwd", "decode", "decode_step"],
+                    default=None,
                     help="profiling aid: after the warm-up, run only this entry point (or the "
                          "whole step) --steps times and print its mean time (no JSON line)")
     ap.add_argument("--summarize-counters", metavar="DIR", default=None,
@@ -567,8 +700,35 @@ def main() -> int:
 
     wl = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.ceilings:
+        print(json.dumps({"ceilings": ceilings(dev)}), flush=True)
+        return 0
     if args.only == "decode":
         log("bench: only decode", run_decode(hsa, _lib, workloads, dev, args.generic, args.steps))
+        return 0
+    if args.only == "decode_step":
+        # the decode_1m step alone, --steps times (for counter runs; with --copy-mib the same
+        # copy reference as --only step)
+        wl3 = workloads.WORKLOADS["decode_1m"]
+        x3 = workloads.make_decode_inputs(wl3, seed=0, slab=4)
+        q, qs = x3["q"].to(dev), x3["qs"].to(dev)
+        Kc, Vc = x3["Kc"].to(dev), x3["Vc"].to(dev)
+        del x3
+        Kslc3 = hsa.pool(Kc)
+        prob3 = hsa.problem(wl3.B, wl3.L, wl3.Hq, wl3.Hkv, wl3.D, wl3.K, wl3.dtype,
+                            generic=args.generic)
+        ws3 = hsa.workspace(_lib.HSA_OP_DECODE, prob3, dev)
+        for _ in range(args.warmup):
+            hsa.decode(q, qs, Kc, Vc, Kslc3, wl3.K, generic=args.generic, ws=ws3)
+        torch.cuda.synchronize()
+        copy_reference(dev, args.copy_mib)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            hsa.decode(q, qs, Kc, Vc, Kslc3, wl3.K, generic=args.generic, ws=ws3)
+        e1.record()
+        torch.cuda.synchronize()
+        log(f"bench: only decode_step: {e0.elapsed_time(e1) / args.steps:.4f} ms per step")
         return 0
     log(f"bench: generating {wl.name} inputs")
     x = workloads.make_inputs(wl, seed=0)
@@ -611,17 +771,7 @@ def main() -> int:
                "bwd": lambda: hsa.bwd(Q, K, V, Qs, Kslc, idx, score, w, dO, generic=gen,
                                       ws=ws_bwd)}[args.only]
         torch.cuda.synchronize()
-        if args.copy_mib:
-            # the source is written first and then pushed out of the 256 MB last-level cache
-            # by writing 1 GiB elsewhere, so the copy reads it from HBM
-            src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
-            flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-            dst = torch.empty_like(src)
-            torch.cuda.synchronize()
-            dst.copy_(src)
-            torch.cuda.synchronize()
-            log(f"bench: copied {args.copy_mib} MiB")
-            del src, dst, flush
+        copy_reference(dev, args.copy_mib)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
@@ -790,11 +940,17 @@ def main() -> int:
         del Q2, K2, V2, Qs2, dO2, x2, O2, ws2
 
     if not args.no_decode:
-        out["decode"] = run_decode(hsa, _lib, workloads, dev, gen, reps=50)
+        out["decode"] = run_decode(hsa, _lib, workloads, dev, gen, reps=50,
+                                   cpu=not args.no_cpu_baseline)
 
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(wl, x)
+        wl2 = workloads.WORKLOADS["fwd_64k"]
+        x2 = workloads.make_inputs(wl2, seed=0, with_grad=False)
+        out["cpu_baseline"] = cpu_baseline(wl, x, wl2, x2)
+        if out.get("decode") and out["decode"].get("cpu_baseline"):
+            out["cpu_baseline"]["configs"]["decode_1m_step"] = out["decode"].pop("cpu_baseline")
+        del x2
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -123,6 +123,10 @@ class Oracle:
     def __init__(self, path: str = _LIB):
         self.path = path
         lib = ctypes.CDLL(path)
+        lib.oracle_set_threads.restype = None
+        lib.oracle_set_threads.argtypes = [_I]
+        lib.oracle_max_threads.restype = _I
+        lib.oracle_max_threads.argtypes = []
         lib.oracle_round.restype = _D
         lib.oracle_round.argtypes = [_D, _I]
         lib.oracle_pool.restype = None
@@ -140,6 +144,14 @@ class Oracle:
         lib.oracle_decode.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _D, _D,
                                       _I, _I, _P, _P, _P, _P]
         self.lib = lib
+
+    # -- threads -------------------------------------------------------------------------
+    def set_threads(self, n: int) -> None:
+        """OpenMP threads of the row loops from now on (results do not depend on it)."""
+        self.lib.oracle_set_threads(int(n))
+
+    def max_threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
 
     # -- elementwise -------------------------------------------------------------------
     def round(self, x: float, dt: int) -> float:

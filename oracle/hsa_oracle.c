@@ -36,6 +36,7 @@
  *   - query head h belongs to KV group floor(h / (Hq/Hkv)).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -48,6 +49,10 @@
 #define MUT(n) (ORACLE_MUTATION == (n))
 
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+
+/* Threads of the OpenMP row loops from now on (timing aid; no arithmetic depends on it). */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int oracle_max_threads(void) { return omp_get_max_threads(); }
 
 /* ---- storage helpers ------------------------------------------------------------- */
 
