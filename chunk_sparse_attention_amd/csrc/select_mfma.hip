@@ -147,50 +147,59 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
       *reinterpret_cast<uint4*>(&kl[r][e]) = pre[u];
     }
   };
+  // |k|^2 of the staged rows, each row's D/8 pieces summed across the D/8 consecutive
+  // threads that hold them, folded into a running maximum (pass 1 only; rows past m were
+  // loaded as zeros)
+  float k2run = 0.0f;
+  bool kbad = false;  // a staged row with a NaN or infinite |k|^2 (fmaxf would drop a NaN)
+  auto k2_of_staged = [&]() {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const float k2 = group_sum<D / 8>(sq8(__builtin_bit_cast(bf16x8, pre[u])));
+      k2run = fmaxf(k2run, k2);
+      kbad = kbad || !(k2 <= 3.0e38f);
+    }
+  };
 
   // approximate scores of chunks c0 .. c0+63 (staged) against the wave's 16 tokens: lane
-  // holds chunks c0 + 16*t4 + 4*blk + i of its token; k2 = |k|^2 of chunk c0 + 16*t4 + col
-  auto approx = [&](f32x4 (&sacc)[4], float& k2max) {
+  // holds chunks c0 + 16*t4 + 4*blk + i of its token
+  auto approx = [&](f32x4 (&sacc)[4]) {
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       sacc[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
-      float k2 = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kl[16 * t4 + col][32 * ks + 8 * blk]);
-        k2 += sq8(ka);
         sacc[t4] = mfma_16x16x32(ka, qb[ks], sacc[t4]);
       }
-      k2max = fmaxf(k2max, rows4_sum(k2));
     }
   };
 
   // 1. the KP largest approximate scores of this lane's share (4 KP >= K), kept sorted by a
   //    branch-free compare-exchange chain that the wave skips when no lane beats its last
-  //    entry; any non-finite value marks the token for the exact path
+  //    entry.  Non-finite values are caught once, from |q|^2 and |k|^2, below: when every
+  //    norm is finite and sel |q| max|k| and |q| max|k| stay far below the fp32 range, no
+  //    partial sum of any approximate score can overflow (Cauchy-Schwarz)
   static_assert(4 * KP >= KL, "the token's four lists must hold K scores");
   float top[KP];
 #pragma unroll
   for (int i = 0; i < KP; ++i) top[i] = -__builtin_inff();
-  float k2max = 0.0f;
-  bool bad = (__float_as_uint(q2) & 0x7f800000u) == 0x7f800000u;
   if (m > 0) fetch(0);
   for (int c0 = 0; c0 < m; c0 += 64) {
     __syncthreads();  // the previous group is no longer read
     stage();
+    k2_of_staged();
     __syncthreads();
     if (c0 + 64 < m) fetch(c0 + 64);
     f32x4 sacc[4];
-    approx(sacc, k2max);
+    approx(sacc);
+    const bool tail = c0 + 64 > m;  // the last group: rows past m were staged as zeros
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = c0 + 16 * t4 + 4 * blk + i;
         float v = sacc[t4][i] * sel_f;
-        const bool fin = (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u;  // not inf or NaN
-        bad = bad || (c < m && !fin);
-        v = (c < m && fin) ? v : -__builtin_inff();
+        if (tail && c0 + 16 * t4 + 4 * blk + i >= m) v = -__builtin_inff();
         if (__ballot(v > top[KP - 1])) {
 #pragma unroll
           for (int j = 0; j < KP; ++j) {
@@ -201,7 +210,23 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
         }
       }
   }
-  k2max = row16_max(k2max);  // over the wave's columns: every chunk was in some column
+  // max |k|^2 over every candidate chunk, and whether any was not finite: over the wave,
+  // then over the block's waves
+  __shared__ float k2w[4];
+  __shared__ int kbadw[4];
+  {
+    const float k2wave = rows4_max(row16_max(k2run));
+    const bool kb = __ballot(kbad) != 0;
+    if (lane == 0) {
+      k2w[wave] = k2wave;
+      kbadw[wave] = kb ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  const float k2max = fmaxf(fmaxf(k2w[0], k2w[1]), fmaxf(k2w[2], k2w[3]));
+  const float qk = sqrtf(q2) * sqrtf(k2max);  // bounds |approximate score| / sel and its sums
+  bool bad = !(q2 <= 3.0e38f) || (kbadw[0] | kbadw[1] | kbadw[2] | kbadw[3]) != 0 ||
+             !(qk < 1.0e37f) || !(fabsf(sel_f) * qk < 1.0e37f);
   // T = K-th largest over the token's 4 lanes (lane order breaks equal values apart)
   float T = -__builtin_inff();
   for (int k = 0; k < Kt; ++k) {
@@ -215,7 +240,7 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
     const uint32_t bo = (uint32_t)(best >> 2);
     T = __uint_as_float((bo & 0x80000000u) ? (bo ^ 0x80000000u) : ~bo);
   }
-  const float E = 2.0f * sel_f * sqrtf(q2) * sqrtf(k2max) * (float)(D + 8) * 5.9604645e-8f;
+  const float E = 2.0f * fabsf(sel_f) * qk * (float)(D + 8) * 5.9604645e-8f;
   bad = bad || (__float_as_uint(E) & 0x7f800000u) == 0x7f800000u;
   const float thr = T == -__builtin_inff() ? -__builtin_inff() : T - 2.0f * E;
   const uint64_t badmask = __ballot(bad);
@@ -229,8 +254,7 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
     __syncthreads();
     if (c0 + 64 < m) fetch(c0 + 64);
     f32x4 sacc[4];
-    float unused = 0.0f;
-    approx(sacc, unused);
+    approx(sacc);
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
