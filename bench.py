@@ -646,11 +646,19 @@ def ceilings(dev, reps: int = 20) -> dict:
             t += e0.elapsed_time(e1)
         return round(nbytes / (t / reps / 1e3) / 1e9, 1)
 
-    out = {"read_2GiB_GBs": rate(lambda: big.sum(), big.numel() * 4),
+    # reads: several reductions with small outputs, the best one taken as the read rate
+    reads = {"sum": lambda t: t.sum(),
+             "row_sums_256": lambda t: t.view(-1, 256).sum(1),
+             "row_max_4096": lambda t: t.view(-1, 4096).amax(1),
+             "dot": lambda t: torch.dot(t, t)}
+    rd = {k: rate(lambda f=f: f(big), big.numel() * 4) for k, f in reads.items()}
+    rs = {k: rate(lambda f=f: f(small), small.numel() * 4, prep=lambda: small.fill_(2.0))
+          for k, f in reads.items()}
+    out = {"read_2GiB_GBs": max(rd.values()), "read_2GiB_by_kernel": rd,
            "write_2GiB_GBs": rate(lambda: big.fill_(1.0), big.numel() * 4),
            "copy_1GiB_GBs": rate(lambda: half.copy_(big[:1 << 28]), 2 * half.numel() * 4),
-           "read_128MiB_after_write_GBs": rate(lambda: small.sum(), small.numel() * 4,
-                                               prep=lambda: small.fill_(2.0))}
+           "read_128MiB_after_write_GBs": max(rs.values()),
+           "read_128MiB_after_write_by_kernel": rs}
     del big, half, small
     return out
 

@@ -590,7 +590,10 @@ __global__ void __launch_bounds__(256) k_bwd_tok(
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (k0 + u < Kn) {
-        load_raw<E>(src + (size_t)(k0 + u) * G * D, v[u]);
+        if constexpr (D == 64)  // measured: faster at d = 64, slower at d = 128
+          load_raw_nt<E>(src + (size_t)(k0 + u) * G * D, v[u]);
+        else
+          load_raw<E>(src + (size_t)(k0 + u) * G * D, v[u]);
       } else {
 #pragma unroll
         for (int j = 0; j < E / 2; ++j) v[u][j] = 0u;

@@ -436,24 +436,31 @@ __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
   }
 }
 
-// Token phase of the chunk-major forward: one wave per (b, t, g) row; O = the sum of the
-// row's valid slots' weighted outputs in slot order (fp32), rounded once.  Slots that are not
-// valid have no partial (their workspace bytes are stale) and are masked out by selection.
-template <int D, int G>
+// Token phase of the chunk-major forward: SPLIT waves per (b, t, g) row, each owning a
+// contiguous 1/SPLIT of the row's G x D outputs; O = the sum of the row's valid slots'
+// weighted outputs in slot order (fp32), rounded once.  Slots that are not valid have no
+// partial (their workspace bytes are stale) and are masked out by selection.  The partials
+// are read once, with the non-temporal hint; rows of more than 512 outputs are split so that
+// a wave keeps at most eight 16-byte loads in flight per slot (measured: d = 128, G = 8
+// token phase 0.50 -> 0.465 ms at L = 64K).
+template <int D, int G, int SPLIT>
 __global__ void __launch_bounds__(256) k_fwd_tok(const bf16* __restrict__ o_part,
                                                  const int32_t* __restrict__ idx,
                                                  bf16* __restrict__ O, int L, int Hkv, int Kn,
                                                  int nC, int64_t rows) {
-  constexpr int E = G * D / 64;  // elements of the row's G x D block per lane
+  constexpr int E = G * D / 64 / SPLIT;  // elements of the row's G x D block per lane
   const int lane = threadIdx.x % 64;
-  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // (b * L + t) * Hkv + g
+  const int64_t wid = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const int64_t row = wid / SPLIT;  // (b * L + t) * Hkv + g
+  const int part = (int)(wid % SPLIT);
   if (row >= rows) return;  // whole wave
   const int g = (int)(row % Hkv);
   const int64_t bt = row / Hkv;
   const size_t o = (size_t)row * Kn;
   const int c = lane < Kn ? idx[o + lane] : -1;
   const uint64_t vmask = __ballot(c >= 0 && c < nC);
-  const bf16* src = o_part + o * (size_t)(G * D) + (size_t)lane * E;
+  const size_t off = (size_t)part * (G * D / SPLIT) + (size_t)lane * E;
+  const bf16* src = o_part + o * (size_t)(G * D) + off;
   float acc[E];
 #pragma unroll
   for (int j = 0; j < E; ++j) acc[j] = 0.0f;
@@ -462,7 +469,7 @@ __global__ void __launch_bounds__(256) k_fwd_tok(const bf16* __restrict__ o_part
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (k0 + u < Kn) {
-        load_raw<E>(src + (size_t)(k0 + u) * G * D, v[u]);
+        load_raw_nt<E>(src + (size_t)(k0 + u) * G * D, v[u]);
       } else {
 #pragma unroll
         for (int j = 0; j < E / 2; ++j) v[u][j] = 0u;
@@ -471,7 +478,7 @@ __global__ void __launch_bounds__(256) k_fwd_tok(const bf16* __restrict__ o_part
 #pragma unroll
     for (int u = 0; u < 8; ++u) add_raw<E>(acc, v[u], k0 + u < Kn && ((vmask >> (k0 + u)) & 1));
   }
-  store_row<E>(O + bt * (int64_t)Hkv * G * D + (size_t)g * G * D + (size_t)lane * E, acc);
+  store_row<E>(O + bt * (int64_t)Hkv * G * D + (size_t)g * G * D + off, acc);
 }
 
 int tile_tokens(const Dims& d) { return (d.D == 64 ? 64 : 32) / (d.G == 16 ? 2 : 1); }
@@ -610,18 +617,18 @@ static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const vo
   {
     Timed tm(HSA_KERNEL_FWD_TOKEN, s);
     const int64_t rows = (int64_t)d.B * d.L * d.Hkv;
-    auto go = [&](auto kern) {
-      kern<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(
+    auto go = [&](auto kern, int split) {
+      kern<<<dim3((unsigned)((rows * split + 3) / 4)), 256, 0, s>>>(
           (const bf16*)(ws + st.part), idx, (bf16*)O, d.L, d.Hkv, d.K, d.nC, rows);
     };
     if (d.D == 64) {
-      if (d.G == 4) go(k_fwd_tok<64, 4>);
-      else if (d.G == 8) go(k_fwd_tok<64, 8>);
-      else go(k_fwd_tok<64, 16>);
+      if (d.G == 4) go(k_fwd_tok<64, 4, 1>, 1);
+      else if (d.G == 8) go(k_fwd_tok<64, 8, 1>, 1);
+      else go(k_fwd_tok<64, 16, 2>, 2);
     } else {
-      if (d.G == 4) go(k_fwd_tok<128, 4>);
-      else if (d.G == 8) go(k_fwd_tok<128, 8>);
-      else go(k_fwd_tok<128, 16>);
+      if (d.G == 4) go(k_fwd_tok<128, 4, 1>, 1);
+      else if (d.G == 8) go(k_fwd_tok<128, 8, 2>, 2);
+      else go(k_fwd_tok<128, 16, 4>, 4);
     }
   }
   return hipGetLastError();

@@ -98,6 +98,27 @@ __device__ __forceinline__ void load_raw(const bf16* p, uint32_t (&u)[E / 2]) {
     }
   }
 }
+// The same load with the non-temporal hint, for partials that are read exactly once: the
+// token phases measured faster with it (fwd_16k forward token phase 0.270 -> 0.225 ms).
+template <int E>
+__device__ __forceinline__ void load_raw_nt(const bf16* p, uint32_t (&u)[E / 2]) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (E == 4) {
+    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    u[0] = x[0];
+    u[1] = x[1];
+  } else {
+#pragma unroll
+    for (int h = 0; h < E / 8; ++h) {
+      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 8 * h));
+      u[4 * h] = x[0];
+      u[4 * h + 1] = x[1];
+      u[4 * h + 2] = x[2];
+      u[4 * h + 3] = x[3];
+    }
+  }
+}
 template <int E>
 __device__ __forceinline__ void add_raw(float (&acc)[E], const uint32_t (&u)[E / 2], bool on) {
 #pragma unroll
