@@ -244,12 +244,12 @@ k_bwd_chunk_mfma(
     }
     // the per-edge partials are stored non-temporally: they are read once, by the token
     // phase, and measured faster that way (for the forward's partials it was slower)
-    if (qs_sel < n_here) {  // lane column = query row col: its edge's partial at d = 16*dt + 4*blk
-      bf16* dst = dq_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 4 * blk;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        __builtin_nontemporal_store(pack_bf16x4(dq[dt]), reinterpret_cast<s16x4*>(dst + 16 * dt));
-    }
+    // (regrouped across the lanes first, so that each store writes 64 contiguous bytes of a
+    // query row; all lanes take part in the swaps)
+    uint32_t u[DT][2];
+    regroup_rows_bf16<DT>(dq, u);
+    if (qs_sel < n_here)  // lane column = query row col: its edge's partial
+      store_regrouped<DT, true>(dq_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 8 * blk, u);
     wave_lds_sync();  // ql/dl/sdl reuse by the next job
   }
   // wave 1's sums meet wave 0's in LDS (dK, then dV); wave 0 stores the segment's partials
@@ -529,13 +529,13 @@ k_bwd_chunk_keys(
                               dsT, dq[j]);
       }
     }
-    if (qs_sel < n_here) {  // lane column = query row col: its edge's partial, this wave's half
-      // (stored non-temporally, as in the d = 64 chunk phase)
-      bf16* dst = dq_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 64 * wv + 4 * blk;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        __builtin_nontemporal_store(pack_bf16x4(dq[j]), reinterpret_cast<s16x4*>(dst + 16 * j));
-    }
+    // this wave's half of the edge's partial, regrouped across the lanes and stored
+    // non-temporally, as in the d = 64 chunk phase
+    uint32_t u[4][2];
+    regroup_rows_bf16<4>(dq, u);
+    if (qs_sel < n_here)  // lane column = query row col
+      store_regrouped<4, true>(dq_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 64 * wv + 8 * blk,
+                               u);
     // no barrier here: the next job restages Q and dO after the dK/dV barrier above, and
     // rewrites dS^T and the row exchange only after its own exchange barrier
   }

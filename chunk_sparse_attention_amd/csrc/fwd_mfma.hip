@@ -426,12 +426,12 @@ __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
                                          lds_read_tr4(&vl[32 * kk + 16 + trow][16 * dt + tcol])),
                               pT, o[dt]);
     }
-    if (qs_sel < n_here) {  // lane column = query row col: its edge's output at d = 16*dt + 4*blk
-      bf16* dst = o_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 4 * blk;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<s16x4*>(dst + 16 * dt) = pack_bf16x4(o[dt]);
-    }
+    // regrouped so that each store writes 64 contiguous bytes of every query row (all lanes
+    // take part in the cross-lane swaps); measured: chunk phase 1.05 -> 0.83 ms at fwd_64k
+    uint32_t u[DT][2];
+    regroup_rows_bf16<DT>(o, u);
+    if (qs_sel < n_here)  // lane column = query row col: its edge's output
+      store_regrouped<DT, false>(o_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 8 * blk, u);
     wave_lds_sync();  // pl reuse by the next job
   }
 }

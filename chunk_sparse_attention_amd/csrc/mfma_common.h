@@ -79,6 +79,53 @@ __device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p) {
       (__attribute__((address_space(3))) s16x4*)(p));
 }
 
+// Output tiles of a 16x16 MFMA with rows d and columns the 16 query rows: lane (col, blk)
+// holds d = 16 dt + 4 blk .. +3 of query row col for each of the DT tiles (DT even).  The
+// values are packed to bf16 and regrouped across the four 16-lane rows, a swap with the row
+// two away (permlane32) and then with the neighbouring row (permlane16), so that afterwards
+// lane blk holds d = 32 j + 8 blk .. +7 in u[2j] (first four) and u[2j+1] (next four): a
+// 16-byte store per j then writes 64 contiguous bytes of every query row, the four lanes of
+// the row side by side, instead of four 8-byte pieces 32 bytes apart.
+template <int DT>
+__device__ __forceinline__ void regroup_rows_bf16(const f32x4 (&o)[DT], uint32_t (&u)[DT][2]) {
+  static_assert(DT % 2 == 0, "d-tiles come in pairs");
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const uint2 pk = __builtin_bit_cast(uint2, pack_bf16x4(o[dt]));
+    u[dt][0] = pk.x;
+    u[dt][1] = pk.y;
+  }
+#pragma unroll
+  for (int i = 0; i < DT / 2; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const auto p = __builtin_amdgcn_permlane32_swap(u[2 * i][h], u[2 * i + 1][h], false, false);
+      u[2 * i][h] = p[0];
+      u[2 * i + 1][h] = p[1];
+    }
+#pragma unroll
+  for (int i = 0; i < DT / 2; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const auto p = __builtin_amdgcn_permlane16_swap(u[2 * i][h], u[2 * i + 1][h], false, false);
+      u[2 * i][h] = p[0];
+      u[2 * i + 1][h] = p[1];
+    }
+}
+// Stores the regrouped values of one query row: dst points at the row's d = 8 blk.
+template <int DT, bool NT>
+__device__ __forceinline__ void store_regrouped(bf16* dst, const uint32_t (&u)[DT][2]) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int j = 0; j < DT / 2; ++j) {
+    const u32x4 v = {u[2 * j][0], u[2 * j][1], u[2 * j + 1][0], u[2 * j + 1][1]};
+    if (NT)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + 32 * j));
+    else
+      *reinterpret_cast<u32x4*>(dst + 32 * j) = v;
+  }
+}
+
 // E consecutive bf16 values (E = 4, 8 or 16; 2E-byte aligned): raw load, fp32 accumulation,
 // and the RNE store of E fp32 values
 template <int E>
