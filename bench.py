@@ -379,7 +379,7 @@ def oracle_rates(orc, tokens: int, fn, threads: int) -> dict:
     return out
 
 
-def cpu_baseline(wl, x, wl2, x2, every: int = 16, every2: int = 64) -> dict:
+def cpu_baseline(wl, x, wl2, x2, every: int = 8, every2: int = 32) -> dict:
     """The oracle (test infrastructure, untuned) on the host cores, on bounded samples of the
     workloads: median of three runs at all threads and at one thread.
       step (fwd_16k): sequence 0, every `every`-th token: pooling of the whole sequence, then
