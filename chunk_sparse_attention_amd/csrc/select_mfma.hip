@@ -8,12 +8,13 @@
 //
 // The result is the exact one: scores are the fp64 dot products of the stored values,
 // rounded once to fp32, ranked by (score desc, chunk asc).  Only the work is reduced.
-//   1. Every candidate score is computed approximately on the matrix cores (bf16 products
-//      are exact in fp32, so the fp32 sum is off by at most E = sel * |q| * max|k| * (D+8) *
-//      2^-24 including the scale's own rounding; a factor 2 of headroom is added).
-//   2. T = the K-th largest approximate score of the token.  Every chunk of the exact top-K
-//      has an approximate score >= T - 2E: if V is the exact K-th largest score, then T <=
-//      V + E (else K chunks would score above V exactly) and each member scores >= V - E.
+//   1. Every candidate's sign(scale) * q.k, which orders the chunks as their scores do, is
+//      computed approximately on the matrix cores (bf16 products are exact in fp32, so the
+//      fp32 sum is off by at most E = |q| * max|k| * (D+8) * 2^-24; a factor 2 of headroom
+//      is added, which also covers two chunks whose scores round to the same fp32 value).
+//   2. T = the K-th largest approximate value of the token.  Every chunk of the exact top-K
+//      has an approximate value >= T - 2E: if V is the exact K-th largest value, then T <=
+//      V + E (else K chunks would lie above V exactly) and each member lies >= V - E.
 //      The four lanes of a token keep only their KP largest approximate scores, and T is
 //      taken as the K-th largest of those 4 KP values: a subset's K-th largest is at most
 //      the whole set's, so the bound still holds (a lane holding more than KP of the top-K
@@ -33,18 +34,32 @@ constexpr int kSelCap = 48;  // chunks rescored exactly per token
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Sum of squares of eight bf16 values.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum of squares of eight bf16 values (four bf16 pair dot products; only bounds use it, and
+// its rounding is far inside their headroom).
 __device__ __forceinline__ float sq8(bf16x8 v) {
   const uint4 u = __builtin_bit_cast(uint4, v);
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
-    s = fmaf(a, a, s);
-    s = fmaf(b, b, s);
+    const bf16x2 p = __builtin_bit_cast(bf16x2, w[i]);
+    s = __builtin_amdgcn_fdot2_f32_bf16(p, p, s, false);
   }
   return s;
+}
+
+// Keeps the KP largest values seen in top[] (descending): the new list is the top KP of
+// the old one and v, each entry the median of its old neighbours and v.
+template <int KP>
+__device__ __forceinline__ void keep_top(float (&top)[KP], float v) {
+  float old[KP];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) old[j] = top[j];
+  top[0] = __builtin_amdgcn_fmed3f(old[0], v, __builtin_inff());
+#pragma unroll
+  for (int j = 1; j < KP; ++j) top[j] = __builtin_amdgcn_fmed3f(old[j - 1], old[j], v);
 }
 
 // Order-preserving 32-bit image of a float (NaN never reaches it).
@@ -71,6 +86,15 @@ __device__ __forceinline__ void write_slot(uint64_t key, int k, size_t o, double
   }
 }
 
+// Value of lane j (0..3, the same in every lane) of each quad of lanes, in every lane of it.
+__device__ __forceinline__ double quad_bcast_f64(double x, int j) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const int src = (__lane_id() & ~3) | j;
+  const int lo = __builtin_amdgcn_ds_bpermute(src * 4, (int)(uint32_t)u);
+  const int hi = __builtin_amdgcn_ds_bpermute(src * 4, (int)(uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
 // Inserts key into a descending list of N keys (the smallest falls off).
 template <int N>
 __device__ __forceinline__ void insert_key(uint64_t (&tk)[N], uint64_t key) {
@@ -84,7 +108,7 @@ __device__ __forceinline__ void insert_key(uint64_t (&tk)[N], uint64_t key) {
 }
 
 template <int D, int KL, int KP>
-__global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k_select_mfma(const bf16* __restrict__ Qs,
                                                      const bf16* __restrict__ Kslc,
                                                      int32_t* __restrict__ idx,
                                                      float* __restrict__ score,
@@ -117,14 +141,23 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
   __syncthreads();
 
   // B operand: this lane's token column, 8 dimensions per k-step, read from the token's
-  // Qs row (zero past the sequence); |q|^2 over the 4 lanes
+  // Qs row (zero past the sequence); |q|^2 over the 4 lanes.  The filter works on
+  // sign(scale) * q.k, which orders the chunks as the scaled scores do: with a negative
+  // scale q enters negated (exact in bf16), and the scale's magnitude is left out.
   bf16x8 qb[KS];
   float q2 = 0.0f;
   const bf16* qrow = Qs + ((b * L + (size_t)t) * Hkv + g) * D;
+  const uint32_t qsign = sel_scale < 0.0 ? 0x80008000u : 0u;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     qb[ks] = t < L ? ld_bf16x8(qrow + 32 * ks + 8 * blk) : zero_bf16x8();
     q2 += sq8(qb[ks]);
+    uint4 u = __builtin_bit_cast(uint4, qb[ks]);
+    u.x ^= qsign;
+    u.y ^= qsign;
+    u.z ^= qsign;
+    u.w ^= qsign;
+    qb[ks] = __builtin_bit_cast(bf16x8, u);
   }
   q2 = rows4_sum(q2);
 
@@ -175,11 +208,10 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
     }
   };
 
-  // 1. the KP largest approximate scores of this lane's share (4 KP >= K), kept sorted by a
-  //    branch-free compare-exchange chain that the wave skips when no lane beats its last
-  //    entry.  Non-finite values are caught once, from |q|^2 and |k|^2, below: when every
-  //    norm is finite and sel |q| max|k| and |q| max|k| stay far below the fp32 range, no
-  //    partial sum of any approximate score can overflow (Cauchy-Schwarz)
+  // 1. the KP largest approximate values of this lane's share (4 KP >= K), kept sorted by
+  //    keep_top.  Non-finite values are caught once, from |q|^2 and |k|^2, below: when
+  //    every norm is finite and sel |q| max|k| and |q| max|k| stay far below the fp32 range,
+  //    no partial sum of any approximate score can overflow (Cauchy-Schwarz)
   static_assert(4 * KP >= KL, "the token's four lists must hold K scores");
   float top[KP];
 #pragma unroll
@@ -193,22 +225,18 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
     if (c0 + 64 < m) fetch(c0 + 64);
     f32x4 sacc[4];
     approx(sacc);
-    const bool tail = c0 + 64 > m;  // the last group: rows past m were staged as zeros
+    if (c0 + 64 <= m) {
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
+      for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = sacc[t4][i] * sel_f;
-        if (tail && c0 + 16 * t4 + 4 * blk + i >= m) v = -__builtin_inff();
-        if (__ballot(v > top[KP - 1])) {
+        for (int i = 0; i < 4; ++i) keep_top(top, sacc[t4][i]);
+    } else {  // the last group: rows past m were staged as zeros
 #pragma unroll
-          for (int j = 0; j < KP; ++j) {
-            const float hi = fmaxf(top[j], v);
-            v = fminf(top[j], v);
-            top[j] = hi;
-          }
-        }
-      }
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          keep_top(top, c0 + 16 * t4 + 4 * blk + i < m ? sacc[t4][i] : -__builtin_inff());
+    }
   }
   // max |k|^2 over every candidate chunk, and whether any was not finite: over the wave,
   // then over the block's waves
@@ -224,9 +252,16 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
   }
   __syncthreads();
   const float k2max = fmaxf(fmaxf(k2w[0], k2w[1]), fmaxf(k2w[2], k2w[3]));
-  const float qk = sqrtf(q2) * sqrtf(k2max);  // bounds |approximate score| / sel and its sums
+  const float qk = sqrtf(q2) * sqrtf(k2max);  // bounds |q.k| and its partial sums
+  // Besides non-finite values and overflow, two cases of tiny magnitudes go to the exact
+  // path: scores so small that fp32's subnormal spacing exceeds the headroom below
+  // (|scale| |q| max|k| (D+8) < 2^-125, a zero scale among them), where rounding ties
+  // chunks the filter keeps apart; and |q| max|k| < 2^-60 (its fp32 norms may underflow,
+  // and subnormal products in the approximate sums would no longer be inside the bound).
+  // A tile with no earlier chunk has nothing to rank.
   bool bad = !(q2 <= 3.0e38f) || (kbadw[0] | kbadw[1] | kbadw[2] | kbadw[3]) != 0 ||
-             !(qk < 1.0e37f) || !(fabsf(sel_f) * qk < 1.0e37f);
+             !(qk < 1.0e37f) || !(fabsf(sel_f) * qk < 1.0e37f) ||
+             (m > 0 && !(qk >= 0x1p-60f && fabsf(sel_f) * qk * (float)(D + 8) >= 0x1p-125f));
   // T = K-th largest over the token's 4 lanes (lane order breaks equal values apart)
   float T = -__builtin_inff();
   for (int k = 0; k < Kt; ++k) {
@@ -240,7 +275,8 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
     const uint32_t bo = (uint32_t)(best >> 2);
     T = __uint_as_float((bo & 0x80000000u) ? (bo ^ 0x80000000u) : ~bo);
   }
-  const float E = 2.0f * fabsf(sel_f) * qk * (float)(D + 8) * 5.9604645e-8f;
+  // the approximate values' error bound, with a factor 2 of headroom (in units of q.k)
+  const float E = 2.0f * qk * (float)(D + 8) * 5.9604645e-8f;
   bad = bad || (__float_as_uint(E) & 0x7f800000u) == 0x7f800000u;
   const float thr = T == -__builtin_inff() ? -__builtin_inff() : T - 2.0f * E;
   const uint64_t badmask = __ballot(bad);
@@ -260,7 +296,7 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = c0 + 16 * t4 + 4 * blk + i;
-        if (c < m && sacc[t4][i] * sel_f >= thr) {
+        if (c < m && sacc[t4][i] >= thr) {
           const int pos = atomicAdd(&cnt[tl], 1);
           if (pos < kSelCap) candl[tl][pos] = c;
         }
@@ -269,8 +305,9 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
   __syncthreads();
 
   // 3. exact scores of the candidates: four consecutive lanes per token, each rescoring
-  //    every fourth candidate into its own ranked list of KL >= K keys; the four lists merge
-  //    by quad maxima and the first lane writes each slot as it is ranked
+  //    every fourth candidate (two at a time, so two independent fp64 chains are in flight)
+  //    into its own ranked list of KL >= K keys; the four lists merge by quad maxima, and
+  //    lane s of the quad forms the weights of slots s, s + 4, ...
   {
     const int tj = 16 * wave + lane / 4, sub = lane % 4, tt = t0 + tj;
     const bool fb = fall[tj] || cnt[tj] > kSelCap;
@@ -279,34 +316,69 @@ __global__ void __launch_bounds__(256) k_select_mfma(const bf16* __restrict__ Qs
     uint64_t tk[KL];
 #pragma unroll
     for (int i = 0; i < KL; ++i) tk[i] = 0;
-    for (int r = sub; r < n; r += 4) {
-      const int c = candl[tj][r];
-      const bf16* kr = kbase + (size_t)c * Hkv * D;
-      double dot = 0.0;
+    for (int r = sub; r < n; r += 8) {
+      const bool two = r + 4 < n;
+      const int c1 = candl[tj][r], c2 = two ? candl[tj][r + 4] : c1;
+      const bf16* k1 = kbase + (size_t)c1 * Hkv * D;
+      const bf16* k2 = kbase + (size_t)c2 * Hkv * D;
+      double d1 = 0.0, d2 = 0.0;
 #pragma unroll 2
       for (int e = 0; e < D; e += 8) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(kr + e);
         const uint4 qv = *reinterpret_cast<const uint4*>(qr + e);
-        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, qw[4] = {qv.x, qv.y, qv.z, qv.w};
+        const uint4 kv1 = *reinterpret_cast<const uint4*>(k1 + e);
+        const uint4 kv2 = *reinterpret_cast<const uint4*>(k2 + e);
+        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+        const uint32_t kw1[4] = {kv1.x, kv1.y, kv1.z, kv1.w}, kw2[4] = {kv2.x, kv2.y, kv2.z, kv2.w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          dot = fma((double)bf16_lo(qw[h]), (double)bf16_lo(kw[h]), dot);
-          dot = fma((double)bf16_hi(qw[h]), (double)bf16_hi(kw[h]), dot);
+          const double qlo = (double)bf16_lo(qw[h]), qhi = (double)bf16_hi(qw[h]);
+          d1 = fma(qlo, (double)bf16_lo(kw1[h]), d1);
+          d2 = fma(qlo, (double)bf16_lo(kw2[h]), d2);
+          d1 = fma(qhi, (double)bf16_hi(kw1[h]), d1);
+          d2 = fma(qhi, (double)bf16_hi(kw2[h]), d2);
         }
       }
-      insert_key(tk, rank_key((float)(sel_scale * dot), c));
+      insert_key(tk, rank_key((float)(sel_scale * d1), c1));
+      if (two) insert_key(tk, rank_key((float)(sel_scale * d2), c2));
     }
-    const bool writer = sub == 0 && tt < L && !fb;  // a token without candidates: all masked
+    // K rounds of the quad maximum; every lane of the quad sees each slot's key and keeps
+    // those of its own slots
+    constexpr int NS = (KL + 3) / 4;
+    uint64_t mine[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) mine[j] = 0;
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
+      if (k < Kt) {
+        const uint64_t best = dpp_max_key<0x4E>(dpp_max_key<0xB1>(tk[0]));  // over the quad
+        if (best != 0 && tk[0] == best) {
+#pragma unroll
+          for (int i = 0; i + 1 < KL; ++i) tk[i] = tk[i + 1];
+          tk[KL - 1] = 0;
+        }
+        if ((k & 3) == sub) mine[k >> 2] = best;
+      }
+    }
+    // slot k's weight is sigmoid(s_k) times the stick left by slots < k; the sigmoids are
+    // formed in parallel, the stick passes along the quad in slot order
+    double p[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) p[j] = mine[j] ? sigmoid_d((double)key_score(mine[j])) : 0.0;
+    const bool writes = tt < L && !fb;  // a token without candidates: all masked
     const size_t o = ((b * L + tt) * Hkv + g) * Kt;
     double rem = 1.0;
-    for (int k = 0; k < Kt; ++k) {
-      const uint64_t best = dpp_max_key<0x4E>(dpp_max_key<0xB1>(tk[0]));  // over the quad
-      if (best != 0 && tk[0] == best) {
 #pragma unroll
-        for (int i = 0; i + 1 < KL; ++i) tk[i] = tk[i + 1];
-        tk[KL - 1] = 0;
+    for (int k = 0; k < KL; ++k) {
+      if (k < Kt) {
+        const double pk = quad_bcast_f64(p[k >> 2], k & 3);
+        if (writes && (k & 3) == sub) {
+          const uint64_t key = mine[k >> 2];
+          idx[o + k] = key ? key_chunk(key) : -1;
+          score[o + k] = key ? key_score(key) : -__builtin_inff();
+          w[o + k] = key ? (float)(pk * rem) : 0.0f;
+        }
+        rem *= 1.0 - pk;
       }
-      if (writer) write_slot(best, k, o, rem, idx, score, w);
     }
   }
   // tokens for the exact path over all their candidates, one token at a time per wave

@@ -224,7 +224,8 @@ def test_fold_flag(hsa, dev):
 
 
 @pytest.mark.parametrize("case", ["qs_zero", "qs_half_zero", "equal_chunks", "qs_large",
-                                  "qs_nan", "qs_inf", "k_nan", "signed_zero", "negative_scale"])
+                                  "qs_nan", "qs_inf", "k_nan", "signed_zero", "negative_scale",
+                                  "tiny_scale"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_select_degenerate(hsa, dev, case, d):
     """Exact ties, extreme magnitudes and values that are not ordinary numbers: the ranking
@@ -258,8 +259,9 @@ def test_select_degenerate(hsa, dev, case, d):
     elif case == "signed_zero":  # rows whose every score rounds to +0 or -0 in fp32
         Qs[0, 500:4000:13, :, :] = 0
         Qs[0, 500:4000:13, :, 0] = 2.0 ** -133
-    # a negative selection scale reverses the ranking (the filter's bound takes |scale|)
-    sel = {"signed_zero": 2.0 ** -20, "negative_scale": -0.125}.get(case)
+    # a negative selection scale reverses the ranking (the filter's bound takes |scale|);
+    # a tiny one makes every score subnormal in fp32, where rounding ties many chunks
+    sel = {"signed_zero": 2.0 ** -20, "negative_scale": -0.125, "tiny_scale": 2.0 ** -140}.get(case)
     Kslc, idx, score, w = hsa.select(Qs.to(dev), K.to(dev), wl.K, sel_scale=sel)
     torch.cuda.synchronize()
     orc = oracle.get()
