@@ -21,6 +21,7 @@
 
 #include "hsa_common.h"
 #include "hsa_launch.h"
+#include "mfma_common.h"
 #include "tile_common.h"
 
 namespace hsa {
@@ -118,32 +119,62 @@ k_dec_scan_fast(const T* __restrict__ qs, const T* __restrict__ Kslc,
         for (int e = 0; e < 8; ++e) dot[i] = fma(qv[e], (double)row[i].get(e0 + e), dot[i]);
     }
   }
-  uint64_t key[kScanPer];
+  static_assert(kScanPer == 1 && kScanWaves <= kWave && kScanWaves >= kMaxK,
+                "one chunk per lane; the wave maxima fill one wave and bound every K");
+  const uint64_t key = cs[0] < nCb ? rank_key((float)(sel_scale * dot[0]), cs[0]) : 0;
+  uint64_t* out = cand + ((size_t)bg * n_blocks + blk) * K;
+  // The block's top-K all have a score (the key's upper half, 0 = no chunk) of at least
+  // thr, the K-th largest of the waves' maximum scores: those are the scores of K keys of
+  // the block.  Usually only about K keys do; they are gathered, and each one's rank is the
+  // number of gathered keys above it (keys are distinct apart from 0).
+  __shared__ uint32_t wmax[kScanWaves];
+  __shared__ uint64_t clist[kWave];
+  __shared__ int ccount;
+  const uint32_t sc = (uint32_t)(key >> 32);
+  const uint32_t mw = wave_max_u32(sc);
+  if (lane == 0) wmax[wave] = mw;
+  if (tid == 0) ccount = 0;
+  __syncthreads();
+  uint32_t thr;
+  {
+    const uint32_t mine = lane < kScanWaves ? wmax[lane] : 0;
+    int n_ge = 0;  // wave maxima at or above this lane's
 #pragma unroll
-  for (int i = 0; i < kScanPer; ++i)
-    key[i] = cs[i] < nCb ? rank_key((float)(sel_scale * dot[i]), cs[i]) : 0;
-  // lane-local descending order, then K rounds of a wave maximum over the lane heads
-#pragma unroll
-  for (int i = 0; i < kScanPer; ++i)
-#pragma unroll
-    for (int j = i + 1; j < kScanPer; ++j)
-      if (key[j] > key[i]) {
-        const uint64_t t = key[i];
-        key[i] = key[j];
-        key[j] = t;
-      }
-  __shared__ uint64_t wtop[kScanWaves][kMaxK];
-  for (int k = 0; k < K; ++k) {
-    const uint64_t best = wave_max_key(key[0]);
-    if (best != 0 && key[0] == best) {
-#pragma unroll
-      for (int i = 0; i + 1 < kScanPer; ++i) key[i] = key[i + 1];
-      key[kScanPer - 1] = 0;
+    for (int j = 0; j < kScanWaves; ++j) n_ge += wmax[j] >= mine ? 1 : 0;
+    thr = wave_max_u32(n_ge >= K ? mine : 0);
+  }
+  const bool is_c = key != 0 && sc >= thr;
+  const uint64_t bal = __ballot(is_c);
+  int base = 0;
+  if (lane == 0 && bal) base = atomicAdd(&ccount, __popcll(bal));
+  base = __shfl(base, 0);
+  const int pos = base + __popcll(bal & ((1ull << lane) - 1));
+  if (is_c && pos < kWave) clist[pos] = key;
+  __syncthreads();
+  const int nc = ccount;  // uniform
+  if (nc <= kWave) {
+    if (wave == 0) {
+      const uint64_t v = lane < nc ? clist[lane] : 0;
+      int r = 0;
+      for (int j = 0; j < nc; ++j) r += clist[j] > v ? 1 : 0;
+      if (lane < nc && r < K) out[r] = v;
+      if (lane >= nc && lane < K) out[lane] = 0;  // fewer chunks than K: masked slots
     }
-    if (lane == 0) wtop[wave][k] = best;
+    return;
+  }
+  // many keys at thr or above (equal scores): K rounds of a wave
+  // maximum in every wave, then the block's ranked top-K from the waves' lists (at most
+  // 16 x 16 keys, four per lane)
+  __shared__ uint64_t wtop[kScanWaves][kMaxK];
+  {
+    uint64_t v = key;
+    for (int k = 0; k < K; ++k) {
+      const uint64_t best = wave_max_key(v);
+      if (best != 0 && v == best) v = 0;
+      if (lane == 0) wtop[wave][k] = best;
+    }
   }
   __syncthreads();
-  // the block's ranked top-K from the waves' lists (at most 16 * 16 keys: four per lane)
   if (wave == 0) {
     uint64_t v[4];
 #pragma unroll
@@ -160,7 +191,6 @@ k_dec_scan_fast(const T* __restrict__ qs, const T* __restrict__ Kslc,
           v[i] = v[j];
           v[j] = t;
         }
-    uint64_t* out = cand + ((size_t)bg * n_blocks + blk) * K;
     for (int k = 0; k < K; ++k) {
       const uint64_t best = wave_max_key(v[0]);
       if (best != 0 && v[0] == best) {
@@ -177,9 +207,42 @@ k_dec_scan_fast(const T* __restrict__ qs, const T* __restrict__ Kslc,
 __device__ __forceinline__ float wave_sum_f(float v) { return rows4_sum(row16_sum(v)); }
 __device__ __forceinline__ float wave_max_f(float v) { return rows4_max(row16_max(v)); }
 
-// Ranked top-K of the scan's candidates in every wave; lane k < K returns slot k's key.
+// Ranked top-K of the scan's candidates (n_cand / K ranked lists of K keys, one per scan
+// block) in every wave; lane k < K returns slot k's key.  lds: kWave + K keys of LDS that
+// only this wave uses.
+//   The top-K all score at least thr, the K-th largest of the lists' first scores (those
+//   are K of the keys).  Usually only about K keys do: they are gathered, and each one's
+//   slot is the number of gathered keys above it (keys are distinct apart from 0).
 __device__ __forceinline__ uint64_t rank_candidates(const uint64_t* __restrict__ cb, int n_cand,
-                                                    int K, int lane) {
+                                                    int K, int lane, uint64_t* lds) {
+  const int nl = n_cand / K;
+  if (nl <= kWave) {
+    const uint32_t mine = lane < nl ? (uint32_t)(cb[lane * K] >> 32) : 0;
+    int n_ge = 0;  // lists whose first score is at least this lane's
+    for (int j = 0; j < nl; ++j) n_ge += (uint32_t)(cb[j * K] >> 32) >= mine ? 1 : 0;
+    const uint32_t thr = wave_max_u32(n_ge >= K ? mine : 0);
+    int nc = 0;
+    for (int i0 = 0; i0 < n_cand; i0 += kWave) {
+      const int i = i0 + lane;
+      const uint64_t k = i < n_cand ? cb[i] : 0;
+      const bool c = k != 0 && (uint32_t)(k >> 32) >= thr;
+      const uint64_t bal = __ballot(c);
+      const int pos = nc + __popcll(bal & ((1ull << lane) - 1));
+      if (c && pos < kWave) lds[pos] = k;
+      nc += __popcll(bal);
+    }
+    if (nc <= kWave) {
+      wave_lds_sync();
+      const uint64_t v = lane < nc ? lds[lane] : 0;
+      int r = 0;
+      for (int j = 0; j < nc; ++j) r += lds[j] > v ? 1 : 0;
+      if (lane < nc && r < K) lds[kWave + r] = v;
+      if (lane >= nc && lane < K) lds[kWave + lane] = 0;  // fewer keys than K: masked slots
+      wave_lds_sync();
+      return lane < K ? lds[kWave + lane] : 0;
+    }
+  }
+  // many keys at thr or above (equal scores): K rounds of a wave maximum
   uint64_t mykey = 0;
   if (n_cand <= 2 * kWave) {
     // at most two keys per lane: a sorted pair
@@ -232,6 +295,7 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
   __shared__ float qsh[ZH][D];
   __shared__ float ash[NS][ZH][kChunk];
   __shared__ float osh[NS][ZH][D];
+  __shared__ uint64_t rk[NS][kWave + kMaxK];  // each wave's candidate ranking
   const int tid = threadIdx.x, lane = tid % kWave, slot = tid / kWave;
   const int hg = blockIdx.x % n_hg, bg = blockIdx.x / n_hg;
   // layer blockIdx.y of a stack of layers that share one selection (strides 0 otherwise)
@@ -257,7 +321,7 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
     }
   } else {
     const uint64_t mykey =
-        n_cand > 0 ? rank_candidates(cand + (size_t)bg * n_cand, n_cand, K, lane) : 0;
+        n_cand > 0 ? rank_candidates(cand + (size_t)bg * n_cand, n_cand, K, lane, rk[slot]) : 0;
     if (softmax_w) {
       // softmax of the valid slots' scores (lanes 0..K-1), shifted by their maximum and
       // summed in slot order

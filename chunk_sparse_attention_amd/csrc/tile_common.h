@@ -438,6 +438,26 @@ __device__ __forceinline__ float rows4_max(float v) {
   return fmaxf(a, b);
 }
 
+// Maximum of unsigned values over the whole wave, in every lane (0 is the identity).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dppu<0xB1>(v));
+  v = max(v, dppu<0x4E>(v));
+  v = max(v, dppu<0x141>(v));
+  v = max(v, dppu<0x140>(v));
+  auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  unsigned p0 = p[0], p1 = p[1];
+  asm volatile("" : "+v"(p0), "+v"(p1));
+  v = max(p0, p1);
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  unsigned r0 = r[0], r1 = r[1];
+  asm volatile("" : "+v"(r0), "+v"(r1));
+  return max(r0, r1);
+}
+
 // ---- 64-bit rank keys across lanes ---------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ uint64_t dpp_max_key(uint64_t v) {
