@@ -226,41 +226,50 @@ __global__ void __launch_bounds__(1024) k_inv_order(const int32_t* __restrict__ 
   for (int s = threadIdx.x; s < ns; s += blockDim.x) order[atomicAdd(&hist[bucket(s)], 1)] = s;
 }
 
-// Per (b, g, tile), one wave: walk the tile's tokens in order; lane k places slot k.  The
-// tile's selections are first staged in LDS, 256 tokens at a time, so the serial walk waits on
-// LDS only.  A chunk's entries from this tile start at offsets[c] + the tile's prefix for c.
-// A selection from hsa_select never repeats a chunk within a row, but a caller's may: such
-// slots are given consecutive entries in slot order (rank r among the row's equal slots goes
-// to the counter's value + r, and the first of them advances the counter past all), which is
-// the count k_inv_count made for them, so every entry is written exactly once.
+// Per (b, g, tile): place the tile's entries, a chunk's entries in token order from
+// offsets[c] + the tile's prefix for c.
+//   Bitmap path (W > 0: the tile's tokens fit W 64-bit words, and the block's LDS holds a
+//   word row per chunk): each chunk's row marks the tile's tokens that chose it, and an
+//   entry's place among the chunk's entries of the tile is the number of marked tokens before
+//   its own, so every entry is placed in parallel.  This needs each row's chunks distinct.
+//   Walk path (W = 0, or a row that repeats a chunk): wave 0 walks the tile's tokens in order
+//   and lane k places slot k.  A selection from hsa_select never repeats a chunk within a
+//   row, but a caller's may: such slots are given consecutive entries in slot order (rank r
+//   among the row's equal slots goes to the counter's value + r, and the first of them
+//   advances the counter past all), which is the count k_inv_count made for them, so every
+//   entry is written exactly once.
+// Tokens are staged in LDS kScatterBatch at a time (the bitmap path takes the whole tile:
+// W * 64 <= kScatterBatch).
 constexpr int kScatterBatch = 256;
-__global__ void __launch_bounds__(64) k_inv_scatter(const int32_t* __restrict__ idx,
-                                                    const int32_t* __restrict__ tile_prefix,
-                                                    const int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ entries, int L,
-                                                    int Hkv, int K, int nC, int tile_tokens,
-                                                    int n_tiles) {
-  extern __shared__ int32_t cnt[];
+constexpr int kScatterThreads = 256;
+__global__ void __launch_bounds__(kScatterThreads) k_inv_scatter(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ tile_prefix,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ entries, int L, int Hkv, int K,
+    int nC, int tile_tokens, int n_tiles, int W) {
+  extern __shared__ int32_t cnt[];  // nC counters, then (bitmap path) nC * W mask words
   __shared__ int32_t sel[kScatterBatch * kMaxK];
   __shared__ uint16_t dup[kScatterBatch * kMaxK];  // rank among equal slots | their number << 8
   const int tile = blockIdx.x % n_tiles;
   const int bg = blockIdx.x / n_tiles;
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid % kWave;
   const int32_t* tp = tile_prefix + (size_t)bg * nC * n_tiles + tile;
   const int32_t* off = offsets + (size_t)bg * (nC + 1);
-  for (int c = lane; c < nC; c += kWave) cnt[c] = off[c] + tp[(size_t)c * n_tiles];
+  unsigned long long* mask = reinterpret_cast<unsigned long long*>(cnt + ((nC + 1) & ~1));
+  for (int c = tid; c < nC; c += kScatterThreads) cnt[c] = off[c] + tp[(size_t)c * n_tiles];
+  for (int i = tid; i < nC * W; i += kScatterThreads) mask[i] = 0;
   int32_t* ent = entries + (size_t)bg * L * K;
   const int t0 = tile * tile_tokens;
   const int t1 = min(L, t0 + tile_tokens);
   for (int tb0 = t0; tb0 < t1; tb0 += kScatterBatch) {
     const int nt = min(kScatterBatch, t1 - tb0);
     __syncthreads();
-    for (int i = lane; i < nt * K; i += kWave)
+    for (int i = tid; i < nt * K; i += kScatterThreads)
       sel[i] = idx[((b * L + tb0 + i / K) * Hkv + g) * K + i % K];
     __syncthreads();
-    for (int tt = lane; tt < nt; tt += kWave) {  // one token per lane: its slots' repeats
+    bool rep = false;  // some row of the batch repeats a chunk
+    for (int tt = tid; tt < nt; tt += kScatterThreads) {  // one token per thread
       int cv[kMaxK];
 #pragma unroll
       for (int j = 0; j < kMaxK; ++j) cv[j] = j < K ? sel[tt * K + j] : 0;
@@ -275,18 +284,41 @@ __global__ void __launch_bounds__(64) k_inv_scatter(const int32_t* __restrict__ 
             n += eq ? 1 : 0;
           }
           dup[tt * K + k] = (uint16_t)(rank | (n << 8));
+          rep = rep || (n > 1 && cv[k] >= 0 && cv[k] < nC);
         }
       }
     }
-    __syncthreads();
-    for (int tt = 0; tt < nt; ++tt) {
-      if (lane < K) {
-        const int c = sel[tt * K + lane];
+    if (!__syncthreads_or(rep) && W > 0) {
+      for (int i = tid; i < nt * K; i += kScatterThreads) {
+        const int c = sel[i];
         if (c >= 0 && c < nC) {
-          const int r = dup[tt * K + lane];
-          const int pos = cnt[c] + (r & 0xff);  // every lane reads before any lane writes
-          if ((r & 0xff) == 0) cnt[c] = pos + (r >> 8);
-          ent[pos] = (tb0 + tt) * K + lane;
+          const int tt = i / K;
+          atomicOr(&mask[c * W + tt / 64], 1ull << (tt % 64));
+        }
+      }
+      __syncthreads();
+      for (int i = tid; i < nt * K; i += kScatterThreads) {
+        const int c = sel[i];
+        if (c >= 0 && c < nC) {
+          const int tt = i / K;
+          const unsigned long long* m = mask + c * W;
+          int r = __popcll(m[tt / 64] & ((1ull << (tt % 64)) - 1));
+          for (int w = 0; w < tt / 64; ++w) r += __popcll(m[w]);
+          ent[cnt[c] + r] = (tb0 + tt) * K + i % K;
+        }
+      }
+      continue;  // W * 64 >= tile_tokens: this was the tile's only batch
+    }
+    if (tid < kWave) {
+      for (int tt = 0; tt < nt; ++tt) {
+        if (lane < K) {
+          const int c = sel[tt * K + lane];
+          if (c >= 0 && c < nC) {
+            const int r = dup[tt * K + lane];
+            const int pos = cnt[c] + (r & 0xff);  // every lane reads before any lane writes
+            if ((r & 0xff) == 0) cnt[c] = pos + (r >> 8);
+            ent[pos] = (tb0 + tt) * K + lane;
+          }
         }
       }
     }
@@ -310,10 +342,13 @@ hipError_t launch_invidx(const Dims& d, const IndexLayout& lay, const int32_t* i
                                        (int32_t*)(ws + lay.seg_start),
                                        (int32_t*)(ws + lay.seg_chunk),
                                        (int32_t*)(ws + lay.n_seg), d.nC, lay.max_seg);
-  k_inv_scatter<<<dim3(bg * lay.n_tiles), 64, lds, s>>>(idx, tc, (const int32_t*)(ws + lay.offsets),
-                                                         (int32_t*)(ws + lay.entries), d.L,
-                                                         d.Hkv, d.K, d.nC, lay.tile_tokens,
-                                                         lay.n_tiles);
+  // the bitmap path when the tile's tokens fit four words and the masks 48 KB of LDS
+  const int W = (lay.tile_tokens + 63) / 64;
+  const size_t lds_bm = sizeof(int32_t) * ((d.nC + 1) & ~1) + sizeof(uint64_t) * (size_t)d.nC * W;
+  const bool bm = W <= 4 && W * 64 <= kScatterBatch && lds_bm <= 48 * 1024;
+  k_inv_scatter<<<dim3(bg * lay.n_tiles), kScatterThreads, bm ? lds_bm : lds, s>>>(
+      idx, tc, (const int32_t*)(ws + lay.offsets), (int32_t*)(ws + lay.entries), d.L, d.Hkv,
+      d.K, d.nC, lay.tile_tokens, lay.n_tiles, bm ? W : 0);
   k_inv_order<<<dim3(bg), 1024, 0, s>>>((const int32_t*)(ws + lay.offsets),
                                         (const int32_t*)(ws + lay.seg_start),
                                         (const int32_t*)(ws + lay.seg_chunk),

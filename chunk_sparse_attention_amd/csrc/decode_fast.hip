@@ -433,6 +433,7 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
       const int j = jg + JG * i;
 #pragma unroll
       for (int h = 0; h < ZH; ++h) {
+        if (h >= nh) continue;
         const float aw = ash[slot][h][j];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(aw, vp[i].get(e), acc[h][e]);
@@ -443,6 +444,7 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
     for (int h = 0; h < ZH; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
+        if (h >= nh) continue;
         float sum = acc[h][e];
         if (P == 8) sum += dppc<0x128>(sum);  // row_ror:8 pairs lanes l and l^8 in a row
         acc[h][e] = rows4_sum(sum);
@@ -499,6 +501,7 @@ static void launch_dec_fast_t(const Dims& d, const void* q, const void* qs, cons
   constexpr int ZW = 8;  // heads per block for host caches, up to 8 slots
   if (d.K > 8) go(k_dec_attend_heads<T, D, 4, 1024>, 4);
   else if (host_kv) go(k_dec_attend_heads<T, D, ZW, 512>, ZW);
+  else if ((d.G + 3) / 4 <= 2) go(k_dec_attend_heads<T, D, 2, 512>, 2);
   else go(k_dec_attend_heads<T, D, 4, 512>, 4);
 }
 
@@ -523,6 +526,7 @@ static void launch_dec_shared_t(const Dims& d, int n_layers, const void* q, cons
   };
   if (d.K > 8) go(k_dec_attend_heads<T, D, 4, 1024>, 4);
   else if (host_kv) go(k_dec_attend_heads<T, D, 8, 512>, 8);
+  else if ((d.G + 3) / 4 <= 2) go(k_dec_attend_heads<T, D, 2, 512>, 2);
   else go(k_dec_attend_heads<T, D, 4, 512>, 4);
 }
 
