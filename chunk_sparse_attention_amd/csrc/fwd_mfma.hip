@@ -427,11 +427,13 @@ __global__ void __launch_bounds__(64 * NW) k_fwd_chunk(
                               pT, o[dt]);
     }
     // regrouped so that each store writes 64 contiguous bytes of every query row (all lanes
-    // take part in the cross-lane swaps); measured: chunk phase 1.05 -> 0.83 ms at fwd_64k
+    // take part in the cross-lane swaps); measured: chunk phase 1.05 -> 0.83 ms at fwd_64k.
+    // At D = 128 the partials are stored non-temporally: the chunk phase loses less than the
+    // token phase that reads them gains (at D = 64 the two even out).
     uint32_t u[DT][2];
     regroup_rows_bf16<DT>(o, u);
     if (qs_sel < n_here)  // lane column = query row col: its edge's output
-      store_regrouped<DT, false>(o_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 8 * blk, u);
+      store_regrouped<DT, D == 128>(o_part + (eo_l[ej + qs_sel] * G + qs_head) * D + 8 * blk, u);
     wave_lds_sync();  // pl reuse by the next job
   }
 }
