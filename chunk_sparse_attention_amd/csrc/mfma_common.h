@@ -53,8 +53,16 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+// Four fp32 values to bf16 (RNE), as two pair conversions: written per pair, the compiler
+// keeps one v_cvt_pk_bf16_f32 per pair where the whole-vector form was sometimes split into
+// four single conversions and two permutes.
 __device__ __forceinline__ s16x4 pack_bf16x4(f32x4 v) {
-  return __builtin_bit_cast(s16x4, __builtin_convertvector(v, bf16x4));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 lo = __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
+  const uint2 u = {__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+  return __builtin_bit_cast(s16x4, u);
 }
 // Orders this wave's earlier LDS accesses before its later ones that touch other lanes' data
 // (the LDS serves one wave's instructions in order; the wait and the compiler barrier keep
