@@ -332,6 +332,45 @@ def test_decode_nonfinite_scores(hsa, dev, generic):
     assert np.all(npy(O)[1, :8] == 0)
 
 
+@pytest.mark.parametrize("k", [8, 16])
+@pytest.mark.parametrize("case", ["nan_query", "equal_chunks"])
+def test_decode_ties(hsa, dev, case, k):
+    """Decode where many chunks tie (a NaN selection query ranks every chunk as -inf; equal
+    chunk keys give every chunk the same score): more tied keys than one wave holds reach
+    both the scan blocks' and the merge's ranking, which must still give the oracle's
+    ranks (ties to the lower chunk index) bit for bit."""
+    ctx = 64 * 5200 + 7  # six scan blocks of 1024 chunks
+    wl = W("decode_ties", 2, ctx, 16, 2, 64, 64, k, torch.bfloat16)
+    say("case decode ties", case, k)
+    x = workloads.make_decode_inputs(wl, seed=13, ctx=ctx)
+    qs, Kc = x["qs"].clone(), x["Kc"].clone()
+    if case == "nan_query":
+        qs[0, 1, :] = float("nan")
+        qs[1, 0, 3] = float("nan")
+    else:
+        nC = ctx // 64
+        Kc[1, :nC * 64] = Kc[1, :64].repeat(nC, 1, 1)
+    q, Vc = x["q"].to(dev), x["Vc"].to(dev)
+    Kd = Kc.to(dev)
+    Kslc = hsa.pool(Kd)
+    O, idx, score, w = hsa.decode(q, qs.to(dev), Kd, Vc, Kslc, wl.K)
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    ks = orc.pool(Kc, 64)
+    d = orc.decode(x["q"], qs, Kc, x["Vc"], ks, 64, wl.K)
+    if case == "nan_query":
+        assert list(d["idx"][0, 1]) == list(range(k))
+    else:
+        assert np.array_equal(d["idx"][1], np.tile(np.arange(k), (2, 1)))
+    assert np.array_equal(npy(idx), d["idx"])
+    sc = npy(score)
+    fin = np.isfinite(d["score"])
+    assert np.array_equal(sc[~fin], d["score"][~fin])
+    assert np.array_equal(sc[fin].astype(np.float32), d["score"][fin].astype(np.float32))
+    assert max_abs(npy(w), d["w"]) <= 1e-5
+    assert max_abs(npy(O), d["O"]) <= 2e-2
+
+
 SOFTMAX_CASES = [w for w in SMALL if w.name in ("tiny_fp32", "bf16_d64_ragged", "bf16_d128_ragged",
                                                "bf16_g1_k3", "fp32_k1", "bf16_d64_g16_k16")]
 
