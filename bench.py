@@ -18,8 +18,9 @@ the HIP events libhsa.so records around each of its launches on the launch's own
 algorithmic bytes and flops per launch are the workload's, from kernel_counts().  "kernels"
 holds the same for every kernel class, "softmax_weights" the step with the softmax chunk
 weights (HSA_FLAG_SOFTMAX_WEIGHTS), "secondary" the select+fwd+bwd pass of the L=65536,
-d=128 workload (tokens/s of the whole pass and of select+fwd), "decode" the 1M-context decode
-step.  cpu_baseline times the CPU oracle (test
+d=128 workload (tokens/s of the whole pass and of select+fwd), "backward_b2" the same pass of
+the B=2, L=16384, d=64 backward workload (its hsa_bwd time and tokens/s), "decode" the
+1M-context decode step.  cpu_baseline times the CPU oracle (test
 infrastructure) on the same workload; it is a reported baseline, not the target.
 """
 from __future__ import annotations
@@ -312,9 +313,17 @@ def summarize_counters(cdir: str, workload: str, copy_mib: int) -> int:
 
 
 def summarize_trace(tdir: str, bench_json: str) -> int:
-    """Markdown table of a rocprofv3 --kernel-trace --stats run (run_kernel_stats.csv under
-    tdir) beside the per-launch averages the bench's own HIP-event timer printed."""
+    """Markdown tables of a rocprofv3 --kernel-trace --stats run under tdir: the per-kernel
+    statistics (run_kernel_stats.csv), the same split by launch grid (run_kernel_trace.csv;
+    one workload's launches share a grid), and the per-launch averages the bench's own
+    HIP-event timer printed beside those of the launch grid with the most calls (the bench
+    step's: it runs more steps than any other leg)."""
+    import collections
     import csv
+
+    def short(n):
+        return re.sub(r"\(.*", "", n).replace("void ", "").strip()
+
     files = glob.glob(os.path.join(tdir, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         log(f"bench: no kernel_stats.csv under {tdir}")
@@ -322,22 +331,40 @@ def summarize_trace(tdir: str, bench_json: str) -> int:
     rows = list(csv.DictReader(open(files[0])))
     print("| kernel | calls | avg µs | min µs | max µs | % of GPU time |")
     print("|---|---:|---:|---:|---:|---:|")
-    by_cls = {}
     for r in rows:
-        name = re.sub(r"\(.*", "", r["Name"]).replace("void ", "").strip()
-        calls = int(r["Calls"])
-        avg = float(r["AverageNs"]) / 1e3
-        print(f"| `{name[:90]}` | {calls} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+        print(f"| `{short(r['Name'])[:90]}` | {int(r['Calls'])} | "
+              f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
               f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
-        cls, _ = kernel_class(r["Name"])
-        if cls:
-            by_cls.setdefault(cls, []).append(f"`{name}` {avg / 1e3:.4f}")
+    tfiles = glob.glob(os.path.join(tdir, "**", "*kernel_trace.csv"), recursive=True)
+    shapes = collections.defaultdict(list)
+    if tfiles:
+        for r in csv.DictReader(open(tfiles[0])):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            shapes[(short(r["Kernel_Name"]), grid)].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print("\n| kernel (library kernels) | grid (work-items) | calls | avg µs | min µs | max µs |")
+        print("|---|---:|---:|---:|---:|---:|")
+        for (name, grid), d in sorted(shapes.items()):
+            if kernel_class(name)[0] is None:
+                continue
+            print(f"| `{name[:90]}` | {grid} | {len(d)} | {sum(d) / len(d):.1f} | "
+                  f"{min(d):.1f} | {max(d):.1f} |")
+    by_cls = {}
+    for (name, grid), d in shapes.items():
+        cls, _ = kernel_class(name)
+        if cls is None:
+            continue
+        best = by_cls.setdefault(cls, {})
+        if name not in best or len(d) > best[name][0]:
+            best[name] = (len(d), grid, sum(d) / len(d))
     with open(bench_json) as fh:
         b = json.loads(fh.read().strip().splitlines()[-1])
-    print("\n| kernel class | bench.py avg ms per launch | rocprofv3 avg ms per kernel |")
+    print("\n| kernel class | bench.py avg ms per launch | rocprofv3 avg ms per kernel (grid, calls) |")
     print("|---|---:|---|")
     for cls, k in sorted(b["kernels"].items(), key=lambda kv: -kv[1]["ms_per_step"]):
-        print(f"| {cls} | {k['avg_ms']:.4f} | {'; '.join(by_cls.get(cls, []))} |")
+        cell = "; ".join(f"`{n}` {avg / 1e3:.4f} ({grid}, {c})"
+                         for n, (c, grid, avg) in sorted(by_cls.get(cls, {}).items()))
+        print(f"| {cls} | {k['avg_ms']:.4f} | {cell} |")
     return 0
 
 
@@ -599,6 +626,67 @@ def run_decode(hsa, _lib, workloads, dev, gen: bool, reps: int, cpu: bool = Fals
             "shared_selection": {"workload": f"{nl} layers, B={wl4.B} ctx={ctx4} Hq={wl4.Hq} "
                                              f"Hkv={wl4.Hkv} d={wl4.D} K={wl4.K}", **lay},
             "cpu_baseline": cpu_dec}
+
+
+def run_pass(hsa, _lib, workloads, dev, gen: bool, name: str, reps: int) -> dict:
+    """One select+fwd+bwd pass over another workload, timed per entry point with events on the
+    current stream and per kernel class with the library's launch timer (average over reps
+    passes after two untimed ones)."""
+    import torch
+    wl2 = workloads.WORKLOADS[name]
+    log(f"bench: {wl2.name} select+fwd+bwd")
+    x2 = workloads.make_inputs(wl2, seed=0)
+    Q2, K2, V2, Qs2, dO2 = (x2[k].to(dev) for k in ("Q", "K", "V", "Qs", "dO"))
+    del x2
+    prob2 = hsa.problem(wl2.B, wl2.L, wl2.Hq, wl2.Hkv, wl2.D, wl2.K, wl2.dtype, generic=gen)
+    ws2 = hsa.workspace(_lib.HSA_OP_BWD, prob2, dev)
+    O2 = torch.empty_like(Q2)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step2():
+        Kslc2, i2, sc2, w2 = hsa.select(Qs2, K2, wl2.K, generic=gen)
+        e[1].record()
+        hsa.fwd(Q2, K2, V2, i2, w2, generic=gen, ws=ws2, out=O2)
+        e[2].record()
+        hsa.bwd(Q2, K2, V2, Qs2, Kslc2, i2, sc2, w2, dO2, generic=gen, ws=ws2,
+                after_fwd=True)
+        return i2
+
+    for _ in range(2):
+        i2 = step2()
+    torch.cuda.synchronize()
+    n2 = int((i2 >= 0).sum().item())
+    ts, tf, tb = 0.0, 0.0, 0.0
+    hsa.timer_enable(True)
+    for _ in range(reps):
+        e[0].record()
+        step2()
+        e[3].record()
+        torch.cuda.synchronize()
+        ts += e[0].elapsed_time(e[1])
+        tf += e[1].elapsed_time(e[2])
+        tb += e[2].elapsed_time(e[3])
+    hsa.timer_enable(False)
+    kt2 = hsa.timer_read()
+    ts /= reps
+    tf /= reps
+    tb /= reps
+    c2 = kernel_counts(wl2, n2, fused_backward(wl2, gen), chunked_forward(wl2, gen),
+                       mfma_select(wl2, gen))
+    k2 = {k: roofline(k, c2[k], total / n, measured_traffic(wl2.name, k))
+          for k, (n, total) in kt2.items() if n}
+    tokens = wl2.B * wl2.L
+    r = {
+        "workload": f"{wl2.name}: select+fwd+bwd B={wl2.B} L={wl2.L} Hq={wl2.Hq} "
+                    f"Hkv={wl2.Hkv} d={wl2.D} K={wl2.K}",
+        "select_ms": round(ts, 4), "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4),
+        "tokens_per_s": round(tokens / ((ts + tf + tb) / 1e3), 1),
+        "fwd_tokens_per_s": round(tokens / ((ts + tf) / 1e3), 1),
+        "bwd_tokens_per_s": round(tokens / (tb / 1e3), 1),
+        "kernels": k2,
+    }
+    del Q2, K2, V2, Qs2, dO2, O2, ws2
+    return r
 
 
 def copy_reference(dev, mib: int) -> None:
@@ -895,57 +983,12 @@ def main() -> int:
     }
 
     if not args.no_secondary:
-        wl2 = workloads.WORKLOADS["fwd_64k"]
-        log(f"bench: secondary {wl2.name} select+fwd+bwd")
-        x2 = workloads.make_inputs(wl2, seed=0)
-        Q2, K2, V2, Qs2, dO2 = (x2[k].to(dev) for k in ("Q", "K", "V", "Qs", "dO"))
-        prob2 = hsa.problem(wl2.B, wl2.L, wl2.Hq, wl2.Hkv, wl2.D, wl2.K, wl2.dtype, generic=gen)
-        ws2 = hsa.workspace(_lib.HSA_OP_BWD, prob2, dev)
-        O2 = torch.empty_like(Q2)
-
-        def step2():
-            Kslc2, i2, sc2, w2 = hsa.select(Qs2, K2, wl2.K, generic=gen)
-            e[1].record()
-            hsa.fwd(Q2, K2, V2, i2, w2, generic=gen, ws=ws2, out=O2)
-            e[2].record()
-            hsa.bwd(Q2, K2, V2, Qs2, Kslc2, i2, sc2, w2, dO2, generic=gen, ws=ws2,
-                    after_fwd=True)
-            return i2
-
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        for _ in range(2):
-            i2 = step2()
-        torch.cuda.synchronize()
-        n2 = int((i2 >= 0).sum().item())
-        reps = max(3, args.steps // 4)
-        ts, tf, tb = 0.0, 0.0, 0.0
-        hsa.timer_enable(True)
-        for _ in range(reps):
-            e[0].record()
-            step2()
-            e[3].record()
-            torch.cuda.synchronize()
-            ts += e[0].elapsed_time(e[1])
-            tf += e[1].elapsed_time(e[2])
-            tb += e[2].elapsed_time(e[3])
-        hsa.timer_enable(False)
-        kt2 = hsa.timer_read()
-        ts /= reps
-        tf /= reps
-        tb /= reps
-        c2 = kernel_counts(wl2, n2, fused_backward(wl2, gen), chunked_forward(wl2, gen),
-                           mfma_select(wl2, gen))
-        k2 = {name: roofline(name, c2[name], total / n, measured_traffic(wl2.name, name))
-              for name, (n, total) in kt2.items() if n}
-        out["secondary"] = {
-            "workload": f"{wl2.name}: select+fwd+bwd B={wl2.B} L={wl2.L} Hq={wl2.Hq} "
-                        f"Hkv={wl2.Hkv} d={wl2.D} K={wl2.K}",
-            "select_ms": round(ts, 4), "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4),
-            "tokens_per_s": round(wl2.B * wl2.L / ((ts + tf + tb) / 1e3), 1),
-            "fwd_tokens_per_s": round(wl2.B * wl2.L / ((ts + tf) / 1e3), 1),
-            "kernels": k2,
-        }
-        del Q2, K2, V2, Qs2, dO2, x2, O2, ws2
+        out["secondary"] = run_pass(hsa, _lib, workloads, dev, gen, "fwd_64k",
+                                    max(3, args.steps // 4))
+        # the backward workload: the same pass at B=2, L=16384, d=64, reported for its
+        # hsa_bwd time (selection fixed by the pass's own hsa_select)
+        out["backward_b2"] = run_pass(hsa, _lib, workloads, dev, gen, "bwd_16k",
+                                      max(3, args.steps // 4))
 
     if not args.no_decode:
         out["decode"] = run_decode(hsa, _lib, workloads, dev, gen, reps=50,
