@@ -33,7 +33,7 @@ namespace hsa {
 //   S = Q K_c^T, dP = dO V_c^T                               (MFMA 16x16x32)
 //   P = exp(S - lse), with lse the forward's normaliser (HL) or computed here over the
 //   chunk's 64 keys; D = rowsum(P * dP); dS = w P (dP - D)
-//   dV^T += dO^T (w P), dK^T += Q^T dS                       (MFMA 16x16x16, registers)
+//   dV^T += dO^T (w P), dK^T += Q^T dS                       (MFMA 32x32x16, registers)
 //   dQ_k^T = K_c^T dS^T                                      (MFMA 16x16x32, per edge)
 //   dw_edge = sum over the edge's G heads of D
 // Every selection edge belongs to exactly one segment, so the edge's dQ contribution (bf16,
@@ -95,14 +95,18 @@ k_bwd_chunk_mfma(
     *reinterpret_cast<uint4*>(&kl[key][d]) = *reinterpret_cast<const uint4*>(K + cb + key * kvrow + d);
     *reinterpret_cast<uint4*>(&vl[key][d]) = *reinterpret_cast<const uint4*>(V + cb + key * kvrow + d);
   }
-  f32x4 dk[DT][4], dv[DT][4];
+  // dK^T and dV^T as 32x32 tiles: [d2][k2] holds d = 32*d2 + 8*(i/4) + 4*(lane/32) + i%4,
+  // keys 32*k2 + lane%32
+  f32x16 dk[2][2], dv[2][2];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      dk[dt][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dv[dt][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dk[d2][k2][i] = 0.0f;
+        dv[d2][k2][i] = 0.0f;
+      }
   const int qs_sel = col / G, qs_head = col % G;  // this lane's A-operand row -> selector, head
   __syncthreads();
 
@@ -199,30 +203,40 @@ k_bwd_chunk_mfma(
       const int s = (4 * blk) / G;
       if (col == 0 && (4 * blk) % G == 0 && s < n_here) dw_out[eo_l[ej + s]] = dsel;
     }
-    // dV^T += dO^T (w P), dK^T += Q^T dS  (k = the 16 query rows, 4 per lane block), the
-    // transposed operands read from LDS with the transposing read; dS^T goes to LDS for dQ
-    s16x4 doT[DT], qT[DT];
+    // dV^T += dO^T (w P), dK^T += Q^T dS on the 32x32x16 product, whose contraction is the
+    // job's 16 query rows: A = 32 dimensions of dO^T or Q^T (transposing reads), B = the
+    // w P or dS tiles of 32 keys brought to the same rows by one lane swap; dS^T also goes
+    // to LDS for dQ
+    bf16x8 doT[2], qT[2];
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2) {
+      doT[d2] = lds_read_tr8_rows(&dl[0][0], KROW, 32 * d2, lane);
+      qT[d2] = lds_read_tr8_rows(&ql[0][0], KROW, 32 * d2, lane);
+    }
     const int trow = 4 * blk + col / 4, tcol = 4 * (col % 4);
     const int pcol = 4 * ((col % 4) ^ blk);  // tcol in the swizzled dS^T rows 4*blk + col/4
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      doT[dt] = lds_read_tr4(&dl[trow][16 * dt + tcol]);
-      qT[dt] = lds_read_tr4(&ql[trow][16 * dt + tcol]);
-    }
+    for (int k2 = 0; k2 < 2; ++k2) {
+      uint2 wpu[2], dsu[2];
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      f32x4 wp, dsv;
+      for (int h = 0; h < 2; ++h) {
+        const int t4 = 2 * k2 + h;
+        f32x4 wp, dsv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wp[i] = wr[i] * sa[t4][i];
-        dsv[i] = wr[i] * sa[t4][i] * (pa[t4][i] - dr[i]);
+        for (int i = 0; i < 4; ++i) {
+          wp[i] = wr[i] * sa[t4][i];
+          dsv[i] = wr[i] * sa[t4][i] * (pa[t4][i] - dr[i]);
+        }
+        const s16x4 dsb = pack_bf16x4(dsv);
+        *reinterpret_cast<s16x4*>(&sdl[16 * t4 + col][4 * (blk ^ (col / 4))]) = dsb;
+        wpu[h] = __builtin_bit_cast(uint2, pack_bf16x4(wp));
+        dsu[h] = __builtin_bit_cast(uint2, dsb);
       }
-      const s16x4 wpb = pack_bf16x4(wp), dsb = pack_bf16x4(dsv);
-      *reinterpret_cast<s16x4*>(&sdl[16 * t4 + col][4 * (blk ^ (col / 4))]) = dsb;
+      const bf16x8 wpb = tiles_to_b32(wpu[0], wpu[1]), dsb = tiles_to_b32(dsu[0], dsu[1]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        dv[dt][t4] = mfma_16x16x16(doT[dt], wpb, dv[dt][t4]);
-        dk[dt][t4] = mfma_16x16x16(qT[dt], dsb, dk[dt][t4]);
+      for (int d2 = 0; d2 < 2; ++d2) {
+        dv[d2][k2] = mfma_32x32x16(doT[d2], wpb, dv[d2][k2]);
+        dk[d2][k2] = mfma_32x32x16(qT[d2], dsb, dk[d2][k2]);
       }
     }
     wave_lds_sync();  // sdl is read transposed below
@@ -256,40 +270,52 @@ k_bwd_chunk_mfma(
   __syncthreads();  // every job is done: the chunk and staging areas are free
   f32x4* xs = reinterpret_cast<f32x4*>(sm);  // 16 x 64 lanes x 16 bytes
   const size_t pb = (size_t)bg * max_seg + sidx;
+  // four consecutive d of one key: elements 4j .. 4j+3 of a 32x32 tile
+  auto quad = [](const f32x16& v, int j) {
+    return f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+  };
   if (wv == 1) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) xs[(dt * 4 + t4) * 64 + lane] = dk[dt][t4];
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xs[((d2 * 2 + k2) * 4 + j) * 64 + lane] = quad(dk[d2][k2], j);
   }
   __syncthreads();
   if (wv == 0) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const int key = 16 * t4 + col, d = 16 * dt + 4 * blk;
-        *reinterpret_cast<f32x4*>(part_dk + (pb * 64 + key) * D + d) =
-            (dk[dt][t4] + xs[(dt * 4 + t4) * 64 + lane]) * sm_scale;
-      }
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = 32 * k2 + lane % 32, d = 32 * d2 + 8 * j + 4 * (lane / 32);
+          *reinterpret_cast<f32x4*>(part_dk + (pb * 64 + key) * D + d) =
+              (quad(dk[d2][k2], j) + xs[((d2 * 2 + k2) * 4 + j) * 64 + lane]) * sm_scale;
+        }
   }
   __syncthreads();
   if (wv == 1) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) xs[(dt * 4 + t4) * 64 + lane] = dv[dt][t4];
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xs[((d2 * 2 + k2) * 4 + j) * 64 + lane] = quad(dv[d2][k2], j);
   }
   __syncthreads();
   if (wv == 0) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const int key = 16 * t4 + col, d = 16 * dt + 4 * blk;
-        *reinterpret_cast<f32x4*>(part_dv + (pb * 64 + key) * D + d) =
-            dv[dt][t4] + xs[(dt * 4 + t4) * 64 + lane];
-      }
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = 32 * k2 + lane % 32, d = 32 * d2 + 8 * j + 4 * (lane / 32);
+          *reinterpret_cast<f32x4*>(part_dv + (pb * 64 + key) * D + d) =
+              quad(dv[d2][k2], j) + xs[((d2 * 2 + k2) * 4 + j) * 64 + lane];
+        }
   }
 }
 
@@ -363,13 +389,15 @@ k_bwd_chunk_keys(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       vb[t2][ks] = ld_bf16x8(V + cb + (32 * wv + 16 * t2 + col) * kvrow + 32 * ks + 8 * blk);
-  f32x4 dk[DT][2], dv[DT][2];  // keys 32*wv + 16*t2 + col, d = 16*dt + 4*blk + i
+  // dK^T and dV^T of this wave's keys as 32x32 tiles: [d4] holds keys 32*wv + lane%32,
+  // d = 32*d4 + 8*(i/4) + 4*(lane/32) + i%4
+  f32x16 dk[4], dv[4];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      dk[dt][t2] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dv[dt][t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; ++i) {
+      dk[d4][i] = 0.0f;
+      dv[d4][i] = 0.0f;
     }
   const int qs_sel = col / G, qs_head = col % G;  // this lane's query row -> selector, head
   const int trow = 4 * blk + col / 4, tcol = 4 * (col % 4);
@@ -485,9 +513,10 @@ k_bwd_chunk_keys(
       const int s = (4 * blk) / G;
       if (col == 0 && (4 * blk) % G == 0 && s < n_here) dw_out[eo_l[ej + s]] = dsel;
     }
-    // dV^T += dO^T (w P), dK^T += Q^T dS over this wave's keys (k = the 16 query rows); dS^T
-    // of its keys to the shared tile
-    s16x4 wpb[2], dsb[2];
+    // dV^T += dO^T (w P), dK^T += Q^T dS over this wave's 32 keys on the 32x32x16 product
+    // (contraction: the job's 16 query rows; the B operands brought to the A operands' rows
+    // by one lane swap); dS^T of its keys to the shared tile
+    uint2 wpu[2], dsu[2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       f32x4 wp, dsv;
@@ -496,18 +525,17 @@ k_bwd_chunk_keys(
         wp[i] = wr[i] * sa[t2][i];
         dsv[i] = wr[i] * sa[t2][i] * (pa[t2][i] - dr[i]);
       }
-      wpb[t2] = pack_bf16x4(wp);
-      dsb[t2] = pack_bf16x4(dsv);
-      *reinterpret_cast<s16x4*>(&sdl[32 * wv + 16 * t2 + col][4 * (blk ^ (col / 4))]) = dsb[t2];
+      const s16x4 dsb = pack_bf16x4(dsv);
+      *reinterpret_cast<s16x4*>(&sdl[32 * wv + 16 * t2 + col][4 * (blk ^ (col / 4))]) = dsb;
+      wpu[t2] = __builtin_bit_cast(uint2, pack_bf16x4(wp));
+      dsu[t2] = __builtin_bit_cast(uint2, dsb);
     }
+    {
+      const bf16x8 wpb = tiles_to_b32(wpu[0], wpu[1]), dsb = tiles_to_b32(dsu[0], dsu[1]);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const s16x4 doT = lds_read_tr4(&dl[trow][16 * dt + tcol]);
-      const s16x4 qT = lds_read_tr4(&ql[trow][16 * dt + tcol]);
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        dv[dt][t2] = mfma_16x16x16(doT, wpb[t2], dv[dt][t2]);
-        dk[dt][t2] = mfma_16x16x16(qT, dsb[t2], dk[dt][t2]);
+      for (int d4 = 0; d4 < 4; ++d4) {
+        dv[d4] = mfma_32x32x16(lds_read_tr8_rows(&dl[0][0], KROW, 32 * d4, lane), wpb, dv[d4]);
+        dk[d4] = mfma_32x32x16(lds_read_tr8_rows(&ql[0][0], KROW, 32 * d4, lane), dsb, dk[d4]);
       }
     }
     __syncthreads();  // the shared dS^T tile is complete
@@ -540,13 +568,16 @@ k_bwd_chunk_keys(
     // rewrites dS^T and the row exchange only after its own exchange barrier
   }
   const size_t pb = (size_t)bg * max_seg + sidx;
+  const int key = 32 * wv + lane % 32;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const int key = 32 * wv + 16 * t2 + col, d = 16 * dt + 4 * blk;
-      *reinterpret_cast<f32x4*>(part_dk + (pb * 64 + key) * D + d) = dk[dt][t2] * sm_scale;
-      *reinterpret_cast<f32x4*>(part_dv + (pb * 64 + key) * D + d) = dv[dt][t2];
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * d4 + 8 * j + 4 * (lane / 32);
+      *reinterpret_cast<f32x4*>(part_dk + (pb * 64 + key) * D + d) =
+          f32x4{dk[d4][4 * j], dk[d4][4 * j + 1], dk[d4][4 * j + 2], dk[d4][4 * j + 3]} * sm_scale;
+      *reinterpret_cast<f32x4*>(part_dv + (pb * 64 + key) * D + d) =
+          f32x4{dv[d4][4 * j], dv[d4][4 * j + 1], dv[d4][4 * j + 2], dv[d4][4 * j + 3]};
     }
 }
 

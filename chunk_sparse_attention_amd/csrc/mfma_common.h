@@ -46,13 +46,10 @@ __host__ __device__ __forceinline__ int perm_key(int s, int block, int e) {
   return 32 * s + 16 * (e / 4) + 4 * block + (e % 4);
 }
 
-// ---- 16x16x16 operands, transposing LDS reads, wave-local LDS ordering ----------------
+// ---- four-element operands, transposing LDS reads, wave-local LDS ordering -------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 // Four fp32 values to bf16 (RNE), as two pair conversions: written per pair, the compiler
 // keeps one v_cvt_pk_bf16_f32 per pair where the whole-vector form was sometimes split into
 // four single conversions and two permutes.
@@ -63,6 +60,29 @@ __device__ __forceinline__ s16x4 pack_bf16x4(f32x4 v) {
   const bf16x2 hi = __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2);
   const uint2 u = {__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
   return __builtin_bit_cast(s16x4, u);
+}
+// ---- 32x32x16 products over 16 rows ------------------------------------------------------
+// v_mfma_f32_32x32x16_bf16: D[32x32] = A[32x16] * B[16x32] + C, fp32 accumulate, at the full
+// matrix-core rate with a contraction only 16 deep (the legacy 16x16x16 form issues at the
+// 16x16x32 form's rate, so it delivers half the flops).
+//   A: lane l holds row l%32, k = 8*(l/32) .. +7;  B: lane l holds column l%32, the same k
+//   D: lane l holds column l%32, rows 8*(i/4) + 4*(l/32) + i%4 in element i (i = 0..15)
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// The B operand of a 32x32x16 product whose contraction runs over the 16 rows of two 16x16
+// output tiles: lo covers columns 32g .. 32g+15, hi columns 32g+16 .. 32g+31, each packed to
+// bf16 (lane (c, blk) holds rows 4*blk .. 4*blk+3 of column c).  One swap with the
+// neighbouring 16-lane row leaves lane l with rows 8*(l/32) .. +7 of column 32g + l%32, in
+// row order: the lane of an even row keeps its lo rows and takes its partner's lo rows, the
+// lane of an odd row takes its partner's hi rows and keeps its own.
+__device__ __forceinline__ bf16x8 tiles_to_b32(uint2 lo, uint2 hi) {
+  const auto p0 = __builtin_amdgcn_permlane16_swap(lo.x, hi.x, false, false);
+  const auto p1 = __builtin_amdgcn_permlane16_swap(lo.y, hi.y, false, false);
+  const uint4 v = {p0[0], p1[0], p0[1], p1[1]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 // Orders this wave's earlier LDS accesses before its later ones that touch other lanes' data
 // (the LDS serves one wave's instructions in order; the wait and the compiler barrier keep
@@ -80,11 +100,21 @@ __device__ __forceinline__ bf16x8 cat_bf16x8(s16x4 lo, s16x4 hi) {
 // gfx950 transposing LDS read of four 16-bit elements: in each group of 16 lanes, lane j
 // receives element j%4 of the 8-byte word that lane 4*i + j/4 addresses, for i = 0..3.
 // With lane m of group `blk` addressing row 4*blk + m/4, column c0 + 4*(m%4) of a row-major
-// LDS matrix, lane j gets column c0 + j of rows 4*blk .. 4*blk+3: the 16x16x16 MFMA
-// A operand of the transposed matrix.  p must point into LDS.
+// LDS matrix, lane j gets column c0 + j of rows 4*blk .. 4*blk+3 of that matrix.  p must
+// point into LDS.
 __device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
+}
+// The A operand of a 32x32x16 product that matches tiles_to_b32: rows d0 .. d0+31 of the
+// transpose of a row-major LDS matrix m (16 rows, row stride `stride` elements), i.e. lane l
+// gets column d0 + l%32 of rows 8*(l/32) .. +7, by two transposing reads.  Lane
+// l = 16*blk + col of group blk = 2h + u addresses row 8h + col/4 (then 4 rows further),
+// columns d0 + 16u + 4*(col%4).
+__device__ __forceinline__ bf16x8 lds_read_tr8_rows(const uint16_t* m, int stride, int d0, int lane) {
+  const int col = lane % 16, blk = lane / 16;
+  const uint16_t* p = m + (8 * (blk / 2) + col / 4) * stride + d0 + 16 * (blk % 2) + 4 * (col % 4);
+  return cat_bf16x8(lds_read_tr4(p), lds_read_tr4(p + 4 * stride));
 }
 
 // Output tiles of a 16x16 MFMA with rows d and columns the 16 query rows: lane (col, blk)
