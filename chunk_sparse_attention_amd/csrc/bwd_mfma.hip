@@ -27,6 +27,29 @@ namespace hsa {
 
 // ---- chunk phase, then token phase ----------------------------------------------------------
 
+// dw of the job's edges from the row sums D of rows 4*blk + i (i = 0..3; row r belongs to
+// selector r / G): one lane per edge writes the sum of its G rows.  For G >= 4 a selector's
+// rows span G/4 lane blocks (added across them, 16 and 32 lanes apart); for G < 4 a lane
+// block holds 4/G selectors.
+template <int G>
+__device__ __forceinline__ void edge_dw(const float (&dr)[4], int blk, int col, int n_here,
+                                        int ej, const int64_t* eo_l, float* __restrict__ dw_out) {
+  if constexpr (G >= 4) {
+    float dsel = (dr[0] + dr[1]) + (dr[2] + dr[3]);
+    if (G >= 8) dsel += __shfl_xor(dsel, 16);
+    if (G == 16) dsel += __shfl_xor(dsel, 32);
+    const int s = (4 * blk) / G;
+    if (col == 0 && (4 * blk) % G == 0 && s < n_here) dw_out[eo_l[ej + s]] = dsel;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4 / G; ++j) {
+      const float dsel = G == 2 ? dr[2 * j] + dr[2 * j + 1] : dr[j];
+      const int s = (4 * blk) / G + j;
+      if (col == 0 && s < n_here) dw_out[eo_l[ej + s]] = dsel;
+    }
+  }
+}
+
 // Chunk phase for D = 64: one block of two waves per segment of a chunk's selector list.  The
 // chunk's keys and values sit in LDS; a job takes 16/G selectors (16 query rows, row
 // q = selector * G + head), and the two waves take alternate jobs:
@@ -112,7 +135,7 @@ k_bwd_chunk_mfma(
 
   // this lane's query row of job j (a padding row repeats the job's first selector) and, with
   // HL, the forward's normaliser of the lane's four output rows 4*blk + i: four consecutive
-  // heads of one selector (G >= 4), one 16-byte load
+  // heads of one selector for G >= 4 (one 16-byte load), one load per row otherwise
   const size_t row_off = (b * L * Hq + (size_t)g * G + qs_head) * D + 8 * blk;
   const size_t tok_stride = (size_t)Hq * D;
   auto load_rows = [&](int ej, bf16x8 (&qa)[KS], bf16x8 (&da)[KS], float (&le)[4]) {
@@ -124,12 +147,20 @@ k_bwd_chunk_mfma(
       da[ks] = ld_bf16x8(dO + qoff + 32 * ks);
     }
     if (HL) {
-      const int s2 = (4 * blk) / G, e = ej + (s2 < n_here ? s2 : 0);
-      const float4 v = *reinterpret_cast<const float4*>(lse_in + eo_l[e] * G + (4 * blk) % G);
-      le[0] = v.x;
-      le[1] = v.y;
-      le[2] = v.z;
-      le[3] = v.w;
+      if constexpr (G >= 4) {
+        const int s2 = (4 * blk) / G, e = ej + (s2 < n_here ? s2 : 0);
+        const float4 v = *reinterpret_cast<const float4*>(lse_in + eo_l[e] * G + (4 * blk) % G);
+        le[0] = v.x;
+        le[1] = v.y;
+        le[2] = v.z;
+        le[3] = v.w;
+      } else {  // the four rows belong to 4/G selectors
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s2 = (4 * blk + i) / G, e = ej + (s2 < n_here ? s2 : 0);
+          le[i] = lse_in[eo_l[e] * G + (4 * blk + i) % G];
+        }
+      }
     }
   };
   bf16x8 qn[KS], dn[KS];
@@ -196,13 +227,7 @@ k_bwd_chunk_mfma(
       wr[i] = s < n_here ? w_l[ej + s] : 0.0f;
     }
     // dw of each edge: its G rows' D (rows 4*blk .. 4*blk+3 per lane block)
-    {
-      float dsel = (dr[0] + dr[1]) + (dr[2] + dr[3]);
-      if (G >= 8) dsel += __shfl_xor(dsel, 16);
-      if (G == 16) dsel += __shfl_xor(dsel, 32);
-      const int s = (4 * blk) / G;
-      if (col == 0 && (4 * blk) % G == 0 && s < n_here) dw_out[eo_l[ej + s]] = dsel;
-    }
+    edge_dw<G>(dr, blk, col, n_here, ej, eo_l, dw_out);
     // dV^T += dO^T (w P), dK^T += Q^T dS on the 32x32x16 product, whose contraction is the
     // job's 16 query rows: A = 32 dimensions of dO^T or Q^T (transposing reads), B = the
     // w P or dS tiles of 32 keys brought to the same rows by one lane swap; dS^T also goes
@@ -423,8 +448,18 @@ k_bwd_chunk_keys(
     r.d1 = *reinterpret_cast<const uint4*>(dO + qoff + 8);
     r.le = float4{0.f, 0.f, 0.f, 0.f};
     if (HL) {  // the normaliser of this lane's four output rows 4*blk .. 4*blk+3
-      const int s3 = (4 * blk) / G, e = ej + (s3 < n_here ? s3 : 0);
-      r.le = *reinterpret_cast<const float4*>(lse_in + eo_l[e] * G + (4 * blk) % G);
+      if constexpr (G >= 4) {
+        const int s3 = (4 * blk) / G, e = ej + (s3 < n_here ? s3 : 0);
+        r.le = *reinterpret_cast<const float4*>(lse_in + eo_l[e] * G + (4 * blk) % G);
+      } else {  // the four rows belong to 4/G selectors
+        float le[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s3 = (4 * blk + i) / G, e = ej + (s3 < n_here ? s3 : 0);
+          le[i] = lse_in[eo_l[e] * G + (4 * blk + i) % G];
+        }
+        r.le = float4{le[0], le[1], le[2], le[3]};
+      }
     }
     return r;
   };
@@ -506,13 +541,7 @@ k_bwd_chunk_keys(
     __syncthreads();  // both halves of D
 #pragma unroll
     for (int i = 0; i < 4; ++i) dr[i] = xl[0][0][4 * blk + i] + xl[0][1][4 * blk + i];
-    if (wv == 0) {  // dw of each edge: its G rows' D
-      float dsel = (dr[0] + dr[1]) + (dr[2] + dr[3]);
-      if (G >= 8) dsel += __shfl_xor(dsel, 16);
-      if (G == 16) dsel += __shfl_xor(dsel, 32);
-      const int s = (4 * blk) / G;
-      if (col == 0 && (4 * blk) % G == 0 && s < n_here) dw_out[eo_l[ej + s]] = dsel;
-    }
+    if (wv == 0) edge_dw<G>(dr, blk, col, n_here, ej, eo_l, dw_out);  // each edge: its G rows' D
     // dV^T += dO^T (w P), dK^T += Q^T dS over this wave's 32 keys on the 32x32x16 product
     // (contraction: the job's 16 query rows; the B operands brought to the A operands' rows
     // by one lane swap); dS^T of its keys to the shared tile
@@ -593,8 +622,11 @@ __global__ void __launch_bounds__(256) k_bwd_tok(
     const float* __restrict__ w, const bf16* __restrict__ Kslc, bf16* __restrict__ dQ,
     bf16* __restrict__ dQs, float* __restrict__ ds_out, int L, int Hkv, int Kn, int nC,
     int64_t rows, float sm_scale, float sel_scale, int softmax_w) {
-  constexpr int E = G * D / 64;  // elements of the row's G x D block per lane
-  constexpr int F = D / 64;      // features of dQs per lane: lane + 64 f
+  // elements of the row's G x D block per lane: at least four (8-byte pieces), so rows of
+  // fewer than 256 values (G < 4 at d = 64, G = 1 at d = 128) leave the upper lanes idle
+  constexpr int E = G * D / 64 >= 4 ? G * D / 64 : 4;
+  constexpr int LANES = G * D / E;
+  constexpr int F = D / 64;  // features of dQs per lane: lane + 64 f
   const int lane = threadIdx.x % 64;
   const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // (b * L + t) * Hkv + g
   if (row >= rows) return;  // whole wave
@@ -611,12 +643,13 @@ __global__ void __launch_bounds__(256) k_bwd_tok(
     dwk = dw_in[o + lane];
   }
   const bool valid = c >= 0 && c < nC;
-  const bf16* src = dq_part + o * (size_t)(G * D) + (size_t)lane * E;
+  const bool dq_lane = LANES == 64 || lane < LANES;
+  const bf16* src = dq_part + o * (size_t)(G * D) + (size_t)(dq_lane ? lane : 0) * E;
   float acc[E];
 #pragma unroll
   for (int j = 0; j < E; ++j) acc[j] = 0.0f;
   const uint64_t vmask = __ballot(valid);
-  for (int k0 = 0; k0 < Kn; k0 += 8) {
+  for (int k0 = 0; dq_lane && k0 < Kn; k0 += 8) {
     uint32_t v[8][E / 2];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -635,7 +668,8 @@ __global__ void __launch_bounds__(256) k_bwd_tok(
   }
 #pragma unroll
   for (int j = 0; j < E; ++j) acc[j] *= sm_scale;
-  store_row<E>(dQ + bt * (int64_t)Hkv * G * D + (size_t)g * G * D + (size_t)lane * E, acc);
+  if (dq_lane)
+    store_row<E>(dQ + bt * (int64_t)Hkv * G * D + (size_t)g * G * D + (size_t)lane * E, acc);
   // stick-breaking: ds_k = dw_k w_k (1 - p_k) - p_k * sum_{k' > k} dw_k' w_k'  (fp64, suffix
   // from the last slot); softmax weights: ds_k = w_k (dw_k - sum_j w_j dw_j)  (fp64, slot order)
   const double dww = valid ? (double)dwk * (double)wk : 0.0;
@@ -760,8 +794,9 @@ __global__ void __launch_bounds__(256) k_bwd_dks(
 }
 
 bool bwd_mfma_supported(const Dims& d) {
-  return d.dtype == 1 && (d.D == 64 || d.D == 128) && (d.G == 4 || d.G == 8 || d.G == 16) &&
-         d.nC < 32768 && !(d.flags & 1u);
+  return d.dtype == 1 && (d.D == 64 || d.D == 128) &&
+         (d.G == 1 || d.G == 2 || d.G == 4 || d.G == 8 || d.G == 16) && d.nC < 32768 &&
+         !(d.flags & 1u);
 }
 
 // Chunk phase, token phase (+ dKslc partials), reduction.
@@ -790,11 +825,15 @@ static hipError_t launch_bwd_fused(const Dims& d, const BwdLayout& lay, const vo
                                lay.max_seg, c2, (float)d.sm_scale);
     };
     if (d.D == 64) {
-      if (d.G == 4) after_fwd ? go(k_bwd_chunk_mfma<4, true>) : go(k_bwd_chunk_mfma<4, false>);
+      if (d.G == 1) after_fwd ? go(k_bwd_chunk_mfma<1, true>) : go(k_bwd_chunk_mfma<1, false>);
+      else if (d.G == 2) after_fwd ? go(k_bwd_chunk_mfma<2, true>) : go(k_bwd_chunk_mfma<2, false>);
+      else if (d.G == 4) after_fwd ? go(k_bwd_chunk_mfma<4, true>) : go(k_bwd_chunk_mfma<4, false>);
       else if (d.G == 8) after_fwd ? go(k_bwd_chunk_mfma<8, true>) : go(k_bwd_chunk_mfma<8, false>);
       else after_fwd ? go(k_bwd_chunk_mfma<16, true>) : go(k_bwd_chunk_mfma<16, false>);
     } else {
-      if (d.G == 4) after_fwd ? go(k_bwd_chunk_keys<4, true>) : go(k_bwd_chunk_keys<4, false>);
+      if (d.G == 1) after_fwd ? go(k_bwd_chunk_keys<1, true>) : go(k_bwd_chunk_keys<1, false>);
+      else if (d.G == 2) after_fwd ? go(k_bwd_chunk_keys<2, true>) : go(k_bwd_chunk_keys<2, false>);
+      else if (d.G == 4) after_fwd ? go(k_bwd_chunk_keys<4, true>) : go(k_bwd_chunk_keys<4, false>);
       else if (d.G == 8) after_fwd ? go(k_bwd_chunk_keys<8, true>) : go(k_bwd_chunk_keys<8, false>);
       else after_fwd ? go(k_bwd_chunk_keys<16, true>) : go(k_bwd_chunk_keys<16, false>);
     }
@@ -809,11 +848,15 @@ static hipError_t launch_bwd_fused(const Dims& d, const BwdLayout& lay, const vo
           d.nC, rows, (float)d.sm_scale, (float)d.sel_scale, softmax_w(d));
     };
     if (d.D == 64) {
-      if (d.G == 4) go(k_bwd_tok<64, 4>);
+      if (d.G == 1) go(k_bwd_tok<64, 1>);
+      else if (d.G == 2) go(k_bwd_tok<64, 2>);
+      else if (d.G == 4) go(k_bwd_tok<64, 4>);
       else if (d.G == 8) go(k_bwd_tok<64, 8>);
       else go(k_bwd_tok<64, 16>);
     } else {
-      if (d.G == 4) go(k_bwd_tok<128, 4>);
+      if (d.G == 1) go(k_bwd_tok<128, 1>);
+      else if (d.G == 2) go(k_bwd_tok<128, 2>);
+      else if (d.G == 4) go(k_bwd_tok<128, 4>);
       else if (d.G == 8) go(k_bwd_tok<128, 8>);
       else go(k_bwd_tok<128, 16>);
     }

@@ -5,7 +5,8 @@
 // papernotes.org note, 方法详解 › 层次化稀疏注意力（HSA） 第一阶段/第二阶段, 硬件对齐 Kernel).
 //
 // Two designs.  The chunk-major one (below k_fwd_tile) runs whenever the inverse index fits
-// (at most 16384 chunks); the token-tile one covers longer sequences.
+// (at most 16384 chunks), for G = 1, 2, 4, 8 and 16; the token-tile one covers longer
+// sequences for G = 4, 8 and 16.
 //
 // Token tiles: one workgroup owns a tile of TT consecutive tokens of one (batch, group) and keeps their
 // fp32 outputs in LDS.  The tile's (token, slot) edges are sorted by chunk; each wave takes a
@@ -450,7 +451,11 @@ __global__ void __launch_bounds__(256) k_fwd_tok(const bf16* __restrict__ o_part
                                                  const int32_t* __restrict__ idx,
                                                  bf16* __restrict__ O, int L, int Hkv, int Kn,
                                                  int nC, int64_t rows) {
-  constexpr int E = G * D / 64 / SPLIT;  // elements of the row's G x D block per lane
+  // elements of the row's G x D block per lane: at least four (8-byte pieces), so rows of
+  // fewer than 256 outputs (G < 4 at d = 64, G = 1 at d = 128) leave the upper lanes idle
+  constexpr int E = G * D / 64 / SPLIT >= 4 ? G * D / 64 / SPLIT : 4;
+  constexpr int LANES = G * D / SPLIT / E;
+  static_assert(LANES >= 1 && LANES <= 64, "one wave covers its part of the row");
   const int lane = threadIdx.x % 64;
   const int64_t wid = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
   const int64_t row = wid / SPLIT;  // (b * L + t) * Hkv + g
@@ -461,6 +466,7 @@ __global__ void __launch_bounds__(256) k_fwd_tok(const bf16* __restrict__ o_part
   const size_t o = (size_t)row * Kn;
   const int c = lane < Kn ? idx[o + lane] : -1;
   const uint64_t vmask = __ballot(c >= 0 && c < nC);
+  if (LANES < 64 && lane >= LANES) return;  // after the ballot
   const size_t off = (size_t)part * (G * D / SPLIT) + (size_t)lane * E;
   const bf16* src = o_part + o * (size_t)(G * D) + off;
   float acc[E];
@@ -534,9 +540,10 @@ static bool launch_fwd_tile_g(const Dims& d, const void* Q, const void* K, const
 }
 
 bool fwd_mfma_supported(const Dims& d) {
-  return d.dtype == 1 && (d.D == 64 || d.D == 128) &&
-         (d.G == 4 || d.G == 8 || d.G == 16) && d.nC < 32768 &&
-         !(d.flags & 1u);
+  // G = 1 and 2 run chunk-major only (the token tiles past 16384 chunks need G >= 4)
+  return d.dtype == 1 && (d.D == 64 || d.D == 128) && !(d.flags & 1u) &&
+         (((d.G == 4 || d.G == 8 || d.G == 16) && d.nC < 32768) ||
+          ((d.G == 1 || d.G == 2) && d.nC <= 16384));
 }
 
 bool fwd_chunked(const Dims& d) { return fwd_mfma_supported(d) && d.nC <= 16384; }
@@ -607,11 +614,15 @@ static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const vo
           d.L, d.Hq, d.Hkv, d.K, d.nC, st.ix.seg, st.ix.max_seg, c2);
     };
     if (d.D == 64) {
-      if (d.G == 4) go(k_fwd_chunk<64, 4, kFwdWaves>, kFwdWaves);
+      if (d.G == 1) go(k_fwd_chunk<64, 1, kFwdWaves>, kFwdWaves);
+      else if (d.G == 2) go(k_fwd_chunk<64, 2, kFwdWaves>, kFwdWaves);
+      else if (d.G == 4) go(k_fwd_chunk<64, 4, kFwdWaves>, kFwdWaves);
       else if (d.G == 8) go(k_fwd_chunk<64, 8, kFwdWaves>, kFwdWaves);
       else go(k_fwd_chunk<64, 16, kFwdWaves>, kFwdWaves);
     } else {
-      if (d.G == 4) go(k_fwd_chunk<128, 4, kFwdWaves128>, kFwdWaves128);
+      if (d.G == 1) go(k_fwd_chunk<128, 1, kFwdWaves128>, kFwdWaves128);
+      else if (d.G == 2) go(k_fwd_chunk<128, 2, kFwdWaves128>, kFwdWaves128);
+      else if (d.G == 4) go(k_fwd_chunk<128, 4, kFwdWaves128>, kFwdWaves128);
       else if (d.G == 8) go(k_fwd_chunk<128, 8, kFwdWaves128>, kFwdWaves128);
       else go(k_fwd_chunk<128, 16, kFwdWaves128>, kFwdWaves128);
     }
@@ -624,11 +635,15 @@ static hipError_t launch_fwd_chunked(const Dims& d, const FwdState& st, const vo
           (const bf16*)(ws + st.part), idx, (bf16*)O, d.L, d.Hkv, d.K, d.nC, rows);
     };
     if (d.D == 64) {
-      if (d.G == 4) go(k_fwd_tok<64, 4, 1>, 1);
+      if (d.G == 1) go(k_fwd_tok<64, 1, 1>, 1);
+      else if (d.G == 2) go(k_fwd_tok<64, 2, 1>, 1);
+      else if (d.G == 4) go(k_fwd_tok<64, 4, 1>, 1);
       else if (d.G == 8) go(k_fwd_tok<64, 8, 1>, 1);
       else go(k_fwd_tok<64, 16, 2>, 2);
     } else {
-      if (d.G == 4) go(k_fwd_tok<128, 4, 1>, 1);
+      if (d.G == 1) go(k_fwd_tok<128, 1, 1>, 1);
+      else if (d.G == 2) go(k_fwd_tok<128, 2, 1>, 1);
+      else if (d.G == 4) go(k_fwd_tok<128, 4, 1>, 1);
       else if (d.G == 8) go(k_fwd_tok<128, 8, 2>, 2);
       else go(k_fwd_tok<128, 16, 4>, 4);
     }

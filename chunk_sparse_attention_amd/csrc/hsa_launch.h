@@ -147,7 +147,7 @@ hipError_t launch_bwd_mfma(const Dims& d, const BwdLayout& lay, const void* Q, c
                            float* dKslc, bool fold, bool after_fwd, char* ws, hipStream_t s);
 bool fwd_mfma_supported(const Dims& d);
 // bf16 up to 16384 chunks: the forward runs chunk-major (inverse index, per-edge partials,
-// token sums); beyond, on token tiles.
+// token sums); beyond, on token tiles (G >= 4; fwd_mfma_supported is false there for G < 4).
 bool fwd_chunked(const Dims& d);
 size_t fwd_mfma_ws(const Dims& d);
 // index_ready: ws already holds the inverse index (or the token tiles' job lists) of this

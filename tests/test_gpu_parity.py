@@ -52,6 +52,10 @@ SMALL = [
     W("planted_d128", 1, 64 * 100, 16, 2, 128, 64, 8, torch.bfloat16, planted=True),
     W("bf16_d64_g4_ragged", 1, 64 * 17 + 9, 8, 2, 64, 64, 6, torch.bfloat16),
     W("bf16_d64_g16_k16", 1, 64 * 19 + 3, 16, 1, 64, 64, 16, torch.bfloat16),
+    # one and two query heads per group: 16 and 8 selectors per matrix-core job
+    W("bf16_g2_d64_ragged", 1, 64 * 13 + 11, 8, 4, 64, 64, 8, torch.bfloat16),
+    W("bf16_g2_d128", 1, 64 * 12 + 3, 4, 2, 128, 64, 5, torch.bfloat16),
+    W("bf16_g1_d128_b2", 2, 64 * 9 + 7, 2, 2, 128, 64, 4, torch.bfloat16),
 ]
 
 
@@ -901,7 +905,7 @@ def test_full_decode(hsa, dev):
 # ---- the normalisers at the boundary, and the forward state's records ----------------------
 
 LSE_CASES = [w for w in SMALL if w.name in ("tiny_fp32", "bf16_d64_ragged", "bf16_d128_ragged",
-                                           "bf16_g1_k3", "bf16_d64_g16_k16")]
+                                           "bf16_g1_k3", "bf16_d64_g16_k16", "bf16_g2_d128")]
 
 
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
