@@ -71,29 +71,36 @@ BwdLayout bwd_layout(const Dims& d) {
 
 // ---- inverse index ---------------------------------------------------------------------
 
-// Per (b, g, tile): how many of the tile's (token, slot) entries chose each chunk, stored
-// chunk-major: tile_counts[(bg * nC + c) * n_tiles + tile].
+// The counting and scattering blocks keep one LDS counter per chunk; past kIndexPart chunks
+// the chunks are split into parts of that many, one block per (b, g, tile, part), each
+// handling only the entries whose chunk lies in its part.
+constexpr int kIndexPart = 16384;
+
+// Per (b, g, tile, part): how many of the tile's (token, slot) entries chose each chunk of
+// the part, stored chunk-major: tile_counts[(bg * nC + c) * n_tiles + tile].
 __global__ void __launch_bounds__(256) k_inv_count(const int32_t* __restrict__ idx,
                                                    int32_t* __restrict__ tile_counts, int L,
                                                    int Hkv, int K, int nC, int tile_tokens,
-                                                   int n_tiles) {
+                                                   int n_tiles, int n_parts) {
   extern __shared__ int32_t cnt[];
-  const int tile = blockIdx.x % n_tiles;
-  const int bg = blockIdx.x / n_tiles;
+  const int part = blockIdx.x % n_parts;
+  const int tile = (blockIdx.x / n_parts) % n_tiles;
+  const int bg = blockIdx.x / n_parts / n_tiles;
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
-  for (int c = threadIdx.x; c < nC; c += blockDim.x) cnt[c] = 0;
+  const int c_lo = part * kIndexPart, nCp = min(nC - c_lo, kIndexPart);
+  for (int c = threadIdx.x; c < nCp; c += blockDim.x) cnt[c] = 0;
   __syncthreads();
   const int t0 = tile * tile_tokens;
   const int n = (min(L, t0 + tile_tokens) - t0) * K;
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int t = t0 + i / K, k = i % K;
-    const int c = idx[((b * L + t) * Hkv + g) * K + k];
-    if (c >= 0 && c < nC) atomicAdd(&cnt[c], 1);
+    const int c = idx[((b * L + t) * Hkv + g) * K + k] - c_lo;
+    if (c >= 0 && c < nCp) atomicAdd(&cnt[c], 1);
   }
   __syncthreads();
-  int32_t* out = tile_counts + (size_t)bg * nC * n_tiles + tile;
-  for (int c = threadIdx.x; c < nC; c += blockDim.x) out[(size_t)c * n_tiles] = cnt[c];
+  int32_t* out = tile_counts + ((size_t)bg * nC + c_lo) * n_tiles + tile;
+  for (int c = threadIdx.x; c < nCp; c += blockDim.x) out[(size_t)c * n_tiles] = cnt[c];
 }
 
 // One wave per (b, g, chunk): exclusive prefix of the chunk's tile counts over the tiles
@@ -226,10 +233,10 @@ __global__ void __launch_bounds__(1024) k_inv_order(const int32_t* __restrict__ 
   for (int s = threadIdx.x; s < ns; s += blockDim.x) order[atomicAdd(&hist[bucket(s)], 1)] = s;
 }
 
-// Per (b, g, tile): place the tile's entries, a chunk's entries in token order from
-// offsets[c] + the tile's prefix for c.
-//   Bitmap path (W > 0: the tile's tokens fit W 64-bit words, and the block's LDS holds a
-//   word row per chunk): each chunk's row marks the tile's tokens that chose it, and an
+// Per (b, g, tile, part): place the tile's entries whose chunk lies in the part, a chunk's
+// entries in token order from offsets[c] + the tile's prefix for c.
+//   Bitmap path (W > 0: a single part, the tile's tokens fit W 64-bit words, and the block's
+//   LDS holds a word row per chunk): each chunk's row marks the tile's tokens that chose it, and an
 //   entry's place among the chunk's entries of the tile is the number of marked tokens before
 //   its own, so every entry is placed in parallel.  This needs each row's chunks distinct.
 //   Walk path (W = 0, or a row that repeats a chunk): wave 0 walks the tile's tokens in order
@@ -245,20 +252,23 @@ constexpr int kScatterThreads = 256;
 __global__ void __launch_bounds__(kScatterThreads) k_inv_scatter(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ tile_prefix,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ entries, int L, int Hkv, int K,
-    int nC, int tile_tokens, int n_tiles, int W) {
-  extern __shared__ int32_t cnt[];  // nC counters, then (bitmap path) nC * W mask words
+    int nC, int tile_tokens, int n_tiles, int n_parts, int W) {
+  // the part's counters, then (bitmap path) nC * W mask words
+  extern __shared__ int32_t cnt[];
   __shared__ int32_t sel[kScatterBatch * kMaxK];
   __shared__ uint16_t dup[kScatterBatch * kMaxK];  // rank among equal slots | their number << 8
-  const int tile = blockIdx.x % n_tiles;
-  const int bg = blockIdx.x / n_tiles;
+  const int part = blockIdx.x % n_parts;
+  const int tile = (blockIdx.x / n_parts) % n_tiles;
+  const int bg = blockIdx.x / n_parts / n_tiles;
   const int g = bg % Hkv;
   const size_t b = bg / Hkv;
   const int tid = threadIdx.x, lane = tid % kWave;
-  const int32_t* tp = tile_prefix + (size_t)bg * nC * n_tiles + tile;
-  const int32_t* off = offsets + (size_t)bg * (nC + 1);
-  unsigned long long* mask = reinterpret_cast<unsigned long long*>(cnt + ((nC + 1) & ~1));
-  for (int c = tid; c < nC; c += kScatterThreads) cnt[c] = off[c] + tp[(size_t)c * n_tiles];
-  for (int i = tid; i < nC * W; i += kScatterThreads) mask[i] = 0;
+  const int c_lo = part * kIndexPart, nCp = min(nC - c_lo, kIndexPart);
+  const int32_t* tp = tile_prefix + ((size_t)bg * nC + c_lo) * n_tiles + tile;
+  const int32_t* off = offsets + (size_t)bg * (nC + 1) + c_lo;
+  unsigned long long* mask = reinterpret_cast<unsigned long long*>(cnt + ((nCp + 1) & ~1));
+  for (int c = tid; c < nCp; c += kScatterThreads) cnt[c] = off[c] + tp[(size_t)c * n_tiles];
+  for (int i = tid; i < nCp * W; i += kScatterThreads) mask[i] = 0;
   int32_t* ent = entries + (size_t)bg * L * K;
   const int t0 = tile * tile_tokens;
   const int t1 = min(L, t0 + tile_tokens);
@@ -290,16 +300,16 @@ __global__ void __launch_bounds__(kScatterThreads) k_inv_scatter(
     }
     if (!__syncthreads_or(rep) && W > 0) {
       for (int i = tid; i < nt * K; i += kScatterThreads) {
-        const int c = sel[i];
-        if (c >= 0 && c < nC) {
+        const int c = sel[i] - c_lo;
+        if (c >= 0 && c < nCp) {
           const int tt = i / K;
           atomicOr(&mask[c * W + tt / 64], 1ull << (tt % 64));
         }
       }
       __syncthreads();
       for (int i = tid; i < nt * K; i += kScatterThreads) {
-        const int c = sel[i];
-        if (c >= 0 && c < nC) {
+        const int c = sel[i] - c_lo;
+        if (c >= 0 && c < nCp) {
           const int tt = i / K;
           const unsigned long long* m = mask + c * W;
           int r = __popcll(m[tt / 64] & ((1ull << (tt % 64)) - 1));
@@ -312,8 +322,8 @@ __global__ void __launch_bounds__(kScatterThreads) k_inv_scatter(
     if (tid < kWave) {
       for (int tt = 0; tt < nt; ++tt) {
         if (lane < K) {
-          const int c = sel[tt * K + lane];
-          if (c >= 0 && c < nC) {
+          const int c = sel[tt * K + lane] - c_lo;
+          if (c >= 0 && c < nCp) {
             const int r = dup[tt * K + lane];
             const int pos = cnt[c] + (r & 0xff);  // every lane reads before any lane writes
             if ((r & 0xff) == 0) cnt[c] = pos + (r >> 8);
@@ -330,10 +340,11 @@ hipError_t launch_invidx(const Dims& d, const IndexLayout& lay, const int32_t* i
   const int bg = d.B * d.Hkv;
   if (bg == 0 || d.nC == 0) return hipSuccess;
   int32_t* tc = (int32_t*)(ws + lay.tile_counts);
-  size_t lds = sizeof(int32_t) * d.nC;
+  const int n_parts = (d.nC + kIndexPart - 1) / kIndexPart;
+  const size_t lds = sizeof(int32_t) * (d.nC < kIndexPart ? d.nC : kIndexPart);
   Timed tm(HSA_KERNEL_INVIDX, s);
-  k_inv_count<<<dim3(bg * lay.n_tiles), 256, lds, s>>>(idx, tc, d.L, d.Hkv, d.K, d.nC,
-                                                        lay.tile_tokens, lay.n_tiles);
+  k_inv_count<<<dim3(bg * lay.n_tiles * n_parts), 256, lds, s>>>(
+      idx, tc, d.L, d.Hkv, d.K, d.nC, lay.tile_tokens, lay.n_tiles, n_parts);
   const int rows = bg * d.nC;
   k_inv_colscan<<<dim3((rows + 3) / 4), 256, 0, s>>>(tc, (int32_t*)(ws + lay.offsets),
                                                      (int32_t*)(ws + lay.seg_start), d.nC,
@@ -342,13 +353,14 @@ hipError_t launch_invidx(const Dims& d, const IndexLayout& lay, const int32_t* i
                                        (int32_t*)(ws + lay.seg_start),
                                        (int32_t*)(ws + lay.seg_chunk),
                                        (int32_t*)(ws + lay.n_seg), d.nC, lay.max_seg);
-  // the bitmap path when the tile's tokens fit four words and the masks 48 KB of LDS
+  // the bitmap path when the tile's tokens fit four words and the masks 48 KB of LDS (which
+  // also keeps it to a single part)
   const int W = (lay.tile_tokens + 63) / 64;
   const size_t lds_bm = sizeof(int32_t) * ((d.nC + 1) & ~1) + sizeof(uint64_t) * (size_t)d.nC * W;
-  const bool bm = W <= 4 && W * 64 <= kScatterBatch && lds_bm <= 48 * 1024;
-  k_inv_scatter<<<dim3(bg * lay.n_tiles), kScatterThreads, bm ? lds_bm : lds, s>>>(
+  const bool bm = n_parts == 1 && W <= 4 && W * 64 <= kScatterBatch && lds_bm <= 48 * 1024;
+  k_inv_scatter<<<dim3(bg * lay.n_tiles * n_parts), kScatterThreads, bm ? lds_bm : lds, s>>>(
       idx, tc, (const int32_t*)(ws + lay.offsets), (int32_t*)(ws + lay.entries), d.L, d.Hkv,
-      d.K, d.nC, lay.tile_tokens, lay.n_tiles, bm ? W : 0);
+      d.K, d.nC, lay.tile_tokens, lay.n_tiles, n_parts, bm ? W : 0);
   k_inv_order<<<dim3(bg), 1024, 0, s>>>((const int32_t*)(ws + lay.offsets),
                                         (const int32_t*)(ws + lay.seg_start),
                                         (const int32_t*)(ws + lay.seg_chunk),

@@ -64,8 +64,8 @@ hsa_status_t check_problem(int op, const hsa_problem_t* p, hsa::Dims* d) {
   if (!isfinite(p->sm_scale) || !isfinite(p->sel_scale))
     return fail(HSA_ERR_INVALID_ARG, "scales must be finite");
   const int nC = p->L / p->S;
-  if (op == HSA_OP_BWD && nC > 16384)
-    return fail(HSA_ERR_UNSUPPORTED, "backward supports at most 16384 chunks (nC=%d)", nC);
+  if (op == HSA_OP_BWD && nC > 32767)
+    return fail(HSA_ERR_UNSUPPORTED, "backward supports at most 32767 chunks (nC=%d)", nC);
   d->B = p->B;
   d->L = p->L;
   d->Hq = p->Hq;

@@ -46,8 +46,8 @@
  *   - Calls are reentrant; concurrent calls must use distinct workspaces.
  *
  * Supported envelope: S = 64; D in {64, 128}; 1 <= K <= 16; Hq % Hkv == 0 with
- * 1 <= Hq/Hkv <= 16; dtype fp32 or bf16; L*K < 2^31.  Anything else returns
- * HSA_ERR_UNSUPPORTED.
+ * 1 <= Hq/Hkv <= 16; dtype fp32 or bf16; L*K < 2^31; hsa_bwd at most 32767 chunks (L/S).
+ * Anything else returns HSA_ERR_UNSUPPORTED.
  */
 #ifndef HSA_H_
 #define HSA_H_

@@ -72,6 +72,18 @@ def test_workspace_sizes_positive_where_needed():
     assert lib.hsa_workspace_size(9, ctypes.byref(p), ctypes.byref(n)) == 1
 
 
+def test_backward_chunk_limit():
+    """The backward takes up to 32767 chunks (its inverse index splits the chunks into parts
+    of 16384 past that many); beyond, HSA_ERR_UNSUPPORTED."""
+    from chunk_sparse_attention_amd import _lib
+    lib = _lib.lib()
+    n = ctypes.c_size_t(0)
+    for nC, status in ((16384, 0), (16385, 0), (32767, 0), (32768, 2)):
+        p = _prob(L=64 * nC, K=2)
+        assert lib.hsa_workspace_size(_lib.HSA_OP_BWD, ctypes.byref(p), ctypes.byref(n)) == status, nC
+    assert b"32767" in lib.hsa_last_error()
+
+
 def test_entry_points_reject_before_launch():
     """NULL / misaligned pointers and missing workspace are reported without any launch."""
     from chunk_sparse_attention_amd import _lib

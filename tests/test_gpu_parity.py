@@ -842,15 +842,19 @@ def test_full_step_sampled(hsa, dev, name):
     compare_backward(orc, x, wl, g, f, diff, grads, tok_mask=tm, chunk_mask=cm)
 
 
-@pytest.mark.parametrize("D,Hq,Hkv", [(64, 8, 2), (128, 4, 1)], ids=["d64", "d128"])
-def test_max_chunks_step_sampled(hsa, dev, D, Hq, Hkv):
-    """The largest sequence the backward takes (16384 chunks and a ragged tail of 37 tokens):
-    select, forward and backward on one workspace.  dO is zero except on a sample T of rows,
-    so that the rows outside T add exact zeros to every gradient; the oracle then needs only
-    T's selection (its other rows select nothing), and dK, dV, dKslc are compared on the
-    chunks T selected plus others that must stay zero, dQ and dQs on T and rows outside it."""
+@pytest.mark.parametrize("D,Hq,Hkv,nC", [(64, 8, 2, 16384), (128, 4, 1, 16384),
+                                         (64, 4, 1, 16384 + 1500)],
+                         ids=["d64", "d128", "d64_two_index_parts"])
+def test_max_chunks_step_sampled(hsa, dev, D, Hq, Hkv, nC):
+    """Long sequences (16384 chunks, the most the chunk-major forward takes, and 17884, where
+    the forward runs on token tiles and the backward's inverse index splits the chunks into
+    two parts), each with a ragged tail of 37 tokens: select, forward and backward on one
+    workspace.  dO is zero except on a sample T of rows, so that the rows outside T add exact
+    zeros to every gradient; the oracle then needs only T's selection (its other rows select
+    nothing), and dK, dV, dKslc are compared on the chunks T selected plus others that must
+    stay zero, dQ and dQs on T and rows outside it."""
     from chunk_sparse_attention_amd import _lib
-    wl = W(f"max_chunks_d{D}", 1, 64 * 16384 + 37, Hq, Hkv, D, 64, 8, torch.bfloat16)
+    wl = W(f"max_chunks_d{D}_nc{nC}", 1, 64 * nC + 37, Hq, Hkv, D, 64, 8, torch.bfloat16)
     assert wl.G == 4  # the matrix-core forward and backward
     say("case max chunks step", wl)
     x = workloads.make_inputs(wl, seed=11)
