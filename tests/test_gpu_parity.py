@@ -721,6 +721,7 @@ def test_decode_host_kv_rejects_other_memory(hsa, dev):
     ("f32_d64_g4_k4", torch.float32, 64, 4, 1, 4, 1024 + 17),
     ("bf16_d128_g16_k16", torch.bfloat16, 128, 32, 2, 16, 64 * 40 + 5),
     ("bf16_d64_g1_k1", torch.bfloat16, 64, 8, 8, 1, 64 * 20),
+    ("bf16_d64_g2_k8", torch.bfloat16, 64, 4, 2, 8, 64 * 33 + 9),
     ("f32_d128_g4_k3", torch.float32, 128, 16, 4, 3, 64 * 9),
 ], ids=lambda s: s[0])
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
