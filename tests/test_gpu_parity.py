@@ -376,7 +376,8 @@ def test_decode_ties(hsa, dev, case, k):
 
 
 SOFTMAX_CASES = [w for w in SMALL if w.name in ("tiny_fp32", "bf16_d64_ragged", "bf16_d128_ragged",
-                                               "bf16_g1_k3", "fp32_k1", "bf16_d64_g16_k16")]
+                                               "bf16_g1_k3", "fp32_k1", "bf16_d64_g16_k16",
+                                               "bf16_g2_d128")]
 
 
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
@@ -416,7 +417,8 @@ def test_decode_softmax_weights(hsa, dev, ctx, generic):
     assert max_abs(npy(O), d["O"]) <= 2e-2
 
 
-LAYER_CASES = [w for w in SMALL if w.name in ("tiny_fp32", "bf16_d64_ragged", "bf16_d128_ragged")]
+LAYER_CASES = [w for w in SMALL if w.name in ("tiny_fp32", "bf16_d64_ragged", "bf16_d128_ragged",
+                                             "bf16_g2_d64_ragged")]
 
 
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
