@@ -217,14 +217,30 @@ __device__ __forceinline__ uint64_t rank_candidates(const uint64_t* __restrict__
                                                     int K, int lane, uint64_t* lds) {
   const int nl = n_cand / K;
   if (nl <= kWave) {
-    const uint32_t mine = lane < nl ? (uint32_t)(cb[lane * K] >> 32) : 0;
+    // With at most two keys per lane every key is loaded at once and the list heads are
+    // taken from the lanes that hold them, so that the ranking waits for one round trip.
+    const bool two = n_cand <= 2 * kWave;
+    uint64_t ka = 0, kb = 0;
+    uint32_t mine;
+    if (two) {
+      ka = lane < n_cand ? cb[lane] : 0;
+      kb = lane + kWave < n_cand ? cb[lane + kWave] : 0;
+      const int h = lane * K;  // this lane's list head (lanes < nl)
+      const uint64_t ha = __shfl(ka, h % kWave), hb = __shfl(kb, h % kWave);
+      mine = lane < nl ? (uint32_t)((h < kWave ? ha : hb) >> 32) : 0;
+    } else {
+      mine = lane < nl ? (uint32_t)(cb[lane * K] >> 32) : 0;
+    }
+    lds[lane] = mine;
+    wave_lds_sync();
     int n_ge = 0;  // lists whose first score is at least this lane's
-    for (int j = 0; j < nl; ++j) n_ge += (uint32_t)(cb[j * K] >> 32) >= mine ? 1 : 0;
+    for (int j = 0; j < nl; ++j) n_ge += (uint32_t)lds[j] >= mine ? 1 : 0;
     const uint32_t thr = wave_max_u32(n_ge >= K ? mine : 0);
+    wave_lds_sync();  // lds is reused below
     int nc = 0;
     for (int i0 = 0; i0 < n_cand; i0 += kWave) {
       const int i = i0 + lane;
-      const uint64_t k = i < n_cand ? cb[i] : 0;
+      const uint64_t k = two ? (i0 == 0 ? ka : kb) : (i < n_cand ? cb[i] : 0);
       const bool c = k != 0 && (uint32_t)(k >> 32) >= thr;
       const uint64_t bal = __ballot(c);
       const int pos = nc + __popcll(bal & ((1ull << lane) - 1));
