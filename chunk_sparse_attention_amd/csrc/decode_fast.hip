@@ -328,6 +328,7 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
 
   int my_c = -1;       // lane k < K: slot k's chunk (-1 = masked)
   double wslot = 0.0;  // and its weight
+  uint64_t mykey = 0;
   if (sel_idx) {
     // a selection made before (an earlier layer's): the slots' chunks and weights as given
     if (lane < K) {
@@ -336,8 +337,43 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
       wslot = my_c >= 0 ? (double)sel_w[(size_t)bg * K + lane] : 0.0;
     }
   } else {
-    const uint64_t mykey =
+    mykey =
         n_cand > 0 ? rank_candidates(cand + (size_t)bg * n_cand, n_cand, K, lane, rk[slot]) : 0;
+    my_c = mykey != 0 ? key_chunk(mykey) : -1;
+  }
+  // this wave's slot, read from lane `slot`
+  const int mine = __builtin_amdgcn_readlane(my_c, slot);
+  const size_t kvstride = (size_t)Hkv * D;
+  const size_t cbase = ((b * ctx + (size_t)(mine >= 0 ? mine : 0) * kChunk) * Hkv + g) * D;
+  const int p8 = lane % P, jg = lane / P;
+  // key row j in lane j; the value pieces are requested at the same time where the
+  // register budget holds both (otherwise after the logits)
+  constexpr bool kEarlyV = sizeof(T) == 2 && (NT <= 512 || D == 64);
+  // with 128 registers per lane a D = 128 key row is taken in two halves, one after the
+  // other (the logits still accumulate in dimension order)
+  constexpr int KP = (NT > 512 && D == 128) ? 2 : 1;
+  constexpr int DK = D / KP;
+  // fp32 d = 128 value rows in 1024-thread blocks are taken in two parts (128 registers per
+  // lane would not hold them all)
+  constexpr int VP = (sizeof(T) == 4 && NT > 512 && D == 128) ? 2 : 1;
+  constexpr int RPV = RPL / VP;
+  RawRow<T, 8> vp[RPV];
+  auto load_v = [&](int part) {
+#pragma unroll
+    for (int i = 0; i < RPV; ++i)
+      vp[i].load(Vc + cbase + (size_t)(jg + JG * (part * RPV + i)) * kvstride + 8 * p8);
+  };
+  // the slot's key row (the whole row, or its first half) and, where they fit, its value
+  // pieces are requested before the weights are formed, whose work then overlaps their
+  // latency (not for fp32 rows in 1024-thread blocks, whose 128 registers per lane would
+  // not hold them across the weights)
+  constexpr bool kEarlyK = sizeof(T) == 2 || NT <= 512;
+  RawRow<T, DK> kr0;
+  if (kEarlyK && mine >= 0) {
+    kr0.load(Kc + cbase + (size_t)lane * kvstride);
+    if (kEarlyV) load_v(0);
+  }
+  if (!sel_idx) {
     if (softmax_w) {
       // softmax of the valid slots' scores (lanes 0..K-1), shifted by their maximum and
       // summed in slot order
@@ -374,41 +410,24 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
         w[o] = (float)wslot;
       }
     }
-    my_c = mykey != 0 ? key_chunk(mykey) : -1;
   }
   // the valid slots (the first ones, in what the scan ranks; in a given selection, any)
   const uint64_t vmask = __ballot(lane < K && my_c >= 0);
-  // this wave's slot, read from lane `slot`
-  const int mine = __builtin_amdgcn_readlane(my_c, slot);
   const float wf = __shfl((float)wslot, slot);
   __syncthreads();  // qsh ready
 
   if (mine >= 0) {
-    const int c = mine;
-    const size_t kvstride = (size_t)Hkv * D;
-    const size_t cbase = ((b * ctx + (size_t)c * kChunk) * Hkv + g) * D;
-    const int p8 = lane % P, jg = lane / P;
-    // key row j in lane j; the value pieces are requested at the same time where the
-    // register budget holds both (otherwise after the logits)
-    constexpr bool kEarlyV = sizeof(T) == 2 && (NT <= 512 || D == 64);
-    // with 128 registers per lane a D = 128 key row is taken in two halves, one after the
-    // other (the logits still accumulate in dimension order)
-    constexpr int KP = (NT > 512 && D == 128) ? 2 : 1;
-    constexpr int DK = D / KP;
-    RawRow<T, 8> vp[RPL];
-    auto load_v = [&]() {
-#pragma unroll
-      for (int i = 0; i < RPL; ++i)
-        vp[i].load(Vc + cbase + (size_t)(jg + JG * i) * kvstride + 8 * p8);
-    };
     float z[ZH];
 #pragma unroll
     for (int h = 0; h < ZH; ++h) z[h] = 0.0f;
 #pragma unroll 1
     for (int kp = 0; kp < KP; ++kp) {
       RawRow<T, DK> kr;
-      kr.load(Kc + cbase + (size_t)lane * kvstride + kp * DK);
-      if (kEarlyV && kp == 0) load_v();
+      if (kEarlyK && kp == 0)
+        kr = kr0;
+      else
+        kr.load(Kc + cbase + (size_t)lane * kvstride + kp * DK);
+      if (!kEarlyK && kEarlyV && kp == 0) load_v(0);
 #pragma unroll
       for (int h = 0; h < ZH; ++h) {
         if (h < nh) {
@@ -437,22 +456,25 @@ __global__ void __launch_bounds__(NT) k_dec_attend_heads(
       }
       ash[slot][h][lane] = aw;
     }
-    if (!kEarlyV) load_v();
-    // value product: lane (jg, p8) accumulates rows jg + JG*i of piece p8
+    // value product: lane (jg, p8) accumulates rows jg + JG*i of piece p8, in row order
     float acc[ZH][8];
 #pragma unroll
     for (int h = 0; h < ZH; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      const int j = jg + JG * i;
+    for (int part = 0; part < VP; ++part) {
+      if (!kEarlyV) load_v(part);
 #pragma unroll
-      for (int h = 0; h < ZH; ++h) {
-        if (h >= nh) continue;
-        const float aw = ash[slot][h][j];
+      for (int i = 0; i < RPV; ++i) {
+        const int j = jg + JG * (part * RPV + i);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(aw, vp[i].get(e), acc[h][e]);
+        for (int h = 0; h < ZH; ++h) {
+          if (h >= nh) continue;
+          const float aw = ash[slot][h][j];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(aw, vp[i].get(e), acc[h][e]);
+        }
       }
     }
     // sum over the JG row groups: lanes p8 + P*jg

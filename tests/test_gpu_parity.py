@@ -725,6 +725,7 @@ def test_decode_host_kv_rejects_other_memory(hsa, dev):
     ("bf16_d64_g1_k1", torch.bfloat16, 64, 8, 8, 1, 64 * 20),
     ("bf16_d64_g2_k8", torch.bfloat16, 64, 4, 2, 8, 64 * 33 + 9),
     ("f32_d128_g4_k3", torch.float32, 128, 16, 4, 3, 64 * 9),
+    ("f32_d128_g4_k12", torch.float32, 128, 8, 2, 12, 64 * 30 + 3),
 ], ids=lambda s: s[0])
 @pytest.mark.parametrize("generic", [True, False], ids=["generic", "default"])
 def test_decode_shapes(hsa, dev, shape, generic):
