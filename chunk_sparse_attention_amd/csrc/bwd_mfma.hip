@@ -366,7 +366,7 @@ k_bwd_chunk_keys(
     const int32_t* __restrict__ seg_order, float* __restrict__ part_dk, float* __restrict__ part_dv,
     bf16* __restrict__ dq_part, float* __restrict__ dw_out, int L, int Hq, int Hkv, int Kn,
     int nC, int seg, int64_t max_seg, float c2, float sm_scale) {
-  constexpr int D = 128, TPJ = 16 / G, KS = D / 32, DT = D / 16, NT = 128;
+  constexpr int D = 128, TPJ = 16 / G, KS = D / 32, NT = 128;
   // rows of D + 16 elements: no LDS bank conflicts in the operand and transposing reads
   constexpr int KROW = D + 16;
   __shared__ __attribute__((aligned(16))) uint16_t kl[64][KROW];
