@@ -56,6 +56,8 @@ SMALL = [
     W("bf16_g2_d64_ragged", 1, 64 * 13 + 11, 8, 4, 64, 64, 8, torch.bfloat16),
     W("bf16_g2_d128", 1, 64 * 12 + 3, 4, 2, 128, 64, 5, torch.bfloat16),
     W("bf16_g1_d128_b2", 2, 64 * 9 + 7, 2, 2, 128, 64, 4, torch.bfloat16),
+    W("bf16_g1_d64_k16", 1, 64 * 22 + 13, 4, 4, 64, 64, 16, torch.bfloat16),
+    W("bf16_g2_d128_k16", 1, 64 * 19 + 1, 8, 4, 128, 64, 16, torch.bfloat16),
 ]
 
 
